@@ -1,0 +1,318 @@
+/*
+ * q8s_oracle.c -- the CPU oracle for the Q8_0 GEMV / sparse-MoE hot path.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT.  Only the test-suite, the smoke check and
+ * the CPU-baseline leg of the benchmark may load this library.  It shares no
+ * code, header, table or helper with the HIP library under
+ * q8_gemv_sparse_amd/csrc, and that library never calls it.
+ *
+ * Every function here is a plain, slow, obviously-correct statement of what the
+ * path computes: loops in index order, double precision for every
+ * floating-point sum, no blocking, no fusion, no reordering.  Build it with
+ * floating-point contraction off and no fast-math (oracle/build.py does), so
+ * that the few float32 steps (the residual sum and the activation quantiser)
+ * are single IEEE float32 operations.
+ *
+ * Sources (the pages this follows), cited by page and item:
+ *   [Q8Ref]      codegen_cuda::qwen_emit module page, struct Q8Ref:
+ *                W[o][t] = quants[o*in + t] * scales[o*nb + t/32].
+ *   [MoeWeights] same page, struct MoeWeights: router [E,d], gate/up
+ *                [E*dff, d], down [E*d, dff], expert e's rows start at e*dff
+ *                (gate/up) or e*d (down).
+ *   [emit_moe]   same page, fn emit_moe_forward: router GEMV, top-K route
+ *                (softmax, keep K, renormalise), each kept expert's SwiGLU with
+ *                an expert-indexed weight base, weighted combine; f32
+ *                activations times int8 weights with f64 sums.
+ *   [Q8MatKind]  same page, enum Q8MatKind, and codegen_cuda/lane/mod.rs
+ *                module doc (CudaKnobs `activations`): f32 activations with
+ *                f64 sums, or llama.cpp's one int8 word per activation.
+ *   [numerics]   codegen_cuda/forward_shim.rs, impl Shim for ForwardShim,
+ *                fn numerics / fn fits: 32-bit integer accumulators.
+ *   [add_norm]   codegen_cuda/forward_shim.rs module doc: a sum and the RMS
+ *                norm of it as one row kernel writing the sum; a weighted RMS
+ *                norm scales and never shifts (fn kernel_refusal).
+ *   [epilogue]   codegen_cuda/forward_shim.rs module doc: under the one-word
+ *                int8 numerics the activation a Q8_0 projection reads is
+ *                quantised in its producer's epilogue.
+ *   [scratch]    codegen_cuda/lane/arena.rs, fn scratch / fn array_bytes: a
+ *                quantised activation is int8 words plus one f32 scale a
+ *                32-value block; the decode mixture keeps its hidden row
+ *                quantised (hq/hs) in one-word int8 mode.
+ *
+ * Readings taken where the pages are silent (each is listed with its reason
+ * in the project's design notes):
+ *   - the activation quantiser is llama.cpp's Q8_0 reference quantiser with an
+ *     f32 scale: d = amax/127, id = 1/d (0 when d = 0), q = round-half-away(v*id)
+ *     clamped to [-127, 127], every step in float32;
+ *   - RMSNorm: y = (s / sqrt(mean(s^2) + eps)) * w, eps inside the root;
+ *   - routing ranks by logit, ties to the lower expert index; softmax over all
+ *     E experts, then the kept weights renormalised to sum 1;
+ *   - SiLU(z) = z / (1 + exp(-z)); the hidden row h = SiLU(g) * u is held as a
+ *     float32 tensor between the gate-up and the down projection (and, in int8
+ *     mode, quantised per 32-value block of each expert's row).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define QBLOCK 32
+
+/* ---------------------------------------------------------------------------
+ * G -- Q8_0 GEMV with f32 activations [Q8Ref], [emit_moe], [Q8MatKind]:
+ *   y[r][o] = sum_t (Wq[o*n_in + t] * Ws[o*nb + t/32]) * x[r*n_in + t]
+ * every product and the sum in double, t in index order.
+ */
+void oracle_gemv_f32(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in,
+                     const float *x, int64_t m, double *y)
+{
+    int64_t nb = n_in / QBLOCK;
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t o = 0; o < n_out; o++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < n_in; t++) {
+                double w = (double)Wq[o * n_in + t] * (double)Ws[o * nb + t / QBLOCK];
+                acc += w * (double)x[r * n_in + t];
+            }
+            y[r * n_out + o] = acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Q -- the Q8_0 activation quantiser [Q8MatKind] (llama.cpp's one int8 word),
+ * [scratch] (f32 scale per 32 values).  Each 32-value block of each row:
+ *   amax = max |v|;  d = amax / 127;  id = d ? 1/d : 0;
+ *   q = clamp(round_half_away_from_zero(v * id), -127, 127)
+ * all in float32.  roundf rounds halfway cases away from zero.
+ */
+void oracle_quantize(const float *v, int64_t rows, int64_t n, int8_t *q, float *d)
+{
+    int64_t nb = n / QBLOCK;
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            const float *blk = v + r * n + b * QBLOCK;
+            float amax = 0.0f;
+            for (int t = 0; t < QBLOCK; t++) {
+                float a = fabsf(blk[t]);
+                if (a > amax)
+                    amax = a;
+            }
+            float dsc = amax / 127.0f;
+            float id = (dsc != 0.0f) ? 1.0f / dsc : 0.0f;
+            for (int t = 0; t < QBLOCK; t++) {
+                float p = blk[t] * id;
+                float rq = roundf(p);
+                if (rq > 127.0f)
+                    rq = 127.0f;
+                if (rq < -127.0f)
+                    rq = -127.0f;
+                q[r * n + b * QBLOCK + t] = (int8_t)rq;
+            }
+            d[r * nb + b] = dsc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * The exact int32 block dots of the one-word int8 mode [numerics]:
+ *   isum[r][o][b] = sum_{t in block b} Wq[o][t] * xq[r][t]
+ * |isum| <= 32 * 127 * 127 = 516128, so int32 holds it exactly.
+ */
+void oracle_block_dots(const int8_t *Wq, int64_t n_out, int64_t n_in, const int8_t *xq,
+                       int64_t m, int32_t *isum)
+{
+    int64_t nb = n_in / QBLOCK;
+    for (int64_t r = 0; r < m; r++)
+        for (int64_t o = 0; o < n_out; o++)
+            for (int64_t b = 0; b < nb; b++) {
+                int32_t s = 0;
+                for (int t = 0; t < QBLOCK; t++)
+                    s += (int32_t)Wq[o * n_in + b * QBLOCK + t] * (int32_t)xq[r * n_in + b * QBLOCK + t];
+                isum[(r * n_out + o) * nb + b] = s;
+            }
+}
+
+/* ---------------------------------------------------------------------------
+ * I -- Q8_0 GEMV with one-word int8 activations [Q8MatKind], [numerics]:
+ *   y[r][o] = sum_b (Ws[o][b] * xs[r][b]) * isum[r][o][b]
+ * the block dots exact in int32, the scaling and the sum over blocks in double.
+ */
+void oracle_gemv_i8(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in,
+                    const int8_t *xq, const float *xs, int64_t m, double *y)
+{
+    int64_t nb = n_in / QBLOCK;
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t o = 0; o < n_out; o++) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; b++) {
+                int32_t s = 0;
+                for (int t = 0; t < QBLOCK; t++)
+                    s += (int32_t)Wq[o * n_in + b * QBLOCK + t] * (int32_t)xq[r * n_in + b * QBLOCK + t];
+                acc += ((double)Ws[o * nb + b] * (double)xs[r * nb + b]) * (double)s;
+            }
+            y[r * n_out + o] = acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * N -- residual add + weighted RMSNorm [add_norm]:
+ *   sum = h + r                     (one float32 add per element, written)
+ *   ms  = (1/d) sum_i sum_i^2       (double, index order)
+ *   y   = (sum / sqrt(ms + eps)) * w  computed as (sum * inv) * w in double,
+ *         inv = 1 / sqrt(ms + eps)
+ * y is returned in double; the path stores it as float32 (and/or its Q8_0 form,
+ * [epilogue]), which the caller derives by rounding and oracle_quantize.
+ */
+void oracle_add_rmsnorm(const float *h, const float *r, const float *w, int64_t rows, int64_t d,
+                        float eps, float *sum, double *y)
+{
+    for (int64_t i = 0; i < rows; i++) {
+        double ss = 0.0;
+        for (int64_t t = 0; t < d; t++) {
+            float s = h[i * d + t] + r[i * d + t];
+            sum[i * d + t] = s;
+            ss += (double)s * (double)s;
+        }
+        double ms = ss / (double)d;
+        double inv = 1.0 / sqrt(ms + (double)eps);
+        for (int64_t t = 0; t < d; t++)
+            y[i * d + t] = ((double)sum[i * d + t] * inv) * (double)w[t];
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * R -- the top-K softmax router [emit_moe] (softmax, keep K, renormalise),
+ * forward_shim.rs fn kernel_refusal (no router bias; renormalising; a softmax
+ * over every expert, not grouped):
+ *   l[e] = sum_t Wr[e][t] * x[t]      (double)
+ *   p    = softmax over all E         (double, max subtracted)
+ *   idx  = the K experts of largest l, ties to the lower index, in rank order
+ *   w[j] = p[idx[j]] / sum_{i<K} p[idx[i]]
+ * logits may be NULL.
+ */
+void oracle_route(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k,
+                  int32_t *idx, double *wts, double *logits)
+{
+    double *l = (double *)malloc((size_t)E * sizeof(double));
+    double *p = (double *)malloc((size_t)E * sizeof(double));
+    char *taken = (char *)malloc((size_t)E);
+    for (int64_t i = 0; i < rows; i++) {
+        for (int64_t e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int64_t t = 0; t < d; t++)
+                acc += (double)Wr[e * d + t] * (double)x[i * d + t];
+            l[e] = acc;
+            if (logits)
+                logits[i * E + e] = acc;
+        }
+        double mx = l[0];
+        for (int64_t e = 1; e < E; e++)
+            if (l[e] > mx)
+                mx = l[e];
+        double z = 0.0;
+        for (int64_t e = 0; e < E; e++) {
+            p[e] = exp(l[e] - mx);
+            z += p[e];
+        }
+        for (int64_t e = 0; e < E; e++)
+            p[e] = p[e] / z;
+        memset(taken, 0, (size_t)E);
+        double kept = 0.0;
+        for (int64_t j = 0; j < k; j++) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; e++) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || l[e] > l[best])
+                    best = e; /* strict '>' keeps the lower index on a tie */
+            }
+            taken[best] = 1;
+            idx[i * k + j] = (int32_t)best;
+            kept += p[best];
+        }
+        for (int64_t j = 0; j < k; j++)
+            wts[i * k + j] = p[idx[i * k + j]] / kept;
+    }
+    free(l);
+    free(p);
+    free(taken);
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* ---------------------------------------------------------------------------
+ * M -- the sparse MoE FFN block [emit_moe], [MoeWeights], each row apart:
+ *   route x (always from the float32 x, [epilogue]: an f32 router reads x);
+ *   for each kept expert j (e = idx[j]):
+ *     g = Wg[e*dff + o] . x,  u = Wu[e*dff + o] . x     (G, or I on Q(x))
+ *     h[j][o] = float32( SiLU(g) * u )                  (a float32 tensor)
+ *     dn[j][o'] = Wd[e*d + o'] . h[j]                   (G, or I on Q(h[j]))
+ *   y[o'] = sum_{j<K} w[j] * dn[j][o']                  (double, j order)
+ * act = 0: f32 activations; act = 1: one-word int8 activations, where x is
+ * quantised once per row and each expert's hidden row per 32-value block
+ * ([scratch]: hq/hs over K*dff).
+ * Outputs: idx [rows*k], wts [rows*k] (double), h [rows*k*dff] (float32),
+ * y [rows*d] (double).  Returns 0, or -1 for an unknown mode.
+ */
+int oracle_moe(int act, const float *x, const float *Wr, const int8_t *Wgq, const float *Wgs,
+               const int8_t *Wuq, const float *Wus, const int8_t *Wdq, const float *Wds,
+               int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
+               int32_t *idx, double *wts, float *h, double *y)
+{
+    if (act != 0 && act != 1)
+        return -1;
+    int64_t nbd = d / QBLOCK, nbf = dff / QBLOCK;
+    int8_t *xq = (int8_t *)malloc((size_t)d);
+    float *xs = (float *)malloc((size_t)nbd * sizeof(float));
+    int8_t *hq = (int8_t *)malloc((size_t)dff);
+    float *hs = (float *)malloc((size_t)nbf * sizeof(float));
+    double *g = (double *)malloc((size_t)dff * sizeof(double));
+    double *u = (double *)malloc((size_t)dff * sizeof(double));
+    double *dn = (double *)malloc((size_t)d * sizeof(double));
+
+    oracle_route(x, Wr, rows, d, E, k, idx, wts, NULL);
+    for (int64_t i = 0; i < rows; i++) {
+        const float *xr = x + i * d;
+        double *yr = y + i * d;
+        for (int64_t o = 0; o < d; o++)
+            yr[o] = 0.0;
+        if (act == 1)
+            oracle_quantize(xr, 1, d, xq, xs);
+        for (int64_t j = 0; j < k; j++) {
+            int64_t e = idx[i * k + j];
+            const int8_t *gq = Wgq + e * dff * d, *uq = Wuq + e * dff * d;
+            const float *gs = Wgs + e * dff * nbd, *us = Wus + e * dff * nbd;
+            const int8_t *dq = Wdq + e * d * dff;
+            const float *ds = Wds + e * d * nbf;
+            float *hj = h + (i * k + j) * dff;
+            if (act == 0) {
+                oracle_gemv_f32(gq, gs, dff, d, xr, 1, g);
+                oracle_gemv_f32(uq, us, dff, d, xr, 1, u);
+            } else {
+                oracle_gemv_i8(gq, gs, dff, d, xq, xs, 1, g);
+                oracle_gemv_i8(uq, us, dff, d, xq, xs, 1, u);
+            }
+            for (int64_t o = 0; o < dff; o++)
+                hj[o] = (float)(silu(g[o]) * u[o]);
+            if (act == 0) {
+                oracle_gemv_f32(dq, ds, d, dff, hj, 1, dn);
+            } else {
+                oracle_quantize(hj, 1, dff, hq, hs);
+                oracle_gemv_i8(dq, ds, d, dff, hq, hs, 1, dn);
+            }
+            double wj = wts[i * k + j];
+            for (int64_t o = 0; o < d; o++)
+                yr[o] += wj * dn[o];
+        }
+    }
+    free(xq);
+    free(xs);
+    free(hq);
+    free(hs);
+    free(g);
+    free(u);
+    free(dn);
+    return 0;
+}

@@ -1,0 +1,419 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each test checks the oracle against something other than its own formula:
+exact rational arithmetic, closed forms, brute force over tiny inputs, a
+library routine that computes the same definition another way, or an
+invariant.  The cases are chosen so that a plausible slip in the oracle (a
+dropped term, a wrong scale index, a transposed operand, a wrong rounding
+mode, mean vs sum, a sign) fails at least one of them.
+"""
+import itertools
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_q8(rng, n_out, n_in):
+    return synthetic.q8_matrix(rng, n_out, n_in)
+
+
+# ---------------------------------------------------------------------------
+# G: f32-activation GEMV
+
+
+@pytest.mark.parametrize("n_out,n_in,m", [(3, 64, 1), (4, 96, 2), (5, 32, 3)])
+def test_gemv_f32_matches_exact_rational(n_out, n_in, m):
+    rng = np.random.default_rng(11)
+    Wq, Ws = _rand_q8(rng, n_out, n_in)
+    x = synthetic.normal(rng, m, n_in)
+    y = oracle.gemv_f32(Wq, Ws, x)
+    for r in range(m):
+        for o in range(n_out):
+            terms = [Fraction(int(Wq[o, t])) * Fraction(float(Ws[o, t // 32])) * Fraction(float(x[r, t]))
+                     for t in range(n_in)]
+            exact = sum(terms, Fraction(0))
+            mag = float(sum(abs(t) for t in terms))
+            assert abs(Fraction(y[r, o]) - exact) <= Fraction((n_in + 1) * mag) * Fraction(2) ** -52
+
+
+def test_gemv_f32_equals_dense_dequant_matmul():
+    rng = np.random.default_rng(12)
+    Wq, Ws = _rand_q8(rng, 37, 320)
+    x = synthetic.normal(rng, 3, 320)
+    W = Wq.astype(np.float64) * np.repeat(Ws.astype(np.float64), 32, axis=1)
+    ref = x.astype(np.float64) @ W.T
+    y = oracle.gemv_f32(Wq, Ws, x)
+    assert np.max(np.abs(y - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_gemv_f32_scale_index_is_per_block_of_32():
+    # Wq = 1, x = 1, distinct power-of-two scale per (row, block):
+    # y[o] = 32 * sum_b Ws[o, b].  A t%32 (instead of t/32) index, or a
+    # transposed scale table, gives a different sum.
+    n_out, n_in = 3, 128
+    Wq = np.ones((n_out, n_in), np.int8)
+    Ws = np.array([[2.0 ** -(o * 4 + b) for b in range(4)] for o in range(n_out)], np.float32)
+    x = np.ones((1, n_in), np.float32)
+    y = oracle.gemv_f32(Wq, Ws, x)[0]
+    for o in range(n_out):
+        assert y[o] == 32 * sum(2.0 ** -(o * 4 + b) for b in range(4))
+
+
+def test_gemv_f32_rows_are_outputs():
+    # A weight with one non-zero row picks out exactly that output.
+    Wq = np.zeros((4, 64), np.int8)
+    Wq[2, 5] = -7
+    Ws = np.ones((4, 2), np.float32)
+    x = np.arange(64, dtype=np.float32)[None, :]
+    y = oracle.gemv_f32(Wq, Ws, x)[0]
+    assert list(y) == [0.0, 0.0, -35.0, 0.0]
+
+
+def test_gemv_f32_fill_closed_forms():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "fill_closed_forms.txt")) if l.strip() and not l.startswith("#")]
+    assert rows
+    for n_in, s, expect in rows:
+        n_in, s, expect = int(n_in), float(s), float(expect)
+        Wq = np.ones((2, n_in), np.int8)
+        Ws = np.full((2, n_in // 32), s, np.float32)
+        x = synthetic.fill_pattern(n_in)[None, :]
+        y = oracle.gemv_f32(Wq, Ws, x)[0]
+        assert list(y) == [expect, expect]
+
+
+def test_gemv_f32_linear_in_power_of_two_factors():
+    rng = np.random.default_rng(13)
+    Wq, Ws = _rand_q8(rng, 8, 64)
+    x = synthetic.normal(rng, 1, 64)
+    z = synthetic.normal(rng, 1, 64)
+    y1 = oracle.gemv_f32(Wq, Ws, 4.0 * x)
+    assert np.array_equal(y1, 4.0 * oracle.gemv_f32(Wq, Ws, x))
+    yx, yz, ys = oracle.gemv_f32(Wq, Ws, x), oracle.gemv_f32(Wq, Ws, z), oracle.gemv_f32(Wq, Ws, x + z)
+    # x + z is rounded to f32, so linearity holds to the f32 rounding of the sum
+    assert np.max(np.abs(ys - (yx + yz))) <= 1e-6 * np.max(np.abs(ys))
+
+
+# ---------------------------------------------------------------------------
+# Q: the Q8_0 activation quantiser
+
+
+def _nearest_away(p):
+    """Brute force: of the 255 codes -127..127, the one nearest to the float p,
+    ties away from zero."""
+    best = None
+    for c in range(-127, 128):
+        dist = abs(Fraction(c) - Fraction(float(p)))
+        if best is None or dist < best[0] or (dist == best[0] and abs(c) > abs(best[1])):
+            best = (dist, c)
+    return best[1]
+
+
+def test_quantize_brute_force():
+    rng = np.random.default_rng(21)
+    v = np.concatenate([synthetic.normal(rng, 2, 64), 1e-3 * synthetic.normal(rng, 1, 64),
+                        np.round(synthetic.normal(rng, 1, 64) * 20) / 4], axis=0).astype(np.float32)
+    q, d = oracle.quantize(v)
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            blk = v[r, b * 32:(b + 1) * 32]
+            amax = np.float32(np.max(np.abs(blk)))
+            dd = np.float32(amax) / np.float32(127.0)
+            assert d[r, b] == dd
+            idv = np.float32(1.0) / dd if dd != 0 else np.float32(0.0)
+            for t in range(32):
+                p = np.float32(blk[t]) * np.float32(idv)
+                assert q[r, b * 32 + t] == _nearest_away(p), (r, b, t)
+
+
+def test_quantize_closed_forms():
+    # A block of integers holding +-127 has d = 1 and q = v.
+    blk = np.array([127, -127] + list(range(-15, 15)), np.float32)
+    q, d = oracle.quantize(blk[None, :])
+    assert d[0, 0] == 1.0 and np.array_equal(q[0].astype(np.float32), blk)
+    # A zero block: d = 0, q = 0.
+    q, d = oracle.quantize(np.zeros((1, 32), np.float32))
+    assert d[0, 0] == 0.0 and not q.any()
+    # Halfway cases round away from zero (amax 127 gives d = 1, id = 1).
+    blk = np.zeros(32, np.float32)
+    blk[:7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.5, -126.5]
+    q, d = oracle.quantize(blk[None, :])
+    assert list(q[0, :7]) == [127, 3, -3, 1, -1, 2, -127]
+
+
+def test_quantize_round_trip_bound():
+    rng = np.random.default_rng(22)
+    v = synthetic.normal(rng, 8, 256)
+    q, d = oracle.quantize(v)
+    back = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    bound = np.repeat(d.astype(np.float64), 32, axis=1) * (0.5 + 1e-5)
+    assert np.all(np.abs(back - v) <= bound)
+    assert np.all(np.abs(q) <= 127)
+
+
+# ---------------------------------------------------------------------------
+# exact int32 block dots, and I: the int8-activation GEMV
+
+
+def test_block_dots_brute_force_and_extremes():
+    rng = np.random.default_rng(31)
+    Wq = synthetic.quants(rng, 3, 64)
+    xq = synthetic.quants(rng, 2, 64)
+    isum = oracle.block_dots(Wq, xq)
+    for r in range(2):
+        for o in range(3):
+            for b in range(2):
+                s = sum(int(Wq[o, t]) * int(xq[r, t]) for t in range(b * 32, b * 32 + 32))
+                assert isum[r, o, b] == s
+    W = np.full((1, 32), 127, np.int8)
+    X = np.full((1, 32), -127, np.int8)
+    assert oracle.block_dots(W, X)[0, 0, 0] == -516128
+
+
+def test_gemv_i8_exact_special_case():
+    # Power-of-two scales and the (p % 7) - 3 fill make every float step exact.
+    n_out, n_in = 6, 128
+    Wq = (synthetic.fill_pattern(n_out * n_in).reshape(n_out, n_in)).astype(np.int8)
+    xq = synthetic.fill_pattern(n_in + 3)[3:].astype(np.int8)[None, :]
+    Ws = np.array([[2.0 ** -((o + b) % 5) for b in range(4)] for o in range(n_out)], np.float32)
+    xs = np.array([[2.0 ** -(b % 3) for b in range(4)]], np.float32)
+    y = oracle.gemv_i8(Wq, Ws, xq, xs)[0]
+    for o in range(n_out):
+        exact = sum(Fraction(float(Ws[o, b])) * Fraction(float(xs[0, b])) *
+                    sum(int(Wq[o, t]) * int(xq[0, t]) for t in range(32 * b, 32 * b + 32)) for b in range(4))
+        assert Fraction(y[o]) == exact
+
+
+def test_gemv_i8_matches_exact_rational():
+    rng = np.random.default_rng(32)
+    Wq, Ws = _rand_q8(rng, 4, 96)
+    x = synthetic.normal(rng, 2, 96)
+    xq, xs = oracle.quantize(x)
+    y = oracle.gemv_i8(Wq, Ws, xq, xs)
+    for r in range(2):
+        for o in range(4):
+            terms = [Fraction(float(Ws[o, b])) * Fraction(float(xs[r, b])) *
+                     sum(int(Wq[o, t]) * int(xq[r, t]) for t in range(32 * b, 32 * b + 32)) for b in range(3)]
+            exact = sum(terms, Fraction(0))
+            mag = float(sum(abs(t) for t in terms))
+            assert abs(Fraction(y[r, o]) - exact) <= Fraction(8 * mag) * Fraction(2) ** -52
+
+
+def test_gemv_i8_within_quantisation_bound_of_f32_mode():
+    rng = np.random.default_rng(33)
+    Wq, Ws = _rand_q8(rng, 64, 256)
+    x = synthetic.normal(rng, 2, 256)
+    xq, xs = oracle.quantize(x)
+    yi = oracle.gemv_i8(Wq, Ws, xq, xs)
+    yf = oracle.gemv_f32(Wq, Ws, x)
+    Wabs = np.abs(Wq.astype(np.float64)) * np.repeat(Ws.astype(np.float64), 32, axis=1)
+    bound = Wabs @ (np.repeat(xs.astype(np.float64), 32, axis=1) * 0.50001).T
+    assert np.all(np.abs(yi - yf) <= bound.T + 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# N: residual add + RMSNorm
+
+
+def test_add_rmsnorm_sum_is_f32_add():
+    rng = np.random.default_rng(41)
+    h, r = synthetic.normal(rng, 3, 96), synthetic.normal(rng, 3, 96)
+    w = rng.uniform(0.5, 1.5, 96).astype(np.float32)
+    s, _ = oracle.add_rmsnorm(h, r, w, 1e-6)
+    assert np.array_equal(s, (h + r).astype(np.float32))
+
+
+def test_add_rmsnorm_constant_row_closed_form():
+    d, c, eps = 64, 0.75, 1e-6
+    h = np.full((1, d), c, np.float32)
+    r = np.zeros((1, d), np.float32)
+    w = np.linspace(0.5, 1.5, d).astype(np.float32)
+    _, y = oracle.add_rmsnorm(h, r, w, eps)
+    ref = w.astype(np.float64) * c / math.sqrt(c * c + np.float64(np.float32(eps)))
+    assert np.max(np.abs(y[0] - ref)) <= 1e-15
+
+
+def test_add_rmsnorm_matches_high_precision():
+    getcontext().prec = 60
+    rng = np.random.default_rng(42)
+    d = 96
+    h, r = synthetic.normal(rng, 2, d), synthetic.normal(rng, 2, d)
+    w = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    eps = np.float32(1e-5)
+    s, y = oracle.add_rmsnorm(h, r, w, eps)
+    for i in range(2):
+        ms = sum(Fraction(float(v)) ** 2 for v in s[i]) / d
+        den = (Decimal(ms.numerator) / Decimal(ms.denominator) + Decimal(float(eps))).sqrt()
+        for t in range(d):
+            ref = Decimal(float(s[i, t])) * Decimal(float(w[t])) / den
+            # ss carries up to ~d ulps of rounding; sqrt halves it.  A slip in the
+            # formula (sum for mean, eps outside the root) is >= 1e-6 relative.
+            assert abs(Decimal(y[i, t]) - ref) <= Decimal(4e-15) * abs(ref) + Decimal(1e-300)
+
+
+def test_add_rmsnorm_fused_equals_unfused():
+    # add then norm with no residual gives the same result as the fused call
+    rng = np.random.default_rng(43)
+    h, r = synthetic.normal(rng, 2, 128), synthetic.normal(rng, 2, 128)
+    w = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    s, y = oracle.add_rmsnorm(h, r, w, 1e-6)
+    s2, y2 = oracle.add_rmsnorm((h + r).astype(np.float32), np.zeros_like(h), w, 1e-6)
+    assert np.array_equal(s, s2) and np.array_equal(y, y2)
+
+
+# ---------------------------------------------------------------------------
+# R: routing
+
+
+@pytest.mark.parametrize("E,k", [(6, 2), (8, 3), (10, 4), (5, 5)])
+def test_route_brute_force_over_subsets(E, k):
+    rng = np.random.default_rng(51 + E)
+    d = 64
+    Wr = (0.02 * synthetic.normal(rng, E, d)).astype(np.float32)
+    x = synthetic.normal(rng, 3, d)
+    idx, wts, logits = oracle.route(x, Wr, k)
+    for i in range(3):
+        l = [sum(Fraction(float(Wr[e, t])) * Fraction(float(x[i, t])) for t in range(d)) for e in range(E)]
+        # the kept set maximises the summed logit; among equal sums, the
+        # lexicographically smallest index set
+        best = max(itertools.combinations(range(E), k), key=lambda c: (sum(l[e] for e in c), [-e for e in c]))
+        assert sorted(idx[i]) == list(best)
+        # rank order: logit descending, index ascending
+        order = sorted(best, key=lambda e: (-l[e], e))
+        assert list(idx[i]) == order
+        # weights: softmax over E, kept, renormalised (scipy's softmax)
+        p = scipy.special.softmax(np.array([float(v) for v in l]))
+        ref = p[order] / p[order].sum()
+        assert np.max(np.abs(wts[i] - ref)) <= 1e-14
+        assert abs(wts[i].sum() - 1.0) <= 1e-12
+
+
+def test_route_logits_are_router_matvec():
+    rng = np.random.default_rng(52)
+    Wr = (0.02 * synthetic.normal(rng, 128, 256)).astype(np.float32)
+    x = synthetic.normal(rng, 4, 256)
+    _, _, logits = oracle.route(x, Wr, 8)
+    ref = x.astype(np.float64) @ Wr.astype(np.float64).T
+    assert np.max(np.abs(logits - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_route_degenerate_cases():
+    d = 64
+    x = synthetic.normal(np.random.default_rng(53), 1, d)
+    # a zero router: every logit 0, ties to the lower index, equal weights
+    idx, wts, _ = oracle.route(x, np.zeros((16, d), np.float32), 4)
+    assert list(idx[0]) == [0, 1, 2, 3] and np.allclose(wts[0], 0.25, rtol=0, atol=1e-15)
+    # K = 1 gives weight 1
+    Wr = (0.02 * synthetic.normal(np.random.default_rng(54), 16, d)).astype(np.float32)
+    idx, wts, l = oracle.route(x, Wr, 1)
+    assert wts[0, 0] == 1.0 and idx[0, 0] == int(np.argmax(l[0]))
+    # explicit ties: rows 3 and 1 equal and largest -> 1 ranks before 3
+    Wr2 = np.zeros((6, d), np.float32)
+    Wr2[3] = Wr2[1] = x[0] / 8
+    Wr2[5] = x[0] / 16
+    idx, wts, _ = oracle.route(x, Wr2, 3)
+    assert list(idx[0]) == [1, 3, 5]
+    assert wts[0, 0] == wts[0, 1] > wts[0, 2]
+
+
+# ---------------------------------------------------------------------------
+# M: the MoE block
+
+
+def _deq(q, s):
+    return q.astype(np.float64) * np.repeat(s.astype(np.float64), 32, axis=1)
+
+
+def _dense_swiglu(x, Wg, Wu, Wd):
+    """A dense SwiGLU FFN in numpy float64, its hidden row held in float32."""
+    g = Wg @ x
+    u = Wu @ x
+    hid = (g / (1.0 + np.exp(-g)) * u).astype(np.float32).astype(np.float64)
+    return Wd @ hid, hid
+
+
+def _small_moe(seed, d=64, dff=96, E=4, k=2, rows=2):
+    return synthetic.moe_inputs(seed, d, dff, E, k, rows)
+
+
+def test_moe_single_expert_is_dense_swiglu():
+    m = _small_moe(61, E=1, k=1, rows=2)
+    idx, wts, h, y = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act=0)
+    assert (idx == 0).all() and (wts == 1.0).all()
+    for i in range(2):
+        ref, hid = _dense_swiglu(m.x[i].astype(np.float64), _deq(m.Wgq, m.Wgs), _deq(m.Wuq, m.Wus), _deq(m.Wdq, m.Wds))
+        assert np.max(np.abs(h[i, 0] - hid)) == 0.0
+        assert np.max(np.abs(y[i] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_moe_all_experts_is_softmax_mixture():
+    m = _small_moe(62, E=4, k=4, rows=3)
+    idx, wts, h, y = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 4, act=0)
+    d, dff = m.d, m.dff
+    for i in range(3):
+        l = m.Wr.astype(np.float64) @ m.x[i].astype(np.float64)
+        p = scipy.special.softmax(l)
+        ref = np.zeros(d)
+        for e in range(4):
+            ye, _ = _dense_swiglu(m.x[i].astype(np.float64),
+                                  _deq(m.Wgq[e * dff:(e + 1) * dff], m.Wgs[e * dff:(e + 1) * dff]),
+                                  _deq(m.Wuq[e * dff:(e + 1) * dff], m.Wus[e * dff:(e + 1) * dff]),
+                                  _deq(m.Wdq[e * d:(e + 1) * d], m.Wds[e * d:(e + 1) * d]))
+            ref += p[e] * ye
+        assert np.max(np.abs(y[i] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_moe_identical_experts_any_router_is_dense():
+    base = _small_moe(63, E=1, k=1, rows=2)
+    E, d, dff = 3, base.d, base.dff
+    Wr = (0.02 * synthetic.normal(np.random.default_rng(64), E, d)).astype(np.float32)
+    rep = lambda a: np.concatenate([a] * E, axis=0)
+    idx, wts, h, y = oracle.moe(base.x, Wr, rep(base.Wgq), rep(base.Wgs), rep(base.Wuq), rep(base.Wus),
+                                rep(base.Wdq), rep(base.Wds), E, act=0)
+    for i in range(2):
+        ref, _ = _dense_swiglu(base.x[i].astype(np.float64), _deq(base.Wgq, base.Wgs), _deq(base.Wuq, base.Wus),
+                               _deq(base.Wdq, base.Wds))
+        assert np.max(np.abs(y[i] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_moe_int8_gate_up_exact_when_x_is_q8_exact():
+    # x of integers with |x| reaching 127 in every block quantises exactly
+    # (d = 1, q = x), so the int8 mode's hidden row equals the f32 mode's.
+    m = _small_moe(65, E=4, k=2, rows=1)
+    rng = np.random.default_rng(66)
+    x = rng.integers(-126, 127, size=(1, m.d)).astype(np.float32)
+    x[0, ::32] = 127.0
+    _, _, hf, _ = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=0)
+    _, _, hi, _ = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=1)
+    assert np.max(np.abs(hi - hf) / (np.abs(hf) + 1e-30)) <= 2.0 ** -23
+
+
+def test_moe_int8_within_bound_of_f32_mode():
+    m = _small_moe(67, d=128, dff=128, E=4, k=2, rows=2)
+    _, _, _, yf = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=0)
+    _, _, _, yi = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=1)
+    assert np.max(np.abs(yi - yf)) <= 3e-2 * np.max(np.abs(yf))
+
+
+def test_moe_chunk_rows_are_independent():
+    m = _small_moe(68, E=6, k=2, rows=5)
+    for act in (0, 1):
+        idx, wts, h, y = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=act)
+        for i in range(5):
+            i1, w1, h1, y1 = oracle.moe(m.x[i:i + 1], m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=act)
+            assert np.array_equal(idx[i], i1[0]) and np.array_equal(y[i], y1[0]) and np.array_equal(h[i], h1[0])
+
+
+def test_moe_rejects_unknown_mode():
+    m = _small_moe(69, E=2, k=1, rows=1)
+    with pytest.raises(AssertionError):
+        oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act=2)
