@@ -1,0 +1,201 @@
+/*
+ * q8s.h -- C ABI of the Q8_0 GEMV / sparse mixture-of-experts library for
+ * MI355X (gfx950).  libq8s.so exports exactly the functions declared here.
+ *
+ * Sources, cited by page and item (the text of each page is the authority on
+ * what an operation computes):
+ *   - codegen_cuda::qwen_emit module page: struct Q8Ref (Q8_0 rows: int8 quants
+ *     row-major plus one f32 scale per 32 inputs, W[o][t] = q[o*in+t] *
+ *     s[o*nb + t/32]); struct MoeWeights (stacked experts, router [E,d],
+ *     gate/up [E*dff,d], down [E*d,dff], expert e's rows from e*dff or e*d);
+ *     fn emit_moe_forward (router GEMV, softmax top-K, renormalise, SwiGLU per
+ *     kept expert with an expert-indexed weight base, weighted combine);
+ *     enum Q8MatKind and fn moe_dp4a_kernels (router + top-K, then quantise,
+ *     gate-up-SwiGLU, down-combine).
+ *   - codegen_cuda/forward_shim.rs: module doc (sum + RMS norm as one row
+ *     kernel writing the sum; the Q8_0 activation quantised in its producer's
+ *     epilogue; every stage reads and writes whole buffers); fn kernel_refusal
+ *     (no bias on an RMSNorm or a mixture; renormalised softmax routing over
+ *     every expert); fn numerics (32-bit integer accumulators).
+ *   - codegen_cuda/lane_link.rs: fn prim, Moe arm (refuses more than 32 kept
+ *     experts or more than 8192 experts); Matmul arm (weight rows are the
+ *     outputs).
+ *   - codegen_cuda/lane/arena.rs: fn scratch (router logits, choices,
+ *     weights, an arrival counter left zero by the launch that uses it,
+ *     per-choice results of a chunk's mixture) and const ALIGN.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked "device" are HIP device addresses (e.g. torch.cuda
+ *     tensors' data_ptr()).  The caller allocates and owns every buffer --
+ *     inputs, outputs and scratch; the library allocates nothing and keeps
+ *     no device state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously; no call synchronises the host.
+ *   - Layouts are row-major and dense.  A Q8_0 matrix [n_out, n_in] is a
+ *     pair: quants int8 [n_out, n_in] and scales f32 [n_out, n_in/32].  A
+ *     Q8_0 activation row set [rows, n] is int8 [rows, n] + f32 [rows, n/32].
+ *   - Every reduced dimension (n_in, d, dff, n) is a positive multiple of 32.
+ *     Every pointer is 16-byte aligned.  Outputs never overlap inputs or each
+ *     other (whole buffers).  Sizes are 64-bit.
+ *   - Validation happens on the host, before any HIP call: a refused call
+ *     returns a negative Q8S_E* code, enqueues nothing and leaves a message
+ *     naming the violated rule in q8s_last_error() (thread-local).  A launch
+ *     failure returns Q8S_ELAUNCH with the HIP error string.
+ *   - `act` picks the activation numerics (enum Q8MatKind): Q8S_ACT_F32 reads
+ *     f32 activations; Q8S_ACT_INT8 reads one-word Q8_0 activations and forms
+ *     exact int32 dots per 32-value block.
+ *   - Expert choices (idx) are read on the device.  An index outside [0, E)
+ *     is never dereferenced: that choice contributes zero.
+ */
+#ifndef Q8S_H
+#define Q8S_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+/* Entry points keep default visibility; the library hides everything else. */
+#if defined(__GNUC__) || defined(__clang__)
+#define Q8S_API __attribute__((visibility("default")))
+#else
+#define Q8S_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q8S_OK 0
+#define Q8S_EINVAL (-1)       /* null pointer, bad shape, overlapping buffers */
+#define Q8S_EUNSUPPORTED (-2) /* outside the kernels' limits or an unknown mode */
+#define Q8S_EALIGN (-3)       /* a pointer not 16-byte aligned */
+#define Q8S_ESCRATCH (-4)     /* scratch missing or smaller than q8s_scratch_bytes */
+#define Q8S_ELAUNCH (-5)      /* the HIP launch failed */
+
+#define Q8S_ACT_F32 0  /* f32 activations (dequantise in kernel) */
+#define Q8S_ACT_INT8 1 /* one-word Q8_0 int8 activations */
+
+/* Ids of the calls that take scratch, for q8s_scratch_bytes. */
+#define Q8S_FN_ROUTE 1
+#define Q8S_FN_DOWN 2
+
+#define Q8S_MAX_K 32
+#define Q8S_MAX_E 8192
+
+/*
+ * q8_gemv -- Q8_0 matrix times activation rows (struct Q8Ref; fn prim,
+ * Matmul arm: weight rows are outputs).
+ *   y[r][o] = sum_t Wq[o][t] * Ws[o][t/32] * x[r][t]      (act = F32)
+ *   y[r][o] = sum_b Ws[o][b] * xs[r][b] * isum(r,o,b),     (act = INT8)
+ *             isum(r,o,b) = sum_{t in b} Wq[o][t]*xq[r][t] exact in int32
+ * Wq: device int8 [n_out, n_in]; Ws: device f32 [n_out, n_in/32].
+ * x: device f32 [m, n_in] (F32; NULL otherwise).  xq/xs: device int8
+ * [m, n_in] / f32 [m, n_in/32] (INT8; NULL otherwise).  y: device f32
+ * [m, n_out], written whole.  m >= 1.  Each weight row is read from HBM once
+ * per call for m <= 4 (register path) and for any m in INT8 mode (matrix-core
+ * path for m >= 16).  Limits: n_in <= 65536.
+ */
+Q8S_API int q8_gemv(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in,
+            const float *x, const int8_t *xq, const float *xs, int64_t m,
+            float *y, int act, void *stream);
+
+/*
+ * q8_quantize_rows -- the Q8_0 activation quantiser ("quantize" of the
+ * quantise/gate-up/down trio, fn moe_dp4a_kernels; llama.cpp's one int8 word,
+ * enum Q8MatKind), per 32-value block, all in float32:
+ *   amax = max|v|; d = amax/127; id = d ? 1/d : 0;
+ *   q = clamp(round-half-away-from-zero(v*id), -127, 127)
+ * x: device f32 [rows, n]; xq: device int8 [rows, n]; xs: device f32
+ * [rows, n/32].
+ */
+Q8S_API int q8_quantize_rows(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, void *stream);
+
+/*
+ * add_rmsnorm_q8 -- residual add + weighted RMSNorm as one row kernel that
+ * writes the sum (forward_shim.rs module doc, add_norm), quantising its
+ * output to Q8_0 in its epilogue:
+ *   sum = h + r                                       (float32 add, written)
+ *   y   = (sum / sqrt(mean(sum^2) + eps)) * w          (double inside the row,
+ *                                                      rounded to float32)
+ *   yq, ys = Q8_0(y) by the q8_quantize_rows rule
+ * h, r: device f32 [rows, d]; w: device f32 [d]; sum: device f32 [rows, d]
+ * (required); y: device f32 [rows, d] or NULL; yq/ys: device int8 [rows, d]
+ * and f32 [rows, d/32], both or neither.  At least one of y, yq is given.
+ * eps >= 0.  Limits: d <= 65536.
+ */
+Q8S_API int add_rmsnorm_q8(const float *h, const float *r, const float *w, int64_t rows, int64_t d,
+                   float eps, float *sum, float *y, int8_t *yq, float *ys, void *stream);
+
+/*
+ * moe_route_topk -- the mixture's router and top-K (fn emit_moe_forward:
+ * softmax, keep K, renormalise; fn kernel_refusal: no bias, a softmax over
+ * every expert):
+ *   l[r][e] = sum_t Wr[e][t] * x[r][t]   (double sums)
+ *   p = softmax_e(l[r]);  idx[r] = the K largest l, ties to the lower index,
+ *   in rank order;  wts[r][j] = p[idx[r][j]] / sum_{i<K} p[idx[r][i]]
+ * x: device f32 [rows, d] (the router reads f32 x in both numerics);
+ * Wr: device f32 [E, d]; idx: device int32 [rows, k]; wts: device f32
+ * [rows, k].  1 <= k <= min(32, E), E <= 8192.
+ * scratch: device, >= q8s_scratch_bytes(Q8S_FN_ROUTE, ...), 256-byte aligned,
+ * zero-filled once when allocated; every call leaves its counter region zero
+ * again (arena.rs fn scratch: an arrival count the last block resets).  Calls
+ * that share a scratch buffer must be ordered on one stream.
+ */
+Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k,
+                   int32_t *idx, float *wts, void *scratch, size_t scratch_bytes, void *stream);
+
+/*
+ * moe_gate_up -- each kept expert's gate and up projections with SiLU gating
+ * (fn emit_moe_forward; struct MoeWeights stacked rows, expert base taken from
+ * idx on the device):
+ *   for every row r, slot j (e = idx[r][j]), output o < dff:
+ *     g = Wg[e*dff + o] . x[r],  u = Wu[e*dff + o] . x[r]
+ *     h[r][j][o] = SiLU(g) * u,   SiLU(z) = z / (1 + exp(-z))
+ *   INT8: the dots read x's Q8_0 form, and h is also written quantised per
+ *   32-value block of each (r, j) row (hq/hs, arena.rs fn scratch).
+ * x: device f32 [rows, d] (F32) or NULL; xq/xs: device Q8_0 [rows, d] (INT8)
+ * or NULL.  Wgq/Wuq: device int8 [E*dff, d]; Wgs/Wus: device f32
+ * [E*dff, d/32].  idx: device int32 [rows, k].  h: device f32 [rows, k, dff]
+ * (required for F32; optional for INT8).  hq/hs: device int8 [rows, k, dff]
+ * and f32 [rows, k, dff/32] (INT8 only, required).  With rows > 1 the
+ * choices are grouped by expert on the device, so each chosen expert's rows
+ * are read once per call.
+ */
+Q8S_API int moe_gate_up(const float *x, const int8_t *xq, const float *xs,
+                const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                const int32_t *idx, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
+                float *h, int8_t *hq, float *hs, int act, void *stream);
+
+/*
+ * moe_down_combine -- each kept expert's down projection, weighted and
+ * summed in slot order (fn emit_moe_forward):
+ *   y[r][o] = sum_{j<K} wts[r][j] * (Wd[e*d + o] . h[r][j]),  e = idx[r][j]
+ * F32 reads h: device f32 [rows, k, dff]; INT8 reads hq/hs (device Q8_0
+ * [rows, k, dff]).  Wdq: device int8 [E*d, dff]; Wds: device f32
+ * [E*d, dff/32]; idx/wts: device [rows, k]; y: device f32 [rows, d].
+ * scratch: device, >= q8s_scratch_bytes(Q8S_FN_DOWN, ...) (zero bytes when
+ * rows == 1, where NULL is accepted): per-choice results of a chunk, combined
+ * per row in slot order.
+ */
+Q8S_API int moe_down_combine(const float *h, const int8_t *hq, const float *hs,
+                     const int8_t *Wdq, const float *Wds, const int32_t *idx, const float *wts,
+                     int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
+                     float *y, int act, void *scratch, size_t scratch_bytes, void *stream);
+
+/*
+ * q8s_scratch_bytes -- bytes of scratch the call `fn` (Q8S_FN_ROUTE or
+ * Q8S_FN_DOWN) needs for these sizes; 0 for a call that needs none, or for an
+ * unknown fn.
+ */
+Q8S_API size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
+
+/* The message of this thread's last refused or failed call ("" if none). */
+Q8S_API const char *q8s_last_error(void);
+
+/* The library's version string. */
+Q8S_API const char *q8s_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8S_H */

@@ -1,0 +1,235 @@
+"""Python binding of libq8s.so, the Q8_0 GEMV / sparse-MoE library for MI355X.
+
+The functions carry the C entry points' names (include/q8s.h) and only
+marshal arguments: they check that tensors are contiguous device tensors of
+the right dtype, read sizes off their shapes, pass ``data_ptr()`` and the
+current HIP stream, and raise ``Q8sError`` with the library's message when a
+call is refused.  Every step of the computation runs in the HIP kernels;
+there is no fallback.  PyTorch supplies device memory and streams only.
+
+Importing this package loads ``libq8s.so`` from this directory and fails
+loudly if it has not been built (``python -m q8_gemv_sparse_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ACT_F32", "ACT_INT8", "FN_ROUTE", "FN_DOWN", "Q8sError", "LIB_PATH",
+    "q8_gemv", "q8_quantize_rows", "add_rmsnorm_q8", "moe_route_topk",
+    "moe_gate_up", "moe_down_combine", "q8s_scratch_bytes", "q8s_last_error",
+    "q8s_version", "library",
+]
+
+ACT_F32 = 0
+ACT_INT8 = 1
+FN_ROUTE = 1
+FN_DOWN = 2
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8s.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libq8s.so is not built at %s; build it with `python -m q8_gemv_sparse_amd.build`" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "q8_gemv": [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p, ctypes.c_int, _p],
+    "q8_quantize_rows": [_p, _i64, _i64, _p, _p, _p],
+    "add_rmsnorm_q8": [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p],
+    "moe_route_topk": [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p],
+    "moe_gate_up": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, ctypes.c_int, _p],
+    "moe_down_combine": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, ctypes.c_int, _p, _sz, _p],
+    "q8s_scratch_bytes": [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int
+_lib.q8s_scratch_bytes.restype = _sz
+_lib.q8s_last_error.restype = ctypes.c_char_p
+_lib.q8s_last_error.argtypes = []
+_lib.q8s_version.restype = ctypes.c_char_p
+_lib.q8s_version.argtypes = []
+
+
+def library():
+    """The loaded ctypes library (for callers that marshal raw pointers)."""
+    return _lib
+
+
+class Q8sError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("q8s error %d: %s" % (code, msg))
+        self.code = code
+
+
+def q8s_last_error():
+    return _lib.q8s_last_error().decode()
+
+
+def q8s_version():
+    return _lib.q8s_version().decode()
+
+
+def q8s_scratch_bytes(fn, rows, d, dff, E, k, act=ACT_F32):
+    return int(_lib.q8s_scratch_bytes(fn, rows, d, dff, E, k, act))
+
+
+def _check(rc):
+    if rc != 0:
+        raise Q8sError(rc, q8s_last_error())
+
+
+def _dev(t, dtype, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def q8_gemv(Wq, Ws, x=None, xq=None, xs=None, y=None, act=ACT_F32, stream=None):
+    """y[m, n_out] = Q8_0(Wq, Ws) @ activations; f32 ``x`` or Q8_0 ``xq``/``xs``."""
+    _dev(Wq, torch.int8, "Wq"); _dev(Ws, torch.float32, "Ws")
+    n_out, n_in = Wq.shape
+    if act == ACT_F32:
+        _dev(x, torch.float32, "x")
+        m = x.numel() // n_in
+    else:
+        _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
+        m = xq.numel() // n_in
+    if y is None:
+        y = torch.empty((m, n_out), dtype=torch.float32, device=Wq.device)
+    _dev(y, torch.float32, "y")
+    _check(_lib.q8_gemv(_ptr(Wq), _ptr(Ws), n_out, n_in, _ptr(x), _ptr(xq), _ptr(xs), m, _ptr(y), act,
+                        _stream(stream)))
+    return y
+
+
+def q8_quantize_rows(x, xq=None, xs=None, stream=None):
+    """Q8_0 form of f32 rows ``x [rows, n]``: (xq int8 [rows, n], xs f32 [rows, n/32])."""
+    _dev(x, torch.float32, "x")
+    n = x.shape[-1]
+    rows = x.numel() // n
+    if xq is None:
+        xq = torch.empty((rows, n), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((rows, n // 32), dtype=torch.float32, device=x.device)
+    _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
+    _check(_lib.q8_quantize_rows(_ptr(x), rows, n, _ptr(xq), _ptr(xs), _stream(stream)))
+    return xq, xs
+
+
+def add_rmsnorm_q8(h, r, w, eps, sum=None, y=None, yq=None, ys=None, want_f32=True, want_q8=True, stream=None):
+    """sum = h + r; y = RMSNorm(sum) * w; Q8_0(y).  Returns (sum, y or None, yq or None, ys or None)."""
+    _dev(h, torch.float32, "h"); _dev(r, torch.float32, "r"); _dev(w, torch.float32, "w")
+    d = h.shape[-1]
+    rows = h.numel() // d
+    dev = h.device
+    if sum is None:
+        sum = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_f32 and y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_q8 and yq is None:
+        yq = torch.empty((rows, d), dtype=torch.int8, device=dev)
+        ys = torch.empty((rows, d // 32), dtype=torch.float32, device=dev)
+    for t, dt, n in ((sum, torch.float32, "sum"), (y, torch.float32, "y"), (yq, torch.int8, "yq"),
+                     (ys, torch.float32, "ys")):
+        _dev(t, dt, n)
+    _check(_lib.add_rmsnorm_q8(_ptr(h), _ptr(r), _ptr(w), rows, d, float(eps), _ptr(sum), _ptr(y), _ptr(yq),
+                               _ptr(ys), _stream(stream)))
+    return sum, y, yq, ys
+
+
+def moe_route_topk(x, Wr, k, idx=None, wts=None, scratch=None, stream=None):
+    """Router + top-K: (idx int32 [rows, k], wts f32 [rows, k]).  ``scratch`` is a
+    zero-filled uint8 device tensor of at least q8s_scratch_bytes(FN_ROUTE, ...)
+    bytes, kept across calls (its counters are left zero)."""
+    _dev(x, torch.float32, "x"); _dev(Wr, torch.float32, "Wr")
+    E, d = Wr.shape
+    rows = x.numel() // d
+    dev = x.device
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if wts is None:
+        wts = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    if scratch is None:
+        scratch = torch.zeros(q8s_scratch_bytes(FN_ROUTE, rows, d, 32, E, k), dtype=torch.uint8, device=dev)
+    _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts"); _dev(scratch, torch.uint8, "scratch")
+    _check(_lib.moe_route_topk(_ptr(x), _ptr(Wr), rows, d, E, k, _ptr(idx), _ptr(wts), _ptr(scratch),
+                               scratch.numel(), _stream(stream)))
+    return idx, wts
+
+
+def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq=None, hs=None, act=ACT_F32,
+                want_h=True, stream=None):
+    """h[rows, k, dff] = SiLU(Wg[e] x) * (Wu[e] x) for each kept expert; INT8 also returns hq/hs."""
+    for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq")):
+        _dev(t, torch.int8, n)
+    for t, n in ((Wgs, "Wgs"), (Wus, "Wus")):
+        _dev(t, torch.float32, n)
+    _dev(idx, torch.int32, "idx")
+    rows, k = idx.shape
+    d = Wgq.shape[1]
+    dff = Wgq.shape[0] // E
+    dev = Wgq.device
+    if act == ACT_F32:
+        _dev(x, torch.float32, "x")
+    else:
+        _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
+        if hq is None:
+            hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
+            hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
+    if h is None and (want_h or act == ACT_F32):
+        h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)
+    _dev(h, torch.float32, "h"); _dev(hq, torch.int8, "hq"); _dev(hs, torch.float32, "hs")
+    _check(_lib.moe_gate_up(_ptr(x), _ptr(xq), _ptr(xs), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq), _ptr(Wus), _ptr(idx),
+                            rows, d, dff, E, k, _ptr(h), _ptr(hq), _ptr(hs), act, _stream(stream)))
+    return h, hq, hs
+
+
+def moe_down_combine(Wdq, Wds, idx, wts, E, h=None, hq=None, hs=None, y=None, act=ACT_F32, scratch=None,
+                     stream=None):
+    """y[rows, d] = sum_j wts[:, j] * (Wd[idx[:, j]] @ h[:, j])."""
+    _dev(Wdq, torch.int8, "Wdq"); _dev(Wds, torch.float32, "Wds")
+    _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
+    rows, k = idx.shape
+    dff = Wdq.shape[1]
+    d = Wdq.shape[0] // E
+    dev = Wdq.device
+    if act == ACT_F32:
+        _dev(h, torch.float32, "h")
+    else:
+        _dev(hq, torch.int8, "hq"); _dev(hs, torch.float32, "hs")
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    _dev(y, torch.float32, "y")
+    need = q8s_scratch_bytes(FN_DOWN, rows, d, dff, E, k, act)
+    if need and scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(scratch, torch.uint8, "scratch")
+    _check(_lib.moe_down_combine(_ptr(h), _ptr(hq), _ptr(hs), _ptr(Wdq), _ptr(Wds), _ptr(idx), _ptr(wts), rows, d,
+                                 dff, E, k, _ptr(y), act, _ptr(scratch), 0 if scratch is None else scratch.numel(),
+                                 _stream(stream)))
+    return y

@@ -1,0 +1,350 @@
+// q8s_abi.hip -- the C ABI declared in include/q8s.h.
+//
+// Each entry point checks its arguments on the host before any HIP call --
+// null pointers, shapes, alignment, limits, overlapping buffers, scratch size
+// -- and refuses by naming the rule it breaks, in the style of the refusals
+// of codegen_cuda/forward_shim.rs (fn kernel_refusal) and lane_link.rs (fn
+// prim).  Accepted calls enqueue their kernels on the caller's stream and
+// return without synchronising.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/q8s.h"
+#include "q8s_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+// Clears a stale error left by an earlier, unrelated HIP call, so a launch
+// failure is reported as this call's own.
+void clear_stale() { (void)hipGetLastError(); }
+
+int launched(hipError_t e, const char *fn)
+{
+    if (e != hipSuccess)
+        return fail(Q8S_ELAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    g_err.clear();
+    return Q8S_OK;
+}
+
+struct Span {
+    const void *p;
+    size_t bytes;
+    const char *name;
+};
+
+// A buffer list check: present, 16-byte aligned.  Returns 0 or an error code.
+int check_ptrs(const char *fn, const std::vector<Span> &v)
+{
+    for (const Span &s : v) {
+        if (!s.p)
+            return fail(Q8S_EINVAL, "%s: `%s` is null", fn, s.name);
+        if (reinterpret_cast<uintptr_t>(s.p) % 16 != 0)
+            return fail(Q8S_EALIGN, "%s: `%s` is not 16-byte aligned", fn, s.name);
+    }
+    return 0;
+}
+
+bool overlap(const Span &a, const Span &b)
+{
+    const char *pa = static_cast<const char *>(a.p), *pb = static_cast<const char *>(b.p);
+    return pa < pb + b.bytes && pb < pa + a.bytes;
+}
+
+// Outputs may overlap neither an input nor another output: every stage reads
+// and writes whole buffers (forward_shim.rs module doc).
+int check_disjoint(const char *fn, const std::vector<Span> &ins, const std::vector<Span> &outs)
+{
+    for (size_t i = 0; i < outs.size(); i++) {
+        for (const Span &in : ins)
+            if (overlap(outs[i], in))
+                return fail(Q8S_EINVAL, "%s: output `%s` overlaps input `%s` -- a stage writes whole buffers of its own",
+                            fn, outs[i].name, in.name);
+        for (size_t j = i + 1; j < outs.size(); j++)
+            if (overlap(outs[i], outs[j]))
+                return fail(Q8S_EINVAL, "%s: outputs `%s` and `%s` overlap", fn, outs[i].name, outs[j].name);
+    }
+    return 0;
+}
+
+int check_dim32(const char *fn, const char *name, int64_t n)
+{
+    if (n <= 0 || n % 32 != 0)
+        return fail(Q8S_EINVAL, "%s: `%s` = %lld is not a positive multiple of 32 (whole Q8_0 blocks)", fn, name,
+                    (long long)n);
+    if (n > q8s::MAX_NIN)
+        return fail(Q8S_EUNSUPPORTED, "%s: `%s` = %lld exceeds the kernels' longest row of %lld values", fn, name,
+                    (long long)n, (long long)q8s::MAX_NIN);
+    return 0;
+}
+
+int check_count(const char *fn, const char *name, int64_t n, int64_t hi)
+{
+    if (n <= 0)
+        return fail(Q8S_EINVAL, "%s: `%s` = %lld must be at least 1", fn, name, (long long)n);
+    if (n > hi)
+        return fail(Q8S_EUNSUPPORTED, "%s: `%s` = %lld exceeds %lld", fn, name, (long long)n, (long long)hi);
+    return 0;
+}
+
+int check_act(const char *fn, int act)
+{
+    if (act == Q8S_ACT_F32 || act == Q8S_ACT_INT8)
+        return 0;
+    if (act == 2)
+        return fail(Q8S_EUNSUPPORTED, "%s: act = 2 (two-word int8 activations) is not implemented", fn);
+    return fail(Q8S_EUNSUPPORTED, "%s: unknown activation mode act = %d", fn, act);
+}
+
+int check_moe_shape(const char *fn, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k)
+{
+    int rc;
+    if ((rc = check_count(fn, "rows", rows, 65535)) || (rc = check_dim32(fn, "d", d)) ||
+        (rc = check_dim32(fn, "dff", dff)))
+        return rc;
+    if (E <= 0)
+        return fail(Q8S_EINVAL, "%s: `E` = %lld must be at least 1", fn, (long long)E);
+    if (k <= 0 || k > E)
+        return fail(Q8S_EINVAL, "%s: k = %lld kept experts of E = %lld: 1 <= k <= E", fn, (long long)k, (long long)E);
+    if (k > Q8S_MAX_K || E > Q8S_MAX_E)
+        return fail(Q8S_EUNSUPPORTED, "%s: more than %d experts kept, or more than %d experts (k = %lld, E = %lld)", fn,
+                    Q8S_MAX_K, Q8S_MAX_E, (long long)k, (long long)E);
+    if (E * dff > INT32_MAX || E * d > INT32_MAX)
+        return fail(Q8S_EUNSUPPORTED, "%s: E*dff or E*d past 2^31 rows", fn);
+    return 0;
+}
+
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+} // namespace
+
+extern "C" {
+
+const char *q8s_last_error(void) { return g_err.c_str(); }
+
+const char *q8s_version(void) { return "q8s 0.1 gfx950"; }
+
+size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
+{
+    (void)dff;
+    (void)act;
+    if (rows <= 0 || E <= 0 || k <= 0 || d <= 0)
+        return 0;
+    switch (fn) {
+    case Q8S_FN_ROUTE:
+        return q8s::route_scratch_bytes(rows, E);
+    case Q8S_FN_DOWN:
+        return q8s::down_scratch_bytes(rows, d, k);
+    default:
+        return 0;
+    }
+}
+
+int q8_gemv(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in, const float *x, const int8_t *xq,
+            const float *xs, int64_t m, float *y, int act, void *stream)
+{
+    const char *fn = "q8_gemv";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_dim32(fn, "n_in", n_in)) ||
+        (rc = check_count(fn, "n_out", n_out, INT32_MAX / 2)) || (rc = check_count(fn, "m", m, 65535)))
+        return rc;
+    const size_t nb = (size_t)(n_in / 32);
+    std::vector<Span> ins = {{Wq, (size_t)(n_out * n_in), "Wq"}, {Ws, (size_t)n_out * nb * 4, "Ws"}};
+    if (act == Q8S_ACT_F32) {
+        ins.push_back({x, (size_t)(m * n_in) * 4, "x"});
+    } else {
+        ins.push_back({xq, (size_t)(m * n_in), "xq"});
+        ins.push_back({xs, (size_t)m * nb * 4, "xs"});
+    }
+    std::vector<Span> outs = {{y, (size_t)(m * n_out) * 4, "y"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::GemvArgs a{Wq, Ws, n_out, n_in, act == 0 ? x : nullptr, act == 1 ? xq : nullptr, act == 1 ? xs : nullptr,
+                    m, y, act};
+    clear_stale();
+    return launched(q8s::gemv_launch(a, as_stream(stream)), fn);
+}
+
+int q8_quantize_rows(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, void *stream)
+{
+    const char *fn = "q8_quantize_rows";
+    int rc;
+    if ((rc = check_count(fn, "rows", rows, 65535)) || (rc = check_dim32(fn, "n", n)))
+        return rc;
+    std::vector<Span> ins = {{x, (size_t)(rows * n) * 4, "x"}};
+    std::vector<Span> outs = {{xq, (size_t)(rows * n), "xq"}, {xs, (size_t)(rows * n / 32) * 4, "xs"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::quantize_launch(x, rows, n, xq, xs, as_stream(stream)), fn);
+}
+
+int add_rmsnorm_q8(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps, float *sum,
+                   float *y, int8_t *yq, float *ys, void *stream)
+{
+    const char *fn = "add_rmsnorm_q8";
+    int rc;
+    if ((rc = check_count(fn, "rows", rows, INT32_MAX)) || (rc = check_dim32(fn, "d", d)))
+        return rc;
+    if (!(eps >= 0.0f) || eps != eps)
+        return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    if ((yq == nullptr) != (ys == nullptr))
+        return fail(Q8S_EINVAL, "%s: `yq` and `ys` are given together or not at all", fn);
+    if (!y && !yq)
+        return fail(Q8S_EINVAL, "%s: neither `y` nor `yq` is given -- the norm would write nothing but the sum", fn);
+    const size_t n = (size_t)(rows * d);
+    std::vector<Span> ins = {{h, n * 4, "h"}, {r, n * 4, "r"}, {w, (size_t)d * 4, "w"}};
+    std::vector<Span> outs = {{sum, n * 4, "sum"}};
+    if (y)
+        outs.push_back({y, n * 4, "y"});
+    if (yq) {
+        outs.push_back({yq, n, "yq"});
+        outs.push_back({ys, n / 32 * 4, "ys"});
+    }
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::add_rmsnorm_launch(h, r, w, rows, d, eps, sum, y, yq, ys, as_stream(stream)), fn);
+}
+
+int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
+                   float *wts, void *scratch, size_t scratch_bytes, void *stream)
+{
+    const char *fn = "moe_route_topk";
+    int rc;
+    if ((rc = check_moe_shape(fn, rows, d, 32, E, k)))
+        return rc;
+    std::vector<Span> ins = {{x, (size_t)(rows * d) * 4, "x"}, {Wr, (size_t)(E * d) * 4, "Wr"}};
+    std::vector<Span> outs = {{idx, (size_t)(rows * k) * 4, "idx"}, {wts, (size_t)(rows * k) * 4, "wts"}};
+    const size_t need = q8s::route_scratch_bytes(rows, E);
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
+        return rc;
+    if (!scratch || scratch_bytes < need)
+        return fail(Q8S_ESCRATCH, "%s: scratch of %zu bytes given, %zu needed (logits and arrival counters)", fn,
+                    scratch ? scratch_bytes : (size_t)0, need);
+    if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0)
+        return fail(Q8S_EALIGN, "%s: `scratch` is not 256-byte aligned", fn);
+    outs.push_back({scratch, need, "scratch"});
+    if ((rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::route_launch(x, Wr, rows, d, E, k, idx, wts, scratch, as_stream(stream)), fn);
+}
+
+int moe_gate_up(const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq, const float *Wgs,
+                const int8_t *Wuq, const float *Wus, const int32_t *idx, int64_t rows, int64_t d, int64_t dff,
+                int64_t E, int64_t k, float *h, int8_t *hq, float *hs, int act, void *stream)
+{
+    const char *fn = "moe_gate_up";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
+    const size_t nh = (size_t)(rows * k * dff);
+    std::vector<Span> ins = {{Wgq, wq, "Wgq"}, {Wgs, wsb, "Wgs"}, {Wuq, wq, "Wuq"}, {Wus, wsb, "Wus"},
+                             {idx, (size_t)(rows * k) * 4, "idx"}};
+    std::vector<Span> outs;
+    if (act == Q8S_ACT_F32) {
+        ins.push_back({x, (size_t)(rows * d) * 4, "x"});
+        outs.push_back({h, nh * 4, "h"});
+    } else {
+        ins.push_back({xq, (size_t)(rows * d), "xq"});
+        ins.push_back({xs, (size_t)(rows * d / 32) * 4, "xs"});
+        if (h)
+            outs.push_back({h, nh * 4, "h"});
+        outs.push_back({hq, nh, "hq"});
+        outs.push_back({hs, nh / 32 * 4, "hs"});
+    }
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::MoeArgs a{};
+    a.x = act == 0 ? x : nullptr;
+    a.xq = act == 1 ? xq : nullptr;
+    a.xs = act == 1 ? xs : nullptr;
+    a.Wgq = Wgq;
+    a.Wgs = Wgs;
+    a.Wuq = Wuq;
+    a.Wus = Wus;
+    a.idx = idx;
+    a.rows = rows;
+    a.d = d;
+    a.dff = dff;
+    a.E = E;
+    a.k = k;
+    a.h = h;
+    a.hq = act == 1 ? hq : nullptr;
+    a.hs = act == 1 ? hs : nullptr;
+    a.act = act;
+    clear_stale();
+    return launched(q8s::gate_up_launch(a, as_stream(stream)), fn);
+}
+
+int moe_down_combine(const float *h, const int8_t *hq, const float *hs, const int8_t *Wdq, const float *Wds,
+                     const int32_t *idx, const float *wts, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
+                     float *y, int act, void *scratch, size_t scratch_bytes, void *stream)
+{
+    const char *fn = "moe_down_combine";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    const size_t nh = (size_t)(rows * k * dff);
+    std::vector<Span> ins = {{Wdq, (size_t)(E * d) * (size_t)dff, "Wdq"},
+                             {Wds, (size_t)(E * d) * (size_t)(dff / 32) * 4, "Wds"},
+                             {idx, (size_t)(rows * k) * 4, "idx"},
+                             {wts, (size_t)(rows * k) * 4, "wts"}};
+    if (act == Q8S_ACT_F32) {
+        ins.push_back({h, nh * 4, "h"});
+    } else {
+        ins.push_back({hq, nh, "hq"});
+        ins.push_back({hs, nh / 32 * 4, "hs"});
+    }
+    std::vector<Span> outs = {{y, (size_t)(rows * d) * 4, "y"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
+        return rc;
+    const size_t need = q8s::down_scratch_bytes(rows, d, k);
+    if (need) {
+        if (!scratch || scratch_bytes < need)
+            return fail(Q8S_ESCRATCH, "%s: scratch of %zu bytes given, %zu needed (per-choice results)", fn,
+                        scratch ? scratch_bytes : (size_t)0, need);
+        if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0)
+            return fail(Q8S_EALIGN, "%s: `scratch` is not 256-byte aligned", fn);
+        outs.push_back({scratch, need, "scratch"});
+    }
+    if ((rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::MoeArgs a{};
+    a.h = act == 0 ? const_cast<float *>(h) : nullptr;
+    a.hq = act == 1 ? const_cast<int8_t *>(hq) : nullptr;
+    a.hs = act == 1 ? const_cast<float *>(hs) : nullptr;
+    a.Wdq = Wdq;
+    a.Wds = Wds;
+    a.idx = idx;
+    a.wts = wts;
+    a.rows = rows;
+    a.d = d;
+    a.dff = dff;
+    a.E = E;
+    a.k = k;
+    a.y = y;
+    a.act = act;
+    a.scratch = need ? scratch : nullptr;
+    clear_stale();
+    return launched(q8s::down_launch(a, as_stream(stream)), fn);
+}
+
+} // extern "C"

@@ -1,0 +1,248 @@
+// q8s_device.h -- device-side building blocks of the Q8_0 GEMV / MoE kernels
+// for gfx950 (CDNA4, wave64).
+//
+// The weight stream is the whole cost of a batch-1 Q8_0 projection: its
+// bytes, not its arithmetic, bound it (codegen_cuda::qwen_emit module page,
+// enum Q8MatKind).  The pieces here are shaped for that:
+//   * a row of quants is read as 16-byte chunks, chunk c of a row by lane
+//     (c mod LPR) of an LPR-lane group, so each load instruction of a wave
+//     covers LPR*16 contiguous bytes of every row it touches;
+//   * the activation slice a lane multiplies against stays in registers for
+//     every row the wave streams, so activations are read once per wave;
+//   * partial sums are reduced across the lane group with DPP row operations,
+//     no LDS round trip.
+// A Q8_0 block (32 values, struct Q8Ref) is two chunks, held by lanes 2i and
+// 2i+1 of a group; in int8 mode their exact int32 half-block sums are added
+// across that lane pair before the block's two scales are applied.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8s {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int QB = 32;  // values per Q8_0 block
+constexpr int WAVE = 64;
+
+#define Q8S_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------------------
+// loads
+
+// A streamed (non-temporal) 16-byte load: weight rows are read once.
+Q8S_DEV i32x4 ld_stream16(const int8_t *p) { return __builtin_nontemporal_load(reinterpret_cast<const i32x4 *>(p)); }
+Q8S_DEV float ld_stream_f32(const float *p) { return __builtin_nontemporal_load(p); }
+Q8S_DEV i32x4 ld16(const void *p) { return *reinterpret_cast<const i32x4 *>(p); }
+Q8S_DEV f32x4 ldf4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions
+
+// DPP controls (gfx9 encoding).
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- lane 7-i within each 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <- lane 15-i within each 16
+
+template <int CTRL>
+Q8S_DEV float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+Q8S_DEV int dpp_i(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over each 16-lane row; every lane of the row receives the row's sum.
+Q8S_DEV float sum16(float v)
+{
+    v += dpp_f<DPP_XOR1>(v);
+    v += dpp_f<DPP_XOR2>(v);
+    v += dpp_f<DPP_HALF_MIRROR>(v);
+    v += dpp_f<DPP_MIRROR>(v);
+    return v;
+}
+
+// Sum over each group of LPR consecutive lanes (LPR = 16, 32 or 64); every
+// lane of a group receives its group's sum.
+template <int LPR>
+Q8S_DEV float group_sum(float v)
+{
+    static_assert(LPR == 16 || LPR == 32 || LPR == 64, "lane group of 16, 32 or 64");
+    v = sum16(v);
+    if constexpr (LPR >= 32)
+        v += __shfl_xor(v, 16);
+    if constexpr (LPR >= 64)
+        v += __shfl_xor(v, 32);
+    return v;
+}
+
+Q8S_DEV float wave_max(float v)
+{
+    for (int o = 32; o >= 1; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+Q8S_DEV double wave_sum_f64(double v)
+{
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// the Q8_0 activation quantiser, float32 throughout:
+//   d = amax/127; id = d ? 1/d : 0; q = clamp(round-half-away(v*id), +-127)
+// The divisions are IEEE float32 divisions (the library is built with
+// correctly rounded float32 division); roundf rounds halfway cases away
+// from zero.
+
+Q8S_DEV float q8_scale(float amax) { return amax / 127.0f; }
+Q8S_DEV float q8_inv(float d) { return d != 0.0f ? 1.0f / d : 0.0f; }
+Q8S_DEV int q8_code(float v, float id)
+{
+    float p = v * id;
+    float r = roundf(p);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
+// ---------------------------------------------------------------------------
+// a lane's share of one row: C chunks of 16 bytes plus their block scales
+
+template <int C>
+struct RowSlice {
+    i32x4 q[C];
+    float s[C];
+};
+
+// The activation slice a lane multiplies against: float32 values, or Q8_0
+// words + block scales.
+template <int ACT, int C>
+struct XSlice;
+template <int C>
+struct XSlice<0, C> {
+    f32x4 v[C][4];
+};
+template <int C>
+struct XSlice<1, C> {
+    i32x4 q[C];
+    float s[C];
+};
+
+// Chunk index (within the row) of a lane's c-th chunk: ch0 + c*LPR + lig.
+// Chunks at or past `nch` (the slice's end) are masked to zero.
+template <int LPR, int C>
+Q8S_DEV void load_row(RowSlice<C> &w, const int8_t *__restrict__ rowq, const float *__restrict__ rows, int ch0, int nch,
+                      int lig)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        int ch = c * LPR + lig;
+        if (ch < nch) {
+            w.q[c] = ld_stream16(rowq + (int64_t)(ch0 + ch) * 16);
+            w.s[c] = ld_stream_f32(rows + ((ch0 + ch) >> 1));
+        } else {
+            w.q[c] = i32x4{0, 0, 0, 0};
+            w.s[c] = 0.0f;
+        }
+    }
+}
+
+template <int LPR, int C>
+Q8S_DEV void load_x(XSlice<0, C> &x, const float *__restrict__ xr, const int8_t *, const float *, int ch0, int nch, int lig)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        int ch = c * LPR + lig;
+        if (ch < nch) {
+            const float *p = xr + (int64_t)(ch0 + ch) * 16;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                x.v[c][i] = ldf4(p + 4 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                x.v[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
+template <int LPR, int C>
+Q8S_DEV void load_x(XSlice<1, C> &x, const float *, const int8_t *__restrict__ xq, const float *__restrict__ xs, int ch0,
+                    int nch, int lig)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        int ch = c * LPR + lig;
+        if (ch < nch) {
+            x.q[c] = ld16(xq + (int64_t)(ch0 + ch) * 16);
+            x.s[c] = xs[(ch0 + ch) >> 1];
+        } else {
+            x.q[c] = i32x4{0, 0, 0, 0};
+            x.s[c] = 0.0f;
+        }
+    }
+}
+
+// sum_i q_i * x_i over one 16-byte chunk, float32 (each int8 converted
+// exactly; the multiply-adds accumulate in float32).
+Q8S_DEV float chunk_dot_f32(i32x4 q, const f32x4 (&x)[4])
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        int dw = q[i];
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+            acc = __builtin_fmaf((float)(signed char)(dw >> (8 * b)), x[i][b], acc);
+    }
+    return acc;
+}
+
+// Exact int32 dot of two 16-byte int8 chunks (v_dot4_i32_i8).
+Q8S_DEV int chunk_dot_i8(i32x4 a, i32x4 b)
+{
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        s = __builtin_amdgcn_sdot4(a[i], b[i], s, false);
+    return s;
+}
+
+// The lane's partial of one row's dot with the activation slice.
+//   f32 : sum_c s_c * sum_i q_i x_i
+//   int8: sum over the lane's blocks of (ws*xs) * isum_block, where the
+//         block's exact isum joins the half-block sums of lanes 2i, 2i+1; the
+//         odd lane of the pair contributes nothing.
+template <int C>
+Q8S_DEV float row_dot(const RowSlice<C> &w, const XSlice<0, C> &x, int)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; c++)
+        acc = __builtin_fmaf(chunk_dot_f32(w.q[c], x.v[c]), w.s[c], acc);
+    return acc;
+}
+
+template <int C>
+Q8S_DEV float row_dot(const RowSlice<C> &w, const XSlice<1, C> &x, int lig)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        int half = chunk_dot_i8(w.q[c], x.q[c]);
+        int blk = half + dpp_i<DPP_XOR1>(half);
+        float f = (float)blk * (w.s[c] * x.s[c]);
+        acc += (lig & 1) ? 0.0f : f;
+    }
+    return acc;
+}
+
+} // namespace q8s

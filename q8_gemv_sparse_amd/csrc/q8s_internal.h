@@ -1,0 +1,94 @@
+// q8s_internal.h -- launch-side declarations shared by the library's
+// translation units (host code; the C ABI lives in q8s_abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace q8s {
+
+// Most experts kept per row, and most experts (lane_link.rs fn prim, Moe arm).
+constexpr int Q8S_MAX_K_DEV = 32;
+constexpr int Q8S_MAX_E_DEV = 8192;
+
+// Rows from which int8-activation projections go to the MFMA GEMM (below it
+// the register GEMV serves up to four rows a pass).
+constexpr int64_t GEMM_MIN_ROWS = 5;
+
+// How a row of n_in values is cut for the streaming kernels: lane groups of
+// `lpr` lanes holding `c` 16-byte chunks each; `ks` slices (waves) when one
+// wave's share (lpr*c chunks) does not cover the row.
+struct SliceShape {
+    int lpr, c, ks;
+};
+
+inline SliceShape slice_shape(int64_t n_in)
+{
+    const int64_t nch = n_in / 16;
+    if (nch <= 16)
+        return {16, 1, 1};
+    if (nch <= 48)
+        return {16, 3, 1};
+    if (nch <= 64)
+        return {64, 1, 1};
+    if (nch <= 128)
+        return {64, 2, 1};
+    if (nch <= 256)
+        return {64, 4, 1};
+    return {64, 4, (int)((nch + 255) / 256)};
+}
+
+// Longest reduced dimension the streaming kernels take (16 slices of 4096).
+constexpr int64_t MAX_NIN = 65536;
+
+struct GemvArgs {
+    const int8_t *Wq;
+    const float *Ws;
+    int64_t n_out, n_in;
+    const float *x;
+    const int8_t *xq;
+    const float *xs;
+    int64_t m;
+    float *y;
+    int act;
+};
+hipError_t gemv_launch(const GemvArgs &a, hipStream_t st);
+
+hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st);
+hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
+                              float *sum, float *y, int8_t *yq, float *ys, hipStream_t st);
+
+// router scratch: f64 logits [rows, E], then int arrival counters [row tiles]
+size_t route_scratch_bytes(int64_t rows, int64_t E);
+hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
+                        float *wts, void *scratch, hipStream_t st);
+
+struct MoeArgs {
+    const float *x;
+    const int8_t *xq;
+    const float *xs;
+    const int8_t *Wgq;
+    const float *Wgs;
+    const int8_t *Wuq;
+    const float *Wus;
+    const int8_t *Wdq;
+    const float *Wds;
+    const int32_t *idx;
+    const float *wts;
+    int64_t rows, d, dff, E, k;
+    float *h;
+    int8_t *hq;
+    float *hs;
+    float *y;
+    int act;
+    void *scratch;
+};
+hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st);
+size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t k);
+hipError_t down_launch(const MoeArgs &a, hipStream_t st);
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+} // namespace q8s

@@ -1,0 +1,266 @@
+// q8s_moe.hip -- the sparse MoE FFN's gate-up and down-combine kernels.
+//
+// The block is fn emit_moe_forward's (codegen_cuda::qwen_emit module page):
+// every kept expert's SwiGLU with an expert-indexed weight base, then the
+// weighted combine.  The weights are struct MoeWeights' stacked Q8_0 rows:
+// gate/up [E*dff, d] (expert e from row e*dff), down [E*d, dff] (from e*d).
+// The expert index is read on the device, so the choices never travel to the
+// host; an index outside [0, E) reads nothing and contributes zero.
+//
+// gate-up (one workgroup per 32 hidden outputs of one (row, slot)): each wave
+//   streams gate and up rows side by side against the activation slice in its
+//   registers; the 32 SiLU(g)*u values meet in LDS, where int8 mode also
+//   quantises them as one Q8_0 block (arena.rs fn scratch: hq/hs).
+// down-combine (one workgroup per 8 outputs of one row): waves take
+//   (slot, k-slice) pairs, so all K experts' rows of those outputs stream at
+//   once; the partials meet in LDS and are weighted and summed in slot order.
+#include "q8s_device.h"
+#include "q8s_internal.h"
+
+namespace q8s {
+
+Q8S_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+
+constexpr int GU_THREADS = 512;
+constexpr int GU_TILE = 32;
+constexpr int DN_TILE = 8;
+constexpr int MAX_KS = 16;
+constexpr int DN_MAX_WAVES = 8;
+
+// Outputs per lane group per step: enough 16-byte loads in flight per lane
+// (8-16) without spilling.  f32 mode holds its converted weights and 16-float
+// activation chunks, so it takes fewer rows at a time than int8 mode.
+template <int ACT, int LPR, int C>
+constexpr int gu_unroll()
+{
+    if (ACT == 0)
+        return C == 1 ? (LPR == 16 ? 2 : 4) : (C == 2 ? 2 : 1);
+    return C == 1 ? (LPR == 16 ? 2 : 4) : (C == 2 ? 4 : (C == 3 ? 1 : 2));
+}
+
+template <int ACT, int LPR, int C>
+__global__ void __launch_bounds__(GU_THREADS) k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq,
+                                                        const float *__restrict__ xs, const int8_t *__restrict__ Wgq,
+                                                        const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
+                                                        const float *__restrict__ Wus, const int32_t *__restrict__ idx,
+                                                        int d, int dff, int E, int k, int ks, float *__restrict__ h,
+                                                        int8_t *__restrict__ hq, float *__restrict__ hs)
+{
+    constexpr int G = WAVE / LPR;
+    constexpr int U = gu_unroll<ACT, LPR, C>();
+    constexpr int OPS = G * U;
+    constexpr int STEPS = GU_TILE / OPS;
+    static_assert(GU_TILE % OPS == 0, "a step covers a divisor of the tile");
+    __shared__ float gp[MAX_KS][GU_TILE];
+    __shared__ float up[MAX_KS][GU_TILE];
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
+    const int nwaves = blockDim.x >> 6;
+    const int o0 = blockIdx.x * GU_TILE;
+    const int j = blockIdx.y;
+    const int64_t row = blockIdx.z;
+    const int nch = d >> 4, nb = d >> 5;
+    const int e = idx[row * k + j];
+    const bool valid = (e >= 0 && e < E);
+    const int64_t rbase = (int64_t)(valid ? e : 0) * dff + o0;
+
+    for (int item = wid; item < ks * STEPS; item += nwaves) {
+        const int s = item / STEPS, st = item % STEPS;
+        const int ch0 = s * LPR * C;
+        const int sl = min(LPR * C, nch - ch0);
+        XSlice<ACT, C> xv;
+        load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
+                       ACT == 1 ? xs + row * nb : nullptr, ch0, sl, lig);
+        RowSlice<C> wg[U], wu[U];
+        if (valid) {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int64_t o = rbase + st * OPS + u * G + grp;
+                load_row<LPR, C>(wg[u], Wgq + o * d, Wgs + o * nb, ch0, sl, lig);
+                load_row<LPR, C>(wu[u], Wuq + o * d, Wus + o * nb, ch0, sl, lig);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            float g = 0.0f, v = 0.0f;
+            if (valid) {
+                g = row_dot(wg[u], xv, lig);
+                v = row_dot(wu[u], xv, lig);
+            }
+            g = group_sum<LPR>(g);
+            v = group_sum<LPR>(v);
+            if (lig == 0) {
+                gp[s][st * OPS + u * G + grp] = g;
+                up[s][st * OPS + u * G + grp] = v;
+            }
+        }
+    }
+    __syncthreads();
+    if (wid != 0)
+        return;
+    // Wave 0 finishes the tile: lane t < 32 owns output o0 + t.
+    const int t = lane & 31;
+    float g = 0.0f, v = 0.0f;
+    for (int s = 0; s < ks; s++) {
+        g += gp[s][t];
+        v += up[s][t];
+    }
+    const float hv = valid ? silu(g) * v : 0.0f;
+    const int64_t hoff = (row * k + j) * dff + o0 + t;
+    if (h && lane < 32)
+        h[hoff] = hv;
+    if (ACT == 1) {
+        float amax = fabsf(hv);
+        for (int off = 16; off >= 1; off >>= 1)
+            amax = fmaxf(amax, __shfl_xor(amax, off));
+        const float dsc = q8_scale(amax);
+        const float id = q8_inv(dsc);
+        if (lane < 32)
+            hq[hoff] = (int8_t)q8_code(hv, id);
+        if (lane == 0)
+            hs[((row * k + j) * dff + o0) / QB] = dsc;
+    }
+}
+
+template <int ACT, int LPR, int C>
+constexpr int dn_unroll()
+{
+    if (ACT == 0)
+        return C >= 3 ? 1 : (C == 2 ? 2 : (LPR == 16 ? 2 : 4));
+    return C >= 3 ? (LPR == 16 ? 1 : 2) : (LPR == 16 ? 2 : 4);
+}
+
+template <int ACT, int LPR, int C>
+__global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__restrict__ h, const int8_t *__restrict__ hq,
+                                               const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
+                                               const float *__restrict__ Wds, const int32_t *__restrict__ idx,
+                                               const float *__restrict__ wts, int d, int dff, int E, int k, int ks,
+                                               float *__restrict__ y)
+{
+    constexpr int G = WAVE / LPR;
+    constexpr int U = dn_unroll<ACT, LPR, C>();
+    constexpr int OPS = G * U < DN_TILE ? G * U : DN_TILE;
+    constexpr int STEPS = DN_TILE / OPS;
+    static_assert(DN_TILE % OPS == 0 && OPS % G == 0, "steps tile the outputs");
+    constexpr int UU = OPS / G;
+    __shared__ float part[Q8S_MAX_K_DEV * MAX_KS][DN_TILE];
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
+    const int nwaves = blockDim.x >> 6;
+    const int o0 = blockIdx.x * DN_TILE;
+    const int64_t row = blockIdx.z;
+    const int nch = dff >> 4, nb = dff >> 5;
+    const int pairs = k * ks;
+
+    for (int p = wid; p < pairs; p += nwaves) {
+        const int j = p / ks, s = p % ks;
+        const int e = idx[row * k + j];
+        const bool valid = (e >= 0 && e < E);
+        const int ch0 = s * LPR * C;
+        const int sl = min(LPR * C, nch - ch0);
+        const int64_t hrow = (row * k + j) * dff;
+        XSlice<ACT, C> xv;
+        load_x<LPR, C>(xv, ACT == 0 ? h + hrow : nullptr, ACT == 1 ? hq + hrow : nullptr,
+                       ACT == 1 ? hs + hrow / QB : nullptr, ch0, sl, lig);
+        const int64_t rbase = (int64_t)(valid ? e : 0) * d + o0;
+        for (int st = 0; st < STEPS; st++) {
+            RowSlice<C> w[UU];
+            if (valid) {
+#pragma unroll
+                for (int u = 0; u < UU; u++) {
+                    const int64_t o = rbase + st * OPS + u * G + grp;
+                    load_row<LPR, C>(w[u], Wdq + o * dff, Wds + o * nb, ch0, sl, lig);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UU; u++) {
+                float a = valid ? row_dot(w[u], xv, lig) : 0.0f;
+                a = group_sum<LPR>(a);
+                if (lig == 0)
+                    part[p][st * OPS + u * G + grp] = a;
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < DN_TILE) {
+        const int t = threadIdx.x;
+        float acc = 0.0f;
+        for (int j = 0; j < k; j++) {
+            float dj = 0.0f;
+            for (int s = 0; s < ks; s++)
+                dj += part[j * ks + s][t];
+            acc = __builtin_fmaf(wts[row * k + j], dj, acc);
+        }
+        y[row * d + o0 + t] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host dispatch
+
+namespace {
+
+template <int ACT, int LPR, int C>
+hipError_t gu_go(const MoeArgs &a, int ks, hipStream_t st)
+{
+    dim3 grid((unsigned)(a.dff / GU_TILE), (unsigned)a.k, (unsigned)a.rows);
+    hipLaunchKernelGGL((k_gate_up<ACT, LPR, C>), grid, dim3(GU_THREADS), 0, st, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
+                       a.Wus, a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
+    return hipGetLastError();
+}
+
+template <int ACT, int LPR, int C>
+hipError_t dn_go(const MoeArgs &a, int ks, hipStream_t st)
+{
+    const int pairs = (int)a.k * ks;
+    const int nw = std::min(DN_MAX_WAVES, pairs);
+    dim3 grid((unsigned)(a.d / DN_TILE), 1, (unsigned)a.rows);
+    hipLaunchKernelGGL((k_down<ACT, LPR, C>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds, a.idx, a.wts,
+                       (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.y);
+    return hipGetLastError();
+}
+
+template <int ACT, template <int, int, int> class F>
+hipError_t by_shape(const MoeArgs &a, int64_t n_in, hipStream_t st)
+{
+    const SliceShape sh = slice_shape(n_in);
+    if (sh.ks > 1)
+        return F<ACT, 64, 4>::go(a, sh.ks, st);
+    switch (sh.lpr * 8 + sh.c) {
+    case 16 * 8 + 1:
+        return F<ACT, 16, 1>::go(a, 1, st);
+    case 16 * 8 + 3:
+        return F<ACT, 16, 3>::go(a, 1, st);
+    case 64 * 8 + 1:
+        return F<ACT, 64, 1>::go(a, 1, st);
+    case 64 * 8 + 2:
+        return F<ACT, 64, 2>::go(a, 1, st);
+    default:
+        return F<ACT, 64, 4>::go(a, 1, st);
+    }
+}
+
+template <int ACT, int LPR, int C>
+struct GU {
+    static hipError_t go(const MoeArgs &a, int ks, hipStream_t st) { return gu_go<ACT, LPR, C>(a, ks, st); }
+};
+template <int ACT, int LPR, int C>
+struct DN {
+    static hipError_t go(const MoeArgs &a, int ks, hipStream_t st) { return dn_go<ACT, LPR, C>(a, ks, st); }
+};
+
+} // namespace
+
+hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st)
+{
+    return a.act == 0 ? by_shape<0, GU>(a, a.d, st) : by_shape<1, GU>(a, a.d, st);
+}
+
+size_t down_scratch_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+hipError_t down_launch(const MoeArgs &a, hipStream_t st)
+{
+    return a.act == 0 ? by_shape<0, DN>(a, a.dff, st) : by_shape<1, DN>(a, a.dff, st);
+}
+
+} // namespace q8s

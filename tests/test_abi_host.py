@@ -1,0 +1,124 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/q8s.h declares, and refuses bad arguments by naming the rule -- all
+before any HIP call, so these run without a GPU (pointers here are fake,
+never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import q8_gemv_sparse_amd as q8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8s.h")
+LIB = q8.library()
+
+A = 0x10000  # fake, 16-byte aligned device addresses, far apart
+B = 0x20000000
+C = 0x40000000
+D = 0x60000000
+F = 0x80000000
+G = 0xA0000000
+H = 0xC0000000
+J = 0xE0000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"Q8S_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"q8_gemv", "add_rmsnorm_q8", "moe_route_topk", "moe_gate_up", "moe_down_combine",
+                          "q8_quantize_rows", "q8s_scratch_bytes", "q8s_last_error"}
+    for n in names:
+        assert hasattr(LIB, n), n
+    assert q8.q8s_version().startswith("q8s")
+
+
+def _err():
+    return q8.q8s_last_error()
+
+
+def gemv(n_out=64, n_in=64, m=1, act=0, Wq=A, Ws=B, x=C, xq=D, xs=F, y=G):
+    return LIB.q8_gemv(Wq, Ws, n_out, n_in, x, xq, xs, m, y, act, None)
+
+
+def test_gemv_refusals():
+    assert gemv(n_in=48) == -1 and "multiple of 32" in _err()
+    assert gemv(n_in=0) == -1
+    assert gemv(n_out=0) == -1 and "n_out" in _err()
+    assert gemv(m=0) == -1
+    assert gemv(act=2) == -2 and "two-word" in _err()
+    assert gemv(act=7) == -2 and "unknown activation" in _err()
+    assert gemv(x=None) == -1 and "`x` is null" in _err()
+    assert gemv(act=1, xq=None) == -1 and "`xq` is null" in _err()
+    assert gemv(Wq=A + 8) == -3 and "16-byte aligned" in _err()
+    assert gemv(n_in=65536 * 2) == -2 and "longest row" in _err()
+    # output overlapping an input: y placed inside x
+    assert gemv(y=C + 64) == -1 and "overlaps input `x`" in _err()
+
+
+def test_quantize_refusals():
+    assert LIB.q8_quantize_rows(A, 2, 40, B, C, None) == -1 and "multiple of 32" in _err()
+    assert LIB.q8_quantize_rows(A, 2, 64, A + 256, C, None) == -1 and "overlaps" in _err()
+
+
+def norm(rows=1, d=64, eps=1e-6, h=A, r=B, w=C, s=D, y=F, yq=G, ys=H):
+    return LIB.add_rmsnorm_q8(h, r, w, rows, d, ctypes.c_float(eps), s, y, yq, ys, None)
+
+
+def test_norm_refusals():
+    assert norm(d=20) == -1
+    assert norm(yq=None) == -1 and "together" in _err()
+    assert norm(y=None, yq=None, ys=None) == -1 and "neither" in _err()
+    assert norm(eps=-1.0) == -1 and "eps" in _err()
+    assert norm(eps=float("nan")) == -1
+    assert norm(s=None) == -1 and "`sum` is null" in _err()
+    assert norm(y=A) == -1 and "overlaps input `h`" in _err()
+    assert norm(y=D) == -1 and "outputs `sum` and `y` overlap" in _err()
+
+
+def route(rows=1, d=64, E=8, k=2, sb=None, scratch=J, x=A, Wr=B, idx=C, wts=D):
+    if sb is None:
+        sb = q8.q8s_scratch_bytes(q8.FN_ROUTE, rows, d, 32, E, k)
+    return LIB.moe_route_topk(x, Wr, rows, d, E, k, idx, wts, scratch, sb, None)
+
+
+def test_route_refusals_and_scratch():
+    assert q8.q8s_scratch_bytes(q8.FN_ROUTE, 1, 2048, 768, 128, 8) >= 128 * 8 + 4
+    assert q8.q8s_scratch_bytes(99, 1, 2048, 768, 128, 8) == 0
+    assert route(k=0) == -1 and "1 <= k <= E" in _err()
+    assert route(k=9) == -1
+    assert route(E=64, k=33) == -2 and "32 experts kept" in _err()
+    assert route(E=8193, k=8) == -2
+    assert route(d=100) == -1
+    assert route(sb=8) == -4 and "scratch" in _err()
+    assert route(scratch=None) == -4
+    assert route(scratch=J + 16) == -3 and "256-byte" in _err()
+    assert route(scratch=A) == -1 and "overlaps input `x`" in _err()
+
+
+def gate_up(act=0, rows=1, d=64, dff=64, E=4, k=2, x=A, xq=A, xs=B, h=J, hq=H, hs=0xF0000000):
+    return LIB.moe_gate_up(x, xq, xs, C, D, F, G, 0xD0000000, rows, d, dff, E, k, h, hq, hs, act, None)
+
+
+def test_gate_up_refusals():
+    assert gate_up(dff=48) == -1 and "dff" in _err()
+    assert gate_up(k=5) == -1
+    assert gate_up(act=1, hq=None) == -1 and "`hq` is null" in _err()
+    assert gate_up(act=0, h=None) == -1 and "`h` is null" in _err()
+    assert gate_up(act=2) == -2
+    assert gate_up(h=C) == -1 and "overlaps input `Wgq`" in _err()
+
+
+def test_down_refusals():
+    assert q8.q8s_scratch_bytes(q8.FN_DOWN, 1, 64, 64, 4, 2) == 0  # a decode row needs none
+    need = q8.q8s_scratch_bytes(q8.FN_DOWN, 4, 64, 64, 4, 2)
+    if need:
+        r = LIB.moe_down_combine(A, None, None, B, C, D, F, 4, 64, 64, 4, 2, G, 0, None, 0, None)
+        assert r == -4 and "scratch" in _err()
+    r = LIB.moe_down_combine(A, None, None, B, C, D, F, 1, 64, 64, 4, 2, A, 0, None, 0, None)
+    assert r == -1 and "overlaps" in _err()

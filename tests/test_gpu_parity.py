@@ -1,0 +1,351 @@
+"""Parity of the HIP path with the CPU oracle, element by element, on seeded
+inputs: small shapes spanning several tiles and ragged tails, edge cases, and
+the full sizes of the five workloads in the launch shapes the benchmark uses.
+
+Tolerances (max |gpu - oracle| / max |oracle|, float64):
+  * f32-activation mode: 1e-5;
+  * int8-activation mode: 2e-3 against the oracle's int8 mode;
+  * integer results (quantised codes, routing choices, exact block dots):
+    bit-exact, except where the oracle's own float64 value sits on a float32
+    rounding boundary (flagged, counted, and checked for validity instead).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import q8_gemv_sparse_amd as q8
+import synthetic
+from gpu_helpers import dev, f32_ambiguous, host, rel_err, route_ambiguous
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_I8 = 2e-3
+
+
+def banner(msg):
+    print("[case] " + msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# q8_gemv, f32 activations
+
+GEMV_F32_CASES = [
+    (512, 256, 1),      # the 512x256 batch-1 workload
+    (4096, 2048, 1),    # the 2048 -> 4096 batch-1 projection
+    (97, 160, 1),       # ragged rows, a row shorter than a lane group's reach
+    (130, 768, 3),      # lane groups of 16 with 3 chunks, 3 activation rows
+    (64, 1024, 2),
+    (33, 4096, 4),
+    (40, 8192, 1),      # cut along k across 2 waves
+    (19, 14336, 2),     # cut along k across 4 waves, last slice partial
+    (5, 32, 1),         # one block
+    (300, 2048, 7),     # more activation rows than a register pass holds
+]
+
+
+@pytest.mark.parametrize("n_out,n_in,m", GEMV_F32_CASES)
+def test_gemv_f32(n_out, n_in, m):
+    banner("gemv f32 %dx%d m=%d" % (n_out, n_in, m))
+    g = synthetic.gemv_inputs(1, n_out, n_in, m)
+    ref = oracle.gemv_f32(g.Wq, g.Ws, g.x)
+    y = q8.q8_gemv(dev(g.Wq), dev(g.Ws), x=dev(g.x), act=q8.ACT_F32)
+    assert rel_err(host(y), ref) <= TOL_F32
+
+
+def test_gemv_f32_fill_closed_form_exact():
+    banner("gemv f32 closed form")
+    n_in = 2048
+    Wq = np.ones((70, n_in), np.int8)
+    Ws = np.full((70, n_in // 32), 1.0, np.float32)
+    x = synthetic.fill_pattern(n_in)[None, :]
+    y = host(q8.q8_gemv(dev(Wq), dev(Ws), x=dev(x)))
+    assert np.all(y == -6.0)  # tests/golden/fill_closed_forms.txt, n_in = 2048
+
+
+# ---------------------------------------------------------------------------
+# q8_gemv, int8 activations
+
+GEMV_I8_CASES = [
+    (4096, 2048, 1), (512, 256, 1), (97, 160, 2), (130, 768, 4), (19, 14336, 1),
+    (100, 2048, 5), (4096, 2048, 64), (77, 96, 16), (33, 512, 65), (16, 4096, 130),
+]
+
+
+@pytest.mark.parametrize("n_out,n_in,m", GEMV_I8_CASES)
+def test_gemv_int8(n_out, n_in, m):
+    banner("gemv int8 %dx%d m=%d" % (n_out, n_in, m))
+    rng = np.random.default_rng(2)
+    Wq, Ws = synthetic.q8_matrix(rng, n_out, n_in)
+    xq, xs = synthetic.q8_matrix(rng, m, n_in)
+    ref = oracle.gemv_i8(Wq, Ws, xq, xs)
+    y = q8.q8_gemv(dev(Wq), dev(Ws), xq=dev(xq), xs=dev(xs), act=q8.ACT_INT8)
+    assert rel_err(host(y), ref) <= TOL_I8
+
+
+@pytest.mark.parametrize("n_out,n_in,m", [(64, 256, 1), (200, 2048, 3), (48, 4096, 20), (50, 9216, 1)])
+def test_gemv_int8_block_dots_bit_exact(n_out, n_in, m):
+    # Power-of-two scales and small integers make every float step exact: the
+    # result is then the exact integer block dots, on both sides, bit for bit
+    # (register path for m <= 4, MFMA path above).
+    banner("gemv int8 exact %dx%d m=%d" % (n_out, n_in, m))
+    Wq = synthetic.fill_pattern(n_out * n_in).reshape(n_out, n_in).astype(np.int8)
+    xq = synthetic.fill_pattern(m * n_in + 5)[5:].reshape(m, n_in).astype(np.int8)
+    nb = n_in // 32
+    Ws = np.array([[2.0 ** -((o + b) % 4) for b in range(nb)] for o in range(n_out)], np.float32)
+    xs = np.array([[2.0 ** -((r * 3 + b) % 3) for b in range(nb)] for r in range(m)], np.float32)
+    ref = oracle.gemv_i8(Wq, Ws, xq, xs)
+    y = host(q8.q8_gemv(dev(Wq), dev(Ws), xq=dev(xq), xs=dev(xs), act=q8.ACT_INT8))
+    assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_gemv_int8_extreme_block_dots():
+    # every block dot at its extreme, -516128 (int32 headroom), both paths
+    banner("gemv int8 extremes")
+    for m in (1, 16):
+        Wq = np.full((32, 256), 127, np.int8)
+        xq = np.full((m, 256), -127, np.int8)
+        Ws = np.ones((32, 8), np.float32)
+        xs = np.ones((m, 8), np.float32)
+        y = host(q8.q8_gemv(dev(Wq), dev(Ws), xq=dev(xq), xs=dev(xs), act=q8.ACT_INT8))
+        assert np.all(y == -516128.0 * 8)
+
+
+# ---------------------------------------------------------------------------
+# quantiser and fused add + RMSNorm
+
+
+def _quant_edge_rows(n):
+    rng = np.random.default_rng(3)
+    rows = [synthetic.normal(rng, n), 1e-4 * synthetic.normal(rng, n), 1e4 * synthetic.normal(rng, n),
+            np.zeros(n, np.float32)]
+    ties = np.zeros(n, np.float32)
+    ties[0::32] = 127.0
+    ties[1::32] = 2.5
+    ties[2::32] = -2.5
+    ties[3::32] = 0.5
+    ties[4::32] = -126.5
+    rows.append(ties)
+    ints = np.round(synthetic.normal(rng, n) * 30).astype(np.float32)
+    rows.append(ints)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("n", [32, 96, 2048, 2080, 6144])
+def test_quantize_rows_bit_exact(n):
+    banner("quantize n=%d" % n)
+    x = _quant_edge_rows(n)
+    rq, rs = oracle.quantize(x)
+    xq, xs = q8.q8_quantize_rows(dev(x))
+    assert np.array_equal(host(xq), rq)
+    assert np.array_equal(host(xs), rs)
+
+
+@pytest.mark.parametrize("rows,d", [(1, 2048), (3, 96), (2, 2080), (64, 2048), (1, 4096), (1, 32), (2, 16384)])
+def test_add_rmsnorm_q8(rows, d):
+    banner("add_rmsnorm rows=%d d=%d" % (rows, d))
+    inp = synthetic.norm_gemv_inputs(4, d, 32, rows)
+    eps = 1e-6
+    rsum, y64 = oracle.add_rmsnorm(inp.h, inp.r, inp.w, eps)
+    s, y, yq, ys = q8.add_rmsnorm_q8(dev(inp.h), dev(inp.r), dev(inp.w), eps)
+    s, y, yq, ys = host(s), host(y), host(yq), host(ys)
+    assert np.array_equal(s, rsum)
+    assert rel_err(y, y64) <= TOL_F32
+    y32 = y64.astype(np.float32)
+    # The two sides sum the mean square in different orders: float64 values
+    # agree to ~d * 2^-53 relative (~2.3e-13 at d = 2048, the worst case);
+    # elements within 4e-13 of a float32 rounding boundary may round either way.
+    amb = f32_ambiguous(y64, rel=4e-13)
+    # codes are decided by the float32 y: exact wherever the oracle's float32
+    # y is fixed by its float64 value
+    rq, rs = oracle.quantize(y32)
+    blocks_amb = amb.reshape(rows, d // 32, 32).any(axis=2)
+    ok = ~blocks_amb
+    assert blocks_amb.mean() <= 0.01
+    assert np.array_equal(ys[ok], rs[ok])
+    assert np.array_equal(yq.reshape(rows, d // 32, 32)[ok], rq.reshape(rows, d // 32, 32)[ok])
+    # y itself to the nearest float32 where unambiguous, one ulp where not
+    assert np.array_equal(y[~amb], y32[~amb])
+    assert np.all(np.abs(y[amb].astype(np.float64) - y64[amb]) <= np.spacing(np.abs(y32[amb])))
+    # ambiguous blocks: still a valid Q8_0 encoding of the GPU's own y, codes
+    # within one step of the oracle's
+    qb = yq.reshape(rows, d // 32, 32)[blocks_amb].astype(np.int32)
+    assert np.all(np.abs(qb - rq.reshape(rows, d // 32, 32)[blocks_amb].astype(np.int32)) <= 1)
+    assert np.all(np.abs(ys[blocks_amb] - rs[blocks_amb]) <= np.spacing(rs[blocks_amb]))
+
+
+def test_add_rmsnorm_modes_and_fusion():
+    # the fused kernel equals the unfused chain add -> norm -> quantise
+    banner("add_rmsnorm fusion")
+    inp = synthetic.norm_gemv_inputs(5, 2048, 32, 2)
+    h, r, w = dev(inp.h), dev(inp.r), dev(inp.w)
+    s1, y1, q1, d1 = q8.add_rmsnorm_q8(h, r, w, 1e-6)
+    s2, y2, _, _ = q8.add_rmsnorm_q8(h, r, w, 1e-6, want_q8=False)
+    s3, _, q3, d3 = q8.add_rmsnorm_q8(h, r, w, 1e-6, want_f32=False)
+    qx, dx = q8.q8_quantize_rows(y1)
+    for a, b in ((s1, s2), (s1, s3), (y1, y2), (q1, q3), (d1, d3), (q1, qx), (d1, dx)):
+        assert torch.equal(a, b)
+    # no residual: the norm of h alone
+    s4, y4, _, _ = q8.add_rmsnorm_q8(s1, torch.zeros_like(s1), w, 1e-6, want_q8=False)
+    assert torch.equal(y4, y1)
+
+
+# ---------------------------------------------------------------------------
+# router + top-K
+
+ROUTE_CASES = [
+    (1, 2048, 128, 8),   # the 128-expert decode router
+    (1, 4096, 8, 2),     # the 8-expert decode router
+    (64, 2048, 128, 8),  # a 64-row chunk
+    (5, 96, 6, 6),       # K = E
+    (3, 64, 1, 1),       # one expert
+    (2, 128, 300, 1),    # E not a multiple of the workgroup's 4 experts
+    (1, 256, 8192, 32),  # the limits
+    (7, 32, 40, 32),
+]
+
+
+@pytest.mark.parametrize("rows,d,E,k", ROUTE_CASES)
+def test_route_topk(rows, d, E, k):
+    banner("route rows=%d d=%d E=%d k=%d" % (rows, d, E, k))
+    rng = np.random.default_rng(6)
+    Wr = (0.02 * synthetic.normal(rng, E, d)).astype(np.float32)
+    x = synthetic.normal(rng, rows, d)
+    ridx, rw, logits = oracle.route(x, Wr, k)
+    idx, wts = q8.moe_route_topk(dev(x), dev(Wr), k)
+    idx, wts = host(idx), host(wts)
+    amb = route_ambiguous(logits, k)
+    assert amb.sum() == 0 or rows > 1
+    assert np.array_equal(idx[~amb], ridx[~amb])
+    assert rel_err(wts[~amb], rw[~amb]) <= TOL_F32
+    assert np.allclose(wts.sum(axis=1), 1.0, atol=1e-6)
+    # every row's choices are distinct valid experts
+    for row in idx:
+        assert len(set(row.tolist())) == k and row.min() >= 0 and row.max() < E
+
+
+def test_route_ties_and_zero_router():
+    banner("route ties")
+    d = 64
+    x = synthetic.normal(np.random.default_rng(7), 2, d)
+    idx, wts = q8.moe_route_topk(dev(x), dev(np.zeros((16, d), np.float32)), 4)
+    assert (host(idx) == np.arange(4)).all() and np.allclose(host(wts), 0.25)
+    Wr = np.zeros((6, d), np.float32)
+    Wr[3] = Wr[1] = x[0] / 8
+    Wr[5] = x[0] / 16
+    idx, _ = q8.moe_route_topk(dev(x[:1]), dev(Wr), 3)
+    assert list(host(idx)[0]) == [1, 3, 5]
+
+
+def test_route_scratch_reuse_keeps_counters_zero():
+    banner("route scratch reuse")
+    rng = np.random.default_rng(8)
+    Wr = (0.02 * synthetic.normal(rng, 128, 2048)).astype(np.float32)
+    xs = [synthetic.normal(rng, r, 2048) for r in (1, 64, 1, 3)]
+    scratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_ROUTE, 64, 2048, 32, 128, 8), dtype=torch.uint8, device="cuda")
+    for x in xs:
+        ridx, _, _ = oracle.route(x, Wr, 8)
+        idx, _ = q8.moe_route_topk(dev(x), dev(Wr), 8, scratch=scratch)
+        assert np.array_equal(host(idx), ridx)
+    # the counter region (the scratch's first 64 KiB) is left zero
+    assert int(host(scratch)[:65536].astype(np.int64).sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# the MoE block
+
+
+def run_moe_gpu(m, act):
+    """The GPU pipeline: route (f32 x), [quantise x], gate-up, down-combine."""
+    x = dev(m.x)
+    Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds = (dev(a) for a in (m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds))
+    idx, wts = q8.moe_route_topk(x, Wr, m.k)
+    if act == q8.ACT_F32:
+        h, _, _ = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, m.E, x=x, act=act)
+        y = q8.moe_down_combine(Wdq, Wds, idx, wts, m.E, h=h, act=act)
+    else:
+        xq, xs = q8.q8_quantize_rows(x)
+        h, hq, hs = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, m.E, xq=xq, xs=xs, act=act)
+        y = q8.moe_down_combine(Wdq, Wds, idx, wts, m.E, hq=hq, hs=hs, act=act)
+    return host(idx), host(wts), host(h), host(y)
+
+
+MOE_SMALL = [
+    dict(d=96, dff=160, E=5, k=3, rows=1),
+    dict(d=768, dff=256, E=6, k=2, rows=1),
+    dict(d=256, dff=96, E=4, k=4, rows=2),
+    dict(d=2048, dff=768, E=16, k=8, rows=3),
+    dict(d=64, dff=14336 // 4, E=3, k=1, rows=1),
+]
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("shape", MOE_SMALL, ids=lambda s: "d%(d)d_dff%(dff)d_E%(E)d_k%(k)d_r%(rows)d" % s)
+def test_moe_block_small(shape, act):
+    banner("moe small %s act=%d" % (shape, act))
+    m = synthetic.moe_inputs(9, shape["d"], shape["dff"], shape["E"], shape["k"], shape["rows"])
+    ridx, rw, rh, ry = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, m.k, act)
+    idx, wts, h, y = run_moe_gpu(m, act)
+    tol = TOL_F32 if act == 0 else TOL_I8
+    assert np.array_equal(idx, ridx)
+    assert rel_err(wts, rw) <= TOL_F32
+    assert rel_err(h, rh) <= tol
+    assert rel_err(y, ry) <= tol
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("name", ["moe_d2048_dff768_e128_k8", "moe_d4096_dff14336_e8_k2"])
+def test_moe_block_full_size(name, act):
+    cfg = synthetic.CONFIGS[name]
+    banner("moe full %s act=%d" % (name, act))
+    m = synthetic.moe_inputs(0, cfg["d"], cfg["dff"], cfg["E"], cfg["k"], 1)
+    ridx, rw, rh, ry = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, m.k, act)
+    idx, wts, h, y = run_moe_gpu(m, act)
+    tol = TOL_F32 if act == 0 else TOL_I8
+    assert np.array_equal(idx, ridx)
+    assert rel_err(h, rh) <= tol
+    assert rel_err(y, ry) <= tol
+
+
+def test_moe_invalid_expert_index_contributes_zero():
+    banner("moe invalid idx")
+    m = synthetic.moe_inputs(10, 64, 64, 4, 2, 1)
+    Wgq, Wgs, Wuq, Wus, Wdq, Wds = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds))
+    idx = dev(np.array([[-1, 7]], np.int32))
+    wts = dev(np.array([[0.5, 0.5]], np.float32))
+    h, _, _ = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, 4, x=dev(m.x))
+    y = q8.moe_down_combine(Wdq, Wds, idx, wts, 4, h=h)
+    assert not host(h).any() and not host(y).any()
+
+
+def test_moe_deterministic():
+    banner("moe determinism")
+    m = synthetic.moe_inputs(11, 2048, 768, 32, 8, 1)
+    a = run_moe_gpu(m, 1)
+    b = run_moe_gpu(m, 1)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# the 64-row prefill chunk: MoE over expert-grouped rows + dense GEMM
+
+
+def test_chunk_full_size():
+    cfg = synthetic.CONFIGS["chunk64_moe_d2048_dense4096"]
+    banner("chunk 64 rows, int8")
+    m, Dq, Ds = synthetic.chunk_inputs(0, cfg["d"], cfg["dff"], cfg["E"], cfg["k"], cfg["rows"], cfg["n_dense"])
+    ridx, rw, rh, ry = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, m.k, 1)
+    idx, wts, h, y = run_moe_gpu(m, 1)
+    assert np.array_equal(idx, ridx)
+    for r in range(cfg["rows"]):
+        assert rel_err(y[r], ry[r]) <= TOL_I8, r
+    # the dense projection of the same rows' Q8_0 form
+    xq, xs = q8.q8_quantize_rows(dev(m.x))
+    rq, rs = oracle.quantize(m.x)
+    assert np.array_equal(host(xq), rq) and np.array_equal(host(xs), rs)
+    Y = host(q8.q8_gemv(dev(Dq), dev(Ds), xq=xq, xs=xs, act=q8.ACT_INT8))
+    ref = oracle.gemv_i8(Dq, Ds, rq, rs)
+    for r in range(cfg["rows"]):
+        assert rel_err(Y[r], ref[r]) <= TOL_I8, r
