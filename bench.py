@@ -1,0 +1,479 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 GEMV / sparse-MoE hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--act int8|f32]
+
+A step is one pass of the hot path over one batch of synthetic input.  The
+default workload is the batch-1 MoE FFN block at the Qwen3-30B-A3B-like shape
+(d 2048, dff 768, 128 experts, top 8), fed by its producer:
+
+    add_rmsnorm_q8 -> moe_route_topk -> moe_gate_up -> moe_down_combine
+
+Inputs are resident in HBM before timing starts.  Weight reads are kept
+cache-cold: the step rotates over `copies` copies of every weight array (more
+bytes between two uses of a copy than the 256 MB Infinity Cache holds) and
+over a pool of different input rows (so the chosen experts change from step
+to step).
+
+Timing: the steps are captured once in a HIP graph (a graph of `copies`
+consecutive steps) and the graph is replayed; HIP events on the replay stream
+bracket exactly K steps, with a device synchronisation on both sides.  The
+dominant kernel's average duration is measured with HIP event pairs around
+each of its launches (eager launches on the same stream), and reported against
+the HBM roofline on its algorithmic bytes (the weight bytes one launch must
+read).  The CPU oracle is timed on a bounded sample of the same workload.
+
+Prints one JSON line on stdout; details go to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs and effective HBM GB/s per batch-1 MoE FFN block / Q8_0 GEMV (% of peak)"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--workload", default="moe_d2048_dff768_e128_k8")
+    p.add_argument("--act", choices=["int8", "f32"], default="int8")
+    p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough to defeat the MALL)")
+    p.add_argument("--kernel-launches", type=int, default=400, help="eager launches timed for the dominant kernel")
+    p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
+    return p.parse_args()
+
+
+def src_digest(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# workloads
+
+
+class Workload:
+    name = ""
+    dominant = ""          # kernel symbol stem of the dominant kernel
+    dominant_src = ()      # sources that define it (for the counter-file check)
+
+    def step(self, c):
+        raise NotImplementedError
+
+    def launch_dominant(self, c):
+        raise NotImplementedError
+
+
+def _copies(step_bytes, want):
+    """Weight copies to rotate so that more than two MALLs' worth of weight
+    traffic passes between two uses of one copy."""
+    if want:
+        return want
+    return max(2, min(64, -(-(2 * MALL_BYTES) // max(step_bytes, 1)) + 1))
+
+
+class MoeBlock(Workload):
+    """add_rmsnorm_q8 -> route -> gate-up -> down-combine, `rows` rows."""
+
+    dominant = "k_gate_up"
+    dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
+
+    def __init__(self, name, cfg, act, copies, rows=1, pool=64):
+        import numpy as np
+        import torch
+
+        import q8_gemv_sparse_amd as q8
+        import synthetic
+        self.q8, self.torch, self.np = q8, torch, np
+        self.name, self.act = name, act
+        d, dff, E, k = cfg["d"], cfg["dff"], cfg["E"], cfg["k"]
+        self.d, self.dff, self.E, self.k, self.rows = d, dff, E, k, rows
+        t0 = time.time()
+        m = synthetic.moe_inputs(0, d, dff, E, k, rows=1)
+        self.host_w = m
+        rng = np.random.default_rng(1)
+        self.norm_w = rng.uniform(0.5, 1.5, size=d).astype(np.float32)
+        self.pool_h = [synthetic.normal(rng, rows, d) for _ in range(pool)]
+        self.pool_r = [synthetic.normal(rng, rows, d) for _ in range(pool)]
+        log("[bench] generated inputs in %.1fs" % (time.time() - t0))
+        per_expert = 3 * dff * d + 3 * dff * (d // 32) * 4
+        self.bytes_all = E * d * 4 + E * per_expert
+        # rotate enough copies that a copy was last touched more than two
+        # MALLs of traffic ago
+        step_bytes = E * d * 4 + min(E, rows * k) * per_expert
+        self.copies = copies or _copies(step_bytes, 0)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        base = [dev(a) for a in (m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds)]
+        self.W = [base] + [[t.clone() for t in base] for _ in range(self.copies - 1)]
+        self.w = dev(self.norm_w)
+        self.h = [dev(a) for a in self.pool_h]
+        self.r = [dev(a) for a in self.pool_r]
+        self.pool = pool
+        z = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device="cuda")
+        self.sum = z(rows, d)
+        self.y = z(rows, d)
+        self.xq, self.xs = z(rows, d, dt=torch.int8), z(rows, d // 32)
+        self.idx = [z(rows, k, dt=torch.int32) for _ in range(self.copies)]
+        self.wts = [z(rows, k) for _ in range(self.copies)]
+        self.hf = z(rows, k, dff)
+        self.hq, self.hs = z(rows, k, dff, dt=torch.int8), z(rows, k, dff // 32)
+        self.out = z(rows, d)
+        self.rscratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_ROUTE, rows, d, dff, E, k), dtype=torch.uint8,
+                                    device="cuda")
+        dn = q8.q8s_scratch_bytes(q8.FN_DOWN, rows, d, dff, E, k)
+        self.dscratch = torch.zeros(dn, dtype=torch.uint8, device="cuda") if dn else None
+        torch.cuda.synchronize()
+        log("[bench] %s: %d weight copies of %.1f MB on the device" % (name, self.copies, self.bytes_all / 1e6))
+
+    # one pass; copy c, input c % pool
+    def step(self, c):
+        q8 = self.q8
+        W = self.W[c % self.copies]
+        i = c % self.pool
+        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y,
+                          yq=self.xq if a == q8.ACT_INT8 else None, ys=self.xs if a == q8.ACT_INT8 else None,
+                          want_q8=(a == q8.ACT_INT8))
+        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+        q8.moe_route_topk(self.y, W[0], self.k, idx=idx, wts=wts, scratch=self.rscratch)
+        self._gate_up(c, a)
+        if a == q8.ACT_INT8:
+            q8.moe_down_combine(W[5], W[6], idx, wts, self.E, hq=self.hq, hs=self.hs, y=self.out, act=a,
+                                scratch=self.dscratch)
+        else:
+            q8.moe_down_combine(W[5], W[6], idx, wts, self.E, h=self.hf, y=self.out, act=a, scratch=self.dscratch)
+
+    def _gate_up(self, c, a):
+        q8 = self.q8
+        W = self.W[c % self.copies]
+        idx = self.idx[c % self.copies]
+        if a == q8.ACT_INT8:
+            q8.moe_gate_up(W[1], W[2], W[3], W[4], idx, self.E, xq=self.xq, xs=self.xs, hq=self.hq, hs=self.hs,
+                           act=a, want_h=False)
+        else:
+            q8.moe_gate_up(W[1], W[2], W[3], W[4], idx, self.E, x=self.y, h=self.hf, act=a)
+
+    def launch_dominant(self, c):
+        self._gate_up(c, self.q8.ACT_INT8 if self.act == "int8" else self.q8.ACT_F32)
+
+    def distinct_experts(self, c):
+        """Experts chosen by copy c's last route (for the bytes a chunk reads)."""
+        return int(self.torch.unique(self.idx[c % self.copies]).numel())
+
+    def weight_bytes(self, c=None):
+        """Weight bytes one step must read: the router and each distinct chosen
+        expert's gate, up and down (quants + scales)."""
+        d, dff, E = self.d, self.dff, self.E
+        per_expert = 3 * (dff * d + dff * (d // 32) * 4)
+        u = self.k if self.rows == 1 else self.distinct_experts(c)
+        return E * d * 4 + u * per_expert
+
+    def dominant_bytes(self, c=None):
+        d, dff = self.d, self.dff
+        u = self.k if self.rows == 1 else self.distinct_experts(c)
+        return u * 2 * (dff * d + dff * (d // 32) * 4)
+
+    def verify(self):
+        """One eager step against the oracle (the same input, every stage)."""
+        import oracle
+        np = self.np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        m = self.host_w
+        s, y64 = oracle.add_rmsnorm(self.pool_h[0], self.pool_r[0], self.norm_w, 1e-6)
+        x = y64.astype(np.float32)
+        a = 1 if self.act == "int8" else 0
+        ridx, rw, rh, ry = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a)
+        got = self.out.cpu().numpy()
+        err = float(np.max(np.abs(got - ry)) / np.max(np.abs(ry)))
+        same_idx = bool(np.array_equal(self.idx[0].cpu().numpy(), ridx))
+        return {"idx_equal": same_idx, "max_rel_err": err, "tol": 2e-3 if a else 1e-5}
+
+    def cpu_baseline(self, budget):
+        import oracle
+        np = self.np
+        m = self.host_w
+        a = 1 if self.act == "int8" else 0
+        n, t0 = 0, time.perf_counter()
+        while True:
+            i = n % self.pool
+            s, y64 = oracle.add_rmsnorm(self.pool_h[i], self.pool_r[i], self.norm_w, 1e-6)
+            x = y64.astype(np.float32)
+            if a:
+                oracle.quantize(x)
+            oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget or n >= 100000:
+                break
+        per_step = el / n
+        return per_step, "%d steps (rows %d, inputs from the same pool), %.1f s" % (n, self.rows, el)
+
+
+class NormGemv(Workload):
+    """add_rmsnorm_q8 -> q8_gemv (the 2048 -> 4096 batch-1 projection)."""
+
+    dominant = "k_gemv_rows"
+    dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
+
+    def __init__(self, name, cfg, act, copies, pool=64):
+        import numpy as np
+        import torch
+
+        import q8_gemv_sparse_amd as q8
+        import synthetic
+        self.q8, self.torch, self.np = q8, torch, np
+        self.name, self.act = name, act
+        d, n_out = cfg["d"], cfg["n_out"]
+        self.d, self.n_out = d, n_out
+        inp = synthetic.norm_gemv_inputs(0, d, n_out, rows=1)
+        self.inp = inp
+        rng = np.random.default_rng(1)
+        self.pool_h = [synthetic.normal(rng, 1, d) for _ in range(pool)]
+        self.pool_r = [synthetic.normal(rng, 1, d) for _ in range(pool)]
+        self.pool = pool
+        wbytes = n_out * d + n_out * (d // 32) * 4
+        self.copies = copies or _copies(wbytes, 0)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        base = [dev(inp.Wq), dev(inp.Ws)]
+        self.W = [base] + [[t.clone() for t in base] for _ in range(self.copies - 1)]
+        self.w = dev(inp.w)
+        self.h = [dev(a) for a in self.pool_h]
+        self.r = [dev(a) for a in self.pool_r]
+        z = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device="cuda")
+        self.sum, self.y = z(1, d), z(1, d)
+        self.xq, self.xs = z(1, d, dt=torch.int8), z(1, d // 32)
+        self.out = z(1, n_out)
+        self.wbytes = wbytes
+        torch.cuda.synchronize()
+
+    def step(self, c):
+        q8 = self.q8
+        i = c % self.pool
+        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y,
+                          yq=self.xq if a else None, ys=self.xs if a else None, want_q8=bool(a))
+        self.launch_dominant(c)
+
+    def launch_dominant(self, c):
+        q8 = self.q8
+        W = self.W[c % self.copies]
+        if self.act == "int8":
+            q8.q8_gemv(W[0], W[1], xq=self.xq, xs=self.xs, y=self.out, act=q8.ACT_INT8)
+        else:
+            q8.q8_gemv(W[0], W[1], x=self.y, y=self.out, act=q8.ACT_F32)
+
+    def weight_bytes(self, c=None):
+        return self.wbytes
+
+    def dominant_bytes(self, c=None):
+        return self.wbytes
+
+    def verify(self):
+        import oracle
+        np = self.np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        s, y64 = oracle.add_rmsnorm(self.pool_h[0], self.pool_r[0], self.inp.w, 1e-6)
+        x = y64.astype(np.float32)
+        if self.act == "int8":
+            q, sc = oracle.quantize(x)
+            ref = oracle.gemv_i8(self.inp.Wq, self.inp.Ws, q, sc)
+        else:
+            ref = oracle.gemv_f32(self.inp.Wq, self.inp.Ws, x)
+        got = self.out.cpu().numpy()
+        err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        return {"max_rel_err": err, "tol": 2e-3 if self.act == "int8" else 1e-5}
+
+    def cpu_baseline(self, budget):
+        import oracle
+        np = self.np
+        n, t0 = 0, time.perf_counter()
+        while True:
+            i = n % self.pool
+            s, y64 = oracle.add_rmsnorm(self.pool_h[i], self.pool_r[i], self.inp.w, 1e-6)
+            x = y64.astype(np.float32)
+            if self.act == "int8":
+                q, sc = oracle.quantize(x)
+                oracle.gemv_i8(self.inp.Wq, self.inp.Ws, q, sc)
+            else:
+                oracle.gemv_f32(self.inp.Wq, self.inp.Ws, x)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                break
+        return el / n, "%d steps, %.1f s" % (n, el)
+
+
+def make_workload(name, act, copies):
+    import synthetic
+    cfg = synthetic.CONFIGS[name]
+    if cfg["kind"] == "moe":
+        return MoeBlock(name, cfg, act, copies)
+    if cfg["kind"] == "norm_gemv":
+        return NormGemv(name, cfg, act, copies)
+    if cfg["kind"] == "chunk":
+        return MoeBlock(name, cfg, "int8", copies, rows=cfg["rows"], pool=8)
+    raise SystemExit("workload %s is a parity case, not a bench workload" % name)
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = make_workload(args.workload, args.act, args.copies)
+    ver = wl.verify()
+    log("[bench] verify against the oracle:", ver)
+
+    stream = torch.cuda.Stream()
+    C = wl.copies
+    # capture a graph of C consecutive steps, one per weight copy
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for c in range(C):  # eager warm-up on the capture stream
+            wl.step(c)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for c in range(C):
+            wl.step(c)
+    torch.cuda.synchronize()
+    replays = max(1, -(-args.steps // C))
+    steps = replays * C
+    wreps = -(-args.warmup // C) if args.warmup > 0 else 0
+    with torch.cuda.stream(stream):
+        for _ in range(wreps):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / steps
+    # the graph's result equals an eager step's
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_out = wl.out.clone()
+    with torch.cuda.stream(stream):
+        wl.step(C - 1)
+    torch.cuda.synchronize()
+    graph_matches = bool(torch.equal(graph_out, wl.out))
+
+    # the dominant kernel, event pairs around each launch
+    n = max(args.kernel_launches, 1)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for c in range(C):
+            wl.step(c)  # leaves each copy's routing in place
+        for i in range(n):
+            a, b = evs[i]
+            a.record(stream)
+            wl.launch_dominant(i % C)
+            b.record(stream)
+    torch.cuda.synchronize()
+    kms = sum(a.elapsed_time(b) for a, b in evs) / n
+    dom_bytes = sum(wl.dominant_bytes(i % C) for i in range(C)) / C
+    step_bytes = sum(wl.weight_bytes(c) for c in range(C)) / C
+    achieved = dom_bytes / (kms * 1e-3) / 1e9
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy: %d MiB" % args.calib_copy_mib)
+
+    traffic = None
+    cfile = os.path.join(ROOT, "profiles", "%s_%s_%s_counters.json" % (wl.dominant, wl.name, args.act))
+    if os.path.exists(cfile):
+        with open(cfile) as fh:
+            cnt = json.load(fh)
+        if cnt.get("source_digest") == src_digest(*wl.dominant_src):
+            traffic = cnt.get("hbm_bytes_per_launch")
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        per_step, sample = wl.cpu_baseline(args.cpu_budget)
+        cpu = {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": sample + "; %.1f ms per step" % (per_step * 1e3)}
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wreps * C,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8" if args.act == "int8" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "act": args.act,
+            "rows": getattr(wl, "rows", 1),
+            "weight_bytes_per_step": int(step_bytes),
+            "us_per_step": round(ms_per_step * 1e3, 3),
+            "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+            "weight_copies": C,
+            "timing": "HIP graph of %d steps replayed %d times" % (C, replays),
+            "verified": ver,
+            "graph_equals_eager": graph_matches,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": wl.dominant,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": int(dom_bytes),
+            "us_per_launch": round(kms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    log("[bench] wall %.3fs for %d steps" % (t_wall, steps))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

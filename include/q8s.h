@@ -135,10 +135,9 @@ Q8S_API int add_rmsnorm_q8(const float *h, const float *r, const float *w, int64
  * x: device f32 [rows, d] (the router reads f32 x in both numerics);
  * Wr: device f32 [E, d]; idx: device int32 [rows, k]; wts: device f32
  * [rows, k].  1 <= k <= min(32, E), E <= 8192.
- * scratch: device, >= q8s_scratch_bytes(Q8S_FN_ROUTE, ...), 256-byte aligned,
- * zero-filled once when allocated; every call leaves its counter region zero
- * again (arena.rs fn scratch: an arrival count the last block resets).  Calls
- * that share a scratch buffer must be ordered on one stream.
+ * scratch: device, >= q8s_scratch_bytes(Q8S_FN_ROUTE, ...) bytes, 256-byte
+ * aligned: the rows' double-precision logits (arena.rs fn scratch, `rl`);
+ * no initial contents are needed.  Two kernels run, logits then top-K.
  */
 Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k,
                    int32_t *idx, float *wts, void *scratch, size_t scratch_bytes, void *stream);
@@ -150,15 +149,16 @@ Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_
  *   for every row r, slot j (e = idx[r][j]), output o < dff:
  *     g = Wg[e*dff + o] . x[r],  u = Wu[e*dff + o] . x[r]
  *     h[r][j][o] = SiLU(g) * u,   SiLU(z) = z / (1 + exp(-z))
- *   INT8: the dots read x's Q8_0 form, and h is also written quantised per
- *   32-value block of each (r, j) row (hq/hs, arena.rs fn scratch).
+ *   INT8: the dots read x's Q8_0 form (xq/xs, written by add_rmsnorm_q8's
+ *   epilogue or q8_quantize_rows), and the hidden row is also written in its
+ *   Q8_0 form, each 32-value block of each (r, j) row quantised by the
+ *   q8_quantize_rows rule from the float32 h (arena.rs fn scratch: hq/hs).
  * x: device f32 [rows, d] (F32) or NULL; xq/xs: device Q8_0 [rows, d] (INT8)
  * or NULL.  Wgq/Wuq: device int8 [E*dff, d]; Wgs/Wus: device f32
- * [E*dff, d/32].  idx: device int32 [rows, k].  h: device f32 [rows, k, dff]
- * (required for F32; optional for INT8).  hq/hs: device int8 [rows, k, dff]
- * and f32 [rows, k, dff/32] (INT8 only, required).  With rows > 1 the
- * choices are grouped by expert on the device, so each chosen expert's rows
- * are read once per call.
+ * [E*dff, d/32].  idx: device int32 [rows, k].  h: device f32
+ * [rows, k, dff] (required for F32, optional for INT8).  hq/hs: device int8
+ * [rows, k, dff] and f32 [rows, k, dff/32] (INT8 only, required).  A choice
+ * whose expert index is invalid gets zeros.
  */
 Q8S_API int moe_gate_up(const float *x, const int8_t *xq, const float *xs,
                 const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
@@ -169,12 +169,13 @@ Q8S_API int moe_gate_up(const float *x, const int8_t *xq, const float *xs,
  * moe_down_combine -- each kept expert's down projection, weighted and
  * summed in slot order (fn emit_moe_forward):
  *   y[r][o] = sum_{j<K} wts[r][j] * (Wd[e*d + o] . h[r][j]),  e = idx[r][j]
- * F32 reads h: device f32 [rows, k, dff]; INT8 reads hq/hs (device Q8_0
- * [rows, k, dff]).  Wdq: device int8 [E*d, dff]; Wds: device f32
- * [E*d, dff/32]; idx/wts: device [rows, k]; y: device f32 [rows, d].
- * scratch: device, >= q8s_scratch_bytes(Q8S_FN_DOWN, ...) (zero bytes when
- * rows == 1, where NULL is accepted): per-choice results of a chunk, combined
- * per row in slot order.
+ * F32 reads h: device f32 [rows, k, dff].  INT8 reads the hidden row's Q8_0
+ * form hq/hs (device int8 [rows, k, dff], f32 [rows, k, dff/32], as
+ * moe_gate_up writes it) and forms exact int32 block dots.  Wdq: device int8
+ * [E*d, dff]; Wds: device f32 [E*d, dff/32]; idx/wts: device [rows, k];
+ * y: device f32 [rows, d].  scratch: device, >= q8s_scratch_bytes(Q8S_FN_DOWN,
+ * ...) bytes, 256-byte aligned (zero bytes when rows == 1, where NULL is
+ * accepted): per-choice results of a chunk, combined per row in slot order.
  */
 Q8S_API int moe_down_combine(const float *h, const int8_t *hq, const float *hs,
                      const int8_t *Wdq, const float *Wds, const int32_t *idx, const float *wts,

@@ -164,8 +164,8 @@ def add_rmsnorm_q8(h, r, w, eps, sum=None, y=None, yq=None, ys=None, want_f32=Tr
 
 def moe_route_topk(x, Wr, k, idx=None, wts=None, scratch=None, stream=None):
     """Router + top-K: (idx int32 [rows, k], wts f32 [rows, k]).  ``scratch`` is a
-    zero-filled uint8 device tensor of at least q8s_scratch_bytes(FN_ROUTE, ...)
-    bytes, kept across calls (its counters are left zero)."""
+    uint8 device tensor of at least q8s_scratch_bytes(FN_ROUTE, ...) bytes (the
+    logits); one is allocated when none is given."""
     _dev(x, torch.float32, "x"); _dev(Wr, torch.float32, "Wr")
     E, d = Wr.shape
     rows = x.numel() // d
@@ -175,7 +175,7 @@ def moe_route_topk(x, Wr, k, idx=None, wts=None, scratch=None, stream=None):
     if wts is None:
         wts = torch.empty((rows, k), dtype=torch.float32, device=dev)
     if scratch is None:
-        scratch = torch.zeros(q8s_scratch_bytes(FN_ROUTE, rows, d, 32, E, k), dtype=torch.uint8, device=dev)
+        scratch = torch.empty(q8s_scratch_bytes(FN_ROUTE, rows, d, 32, E, k), dtype=torch.uint8, device=dev)
     _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts"); _dev(scratch, torch.uint8, "scratch")
     _check(_lib.moe_route_topk(_ptr(x), _ptr(Wr), rows, d, E, k, _ptr(idx), _ptr(wts), _ptr(scratch),
                                scratch.numel(), _stream(stream)))
@@ -184,7 +184,9 @@ def moe_route_topk(x, Wr, k, idx=None, wts=None, scratch=None, stream=None):
 
 def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq=None, hs=None, act=ACT_F32,
                 want_h=True, stream=None):
-    """h[rows, k, dff] = SiLU(Wg[e] x) * (Wu[e] x) for each kept expert; INT8 also returns hq/hs."""
+    """h[rows, k, dff] = SiLU(Wg[e] x) * (Wu[e] x) for each kept expert e.
+    Returns (h, hq, hs): INT8 also writes the hidden row's Q8_0 form; h may be
+    skipped there (want_h=False)."""
     for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq")):
         _dev(t, torch.int8, n)
     for t, n in ((Wgs, "Wgs"), (Wus, "Wus")):
@@ -200,6 +202,7 @@ def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq
         _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
         if hq is None:
             hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
+        if hs is None:
             hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
     if h is None and (want_h or act == ACT_F32):
         h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)
@@ -211,7 +214,7 @@ def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq
 
 def moe_down_combine(Wdq, Wds, idx, wts, E, h=None, hq=None, hs=None, y=None, act=ACT_F32, scratch=None,
                      stream=None):
-    """y[rows, d] = sum_j wts[:, j] * (Wd[idx[:, j]] @ h[:, j])."""
+    """y[rows, d] = sum_j wts[:, j] * (Wd[idx[:, j]] @ h[:, j]); INT8 reads hq/hs."""
     _dev(Wdq, torch.int8, "Wdq"); _dev(Wds, torch.float32, "Wds")
     _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
     rows, k = idx.shape

@@ -191,6 +191,74 @@ Q8S_DEV void load_x(XSlice<1, C> &x, const float *, const int8_t *__restrict__ x
     }
 }
 
+// Quantising an f32 activation slice on the spot, in two halves so the loads
+// can be issued before other traffic (waits on the vector-memory counter are
+// in issue order: a load issued after the weight rows could only be used once
+// all of them had landed).
+// Block b is chunks 2b, 2b+1, held by lanes 2i, 2i+1 of the group, so the
+// block's absolute maximum is the pair's, one DPP step.  The scale and codes
+// follow the float32 quantiser above, step for step, so they equal what
+// q8_quantize_rows writes for the same values.
+template <int C>
+struct XRaw {
+    f32x4 v[C][4];
+};
+
+template <int LPR, int C>
+Q8S_DEV void load_x_raw(XRaw<C> &r, const float *__restrict__ xr, int ch0, int nch, int lig)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        const int ch = c * LPR + lig;
+        if (ch < nch) {
+            const float *p = xr + (int64_t)(ch0 + ch) * 16;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                r.v[c][i] = ldf4(p + 4 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                r.v[c][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+}
+
+template <int C>
+Q8S_DEV void quantize_slice(XSlice<1, C> &x, const XRaw<C> &r)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+                amax = fmaxf(amax, fabsf(r.v[c][i][b]));
+        amax = fmaxf(amax, dpp_f<DPP_XOR1>(amax));
+        const float d = q8_scale(amax);
+        const float id = q8_inv(d);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            uint32_t dw = 0;
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+                dw |= (uint32_t)(q8_code(r.v[c][i][b], id) & 0xFF) << (8 * b);
+            x.q[c][i] = (int)dw;
+        }
+        x.s[c] = d;
+    }
+}
+
+template <int C>
+Q8S_DEV void raw_to_slice(XSlice<0, C> &x, const XRaw<C> &r)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            x.v[c][i] = r.v[c][i];
+}
+
 // sum_i q_i * x_i over one 16-byte chunk, float32 (each int8 converted
 // exactly; the multiply-adds accumulate in float32).
 Q8S_DEV float chunk_dot_f32(i32x4 q, const f32x4 (&x)[4])

@@ -226,7 +226,9 @@ struct Shape {
 template <int ACT, int LPR, int C, int MR, bool SPLIT>
 hipError_t launch_rows(const GemvArgs &a, int ks, hipStream_t st)
 {
-    constexpr int U = (ACT == 0 && SPLIT) ? 1 : ((C >= 3) ? 2 : 4);
+    // one or two rows' loads in flight per lane group: at these sizes many
+    // waves with few loads each beat fewer waves with more (measured)
+    constexpr int U = (C == 1) ? 2 : 1;
     constexpr int RB = (WAVE / LPR) * U;
     const int64_t nrb = (a.n_out + RB - 1) / RB;
     dim3 grid, block;

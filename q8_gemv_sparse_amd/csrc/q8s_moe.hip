@@ -7,10 +7,11 @@
 // The expert index is read on the device, so the choices never travel to the
 // host; an index outside [0, E) reads nothing and contributes zero.
 //
-// gate-up (one workgroup per 32 hidden outputs of one (row, slot)): each wave
-//   streams gate and up rows side by side against the activation slice in its
-//   registers; the 32 SiLU(g)*u values meet in LDS, where int8 mode also
-//   quantises them as one Q8_0 block (arena.rs fn scratch: hq/hs).
+// gate-up (one workgroup per tile of hidden outputs of one (row, slot)): each
+//   wave streams gate and up rows side by side against the activation slice
+//   in its registers and forms SiLU(g)*u; in int8 mode a tile is one 32-value
+//   block, which the workgroup quantises once into the hidden row's Q8_0 form
+//   (arena.rs fn scratch: hq/hs).
 // down-combine (one workgroup per 8 outputs of one row): waves take
 //   (slot, k-slice) pairs, so all K experts' rows of those outputs stream at
 //   once; the partials meet in LDS and are weighted and summed in slot order.
@@ -21,56 +22,64 @@ namespace q8s {
 
 Q8S_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
 
-constexpr int GU_THREADS = 512;
-constexpr int GU_TILE = 32;
 constexpr int DN_TILE = 8;
 constexpr int MAX_KS = 16;
+constexpr int GU_MAX_KS = 32;
 constexpr int DN_MAX_WAVES = 8;
 
-// Outputs per lane group per step: enough 16-byte loads in flight per lane
-// (8-16) without spilling.  f32 mode holds its converted weights and 16-float
-// activation chunks, so it takes fewer rows at a time than int8 mode.
+// Gate-up launch shape per mode and row cut.  At these sizes the kernels are
+// bound by memory latency more than by bandwidth: many waves with one or two
+// rows' loads in flight each beat fewer waves with more (measured).
+//   f32 : 8 waves, one gate/up pair per lane group (two for short rows);
+//         tiles of 8 (or 16, 32) hidden outputs.
+//   int8: a tile is one 32-value block, so the workgroup also writes the
+//         block's Q8_0 form (the down projection's activation) once, in its
+//         epilogue: 16 waves of 2 pairs (8 of 1 for lane groups of 16); rows
+//         longer than 2048 are cut into 2048-value slices (gu_slices), which
+//         keeps each wave at 8 loads in flight.
 template <int ACT, int LPR, int C>
-constexpr int gu_unroll()
-{
-    if (ACT == 0)
-        return C == 1 ? (LPR == 16 ? 2 : 4) : (C == 2 ? 2 : 1);
-    return C == 1 ? (LPR == 16 ? 2 : 4) : (C == 2 ? 4 : (C == 3 ? 1 : 2));
-}
+struct GuShape {
+    static constexpr int G = WAVE / LPR;
+    static constexpr int NW = ACT == 1 ? (LPR == 64 ? 16 : 8) : 8;
+    static constexpr int U = ACT == 1 ? (LPR == 64 ? 2 : 1) : ((C == 1 && LPR == 64) ? 2 : 1);
+    static constexpr int OPS = G * U;
+    static constexpr int T = NW * OPS;
+    static_assert(QB % T == 0, "a tile divides a 32-value block, so it divides dff");
+    static_assert(ACT == 0 || T == QB, "int8 tiles are whole blocks");
+};
 
+// gate-up: one workgroup per tile of hidden outputs of one (row, slot).  With
+// the row in one slice (ks == 1) each wave finishes its own outputs;
+// otherwise the waves deal out (slice, step) items and the slices' partial
+// sums meet in LDS.
 template <int ACT, int LPR, int C>
-__global__ void __launch_bounds__(GU_THREADS) k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq,
-                                                        const float *__restrict__ xs, const int8_t *__restrict__ Wgq,
-                                                        const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
-                                                        const float *__restrict__ Wus, const int32_t *__restrict__ idx,
-                                                        int d, int dff, int E, int k, int ks, float *__restrict__ h,
-                                                        int8_t *__restrict__ hq, float *__restrict__ hs)
+__global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
+    k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
+              const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
+              const float *__restrict__ Wus, const int32_t *__restrict__ idx, int d, int dff, int E, int k, int ks,
+              float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
 {
-    constexpr int G = WAVE / LPR;
-    constexpr int U = gu_unroll<ACT, LPR, C>();
-    constexpr int OPS = G * U;
-    constexpr int STEPS = GU_TILE / OPS;
-    static_assert(GU_TILE % OPS == 0, "a step covers a divisor of the tile");
-    __shared__ float gp[MAX_KS][GU_TILE];
-    __shared__ float up[MAX_KS][GU_TILE];
+    using S = GuShape<ACT, LPR, C>;
+    constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, NW = S::NW;
+    constexpr int STEPS = T / OPS;
+    __shared__ float gp[GU_MAX_KS][T];
+    __shared__ float up[GU_MAX_KS][T];
+    __shared__ float hv[T];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
-    const int nwaves = blockDim.x >> 6;
-    const int o0 = blockIdx.x * GU_TILE;
+    const int o0 = blockIdx.x * T;
     const int j = blockIdx.y;
     const int64_t row = blockIdx.z;
     const int nch = d >> 4, nb = d >> 5;
     const int e = idx[row * k + j];
     const bool valid = (e >= 0 && e < E);
     const int64_t rbase = (int64_t)(valid ? e : 0) * dff + o0;
+    const int64_t hbase = (row * k + j) * dff + o0;
 
-    for (int item = wid; item < ks * STEPS; item += nwaves) {
+    for (int item = wid; item < ks * STEPS; item += NW) {
         const int s = item / STEPS, st = item % STEPS;
         const int ch0 = s * LPR * C;
         const int sl = min(LPR * C, nch - ch0);
-        XSlice<ACT, C> xv;
-        load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
-                       ACT == 1 ? xs + row * nb : nullptr, ch0, sl, lig);
         RowSlice<C> wg[U], wu[U];
         if (valid) {
 #pragma unroll
@@ -80,6 +89,9 @@ __global__ void __launch_bounds__(GU_THREADS) k_gate_up(const float *__restrict_
                 load_row<LPR, C>(wu[u], Wuq + o * d, Wus + o * nb, ch0, sl, lig);
             }
         }
+        XSlice<ACT, C> xv;
+        load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
+                       ACT == 1 ? xs + row * nb : nullptr, ch0, sl, lig);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             float g = 0.0f, v = 0.0f;
@@ -89,36 +101,53 @@ __global__ void __launch_bounds__(GU_THREADS) k_gate_up(const float *__restrict_
             }
             g = group_sum<LPR>(g);
             v = group_sum<LPR>(v);
+            const int ol = st * OPS + u * G + grp;
             if (lig == 0) {
-                gp[s][st * OPS + u * G + grp] = g;
-                up[s][st * OPS + u * G + grp] = v;
+                if (ks == 1) {
+                    const float r = valid ? silu(g) * v : 0.0f;
+                    if (ACT == 1)
+                        hv[ol] = r;
+                    if (h)
+                        h[hbase + ol] = r;
+                } else {
+                    gp[s][ol] = g;
+                    up[s][ol] = v;
+                }
             }
         }
     }
-    __syncthreads();
-    if (wid != 0)
+    if (ks == 1 && ACT == 0)
         return;
-    // Wave 0 finishes the tile: lane t < 32 owns output o0 + t.
-    const int t = lane & 31;
-    float g = 0.0f, v = 0.0f;
-    for (int s = 0; s < ks; s++) {
-        g += gp[s][t];
-        v += up[s][t];
+    __syncthreads();
+    if (ks > 1) {
+        for (int t = threadIdx.x; t < T; t += blockDim.x) {
+            float g = 0.0f, v = 0.0f;
+            for (int s = 0; s < ks; s++) {
+                g += gp[s][t];
+                v += up[s][t];
+            }
+            const float r = valid ? silu(g) * v : 0.0f;
+            if (ACT == 1)
+                hv[t] = r;
+            if (h)
+                h[hbase + t] = r;
+        }
+        if (ACT == 1)
+            __syncthreads();
     }
-    const float hv = valid ? silu(g) * v : 0.0f;
-    const int64_t hoff = (row * k + j) * dff + o0 + t;
-    if (h && lane < 32)
-        h[hoff] = hv;
-    if (ACT == 1) {
-        float amax = fabsf(hv);
+    if (ACT == 1 && wid == 0) {
+        // the tile is one Q8_0 block of the hidden row: quantise it once
+        const int t = lane & 31;
+        const float v = hv[t];
+        float amax = fabsf(v);
         for (int off = 16; off >= 1; off >>= 1)
             amax = fmaxf(amax, __shfl_xor(amax, off));
         const float dsc = q8_scale(amax);
         const float id = q8_inv(dsc);
         if (lane < 32)
-            hq[hoff] = (int8_t)q8_code(hv, id);
+            hq[hbase + t] = (int8_t)q8_code(v, id);
         if (lane == 0)
-            hs[((row * k + j) * dff + o0) / QB] = dsc;
+            hs[hbase / QB] = dsc;
     }
 }
 
@@ -132,7 +161,7 @@ constexpr int dn_unroll()
 
 template <int ACT, int LPR, int C>
 __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__restrict__ h, const int8_t *__restrict__ hq,
-                                               const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
+                                                              const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
                                                const float *__restrict__ Wds, const int32_t *__restrict__ idx,
                                                const float *__restrict__ wts, int d, int dff, int E, int k, int ks,
                                                float *__restrict__ y)
@@ -159,12 +188,10 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
         const int ch0 = s * LPR * C;
         const int sl = min(LPR * C, nch - ch0);
         const int64_t hrow = (row * k + j) * dff;
-        XSlice<ACT, C> xv;
-        load_x<LPR, C>(xv, ACT == 0 ? h + hrow : nullptr, ACT == 1 ? hq + hrow : nullptr,
-                       ACT == 1 ? hs + hrow / QB : nullptr, ch0, sl, lig);
         const int64_t rbase = (int64_t)(valid ? e : 0) * d + o0;
-        for (int st = 0; st < STEPS; st++) {
-            RowSlice<C> w[UU];
+        // Each step's weight rows are requested before the previous step is
+        // reduced.
+        auto load_step = [&](RowSlice<C>(&w)[UU], int st) {
             if (valid) {
 #pragma unroll
                 for (int u = 0; u < UU; u++) {
@@ -172,6 +199,19 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
                     load_row<LPR, C>(w[u], Wdq + o * dff, Wds + o * nb, ch0, sl, lig);
                 }
             }
+        };
+        // The hidden row's chunks are requested first (they come from cache),
+        // then the weight rows of step 0.
+        XSlice<ACT, C> xv;
+        load_x<LPR, C>(xv, ACT == 0 ? h + hrow : nullptr, ACT == 1 ? hq + hrow : nullptr,
+                       ACT == 1 ? hs + hrow / QB : nullptr, ch0, sl, lig);
+        RowSlice<C> wa[UU], wb[UU];
+        load_step(wa, 0);
+#pragma unroll
+        for (int st = 0; st < STEPS; st++) {
+            if (st + 1 < STEPS)
+                load_step((st & 1) ? wa : wb, st + 1);
+            RowSlice<C>(&w)[UU] = (st & 1) ? wb : wa;
 #pragma unroll
             for (int u = 0; u < UU; u++) {
                 float a = valid ? row_dot(w[u], xv, lig) : 0.0f;
@@ -203,9 +243,10 @@ namespace {
 template <int ACT, int LPR, int C>
 hipError_t gu_go(const MoeArgs &a, int ks, hipStream_t st)
 {
-    dim3 grid((unsigned)(a.dff / GU_TILE), (unsigned)a.k, (unsigned)a.rows);
-    hipLaunchKernelGGL((k_gate_up<ACT, LPR, C>), grid, dim3(GU_THREADS), 0, st, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
-                       a.Wus, a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
+    using S = GuShape<ACT, LPR, C>;
+    dim3 grid((unsigned)(a.dff / S::T), (unsigned)a.k, (unsigned)a.rows);
+    hipLaunchKernelGGL((k_gate_up<ACT, LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq, a.Wgs,
+                       a.Wuq, a.Wus, a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
     return hipGetLastError();
 }
 
@@ -216,7 +257,8 @@ hipError_t dn_go(const MoeArgs &a, int ks, hipStream_t st)
     const int nw = std::min(DN_MAX_WAVES, pairs);
     dim3 grid((unsigned)(a.d / DN_TILE), 1, (unsigned)a.rows);
     hipLaunchKernelGGL((k_down<ACT, LPR, C>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds, a.idx, a.wts,
-                       (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.y);
+                       (int)a.d,
+                       (int)a.dff, (int)a.E, (int)a.k, ks, a.y);
     return hipGetLastError();
 }
 
@@ -253,7 +295,12 @@ struct DN {
 
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st)
 {
-    return a.act == 0 ? by_shape<0, GU>(a, a.d, st) : by_shape<1, GU>(a, a.d, st);
+    if (a.act == 0)
+        return by_shape<0, GU>(a, a.d, st);
+    const int64_t nch = a.d / 16;
+    if (nch > 128)  // int8 rows past 2048: slices of 2048 (lane groups of 64, 2 chunks)
+        return GU<1, 64, 2>::go(a, (int)((nch + 127) / 128), st);
+    return by_shape<1, GU>(a, a.d, st);
 }
 
 size_t down_scratch_bytes(int64_t, int64_t, int64_t) { return 0; }

@@ -42,27 +42,58 @@ Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool lea
         *scale = d;
 }
 
+// SEGS > 0: the row has at most SEGS 2048-value segments, and each thread keeps
+// its sums and weights in registers between the two passes.  SEGS == 0: any
+// length; the second pass re-forms the sums from h and r (the same float32
+// adds, bit for bit).
+template <int SEGS>
 __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__restrict__ h, const float *__restrict__ r,
                                                                  const float *__restrict__ w, int d, float eps,
                                                                  float *__restrict__ sum, float *__restrict__ y,
                                                                  int8_t *__restrict__ yq, float *__restrict__ ys)
 {
+    constexpr int NS = SEGS > 0 ? SEGS : 1;
     __shared__ double wsum[NORM_THREADS / WAVE];
     const int64_t row = blockIdx.x;
     const float *hr = h + row * d;
     const float *rr = r + row * d;
     const int t8 = threadIdx.x * 8;
 
+    f32x4 sv[NS][2], wv[NS][2];
     double ss = 0.0;
-    for (int base = t8; base < d; base += NORM_SEG) {
-        const f32x4 a0 = ldf4(hr + base), a1 = ldf4(hr + base + 4);
-        const f32x4 b0 = ldf4(rr + base), b1 = ldf4(rr + base + 4);
-        const f32x4 s0 = a0 + b0, s1 = a1 + b1;
-        *reinterpret_cast<f32x4 *>(sum + row * d + base) = s0;
-        *reinterpret_cast<f32x4 *>(sum + row * d + base + 4) = s1;
+    if (SEGS > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            ss += (double)s0[i] * (double)s0[i] + (double)s1[i] * (double)s1[i];
+        for (int g = 0; g < NS; g++) {
+            const int base = t8 + g * NORM_SEG;
+            if (base < d) {
+                const f32x4 a0 = ldf4(hr + base), a1 = ldf4(hr + base + 4);
+                const f32x4 b0 = ldf4(rr + base), b1 = ldf4(rr + base + 4);
+                wv[g][0] = ldf4(w + base);
+                wv[g][1] = ldf4(w + base + 4);
+                sv[g][0] = a0 + b0;
+                sv[g][1] = a1 + b1;
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < NS; g++) {
+            const int base = t8 + g * NORM_SEG;
+            if (base < d) {
+                *reinterpret_cast<f32x4 *>(sum + row * d + base) = sv[g][0];
+                *reinterpret_cast<f32x4 *>(sum + row * d + base + 4) = sv[g][1];
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    ss += (double)sv[g][0][i] * (double)sv[g][0][i] + (double)sv[g][1][i] * (double)sv[g][1][i];
+            }
+        }
+    } else {
+        for (int base = t8; base < d; base += NORM_SEG) {
+            const f32x4 s0 = ldf4(hr + base) + ldf4(rr + base), s1 = ldf4(hr + base + 4) + ldf4(rr + base + 4);
+            *reinterpret_cast<f32x4 *>(sum + row * d + base) = s0;
+            *reinterpret_cast<f32x4 *>(sum + row * d + base + 4) = s1;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                ss += (double)s0[i] * (double)s0[i] + (double)s1[i] * (double)s1[i];
+        }
     }
     ss = wave_sum_f64(ss);
     if ((threadIdx.x & 63) == 0)
@@ -74,12 +105,22 @@ __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__
         tot += wsum[i];
     const double inv = 1.0 / sqrt(tot / (double)d + (double)eps);
 
-    for (int base = t8; base < d; base += NORM_SEG) {
-        // The sum again from h and r: the same float32 adds, bit for bit.
-        const f32x4 a0 = ldf4(hr + base), a1 = ldf4(hr + base + 4);
-        const f32x4 b0 = ldf4(rr + base), b1 = ldf4(rr + base + 4);
-        const f32x4 s0 = a0 + b0, s1 = a1 + b1;
-        const f32x4 w0 = ldf4(w + base), w1 = ldf4(w + base + 4);
+    for (int g = 0; SEGS > 0 ? g < NS : true; g++) {
+        const int base = t8 + g * NORM_SEG;
+        if (base >= d)
+            break;
+        f32x4 s0, s1, w0, w1;
+        if (SEGS > 0) {
+            s0 = sv[g][0];
+            s1 = sv[g][1];
+            w0 = wv[g][0];
+            w1 = wv[g][1];
+        } else {
+            s0 = ldf4(hr + base) + ldf4(rr + base);
+            s1 = ldf4(hr + base + 4) + ldf4(rr + base + 4);
+            w0 = ldf4(w + base);
+            w1 = ldf4(w + base + 4);
+        }
         float v[8];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -120,8 +161,16 @@ hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, 
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               float *sum, float *y, int8_t *yq, float *ys, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_add_rmsnorm_q8, dim3((unsigned)rows), dim3(NORM_THREADS), 0, st, h, r, w, (int)d, eps, sum, y,
-                       yq, ys);
+    const int segs = (int)((d + NORM_SEG - 1) / NORM_SEG);
+    const dim3 grid((unsigned)rows), block(NORM_THREADS);
+    if (segs <= 1)
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<1>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+    else if (segs <= 2)
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<2>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+    else if (segs <= 4)
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<4>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+    else
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<0>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
     return hipGetLastError();
 }
 

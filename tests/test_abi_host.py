@@ -88,7 +88,7 @@ def route(rows=1, d=64, E=8, k=2, sb=None, scratch=J, x=A, Wr=B, idx=C, wts=D):
 
 
 def test_route_refusals_and_scratch():
-    assert q8.q8s_scratch_bytes(q8.FN_ROUTE, 1, 2048, 768, 128, 8) >= 128 * 8 + 4
+    assert q8.q8s_scratch_bytes(q8.FN_ROUTE, 1, 2048, 768, 128, 8) >= 128 * 8  # the f64 logits
     assert q8.q8s_scratch_bytes(99, 1, 2048, 768, 128, 8) == 0
     assert route(k=0) == -1 and "1 <= k <= E" in _err()
     assert route(k=9) == -1
@@ -108,6 +108,7 @@ def gate_up(act=0, rows=1, d=64, dff=64, E=4, k=2, x=A, xq=A, xs=B, h=J, hq=H, h
 def test_gate_up_refusals():
     assert gate_up(dff=48) == -1 and "dff" in _err()
     assert gate_up(k=5) == -1
+    assert gate_up(act=1, xq=None) == -1 and "`xq` is null" in _err()
     assert gate_up(act=1, hq=None) == -1 and "`hq` is null" in _err()
     assert gate_up(act=0, h=None) == -1 and "`h` is null" in _err()
     assert gate_up(act=2) == -2
@@ -122,3 +123,5 @@ def test_down_refusals():
         assert r == -4 and "scratch" in _err()
     r = LIB.moe_down_combine(A, None, None, B, C, D, F, 1, 64, 64, 4, 2, A, 0, None, 0, None)
     assert r == -1 and "overlaps" in _err()
+    r = LIB.moe_down_combine(None, A, None, B, C, D, F, 1, 64, 64, 4, 2, G, 1, None, 0, None)
+    assert r == -1 and "`hs` is null" in _err()
