@@ -141,15 +141,13 @@ const char *q8s_version(void) { return "q8s 0.1 gfx950"; }
 
 size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
 {
-    (void)dff;
-    (void)act;
     if (rows <= 0 || E <= 0 || k <= 0 || d <= 0)
         return 0;
     switch (fn) {
     case Q8S_FN_ROUTE:
         return q8s::route_scratch_bytes(rows, E);
     case Q8S_FN_DOWN:
-        return q8s::down_scratch_bytes(rows, d, k);
+        return q8s::down_scratch_bytes(rows, d, dff, k, act);
     default:
         return 0;
     }
@@ -316,7 +314,7 @@ int moe_down_combine(const float *h, const int8_t *hq, const float *hs, const in
     std::vector<Span> outs = {{y, (size_t)(rows * d) * 4, "y"}};
     if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
         return rc;
-    const size_t need = q8s::down_scratch_bytes(rows, d, k);
+    const size_t need = q8s::down_scratch_bytes(rows, d, dff, k, act);
     if (need) {
         if (!scratch || scratch_bytes < need)
             return fail(Q8S_ESCRATCH, "%s: scratch of %zu bytes given, %zu needed (per-choice results)", fn,

@@ -313,4 +313,47 @@ Q8S_DEV float row_dot(const RowSlice<C> &w, const XSlice<1, C> &x, int lig)
     return acc;
 }
 
+// ---------------------------------------------------------------------------
+// the MoE block's pieces shared by its decode and chunk kernels
+
+Q8S_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// Decode gate-up launch shape per mode and row cut.  At these sizes the kernels are
+// bound by memory latency more than by bandwidth: many waves with one or two
+// rows' loads in flight each beat fewer waves with more (measured).
+//   f32 : 8 waves, one gate/up pair per lane group (two for short rows);
+//         tiles of 8 (or 16, 32) hidden outputs.
+//   int8: a tile is one 32-value block, so the workgroup also writes the
+//         block's Q8_0 form (the down projection's activation) once, in its
+//         epilogue: 16 waves of 2 pairs (8 of 1 for lane groups of 16); rows
+//         longer than 2048 are cut into 2048-value slices (gu_slices), which
+//         keeps each wave at 8 loads in flight.
+template <int ACT, int LPR, int C>
+struct GuShape {
+    static constexpr int G = WAVE / LPR;
+    static constexpr int NW = ACT == 1 ? (LPR == 64 ? 16 : 8) : 8;
+    static constexpr int U = ACT == 1 ? (LPR == 64 ? 2 : 1) : ((C == 1 && LPR == 64) ? 2 : 1);
+    static constexpr int OPS = G * U;
+    static constexpr int T = NW * OPS;
+    static_assert(QB % T == 0, "a tile divides a 32-value block, so it divides dff");
+    static_assert(ACT == 0 || T == QB, "int8 tiles are whole blocks");
+};
+
+// Chunk gate-up shape (int8, rows of up to two chunks a lane): a tile is one
+// or two 32-value blocks of hidden outputs (the last tile of a row may hold
+// fewer); each of NW waves holds its U gate/up pairs and CG choices'
+// activation slices in registers, as many as fit the register budget.  The
+// more rows a workgroup streams, the better its gather of the expert's choices
+// is amortised.
+template <int LPR, int C>
+struct ChunkGuShape {
+    static constexpr int G = WAVE / LPR;
+    static constexpr int NW = (LPR == 64 && C == 2) ? 16 : 8;
+    static constexpr int U = LPR == 16 ? 2 : (C == 1 ? 8 : 2);
+    static constexpr int CG = (LPR == 64 && C >= 2) ? 2 : 4;
+    static constexpr int OPS = G * U;
+    static constexpr int T = NW * OPS;
+    static_assert(T % QB == 0, "a tile is whole Q8_0 blocks of the hidden row");
+};
+
 } // namespace q8s

@@ -86,8 +86,15 @@ struct MoeArgs {
     void *scratch;
 };
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st);
-size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t k);
+size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t k, int act);
 hipError_t down_launch(const MoeArgs &a, hipStream_t st);
+
+// a chunk's mixture (rows > 1, int8 activations): choices grouped by expert,
+// for rows one slice of a wave covers (d, dff <= 4096)
+bool chunk_supported(int64_t d, int64_t dff);
+hipError_t chunk_gate_up_launch(const MoeArgs &a, hipStream_t st);
+size_t chunk_down_scratch_bytes(int64_t rows, int64_t d, int64_t k);
+hipError_t chunk_down_launch(const MoeArgs &a, hipStream_t st);
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 

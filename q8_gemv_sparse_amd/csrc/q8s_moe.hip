@@ -12,6 +12,9 @@
 //   in its registers and forms SiLU(g)*u; in int8 mode a tile is one 32-value
 //   block, which the workgroup quantises once into the hidden row's Q8_0 form
 //   (arena.rs fn scratch: hq/hs).
+// These kernels serve one row at a time (a batch of rows in f32 numerics runs
+// them row by row); a chunk of rows in int8 numerics goes to the grouped
+// kernels of q8s_moe_chunk.hip.
 // down-combine (one workgroup per 8 outputs of one row): waves take
 //   (slot, k-slice) pairs, so all K experts' rows of those outputs stream at
 //   once; the partials meet in LDS and are weighted and summed in slot order.
@@ -20,33 +23,11 @@
 
 namespace q8s {
 
-Q8S_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
 
 constexpr int DN_TILE = 8;
 constexpr int MAX_KS = 16;
 constexpr int GU_MAX_KS = 32;
 constexpr int DN_MAX_WAVES = 8;
-
-// Gate-up launch shape per mode and row cut.  At these sizes the kernels are
-// bound by memory latency more than by bandwidth: many waves with one or two
-// rows' loads in flight each beat fewer waves with more (measured).
-//   f32 : 8 waves, one gate/up pair per lane group (two for short rows);
-//         tiles of 8 (or 16, 32) hidden outputs.
-//   int8: a tile is one 32-value block, so the workgroup also writes the
-//         block's Q8_0 form (the down projection's activation) once, in its
-//         epilogue: 16 waves of 2 pairs (8 of 1 for lane groups of 16); rows
-//         longer than 2048 are cut into 2048-value slices (gu_slices), which
-//         keeps each wave at 8 loads in flight.
-template <int ACT, int LPR, int C>
-struct GuShape {
-    static constexpr int G = WAVE / LPR;
-    static constexpr int NW = ACT == 1 ? (LPR == 64 ? 16 : 8) : 8;
-    static constexpr int U = ACT == 1 ? (LPR == 64 ? 2 : 1) : ((C == 1 && LPR == 64) ? 2 : 1);
-    static constexpr int OPS = G * U;
-    static constexpr int T = NW * OPS;
-    static_assert(QB % T == 0, "a tile divides a 32-value block, so it divides dff");
-    static_assert(ACT == 0 || T == QB, "int8 tiles are whole blocks");
-};
 
 // gate-up: one workgroup per tile of hidden outputs of one (row, slot).  With
 // the row in one slice (ks == 1) each wave finishes its own outputs;
@@ -295,6 +276,8 @@ struct DN {
 
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st)
 {
+    if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
+        return chunk_gate_up_launch(a, st);
     if (a.act == 0)
         return by_shape<0, GU>(a, a.d, st);
     const int64_t nch = a.d / 16;
@@ -303,10 +286,15 @@ hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st)
     return by_shape<1, GU>(a, a.d, st);
 }
 
-size_t down_scratch_bytes(int64_t, int64_t, int64_t) { return 0; }
+size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t k, int act)
+{
+    return (act == 1 && rows > 1 && chunk_supported(d, dff)) ? chunk_down_scratch_bytes(rows, d, k) : 0;
+}
 
 hipError_t down_launch(const MoeArgs &a, hipStream_t st)
 {
+    if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
+        return chunk_down_launch(a, st);
     return a.act == 0 ? by_shape<0, DN>(a, a.dff, st) : by_shape<1, DN>(a, a.dff, st);
 }
 

@@ -117,10 +117,13 @@ def test_gate_up_refusals():
 
 def test_down_refusals():
     assert q8.q8s_scratch_bytes(q8.FN_DOWN, 1, 64, 64, 4, 2) == 0  # a decode row needs none
-    need = q8.q8s_scratch_bytes(q8.FN_DOWN, 4, 64, 64, 4, 2)
-    if need:
-        r = LIB.moe_down_combine(A, None, None, B, C, D, F, 4, 64, 64, 4, 2, G, 0, None, 0, None)
-        assert r == -4 and "scratch" in _err()
+    assert q8.q8s_scratch_bytes(q8.FN_DOWN, 4, 64, 64, 4, 2, q8.ACT_F32) == 0  # f32 rows run one by one
+    need = q8.q8s_scratch_bytes(q8.FN_DOWN, 4, 64, 64, 4, 2, q8.ACT_INT8)
+    assert need >= 4 * 2 * 64 * 4  # a chunk's per-choice results
+    r = LIB.moe_down_combine(None, A, B, C, D, F, J, 4, 64, 64, 4, 2, G, 1, None, 0, None)
+    assert r == -4 and "scratch" in _err()
+    r = LIB.moe_down_combine(None, A, B, C, D, F, J, 4, 64, 64, 4, 2, G, 1, 0x30000008, need, None)
+    assert r == -3 and "256-byte" in _err()
     r = LIB.moe_down_combine(A, None, None, B, C, D, F, 1, 64, 64, 4, 2, A, 0, None, 0, None)
     assert r == -1 and "overlaps" in _err()
     r = LIB.moe_down_combine(None, A, None, B, C, D, F, 1, 64, 64, 4, 2, G, 1, None, 0, None)

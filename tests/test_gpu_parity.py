@@ -325,6 +325,46 @@ def test_moe_invalid_expert_index_contributes_zero():
     assert not host(y).any()
 
 
+@pytest.mark.parametrize("rows,E,k", [(150, 2, 1), (200, 3, 3), (70, 5, 2)])
+def test_chunk_many_choices_per_expert(rows, E, k):
+    # more than 64 choices of one expert: the grouped kernels take several
+    # passes over the expert's list
+    banner("chunk passes rows=%d E=%d k=%d" % (rows, E, k))
+    m = synthetic.moe_inputs(12, 128, 96, E, k, rows)
+    ridx, rw, rh, ry = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, m.k, 1)
+    idx, wts, h, y = run_moe_gpu(m, 1)
+    assert np.array_equal(idx, ridx)
+    assert rel_err(h, rh) <= TOL_I8
+    for r in range(rows):
+        assert rel_err(y[r], ry[r]) <= TOL_I8, r
+
+
+def test_chunk_invalid_expert_index():
+    banner("chunk invalid idx")
+    m = synthetic.moe_inputs(13, 64, 64, 4, 2, 3)
+    Wgq, Wgs, Wuq, Wus, Wdq, Wds = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds))
+    xq, xs = q8.q8_quantize_rows(dev(m.x))
+    idx = dev(np.array([[-1, 1], [9, 4], [2, 0]], np.int32))
+    wts = dev(np.full((3, 2), 0.5, np.float32))
+    h, hq, hs = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, 4, xq=xq, xs=xs, act=q8.ACT_INT8)
+    y = q8.moe_down_combine(Wdq, Wds, idx, wts, 4, hq=hq, hs=hs, act=q8.ACT_INT8)
+    h, hq, y = host(h), host(hq), host(y)
+    assert not h[0, 0].any() and not h[1].any() and not hq[1].any()
+    assert h[0, 1].any() and h[2].any()
+    assert not y[1].any()
+    # row 2 (choices 2 and 0, weights 0.5): the oracle's pieces, expert by
+    # expert -- int8 gate/up dots over the stacked rows, h in float32, h
+    # quantised, int8 down dots
+    xr = m.x[2:3]
+    g, u = (oracle.gemv_i8(W, S, *oracle.quantize(xr)) for W, S in ((m.Wgq, m.Wgs), (m.Wuq, m.Wus)))
+    hid = (g / (1 + np.exp(-g)) * u).astype(np.float32).reshape(4, 64)
+    yref = np.zeros(64)
+    for e in (2, 0):
+        hqq, hss = oracle.quantize(hid[e:e + 1])
+        yref += 0.5 * oracle.gemv_i8(m.Wdq[e * 64:(e + 1) * 64], m.Wds[e * 64:(e + 1) * 64], hqq, hss)[0]
+    assert rel_err(y[2], yref) <= TOL_I8
+
+
 def test_moe_deterministic():
     banner("moe determinism")
     m = synthetic.moe_inputs(11, 2048, 768, 32, 8, 1)
