@@ -44,6 +44,58 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# dominant kernel of each workload kind, and the sources that define it
+DOMINANT = {
+    "moe": ("k_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
+    "chunk": ("k_chunk_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe_chunk.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
+    "norm_gemv": ("k_gemv_rows", ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
+}
+
+
+def counters_path(kernel, workload, act):
+    return os.path.join(ROOT, "profiles", "%s_%s_%s_counters.txt" % (kernel, workload, act))
+
+
+def summarize_counters(args):
+    """Turns two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE; counter_collection.csv files, KiB per dispatch) into the HBM
+    bytes one launch of the workload's dominant kernel moves.  Each counter is
+    scaled by what it reads for the run's plain device copy of known size
+    (--calib-copy-mib): the last copy dispatch of that size."""
+    import csv
+    import re
+    import synthetic
+    kind = synthetic.CONFIGS[args.workload]["kind"]
+    kernel, srcs = DOMINANT[kind]
+    calib = args.calib_copy_mib * 1024  # KiB moved each way by the copy
+    run = ("python3 bench.py --workload %s --act %s --no-graph --steps 28 --warmup 14 --kernel-launches 14 "
+           "--no-cpu --calib-copy-mib %d" % (args.workload, args.act, args.calib_copy_mib))
+    out = {"kernel": kernel, "workload": args.workload, "act": args.act,
+           "source_digest": src_digest(*srcs), "calib_copy_kib": calib,
+           "commands": ["rocprofv3 --pmc %s -f csv -d <out> -o run -- %s" % (c, run)
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")] +
+                       ["python3 bench.py --workload %s --act %s --calib-copy-mib %d --summarize-counters "
+                        "<FETCH_SIZE counter_collection.csv> <WRITE_SIZE counter_collection.csv>"
+                        % (args.workload, args.act, args.calib_copy_mib)]}
+    for counter, path in (("FETCH_SIZE", args.summarize_counters[0]), ("WRITE_SIZE", args.summarize_counters[1])):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        mine = [float(r["Counter_Value"]) for r in rows if re.search(r"q8s::%s\b" % kernel, r["Kernel_Name"])]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        # the calibration copy is the run's last copy dispatch
+        ref = copies[-1]
+        scale = calib / ref
+        out[counter] = {"dispatches": len(mine), "kib_per_dispatch": sum(mine) / len(mine),
+                        "copy_kib": ref, "scale": scale,
+                        "scaled_bytes_per_dispatch": sum(mine) / len(mine) * scale * 1024}
+    out["hbm_bytes_per_launch"] = int(out["FETCH_SIZE"]["scaled_bytes_per_dispatch"] +
+                                      out["WRITE_SIZE"]["scaled_bytes_per_dispatch"])
+    dst = counters_path(kernel, args.workload, args.act)
+    with open(dst, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -55,6 +107,11 @@ def parse():
     p.add_argument("--kernel-launches", type=int, default=400, help="eager launches timed for the dominant kernel")
     p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    p.add_argument("--no-graph", action="store_true",
+                   help="launch every step eagerly instead of replaying a captured graph (for counter runs, which "
+                        "profile each dispatch)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU run: summarise two counter passes of this script into the traffic file")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     return p.parse_args()
@@ -408,6 +465,9 @@ def make_workload(name, act, copies):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
@@ -422,38 +482,46 @@ def main():
 
     stream = torch.cuda.Stream()
     C = wl.copies
-    # capture a graph of C consecutive steps, one per weight copy
-    g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
-        for c in range(C):  # eager warm-up on the capture stream
+        for c in range(C):  # eager warm-up on the timing stream
             wl.step(c)
     torch.cuda.synchronize()
-    with torch.cuda.graph(g, stream=stream):
-        for c in range(C):
-            wl.step(c)
-    torch.cuda.synchronize()
+    if args.no_graph:
+        def run_steps(reps):
+            for _ in range(reps):
+                for c in range(C):
+                    wl.step(c)
+    else:
+        # capture a graph of C consecutive steps, one per weight copy
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(C):
+                wl.step(c)
+        torch.cuda.synchronize()
+
+        def run_steps(reps):
+            for _ in range(reps):
+                g.replay()
     replays = max(1, -(-args.steps // C))
     steps = replays * C
     wreps = -(-args.warmup // C) if args.warmup > 0 else 0
     with torch.cuda.stream(stream):
-        for _ in range(wreps):
-            g.replay()
+        run_steps(wreps)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     with torch.cuda.stream(stream):
         e0.record(stream)
-        for _ in range(replays):
-            g.replay()
+        run_steps(replays)
         e1.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1)
     ms_per_step = ms / steps
-    # the graph's result equals an eager step's
+    # the replayed result equals an eager step's
     with torch.cuda.stream(stream):
-        g.replay()
+        run_steps(1)
     torch.cuda.synchronize()
     graph_out = wl.out.clone()
     with torch.cuda.stream(stream):
@@ -464,19 +532,27 @@ def main():
     # the dominant kernel: a graph of its launches on each copy (the routing
     # each copy's last step left in place), replayed back to back; HIP events
     # on the replay stream around the replays
-    g2 = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g2, stream=stream):
-        for c in range(C):
-            wl.launch_dominant(c)
+    if args.no_graph:
+        def run_dom():
+            for c in range(C):
+                wl.launch_dominant(c)
+    else:
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=stream):
+            for c in range(C):
+                wl.launch_dominant(c)
+
+        def run_dom():
+            g2.replay()
     reps2 = max(1, -(-args.kernel_launches // C))
     with torch.cuda.stream(stream):
-        g2.replay()
+        run_dom()
     torch.cuda.synchronize()
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         k0.record(stream)
         for _ in range(reps2):
-            g2.replay()
+            run_dom()
         k1.record(stream)
     torch.cuda.synchronize()
     kms = k0.elapsed_time(k1) / (reps2 * C)
@@ -492,7 +568,7 @@ def main():
         log("[bench] calibration copy: %d MiB" % args.calib_copy_mib)
 
     traffic = None
-    cfile = os.path.join(ROOT, "profiles", "%s_%s_%s_counters.json" % (wl.dominant, wl.name, args.act))
+    cfile = counters_path(wl.dominant, wl.name, args.act)
     if os.path.exists(cfile):
         with open(cfile) as fh:
             cnt = json.load(fh)
@@ -526,7 +602,8 @@ def main():
             "us_per_step": round(ms_per_step * 1e3, 3),
             "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
             "weight_copies": C,
-            "timing": "HIP graph of %d steps replayed %d times" % (C, replays),
+            "timing": ("eager launches, %d rounds of %d steps" if args.no_graph else
+                       "HIP graph of %d steps replayed %d times") % ((replays, C) if args.no_graph else (C, replays)),
             "verified": ver,
             "graph_equals_eager": graph_matches,
         },
