@@ -5,7 +5,10 @@
 
 A step is one pass of the hot path over one batch of synthetic input.  The
 default workload is the batch-1 MoE FFN block at the Qwen3-30B-A3B-like shape
-(d 2048, dff 768, 128 experts, top 8), fed by its producer:
+(d 2048, dff 768, 128 experts, top 8), fed by its producer, as one
+moe_ffn_block call a step (add + norm fused into the router's logits, the
+top-K taken inside the gate-up launch, then down-combine); --separate runs
+the same block as the separate calls
 
     add_rmsnorm_q8 -> moe_route_topk -> moe_gate_up -> moe_down_combine
 
@@ -46,7 +49,7 @@ def log(*a):
 
 # dominant kernel of each workload kind, and the sources that define it
 DOMINANT = {
-    "moe": ("k_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
+    "moe": ("k_route_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
     "chunk": ("k_chunk_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe_chunk.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
     "norm_gemv": ("k_gemv_rows", ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
 }
@@ -110,6 +113,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true",
                    help="launch every step eagerly instead of replaying a captured graph (for counter runs, which "
                         "profile each dispatch)")
+    p.add_argument("--separate", action="store_true",
+                   help="MoE workloads: the five separate calls a step instead of one moe_ffn_block call")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU run: summarise two counter passes of this script into the traffic file")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -140,6 +145,10 @@ class Workload:
     def launch_dominant(self, c):
         raise NotImplementedError
 
+    def prepare_dominant(self):
+        """Anything the dominant kernel's launches read that the steps leave
+        elsewhere (called once before they are captured)."""
+
 
 def _copies(step_bytes, want):
     """Weight copies to rotate so that more than two MALLs' worth of weight
@@ -150,12 +159,15 @@ def _copies(step_bytes, want):
 
 
 class MoeBlock(Workload):
-    """add_rmsnorm_q8 -> route -> gate-up -> down-combine, `rows` rows."""
+    """The mixture block of a layer, `rows` rows: add + norm -> router + top-K
+    -> gate-up -> down-combine.  By default one moe_ffn_block call a step
+    (three launches: norm fused into the router, top-K inside gate-up,
+    down-combine); with separate=True the five calls add_rmsnorm_q8,
+    moe_route_topk, moe_gate_up, moe_down_combine (five launches)."""
 
-    dominant = "k_gate_up"
     dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
 
-    def __init__(self, name, cfg, act, copies, rows=1, pool=64):
+    def __init__(self, name, cfg, act, copies, rows=1, pool=64, separate=False):
         import numpy as np
         import torch
 
@@ -163,6 +175,8 @@ class MoeBlock(Workload):
         import synthetic
         self.q8, self.torch, self.np = q8, torch, np
         self.name, self.act = name, act
+        self.separate = separate
+        self.dominant = "k_gate_up" if separate else "k_route_gate_up"
         d, dff, E, k = cfg["d"], cfg["dff"], cfg["E"], cfg["k"]
         self.d, self.dff, self.E, self.k, self.rows = d, dff, E, k, rows
         t0 = time.time()
@@ -199,6 +213,10 @@ class MoeBlock(Workload):
                                     device="cuda")
         dn = q8.q8s_scratch_bytes(q8.FN_DOWN, rows, d, dff, E, k)
         self.dscratch = torch.zeros(dn, dtype=torch.uint8, device="cuda") if dn else None
+        a = q8.ACT_INT8 if act == "int8" else q8.ACT_F32
+        self.bscratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, a), dtype=torch.uint8,
+                                    device="cuda")
+        self.logits = [z(rows, E, dt=torch.float64) for _ in range(self.copies)]
         torch.cuda.synchronize()
         log("[bench] %s: %d weight copies of %.1f MB on the device" % (name, self.copies, self.bytes_all / 1e6))
 
@@ -208,10 +226,14 @@ class MoeBlock(Workload):
         W = self.W[c % self.copies]
         i = c % self.pool
         a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+        if not self.separate:
+            q8.moe_ffn_block(self.h[i], self.r[i], self.w, 1e-6, *W, self.k, act=a, sum=self.sum, idx=idx, wts=wts,
+                             out=self.out, scratch=self.bscratch)
+            return
         q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y,
                           yq=self.xq if a == q8.ACT_INT8 else None, ys=self.xs if a == q8.ACT_INT8 else None,
                           want_q8=(a == q8.ACT_INT8))
-        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
         q8.moe_route_topk(self.y, W[0], self.k, idx=idx, wts=wts, scratch=self.rscratch)
         self._gate_up(c, a)
         if a == q8.ACT_INT8:
@@ -230,8 +252,32 @@ class MoeBlock(Workload):
         else:
             q8.moe_gate_up(W[1], W[2], W[3], W[4], idx, self.E, x=self.y, h=self.hf, act=a)
 
+    def prepare_dominant(self):
+        """The fused gate-up reads router logits: form each copy's from its
+        own input row (as its steps do), so its choices rotate like theirs."""
+        if self.separate:
+            return
+        q8 = self.q8
+        for c in range(self.copies):
+            i = c % self.pool
+            q8.add_rmsnorm_router(self.h[i], self.r[i], self.w, 1e-6, self.W[c][0], sum=self.sum, x=self.y,
+                                  xq=self.xq, xs=self.xs, logits=self.logits[c], want_q8=True)
+        self.torch.cuda.synchronize()
+
     def launch_dominant(self, c):
-        self._gate_up(c, self.q8.ACT_INT8 if self.act == "int8" else self.q8.ACT_F32)
+        q8 = self.q8
+        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        if self.separate:
+            self._gate_up(c, a)
+            return
+        W = self.W[c % self.copies]
+        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+        if a == q8.ACT_INT8:
+            q8.moe_topk_gate_up(self.logits[c % self.copies], W[1], W[2], W[3], W[4], self.k, xq=self.xq, xs=self.xs,
+                                idx=idx, wts=wts, hq=self.hq, hs=self.hs, act=a, want_h=False)
+        else:
+            q8.moe_topk_gate_up(self.logits[c % self.copies], W[1], W[2], W[3], W[4], self.k, x=self.y, idx=idx,
+                                wts=wts, h=self.hf, act=a)
 
     def distinct_experts(self, c):
         """Experts chosen by copy c's last route (for the bytes a chunk reads)."""
@@ -448,11 +494,11 @@ class ChunkBlock(MoeBlock):
         return el / n, "%d chunks of %d rows, %.1f s" % (n, self.rows, el)
 
 
-def make_workload(name, act, copies):
+def make_workload(name, act, copies, separate=False):
     import synthetic
     cfg = synthetic.CONFIGS[name]
     if cfg["kind"] == "moe":
-        return MoeBlock(name, cfg, act, copies)
+        return MoeBlock(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "norm_gemv":
         return NormGemv(name, cfg, act, copies)
     if cfg["kind"] == "chunk":
@@ -476,7 +522,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
-    wl = make_workload(args.workload, args.act, args.copies)
+    wl = make_workload(args.workload, args.act, args.copies, args.separate)
     ver = wl.verify()
     log("[bench] verify against the oracle:", ver)
 
@@ -532,6 +578,7 @@ def main():
     # the dominant kernel: a graph of its launches on each copy (the routing
     # each copy's last step left in place), replayed back to back; HIP events
     # on the replay stream around the replays
+    wl.prepare_dominant()
     if args.no_graph:
         def run_dom():
             for c in range(C):

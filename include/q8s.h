@@ -77,6 +77,7 @@ extern "C" {
 /* Ids of the calls that take scratch, for q8s_scratch_bytes. */
 #define Q8S_FN_ROUTE 1
 #define Q8S_FN_DOWN 2
+#define Q8S_FN_BLOCK 3
 
 #define Q8S_MAX_K 32
 #define Q8S_MAX_E 8192
@@ -92,7 +93,7 @@ extern "C" {
  * [m, n_in] / f32 [m, n_in/32] (INT8; NULL otherwise).  y: device f32
  * [m, n_out], written whole.  m >= 1.  Each weight row is read from HBM once
  * per call for m <= 4 (register path) and for any m in INT8 mode (matrix-core
- * path for m >= 16).  Limits: n_in <= 65536.
+ * path for m >= 5).  Limits: n_in <= 65536.
  */
 Q8S_API int q8_gemv(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in,
             const float *x, const int8_t *xq, const float *xs, int64_t m,
@@ -183,9 +184,77 @@ Q8S_API int moe_down_combine(const float *h, const int8_t *hq, const float *hs,
                      float *y, int act, void *scratch, size_t scratch_bytes, void *stream);
 
 /*
- * q8s_scratch_bytes -- bytes of scratch the call `fn` (Q8S_FN_ROUTE or
- * Q8S_FN_DOWN) needs for these sizes; 0 for a call that needs none, or for an
- * unknown fn.
+ * add_rmsnorm_router -- add_rmsnorm_q8 with the mixture's router fused in
+ * (forward_shim.rs module doc: the norm as one row kernel writing the sum;
+ * fn emit_moe_forward: the router over the normed row):
+ *   sum, x (and/or xq, xs) exactly as add_rmsnorm_q8 writes them;
+ *   logits[r][e] = sum_t Wr[e][t] * x[r][t]   (double sums)
+ * One workgroup per (expert, row) forms the whole normed row itself, so no
+ * launch waits for a norm launch.  h, r: device f32 [rows, d]; w: device f32
+ * [d]; Wr: device f32 [E, d]; sum: device f32 [rows, d]; x: device f32
+ * [rows, d] or NULL; xq/xs: device int8 [rows, d] and f32 [rows, d/32], both
+ * or neither; at least one of x, xq.  logits: device double [rows, E] (16-byte
+ * aligned).  Limits: d <= 8192 (Q8S_EUNSUPPORTED beyond), E <= 8192.
+ */
+Q8S_API int add_rmsnorm_router(const float *h, const float *r, const float *w, float eps,
+                       const float *Wr, int64_t rows, int64_t d, int64_t E, float *sum,
+                       float *x, int8_t *xq, float *xs, double *logits, void *stream);
+
+/*
+ * moe_topk_gate_up -- moe_gate_up that takes each row's top-K from the
+ * router logits itself (fn emit_moe_forward: softmax, keep K, renormalise):
+ *   idx[r], wts[r] = the K largest logits[r] (ties to the lower index, in rank
+ *                    order) and their renormalised softmax weights, exactly
+ *                    as moe_route_topk forms them from the same logits;
+ *   h (and hq/hs)  = as moe_gate_up with those choices.
+ * Every gate-up workgroup ranks the row's E logits in LDS, so the choices
+ * need no launch of their own.  logits: device double [rows, E] (as
+ * add_rmsnorm_router writes them).  Other arguments as moe_gate_up; idx:
+ * device int32 [rows, k] and wts: device f32 [rows, k] are outputs here.
+ * Rows run one by one (a chunk of rows in INT8 mode reads each expert once
+ * per row here; moe_gate_up groups them).  Limits: E <= 256
+ * (Q8S_EUNSUPPORTED beyond), k <= min(32, E).
+ */
+Q8S_API int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, const float *xs,
+                     const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                     int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
+                     int32_t *idx, float *wts, float *h, int8_t *hq, float *hs, int act, void *stream);
+
+/*
+ * moe_ffn_block -- the whole mixture block of one layer as one call: the
+ * residual add + RMSNorm row kernel feeding the mixture (forward_shim.rs
+ * module doc), then fn emit_moe_forward's router, top-K, gate-up + SiLU and
+ * down-combine (the mixture linked as one launch unit: lane_link.rs fn prim,
+ * Moe arm).  It computes, for each row r,
+ *   sum[r] = h[r] + r[r];  x = RMSNorm(sum[r]) * w       (as add_rmsnorm_q8)
+ *   idx[r], wts[r] = top-K of the router over x          (as moe_route_topk)
+ *   out[r] = sum_j wts[r][j] * down_e(SiLU(gate_e x) * up_e x), e = idx[r][j]
+ *                                                        (as moe_gate_up then
+ *                                                         moe_down_combine)
+ * with the same numerics as that sequence of calls in mode `act` (INT8: x and
+ * each hidden row in Q8_0 form, exact int32 block dots; the router always
+ * reads f32 x).  h, r: device f32 [rows, d]; w: device f32 [d]; Wr: device
+ * f32 [E, d]; gate/up/down: as moe_gate_up and moe_down_combine.  Outputs:
+ * sum (the residual stream, f32 [rows, d]), idx (int32 [rows, k]), wts (f32
+ * [rows, k]), out (f32 [rows, d], the mixture's output).  scratch: device,
+ * >= q8s_scratch_bytes(Q8S_FN_BLOCK, ...) bytes, 256-byte aligned, no initial
+ * contents needed; it holds the logits, the normed row and its Q8_0 form and
+ * the hidden rows between the launches.  Decode rows run three launches
+ * (add_rmsnorm_router, moe_topk_gate_up, moe_down_combine); a chunk of rows
+ * in INT8 mode, E > 256 or d > 8192 run add_rmsnorm_q8, moe_route_topk,
+ * moe_gate_up and moe_down_combine.  eps >= 0; limits as moe_route_topk and
+ * moe_gate_up.
+ */
+Q8S_API int moe_ffn_block(const float *h, const float *r, const float *w, float eps, const float *Wr,
+                  const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                  const int8_t *Wdq, const float *Wds, int64_t rows, int64_t d, int64_t dff,
+                  int64_t E, int64_t k, float *sum, int32_t *idx, float *wts, float *out, int act,
+                  void *scratch, size_t scratch_bytes, void *stream);
+
+/*
+ * q8s_scratch_bytes -- bytes of scratch the call `fn` (Q8S_FN_ROUTE,
+ * Q8S_FN_DOWN or Q8S_FN_BLOCK) needs for these sizes; 0 for a call that needs
+ * none, or for an unknown fn.
  */
 Q8S_API size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
 

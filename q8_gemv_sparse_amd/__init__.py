@@ -8,7 +8,7 @@ call is refused.  Every step of the computation runs in the HIP kernels;
 there is no fallback.  PyTorch supplies device memory and streams only.
 
 Importing this package loads ``libq8s.so`` from this directory and fails
-loudly if it has not been built (``python -m q8_gemv_sparse_amd.build``).
+loudly if it has not been built (``python q8_gemv_sparse_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -18,9 +18,9 @@ import os
 import torch
 
 __all__ = [
-    "ACT_F32", "ACT_INT8", "FN_ROUTE", "FN_DOWN", "Q8sError", "LIB_PATH",
+    "ACT_F32", "ACT_INT8", "FN_ROUTE", "FN_DOWN", "FN_BLOCK", "Q8sError", "LIB_PATH",
     "q8_gemv", "q8_quantize_rows", "add_rmsnorm_q8", "moe_route_topk",
-    "moe_gate_up", "moe_down_combine", "q8s_scratch_bytes", "q8s_last_error",
+    "moe_gate_up", "moe_down_combine", "moe_ffn_block", "add_rmsnorm_router", "moe_topk_gate_up", "q8s_scratch_bytes", "q8s_last_error",
     "q8s_version", "library",
 ]
 
@@ -28,12 +28,13 @@ ACT_F32 = 0
 ACT_INT8 = 1
 FN_ROUTE = 1
 FN_DOWN = 2
+FN_BLOCK = 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8s.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libq8s.so is not built at %s; build it with `python -m q8_gemv_sparse_amd.build`" % LIB_PATH)
+        "libq8s.so is not built at %s; build it with `python q8_gemv_sparse_amd/build.py`" % LIB_PATH)
 
 _lib = ctypes.CDLL(LIB_PATH)
 _p = ctypes.c_void_p
@@ -47,6 +48,11 @@ _SIGS = {
     "moe_route_topk": [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p],
     "moe_gate_up": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, ctypes.c_int, _p],
     "moe_down_combine": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, ctypes.c_int, _p, _sz, _p],
+    "moe_ffn_block": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p,
+                      _p, _p, ctypes.c_int, _p, _sz, _p],
+    "add_rmsnorm_router": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
+    "moe_topk_gate_up": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
+                         ctypes.c_int, _p],
     "q8s_scratch_bytes": [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
 }
 for _name, _args in _SIGS.items():
@@ -236,3 +242,97 @@ def moe_down_combine(Wdq, Wds, idx, wts, E, h=None, hq=None, hs=None, y=None, ac
                                  dff, E, k, _ptr(y), act, _ptr(scratch), 0 if scratch is None else scratch.numel(),
                                  _stream(stream)))
     return y
+
+
+def moe_ffn_block(h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act=ACT_F32, sum=None, idx=None, wts=None,
+                  out=None, scratch=None, stream=None):
+    """The whole mixture block of a layer: sum = h + r, x = RMSNorm(sum) * w,
+    then the router, top-K, gate-up and down-combine over x.  Returns
+    (sum, idx, wts, out).  ``scratch`` is a uint8 device tensor of at least
+    q8s_scratch_bytes(FN_BLOCK, ...) bytes; one is allocated when none is given."""
+    for t, n in ((h, "h"), (r, "r"), (w, "w"), (Wr, "Wr"), (Wgs, "Wgs"), (Wus, "Wus"), (Wds, "Wds")):
+        _dev(t, torch.float32, n)
+    for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq"), (Wdq, "Wdq")):
+        _dev(t, torch.int8, n)
+    E, d = Wr.shape
+    rows = h.numel() // d
+    dff = Wgq.shape[0] // E
+    dev = h.device
+    if sum is None:
+        sum = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if wts is None:
+        wts = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if scratch is None:
+        scratch = torch.empty(max(q8s_scratch_bytes(FN_BLOCK, rows, d, dff, E, k, act), 1), dtype=torch.uint8,
+                              device=dev)
+    _dev(sum, torch.float32, "sum"); _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
+    _dev(out, torch.float32, "out"); _dev(scratch, torch.uint8, "scratch")
+    _check(_lib.moe_ffn_block(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wr), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq),
+                              _ptr(Wus), _ptr(Wdq), _ptr(Wds), rows, d, dff, E, k, _ptr(sum), _ptr(idx), _ptr(wts),
+                              _ptr(out), act, _ptr(scratch), scratch.numel(), _stream(stream)))
+    return sum, idx, wts, out
+
+
+def add_rmsnorm_router(h, r, w, eps, Wr, sum=None, x=None, xq=None, xs=None, logits=None, want_f32=True,
+                       want_q8=True, stream=None):
+    """add_rmsnorm_q8 with the router's logits fused in.  Returns
+    (sum, x or None, xq or None, xs or None, logits float64 [rows, E])."""
+    _dev(h, torch.float32, "h"); _dev(r, torch.float32, "r"); _dev(w, torch.float32, "w")
+    _dev(Wr, torch.float32, "Wr")
+    E, d = Wr.shape
+    rows = h.numel() // d
+    dev = h.device
+    if sum is None:
+        sum = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_f32 and x is None:
+        x = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_q8 and xq is None:
+        xq = torch.empty((rows, d), dtype=torch.int8, device=dev)
+        xs = torch.empty((rows, d // 32), dtype=torch.float32, device=dev)
+    if logits is None:
+        logits = torch.empty((rows, E), dtype=torch.float64, device=dev)
+    for t, dt, n in ((sum, torch.float32, "sum"), (x, torch.float32, "x"), (xq, torch.int8, "xq"),
+                     (xs, torch.float32, "xs"), (logits, torch.float64, "logits")):
+        _dev(t, dt, n)
+    _check(_lib.add_rmsnorm_router(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wr), rows, d, E, _ptr(sum), _ptr(x),
+                                   _ptr(xq), _ptr(xs), _ptr(logits), _stream(stream)))
+    return sum, x, xq, xs, logits
+
+
+def moe_topk_gate_up(logits, Wgq, Wgs, Wuq, Wus, k, x=None, xq=None, xs=None, idx=None, wts=None, h=None, hq=None,
+                     hs=None, act=ACT_F32, want_h=True, stream=None):
+    """moe_gate_up taking each row's top-K from ``logits`` itself.  Returns
+    (idx, wts, h, hq, hs)."""
+    _dev(logits, torch.float64, "logits")
+    for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq")):
+        _dev(t, torch.int8, n)
+    for t, n in ((Wgs, "Wgs"), (Wus, "Wus")):
+        _dev(t, torch.float32, n)
+    rows, E = logits.shape
+    d = Wgq.shape[1]
+    dff = Wgq.shape[0] // E
+    dev = Wgq.device
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if wts is None:
+        wts = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    if act == ACT_F32:
+        _dev(x, torch.float32, "x")
+    else:
+        _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
+        if hq is None:
+            hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
+        if hs is None:
+            hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
+    if h is None and (want_h or act == ACT_F32):
+        h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)
+    _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
+    _dev(h, torch.float32, "h"); _dev(hq, torch.int8, "hq"); _dev(hs, torch.float32, "hs")
+    _check(_lib.moe_topk_gate_up(_ptr(logits), _ptr(x), _ptr(xq), _ptr(xs), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq),
+                                 _ptr(Wus), rows, d, dff, E, k, _ptr(idx), _ptr(wts), _ptr(h), _ptr(hq), _ptr(hs), act,
+                                 _stream(stream)))
+    return idx, wts, h, hq, hs

@@ -1,6 +1,7 @@
 """Builds libq8s.so (the HIP library, gfx950) in place, next to this file.
 
-    python -m q8_gemv_sparse_amd.build        # or build() from Python
+    python q8_gemv_sparse_amd/build.py        # or build() from Python (the package
+                                              # itself refuses to import unbuilt)
 
 hipcc compiles every csrc/*.hip for gfx950 only.  Flags: -O3; float32
 division and square root correctly rounded (the Q8_0 quantiser's scale and

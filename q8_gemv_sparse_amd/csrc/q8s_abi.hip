@@ -148,6 +148,8 @@ size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E
         return q8s::route_scratch_bytes(rows, E);
     case Q8S_FN_DOWN:
         return q8s::down_scratch_bytes(rows, d, dff, k, act);
+    case Q8S_FN_BLOCK:
+        return q8s::block_scratch_bytes(rows, d, dff, E, k, act);
     default:
         return 0;
     }
@@ -343,6 +345,138 @@ int moe_down_combine(const float *h, const int8_t *hq, const float *hs, const in
     a.scratch = need ? scratch : nullptr;
     clear_stale();
     return launched(q8s::down_launch(a, as_stream(stream)), fn);
+}
+
+int add_rmsnorm_router(const float *h, const float *r, const float *w, float eps, const float *Wr, int64_t rows,
+                       int64_t d, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits, void *stream)
+{
+    const char *fn = "add_rmsnorm_router";
+    int rc;
+    if ((rc = check_count(fn, "rows", rows, 65535)) || (rc = check_dim32(fn, "d", d)) ||
+        (rc = check_count(fn, "E", E, Q8S_MAX_E)))
+        return rc;
+    if (!q8s::norm_logits_supported(d))
+        return fail(Q8S_EUNSUPPORTED, "%s: d = %lld exceeds the %lld values a fused norm + router row holds; use "
+                    "add_rmsnorm_q8 then moe_route_topk", fn, (long long)d, (long long)q8s::NORM_LOGITS_MAX_D);
+    if (!(eps >= 0.0f) || eps != eps)
+        return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    if ((xq == nullptr) != (xs == nullptr))
+        return fail(Q8S_EINVAL, "%s: `xq` and `xs` are given together or not at all", fn);
+    if (!x && !xq)
+        return fail(Q8S_EINVAL, "%s: neither `x` nor `xq` is given -- the normed row would not be written", fn);
+    const size_t n = (size_t)(rows * d);
+    std::vector<Span> ins = {{h, n * 4, "h"}, {r, n * 4, "r"}, {w, (size_t)d * 4, "w"}, {Wr, (size_t)(E * d) * 4, "Wr"}};
+    std::vector<Span> outs = {{sum, n * 4, "sum"}, {logits, (size_t)(rows * E) * 8, "logits"}};
+    if (x)
+        outs.push_back({x, n * 4, "x"});
+    if (xq) {
+        outs.push_back({xq, n, "xq"});
+        outs.push_back({xs, n / 32 * 4, "xs"});
+    }
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::norm_logits_launch(h, r, w, rows, d, eps, Wr, E, sum, x, xq, xs, logits, as_stream(stream)),
+                    fn);
+}
+
+int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq,
+                     const float *Wgs, const int8_t *Wuq, const float *Wus, int64_t rows, int64_t d, int64_t dff,
+                     int64_t E, int64_t k, int32_t *idx, float *wts, float *h, int8_t *hq, float *hs, int act,
+                     void *stream)
+{
+    const char *fn = "moe_topk_gate_up";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    if (E > q8s::ROUTE_FUSED_MAX_E)
+        return fail(Q8S_EUNSUPPORTED, "%s: E = %lld experts exceed the %d a gate-up workgroup ranks itself; use "
+                    "moe_route_topk then moe_gate_up", fn, (long long)E, q8s::ROUTE_FUSED_MAX_E);
+    const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
+    const size_t nh = (size_t)(rows * k * dff);
+    std::vector<Span> ins = {{logits, (size_t)(rows * E) * 8, "logits"}, {Wgq, wq, "Wgq"}, {Wgs, wsb, "Wgs"},
+                             {Wuq, wq, "Wuq"}, {Wus, wsb, "Wus"}};
+    std::vector<Span> outs = {{idx, (size_t)(rows * k) * 4, "idx"}, {wts, (size_t)(rows * k) * 4, "wts"}};
+    if (act == Q8S_ACT_F32) {
+        ins.push_back({x, (size_t)(rows * d) * 4, "x"});
+        outs.push_back({h, nh * 4, "h"});
+    } else {
+        ins.push_back({xq, (size_t)(rows * d), "xq"});
+        ins.push_back({xs, (size_t)(rows * d / 32) * 4, "xs"});
+        if (h)
+            outs.push_back({h, nh * 4, "h"});
+        outs.push_back({hq, nh, "hq"});
+        outs.push_back({hs, nh / 32 * 4, "hs"});
+    }
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::MoeArgs a{};
+    a.x = act == 0 ? x : nullptr;
+    a.xq = act == 1 ? xq : nullptr;
+    a.xs = act == 1 ? xs : nullptr;
+    a.Wgq = Wgq;
+    a.Wgs = Wgs;
+    a.Wuq = Wuq;
+    a.Wus = Wus;
+    a.rows = rows;
+    a.d = d;
+    a.dff = dff;
+    a.E = E;
+    a.k = k;
+    a.h = h;
+    a.hq = act == 1 ? hq : nullptr;
+    a.hs = act == 1 ? hs : nullptr;
+    a.act = act;
+    a.logits = logits;
+    a.idx_w = idx;
+    a.wts_w = wts;
+    clear_stale();
+    return launched(q8s::route_gate_up_launch(a, as_stream(stream)), fn);
+}
+
+int moe_ffn_block(const float *h, const float *r, const float *w, float eps, const float *Wr, const int8_t *Wgq,
+                  const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Wdq, const float *Wds,
+                  int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, float *sum, int32_t *idx, float *wts,
+                  float *out, int act, void *scratch, size_t scratch_bytes, void *stream)
+{
+    const char *fn = "moe_ffn_block";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    if (!(eps >= 0.0f) || eps != eps)
+        return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    const size_t n = (size_t)(rows * d);
+    const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
+    std::vector<Span> ins = {{h, n * 4, "h"},
+                             {r, n * 4, "r"},
+                             {w, (size_t)d * 4, "w"},
+                             {Wr, (size_t)(E * d) * 4, "Wr"},
+                             {Wgq, wq, "Wgq"},
+                             {Wgs, wsb, "Wgs"},
+                             {Wuq, wq, "Wuq"},
+                             {Wus, wsb, "Wus"},
+                             {Wdq, (size_t)(E * d) * (size_t)dff, "Wdq"},
+                             {Wds, (size_t)(E * d) * (size_t)(dff / 32) * 4, "Wds"}};
+    std::vector<Span> outs = {{sum, n * 4, "sum"},
+                              {idx, (size_t)(rows * k) * 4, "idx"},
+                              {wts, (size_t)(rows * k) * 4, "wts"},
+                              {out, n * 4, "out"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
+        return rc;
+    const size_t need = q8s::block_scratch_bytes(rows, d, dff, E, k, act);
+    if (!scratch || scratch_bytes < need)
+        return fail(Q8S_ESCRATCH,
+                    "%s: scratch of %zu bytes given, %zu needed (logits, the normed row, the hidden rows)", fn,
+                    scratch ? scratch_bytes : (size_t)0, need);
+    if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0)
+        return fail(Q8S_EALIGN, "%s: `scratch` is not 256-byte aligned", fn);
+    outs.push_back({scratch, need, "scratch"});
+    if ((rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::BlockArgs b{h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, rows, d, dff, E, k, sum, idx, wts, out, act,
+                     scratch};
+    clear_stale();
+    return launched(q8s::block_launch(b, as_stream(stream)), fn);
 }
 
 } // extern "C"

@@ -113,6 +113,30 @@ Q8S_DEV int q8_code(float v, float id)
     return (int)r;
 }
 
+// Quantise 8 consecutive values held by one thread of a 4-thread group that
+// owns one 32-value block (the group's lanes are neighbours within a quad);
+// writes the 8 codes and, from the group's first thread, the block scale.
+Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool leader)
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, dpp_f<DPP_XOR1>(amax));
+    amax = fmaxf(amax, dpp_f<DPP_XOR2>(amax));
+    const float d = q8_scale(amax);
+    const float id = q8_inv(d);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        lo |= (uint32_t)(q8_code(v[i], id) & 0xFF) << (8 * i);
+        hi |= (uint32_t)(q8_code(v[4 + i], id) & 0xFF) << (8 * i);
+    }
+    *reinterpret_cast<uint2 *>(q) = make_uint2(lo, hi);
+    if (leader)
+        *scale = d;
+}
+
 // ---------------------------------------------------------------------------
 // a lane's share of one row: C chunks of 16 bytes plus their block scales
 
@@ -355,5 +379,152 @@ struct ChunkGuShape {
     static constexpr int T = NW * OPS;
     static_assert(T % QB == 0, "a tile is whole Q8_0 blocks of the hidden row");
 };
+
+// ---------------------------------------------------------------------------
+// top-K of one row's router logits, held in LDS (fn emit_moe_forward: the K
+// largest by probability, which is monotone in the logit)
+
+// (l, e) ranks before (l', e') when l > l', or l == l' and e < e'.
+Q8S_DEV bool route_better(double l, int e, double l2, int e2) { return l > l2 || (l == l2 && e < e2); }
+
+// LDS of the in-workgroup top-K, for rows of at most TOPK_LDS_E logits.
+constexpr int TOPK_LDS_E = 256;
+struct alignas(16) TopkLds {
+    double L[TOPK_LDS_E];         // the row's logits
+    double cv[TOPK_LDS_E];        // candidates' logits
+    uint32_t ck[TOPK_LDS_E + 4];  // coarse keys, padded with zeros to whole quads
+    int cand[TOPK_LDS_E];         // candidates' expert indices
+    int ch[32];                   // the choices, in rank order
+    double kl[32];                // their logits
+    int n;                        // candidates
+};
+
+// An order-preserving 32-bit coarse key of a logit: the top half of a 64-bit
+// code whose unsigned order is the order of the values (-0 taken as +0, so
+// equal values get equal keys).  A strictly greater key means a strictly
+// greater logit; equal keys decide nothing.  Finite logits never get key 0.
+Q8S_DEV uint32_t coarse_key(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+    const uint64_t m = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+    return (uint32_t)(m >> 32);
+}
+
+// Sum over each group of S consecutive lanes, S in {1, 2, 4, 8}, S uniform
+// across the wave; every lane of a group receives its group's sum.
+Q8S_DEV int sum_lanes8(int v, int S)
+{
+    if (S >= 2)
+        v += dpp_i<DPP_XOR1>(v);
+    if (S >= 4)
+        v += dpp_i<DPP_XOR2>(v);
+    if (S >= 8)
+        v += dpp_i<DPP_HALF_MIRROR>(v);
+    return v;
+}
+
+// Threads per item when `items` items share the workgroup: a power of two up
+// to 8 with S * items <= blockDim.x.
+Q8S_DEV int lanes_per_item(int items)
+{
+    int S = 1;
+    while (S < 8 && S * 2 * items <= (int)blockDim.x)
+        S *= 2;
+    return S;
+}
+
+// Loads a row's E logits (E <= TOPK_LDS_E) and their coarse keys; every thread
+// calls it, and the caller synchronises before topk_select.
+Q8S_DEV void topk_load(TopkLds &t, const double *__restrict__ lr, int E)
+{
+    for (int i = threadIdx.x; i < ((E + 3) & ~3); i += blockDim.x) {
+        if (i < E) {
+            const double v = lr[i];
+            t.L[i] = v;
+            t.ck[i] = coarse_key(v);
+        } else {
+            t.ck[i] = 0u;
+        }
+    }
+    if (threadIdx.x == 0)
+        t.n = 0;
+}
+
+// The K best of the row's E <= blockDim.x logits by (logit descending, index
+// ascending), in rank order, into t.ch / t.kl.  Every thread calls it; the
+// caller synchronises before reading the choices.
+//   1. Coarse count: logit i's count of strictly greater coarse keys, by S
+//      threads sharing the E keys in interleaved quads.  A logit with K or
+//      more strictly greater keys has K strictly greater logits, so it is not
+//      kept; one with fewer is a candidate.  Every kept logit is a candidate,
+//      and every candidate's key (hence logit) exceeds every non-candidate's,
+//      so a candidate's rank among the candidates is its rank among all E.
+//   2. Exact rank among the candidates (usually exactly K) in double, ties to
+//      the lower index.
+// Both passes are a handful of instructions per thread: the exact compare of
+// all E^2 pairs in double measured several microseconds on a full workgroup.
+Q8S_DEV void topk_select(TopkLds &t, int E, int k)
+{
+    {
+        const int S = lanes_per_item(E);
+        const int i = threadIdx.x / S, part = threadIdx.x % S;
+        int c = 0;
+        if (i < E) {
+            const uint32_t ci = t.ck[i];
+            const uint4 *q = reinterpret_cast<const uint4 *>(t.ck);
+            const int nq = (E + 3) >> 2;
+            for (int q0 = part; q0 < nq; q0 += 4 * S) {
+                uint4 v[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    v[u] = q0 + u * S < nq ? q[q0 + u * S] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    c += (v[u].x > ci) + (v[u].y > ci) + (v[u].z > ci) + (v[u].w > ci);
+            }
+        }
+        c = sum_lanes8(c, S);
+        if (i < E && part == 0 && c < k) {
+            const int p = atomicAdd(&t.n, 1);
+            t.cand[p] = i;
+            t.cv[p] = t.L[i];
+        }
+    }
+    __syncthreads();
+    const int C = t.n;
+    const int S = lanes_per_item(C);
+    const int u = threadIdx.x / S, part = threadIdx.x % S;
+    int r = 0;
+    int i = 0;
+    double li = 0.0;
+    if (u < C) {
+        i = t.cand[u];
+        li = t.cv[u];
+        for (int w = part; w < C; w += S)
+            r += route_better(t.cv[w], t.cand[w], li, i) ? 1 : 0;
+    }
+    r = sum_lanes8(r, S);
+    if (u < C && part == 0 && r < k) {
+        t.ch[r] = i;
+        t.kl[r] = li;
+    }
+}
+
+// The kept weights: softmax over all E, then renormalised over the kept K,
+//   w_j = p_j / sum_i p_i,  p_e = exp(l_e - m) / sum_all exp(l - m),
+// where the all-expert denominator cancels; with m the largest logit (the
+// rank-0 choice) this is w_j = exp(l_j - m) / sum_i exp(l_i - m), formed in
+// double from the K kept logits only.  Called by one whole wave, lane j
+// handling slot j.
+Q8S_DEV void route_finish(const double *kl, const int *ch, int k, int32_t *idx_row, float *wts_row)
+{
+    const int j = threadIdx.x & (WAVE - 1);
+    const double p = j < k ? exp(kl[j] - kl[0]) : 0.0;
+    const double kept = wave_sum_f64(p);
+    if (j < k) {
+        idx_row[j] = ch[j];
+        wts_row[j] = (float)(p / kept);
+    }
+}
 
 } // namespace q8s

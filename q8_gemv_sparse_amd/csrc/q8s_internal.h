@@ -13,6 +13,12 @@ namespace q8s {
 constexpr int Q8S_MAX_K_DEV = 32;
 constexpr int Q8S_MAX_E_DEV = 8192;
 
+// Most experts whose top-K a gate-up workgroup takes itself (one logit per
+// thread at least), and the longest row the fused norm + router launch holds
+// in registers (four 2048-value segments).
+constexpr int ROUTE_FUSED_MAX_E = 256;
+constexpr int64_t NORM_LOGITS_MAX_D = 8192;
+
 // Rows from which int8-activation projections go to the MFMA GEMM (below it
 // the register GEMV serves up to four rows a pass).
 constexpr int64_t GEMM_MIN_ROWS = 5;
@@ -59,8 +65,15 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t st);
 hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st);
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               float *sum, float *y, int8_t *yq, float *ys, hipStream_t st);
+// add + norm of each row fused with the router's logits (grid E x rows); the
+// normed activation goes to x and/or xq/xs (whichever is non-null), logits to
+// `logits`
+bool norm_logits_supported(int64_t d);
+hipError_t norm_logits_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
+                              const float *Wr, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits,
+                              hipStream_t st);
 
-// router scratch: f64 logits [rows, E], then int arrival counters [row tiles]
+// router scratch: f64 logits [rows, E]
 size_t route_scratch_bytes(int64_t rows, int64_t E);
 hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
                         float *wts, void *scratch, hipStream_t st);
@@ -84,18 +97,47 @@ struct MoeArgs {
     float *y;
     int act;
     void *scratch;
+    // the fused route + gate-up launch: logits in, choices and weights out
+    const double *logits;
+    int32_t *idx_w;
+    float *wts_w;
 };
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st);
+// gate-up that takes each row's top-K from `logits` itself (E <= ROUTE_FUSED_MAX_E)
+hipError_t route_gate_up_launch(const MoeArgs &a, hipStream_t st);
 size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t k, int act);
 hipError_t down_launch(const MoeArgs &a, hipStream_t st);
 
 // a chunk's mixture (rows > 1, int8 activations): choices grouped by expert,
-// for rows one slice of a wave covers (d, dff <= 4096)
+// for d <= 2048 and dff <= 4096 (one slice of a wave each)
 bool chunk_supported(int64_t d, int64_t dff);
 hipError_t chunk_gate_up_launch(const MoeArgs &a, hipStream_t st);
 size_t chunk_down_scratch_bytes(int64_t rows, int64_t d, int64_t k);
 hipError_t chunk_down_launch(const MoeArgs &a, hipStream_t st);
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// the whole mixture block: add + norm, router + top-K, gate-up, down-combine
+struct BlockArgs {
+    const float *h, *r, *w;
+    float eps;
+    const float *Wr;
+    const int8_t *Wgq;
+    const float *Wgs;
+    const int8_t *Wuq;
+    const float *Wus;
+    const int8_t *Wdq;
+    const float *Wds;
+    int64_t rows, d, dff, E, k;
+    float *sum;
+    int32_t *idx;
+    float *wts;
+    float *out;
+    int act;
+    void *scratch;
+};
+size_t block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
+bool block_fused(int64_t rows, int64_t d, int64_t dff, int64_t E, int act);
+hipError_t block_launch(const BlockArgs &b, hipStream_t st);
 
 } // namespace q8s

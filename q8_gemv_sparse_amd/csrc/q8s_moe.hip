@@ -15,6 +15,8 @@
 // These kernels serve one row at a time (a batch of rows in f32 numerics runs
 // them row by row); a chunk of rows in int8 numerics goes to the grouped
 // kernels of q8s_moe_chunk.hip.
+// route + gate-up (the mixture block's fused path): the same tiles, each
+//   workgroup first taking the row's top-K from the router logits itself.
 // down-combine (one workgroup per 8 outputs of one row): waves take
 //   (slot, k-slice) pairs, so all K experts' rows of those outputs stream at
 //   once; the partials meet in LDS and are weighted and summed in slot order.
@@ -29,39 +31,46 @@ constexpr int MAX_KS = 16;
 constexpr int GU_MAX_KS = 32;
 constexpr int DN_MAX_WAVES = 8;
 
-// gate-up: one workgroup per tile of hidden outputs of one (row, slot).  With
-// the row in one slice (ks == 1) each wave finishes its own outputs;
-// otherwise the waves deal out (slice, step) items and the slices' partial
-// sums meet in LDS.
+// LDS of a gate-up workgroup: the slices' partial sums (rows cut into
+// slices) and the tile's hidden values (int8 numerics).
+template <int T>
+struct GuLds {
+    float gp[GU_MAX_KS][T];
+    float up[GU_MAX_KS][T];
+    float hv[T];
+};
+
+// One gate-up tile: the T hidden outputs from blockIdx.x*T of choice (row, j)
+// of expert e.  With the row in one slice (ks == 1) each wave finishes its own
+// outputs; otherwise the waves deal out (slice, step) items and the slices'
+// partial sums meet in LDS.
 template <int ACT, int LPR, int C>
-__global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
-    k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
-              const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
-              const float *__restrict__ Wus, const int32_t *__restrict__ idx, int d, int dff, int E, int k, int ks,
-              float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
+Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, int e, bool valid, int64_t row, int j,
+                          const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                          const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs,
+                          const int8_t *__restrict__ Wuq, const float *__restrict__ Wus, int d, int dff, int k, int ks,
+                          float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
 {
     using S = GuShape<ACT, LPR, C>;
     constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, NW = S::NW;
     constexpr int STEPS = T / OPS;
-    __shared__ float gp[GU_MAX_KS][T];
-    __shared__ float up[GU_MAX_KS][T];
-    __shared__ float hv[T];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
     const int o0 = blockIdx.x * T;
-    const int j = blockIdx.y;
-    const int64_t row = blockIdx.z;
     const int nch = d >> 4, nb = d >> 5;
-    const int e = idx[row * k + j];
-    const bool valid = (e >= 0 && e < E);
     const int64_t rbase = (int64_t)(valid ? e : 0) * dff + o0;
     const int64_t hbase = (row * k + j) * dff + o0;
 
-    for (int item = wid; item < ks * STEPS; item += NW) {
+    // A wave's items are wid, wid + NW, ...  Within an item the weight rows go
+    // out before the activation slice: waits on the vector-memory counter are
+    // in issue order.  (Requesting the next item's rows before reducing the
+    // current one measured slower for rows cut into slices: the second set of
+    // registers costs more than the overlap gains.)
+    const int nitems = ks * STEPS;
+    auto load_item = [&](int item, RowSlice<C>(&wg)[U], RowSlice<C>(&wu)[U], XSlice<ACT, C> &xv) {
         const int s = item / STEPS, st = item % STEPS;
         const int ch0 = s * LPR * C;
         const int sl = min(LPR * C, nch - ch0);
-        RowSlice<C> wg[U], wu[U];
         if (valid) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
@@ -70,9 +79,12 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
                 load_row<LPR, C>(wu[u], Wuq + o * d, Wus + o * nb, ch0, sl, lig);
             }
         }
-        XSlice<ACT, C> xv;
         load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
                        ACT == 1 ? xs + row * nb : nullptr, ch0, sl, lig);
+    };
+    auto finish_item = [&](int item, const RowSlice<C>(&wg)[U], const RowSlice<C>(&wu)[U],
+                           const XSlice<ACT, C> &xv) {
+        const int s = item / STEPS, st = item % STEPS;
 #pragma unroll
         for (int u = 0; u < U; u++) {
             float g = 0.0f, v = 0.0f;
@@ -87,15 +99,21 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
                 if (ks == 1) {
                     const float r = valid ? silu(g) * v : 0.0f;
                     if (ACT == 1)
-                        hv[ol] = r;
+                        sm.hv[ol] = r;
                     if (h)
                         h[hbase + ol] = r;
                 } else {
-                    gp[s][ol] = g;
-                    up[s][ol] = v;
+                    sm.gp[s][ol] = g;
+                    sm.up[s][ol] = v;
                 }
             }
         }
+    };
+    for (int item = wid; item < nitems; item += NW) {
+        RowSlice<C> wg[U], wu[U];
+        XSlice<ACT, C> xv;
+        load_item(item, wg, wu, xv);
+        finish_item(item, wg, wu, xv);
     }
     if (ks == 1 && ACT == 0)
         return;
@@ -104,12 +122,12 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
         for (int t = threadIdx.x; t < T; t += blockDim.x) {
             float g = 0.0f, v = 0.0f;
             for (int s = 0; s < ks; s++) {
-                g += gp[s][t];
-                v += up[s][t];
+                g += sm.gp[s][t];
+                v += sm.up[s][t];
             }
             const float r = valid ? silu(g) * v : 0.0f;
             if (ACT == 1)
-                hv[t] = r;
+                sm.hv[t] = r;
             if (h)
                 h[hbase + t] = r;
         }
@@ -119,7 +137,7 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     if (ACT == 1 && wid == 0) {
         // the tile is one Q8_0 block of the hidden row: quantise it once
         const int t = lane & 31;
-        const float v = hv[t];
+        const float v = sm.hv[t];
         float amax = fabsf(v);
         for (int off = 16; off >= 1; off >>= 1)
             amax = fmaxf(amax, __shfl_xor(amax, off));
@@ -130,6 +148,51 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
         if (lane == 0)
             hs[hbase / QB] = dsc;
     }
+}
+
+// gate-up with the choices given: one workgroup per tile of one (row, slot).
+template <int ACT, int LPR, int C>
+__global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
+    k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
+              const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
+              const float *__restrict__ Wus, const int32_t *__restrict__ idx, int d, int dff, int E, int k, int ks,
+              float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
+{
+    __shared__ GuLds<GuShape<ACT, LPR, C>::T> sm;
+    const int j = blockIdx.y;
+    const int64_t row = blockIdx.z;
+    const int e = idx[row * k + j];
+    gate_up_tile<ACT, LPR, C>(sm, e, e >= 0 && e < E, row, j, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, dff, k, ks, h, hq, hs);
+}
+
+// gate-up that first takes the row's top-K itself from the router logits:
+// every workgroup ranks the row's E logits in LDS (topk_select) and reads its
+// expert from the result, so the choices need no launch of their own; the
+// workgroup of tile 0, slot 0 writes the row's idx and wts for the
+// down-combine launch.
+template <int ACT, int LPR, int C>
+__global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
+    k_route_gate_up(const double *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ wts,
+                    const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                    const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
+                    const float *__restrict__ Wus, int d, int dff, int E, int k, int ks, float *__restrict__ h,
+                    int8_t *__restrict__ hq, float *__restrict__ hs)
+{
+    static_assert(ROUTE_FUSED_MAX_E <= TOPK_LDS_E, "the row's logits fit the top-K LDS");
+    __shared__ GuLds<GuShape<ACT, LPR, C>::T> sm;
+    __shared__ TopkLds t;
+    const int j = blockIdx.y;
+    const int64_t row = blockIdx.z;
+    topk_load(t, logits + row * E, E);
+    __syncthreads();
+    topk_select(t, E, k);
+    __syncthreads();
+    const int e = __builtin_amdgcn_readfirstlane(t.ch[j]);
+    gate_up_tile<ACT, LPR, C>(sm, e, true, row, j, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, dff, k, ks, h, hq, hs);
+    // the choices and weights go out after the tile, off its critical path
+    // (only the down-combine launch reads them)
+    if (blockIdx.x == 0 && j == 0 && threadIdx.x < WAVE)
+        route_finish(t.kl, t.ch, k, idx + row * k, wts + row * k);
 }
 
 template <int ACT, int LPR, int C>
@@ -232,6 +295,18 @@ hipError_t gu_go(const MoeArgs &a, int ks, hipStream_t st)
 }
 
 template <int ACT, int LPR, int C>
+hipError_t rgu_go(const MoeArgs &a, int ks, hipStream_t st)
+{
+    using S = GuShape<ACT, LPR, C>;
+    static_assert(S::NW * WAVE >= ROUTE_FUSED_MAX_E, "one thread per logit at least");
+    dim3 grid((unsigned)(a.dff / S::T), (unsigned)a.k, (unsigned)a.rows);
+    hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w, a.wts_w,
+                       a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
+                       a.hq, a.hs);
+    return hipGetLastError();
+}
+
+template <int ACT, int LPR, int C>
 hipError_t dn_go(const MoeArgs &a, int ks, hipStream_t st)
 {
     const int pairs = (int)a.k * ks;
@@ -268,9 +343,39 @@ struct GU {
     static hipError_t go(const MoeArgs &a, int ks, hipStream_t st) { return gu_go<ACT, LPR, C>(a, ks, st); }
 };
 template <int ACT, int LPR, int C>
+struct RGU {
+    static hipError_t go(const MoeArgs &a, int ks, hipStream_t st) { return rgu_go<ACT, LPR, C>(a, ks, st); }
+};
+template <int ACT, int LPR, int C>
 struct DN {
     static hipError_t go(const MoeArgs &a, int ks, hipStream_t st) { return dn_go<ACT, LPR, C>(a, ks, st); }
 };
+
+} // namespace
+
+namespace {
+
+// The decode gate-up's shape for the mode and d, then the launch F.
+template <template <int, int, int> class F>
+hipError_t gu_dispatch(const MoeArgs &a, hipStream_t st)
+{
+    if (a.act == 0)
+        return by_shape<0, F>(a, a.d, st);
+    const int64_t nch = a.d / 16;
+    if (nch > 128)  // int8 rows past 2048: slices of 2048 (lane groups of 64, 2 chunks)
+        return F<1, 64, 2>::go(a, (int)((nch + 127) / 128), st);
+    const SliceShape sh = slice_shape(a.d);
+    switch (sh.lpr * 8 + sh.c) {
+    case 16 * 8 + 1:
+        return F<1, 16, 1>::go(a, 1, st);
+    case 16 * 8 + 3:
+        return F<1, 16, 3>::go(a, 1, st);
+    case 64 * 8 + 1:
+        return F<1, 64, 1>::go(a, 1, st);
+    default:
+        return F<1, 64, 2>::go(a, 1, st);
+    }
+}
 
 } // namespace
 
@@ -278,13 +383,10 @@ hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st)
 {
     if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
         return chunk_gate_up_launch(a, st);
-    if (a.act == 0)
-        return by_shape<0, GU>(a, a.d, st);
-    const int64_t nch = a.d / 16;
-    if (nch > 128)  // int8 rows past 2048: slices of 2048 (lane groups of 64, 2 chunks)
-        return GU<1, 64, 2>::go(a, (int)((nch + 127) / 128), st);
-    return by_shape<1, GU>(a, a.d, st);
+    return gu_dispatch<GU>(a, st);
 }
+
+hipError_t route_gate_up_launch(const MoeArgs &a, hipStream_t st) { return gu_dispatch<RGU>(a, st); }
 
 size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t k, int act)
 {

@@ -32,7 +32,6 @@ namespace q8s {
 namespace {
 
 constexpr int CK_PASS = 64;  // choices of one expert per pass
-constexpr int CK_GROUP = 4;  // choices whose activation slices are in registers at once
 
 // Wave 0 gathers the workgroup's pass of the stable list of choices c
 // (increasing c) whose expert is e (for e == E: whose expert is invalid):

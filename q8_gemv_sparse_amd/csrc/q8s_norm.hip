@@ -19,33 +19,75 @@ namespace q8s {
 constexpr int NORM_THREADS = 256;
 constexpr int NORM_SEG = NORM_THREADS * 8;
 
-// Quantise 8 consecutive values held by one thread of a 4-thread block group;
-// writes the 8 codes and (first thread of the group) the block scale.
-Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool leader)
+// A thread's share of one row for rows of at most SEGS 2048-value segments:
+// its 8 values of each segment (the float32 sums) and their norm weights,
+// kept in registers between the two passes.
+template <int SEGS>
+struct NormShare {
+    f32x4 sv[SEGS][2], wv[SEGS][2];
+};
+
+template <int SEGS>
+Q8S_DEV void norm_load(NormShare<SEGS> &n, const float *hr, const float *rr, const float *w, int d, int t8)
 {
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; i++)
-        amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, dpp_f<DPP_XOR1>(amax));
-    amax = fmaxf(amax, dpp_f<DPP_XOR2>(amax));
-    const float d = q8_scale(amax);
-    const float id = q8_inv(d);
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        lo |= (uint32_t)(q8_code(v[i], id) & 0xFF) << (8 * i);
-        hi |= (uint32_t)(q8_code(v[4 + i], id) & 0xFF) << (8 * i);
+    for (int g = 0; g < SEGS; g++) {
+        const int base = t8 + g * NORM_SEG;
+        if (base < d) {
+            const f32x4 a0 = ldf4(hr + base), a1 = ldf4(hr + base + 4);
+            const f32x4 b0 = ldf4(rr + base), b1 = ldf4(rr + base + 4);
+            n.wv[g][0] = ldf4(w + base);
+            n.wv[g][1] = ldf4(w + base + 4);
+            n.sv[g][0] = a0 + b0;
+            n.sv[g][1] = a1 + b1;
+        }
     }
-    *reinterpret_cast<uint2 *>(q) = make_uint2(lo, hi);
-    if (leader)
-        *scale = d;
 }
 
-// SEGS > 0: the row has at most SEGS 2048-value segments, and each thread keeps
-// its sums and weights in registers between the two passes.  SEGS == 0: any
-// length; the second pass re-forms the sums from h and r (the same float32
-// adds, bit for bit).
+// 1/sqrt(mean(sum^2) + eps) of the row, in double: each thread's squares in
+// order, then the wave sums, then the four waves in order.  Every thread of
+// the workgroup calls it (it synchronises the workgroup once).
+Q8S_DEV double norm_inv(double ss, int d, float eps, double *wsum)
+{
+    ss = wave_sum_f64(ss);
+    if ((threadIdx.x & 63) == 0)
+        wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < NORM_THREADS / WAVE; i++)
+        tot += wsum[i];
+    return 1.0 / sqrt(tot / (double)d + (double)eps);
+}
+
+template <int SEGS>
+Q8S_DEV double norm_squares(const NormShare<SEGS> &n, int d, int t8)
+{
+    double ss = 0.0;
+#pragma unroll
+    for (int g = 0; g < SEGS; g++) {
+        if (t8 + g * NORM_SEG < d) {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                ss += (double)n.sv[g][0][i] * (double)n.sv[g][0][i] + (double)n.sv[g][1][i] * (double)n.sv[g][1][i];
+        }
+    }
+    return ss;
+}
+
+// The normalised values of segment g, formed in double and rounded once.
+Q8S_DEV void norm_values(f32x4 s0, f32x4 s1, f32x4 w0, f32x4 w1, double inv, float (&v)[8])
+{
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        v[i] = (float)(((double)s0[i] * inv) * (double)w0[i]);
+        v[4 + i] = (float)(((double)s1[i] * inv) * (double)w1[i]);
+    }
+}
+
+// SEGS > 0: the row has at most SEGS 2048-value segments (NormShare).
+// SEGS == 0: any length; the second pass re-forms the sums from h and r (the
+// same float32 adds, bit for bit).
 template <int SEGS>
 __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__restrict__ h, const float *__restrict__ r,
                                                                  const float *__restrict__ w, int d, float eps,
@@ -59,32 +101,19 @@ __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__
     const float *rr = r + row * d;
     const int t8 = threadIdx.x * 8;
 
-    f32x4 sv[NS][2], wv[NS][2];
+    NormShare<NS> n;
     double ss = 0.0;
     if (SEGS > 0) {
+        norm_load<NS>(n, hr, rr, w, d, t8);
 #pragma unroll
         for (int g = 0; g < NS; g++) {
             const int base = t8 + g * NORM_SEG;
             if (base < d) {
-                const f32x4 a0 = ldf4(hr + base), a1 = ldf4(hr + base + 4);
-                const f32x4 b0 = ldf4(rr + base), b1 = ldf4(rr + base + 4);
-                wv[g][0] = ldf4(w + base);
-                wv[g][1] = ldf4(w + base + 4);
-                sv[g][0] = a0 + b0;
-                sv[g][1] = a1 + b1;
+                *reinterpret_cast<f32x4 *>(sum + row * d + base) = n.sv[g][0];
+                *reinterpret_cast<f32x4 *>(sum + row * d + base + 4) = n.sv[g][1];
             }
         }
-#pragma unroll
-        for (int g = 0; g < NS; g++) {
-            const int base = t8 + g * NORM_SEG;
-            if (base < d) {
-                *reinterpret_cast<f32x4 *>(sum + row * d + base) = sv[g][0];
-                *reinterpret_cast<f32x4 *>(sum + row * d + base + 4) = sv[g][1];
-#pragma unroll
-                for (int i = 0; i < 4; i++)
-                    ss += (double)sv[g][0][i] * (double)sv[g][0][i] + (double)sv[g][1][i] * (double)sv[g][1][i];
-            }
-        }
+        ss = norm_squares<NS>(n, d, t8);
     } else {
         for (int base = t8; base < d; base += NORM_SEG) {
             const f32x4 s0 = ldf4(hr + base) + ldf4(rr + base), s1 = ldf4(hr + base + 4) + ldf4(rr + base + 4);
@@ -95,37 +124,18 @@ __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__
                 ss += (double)s0[i] * (double)s0[i] + (double)s1[i] * (double)s1[i];
         }
     }
-    ss = wave_sum_f64(ss);
-    if ((threadIdx.x & 63) == 0)
-        wsum[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int i = 0; i < NORM_THREADS / WAVE; i++)
-        tot += wsum[i];
-    const double inv = 1.0 / sqrt(tot / (double)d + (double)eps);
+    const double inv = norm_inv(ss, d, eps, wsum);
 
     for (int g = 0; SEGS > 0 ? g < NS : true; g++) {
         const int base = t8 + g * NORM_SEG;
         if (base >= d)
             break;
-        f32x4 s0, s1, w0, w1;
-        if (SEGS > 0) {
-            s0 = sv[g][0];
-            s1 = sv[g][1];
-            w0 = wv[g][0];
-            w1 = wv[g][1];
-        } else {
-            s0 = ldf4(hr + base) + ldf4(rr + base);
-            s1 = ldf4(hr + base + 4) + ldf4(rr + base + 4);
-            w0 = ldf4(w + base);
-            w1 = ldf4(w + base + 4);
-        }
         float v[8];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            v[i] = (float)(((double)s0[i] * inv) * (double)w0[i]);
-            v[4 + i] = (float)(((double)s1[i] * inv) * (double)w1[i]);
+        if (SEGS > 0) {
+            norm_values(n.sv[g][0], n.sv[g][1], n.wv[g][0], n.wv[g][1], inv, v);
+        } else {
+            norm_values(ldf4(hr + base) + ldf4(rr + base), ldf4(hr + base + 4) + ldf4(rr + base + 4), ldf4(w + base),
+                        ldf4(w + base + 4), inv, v);
         }
         if (y) {
             *reinterpret_cast<f32x4 *>(y + row * d + base) = f32x4{v[0], v[1], v[2], v[3]};
@@ -134,6 +144,81 @@ __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__
         if (yq)
             quant8_store(v, yq + row * d + base, ys + row * (d / QB) + base / QB, (threadIdx.x & 3) == 0);
     }
+}
+
+// The mixture block's first launch: the add + norm of the row, exactly as
+// k_add_rmsnorm_q8 forms it (the same shares, sums and roundings), and one
+// router logit per workgroup, l[row][e] = sum_t Wr[e][t] * y[t] in double
+// (fn emit_moe_forward's router over the normed row).  Every workgroup of a
+// row forms the whole normed row -- it re-reads h, r and w, 24 bytes a value,
+// mostly from cache -- so no workgroup waits for another; the workgroup of
+// expert 0 also writes the sum and the activation the gate-up launch reads
+// (float32 x and/or its Q8_0 form, whichever is given).  The router row's
+// loads are issued first: they do not depend on the norm.
+template <int SEGS>
+__global__ void __launch_bounds__(NORM_THREADS)
+    k_norm_logits(const float *__restrict__ h, const float *__restrict__ r, const float *__restrict__ w, int d,
+                  float eps, const float *__restrict__ Wr, int E, float *__restrict__ sum, float *__restrict__ x,
+                  int8_t *__restrict__ xq, float *__restrict__ xs, double *__restrict__ logits)
+{
+    __shared__ double wsum[NORM_THREADS / WAVE];
+    __shared__ double lsum[NORM_THREADS / WAVE];
+    const int e = blockIdx.x;
+    const int64_t row = blockIdx.y;
+    const bool writer = e == 0;
+    const int t8 = threadIdx.x * 8;
+    const float *wr = Wr + (int64_t)e * d;
+
+    f32x4 rv[SEGS][2];
+#pragma unroll
+    for (int g = 0; g < SEGS; g++) {
+        const int base = t8 + g * NORM_SEG;
+        if (base < d) {
+            rv[g][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base));
+            rv[g][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base + 4));
+        }
+    }
+    NormShare<SEGS> n;
+    norm_load<SEGS>(n, h + row * d, r + row * d, w, d, t8);
+    if (writer) {
+#pragma unroll
+        for (int g = 0; g < SEGS; g++) {
+            const int base = t8 + g * NORM_SEG;
+            if (base < d) {
+                *reinterpret_cast<f32x4 *>(sum + row * d + base) = n.sv[g][0];
+                *reinterpret_cast<f32x4 *>(sum + row * d + base + 4) = n.sv[g][1];
+            }
+        }
+    }
+    const double inv = norm_inv(norm_squares<SEGS>(n, d, t8), d, eps, wsum);
+
+    double lg = 0.0;
+#pragma unroll
+    for (int g = 0; g < SEGS; g++) {
+        const int base = t8 + g * NORM_SEG;
+        if (base < d) {
+            float v[8];
+            norm_values(n.sv[g][0], n.sv[g][1], n.wv[g][0], n.wv[g][1], inv, v);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                lg += (double)rv[g][0][i] * (double)v[i];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                lg += (double)rv[g][1][i] * (double)v[4 + i];
+            if (writer && x) {
+                *reinterpret_cast<f32x4 *>(x + row * d + base) = f32x4{v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4 *>(x + row * d + base + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            }
+            if (writer && xq)
+                quant8_store(v, xq + row * d + base, xs + row * (d / QB) + base / QB, (threadIdx.x & 3) == 0);
+        }
+    }
+    lg = wave_sum_f64(lg);
+    if ((threadIdx.x & 63) == 0)
+        lsum[threadIdx.x >> 6] = lg;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        logits[row * E + e] = ((lsum[0] + lsum[1]) + lsum[2]) + lsum[3];
 }
 
 // q8_quantize_rows: the same epilogue on a given f32 row set.  Threads own 8
@@ -171,6 +256,26 @@ hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, in
         hipLaunchKernelGGL((k_add_rmsnorm_q8<4>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
     else
         hipLaunchKernelGGL((k_add_rmsnorm_q8<0>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+    return hipGetLastError();
+}
+
+bool norm_logits_supported(int64_t d) { return d <= NORM_LOGITS_MAX_D; }
+
+hipError_t norm_logits_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
+                              const float *Wr, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits,
+                              hipStream_t st)
+{
+    const int segs = (int)((d + NORM_SEG - 1) / NORM_SEG);
+    const dim3 grid((unsigned)E, (unsigned)rows), block(NORM_THREADS);
+    if (segs <= 1)
+        hipLaunchKernelGGL((k_norm_logits<1>), grid, block, 0, st, h, r, w, (int)d, eps, Wr, (int)E, sum, x, xq, xs,
+                           logits);
+    else if (segs <= 2)
+        hipLaunchKernelGGL((k_norm_logits<2>), grid, block, 0, st, h, r, w, (int)d, eps, Wr, (int)E, sum, x, xq, xs,
+                           logits);
+    else
+        hipLaunchKernelGGL((k_norm_logits<4>), grid, block, 0, st, h, r, w, (int)d, eps, Wr, (int)E, sum, x, xq, xs,
+                           logits);
     return hipGetLastError();
 }
 

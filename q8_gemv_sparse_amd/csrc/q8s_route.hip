@@ -12,9 +12,10 @@
 //             workgroups.  Products and sums are in double, so near-equal
 //             logits are ranked as the double-precision definition ranks them.
 //   k_topk    one workgroup per row: the K best by (logit descending, index
-//             ascending) -- for E <= 256 each thread ranks one logit against
-//             all E at once, beyond that K selection rounds of a workgroup
-//             arg-max -- then the kept weights.
+//             ascending) -- for E <= 256 a coarse count over order-preserving
+//             32-bit keys picks the candidates and an exact double-precision
+//             rank orders them (topk_select), beyond that K selection rounds
+//             of a workgroup arg-max -- then the kept weights.
 // Handing the logits over at the kernel boundary costs one short launch; doing
 // it inside one launch needs a device-scope release by every workgroup, which
 // measured several times slower on this chip.
@@ -25,12 +26,8 @@ namespace q8s {
 
 constexpr int RT_THREADS = 256;
 constexpr int RT_WAVES = RT_THREADS / WAVE;
-constexpr int TOPK_RANK_MAX_E = 256;
 
 size_t route_scratch_bytes(int64_t rows, int64_t E) { return align256((size_t)rows * E * sizeof(double)); }
-
-// (l, e) ranks before (l', e') when l > l', or l == l' and e < e'.
-Q8S_DEV bool better(double l, int e, double l2, int e2) { return l > l2 || (l == l2 && e < e2); }
 
 template <int RT>
 __global__ void __launch_bounds__(RT_THREADS) k_logits(const float *__restrict__ x, const float *__restrict__ Wr,
@@ -83,70 +80,25 @@ __global__ void __launch_bounds__(RT_THREADS) k_logits(const float *__restrict__
     }
 }
 
-// The kept weights: softmax over all E, then renormalised over the kept K,
-//   w_j = p_j / sum_i p_i,  p_e = exp(l_e - m) / sum_all exp(l - m),
-// where the all-expert denominator cancels; with m the largest logit (the
-// rank-0 choice) this is w_j = exp(l_j - m) / sum_i exp(l_i - m), formed in
-// double from the K kept logits only, one lane per kept slot of wave 0.
-Q8S_DEV void finish_row(const double *kl, const int *ch, int k, int32_t *idx_row, float *wts_row)
-{
-    const int j = threadIdx.x;
-    const double p = j < k ? exp(kl[j] - kl[0]) : 0.0;
-    const double kept = wave_sum_f64(p);
-    if (j < k) {
-        idx_row[j] = ch[j];
-        wts_row[j] = (float)(p / kept);
-    }
-}
-
 __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ logits, int E, int k,
                                                      int32_t *__restrict__ idx, float *__restrict__ wts)
 {
-    extern __shared__ double L[];  // [E]
-    __shared__ int ch[Q8S_MAX_K_DEV];
-    __shared__ double kl[Q8S_MAX_K_DEV];
+    extern __shared__ double Lbig[];  // [E], for rows of more than TOPK_LDS_E logits
+    __shared__ TopkLds t;
     __shared__ double bl[RT_WAVES];
     __shared__ int be[RT_WAVES];
     const int64_t row = blockIdx.x;
     const double *lr = logits + row * E;
-    for (int i = threadIdx.x; i < E; i += RT_THREADS)
-        L[i] = lr[i];
-    __syncthreads();
 
-    if (E <= TOPK_RANK_MAX_E) {
-        // rank of each logit among all E: S = 256/E (a power of two) threads
-        // per logit each count the better ones in a share of the E, and sum;
-        // the K of rank < K are the kept set, in rank order
-        int S = 1;
-        while (S * 2 * E <= RT_THREADS && S < WAVE)
-            S *= 2;
-        const int i = threadIdx.x / S, part = threadIdx.x % S;
-        int rank = 0;
-        double li = 0.0;
-        if (i < E) {
-            li = L[i];
-            const int j0 = part * E / S, j1 = (part + 1) * E / S;
-            int j = j0;
-            for (; j + 8 <= j1; j += 8) {
-                double v[8];
-#pragma unroll
-                for (int u = 0; u < 8; u++)
-                    v[u] = L[j + u];
-#pragma unroll
-                for (int u = 0; u < 8; u++)
-                    rank += better(v[u], j + u, li, i) ? 1 : 0;
-            }
-            for (; j < j1; j++)
-                rank += better(L[j], j, li, i) ? 1 : 0;
-        }
-        for (int o = 1; o < S; o <<= 1)
-            rank += __shfl_xor(rank, o);
-        if (i < E && part == 0 && rank < k) {
-            ch[rank] = i;
-            kl[rank] = li;
-        }
+    if (E <= TOPK_LDS_E) {
+        topk_load(t, lr, E);
+        __syncthreads();
+        topk_select(t, E, k);
         __syncthreads();
     } else {
+        for (int i = threadIdx.x; i < E; i += RT_THREADS)
+            Lbig[i] = lr[i];
+        __syncthreads();
         // K rounds of a workgroup arg-max; a chosen logit is retired to -inf
         // by the thread that scans it (real logits are finite and k <= E)
         const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -154,14 +106,14 @@ __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ 
             double b = -INFINITY;
             int bi = 0x7fffffff;
             for (int i = threadIdx.x; i < E; i += RT_THREADS)
-                if (better(L[i], i, b, bi)) {
-                    b = L[i];
+                if (route_better(Lbig[i], i, b, bi)) {
+                    b = Lbig[i];
                     bi = i;
                 }
             for (int o = 32; o >= 1; o >>= 1) {
                 const double b2 = __shfl_xor(b, o);
                 const int i2 = __shfl_xor(bi, o);
-                if (better(b2, i2, b, bi)) {
+                if (route_better(b2, i2, b, bi)) {
                     b = b2;
                     bi = i2;
                 }
@@ -174,21 +126,21 @@ __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ 
             double wb = bl[0];
             int wi = be[0];
             for (int w = 1; w < RT_WAVES; w++)
-                if (better(bl[w], be[w], wb, wi)) {
+                if (route_better(bl[w], be[w], wb, wi)) {
                     wb = bl[w];
                     wi = be[w];
                 }
             if (threadIdx.x == 0) {
-                ch[jj] = wi;
-                kl[jj] = wb;
+                t.ch[jj] = wi;
+                t.kl[jj] = wb;
             }
             if ((int)threadIdx.x == (wi % RT_THREADS))
-                L[wi] = -INFINITY;
+                Lbig[wi] = -INFINITY;
             __syncthreads();
         }
     }
     if (threadIdx.x < WAVE)
-        finish_row(kl, ch, k, idx + row * k, wts + row * k);
+        route_finish(t.kl, t.ch, k, idx + row * k, wts + row * k);
 }
 
 hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
@@ -204,8 +156,8 @@ hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(RT_THREADS), (size_t)E * sizeof(double), st, logits, (int)E,
-                       (int)k, idx, wts);
+    const size_t big = E > TOPK_LDS_E ? (size_t)E * sizeof(double) : 0;
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(RT_THREADS), big, st, logits, (int)E, (int)k, idx, wts);
     return hipGetLastError();
 }
 

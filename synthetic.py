@@ -137,6 +137,26 @@ def chunk_inputs(seed, d, dff, E, k, rows, n_dense):
     return MoeInputs(Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, X, d, dff, E, k), Dq, Ds
 
 
+@dataclass
+class BlockInputs:
+    moe: MoeInputs   # the mixture's weights (its x is unused: the block forms x)
+    w: np.ndarray    # f32 [d]  RMSNorm weight
+    h: np.ndarray    # f32 [rows, d]
+    r: np.ndarray    # f32 [rows, d]
+
+
+def block_inputs(seed, d, dff, E, k, rows=1):
+    """A whole mixture block of a layer, fed by its add + norm: draw order the
+    weights as ``moe_weights`` lists, then the norm weight, h, r."""
+    rng = _rng(seed)
+    Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds = moe_weights(rng, d, dff, E)
+    w = rng.uniform(0.5, 1.5, size=d).astype(np.float32)
+    h = normal(rng, rows, d)
+    r = normal(rng, rows, d)
+    m = MoeInputs(Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, None, d, dff, E, k)
+    return BlockInputs(m, w, h, r)
+
+
 def fill_pattern(n, scale=1.0):
     """The deterministic small-integer fill ``v[p] = (p % 7) - 3`` (optionally
     scaled) that the ``emit_forward`` item of the ``codegen_cuda::qwen_emit``

@@ -128,3 +128,65 @@ def test_down_refusals():
     assert r == -1 and "overlaps" in _err()
     r = LIB.moe_down_combine(None, A, None, B, C, D, F, 1, 64, 64, 4, 2, G, 1, None, 0, None)
     assert r == -1 and "`hs` is null" in _err()
+
+
+def block(act=0, rows=1, d=64, dff=64, E=4, k=2, eps=1e-6, sb=None, scratch=0x3000000, **over):
+    # inputs h r w Wr Wgq Wgs Wuq Wus Wdq Wds, outputs sum idx wts out: 1 MiB apart
+    names = ["h", "r", "w", "Wr", "Wgq", "Wgs", "Wuq", "Wus", "Wdq", "Wds", "sum", "idx", "wts", "out"]
+    p = {n: 0x100000 * (i + 1) for i, n in enumerate(names)}
+    p.update(over)
+    if sb is None:
+        sb = q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, act)
+    return LIB.moe_ffn_block(p["h"], p["r"], p["w"], ctypes.c_float(eps), p["Wr"], p["Wgq"], p["Wgs"], p["Wuq"],
+                             p["Wus"], p["Wdq"], p["Wds"], rows, d, dff, E, k, p["sum"], p["idx"], p["wts"], p["out"],
+                             act, scratch, sb, None)
+
+
+def test_block_scratch_and_refusals():
+    # the logits, the normed row, the hidden rows: at least their bytes
+    f32 = q8.q8s_scratch_bytes(q8.FN_BLOCK, 1, 2048, 768, 128, 8, q8.ACT_F32)
+    assert f32 >= 128 * 8 + 2048 * 4 + 8 * 768 * 4
+    i8 = q8.q8s_scratch_bytes(q8.FN_BLOCK, 1, 2048, 768, 128, 8, q8.ACT_INT8)
+    assert i8 >= 128 * 8 + 2048 * (4 + 1) + 8 * 768 * (1 + 4 / 32)
+    # a chunk in int8 also holds the down-combine's per-choice results
+    chunk = q8.q8s_scratch_bytes(q8.FN_BLOCK, 64, 2048, 768, 128, 8, q8.ACT_INT8)
+    assert chunk >= q8.q8s_scratch_bytes(q8.FN_DOWN, 64, 2048, 768, 128, 8, q8.ACT_INT8) + 64 * 128 * 8
+    assert block(k=0) == -1 and "1 <= k <= E" in _err()
+    assert block(d=40) == -1 and "multiple of 32" in _err()
+    assert block(act=2) == -2 and "two-word" in _err()
+    assert block(eps=-1.0) == -1 and "eps" in _err()
+    assert block(Wr=None) == -1 and "`Wr` is null" in _err()
+    assert block(out=0x100000 * 14 + 8) == -3 and "16-byte" in _err()
+    assert block(sb=64) == -4 and "scratch" in _err()
+    assert block(scratch=None) == -4
+    assert block(scratch=0x3000010) == -3 and "256-byte" in _err()
+    assert block(out=0x100000 * 1) == -1 and "overlaps input `h`" in _err()
+    assert block(scratch=0x100000 * 11) == -1 and "overlap" in _err()
+
+
+def norm_router(rows=1, d=64, E=4, eps=1e-6, h=A, r=B, w=C, Wr=D, s=F, x=G, xq=H, xs=J, logits=0x30000000):
+    return LIB.add_rmsnorm_router(h, r, w, ctypes.c_float(eps), Wr, rows, d, E, s, x, xq, xs, logits, None)
+
+
+def test_norm_router_refusals():
+    assert norm_router(d=8192 + 32) == -2 and "add_rmsnorm_q8 then moe_route_topk" in _err()
+    assert norm_router(E=0) == -1
+    assert norm_router(xs=None) == -1 and "together" in _err()
+    assert norm_router(x=None, xq=None, xs=None) == -1 and "neither" in _err()
+    assert norm_router(logits=None) == -1 and "`logits` is null" in _err()
+    assert norm_router(logits=A + 64) == -1 and "overlaps input `h`" in _err()
+    assert norm_router(eps=float("inf")) == -1 or norm_router(eps=-2.0) == -1
+
+
+def topk_gate_up(act=0, rows=1, d=64, dff=64, E=4, k=2, logits=A, x=B, xq=B, xs=C, h=J, hq=H, hs=0xF0000000):
+    return LIB.moe_topk_gate_up(logits, x, xq, xs, D, F, G, 0x30000000, rows, d, dff, E, k, 0x38000000, 0x3C000000,
+                                h, hq, hs, act, None)
+
+
+def test_topk_gate_up_refusals():
+    assert topk_gate_up(E=257, k=2) == -2 and "moe_route_topk then moe_gate_up" in _err()
+    assert topk_gate_up(k=5) == -1
+    assert topk_gate_up(logits=None) == -1 and "`logits` is null" in _err()
+    assert topk_gate_up(act=1, hq=None) == -1 and "`hq` is null" in _err()
+    assert topk_gate_up(act=0, h=None) == -1 and "`h` is null" in _err()
+    assert topk_gate_up(h=B) == -1 and "overlaps input" in _err()
