@@ -89,11 +89,34 @@ Q8S_DEV float wave_max(float v)
     return v;
 }
 
+template <int CTRL>
+Q8S_DEV double dpp_d(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+Q8S_DEV double readlane_d(double v, int lane)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sum over the whole wave (every lane active), the same value in every lane:
+// DPP sums within each 16-lane row, then the four row sums in order.  No LDS
+// traffic: the cross-lane permute of __shfl_xor goes through LDS and six
+// dependent steps of it cost a few hundred cycles.
 Q8S_DEV double wave_sum_f64(double v)
 {
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    v += dpp_d<DPP_XOR1>(v);
+    v += dpp_d<DPP_XOR2>(v);
+    v += dpp_d<DPP_HALF_MIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
 }
 
 // ---------------------------------------------------------------------------

@@ -61,16 +61,30 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, int e, bool valid,
     const int64_t rbase = (int64_t)(valid ? e : 0) * dff + o0;
     const int64_t hbase = (row * k + j) * dff + o0;
 
-    // A wave's items are wid, wid + NW, ...  Within an item the weight rows go
-    // out before the activation slice: waits on the vector-memory counter are
-    // in issue order.  (Requesting the next item's rows before reducing the
-    // current one measured slower for rows cut into slices: the second set of
-    // registers costs more than the overlap gains.)
+    // A wave's items are wid, wid + NW, ... (ks of them: T = NW * OPS); item i
+    // is slice i % ks of step i / ks.  For a row cut into slices, with ks
+    // dividing NW, a wave's slice never changes, so its activation slice is
+    // loaded once, before its first weight rows (waits on the vector-memory
+    // counter are in issue order); reloading it for every item measured
+    // several per cent slower on int8 rows cut into 4 slices.  Float32 slices
+    // (16 registers a chunk) and waves with a single item load their weight
+    // rows first: the activation slice then lives in registers for less time,
+    // which for float32 decides occupancy.
     const int nitems = ks * STEPS;
-    auto load_item = [&](int item, RowSlice<C>(&wg)[U], RowSlice<C>(&wu)[U], XSlice<ACT, C> &xv) {
-        const int s = item / STEPS, st = item % STEPS;
+    const bool fixed = ACT == 1 && ks > 1 && (NW % ks) == 0;
+    auto load_xs = [&](int s, XSlice<ACT, C> &xv) {
+        const int ch0 = s * LPR * C;
+        load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
+                       ACT == 1 ? xs + row * nb : nullptr, ch0, min(LPR * C, nch - ch0), lig);
+    };
+    XSlice<ACT, C> xv;
+    if (fixed && wid < nitems)
+        load_xs(wid % ks, xv);
+    for (int item = wid; item < nitems; item += NW) {
+        const int s = item % ks, st = item / ks;
         const int ch0 = s * LPR * C;
         const int sl = min(LPR * C, nch - ch0);
+        RowSlice<C> wg[U], wu[U];
         if (valid) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
@@ -79,12 +93,8 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, int e, bool valid,
                 load_row<LPR, C>(wu[u], Wuq + o * d, Wus + o * nb, ch0, sl, lig);
             }
         }
-        load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
-                       ACT == 1 ? xs + row * nb : nullptr, ch0, sl, lig);
-    };
-    auto finish_item = [&](int item, const RowSlice<C>(&wg)[U], const RowSlice<C>(&wu)[U],
-                           const XSlice<ACT, C> &xv) {
-        const int s = item / STEPS, st = item % STEPS;
+        if (!fixed)
+            load_xs(s, xv);
 #pragma unroll
         for (int u = 0; u < U; u++) {
             float g = 0.0f, v = 0.0f;
@@ -108,12 +118,6 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, int e, bool valid,
                 }
             }
         }
-    };
-    for (int item = wid; item < nitems; item += NW) {
-        RowSlice<C> wg[U], wu[U];
-        XSlice<ACT, C> xv;
-        load_item(item, wg, wu, xv);
-        finish_item(item, wg, wu, xv);
     }
     if (ks == 1 && ACT == 0)
         return;
@@ -195,12 +199,15 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
         route_finish(t.kl, t.ch, k, idx + row * k, wts + row * k);
 }
 
+// Rows a lane group takes per step of the down-combine (measured: one row a
+// step for lane groups holding 3 or 4 chunks, e.g. 22 vs 23.4 us for the
+// 8-expert block's int8 down projection).
 template <int ACT, int LPR, int C>
 constexpr int dn_unroll()
 {
     if (ACT == 0)
         return C >= 3 ? 1 : (C == 2 ? 2 : (LPR == 16 ? 2 : 4));
-    return C >= 3 ? (LPR == 16 ? 1 : 2) : (LPR == 16 ? 2 : 4);
+    return C >= 3 ? 1 : (LPR == 16 ? 2 : 4);
 }
 
 template <int ACT, int LPR, int C>
@@ -361,8 +368,12 @@ hipError_t gu_dispatch(const MoeArgs &a, hipStream_t st)
 {
     if (a.act == 0)
         return by_shape<0, F>(a, a.d, st);
+    // int8 rows past 2048: slices of 1024 values (lane groups of 64, one chunk
+    // each; measured fastest at d 4096), or of 2048 past 32 slices
     const int64_t nch = a.d / 16;
-    if (nch > 128)  // int8 rows past 2048: slices of 2048 (lane groups of 64, 2 chunks)
+    if (nch > 128 && nch <= 64 * GU_MAX_KS)
+        return F<1, 64, 1>::go(a, (int)((nch + 63) / 64), st);
+    if (nch > 128)
         return F<1, 64, 2>::go(a, (int)((nch + 127) / 128), st);
     const SliceShape sh = slice_shape(a.d);
     switch (sh.lpr * 8 + sh.c) {
