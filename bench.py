@@ -51,7 +51,8 @@ def log(*a):
 DOMINANT = {
     "moe": ("k_route_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
     "chunk": ("k_chunk_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe_chunk.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
-    "norm_gemv": ("k_gemv_rows", ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
+    "norm_gemv": ("k_norm_gemv", ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h",
+                                  "q8_gemv_sparse_amd/csrc/q8s_norm_row.h")),
 }
 
 
@@ -114,7 +115,7 @@ def parse():
                    help="launch every step eagerly instead of replaying a captured graph (for counter runs, which "
                         "profile each dispatch)")
     p.add_argument("--separate", action="store_true",
-                   help="MoE workloads: the five separate calls a step instead of one moe_ffn_block call")
+                   help="the separate calls a step instead of one moe_ffn_block / add_rmsnorm_gemv call")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU run: summarise two counter passes of this script into the traffic file")
     p.add_argument("--calib-copy-mib", type=int, default=0,
@@ -334,12 +335,14 @@ class MoeBlock(Workload):
 
 
 class NormGemv(Workload):
-    """add_rmsnorm_q8 -> q8_gemv (the 2048 -> 4096 batch-1 projection)."""
+    """The residual add + RMSNorm feeding the 2048 -> 4096 batch-1 projection:
+    one add_rmsnorm_gemv call a step (one launch); with separate=True the two
+    calls add_rmsnorm_q8 -> q8_gemv."""
 
-    dominant = "k_gemv_rows"
-    dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
+    dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h",
+                    "q8_gemv_sparse_amd/csrc/q8s_norm_row.h")
 
-    def __init__(self, name, cfg, act, copies, pool=64):
+    def __init__(self, name, cfg, act, copies, pool=64, separate=False):
         import numpy as np
         import torch
 
@@ -347,6 +350,8 @@ class NormGemv(Workload):
         import synthetic
         self.q8, self.torch, self.np = q8, torch, np
         self.name, self.act = name, act
+        self.separate = separate
+        self.dominant = "k_gemv_rows" if separate else "k_norm_gemv"
         d, n_out = cfg["d"], cfg["n_out"]
         self.d, self.n_out = d, n_out
         inp = synthetic.norm_gemv_inputs(0, d, n_out, rows=1)
@@ -374,12 +379,21 @@ class NormGemv(Workload):
         q8 = self.q8
         i = c % self.pool
         a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        if not self.separate:
+            W = self.W[c % self.copies]
+            q8.add_rmsnorm_gemv(self.h[i], self.r[i], self.w, 1e-6, W[0], W[1], act=a, sum=self.sum,
+                                y=None if a else self.y, yq=self.xq if a else None, ys=self.xs if a else None,
+                                out=self.out)
+            return
         q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y,
                           yq=self.xq if a else None, ys=self.xs if a else None, want_q8=bool(a))
         self.launch_dominant(c)
 
     def launch_dominant(self, c):
         q8 = self.q8
+        if not self.separate:
+            self.step(c)  # the step is the one fused launch
+            return
         W = self.W[c % self.copies]
         if self.act == "int8":
             q8.q8_gemv(W[0], W[1], xq=self.xq, xs=self.xs, y=self.out, act=q8.ACT_INT8)
@@ -504,7 +518,7 @@ def make_workload(name, act, copies, separate=False):
     if cfg["kind"] == "moe":
         return MoeBlock(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "norm_gemv":
-        return NormGemv(name, cfg, act, copies)
+        return NormGemv(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "chunk":
         return ChunkBlock(name, cfg, copies)
     raise SystemExit("workload %s is a parity case, not a bench workload" % name)

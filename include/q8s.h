@@ -184,6 +184,27 @@ Q8S_API int moe_down_combine(const float *h, const int8_t *hq, const float *hs,
                      float *y, int act, void *scratch, size_t scratch_bytes, void *stream);
 
 /*
+ * add_rmsnorm_gemv -- add_rmsnorm_q8 feeding a Q8_0 projection, as one call
+ * (forward_shim.rs module doc: the sum and the norm as one row kernel, the
+ * Q8_0 activation quantised in its producer's epilogue; struct Q8Ref):
+ *   sum, y (and/or yq, ys) exactly as add_rmsnorm_q8 writes them;
+ *   out[r] = Q8_0(Wq, Ws) . y[r]          (act = F32, as q8_gemv)
+ *   out[r] = Q8_0(Wq, Ws) . Q8_0(y[r])    (act = INT8, as q8_gemv)
+ * For one row of d <= 4096 it is one launch: every workgroup forms the normed
+ * row itself (re-reading h, r and w, mostly from cache) while its weight rows
+ * stream in.  Otherwise it runs add_rmsnorm_q8 then q8_gemv.
+ * h, r: device f32 [rows, d]; w: device f32 [d]; Wq: device int8
+ * [n_out, d]; Ws: device f32 [n_out, d/32]; sum: device f32 [rows, d]; y:
+ * device f32 [rows, d], required for F32, optional for INT8; yq/ys: device
+ * int8 [rows, d] and f32 [rows, d/32], both or neither, required for INT8;
+ * out: device f32 [rows, n_out].  eps >= 0.  Limits as add_rmsnorm_q8 and
+ * q8_gemv.
+ */
+Q8S_API int add_rmsnorm_gemv(const float *h, const float *r, const float *w, float eps,
+                     const int8_t *Wq, const float *Ws, int64_t rows, int64_t d, int64_t n_out,
+                     float *sum, float *y, int8_t *yq, float *ys, float *out, int act, void *stream);
+
+/*
  * add_rmsnorm_router -- add_rmsnorm_q8 with the mixture's router fused in
  * (forward_shim.rs module doc: the norm as one row kernel writing the sum;
  * fn emit_moe_forward: the router over the normed row):

@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "ACT_F32", "ACT_INT8", "FN_ROUTE", "FN_DOWN", "FN_BLOCK", "Q8sError", "LIB_PATH",
     "q8_gemv", "q8_quantize_rows", "add_rmsnorm_q8", "moe_route_topk",
-    "moe_gate_up", "moe_down_combine", "moe_ffn_block", "add_rmsnorm_router", "moe_topk_gate_up", "q8s_scratch_bytes", "q8s_last_error",
+    "moe_gate_up", "moe_down_combine", "moe_ffn_block", "add_rmsnorm_router", "moe_topk_gate_up",
+    "add_rmsnorm_gemv", "q8s_scratch_bytes", "q8s_last_error",
     "q8s_version", "library",
 ]
 
@@ -50,6 +51,7 @@ _SIGS = {
     "moe_down_combine": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, ctypes.c_int, _p, _sz, _p],
     "moe_ffn_block": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p,
                       _p, _p, ctypes.c_int, _p, _sz, _p],
+    "add_rmsnorm_gemv": [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, ctypes.c_int, _p],
     "add_rmsnorm_router": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "moe_topk_gate_up": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                          ctypes.c_int, _p],
@@ -336,3 +338,32 @@ def moe_topk_gate_up(logits, Wgq, Wgs, Wuq, Wus, k, x=None, xq=None, xs=None, id
                                  _ptr(Wus), rows, d, dff, E, k, _ptr(idx), _ptr(wts), _ptr(h), _ptr(hq), _ptr(hs), act,
                                  _stream(stream)))
     return idx, wts, h, hq, hs
+
+
+def add_rmsnorm_gemv(h, r, w, eps, Wq, Ws, act=ACT_F32, sum=None, y=None, yq=None, ys=None, out=None,
+                     want_f32=None, want_q8=None, stream=None):
+    """add_rmsnorm_q8 feeding q8_gemv in one call.  Returns (sum, y or None,
+    yq or None, ys or None, out).  By default the normed row is written in the
+    form the projection reads (f32 for ACT_F32, Q8_0 for ACT_INT8)."""
+    _dev(h, torch.float32, "h"); _dev(r, torch.float32, "r"); _dev(w, torch.float32, "w")
+    _dev(Wq, torch.int8, "Wq"); _dev(Ws, torch.float32, "Ws")
+    n_out, d = Wq.shape
+    rows = h.numel() // d
+    dev = h.device
+    want_f32 = (act == ACT_F32) if want_f32 is None else want_f32
+    want_q8 = (act == ACT_INT8) if want_q8 is None else want_q8
+    if sum is None:
+        sum = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_f32 and y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_q8 and yq is None:
+        yq = torch.empty((rows, d), dtype=torch.int8, device=dev)
+        ys = torch.empty((rows, d // 32), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((rows, n_out), dtype=torch.float32, device=dev)
+    for t, dt, n in ((sum, torch.float32, "sum"), (y, torch.float32, "y"), (yq, torch.int8, "yq"),
+                     (ys, torch.float32, "ys"), (out, torch.float32, "out")):
+        _dev(t, dt, n)
+    _check(_lib.add_rmsnorm_gemv(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wq), _ptr(Ws), rows, d, n_out, _ptr(sum),
+                                 _ptr(y), _ptr(yq), _ptr(ys), _ptr(out), act, _stream(stream)))
+    return sum, y, yq, ys, out

@@ -347,6 +347,53 @@ int moe_down_combine(const float *h, const int8_t *hq, const float *hs, const in
     return launched(q8s::down_launch(a, as_stream(stream)), fn);
 }
 
+int add_rmsnorm_gemv(const float *h, const float *r, const float *w, float eps, const int8_t *Wq, const float *Ws,
+                     int64_t rows, int64_t d, int64_t n_out, float *sum, float *y, int8_t *yq, float *ys, float *out,
+                     int act, void *stream)
+{
+    const char *fn = "add_rmsnorm_gemv";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_count(fn, "rows", rows, 65535)) || (rc = check_dim32(fn, "d", d)) ||
+        (rc = check_count(fn, "n_out", n_out, INT32_MAX / 2)))
+        return rc;
+    if (!(eps >= 0.0f) || eps != eps)
+        return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    if ((yq == nullptr) != (ys == nullptr))
+        return fail(Q8S_EINVAL, "%s: `yq` and `ys` are given together or not at all", fn);
+    if (act == Q8S_ACT_F32 && !y)
+        return fail(Q8S_EINVAL, "%s: f32 numerics read the normed row: `y` is required", fn);
+    if (act == Q8S_ACT_INT8 && !yq)
+        return fail(Q8S_EINVAL, "%s: int8 numerics read the normed row's Q8_0 form: `yq`/`ys` are required", fn);
+    const size_t n = (size_t)(rows * d);
+    std::vector<Span> ins = {{h, n * 4, "h"},
+                             {r, n * 4, "r"},
+                             {w, (size_t)d * 4, "w"},
+                             {Wq, (size_t)(n_out * d), "Wq"},
+                             {Ws, (size_t)n_out * (size_t)(d / 32) * 4, "Ws"}};
+    std::vector<Span> outs = {{sum, n * 4, "sum"}, {out, (size_t)(rows * n_out) * 4, "out"}};
+    if (y)
+        outs.push_back({y, n * 4, "y"});
+    if (yq) {
+        outs.push_back({yq, n, "yq"});
+        outs.push_back({ys, n / 32 * 4, "ys"});
+    }
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    const hipStream_t st = as_stream(stream);
+    if (q8s::norm_gemv_supported(rows, d)) {
+        q8s::NormGemvArgs a{h, r, w, eps, Wq, Ws, d, n_out, sum, y, yq, ys, out, act};
+        return launched(q8s::norm_gemv_launch(a, st), fn);
+    }
+    hipError_t e = q8s::add_rmsnorm_launch(h, r, w, rows, d, eps, sum, y, yq, ys, st);
+    if (e == hipSuccess) {
+        q8s::GemvArgs g{Wq, Ws, n_out, d, act == 0 ? y : nullptr, act == 1 ? yq : nullptr, act == 1 ? ys : nullptr,
+                        rows, out, act};
+        e = q8s::gemv_launch(g, st);
+    }
+    return launched(e, fn);
+}
+
 int add_rmsnorm_router(const float *h, const float *r, const float *w, float eps, const float *Wr, int64_t rows,
                        int64_t d, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits, void *stream)
 {

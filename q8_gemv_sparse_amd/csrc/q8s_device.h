@@ -202,6 +202,23 @@ Q8S_DEV void load_row(RowSlice<C> &w, const int8_t *__restrict__ rowq, const flo
     }
 }
 
+// load_row without branches, for straight-line load sequences (the
+// vector-memory wait before a use can then count exactly the loads issued
+// after it): chunks past the slice read the slice's last chunk instead of
+// zeros.  Only for use against an activation slice whose chunks past the
+// slice are zero (load_x zeroes them), which makes those products vanish.
+template <int LPR, int C>
+Q8S_DEV void load_row_flat(RowSlice<C> &w, const int8_t *__restrict__ rowq, const float *__restrict__ rows, int ch0,
+                           int nch, int lig)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        const int ch = min(c * LPR + lig, nch - 1);
+        w.q[c] = ld_stream16(rowq + (int64_t)(ch0 + ch) * 16);
+        w.s[c] = ld_stream_f32(rows + ((ch0 + ch) >> 1));
+    }
+}
+
 template <int LPR, int C>
 Q8S_DEV void load_x(XSlice<0, C> &x, const float *__restrict__ xr, const int8_t *, const float *, int ch0, int nch, int lig)
 {

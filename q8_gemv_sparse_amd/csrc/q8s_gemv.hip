@@ -1,6 +1,9 @@
 // q8s_gemv.hip -- Q8_0 matrix x activation rows on gfx950.
 //
-// Two kernels:
+// Three kernels:
+//   k_norm_gemv   batch 1 with the residual add + RMSNorm fused in: every
+//                 workgroup forms the normed row itself, then streams its
+//                 rows against it (no launch waits for a norm launch).
 //   k_gemv_rows   the streaming GEMV for batch 1 and small m: weights stream
 //                 from HBM once, every activation row a wave serves sits in
 //                 its registers.  f32 activations (dequantise in kernel) or
@@ -15,6 +18,7 @@
 //                 fn emit_marlin_q8_gemm, codegen_cuda::qwen_emit module page).
 #include "q8s_device.h"
 #include "q8s_internal.h"
+#include "q8s_norm_row.h"
 
 namespace q8s {
 
@@ -122,6 +126,98 @@ __global__ void __launch_bounds__(SPLIT ? 512 : 256) k_gemv_rows(const int8_t *_
             }
             __syncthreads();
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// add + norm fused into the batch-1 GEMV
+//
+// Every 256-thread workgroup requests the row's h, r and w and then its weight
+// rows (which do not depend on the norm, so their latency overlaps it), forms
+// the row's add + norm exactly as add_rmsnorm_q8 does (q8s_norm_row.h) into
+// LDS -- float32, or
+// its Q8_0 form in int8 numerics -- and each wave then forms its U row groups'
+// dots against the LDS row.  The price of no norm launch is the row's h, r
+// and w re-read by every workgroup (12 bytes a value, mostly from cache).  The
+// workgroup of row block 0 also writes the sum and the normed row.  The row
+// fits one wave's slice (n_in <= 4096) and at most two 2048-value segments.
+template <int ACT, int LPR, int C, int SEGS, int U>
+__global__ void __launch_bounds__(NORM_THREADS)
+    k_norm_gemv(const float *__restrict__ h, const float *__restrict__ r, const float *__restrict__ w, int d,
+                float eps, const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out,
+                float *__restrict__ sum, float *__restrict__ y, int8_t *__restrict__ yq, float *__restrict__ ys,
+                float *__restrict__ out)
+{
+    constexpr int G = WAVE / LPR;
+    constexpr int RB = G * U;
+    constexpr int NX = NORM_SEG * SEGS;
+    __shared__ double wsum[NORM_THREADS / WAVE];
+    __shared__ __align__(16) float xf[ACT == 0 ? NX : 4];
+    __shared__ __align__(16) int8_t xqs[ACT == 1 ? NX : 16];
+    __shared__ __align__(16) float xss[ACT == 1 ? NX / QB : 4];
+    const int lane = threadIdx.x & 63, lig = lane % LPR, grp = lane / LPR;
+    const int wid = threadIdx.x >> 6;
+    const int nch = d >> 4, nb = d >> 5;
+    const bool writer = blockIdx.x == 0;
+    const int64_t rb = (int64_t)blockIdx.x * (NORM_THREADS / WAVE) + wid;
+    const bool rows = rb * RB < n_out;
+
+    // h, r and w first, then the weight rows: waits on the vector-memory
+    // counter are in issue order, so the norm can start once its (cached)
+    // inputs land while the weight rows are still streaming in
+    const int t8 = threadIdx.x * 8;
+    NormShare<SEGS> n;
+    f32x4 rr4[SEGS][2];
+    norm_load_raw<SEGS>(n, rr4, h, r, w, d, t8);
+    RowSlice<C> wr[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int o = min((int)(rb * RB) + u * G + grp, n_out - 1);
+        load_row_flat<LPR, C>(wr[u], Wq + (int64_t)o * d, Ws + (int64_t)o * nb, 0, nch, lig);
+    }
+    norm_add<SEGS>(n, rr4, d, t8);
+    if (writer) {
+#pragma unroll
+        for (int g = 0; g < SEGS; g++) {
+            const int base = t8 + g * NORM_SEG;
+            if (base < d) {
+                *reinterpret_cast<f32x4 *>(sum + base) = n.sv[g][0];
+                *reinterpret_cast<f32x4 *>(sum + base + 4) = n.sv[g][1];
+            }
+        }
+    }
+    const double inv = norm_inv(norm_squares<SEGS>(n, d, t8), d, eps, wsum);
+#pragma unroll
+    for (int g = 0; g < SEGS; g++) {
+        const int base = t8 + g * NORM_SEG;
+        if (base < d) {
+            float v[8];
+            norm_values(n.sv[g][0], n.sv[g][1], n.wv[g][0], n.wv[g][1], inv, v);
+            if (ACT == 0) {
+                *reinterpret_cast<f32x4 *>(xf + base) = f32x4{v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4 *>(xf + base + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            } else {
+                quant8_store(v, xqs + base, xss + base / QB, (threadIdx.x & 3) == 0);
+            }
+            if (writer && y) {
+                *reinterpret_cast<f32x4 *>(y + base) = f32x4{v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4 *>(y + base + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            }
+            if (writer && yq)
+                quant8_store(v, yq + base, ys + base / QB, (threadIdx.x & 3) == 0);
+        }
+    }
+    __syncthreads();
+    if (!rows)
+        return;
+    XSlice<ACT, C> xv;
+    load_x<LPR, C>(xv, xf, xqs, xss, 0, nch, lig);
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const float a = group_sum<LPR>(row_dot(wr[u], xv, lig));
+        const int o = (int)(rb * RB) + u * G + grp;
+        if (lig == 0 && o < n_out)
+            out[o] = a;
     }
 }
 
@@ -293,6 +389,53 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t st)
     }
     const SliceShape sh = slice_shape(a.n_in);
     return a.act == 0 ? launch_act<0>(a, sh, st) : launch_act<1>(a, sh, st);
+}
+
+bool norm_gemv_supported(int64_t rows, int64_t d)
+{
+    return rows == 1 && d <= 2 * 2048 && slice_shape(d).ks == 1;
+}
+
+namespace {
+
+template <int ACT, int LPR, int C, int SEGS>
+hipError_t norm_gemv_go(const NormGemvArgs &a, hipStream_t st)
+{
+    // eight (or six) 16-byte loads a lane in flight: U row groups of C chunks
+    constexpr int U = C <= 2 ? 4 : 2;
+    constexpr int RB = (WAVE / LPR) * U;
+    const int64_t nrb = (a.n_out + RB - 1) / RB;
+    const dim3 grid((unsigned)((nrb + NORM_THREADS / WAVE - 1) / (NORM_THREADS / WAVE)));
+    hipLaunchKernelGGL((k_norm_gemv<ACT, LPR, C, SEGS, U>), grid, dim3(NORM_THREADS), 0, st, a.h, a.r, a.w, (int)a.d,
+                       a.eps, a.Wq, a.Ws, (int)a.n_out, a.sum, a.y, a.yq, a.ys, a.out);
+    return hipGetLastError();
+}
+
+// a row of at most 2048 values is one segment; rows in (2048, 4096] take lane
+// groups of 64 with 4 chunks and two segments
+template <int ACT>
+hipError_t norm_gemv_shape(const NormGemvArgs &a, hipStream_t st)
+{
+    const SliceShape sh = slice_shape(a.d);
+    switch (sh.lpr * 8 + sh.c) {
+    case 16 * 8 + 1:
+        return norm_gemv_go<ACT, 16, 1, 1>(a, st);
+    case 16 * 8 + 3:
+        return norm_gemv_go<ACT, 16, 3, 1>(a, st);
+    case 64 * 8 + 1:
+        return norm_gemv_go<ACT, 64, 1, 1>(a, st);
+    case 64 * 8 + 2:
+        return norm_gemv_go<ACT, 64, 2, 1>(a, st);
+    default:
+        return norm_gemv_go<ACT, 64, 4, 2>(a, st);
+    }
+}
+
+} // namespace
+
+hipError_t norm_gemv_launch(const NormGemvArgs &a, hipStream_t st)
+{
+    return a.act == 0 ? norm_gemv_shape<0>(a, st) : norm_gemv_shape<1>(a, st);
 }
 
 } // namespace q8s

@@ -62,6 +62,21 @@ struct GemvArgs {
 };
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t st);
 
+// add + norm fused into the batch-1 GEMV (one row, d <= 4096)
+struct NormGemvArgs {
+    const float *h, *r, *w;
+    float eps;
+    const int8_t *Wq;
+    const float *Ws;
+    int64_t d, n_out;
+    float *sum, *y;
+    int8_t *yq;
+    float *ys, *out;
+    int act;
+};
+bool norm_gemv_supported(int64_t rows, int64_t d);
+hipError_t norm_gemv_launch(const NormGemvArgs &a, hipStream_t st);
+
 hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st);
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               float *sum, float *y, int8_t *yq, float *ys, hipStream_t st);

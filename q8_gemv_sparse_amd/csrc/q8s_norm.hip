@@ -13,77 +13,9 @@
 // float32 once: that float32 value decides the int8 codes.
 #include "q8s_device.h"
 #include "q8s_internal.h"
+#include "q8s_norm_row.h"
 
 namespace q8s {
-
-constexpr int NORM_THREADS = 256;
-constexpr int NORM_SEG = NORM_THREADS * 8;
-
-// A thread's share of one row for rows of at most SEGS 2048-value segments:
-// its 8 values of each segment (the float32 sums) and their norm weights,
-// kept in registers between the two passes.
-template <int SEGS>
-struct NormShare {
-    f32x4 sv[SEGS][2], wv[SEGS][2];
-};
-
-template <int SEGS>
-Q8S_DEV void norm_load(NormShare<SEGS> &n, const float *hr, const float *rr, const float *w, int d, int t8)
-{
-#pragma unroll
-    for (int g = 0; g < SEGS; g++) {
-        const int base = t8 + g * NORM_SEG;
-        if (base < d) {
-            const f32x4 a0 = ldf4(hr + base), a1 = ldf4(hr + base + 4);
-            const f32x4 b0 = ldf4(rr + base), b1 = ldf4(rr + base + 4);
-            n.wv[g][0] = ldf4(w + base);
-            n.wv[g][1] = ldf4(w + base + 4);
-            n.sv[g][0] = a0 + b0;
-            n.sv[g][1] = a1 + b1;
-        }
-    }
-}
-
-// 1/sqrt(mean(sum^2) + eps) of the row, in double: each thread's squares in
-// order, then the wave sums, then the four waves in order.  Every thread of
-// the workgroup calls it (it synchronises the workgroup once).
-Q8S_DEV double norm_inv(double ss, int d, float eps, double *wsum)
-{
-    ss = wave_sum_f64(ss);
-    if ((threadIdx.x & 63) == 0)
-        wsum[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int i = 0; i < NORM_THREADS / WAVE; i++)
-        tot += wsum[i];
-    return 1.0 / sqrt(tot / (double)d + (double)eps);
-}
-
-template <int SEGS>
-Q8S_DEV double norm_squares(const NormShare<SEGS> &n, int d, int t8)
-{
-    double ss = 0.0;
-#pragma unroll
-    for (int g = 0; g < SEGS; g++) {
-        if (t8 + g * NORM_SEG < d) {
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                ss += (double)n.sv[g][0][i] * (double)n.sv[g][0][i] + (double)n.sv[g][1][i] * (double)n.sv[g][1][i];
-        }
-    }
-    return ss;
-}
-
-// The normalised values of segment g, formed in double and rounded once.
-Q8S_DEV void norm_values(f32x4 s0, f32x4 s1, f32x4 w0, f32x4 w1, double inv, float (&v)[8])
-{
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        v[i] = (float)(((double)s0[i] * inv) * (double)w0[i]);
-        v[4 + i] = (float)(((double)s1[i] * inv) * (double)w1[i]);
-    }
-}
 
 // SEGS > 0: the row has at most SEGS 2048-value segments (NormShare).
 // SEGS == 0: any length; the second pass re-forms the sums from h and r (the
@@ -153,8 +85,7 @@ __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__
 // row forms the whole normed row -- it re-reads h, r and w, 24 bytes a value,
 // mostly from cache -- so no workgroup waits for another; the workgroup of
 // expert 0 also writes the sum and the activation the gate-up launch reads
-// (float32 x and/or its Q8_0 form, whichever is given).  The router row's
-// loads are issued first: they do not depend on the norm.
+// (float32 x and/or its Q8_0 form, whichever is given).
 template <int SEGS>
 __global__ void __launch_bounds__(NORM_THREADS)
     k_norm_logits(const float *__restrict__ h, const float *__restrict__ r, const float *__restrict__ w, int d,
@@ -169,17 +100,20 @@ __global__ void __launch_bounds__(NORM_THREADS)
     const int t8 = threadIdx.x * 8;
     const float *wr = Wr + (int64_t)e * d;
 
+    // h, r and w first, then the router row: waits on the vector-memory
+    // counter are in issue order, so the norm can start once its (cached)
+    // inputs land while the router row is still streaming in
+    NormShare<SEGS> n;
+    f32x4 rr4[SEGS][2];
+    norm_load_raw<SEGS>(n, rr4, h + row * d, r + row * d, w, d, t8);
     f32x4 rv[SEGS][2];
 #pragma unroll
     for (int g = 0; g < SEGS; g++) {
-        const int base = t8 + g * NORM_SEG;
-        if (base < d) {
-            rv[g][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base));
-            rv[g][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base + 4));
-        }
+        const int base = min(t8 + g * NORM_SEG, d - 8);  // no branch: see norm_load_raw
+        rv[g][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base));
+        rv[g][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base + 4));
     }
-    NormShare<SEGS> n;
-    norm_load<SEGS>(n, h + row * d, r + row * d, w, d, t8);
+    norm_add<SEGS>(n, rr4, d, t8);
     if (writer) {
 #pragma unroll
         for (int g = 0; g < SEGS; g++) {

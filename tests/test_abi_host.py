@@ -190,3 +190,19 @@ def test_topk_gate_up_refusals():
     assert topk_gate_up(act=1, hq=None) == -1 and "`hq` is null" in _err()
     assert topk_gate_up(act=0, h=None) == -1 and "`h` is null" in _err()
     assert topk_gate_up(h=B) == -1 and "overlaps input" in _err()
+
+
+def norm_gemv(act=0, rows=1, d=64, n_out=64, eps=1e-6, h=A, r=B, w=C, Wq=D, Ws=F, s=G, y=H, yq=J, ys=0x30000000,
+              out=0x38000000):
+    return LIB.add_rmsnorm_gemv(h, r, w, ctypes.c_float(eps), Wq, Ws, rows, d, n_out, s, y, yq, ys, out, act, None)
+
+
+def test_norm_gemv_refusals():
+    assert norm_gemv(d=48) == -1 and "multiple of 32" in _err()
+    assert norm_gemv(act=0, y=None) == -1 and "`y` is required" in _err()
+    assert norm_gemv(act=1, yq=None, ys=None) == -1 and "`yq`/`ys` are required" in _err()
+    assert norm_gemv(ys=None) == -1 and "together" in _err()
+    assert norm_gemv(eps=-1.0) == -1 and "eps" in _err()
+    assert norm_gemv(out=None) == -1 and "`out` is null" in _err()
+    assert norm_gemv(out=D + 64) == -1 and "overlaps input `Wq`" in _err()
+    assert norm_gemv(act=2) == -2
