@@ -241,14 +241,16 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
         const int64_t hrow = (row * k + j) * dff;
         const int64_t rbase = (int64_t)(valid ? e : 0) * d + o0;
         // Each step's weight rows are requested before the previous step is
-        // reduced.
+        // reduced.  The loads are straight-line code (an invalid choice reads
+        // expert 0's rows and is zeroed at the dot; chunks past the slice meet
+        // zero activations), so the wait before a step's dots counts only
+        // the next step's loads: with a branch in between the wait would
+        // cover every load issued, the next step's included.
         auto load_step = [&](RowSlice<C>(&w)[UU], int st) {
-            if (valid) {
 #pragma unroll
-                for (int u = 0; u < UU; u++) {
-                    const int64_t o = rbase + st * OPS + u * G + grp;
-                    load_row<LPR, C>(w[u], Wdq + o * dff, Wds + o * nb, ch0, sl, lig);
-                }
+            for (int u = 0; u < UU; u++) {
+                const int64_t o = rbase + st * OPS + u * G + grp;
+                load_row_flat<LPR, C>(w[u], Wdq + o * dff, Wds + o * nb, ch0, sl, lig);
             }
         };
         // The hidden row's chunks are requested first (they come from cache),
