@@ -249,7 +249,7 @@ class MoeBlock(Workload):
         idx = self.idx[c % self.copies]
         if a == q8.ACT_INT8:
             q8.moe_gate_up(W[1], W[2], W[3], W[4], idx, self.E, xq=self.xq, xs=self.xs, hq=self.hq, hs=self.hs,
-                           act=a, want_h=False)
+                           h=self.hf if self.rows > 1 else None, act=a, want_h=False)
         else:
             q8.moe_gate_up(W[1], W[2], W[3], W[4], idx, self.E, x=self.y, h=self.hf, act=a)
 

@@ -157,7 +157,9 @@ Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_
  * x: device f32 [rows, d] (F32) or NULL; xq/xs: device Q8_0 [rows, d] (INT8)
  * or NULL.  Wgq/Wuq: device int8 [E*dff, d]; Wgs/Wus: device f32
  * [E*dff, d/32].  idx: device int32 [rows, k].  h: device f32
- * [rows, k, dff] (required for F32, optional for INT8).  hq/hs: device int8
+ * [rows, k, dff] (required for F32, and for INT8 with rows > 1, where the
+ * grouped chunk kernels stage the float32 hidden rows in it before a quantise
+ * pass forms hq/hs; optional for INT8 with one row).  hq/hs: device int8
  * [rows, k, dff] and f32 [rows, k, dff/32] (INT8 only, required).  A choice
  * whose expert index is invalid gets zeros.
  */

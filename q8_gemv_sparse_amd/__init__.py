@@ -194,7 +194,8 @@ def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq
                 want_h=True, stream=None):
     """h[rows, k, dff] = SiLU(Wg[e] x) * (Wu[e] x) for each kept expert e.
     Returns (h, hq, hs): INT8 also writes the hidden row's Q8_0 form; h may be
-    skipped there (want_h=False)."""
+    skipped there for one row (want_h=False); with several rows it is the
+    chunk kernels' staging and is always written."""
     for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq")):
         _dev(t, torch.int8, n)
     for t, n in ((Wgs, "Wgs"), (Wus, "Wus")):
@@ -212,7 +213,7 @@ def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq
             hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
         if hs is None:
             hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
-    if h is None and (want_h or act == ACT_F32):
+    if h is None and (want_h or act == ACT_F32 or rows > 1):  # several int8 rows stage h
         h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)
     _dev(h, torch.float32, "h"); _dev(hq, torch.int8, "hq"); _dev(hs, torch.float32, "hs")
     _check(_lib.moe_gate_up(_ptr(x), _ptr(xq), _ptr(xs), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq), _ptr(Wus), _ptr(idx),

@@ -263,6 +263,9 @@ int moe_gate_up(const float *x, const int8_t *xq, const float *xs, const int8_t 
         ins.push_back({x, (size_t)(rows * d) * 4, "x"});
         outs.push_back({h, nh * 4, "h"});
     } else {
+        if (rows > 1 && !h)
+            return fail(Q8S_EINVAL, "%s: int8 numerics with rows > 1: `h` is required (the grouped chunk kernels "
+                        "stage the float32 hidden rows there before forming their Q8_0 form)", fn);
         ins.push_back({xq, (size_t)(rows * d), "xq"});
         ins.push_back({xs, (size_t)(rows * d / 32) * 4, "xs"});
         if (h)

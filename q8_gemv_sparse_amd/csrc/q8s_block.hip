@@ -20,7 +20,8 @@
 // Scratch, 256-byte aligned pieces in this order: the logits (double
 // [rows, E]), the normed row x (f32 [rows, d]), its Q8_0 form (int8
 // [rows, d] + f32 [rows, d/32]), the hidden rows (f32 [rows, k, dff] in f32
-// numerics, or their Q8_0 form in int8), then moe_down_combine's scratch.
+// numerics; their Q8_0 form in int8, plus the f32 rows when rows > 1), then
+// moe_down_combine's scratch.
 #include "q8s_device.h"
 #include "q8s_internal.h"
 
@@ -57,6 +58,8 @@ BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t E, 
         s.xs = reinterpret_cast<float *>(take((size_t)(rows * d / QB) * 4));
         s.hq = reinterpret_cast<int8_t *>(take(nh));
         s.hs = reinterpret_cast<float *>(take(nh / QB * 4));
+        if (rows > 1)  // the chunk kernels stage the float32 hidden rows
+            s.h = reinterpret_cast<float *>(take(nh * 4));
     } else {
         s.h = reinterpret_cast<float *>(take(nh * 4));
     }

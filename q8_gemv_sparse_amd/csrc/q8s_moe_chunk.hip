@@ -7,13 +7,15 @@
 // choice's weighed result (arena.rs fn scratch: the grouped list, and `pa`,
 // per choice, combined per row).  Here, in one-word int8 numerics:
 //
-//   k_chunk_gate_up  one workgroup per (expert e, 32 hidden outputs).  One wave
-//                    gathers, in choice order, the choices routed to e (a
-//                    ballot compaction over idx).  Each wave loads its gate and
-//                    up weight rows into registers once, then applies them to
-//                    the gathered choices' activation rows four at a time
-//                    (v_dot4_i32_i8, exact int32 block sums).  The epilogue
-//                    writes SiLU(g)*u and its Q8_0 form per choice row.
+//   k_chunk_gate_up  one workgroup per (expert e, tile of 8 or 16 hidden
+//                    outputs).  One wave gathers, in choice order, the choices
+//                    routed to e (a ballot compaction over idx).  Each wave
+//                    loads its gate and up weight rows into registers once,
+//                    then applies them to the gathered choices' activation
+//                    rows two at a time (v_dot4_i32_i8, exact int32 block
+//                    sums).  The epilogue writes SiLU(g)*u per choice row in
+//                    float32; a quantise pass (k_quantize_rows) then writes
+//                    the hidden rows' Q8_0 form.
 //   k_chunk_down     one workgroup per (expert e, tile of outputs): the same
 //                    scheme over Wd[e], writing each choice's result pa[c][o].
 //   k_chunk_combine  y[r][o] = sum_j wts[r][j] * pa[r*K + j][o], slot order.
@@ -77,8 +79,7 @@ template <int LPR, int C>
 __global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
     k_chunk_gate_up(const int8_t *__restrict__ xq, const float *__restrict__ xs, const int8_t *__restrict__ Wgq,
                     const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq, const float *__restrict__ Wus,
-                    const int32_t *__restrict__ idx, int nchoice, int k, int d, int dff, int E, float *__restrict__ h,
-                    int8_t *__restrict__ hq, float *__restrict__ hs)
+                    const int32_t *__restrict__ idx, int nchoice, int k, int d, int dff, int E, float *__restrict__ h)
 {
     using S = ChunkGuShape<LPR, C>;
     constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, CG = S::CG;
@@ -89,7 +90,7 @@ __global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
     const int e = blockIdx.y;
     const int o0 = blockIdx.x * T;
-    const int nt = min(T, dff - o0);  // outputs of this tile (a multiple of 32)
+    const int nt = T;  // tiles divide a 32-value block, so they divide dff
     const int nch = d >> 4, nb = d >> 5;
     const int st = wid;  // each wave takes one step of the tile (T = NW * OPS)
 
@@ -125,23 +126,10 @@ __global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
             }
         }
         __syncthreads();
-        // epilogue: a 32-lane half-wave per (choice row, block) of the tile
-        const int nblk = nt / QB;
-        for (int item = threadIdx.x / QB; item < n * nblk; item += blockDim.x / QB) {
-            const int rr = item / nblk, bk = item % nblk;
-            const int t = bk * QB + threadIdx.x % QB;
-            const float v = e < E ? hv[rr][t] : 0.0f;
-            const int64_t off = (int64_t)list[rr] * dff + o0 + t;
-            if (h)
-                h[off] = v;
-            float amax = fabsf(v);
-            for (int o = 16; o >= 1; o >>= 1)
-                amax = fmaxf(amax, __shfl_xor(amax, o));
-            const float dsc = q8_scale(amax);
-            const float id = q8_inv(dsc);
-            hq[off] = (int8_t)q8_code(v, id);
-            if (threadIdx.x % QB == 0)
-                hs[off / QB] = dsc;
+        // epilogue: the tile's float32 hidden values of every gathered choice
+        for (int item = threadIdx.x; item < n * nt; item += blockDim.x) {
+            const int rr = item / nt, t = item % nt;
+            h[(int64_t)list[rr] * dff + o0 + t] = e < E ? hv[rr][t] : 0.0f;
         }
         if (total <= first + CK_PASS)
             break;
@@ -149,17 +137,19 @@ __global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
     }
 }
 
-// Down: NW waves; each streams R = STEPS * G rows of Wd[e], all loaded up
-// front (about 16-24 16-byte loads a lane), then applies them to the
-// gathered choices CG at a time.  Outputs per workgroup TO = NW * R.
+// Down: NW waves; each streams R = SW * G rows of Wd[e], all loaded up
+// front (6-8 16-byte loads a lane), then applies them to the gathered
+// choices CG at a time.  Outputs per workgroup TO = NW * R.  Small
+// workgroups, several to a CU, as for the chunk gate-up (measured 53 vs 64 us
+// for the 64-row chunk's down projection at dff 768).
 template <int LPR, int C>
 struct CkDownShape {
-    static constexpr int NW = 8;
+    static constexpr int NW = 4;
     static constexpr int G = WAVE / LPR;
-    static constexpr int SW = C >= 3 ? 4 : (C == 2 ? 8 : 16);  // row steps a wave holds at once
+    static constexpr int SW = C >= 3 ? 2 : (C == 2 ? 4 : 8);  // row steps a wave holds at once
     static constexpr int R = SW * G;
     static constexpr int TO = NW * R;
-    static constexpr int CG = C >= 3 ? 2 : 4;
+    static constexpr int CG = C >= 3 ? 1 : 2;
 };
 
 template <int LPR, int C>
@@ -242,10 +232,14 @@ template <int LPR, int C>
 hipError_t gu_chunk_go(const MoeArgs &a, hipStream_t st)
 {
     using S = ChunkGuShape<LPR, C>;
-    dim3 grid((unsigned)((a.dff + S::T - 1) / S::T), (unsigned)(a.E + 1));  // + one row for invalid choices
+    dim3 grid((unsigned)(a.dff / S::T), (unsigned)(a.E + 1));  // + one row for invalid choices
     hipLaunchKernelGGL((k_chunk_gate_up<LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
-                       a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h, a.hq, a.hs);
-    return hipGetLastError();
+                       a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    // the hidden rows' Q8_0 form, for the down projection
+    return quantize_launch(a.h, a.rows * a.k, a.dff, a.hq, a.hs, st);
 }
 
 template <int LPR, int C>

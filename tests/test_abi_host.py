@@ -113,6 +113,8 @@ def test_gate_up_refusals():
     assert gate_up(act=0, h=None) == -1 and "`h` is null" in _err()
     assert gate_up(act=2) == -2
     assert gate_up(h=C) == -1 and "overlaps input `Wgq`" in _err()
+    # several int8 rows stage the float32 hidden rows in h
+    assert gate_up(act=1, rows=2, h=None) == -1 and "`h` is required" in _err()
 
 
 def test_down_refusals():
