@@ -222,13 +222,22 @@ __global__ void __launch_bounds__(NORM_THREADS)
 }
 
 // ---------------------------------------------------------------------------
-// int8 MFMA GEMM (m >= 16)
+// int8 MFMA GEMM (m >= GEMM_MIN_ROWS)
 //
 // Workgroup tile: 16 outputs x 64 rows (four 16-row MFMA tiles); its four
-// waves take interleaved Q8_0 blocks of k.  Per block and row tile one
-// v_mfma_i32_16x16x32_i8 yields the 16x16 exact int32 block sums; each lane
-// then adds isum * (ws[o][b] * xs[r][b]) for the four (r, o) it holds.  The
-// four waves' float partials are summed in wave order through LDS.
+// waves take interleaved Q8_0 blocks of k (wave w: blocks w, w + 4, ...).  Per
+// block and row tile one v_mfma_i32_16x16x32_i8 yields the 16x16 exact int32
+// block sums; each lane then adds isum * (ws[o][b] * xs[r][b]) for the four
+// (r, o) it holds.  The four waves' float partials are summed in wave order
+// through LDS.
+//
+// Latency is the whole cost at these sizes (9.4 MB of weights), so:
+//   * every activation scale of the tile goes to LDS once, up front (one
+//     barrier, not one per pass of k);
+//   * a wave requests all its weight fragments and scales before its first
+//     MFMA, in straight-line code (GEMM_WB blocks a wave at most);
+//   * activation fragments (from cache) are requested a batch of GEMM_AB
+//     blocks ahead of the MFMAs that use them.
 //
 // Operand layout of v_mfma_i32_16x16x32_i8 (lane l, j = l%16, g = l/16):
 //   A (16x32, rows x k):    A[j][8g .. 8g+7]
@@ -239,14 +248,16 @@ __global__ void __launch_bounds__(NORM_THREADS)
 
 constexpr int GEMM_TN = 16;
 constexpr int GEMM_TM = 64;
-constexpr int GEMM_KC = 16; // Q8_0 blocks staged per pass
+constexpr int GEMM_PB = 64;            // Q8_0 blocks of k per pass
+constexpr int GEMM_WQ = GEMM_PB / 4;   // of which one wave takes
+constexpr int GEMM_AB = 4;             // activation blocks requested ahead
 
 __global__ void __launch_bounds__(256) k_gemm_i8(const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out,
                                                  int n_in, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                  int m, float *__restrict__ y)
 {
     typedef int v4i __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) float xsT[GEMM_KC][GEMM_TM];  // activation scales, block-major
+    __shared__ __attribute__((aligned(16))) float xsT[GEMM_PB][GEMM_TM];  // activation scales, block-major
     __shared__ float red[4][GEMM_TM][GEMM_TN + 1];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -269,29 +280,55 @@ __global__ void __launch_bounds__(256) k_gemm_i8(const int8_t *__restrict__ Wq, 
         for (int i = 0; i < 4; i++)
             acc[t][i] = 0.0f;
 
-    for (int kb0 = 0; kb0 < nb; kb0 += GEMM_KC) {
-        __syncthreads();
-        for (int e = threadIdx.x; e < GEMM_KC * GEMM_TM; e += blockDim.x) {
-            const int r = e / GEMM_KC, bb = e % GEMM_KC;
-            const int rr = min(rt0 + r, m - 1), b = min(kb0 + bb, nb - 1);
-            xsT[bb][r] = xs[(int64_t)rr * nb + b];
+    for (int p0 = 0; p0 < nb; p0 += GEMM_PB) {
+        // the wave's weight fragments and scales of this pass (blocks
+        // p0 + wid + 4q), all requested at once in straight-line code; a block
+        // past the row re-reads the row's last block and is not used
+        long bfrag[GEMM_WQ];
+        float wsc[GEMM_WQ];
+#pragma unroll
+        for (int q = 0; q < GEMM_WQ; q++) {
+            const int b = min(p0 + wid + 4 * q, nb - 1);
+            bfrag[q] = __builtin_nontemporal_load(reinterpret_cast<const long *>(wrow + (int64_t)b * QB));
+            wsc[q] = ld_stream_f32(wsrow + b);
+        }
+        auto load_a = [&](long (&a)[GEMM_AB][4], int q0) {
+#pragma unroll
+            for (int u = 0; u < GEMM_AB; u++) {
+                const int b = min(p0 + wid + 4 * (q0 + u), nb - 1);
+#pragma unroll
+                for (int t = 0; t < 4; t++)
+                    a[u][t] = *reinterpret_cast<const long *>(arow[t] + (int64_t)b * QB);
+            }
+        };
+        long afrag[2][GEMM_AB][4];
+        load_a(afrag[0], 0);
+        if (p0 > 0)
+            __syncthreads();  // the previous pass is done with xsT
+        for (int e = threadIdx.x; e < GEMM_PB * GEMM_TM; e += blockDim.x) {
+            const int r = e / GEMM_PB, bb = e % GEMM_PB;
+            xsT[bb][r] = xs[(int64_t)min(rt0 + r, m - 1) * nb + min(p0 + bb, nb - 1)];
         }
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < GEMM_KC / 4; q++) {
-            const int bb = q * 4 + wid;
-            const int b = kb0 + bb;
-            if (b < nb) {
-                const long bfrag = __builtin_nontemporal_load(reinterpret_cast<const long *>(wrow + (int64_t)b * QB));
-                const float wsc = ld_stream_f32(wsrow + b);
+        for (int q0 = 0; q0 < GEMM_WQ; q0 += GEMM_AB) {
+            const int cur = (q0 / GEMM_AB) & 1;
+            if (q0 + GEMM_AB < GEMM_WQ)
+                load_a(afrag[cur ^ 1], q0 + GEMM_AB);
 #pragma unroll
-                for (int t = 0; t < 4; t++) {
-                    const long afrag = *reinterpret_cast<const long *>(arow[t] + (int64_t)b * QB);
-                    v4i isum = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag, bfrag, v4i{0, 0, 0, 0}, 0, 0, 0);
-                    const f32x4 sx = *reinterpret_cast<const f32x4 *>(&xsT[bb][16 * t + 4 * g]);
+            for (int u = 0; u < GEMM_AB; u++) {
+                const int q = q0 + u;
+                const int bb = wid + 4 * q;  // block within the pass
+                if (p0 + bb < nb) {
 #pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        acc[t][i] = __builtin_fmaf((float)isum[i], wsc * sx[i], acc[t][i]);
+                    for (int t = 0; t < 4; t++) {
+                        v4i isum = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[cur][u][t], bfrag[q],
+                                                                         v4i{0, 0, 0, 0}, 0, 0, 0);
+                        const f32x4 sx = *reinterpret_cast<const f32x4 *>(&xsT[bb][16 * t + 4 * g]);
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            acc[t][i] = __builtin_fmaf((float)isum[i], wsc[q] * sx[i], acc[t][i]);
+                    }
                 }
             }
         }
