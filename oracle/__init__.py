@@ -45,6 +45,7 @@ def _load():
     lib.oracle_gemv_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p]
     lib.oracle_add_rmsnorm.argtypes = [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p]
     lib.oracle_route.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p]
+    lib.oracle_route_q8.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p]
     lib.oracle_moe.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p,
                                _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p]
     lib.oracle_moe.restype = ctypes.c_int
@@ -133,6 +134,35 @@ def route(x, Wr, k):
     wts = np.empty((rows, k), np.float64)
     logits = np.empty((rows, E), np.float64)
     _load().oracle_route(_ptr(x), _ptr(Wr), rows, d, E, k, _ptr(idx), _ptr(wts), _ptr(logits))
+    return idx, wts, logits
+
+
+def route_q8(Wrq, Wrs, k, x=None, xq=None, xs=None):
+    """The router over Q8_0 rows (E rows of d): logits are the Q8_0 GEMV of
+    `x` (float activations) or of `xq`/`xs` (int8 activations, one word each),
+    then the softmax top-K of `route`.  Returns (idx int32 [rows, k], wts
+    float64 [rows, k], logits float64 [rows, E])."""
+    Wrq = _c(Wrq, np.int8); Wrs = _c(Wrs, np.float32)
+    E, d = Wrq.shape
+    act = 0 if x is not None else 1
+    if act == 0:
+        x = _c(np.atleast_2d(x), np.float32)
+        rows = x.shape[0]
+        assert x.shape == (rows, d)
+        xq_p = xs_p = None
+        x_p = _ptr(x)
+    else:
+        xq = _c(np.atleast_2d(xq), np.int8); xs = _c(np.atleast_2d(xs), np.float32)
+        rows = xq.shape[0]
+        assert xq.shape == (rows, d) and xs.shape == (rows, d // 32)
+        x_p = None
+        xq_p, xs_p = _ptr(xq), _ptr(xs)
+    assert Wrs.shape == (E, d // 32) and d % 32 == 0 and 1 <= k <= E
+    idx = np.empty((rows, k), np.int32)
+    wts = np.empty((rows, k), np.float64)
+    logits = np.empty((rows, E), np.float64)
+    _load().oracle_route_q8(act, x_p, xq_p, xs_p, _ptr(Wrq), _ptr(Wrs), rows, d, E, k,
+                            _ptr(idx), _ptr(wts), _ptr(logits))
     return idx, wts, logits
 
 

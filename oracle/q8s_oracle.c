@@ -182,6 +182,41 @@ void oracle_add_rmsnorm(const float *h, const float *r, const float *w, int64_t 
     }
 }
 
+/* The softmax, top-K and renormalisation of one row's logits l[E]. */
+static void route_row(const double *l, int64_t E, int64_t k, int32_t *idx, double *wts)
+{
+    double *p = (double *)malloc((size_t)E * sizeof(double));
+    char *taken = (char *)calloc((size_t)E, 1);
+    double mx = l[0];
+    for (int64_t e = 1; e < E; e++)
+        if (l[e] > mx)
+            mx = l[e];
+    double z = 0.0;
+    for (int64_t e = 0; e < E; e++) {
+        p[e] = exp(l[e] - mx);
+        z += p[e];
+    }
+    for (int64_t e = 0; e < E; e++)
+        p[e] = p[e] / z;
+    double kept = 0.0;
+    for (int64_t j = 0; j < k; j++) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < E; e++) {
+            if (taken[e])
+                continue;
+            if (best < 0 || l[e] > l[best])
+                best = e; /* strict '>' keeps the lower index on a tie */
+        }
+        taken[best] = 1;
+        idx[j] = (int32_t)best;
+        kept += p[best];
+    }
+    for (int64_t j = 0; j < k; j++)
+        wts[j] = p[idx[j]] / kept;
+    free(p);
+    free(taken);
+}
+
 /* ---------------------------------------------------------------------------
  * R -- the top-K softmax router [emit_moe] (softmax, keep K, renormalise),
  * forward_shim.rs fn kernel_refusal (no router bias; renormalising; a softmax
@@ -196,8 +231,6 @@ void oracle_route(const float *x, const float *Wr, int64_t rows, int64_t d, int6
                   int32_t *idx, double *wts, double *logits)
 {
     double *l = (double *)malloc((size_t)E * sizeof(double));
-    double *p = (double *)malloc((size_t)E * sizeof(double));
-    char *taken = (char *)malloc((size_t)E);
     for (int64_t i = 0; i < rows; i++) {
         for (int64_t e = 0; e < E; e++) {
             double acc = 0.0;
@@ -207,37 +240,35 @@ void oracle_route(const float *x, const float *Wr, int64_t rows, int64_t d, int6
             if (logits)
                 logits[i * E + e] = acc;
         }
-        double mx = l[0];
-        for (int64_t e = 1; e < E; e++)
-            if (l[e] > mx)
-                mx = l[e];
-        double z = 0.0;
-        for (int64_t e = 0; e < E; e++) {
-            p[e] = exp(l[e] - mx);
-            z += p[e];
-        }
-        for (int64_t e = 0; e < E; e++)
-            p[e] = p[e] / z;
-        memset(taken, 0, (size_t)E);
-        double kept = 0.0;
-        for (int64_t j = 0; j < k; j++) {
-            int64_t best = -1;
-            for (int64_t e = 0; e < E; e++) {
-                if (taken[e])
-                    continue;
-                if (best < 0 || l[e] > l[best])
-                    best = e; /* strict '>' keeps the lower index on a tie */
-            }
-            taken[best] = 1;
-            idx[i * k + j] = (int32_t)best;
-            kept += p[best];
-        }
-        for (int64_t j = 0; j < k; j++)
-            wts[i * k + j] = p[idx[i * k + j]] / kept;
+        route_row(l, E, k, idx + i * k, wts + i * k);
     }
     free(l);
-    free(p);
-    free(taken);
+}
+
+/* ---------------------------------------------------------------------------
+ * R8 -- the router over quantized checkpoint rows (lane_link.rs fn prim, Moe
+ * arm: a mixture's router is either quantized rows or float values).  The
+ * router rows Wrq/Wrs are a Q8_0 matrix [Q8Ref] of E rows, so the logits are
+ * that matrix's GEMV: G over f32 x (act 0), or I over the one-word int8
+ * activation xq/xs (act 1) -- a norm whose readers are all Q8_0 projections
+ * is read in its quantised form only under that numerics (lane_link.rs,
+ * fn only_projections: a router of float values keeps it f32).  Then the
+ * softmax, top-K and renormalisation of R.  logits may be NULL.
+ */
+void oracle_route_q8(int act, const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq,
+                     const float *Wrs, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx, double *wts,
+                     double *logits)
+{
+    double *l = (double *)malloc((size_t)(rows * E) * sizeof(double));
+    if (act)
+        oracle_gemv_i8(Wrq, Wrs, E, d, xq, xs, rows, l);
+    else
+        oracle_gemv_f32(Wrq, Wrs, E, d, x, rows, l);
+    for (int64_t i = 0; i < rows; i++)
+        route_row(l + i * E, E, k, idx + i * k, wts + i * k);
+    if (logits)
+        memcpy(logits, l, (size_t)(rows * E) * sizeof(double));
+    free(l);
 }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }

@@ -326,6 +326,98 @@ def test_route_degenerate_cases():
 
 
 # ---------------------------------------------------------------------------
+# R8: routing over Q8_0 router rows
+
+
+@pytest.mark.parametrize("E,k", [(6, 2), (8, 3), (9, 4)])
+def test_route_q8_brute_force_over_subsets(E, k):
+    # float activations: the exact rational logits of the dequantised rows,
+    # the kept set the best-summed subset, the weights scipy's softmax
+    rng = np.random.default_rng(61 + E)
+    d = 64
+    Wq, Ws = _rand_q8(rng, E, d)
+    x = synthetic.normal(rng, 2, d)
+    idx, wts, logits = oracle.route_q8(Wq, Ws, k, x=x)
+    for i in range(2):
+        l = [sum(Fraction(int(Wq[e, t])) * Fraction(float(Ws[e, t // 32])) * Fraction(float(x[i, t]))
+                 for t in range(d)) for e in range(E)]
+        assert np.max(np.abs(logits[i] - np.array([float(v) for v in l]))) <= 1e-14 * max(abs(float(v)) for v in l)
+        best = max(itertools.combinations(range(E), k), key=lambda c: (sum(l[e] for e in c), [-e for e in c]))
+        order = sorted(best, key=lambda e: (-l[e], e))
+        assert list(idx[i]) == order
+        p = scipy.special.softmax(np.array([float(v) for v in l]))
+        assert np.max(np.abs(wts[i] - p[order] / p[order].sum())) <= 1e-14
+
+
+def test_route_q8_int8_logits_brute_force():
+    # int8 activations: per 32-value block, the exact integer dot of the two
+    # quantised rows times both scales, summed (exact rationals)
+    rng = np.random.default_rng(64)
+    E, d, k = 7, 96, 3
+    Wq, Ws = _rand_q8(rng, E, d)
+    xq = rng.integers(-127, 128, size=(2, d)).astype(np.int8)
+    xs = (rng.random((2, d // 32)) * 0.05 + 0.001).astype(np.float32)
+    idx, wts, logits = oracle.route_q8(Wq, Ws, k, xq=xq, xs=xs)
+    for i in range(2):
+        l = []
+        for e in range(E):
+            acc = Fraction(0)
+            for b in range(d // 32):
+                dot = sum(int(Wq[e, t]) * int(xq[i, t]) for t in range(32 * b, 32 * b + 32))
+                acc += Fraction(float(Ws[e, b])) * Fraction(float(xs[i, b])) * dot
+            l.append(acc)
+        assert np.max(np.abs(logits[i] - np.array([float(v) for v in l]))) <= 1e-14 * max(abs(float(v)) for v in l)
+        assert list(idx[i]) == sorted(range(E), key=lambda e: (-l[e], e))[:k]
+
+
+def test_route_q8_equals_float_router_on_exact_rows():
+    # power-of-two scales: every dequantised weight is an exact float32, so
+    # routing over the Q8_0 rows equals routing over those float32 rows
+    rng = np.random.default_rng(65)
+    E, d, k = 64, 256, 6
+    Wq = rng.integers(-127, 128, size=(E, d)).astype(np.int8)
+    Ws = (2.0 ** rng.integers(-12, -6, size=(E, d // 32))).astype(np.float32)
+    Wr = (Wq.astype(np.float32) * np.repeat(Ws, 32, axis=1)).astype(np.float32)
+    x = synthetic.normal(rng, 3, d)
+    a = oracle.route_q8(Wq, Ws, k, x=x)
+    b = oracle.route(x, Wr, k)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_route_q8_int8_equals_float_when_x_is_q8_exact():
+    # x exactly the dequantised form of (xq, xs) with power-of-two scales and
+    # a few nonzero words: both modes' logits are exact, so they agree bit for
+    # bit, and so do the choices and weights
+    rng = np.random.default_rng(66)
+    E, d, k = 32, 128, 4
+    Wq = rng.integers(-127, 128, size=(E, d)).astype(np.int8)
+    Ws = (2.0 ** rng.integers(-10, -6, size=(E, d // 32))).astype(np.float32)
+    xq = rng.integers(-127, 128, size=(2, d)).astype(np.int8)
+    xs = (2.0 ** rng.integers(-9, -5, size=(2, d // 32))).astype(np.float32)
+    x = (xq.astype(np.float32) * np.repeat(xs, 32, axis=1)).astype(np.float32)
+    a = oracle.route_q8(Wq, Ws, k, x=x)
+    b = oracle.route_q8(Wq, Ws, k, xq=xq, xs=xs)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_route_q8_scale_index_is_row_then_block():
+    # one row of ones per expert, scale 2^-e on block e+1 (mod 4) of row e
+    # and 0 elsewhere: expert e's logit is 2^-e times that block's sum of x
+    # (a transposed scale index would read block e-1)
+    E, d = 4, 128
+    Wq = np.ones((E, d), np.int8)
+    Ws = np.zeros((E, d // 32), np.float32)
+    for e in range(E):
+        Ws[e, (e + 1) % 4] = 2.0 ** -e
+    x = np.zeros((1, d), np.float32)
+    x[0, :] = np.repeat(np.array([1.0, 8.0, 64.0, 512.0], np.float32), 32)
+    _, _, logits = oracle.route_q8(Wq, Ws, 1, x=x)
+    assert list(logits[0]) == [256.0, 1024.0, 4096.0, 4.0]
+
+
+# ---------------------------------------------------------------------------
 # M: the MoE block
 
 
