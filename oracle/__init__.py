@@ -49,6 +49,8 @@ def _load():
     lib.oracle_moe.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p,
                                _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p]
     lib.oracle_moe.restype = ctypes.c_int
+    lib.oracle_moe_shared.argtypes = [ctypes.c_int] + [_p] * 16 + [_i64] * 6 + [_p] * 4
+    lib.oracle_moe_shared.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -185,4 +187,48 @@ def moe(x, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act):
     rc = _load().oracle_moe(int(act), _ptr(x), _ptr(Wr), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq), _ptr(Wus),
                             _ptr(Wdq), _ptr(Wds), rows, d, dff, E, k, _ptr(idx), _ptr(wts), _ptr(h), _ptr(y))
     assert rc == 0, "oracle_moe: unknown activation mode"
+    return idx, wts, h, y
+
+
+def moe_shared(x, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act, Wr=None, Wrq=None, Wrs=None, shared=None):
+    """The MoE FFN block with its variants: the router as float rows ``Wr``
+    or Q8_0 rows ``Wrq``/``Wrs``; ``shared`` = (Sgq, Sgs, Suq, Sus, Sdq, Sds)
+    an always-on expert added unweighted.  Returns (idx, wts, h f32
+    [rows, k*dff + sdff], y float64 [rows, d])."""
+    x = _c(np.atleast_2d(x), np.float32)
+    Wgq = _c(Wgq, np.int8); Wgs = _c(Wgs, np.float32)
+    Wuq = _c(Wuq, np.int8); Wus = _c(Wus, np.float32)
+    Wdq = _c(Wdq, np.int8); Wds = _c(Wds, np.float32)
+    rows, d = x.shape
+    assert (Wr is None) != (Wrq is None)
+    if Wr is not None:
+        Wr = _c(Wr, np.float32)
+        E = Wr.shape[0]
+        assert Wr.shape == (E, d)
+    else:
+        Wrq = _c(Wrq, np.int8); Wrs = _c(Wrs, np.float32)
+        E = Wrq.shape[0]
+        assert Wrq.shape == (E, d) and Wrs.shape == (E, d // 32)
+    dff = Wgq.shape[0] // E
+    assert Wgq.shape == (E * dff, d) and Wuq.shape == (E * dff, d) and Wdq.shape == (E * d, dff)
+    assert d % 32 == 0 and dff % 32 == 0 and 1 <= k <= E
+    sp = [None] * 6
+    sdff = 0
+    if shared is not None:
+        Sgq, Sgs, Suq, Sus, Sdq, Sds = shared
+        sdff = Sgq.shape[0]
+        assert sdff % 32 == 0 and Sgq.shape == (sdff, d) and Suq.shape == (sdff, d) and Sdq.shape == (d, sdff)
+        assert Sgs.shape == (sdff, d // 32) and Sus.shape == Sgs.shape and Sds.shape == (d, sdff // 32)
+        keep = [_c(Sgq, np.int8), _c(Sgs, np.float32), _c(Suq, np.int8), _c(Sus, np.float32),
+                _c(Sdq, np.int8), _c(Sds, np.float32)]
+        sp = [_ptr(a) for a in keep]
+    idx = np.empty((rows, k), np.int32)
+    wts = np.empty((rows, k), np.float64)
+    h = np.empty((rows, k * dff + sdff), np.float32)
+    y = np.empty((rows, d), np.float64)
+    rc = _load().oracle_moe_shared(int(act), _ptr(x), _ptr(Wr) if Wr is not None else None,
+                                   _ptr(Wrq) if Wrq is not None else None, _ptr(Wrs) if Wrs is not None else None,
+                                   _ptr(Wgq), _ptr(Wgs), _ptr(Wuq), _ptr(Wus), _ptr(Wdq), _ptr(Wds), *sp,
+                                   sdff, rows, d, dff, E, k, _ptr(idx), _ptr(wts), _ptr(h), _ptr(y))
+    assert rc == 0, "oracle_moe_shared: unknown activation mode"
     return idx, wts, h, y

@@ -34,6 +34,11 @@
  *   [epilogue]   codegen_cuda/forward_shim.rs module doc: under the one-word
  *                int8 numerics the activation a Q8_0 projection reads is
  *                quantised in its producer's epilogue.
+ *   [variants]   codegen_cuda/lane_link.rs, fn prim (Moe arm: the router as
+ *                quantized checkpoint rows or as float values) and fn
+ *                class_launch (SharedExpertFusion arm: a shared expert's gated
+ *                pair and down product carried by the mixture's launch);
+ *                arena.rs fn scratch (Moe arm: K*dff + sdff hidden values).
  *   [scratch]    codegen_cuda/lane/arena.rs, fn scratch / fn array_bytes: a
  *                quantised activation is int8 words plus one f32 scale a
  *                32-value block; the decode mixture keeps its hidden row
@@ -47,6 +52,9 @@
  *   - RMSNorm: y = (s / sqrt(mean(s^2) + eps)) * w, eps inside the root;
  *   - routing ranks by logit, ties to the lower expert index; softmax over all
  *     E experts, then the kept weights renormalised to sum 1;
+ *   - a shared expert is added to the mixture's weighted sum with weight 1 (no
+ *     gate of its own; the pages decompose a router/shared-gate merge), after
+ *     it; a Q8_0 router under one-word int8 numerics reads the quantised row;
  *   - SiLU(z) = z / (1 + exp(-z)); the hidden row h = SiLU(g) * u is held as a
  *     float32 tensor between the gate-up and the down projection (and, in int8
  *     mode, quantised per 32-value block of each expert's row).
@@ -273,13 +281,51 @@ void oracle_route_q8(int act, const float *x, const int8_t *xq, const float *xs,
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
+int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wrq, const float *Wrs,
+                      const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Wdq,
+                      const float *Wds, const int8_t *Sgq, const float *Sgs, const int8_t *Suq, const float *Sus,
+                      const int8_t *Sdq, const float *Sds, int64_t sdff, int64_t rows, int64_t d, int64_t dff,
+                      int64_t E, int64_t k, int32_t *idx, double *wts, float *h, double *y);
+
+/* One expert's SwiGLU FFN on one row, for M and MS: gate/up rows gq/gs, uq/us
+ * [n, d], down rows dq/ds [d, n]:
+ *   g = Wg . x, u = Wu . x                              (G, or I on Q(x))
+ *   hj[o] = float32( SiLU(g[o]) * u[o] )                (a float32 tensor)
+ *   dn[o'] = Wd[o'] . hj                                (G, or I on Q(hj))
+ * act 1 reads the row's Q8_0 form xq/xs. */
+static void expert_ffn(int act, const float *xr, const int8_t *xq, const float *xs, const int8_t *gq,
+                       const float *gs, const int8_t *uq, const float *us, const int8_t *dq, const float *ds,
+                       int64_t d, int64_t n, float *hj, double *dn)
+{
+    double *g = (double *)malloc((size_t)n * sizeof(double));
+    double *u = (double *)malloc((size_t)n * sizeof(double));
+    if (act == 0) {
+        oracle_gemv_f32(gq, gs, n, d, xr, 1, g);
+        oracle_gemv_f32(uq, us, n, d, xr, 1, u);
+    } else {
+        oracle_gemv_i8(gq, gs, n, d, xq, xs, 1, g);
+        oracle_gemv_i8(uq, us, n, d, xq, xs, 1, u);
+    }
+    for (int64_t o = 0; o < n; o++)
+        hj[o] = (float)(silu(g[o]) * u[o]);
+    if (act == 0) {
+        oracle_gemv_f32(dq, ds, d, n, hj, 1, dn);
+    } else {
+        int8_t *hq = (int8_t *)malloc((size_t)n);
+        float *hs = (float *)malloc((size_t)(n / QBLOCK) * sizeof(float));
+        oracle_quantize(hj, 1, n, hq, hs);
+        oracle_gemv_i8(dq, ds, d, n, hq, hs, 1, dn);
+        free(hq);
+        free(hs);
+    }
+    free(g);
+    free(u);
+}
+
 /* ---------------------------------------------------------------------------
  * M -- the sparse MoE FFN block [emit_moe], [MoeWeights], each row apart:
  *   route x (always from the float32 x, [epilogue]: an f32 router reads x);
- *   for each kept expert j (e = idx[j]):
- *     g = Wg[e*dff + o] . x,  u = Wu[e*dff + o] . x     (G, or I on Q(x))
- *     h[j][o] = float32( SiLU(g) * u )                  (a float32 tensor)
- *     dn[j][o'] = Wd[e*d + o'] . h[j]                   (G, or I on Q(h[j]))
+ *   for each kept expert j (e = idx[j]): h[j], dn[j] = expert_ffn of expert e
  *   y[o'] = sum_{j<K} w[j] * dn[j][o']                  (double, j order)
  * act = 0: f32 activations; act = 1: one-word int8 activations, where x is
  * quantised once per row and each expert's hidden row per 32-value block
@@ -292,58 +338,65 @@ int oracle_moe(int act, const float *x, const float *Wr, const int8_t *Wgq, cons
                int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
                int32_t *idx, double *wts, float *h, double *y)
 {
+    return oracle_moe_shared(act, x, Wr, NULL, NULL, Wgq, Wgs, Wuq, Wus, Wdq, Wds, NULL, NULL, NULL, NULL, NULL,
+                             NULL, 0, rows, d, dff, E, k, idx, wts, h, y);
+}
+
+/* ---------------------------------------------------------------------------
+ * MS -- M with the variants linked into the same mixture launch (lane_link.rs
+ * fn prim, Moe arm; fn class_launch, SharedExpertFusion arm; arena.rs
+ * fn scratch, Moe arm, whose hidden scratch holds K*dff + sdff values a row):
+ *   - the router as Q8_0 rows (Wrq/Wrs, Wr NULL): logits as R8, which under
+ *     act 1 reads the row's Q8_0 form; or float32 rows Wr as M;
+ *   - a shared expert (sdff > 0): an always-on SwiGLU expert of its own width
+ *     sdff -- gate/up Sg/Su [sdff, d], down Sd [d, sdff] -- whose down row is
+ *     added, unweighted, to the mixture's sum:
+ *       y[o'] = (sum_{j<K} w[j] * dn[j][o']) + dn_s[o']
+ *     its hidden row h_s (float32; Q8_0 per block under act 1) after the K
+ *     routed ones.
+ * h is [rows, K*dff + sdff].  Returns 0, or -1 for an unknown mode.
+ */
+int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wrq, const float *Wrs,
+                      const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Wdq,
+                      const float *Wds, const int8_t *Sgq, const float *Sgs, const int8_t *Suq, const float *Sus,
+                      const int8_t *Sdq, const float *Sds, int64_t sdff, int64_t rows, int64_t d, int64_t dff,
+                      int64_t E, int64_t k, int32_t *idx, double *wts, float *h, double *y)
+{
     if (act != 0 && act != 1)
         return -1;
-    int64_t nbd = d / QBLOCK, nbf = dff / QBLOCK;
-    int8_t *xq = (int8_t *)malloc((size_t)d);
-    float *xs = (float *)malloc((size_t)nbd * sizeof(float));
-    int8_t *hq = (int8_t *)malloc((size_t)dff);
-    float *hs = (float *)malloc((size_t)nbf * sizeof(float));
-    double *g = (double *)malloc((size_t)dff * sizeof(double));
-    double *u = (double *)malloc((size_t)dff * sizeof(double));
+    const int64_t nbd = d / QBLOCK, nbf = dff / QBLOCK, hw = k * dff + sdff;
+    int8_t *xq = (int8_t *)malloc((size_t)(rows * d));
+    float *xs = (float *)malloc((size_t)(rows * nbd) * sizeof(float));
     double *dn = (double *)malloc((size_t)d * sizeof(double));
 
-    oracle_route(x, Wr, rows, d, E, k, idx, wts, NULL);
+    if (act == 1)
+        oracle_quantize(x, rows, d, xq, xs);
+    if (Wrq)
+        oracle_route_q8(act, x, xq, xs, Wrq, Wrs, rows, d, E, k, idx, wts, NULL);
+    else
+        oracle_route(x, Wr, rows, d, E, k, idx, wts, NULL);
     for (int64_t i = 0; i < rows; i++) {
         const float *xr = x + i * d;
         double *yr = y + i * d;
         for (int64_t o = 0; o < d; o++)
             yr[o] = 0.0;
-        if (act == 1)
-            oracle_quantize(xr, 1, d, xq, xs);
         for (int64_t j = 0; j < k; j++) {
             int64_t e = idx[i * k + j];
-            const int8_t *gq = Wgq + e * dff * d, *uq = Wuq + e * dff * d;
-            const float *gs = Wgs + e * dff * nbd, *us = Wus + e * dff * nbd;
-            const int8_t *dq = Wdq + e * d * dff;
-            const float *ds = Wds + e * d * nbf;
-            float *hj = h + (i * k + j) * dff;
-            if (act == 0) {
-                oracle_gemv_f32(gq, gs, dff, d, xr, 1, g);
-                oracle_gemv_f32(uq, us, dff, d, xr, 1, u);
-            } else {
-                oracle_gemv_i8(gq, gs, dff, d, xq, xs, 1, g);
-                oracle_gemv_i8(uq, us, dff, d, xq, xs, 1, u);
-            }
-            for (int64_t o = 0; o < dff; o++)
-                hj[o] = (float)(silu(g[o]) * u[o]);
-            if (act == 0) {
-                oracle_gemv_f32(dq, ds, d, dff, hj, 1, dn);
-            } else {
-                oracle_quantize(hj, 1, dff, hq, hs);
-                oracle_gemv_i8(dq, ds, d, dff, hq, hs, 1, dn);
-            }
+            expert_ffn(act, xr, xq + i * d, xs + i * nbd, Wgq + e * dff * d, Wgs + e * dff * nbd, Wuq + e * dff * d,
+                       Wus + e * dff * nbd, Wdq + e * d * dff, Wds + e * d * nbf, d, dff, h + i * hw + j * dff, dn);
             double wj = wts[i * k + j];
             for (int64_t o = 0; o < d; o++)
                 yr[o] += wj * dn[o];
         }
+        if (sdff > 0) {
+            expert_ffn(act, xr, xq + i * d, xs + i * nbd, Sgq, Sgs, Suq, Sus, Sdq, Sds, d, sdff,
+                       h + i * hw + k * dff, dn);
+            for (int64_t o = 0; o < d; o++)
+                yr[o] += dn[o];
+        }
     }
     free(xq);
     free(xs);
-    free(hq);
-    free(hs);
-    free(g);
-    free(u);
     free(dn);
     return 0;
 }

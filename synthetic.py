@@ -157,6 +157,37 @@ def block_inputs(seed, d, dff, E, k, rows=1):
     return BlockInputs(m, w, h, r)
 
 
+@dataclass
+class VariantInputs:
+    block: BlockInputs  # the block as ``block_inputs`` draws it
+    Wrq: np.ndarray     # int8 [E, d]   router rows in Q8_0 form
+    Wrs: np.ndarray     # f32  [E, d/32]
+    Sgq: np.ndarray     # int8 [sdff, d] shared expert gate (None when sdff = 0)
+    Sgs: np.ndarray
+    Suq: np.ndarray     # int8 [sdff, d] shared expert up
+    Sus: np.ndarray
+    Sdq: np.ndarray     # int8 [d, sdff] shared expert down
+    Sds: np.ndarray
+    sdff: int
+
+
+def variant_inputs(seed, d, dff, E, k, rows=1, sdff=0):
+    """The mixture block with its variants: ``block_inputs``' draws, then
+    Q8_0 router rows (quants, then scales in [2e-4, 5e-4], so the weights
+    spread about as the float router's 0.02 does), then, for sdff > 0, a
+    shared expert's gate, up and down Q8_0 matrices."""
+    rng = _rng(seed)
+    b = block_inputs(rng, d, dff, E, k, rows)
+    Wrq = quants(rng, E, d)
+    Wrs = rng.uniform(2e-4, 5e-4, size=(E, d // QBLOCK)).astype(np.float32)
+    S = [None] * 6
+    if sdff:
+        S[0], S[1] = q8_matrix(rng, sdff, d)
+        S[2], S[3] = q8_matrix(rng, sdff, d)
+        S[4], S[5] = q8_matrix(rng, d, sdff)
+    return VariantInputs(b, Wrq, Wrs, *S, sdff)
+
+
 def fill_pattern(n, scale=1.0):
     """The deterministic small-integer fill ``v[p] = (p % 7) - 3`` (optionally
     scaled) that the ``emit_forward`` item of the ``codegen_cuda::qwen_emit``

@@ -509,3 +509,88 @@ def test_moe_rejects_unknown_mode():
     m = _small_moe(69, E=2, k=1, rows=1)
     with pytest.raises(AssertionError):
         oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act=2)
+
+
+# ---------------------------------------------------------------------------
+# MS: the mixture with a shared expert and/or Q8_0 router rows
+
+
+def _variant(seed, d=64, dff=96, E=4, k=2, rows=2, sdff=128):
+    v = synthetic.variant_inputs(seed, d, dff, E, k, rows, sdff)
+    m = v.block.moe
+    x = synthetic.normal(np.random.default_rng(seed + 1000), rows, d)
+    return v, m, x
+
+
+def _shared(v):
+    return (v.Sgq, v.Sgs, v.Suq, v.Sus, v.Sdq, v.Sds)
+
+
+def test_moe_shared_without_variants_is_moe():
+    v, m, x = _variant(71)
+    for act in (0, 1):
+        a = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=act)
+        b = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act, Wr=m.Wr)
+        for u, w in zip(a, b):
+            assert np.array_equal(u.reshape(w.shape), w)
+
+
+def test_moe_shared_expert_adds_a_dense_swiglu():
+    # the shared expert's part is the numpy dense SwiGLU of its own weights,
+    # added with weight 1; its hidden row follows the K routed ones
+    v, m, x = _variant(72, sdff=160)
+    idx0, wts0, h0, y0 = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=0)
+    idx, wts, h, y = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 0, Wr=m.Wr,
+                                       shared=_shared(v))
+    assert np.array_equal(idx, idx0) and np.array_equal(wts, wts0)
+    assert np.array_equal(h[:, :2 * m.dff], h0.reshape(2, -1))
+    for i in range(2):
+        ref, hid = _dense_swiglu(x[i].astype(np.float64), _deq(v.Sgq, v.Sgs), _deq(v.Suq, v.Sus), _deq(v.Sdq, v.Sds))
+        assert np.array_equal(h[i, 2 * m.dff:], hid.astype(np.float32))
+        assert np.max(np.abs((y[i] - y0[i]) - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_moe_shared_expert_equal_to_the_only_expert_doubles_it():
+    # one routed expert (weight 1) and a shared expert with the same weights:
+    # the output is exactly twice the dense SwiGLU (x + x is exact)
+    v, m, x = _variant(73, E=1, k=1, sdff=96)
+    sh = (m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds)
+    for act in (0, 1):
+        _, wts, h, y = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act, Wr=m.Wr, shared=sh)
+        _, _, h1, y1 = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act=act)
+        assert (wts == 1.0).all()
+        assert np.array_equal(h[:, :96], h[:, 96:]) and np.array_equal(h[:, :96], h1.reshape(2, 96))
+        assert np.array_equal(y, 2.0 * y1)
+
+
+def test_moe_q8_router_routes_as_route_q8():
+    v, m, x = _variant(74, E=8, k=3, rows=3, sdff=0)
+    for act in (0, 1):
+        idx, wts, _, _ = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 3, act,
+                                           Wrq=v.Wrq, Wrs=v.Wrs)
+        if act == 0:
+            ri, rw, _ = oracle.route_q8(v.Wrq, v.Wrs, 3, x=x)
+        else:
+            xq, xs = oracle.quantize(x)
+            ri, rw, _ = oracle.route_q8(v.Wrq, v.Wrs, 3, xq=xq, xs=xs)
+        assert np.array_equal(idx, ri) and np.array_equal(wts, rw)
+
+
+def test_moe_q8_router_on_exact_rows_equals_float_router():
+    # power-of-two router scales: the Q8_0 rows' dequantised form is exact in
+    # float32, so in f32 numerics the block equals the block on those rows
+    v, m, x = _variant(75, E=6, k=2, rows=2, sdff=64)
+    rng = np.random.default_rng(76)
+    Wrs = (2.0 ** rng.integers(-12, -8, size=v.Wrs.shape)).astype(np.float32)
+    Wr = (v.Wrq.astype(np.float32) * np.repeat(Wrs, 32, axis=1)).astype(np.float32)
+    a = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 0, Wrq=v.Wrq, Wrs=Wrs, shared=_shared(v))
+    b = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 0, Wr=Wr, shared=_shared(v))
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+def test_moe_shared_int8_within_bound_of_f32_mode():
+    v, m, x = _variant(77, d=128, dff=128, E=4, k=2, rows=2, sdff=256)
+    _, _, _, yf = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 0, Wr=m.Wr, shared=_shared(v))
+    _, _, _, yi = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 1, Wr=m.Wr, shared=_shared(v))
+    assert np.max(np.abs(yi - yf)) <= 3e-2 * np.max(np.abs(yf))
