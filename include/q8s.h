@@ -275,6 +275,74 @@ Q8S_API int moe_ffn_block(const float *h, const float *r, const float *w, float 
                   void *scratch, size_t scratch_bytes, void *stream);
 
 /*
+ * moe_route_topk_q8 -- moe_route_topk over a router held as Q8_0 rows
+ * (lane_link.rs fn prim, Moe arm: the router as quantized checkpoint rows;
+ * struct Q8Ref's layout):
+ *   F32:  l[r][e] = sum_t (Wrq[e][t] * Wrs[e][t/32]) * x[r][t]   (double)
+ *   INT8: l[r][e] = sum_b (Wrs[e][b] * xs[r][b]) * isum_b, each isum_b the
+ *         exact int32 dot of a 32-value block of Wrq[e] and xq[r], scaled and
+ *         summed in double (the one-word int8 numerics, where a norm whose
+ *         readers are all Q8_0 projections is read in its Q8_0 form only:
+ *         lane_link.rs fn only_projections)
+ *   then the softmax, top-K and weights exactly as moe_route_topk.
+ * x: device f32 [rows, d] (F32) or NULL; xq/xs: device int8 [rows, d] and
+ * f32 [rows, d/32] (INT8) or NULL.  Wrq: device int8 [E, d]; Wrs: device f32
+ * [E, d/32].  idx, wts, scratch (q8s_scratch_bytes(Q8S_FN_ROUTE, ...)) and
+ * limits as moe_route_topk.
+ */
+Q8S_API int moe_route_topk_q8(const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq,
+                      const float *Wrs, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
+                      float *wts, int act, void *scratch, size_t scratch_bytes, void *stream);
+
+/*
+ * add_rmsnorm_router_q8 -- add_rmsnorm_router over Q8_0 router rows:
+ *   sum, x (and/or xq, xs) exactly as add_rmsnorm_q8 writes them;
+ *   logits[r] as moe_route_topk_q8 forms them, from the normed row (F32) or
+ *   from its Q8_0 form (INT8: each workgroup quantises the normed row by the
+ *   q8_quantize_rows rule itself, whether or not xq is requested).
+ * Wrq: device int8 [E, d]; Wrs: device f32 [E, d/32]; other arguments and
+ * limits as add_rmsnorm_router.
+ */
+Q8S_API int add_rmsnorm_router_q8(const float *h, const float *r, const float *w, float eps,
+                          const int8_t *Wrq, const float *Wrs, int64_t rows, int64_t d, int64_t E,
+                          float *sum, float *x, int8_t *xq, float *xs, double *logits, int act,
+                          void *stream);
+
+/*
+ * moe_ffn_block_ex -- moe_ffn_block with the variants linked into the
+ * mixture's launch (lane_link.rs fn prim, Moe arm; fn class_launch,
+ * SharedExpertFusion arm; arena.rs fn scratch, Moe arm):
+ *   - the router: float32 rows Wr (Wrq, Wrs NULL), or Q8_0 rows Wrq/Wrs (Wr
+ *     NULL), read as moe_route_topk_q8 reads them in mode act (INT8: the
+ *     normed row's Q8_0 form);
+ *   - a shared expert when sdff > 0: an always-on SwiGLU expert of width
+ *     sdff -- Sgq/Suq device int8 [sdff, d], Sgs/Sus device f32
+ *     [sdff, d/32], Sdq device int8 [d, sdff], Sds device f32 [d, sdff/32] --
+ *     whose output is added, unweighted, after the routed sum:
+ *       out[r] = (sum_j wts[r][j] * down_e(...)) + Sd . (SiLU(Sg x) * (Su x))
+ *     its hidden row in the routed experts' numerics.  sdff == 0 (the six
+ *     pointers NULL): no shared expert.
+ * scratch: >= q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act) bytes.
+ * Other arguments, outputs and limits as moe_ffn_block; sdff a multiple of
+ * 32, at most 65536, and the down-combine holds at most 512 (slot, slice)
+ * partials (Q8S_EUNSUPPORTED beyond).  Decode rows run three launches, the
+ * shared expert's tiles inside the gate-up launch and its slices inside the
+ * down-combine; a chunk of rows in INT8 mode runs it after the grouped
+ * kernels as a gate-up and a down-combine that adds into out.
+ */
+Q8S_API int moe_ffn_block_ex(const float *h, const float *r, const float *w, float eps, const float *Wr,
+                     const int8_t *Wrq, const float *Wrs, const int8_t *Wgq, const float *Wgs,
+                     const int8_t *Wuq, const float *Wus, const int8_t *Wdq, const float *Wds,
+                     const int8_t *Sgq, const float *Sgs, const int8_t *Suq, const float *Sus,
+                     const int8_t *Sdq, const float *Sds, int64_t sdff, int64_t rows, int64_t d,
+                     int64_t dff, int64_t E, int64_t k, float *sum, int32_t *idx, float *wts, float *out,
+                     int act, void *scratch, size_t scratch_bytes, void *stream);
+
+/* Bytes of scratch moe_ffn_block_ex needs for these sizes (0 for invalid). */
+Q8S_API size_t q8s_block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k,
+                               int act);
+
+/*
  * q8s_scratch_bytes -- bytes of scratch the call `fn` (Q8S_FN_ROUTE,
  * Q8S_FN_DOWN or Q8S_FN_BLOCK) needs for these sizes; 0 for a call that needs
  * none, or for an unknown fn.

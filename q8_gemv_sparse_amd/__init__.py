@@ -21,7 +21,8 @@ __all__ = [
     "ACT_F32", "ACT_INT8", "FN_ROUTE", "FN_DOWN", "FN_BLOCK", "Q8sError", "LIB_PATH",
     "q8_gemv", "q8_quantize_rows", "add_rmsnorm_q8", "moe_route_topk",
     "moe_gate_up", "moe_down_combine", "moe_ffn_block", "add_rmsnorm_router", "moe_topk_gate_up",
-    "add_rmsnorm_gemv", "q8s_scratch_bytes", "q8s_last_error",
+    "add_rmsnorm_gemv", "moe_route_topk_q8", "add_rmsnorm_router_q8", "moe_ffn_block_ex",
+    "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "library",
 ]
 
@@ -55,13 +56,20 @@ _SIGS = {
     "add_rmsnorm_router": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "moe_topk_gate_up": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
                          ctypes.c_int, _p],
+    "moe_route_topk_q8": [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, ctypes.c_int, _p, _sz, _p],
+    "add_rmsnorm_router_q8": [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p,
+                              ctypes.c_int, _p],
+    "moe_ffn_block_ex": [_p, _p, _p, ctypes.c_float] + [_p] * 15 + [_i64] * 6 + [_p] * 4 + [ctypes.c_int, _p, _sz,
+                                                                                           _p],
     "q8s_scratch_bytes": [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
+    "q8s_block_scratch_bytes": [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
     _f.argtypes = _args
     _f.restype = ctypes.c_int
 _lib.q8s_scratch_bytes.restype = _sz
+_lib.q8s_block_scratch_bytes.restype = _sz
 _lib.q8s_last_error.restype = ctypes.c_char_p
 _lib.q8s_last_error.argtypes = []
 _lib.q8s_version.restype = ctypes.c_char_p
@@ -89,6 +97,10 @@ def q8s_version():
 
 def q8s_scratch_bytes(fn, rows, d, dff, E, k, act=ACT_F32):
     return int(_lib.q8s_scratch_bytes(fn, rows, d, dff, E, k, act))
+
+
+def q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act=ACT_F32):
+    return int(_lib.q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act))
 
 
 def _check(rc):
@@ -368,3 +380,93 @@ def add_rmsnorm_gemv(h, r, w, eps, Wq, Ws, act=ACT_F32, sum=None, y=None, yq=Non
     _check(_lib.add_rmsnorm_gemv(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wq), _ptr(Ws), rows, d, n_out, _ptr(sum),
                                  _ptr(y), _ptr(yq), _ptr(ys), _ptr(out), act, _stream(stream)))
     return sum, y, yq, ys, out
+
+
+def moe_route_topk_q8(Wrq, Wrs, k, x=None, xq=None, xs=None, act=ACT_F32, idx=None, wts=None, scratch=None,
+                      stream=None):
+    """Router over Q8_0 rows + top-K: (idx int32 [rows, k], wts f32 [rows, k]).
+    F32 reads ``x``; INT8 reads ``xq``/``xs``.  ``scratch`` as moe_route_topk."""
+    _dev(Wrq, torch.int8, "Wrq"); _dev(Wrs, torch.float32, "Wrs")
+    _dev(x, torch.float32, "x"); _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
+    E, d = Wrq.shape
+    a = x if act == ACT_F32 else xq
+    rows = a.numel() // d
+    dev = Wrq.device
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if wts is None:
+        wts = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    if scratch is None:
+        scratch = torch.empty(q8s_scratch_bytes(FN_ROUTE, rows, d, 32, E, k), dtype=torch.uint8, device=dev)
+    _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts"); _dev(scratch, torch.uint8, "scratch")
+    _check(_lib.moe_route_topk_q8(_ptr(x), _ptr(xq), _ptr(xs), _ptr(Wrq), _ptr(Wrs), rows, d, E, k, _ptr(idx),
+                                  _ptr(wts), act, _ptr(scratch), scratch.numel(), _stream(stream)))
+    return idx, wts
+
+
+def add_rmsnorm_router_q8(h, r, w, eps, Wrq, Wrs, act=ACT_F32, sum=None, x=None, xq=None, xs=None, logits=None,
+                          want_f32=True, want_q8=True, stream=None):
+    """add_rmsnorm_router over Q8_0 router rows.  Returns
+    (sum, x or None, xq or None, xs or None, logits float64 [rows, E])."""
+    _dev(h, torch.float32, "h"); _dev(r, torch.float32, "r"); _dev(w, torch.float32, "w")
+    _dev(Wrq, torch.int8, "Wrq"); _dev(Wrs, torch.float32, "Wrs")
+    E, d = Wrq.shape
+    rows = h.numel() // d
+    dev = h.device
+    if sum is None:
+        sum = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_f32 and x is None:
+        x = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if want_q8 and xq is None:
+        xq = torch.empty((rows, d), dtype=torch.int8, device=dev)
+        xs = torch.empty((rows, d // 32), dtype=torch.float32, device=dev)
+    if logits is None:
+        logits = torch.empty((rows, E), dtype=torch.float64, device=dev)
+    for t, dt, n in ((sum, torch.float32, "sum"), (x, torch.float32, "x"), (xq, torch.int8, "xq"),
+                     (xs, torch.float32, "xs"), (logits, torch.float64, "logits")):
+        _dev(t, dt, n)
+    _check(_lib.add_rmsnorm_router_q8(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wrq), _ptr(Wrs), rows, d, E,
+                                      _ptr(sum), _ptr(x), _ptr(xq), _ptr(xs), _ptr(logits), act, _stream(stream)))
+    return sum, x, xq, xs, logits
+
+
+def moe_ffn_block_ex(h, r, w, eps, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, E, act=ACT_F32, Wr=None, Wrq=None, Wrs=None,
+                     shared=None, sum=None, idx=None, wts=None, out=None, scratch=None, stream=None):
+    """moe_ffn_block with the router as float rows ``Wr`` or Q8_0 rows
+    ``Wrq``/``Wrs``, and ``shared`` = (Sgq, Sgs, Suq, Sus, Sdq, Sds), an
+    always-on expert added unweighted (None: no shared expert).  Returns
+    (sum, idx, wts, out).  ``scratch`` is a uint8 device tensor of at least
+    q8s_block_scratch_bytes(...) bytes; one is allocated when none is given."""
+    for t, n in ((h, "h"), (r, "r"), (w, "w"), (Wr, "Wr"), (Wrs, "Wrs"), (Wgs, "Wgs"), (Wus, "Wus"), (Wds, "Wds")):
+        _dev(t, torch.float32, n)
+    for t, n in ((Wrq, "Wrq"), (Wgq, "Wgq"), (Wuq, "Wuq"), (Wdq, "Wdq")):
+        _dev(t, torch.int8, n)
+    d = h.shape[-1]
+    rows = h.numel() // d
+    dff = Wgq.shape[0] // E
+    sh = [None] * 6
+    sdff = 0
+    if shared is not None:
+        sh = list(shared)
+        for i, n in enumerate(("Sgq", "Sgs", "Suq", "Sus", "Sdq", "Sds")):
+            _dev(sh[i], torch.int8 if i % 2 == 0 else torch.float32, n)
+        sdff = sh[0].shape[0]
+    dev = h.device
+    if sum is None:
+        sum = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if wts is None:
+        wts = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if scratch is None:
+        scratch = torch.empty(max(q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act), 1), dtype=torch.uint8,
+                              device=dev)
+    _dev(sum, torch.float32, "sum"); _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
+    _dev(out, torch.float32, "out"); _dev(scratch, torch.uint8, "scratch")
+    _check(_lib.moe_ffn_block_ex(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wr), _ptr(Wrq), _ptr(Wrs), _ptr(Wgq),
+                                 _ptr(Wgs), _ptr(Wuq), _ptr(Wus), _ptr(Wdq), _ptr(Wds), *[_ptr(t) for t in sh], sdff,
+                                 rows, d, dff, E, k, _ptr(sum), _ptr(idx), _ptr(wts), _ptr(out), act, _ptr(scratch),
+                                 scratch.numel(), _stream(stream)))
+    return sum, idx, wts, out

@@ -149,10 +149,17 @@ size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E
     case Q8S_FN_DOWN:
         return q8s::down_scratch_bytes(rows, d, dff, k, act);
     case Q8S_FN_BLOCK:
-        return q8s::block_scratch_bytes(rows, d, dff, E, k, act);
+        return q8s::block_scratch_bytes(rows, d, dff, 0, E, k, act);
     default:
         return 0;
     }
+}
+
+size_t q8s_block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k, int act)
+{
+    if (rows <= 0 || E <= 0 || k <= 0 || d <= 0 || dff <= 0 || sdff < 0)
+        return 0;
+    return q8s::block_scratch_bytes(rows, d, dff, sdff, E, k, act);
 }
 
 int q8_gemv(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in, const float *x, const int8_t *xq,
@@ -244,6 +251,39 @@ int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_t d, int
         return rc;
     clear_stale();
     return launched(q8s::route_launch(x, Wr, rows, d, E, k, idx, wts, scratch, as_stream(stream)), fn);
+}
+
+int moe_route_topk_q8(const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq, const float *Wrs,
+                      int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx, float *wts, int act, void *scratch,
+                      size_t scratch_bytes, void *stream)
+{
+    const char *fn = "moe_route_topk_q8";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, 32, E, k)))
+        return rc;
+    std::vector<Span> ins = {{Wrq, (size_t)(E * d), "Wrq"}, {Wrs, (size_t)(E * d / 32) * 4, "Wrs"}};
+    if (act == Q8S_ACT_F32) {
+        ins.push_back({x, (size_t)(rows * d) * 4, "x"});
+    } else {
+        ins.push_back({xq, (size_t)(rows * d), "xq"});
+        ins.push_back({xs, (size_t)(rows * d / 32) * 4, "xs"});
+    }
+    std::vector<Span> outs = {{idx, (size_t)(rows * k) * 4, "idx"}, {wts, (size_t)(rows * k) * 4, "wts"}};
+    const size_t need = q8s::route_scratch_bytes(rows, E);
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
+        return rc;
+    if (!scratch || scratch_bytes < need)
+        return fail(Q8S_ESCRATCH, "%s: scratch of %zu bytes given, %zu needed (the logits)", fn,
+                    scratch ? scratch_bytes : (size_t)0, need);
+    if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0)
+        return fail(Q8S_EALIGN, "%s: `scratch` is not 256-byte aligned", fn);
+    outs.push_back({scratch, need, "scratch"});
+    if ((rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::route_q8_launch(act == 0 ? x : nullptr, act == 1 ? xq : nullptr, act == 1 ? xs : nullptr,
+                                         Wrq, Wrs, rows, d, E, k, act, idx, wts, scratch, as_stream(stream)),
+                    fn);
 }
 
 int moe_gate_up(const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq, const float *Wgs,
@@ -397,10 +437,12 @@ int add_rmsnorm_gemv(const float *h, const float *r, const float *w, float eps, 
     return launched(e, fn);
 }
 
-int add_rmsnorm_router(const float *h, const float *r, const float *w, float eps, const float *Wr, int64_t rows,
-                       int64_t d, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits, void *stream)
+namespace {
+
+int norm_router_common(const char *fn, const float *h, const float *r, const float *w, float eps,
+                       const q8s::RouterRows &rt, int64_t rows, int64_t d, int64_t E, float *sum, float *x,
+                       int8_t *xq, float *xs, double *logits, void *stream)
 {
-    const char *fn = "add_rmsnorm_router";
     int rc;
     if ((rc = check_count(fn, "rows", rows, 65535)) || (rc = check_dim32(fn, "d", d)) ||
         (rc = check_count(fn, "E", E, Q8S_MAX_E)))
@@ -415,7 +457,13 @@ int add_rmsnorm_router(const float *h, const float *r, const float *w, float eps
     if (!x && !xq)
         return fail(Q8S_EINVAL, "%s: neither `x` nor `xq` is given -- the normed row would not be written", fn);
     const size_t n = (size_t)(rows * d);
-    std::vector<Span> ins = {{h, n * 4, "h"}, {r, n * 4, "r"}, {w, (size_t)d * 4, "w"}, {Wr, (size_t)(E * d) * 4, "Wr"}};
+    std::vector<Span> ins = {{h, n * 4, "h"}, {r, n * 4, "r"}, {w, (size_t)d * 4, "w"}};
+    if (rt.Wrq) {
+        ins.push_back({rt.Wrq, (size_t)(E * d), "Wrq"});
+        ins.push_back({rt.Wrs, (size_t)(E * d / 32) * 4, "Wrs"});
+    } else {
+        ins.push_back({rt.Wr, (size_t)(E * d) * 4, "Wr"});
+    }
     std::vector<Span> outs = {{sum, n * 4, "sum"}, {logits, (size_t)(rows * E) * 8, "logits"}};
     if (x)
         outs.push_back({x, n * 4, "x"});
@@ -426,8 +474,31 @@ int add_rmsnorm_router(const float *h, const float *r, const float *w, float eps
     if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
         return rc;
     clear_stale();
-    return launched(q8s::norm_logits_launch(h, r, w, rows, d, eps, Wr, E, sum, x, xq, xs, logits, as_stream(stream)),
+    return launched(q8s::norm_logits_launch(h, r, w, rows, d, eps, rt, E, sum, x, xq, xs, logits, as_stream(stream)),
                     fn);
+}
+
+} // namespace
+
+int add_rmsnorm_router(const float *h, const float *r, const float *w, float eps, const float *Wr, int64_t rows,
+                       int64_t d, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits, void *stream)
+{
+    return norm_router_common("add_rmsnorm_router", h, r, w, eps, q8s::RouterRows{Wr, nullptr, nullptr, 0}, rows, d,
+                              E, sum, x, xq, xs, logits, stream);
+}
+
+int add_rmsnorm_router_q8(const float *h, const float *r, const float *w, float eps, const int8_t *Wrq,
+                          const float *Wrs, int64_t rows, int64_t d, int64_t E, float *sum, float *x, int8_t *xq,
+                          float *xs, double *logits, int act, void *stream)
+{
+    const char *fn = "add_rmsnorm_router_q8";
+    int rc;
+    if ((rc = check_act(fn, act)))
+        return rc;
+    if (!Wrq)
+        return fail(Q8S_EINVAL, "%s: `Wrq` is null", fn);
+    return norm_router_common(fn, h, r, w, eps, q8s::RouterRows{nullptr, Wrq, Wrs, act}, rows, d, E, sum, x, xq, xs,
+                              logits, stream);
 }
 
 int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq,
@@ -484,36 +555,65 @@ int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, con
     return launched(q8s::route_gate_up_launch(a, as_stream(stream)), fn);
 }
 
-int moe_ffn_block(const float *h, const float *r, const float *w, float eps, const float *Wr, const int8_t *Wgq,
-                  const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Wdq, const float *Wds,
-                  int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, float *sum, int32_t *idx, float *wts,
-                  float *out, int act, void *scratch, size_t scratch_bytes, void *stream)
+namespace {
+
+int block_common(const char *fn, const float *h, const float *r, const float *w, float eps,
+                 const q8s::RouterRows &rt, const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                 const int8_t *Wdq, const float *Wds, const int8_t *Sgq, const float *Sgs, const int8_t *Suq,
+                 const float *Sus, const int8_t *Sdq, const float *Sds, int64_t sdff, int64_t rows, int64_t d,
+                 int64_t dff, int64_t E, int64_t k, float *sum, int32_t *idx, float *wts, float *out, int act,
+                 void *scratch, size_t scratch_bytes, void *stream)
 {
-    const char *fn = "moe_ffn_block";
     int rc;
     if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
         return rc;
     if (!(eps >= 0.0f) || eps != eps)
         return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    if (sdff < 0)
+        return fail(Q8S_EINVAL, "%s: sdff = %lld is negative", fn, (long long)sdff);
+    if (sdff > 0) {
+        if ((rc = check_dim32(fn, "sdff", sdff)))
+            return rc;
+        if (!q8s::shared_fits(dff, sdff, k))
+            return fail(Q8S_EUNSUPPORTED, "%s: a shared expert of sdff = %lld next to k = %lld experts of dff = %lld "
+                        "exceeds the down-combine's 512 (slot, slice) partials", fn, (long long)sdff, (long long)k,
+                        (long long)dff);
+    } else if (Sgq || Sgs || Suq || Sus || Sdq || Sds) {
+        return fail(Q8S_EINVAL, "%s: shared-expert matrices given with sdff = 0", fn);
+    }
     const size_t n = (size_t)(rows * d);
     const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
     std::vector<Span> ins = {{h, n * 4, "h"},
                              {r, n * 4, "r"},
                              {w, (size_t)d * 4, "w"},
-                             {Wr, (size_t)(E * d) * 4, "Wr"},
                              {Wgq, wq, "Wgq"},
                              {Wgs, wsb, "Wgs"},
                              {Wuq, wq, "Wuq"},
                              {Wus, wsb, "Wus"},
                              {Wdq, (size_t)(E * d) * (size_t)dff, "Wdq"},
                              {Wds, (size_t)(E * d) * (size_t)(dff / 32) * 4, "Wds"}};
+    if (rt.Wrq) {
+        ins.push_back({rt.Wrq, (size_t)(E * d), "Wrq"});
+        ins.push_back({rt.Wrs, (size_t)(E * d / 32) * 4, "Wrs"});
+    } else {
+        ins.push_back({rt.Wr, (size_t)(E * d) * 4, "Wr"});
+    }
+    if (sdff > 0) {
+        const size_t sq = (size_t)sdff * (size_t)d, ss = (size_t)sdff * (size_t)(d / 32) * 4;
+        ins.push_back({Sgq, sq, "Sgq"});
+        ins.push_back({Sgs, ss, "Sgs"});
+        ins.push_back({Suq, sq, "Suq"});
+        ins.push_back({Sus, ss, "Sus"});
+        ins.push_back({Sdq, sq, "Sdq"});
+        ins.push_back({Sds, (size_t)d * (size_t)(sdff / 32) * 4, "Sds"});
+    }
     std::vector<Span> outs = {{sum, n * 4, "sum"},
                               {idx, (size_t)(rows * k) * 4, "idx"},
                               {wts, (size_t)(rows * k) * 4, "wts"},
                               {out, n * 4, "out"}};
     if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
         return rc;
-    const size_t need = q8s::block_scratch_bytes(rows, d, dff, E, k, act);
+    const size_t need = q8s::block_scratch_bytes(rows, d, dff, sdff, E, k, act);
     if (!scratch || scratch_bytes < need)
         return fail(Q8S_ESCRATCH,
                     "%s: scratch of %zu bytes given, %zu needed (logits, the normed row, the hidden rows)", fn,
@@ -523,10 +623,37 @@ int moe_ffn_block(const float *h, const float *r, const float *w, float eps, con
     outs.push_back({scratch, need, "scratch"});
     if ((rc = check_disjoint(fn, ins, outs)))
         return rc;
-    q8s::BlockArgs b{h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, rows, d, dff, E, k, sum, idx, wts, out, act,
-                     scratch};
+    q8s::BlockArgs b{h,    r,    w,  eps, rt,  Wgq, Wgs, Wuq, Wus, Wdq, Wds,     rows, d,   dff, E,   k,  sum,
+                     idx,  wts,  out, act, scratch, Sgq, Sgs, Suq, Sus, Sdq, Sds, sdff};
     clear_stale();
     return launched(q8s::block_launch(b, as_stream(stream)), fn);
+}
+
+} // namespace
+
+int moe_ffn_block(const float *h, const float *r, const float *w, float eps, const float *Wr, const int8_t *Wgq,
+                  const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Wdq, const float *Wds,
+                  int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, float *sum, int32_t *idx, float *wts,
+                  float *out, int act, void *scratch, size_t scratch_bytes, void *stream)
+{
+    return block_common("moe_ffn_block", h, r, w, eps, q8s::RouterRows{Wr, nullptr, nullptr, 0}, Wgq, Wgs, Wuq, Wus,
+                        Wdq, Wds, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, rows, d, dff, E, k, sum, idx,
+                        wts, out, act, scratch, scratch_bytes, stream);
+}
+
+int moe_ffn_block_ex(const float *h, const float *r, const float *w, float eps, const float *Wr, const int8_t *Wrq,
+                     const float *Wrs, const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                     const int8_t *Wdq, const float *Wds, const int8_t *Sgq, const float *Sgs, const int8_t *Suq,
+                     const float *Sus, const int8_t *Sdq, const float *Sds, int64_t sdff, int64_t rows, int64_t d,
+                     int64_t dff, int64_t E, int64_t k, float *sum, int32_t *idx, float *wts, float *out, int act,
+                     void *scratch, size_t scratch_bytes, void *stream)
+{
+    const char *fn = "moe_ffn_block_ex";
+    if ((Wr != nullptr) == (Wrq != nullptr))
+        return fail(Q8S_EINVAL, "%s: give the router as float rows `Wr` or as Q8_0 rows `Wrq`/`Wrs`, exactly one", fn);
+    return block_common(fn, h, r, w, eps, q8s::RouterRows{Wr, Wrq, Wrs, act}, Wgq, Wgs, Wuq, Wus, Wdq, Wds, Sgq, Sgs,
+                        Suq, Sus, Sdq, Sds, sdff, rows, d, dff, E, k, sum, idx, wts, out, act, scratch, scratch_bytes,
+                        stream);
 }
 
 } // extern "C"

@@ -17,11 +17,17 @@
 // the grouped kernels (add_rmsnorm_q8, moe_route_topk, then the chunk gate-up
 // and down), as do rows too long or experts too many for the fused launches.
 //
+// The router is float32 or Q8_0 rows (lane_link.rs fn prim, Moe arm); a
+// shared expert rides in the gate-up and down-combine launches (fn
+// class_launch, SharedExpertFusion arm), except under a chunk's grouped
+// kernels, after which it runs as its own gate-up and an adding down-combine.
+//
 // Scratch, 256-byte aligned pieces in this order: the logits (double
 // [rows, E]), the normed row x (f32 [rows, d]), its Q8_0 form (int8
-// [rows, d] + f32 [rows, d/32]), the hidden rows (f32 [rows, k, dff] in f32
-// numerics; their Q8_0 form in int8, plus the f32 rows when rows > 1), then
-// moe_down_combine's scratch.
+// [rows, d] + f32 [rows, d/32]), the hidden rows (f32 [rows, k*dff + sdff]
+// in f32 numerics; their Q8_0 form in int8), then for a chunk the f32 hidden
+// rows [rows, k, dff] the grouped kernels stage and the shared expert's own
+// hidden rows [rows, sdff], then moe_down_combine's scratch.
 #include "q8s_device.h"
 #include "q8s_internal.h"
 
@@ -37,11 +43,16 @@ struct BlockScratch {
     float *h;
     int8_t *hq;
     float *hs;
+    float *sh;  // a chunk's shared hidden rows (f32, or their Q8_0 form below)
+    int8_t *shq;
+    float *shs;
     void *down;
     size_t bytes;
 };
 
-BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
+bool chunk_mode(int64_t rows, int64_t d, int64_t dff, int act) { return act == 1 && rows > 1 && chunk_supported(d, dff); }
+
+BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k, int act)
 {
     BlockScratch s{};
     size_t off = 0;
@@ -50,7 +61,9 @@ BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t E, 
         off += align256(n);
         return p;
     };
-    const size_t nh = (size_t)(rows * k * dff);
+    const bool chunk = chunk_mode(rows, d, dff, act);
+    // hidden values a row: the routed ones and, outside a chunk, the shared
+    const size_t nh = (size_t)rows * (size_t)(k * dff + (chunk ? 0 : sdff));
     s.logits = reinterpret_cast<double *>(take((size_t)(rows * E) * sizeof(double)));
     s.x = reinterpret_cast<float *>(take((size_t)(rows * d) * 4));
     if (act == 1) {
@@ -58,10 +71,15 @@ BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t E, 
         s.xs = reinterpret_cast<float *>(take((size_t)(rows * d / QB) * 4));
         s.hq = reinterpret_cast<int8_t *>(take(nh));
         s.hs = reinterpret_cast<float *>(take(nh / QB * 4));
-        if (rows > 1)  // the chunk kernels stage the float32 hidden rows
+        if (chunk)  // the chunk kernels stage the float32 hidden rows
             s.h = reinterpret_cast<float *>(take(nh * 4));
     } else {
         s.h = reinterpret_cast<float *>(take(nh * 4));
+    }
+    if (chunk && sdff > 0) {
+        const size_t ns = (size_t)(rows * sdff);
+        s.shq = reinterpret_cast<int8_t *>(take(ns));
+        s.shs = reinterpret_cast<float *>(take(ns / QB * 4));
     }
     const size_t dn = down_scratch_bytes(rows, d, dff, k, act);
     s.down = dn ? take(dn) : nullptr;
@@ -71,19 +89,20 @@ BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t E, 
 
 } // namespace
 
-size_t block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
+size_t block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k, int act)
 {
-    return carve(nullptr, rows, d, dff, E, k, act).bytes;
+    return carve(nullptr, rows, d, dff, sdff, E, k, act).bytes;
 }
 
 bool block_fused(int64_t rows, int64_t d, int64_t dff, int64_t E, int act)
 {
-    return E <= ROUTE_FUSED_MAX_E && norm_logits_supported(d) && !(act == 1 && rows > 1 && chunk_supported(d, dff));
+    return E <= ROUTE_FUSED_MAX_E && norm_logits_supported(d) && !chunk_mode(rows, d, dff, act);
 }
 
 hipError_t block_launch(const BlockArgs &b, hipStream_t st)
 {
-    const BlockScratch s = carve(static_cast<char *>(b.scratch), b.rows, b.d, b.dff, b.E, b.k, b.act);
+    const BlockScratch s = carve(static_cast<char *>(b.scratch), b.rows, b.d, b.dff, b.sdff, b.E, b.k, b.act);
+    const bool chunk = chunk_mode(b.rows, b.d, b.dff, b.act);
     MoeArgs a{};
     a.x = b.act == 0 ? s.x : nullptr;
     a.xq = s.xq;
@@ -107,10 +126,23 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
     a.y = b.out;
     a.act = b.act;
     a.scratch = s.down;
+    if (!chunk) {
+        a.Sgq = b.Sgq;
+        a.Sgs = b.Sgs;
+        a.Suq = b.Suq;
+        a.Sus = b.Sus;
+        a.Sdq = b.Sdq;
+        a.Sds = b.Sds;
+        a.sdff = b.sdff;
+    }
+    // the router reads the normed row's Q8_0 form only for Q8_0 rows in int8
+    // numerics (a float router reads float32)
+    RouterRows rt = b.rt;
+    rt.act = b.act;
     hipError_t err;
     if (block_fused(b.rows, b.d, b.dff, b.E, b.act)) {
-        err = norm_logits_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, b.Wr, b.E, b.sum, b.act == 0 ? s.x : nullptr, s.xq,
-                                 s.xs, s.logits, st);
+        err = norm_logits_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, rt, b.E, b.sum,
+                                 b.act == 0 ? s.x : nullptr, s.xq, s.xs, s.logits, st);
         if (err != hipSuccess)
             return err;
         a.logits = s.logits;
@@ -121,14 +153,32 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
         err = add_rmsnorm_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, b.sum, s.x, s.xq, s.xs, st);
         if (err != hipSuccess)
             return err;
-        err = route_launch(s.x, b.Wr, b.rows, b.d, b.E, b.k, b.idx, b.wts, s.logits, st);
+        if (rt.Wrq)
+            err = route_q8_launch(s.x, s.xq, s.xs, rt.Wrq, rt.Wrs, b.rows, b.d, b.E, b.k, rt.act, b.idx, b.wts,
+                                  s.logits, st);
+        else
+            err = route_launch(s.x, rt.Wr, b.rows, b.d, b.E, b.k, b.idx, b.wts, s.logits, st);
         if (err != hipSuccess)
             return err;
         err = gate_up_launch(a, st);
     }
     if (err != hipSuccess)
         return err;
-    return down_launch(a, st);
+    err = down_launch(a, st);
+    if (err != hipSuccess || !chunk || b.sdff == 0)
+        return err;
+    MoeArgs sa = a;
+    sa.Sgq = b.Sgq;
+    sa.Sgs = b.Sgs;
+    sa.Suq = b.Suq;
+    sa.Sus = b.Sus;
+    sa.Sdq = b.Sdq;
+    sa.Sds = b.Sds;
+    sa.sdff = b.sdff;
+    sa.h = nullptr;
+    sa.hq = s.shq;
+    sa.hs = s.shs;
+    return shared_launch(sa, st);
 }
 
 } // namespace q8s

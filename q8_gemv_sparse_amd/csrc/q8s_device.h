@@ -137,9 +137,9 @@ Q8S_DEV int q8_code(float v, float id)
 }
 
 // Quantise 8 consecutive values held by one thread of a 4-thread group that
-// owns one 32-value block (the group's lanes are neighbours within a quad);
-// writes the 8 codes and, from the group's first thread, the block scale.
-Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool leader)
+// owns one 32-value block (the group's lanes are neighbours within a quad):
+// the 8 codes packed in two words, and the block scale.
+Q8S_DEV uint2 quant8(const float (&v)[8], float &scale)
 {
     float amax = 0.0f;
 #pragma unroll
@@ -155,7 +155,16 @@ Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool lea
         lo |= (uint32_t)(q8_code(v[i], id) & 0xFF) << (8 * i);
         hi |= (uint32_t)(q8_code(v[4 + i], id) & 0xFF) << (8 * i);
     }
-    *reinterpret_cast<uint2 *>(q) = make_uint2(lo, hi);
+    scale = d;
+    return make_uint2(lo, hi);
+}
+
+// quant8, then the 8 codes written and, from the group's first thread, the
+// block scale.
+Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool leader)
+{
+    float d;
+    *reinterpret_cast<uint2 *>(q) = quant8(v, d);
     if (leader)
         *scale = d;
 }

@@ -80,18 +80,32 @@ hipError_t norm_gemv_launch(const NormGemvArgs &a, hipStream_t st);
 hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st);
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               float *sum, float *y, int8_t *yq, float *ys, hipStream_t st);
+// The router's rows: float32 Wr [E, d], or Q8_0 Wrq [E, d] + Wrs [E, d/32]
+// (Wrq non-null); a Q8_0 router reads float32 activations (act 0) or their
+// one-word int8 form (act 1).
+struct RouterRows {
+    const float *Wr;
+    const int8_t *Wrq;
+    const float *Wrs;
+    int act;
+};
+
 // add + norm of each row fused with the router's logits (grid E x rows); the
 // normed activation goes to x and/or xq/xs (whichever is non-null), logits to
 // `logits`
 bool norm_logits_supported(int64_t d);
 hipError_t norm_logits_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
-                              const float *Wr, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits,
-                              hipStream_t st);
+                              const RouterRows &rt, int64_t E, float *sum, float *x, int8_t *xq, float *xs,
+                              double *logits, hipStream_t st);
 
 // router scratch: f64 logits [rows, E]
 size_t route_scratch_bytes(int64_t rows, int64_t E);
 hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
                         float *wts, void *scratch, hipStream_t st);
+// the router over Q8_0 rows: float32 x (act 0) or its Q8_0 form xq/xs (act 1)
+hipError_t route_q8_launch(const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq, const float *Wrs,
+                           int64_t rows, int64_t d, int64_t E, int64_t k, int act, int32_t *idx, float *wts,
+                           void *scratch, hipStream_t st);
 
 struct MoeArgs {
     const float *x;
@@ -116,12 +130,29 @@ struct MoeArgs {
     const double *logits;
     int32_t *idx_w;
     float *wts_w;
+    // a shared expert (sdff > 0): gate/up [sdff, d], down [d, sdff], its
+    // hidden row after the K routed ones (rows of k*dff + sdff values)
+    const int8_t *Sgq;
+    const float *Sgs;
+    const int8_t *Suq;
+    const float *Sus;
+    const int8_t *Sdq;
+    const float *Sds;
+    int64_t sdff;
+    // the down-combine adds its result to y instead of writing it
+    bool acc_out;
 };
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st);
 // gate-up that takes each row's top-K from `logits` itself (E <= ROUTE_FUSED_MAX_E)
 hipError_t route_gate_up_launch(const MoeArgs &a, hipStream_t st);
 size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t k, int act);
 hipError_t down_launch(const MoeArgs &a, hipStream_t st);
+// whether a shared expert of sdff fits the down-combine's (slot, slice)
+// partials next to k slots of dff
+bool shared_fits(int64_t dff, int64_t sdff, int64_t k);
+// the shared expert alone, per row (gate-up, then a down-combine that adds
+// into y): a chunk's grouped kernels carry no shared expert
+hipError_t shared_launch(const MoeArgs &a, hipStream_t st);
 
 // a chunk's mixture (rows > 1, int8 activations): choices grouped by expert,
 // for d <= 2048 and dff <= 4096 (one slice of a wave each)
@@ -136,7 +167,7 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct BlockArgs {
     const float *h, *r, *w;
     float eps;
-    const float *Wr;
+    RouterRows rt;
     const int8_t *Wgq;
     const float *Wgs;
     const int8_t *Wuq;
@@ -150,8 +181,16 @@ struct BlockArgs {
     float *out;
     int act;
     void *scratch;
+    // the shared expert (sdff 0: none)
+    const int8_t *Sgq;
+    const float *Sgs;
+    const int8_t *Suq;
+    const float *Sus;
+    const int8_t *Sdq;
+    const float *Sds;
+    int64_t sdff;
 };
-size_t block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
+size_t block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k, int act);
 bool block_fused(int64_t rows, int64_t d, int64_t dff, int64_t E, int act);
 hipError_t block_launch(const BlockArgs &b, hipStream_t st);
 

@@ -17,6 +17,12 @@
 // kernels of q8s_moe_chunk.hip.
 // route + gate-up (the mixture block's fused path): the same tiles, each
 //   workgroup first taking the row's top-K from the router logits itself.
+// A shared expert (lane_link.rs fn class_launch, SharedExpertFusion arm: an
+// always-on expert carried by the mixture's launch) adds its own tiles after
+// the K slots' in the gate-up grid, its hidden row after the K routed ones
+// (arena.rs fn scratch: K*dff + sdff hidden values a row), and its slices
+// after the (slot, slice) pairs of the down-combine, summed with weight 1
+// after the routed sum.
 // down-combine (one workgroup per 8 outputs of one row): waves take
 //   (slot, k-slice) pairs, so all K experts' rows of those outputs stream at
 //   once; the partials meet in LDS and are weighted and summed in slot order.
@@ -30,6 +36,8 @@ constexpr int DN_TILE = 8;
 constexpr int MAX_KS = 16;
 constexpr int GU_MAX_KS = 32;
 constexpr int DN_MAX_WAVES = 8;
+// (slot, slice) pairs a down-combine workgroup holds partials of
+constexpr int DN_MAX_PAIRS = Q8S_MAX_K_DEV * MAX_KS;
 
 // LDS of a gate-up workgroup: the slices' partial sums (rows cut into
 // slices) and the tile's hidden values (int8 numerics).
@@ -44,11 +52,13 @@ struct GuLds {
 // of expert e.  With the row in one slice (ks == 1) each wave finishes its own
 // outputs; otherwise the waves deal out (slice, step) items and the slices'
 // partial sums meet in LDS.
+// The tile's weight rows start at row rbase of the gate/up matrices given
+// (an expert's or the shared expert's), its hidden values at hbase.
 template <int ACT, int LPR, int C>
-Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, int e, bool valid, int64_t row, int j,
+Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, bool valid, int64_t row, int64_t rbase, int64_t hbase,
                           const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                           const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs,
-                          const int8_t *__restrict__ Wuq, const float *__restrict__ Wus, int d, int dff, int k, int ks,
+                          const int8_t *__restrict__ Wuq, const float *__restrict__ Wus, int d, int ks,
                           float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
 {
     using S = GuShape<ACT, LPR, C>;
@@ -56,10 +66,7 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, int e, bool valid,
     constexpr int STEPS = T / OPS;
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
-    const int o0 = blockIdx.x * T;
     const int nch = d >> 4, nb = d >> 5;
-    const int64_t rbase = (int64_t)(valid ? e : 0) * dff + o0;
-    const int64_t hbase = (row * k + j) * dff + o0;
 
     // A wave's items are wid, wid + NW, ... (ks of them: T = NW * OPS); item i
     // is slice i % ks of step i / ks.  For a row cut into slices, with ks
@@ -154,49 +161,89 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, int e, bool valid,
     }
 }
 
-// gate-up with the choices given: one workgroup per tile of one (row, slot).
+// The shared expert's matrices (none when sdff == 0): gate/up [sdff, d],
+// down [d, sdff].
+struct SharedW {
+    const int8_t *gq;
+    const float *gs;
+    const int8_t *uq;
+    const float *us;
+    const int8_t *dq;
+    const float *ds;
+    int sdff;
+};
+
+// A row's gate-up workgroups: bx < k*tpe are slot bx/tpe's tile bx%tpe (tpe
+// tiles of T an expert); the rest are the shared expert's tiles.
+struct GuTile {
+    int j, o0;
+    bool shared;
+};
+Q8S_DEV GuTile gu_tile(int bx, int k, int tpe, int T)
+{
+    if (bx < k * tpe)
+        return {bx / tpe, (bx % tpe) * T, false};
+    return {k, (bx - k * tpe) * T, true};
+}
+
+// gate-up with the choices given: one workgroup per tile of one (row, slot),
+// grid (k*dff/T + sdff/T, rows).
 template <int ACT, int LPR, int C>
 __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
               const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
-              const float *__restrict__ Wus, const int32_t *__restrict__ idx, int d, int dff, int E, int k, int ks,
-              float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
+              const float *__restrict__ Wus, SharedW sw, const int32_t *__restrict__ idx, int d, int dff, int E,
+              int k, int ks, float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
 {
-    __shared__ GuLds<GuShape<ACT, LPR, C>::T> sm;
-    const int j = blockIdx.y;
-    const int64_t row = blockIdx.z;
-    const int e = idx[row * k + j];
-    gate_up_tile<ACT, LPR, C>(sm, e, e >= 0 && e < E, row, j, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, dff, k, ks, h, hq, hs);
+    constexpr int T = GuShape<ACT, LPR, C>::T;
+    __shared__ GuLds<T> sm;
+    const int64_t row = blockIdx.y;
+    const GuTile t = gu_tile(blockIdx.x, k, dff / T, T);
+    const int64_t hbase = row * ((int64_t)k * dff + sw.sdff) + (int64_t)t.j * dff + t.o0;
+    const int e = t.shared ? 0 : idx[row * k + t.j];
+    const bool valid = t.shared || (e >= 0 && e < E);
+    const int64_t rbase = t.shared ? t.o0 : (int64_t)(valid ? e : 0) * dff + t.o0;
+    gate_up_tile<ACT, LPR, C>(sm, valid, row, rbase, hbase, x, xq, xs, t.shared ? sw.gq : Wgq,
+                              t.shared ? sw.gs : Wgs, t.shared ? sw.uq : Wuq, t.shared ? sw.us : Wus, d, ks, h, hq,
+                              hs);
 }
 
 // gate-up that first takes the row's top-K itself from the router logits:
-// every workgroup ranks the row's E logits in LDS (topk_select) and reads its
-// expert from the result, so the choices need no launch of their own; the
-// workgroup of tile 0, slot 0 writes the row's idx and wts for the
-// down-combine launch.
+// every routed workgroup ranks the row's E logits in LDS (topk_select) and
+// reads its expert from the result, so the choices need no launch of their
+// own; the workgroup of tile 0, slot 0 writes the row's idx and wts for the
+// down-combine launch.  The shared expert's workgroups need no ranking.
 template <int ACT, int LPR, int C>
 __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     k_route_gate_up(const double *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ wts,
                     const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                     const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
-                    const float *__restrict__ Wus, int d, int dff, int E, int k, int ks, float *__restrict__ h,
-                    int8_t *__restrict__ hq, float *__restrict__ hs)
+                    const float *__restrict__ Wus, SharedW sw, int d, int dff, int E, int k, int ks,
+                    float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
 {
     static_assert(ROUTE_FUSED_MAX_E <= TOPK_LDS_E, "the row's logits fit the top-K LDS");
-    __shared__ GuLds<GuShape<ACT, LPR, C>::T> sm;
-    __shared__ TopkLds t;
-    const int j = blockIdx.y;
-    const int64_t row = blockIdx.z;
-    topk_load(t, logits + row * E, E);
+    constexpr int T = GuShape<ACT, LPR, C>::T;
+    __shared__ GuLds<T> sm;
+    __shared__ TopkLds tk;
+    const int64_t row = blockIdx.y;
+    const GuTile t = gu_tile(blockIdx.x, k, dff / T, T);
+    const int64_t hbase = row * ((int64_t)k * dff + sw.sdff) + (int64_t)t.j * dff + t.o0;
+    if (t.shared) {
+        gate_up_tile<ACT, LPR, C>(sm, true, row, t.o0, hbase, x, xq, xs, sw.gq, sw.gs, sw.uq, sw.us, d, ks, h, hq,
+                                  hs);
+        return;
+    }
+    topk_load(tk, logits + row * E, E);
     __syncthreads();
-    topk_select(t, E, k);
+    topk_select(tk, E, k);
     __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(t.ch[j]);
-    gate_up_tile<ACT, LPR, C>(sm, e, true, row, j, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, dff, k, ks, h, hq, hs);
+    const int e = __builtin_amdgcn_readfirstlane(tk.ch[t.j]);
+    gate_up_tile<ACT, LPR, C>(sm, true, row, (int64_t)e * dff + t.o0, hbase, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, ks, h,
+                              hq, hs);
     // the choices and weights go out after the tile, off its critical path
     // (only the down-combine launch reads them)
-    if (blockIdx.x == 0 && j == 0 && threadIdx.x < WAVE)
-        route_finish(t.kl, t.ch, k, idx + row * k, wts + row * k);
+    if (blockIdx.x == 0 && threadIdx.x < WAVE)
+        route_finish(tk.kl, tk.ch, k, idx + row * k, wts + row * k);
 }
 
 // Rows a lane group takes per step of the down-combine (measured: one row a
@@ -210,12 +257,16 @@ constexpr int dn_unroll()
     return C >= 3 ? 1 : (LPR == 16 ? 2 : 4);
 }
 
+// Waves take (slot, slice) pairs: pairs j*ks + s for the K slots, then
+// k*ks + s for the shared expert's kss slices of its sdff-long rows (the same
+// lane shape).  The grid is (d / DN_TILE, rows); acc_out adds the result to y.
 template <int ACT, int LPR, int C>
 __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__restrict__ h, const int8_t *__restrict__ hq,
                                                               const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
-                                               const float *__restrict__ Wds, const int32_t *__restrict__ idx,
-                                               const float *__restrict__ wts, int d, int dff, int E, int k, int ks,
-                                               float *__restrict__ y)
+                                                              const float *__restrict__ Wds, SharedW sw,
+                                                              const int32_t *__restrict__ idx,
+                                                              const float *__restrict__ wts, int d, int dff, int E, int k,
+                                                              int ks, int kss, int acc_out, float *__restrict__ y)
 {
     constexpr int G = WAVE / LPR;
     constexpr int U = dn_unroll<ACT, LPR, C>();
@@ -223,23 +274,28 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
     constexpr int STEPS = DN_TILE / OPS;
     static_assert(DN_TILE % OPS == 0 && OPS % G == 0, "steps tile the outputs");
     constexpr int UU = OPS / G;
-    __shared__ float part[Q8S_MAX_K_DEV * MAX_KS][DN_TILE];
+    __shared__ float part[DN_MAX_PAIRS][DN_TILE];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
     const int nwaves = blockDim.x >> 6;
     const int o0 = blockIdx.x * DN_TILE;
-    const int64_t row = blockIdx.z;
-    const int nch = dff >> 4, nb = dff >> 5;
-    const int pairs = k * ks;
+    const int64_t row = blockIdx.y;
+    const int64_t hw = (int64_t)k * dff + sw.sdff;
+    const int rp = k * ks, pairs = rp + kss;
 
     for (int p = wid; p < pairs; p += nwaves) {
-        const int j = p / ks, s = p % ks;
-        const int e = idx[row * k + j];
-        const bool valid = (e >= 0 && e < E);
+        const bool sh = p >= rp;
+        const int j = sh ? k : p / ks, s = sh ? p - rp : p % ks;
+        const int e = sh ? 0 : idx[row * k + j];
+        const bool valid = sh || (e >= 0 && e < E);
+        const int n_in = sh ? sw.sdff : dff;
+        const int nch = n_in >> 4, nb = n_in >> 5;
+        const int8_t *wq = sh ? sw.dq : Wdq;
+        const float *ws = sh ? sw.ds : Wds;
         const int ch0 = s * LPR * C;
         const int sl = min(LPR * C, nch - ch0);
-        const int64_t hrow = (row * k + j) * dff;
-        const int64_t rbase = (int64_t)(valid ? e : 0) * d + o0;
+        const int64_t hrow = row * hw + (int64_t)j * dff;
+        const int64_t rbase = (int64_t)(valid && !sh ? e : 0) * d + o0;
         // Each step's weight rows are requested before the previous step is
         // reduced.  The loads are straight-line code (an invalid choice reads
         // expert 0's rows and is zeroed at the dot; chunks past the slice meet
@@ -250,7 +306,7 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
 #pragma unroll
             for (int u = 0; u < UU; u++) {
                 const int64_t o = rbase + st * OPS + u * G + grp;
-                load_row_flat<LPR, C>(w[u], Wdq + o * dff, Wds + o * nb, ch0, sl, lig);
+                load_row_flat<LPR, C>(w[u], wq + o * n_in, ws + o * nb, ch0, sl, lig);
             }
         };
         // The hidden row's chunks are requested first (they come from cache),
@@ -284,7 +340,14 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
                 dj += part[j * ks + s][t];
             acc = __builtin_fmaf(wts[row * k + j], dj, acc);
         }
-        y[row * d + o0 + t] = acc;
+        if (kss > 0) {
+            float ds = 0.0f;
+            for (int s = 0; s < kss; s++)
+                ds += part[rp + s][t];
+            acc += ds;
+        }
+        float *yo = y + row * d + o0 + t;
+        *yo = acc_out ? *yo + acc : acc;
     }
 }
 
@@ -293,13 +356,19 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
 
 namespace {
 
+SharedW shared_w(const MoeArgs &a)
+{
+    return SharedW{a.Sgq, a.Sgs, a.Suq, a.Sus, a.Sdq, a.Sds, (int)a.sdff};
+}
+
 template <int ACT, int LPR, int C>
 hipError_t gu_go(const MoeArgs &a, int ks, hipStream_t st)
 {
     using S = GuShape<ACT, LPR, C>;
-    dim3 grid((unsigned)(a.dff / S::T), (unsigned)a.k, (unsigned)a.rows);
+    dim3 grid((unsigned)((a.k * a.dff + a.sdff) / S::T), (unsigned)a.rows);
     hipLaunchKernelGGL((k_gate_up<ACT, LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq, a.Wgs,
-                       a.Wuq, a.Wus, a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
+                       a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h, a.hq,
+                       a.hs);
     return hipGetLastError();
 }
 
@@ -308,22 +377,25 @@ hipError_t rgu_go(const MoeArgs &a, int ks, hipStream_t st)
 {
     using S = GuShape<ACT, LPR, C>;
     static_assert(S::NW * WAVE >= ROUTE_FUSED_MAX_E, "one thread per logit at least");
-    dim3 grid((unsigned)(a.dff / S::T), (unsigned)a.k, (unsigned)a.rows);
+    dim3 grid((unsigned)((a.k * a.dff + a.sdff) / S::T), (unsigned)a.rows);
     hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w, a.wts_w,
-                       a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
-                       a.hq, a.hs);
+                       a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff, (int)a.E,
+                       (int)a.k, ks, a.h, a.hq, a.hs);
     return hipGetLastError();
 }
+
+// the shared expert's slices in a lane shape of LPR x C chunks
+int shared_slices(int64_t sdff, int lpr, int c) { return (int)((sdff / 16 + lpr * c - 1) / (lpr * c)); }
 
 template <int ACT, int LPR, int C>
 hipError_t dn_go(const MoeArgs &a, int ks, hipStream_t st)
 {
-    const int pairs = (int)a.k * ks;
+    const int kss = a.sdff ? shared_slices(a.sdff, LPR, C) : 0;
+    const int pairs = (int)a.k * ks + kss;
     const int nw = std::min(DN_MAX_WAVES, pairs);
-    dim3 grid((unsigned)(a.d / DN_TILE), 1, (unsigned)a.rows);
-    hipLaunchKernelGGL((k_down<ACT, LPR, C>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds, a.idx, a.wts,
-                       (int)a.d,
-                       (int)a.dff, (int)a.E, (int)a.k, ks, a.y);
+    dim3 grid((unsigned)(a.d / DN_TILE), (unsigned)a.rows);
+    hipLaunchKernelGGL((k_down<ACT, LPR, C>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds, shared_w(a),
+                       a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss, a.acc_out ? 1 : 0, a.y);
     return hipGetLastError();
 }
 
@@ -411,6 +483,29 @@ hipError_t down_launch(const MoeArgs &a, hipStream_t st)
     if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
         return chunk_down_launch(a, st);
     return a.act == 0 ? by_shape<0, DN>(a, a.dff, st) : by_shape<1, DN>(a, a.dff, st);
+}
+
+int64_t down_pairs(int64_t dff, int64_t sdff, int64_t k)
+{
+    const SliceShape sh = slice_shape(dff);
+    const int lpr = sh.ks > 1 ? 64 : sh.lpr, c = sh.ks > 1 ? 4 : sh.c;
+    return k * sh.ks + (sdff ? shared_slices(sdff, lpr, c) : 0);
+}
+
+bool shared_fits(int64_t dff, int64_t sdff, int64_t k)
+{
+    return down_pairs(dff, sdff, k) <= DN_MAX_PAIRS && down_pairs(sdff, sdff, 0) <= DN_MAX_PAIRS;
+}
+
+hipError_t shared_launch(const MoeArgs &a, hipStream_t st)
+{
+    MoeArgs s = a;
+    s.k = 0;
+    s.acc_out = true;
+    hipError_t err = gu_dispatch<GU>(s, st);
+    if (err != hipSuccess)
+        return err;
+    return s.act == 0 ? by_shape<0, DN>(s, s.sdff, st) : by_shape<1, DN>(s, s.sdff, st);
 }
 
 } // namespace q8s

@@ -80,16 +80,23 @@ __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__
 
 // The mixture block's first launch: the add + norm of the row, exactly as
 // k_add_rmsnorm_q8 forms it (the same shares, sums and roundings), and one
-// router logit per workgroup, l[row][e] = sum_t Wr[e][t] * y[t] in double
-// (fn emit_moe_forward's router over the normed row).  Every workgroup of a
-// row forms the whole normed row -- it re-reads h, r and w, 24 bytes a value,
-// mostly from cache -- so no workgroup waits for another; the workgroup of
-// expert 0 also writes the sum and the activation the gate-up launch reads
-// (float32 x and/or its Q8_0 form, whichever is given).
-template <int SEGS>
+// router logit per workgroup (fn emit_moe_forward's router over the normed
+// row), in double.  The router is RF:
+//   0  float32 rows Wr:           l = sum_t Wr[e][t] * y[t]
+//   1  Q8_0 rows Wrq/Wrs (lane_link.rs fn prim, Moe arm: quantized checkpoint
+//      rows) against the float32 normed row:  l = sum_t (q*s) * y[t]
+//   2  Q8_0 rows against the normed row's Q8_0 form (the one-word int8
+//      numerics, where every reader of the norm is a Q8_0 projection):
+//      l = sum_b (ws*ys) * isum_b, each block's isum exact in int32
+// Every workgroup of a row forms the whole normed row -- it re-reads h, r and
+// w, 24 bytes a value, mostly from cache -- so no workgroup waits for another;
+// the workgroup of expert 0 also writes the sum and the activation the gate-up
+// launch reads (float32 x and/or its Q8_0 form, whichever is given).
+template <int SEGS, int RF>
 __global__ void __launch_bounds__(NORM_THREADS)
     k_norm_logits(const float *__restrict__ h, const float *__restrict__ r, const float *__restrict__ w, int d,
-                  float eps, const float *__restrict__ Wr, int E, float *__restrict__ sum, float *__restrict__ x,
+                  float eps, const float *__restrict__ Wr, const int8_t *__restrict__ Wrq,
+                  const float *__restrict__ Wrs, int E, float *__restrict__ sum, float *__restrict__ x,
                   int8_t *__restrict__ xq, float *__restrict__ xs, double *__restrict__ logits)
 {
     __shared__ double wsum[NORM_THREADS / WAVE];
@@ -98,7 +105,7 @@ __global__ void __launch_bounds__(NORM_THREADS)
     const int64_t row = blockIdx.y;
     const bool writer = e == 0;
     const int t8 = threadIdx.x * 8;
-    const float *wr = Wr + (int64_t)e * d;
+    const int nb = d / QB;
 
     // h, r and w first, then the router row: waits on the vector-memory
     // counter are in issue order, so the norm can start once its (cached)
@@ -107,11 +114,20 @@ __global__ void __launch_bounds__(NORM_THREADS)
     f32x4 rr4[SEGS][2];
     norm_load_raw<SEGS>(n, rr4, h + row * d, r + row * d, w, d, t8);
     f32x4 rv[SEGS][2];
+    uint2 rq[SEGS];
+    float rs[SEGS];
 #pragma unroll
     for (int g = 0; g < SEGS; g++) {
         const int base = min(t8 + g * NORM_SEG, d - 8);  // no branch: see norm_load_raw
-        rv[g][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base));
-        rv[g][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + base + 4));
+        if (RF == 0) {
+            const float *wr = Wr + (int64_t)e * d + base;
+            rv[g][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr));
+            rv[g][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wr + 4));
+        } else {
+            const uint64_t q = __builtin_nontemporal_load(reinterpret_cast<const uint64_t *>(Wrq + (int64_t)e * d + base));
+            rq[g] = make_uint2((uint32_t)q, (uint32_t)(q >> 32));
+            rs[g] = __builtin_nontemporal_load(Wrs + (int64_t)e * nb + base / QB);
+        }
     }
     norm_add<SEGS>(n, rr4, d, t8);
     if (writer) {
@@ -133,18 +149,45 @@ __global__ void __launch_bounds__(NORM_THREADS)
         if (base < d) {
             float v[8];
             norm_values(n.sv[g][0], n.sv[g][1], n.wv[g][0], n.wv[g][1], inv, v);
+            if (RF == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                lg += (double)rv[g][0][i] * (double)v[i];
+                for (int i = 0; i < 4; i++)
+                    lg += (double)rv[g][0][i] * (double)v[i];
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                lg += (double)rv[g][1][i] * (double)v[4 + i];
+                for (int i = 0; i < 4; i++)
+                    lg += (double)rv[g][1][i] * (double)v[4 + i];
+            } else if (RF == 1) {
+                const double s = (double)rs[g];
+#pragma unroll
+                for (int i = 0; i < 8; i++) {
+                    const int q = (int)(int8_t)(((i < 4 ? rq[g].x : rq[g].y) >> (8 * (i & 3))) & 0xFF);
+                    lg += ((double)q * s) * (double)v[i];
+                }
+            }
             if (writer && x) {
                 *reinterpret_cast<f32x4 *>(x + row * d + base) = f32x4{v[0], v[1], v[2], v[3]};
                 *reinterpret_cast<f32x4 *>(x + row * d + base + 4) = f32x4{v[4], v[5], v[6], v[7]};
             }
-            if (writer && xq)
-                quant8_store(v, xq + row * d + base, xs + row * (d / QB) + base / QB, (threadIdx.x & 3) == 0);
+            if (RF == 2 || (writer && xq)) {
+                float ys;
+                const uint2 c = quant8(v, ys);
+                const bool leader = (threadIdx.x & 3) == 0;
+                if (writer && xq) {
+                    *reinterpret_cast<uint2 *>(xq + row * d + base) = c;
+                    if (leader)
+                        xs[row * nb + base / QB] = ys;
+                }
+                if (RF == 2) {
+                    // the block's exact dot: this thread's 8 products, then
+                    // the four threads of the block (integer adds)
+                    int is = __builtin_amdgcn_sdot4((int)c.x, (int)rq[g].x, 0, false);
+                    is = __builtin_amdgcn_sdot4((int)c.y, (int)rq[g].y, is, false);
+                    is += dpp_i<DPP_XOR1>(is);
+                    is += dpp_i<DPP_XOR2>(is);
+                    if (leader)
+                        lg += ((double)rs[g] * (double)ys) * (double)is;
+                }
+            }
         }
     }
     lg = wave_sum_f64(lg);
@@ -195,21 +238,39 @@ hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, in
 
 bool norm_logits_supported(int64_t d) { return d <= NORM_LOGITS_MAX_D; }
 
+namespace {
+
+template <int RF>
+void norm_logits_go(int segs, dim3 grid, hipStream_t st, const float *h, const float *r, const float *w, int d,
+                    float eps, const RouterRows &rt, int E, float *sum, float *x, int8_t *xq, float *xs,
+                    double *logits)
+{
+    const dim3 block(NORM_THREADS);
+    if (segs <= 1)
+        hipLaunchKernelGGL((k_norm_logits<1, RF>), grid, block, 0, st, h, r, w, d, eps, rt.Wr, rt.Wrq, rt.Wrs, E, sum,
+                           x, xq, xs, logits);
+    else if (segs <= 2)
+        hipLaunchKernelGGL((k_norm_logits<2, RF>), grid, block, 0, st, h, r, w, d, eps, rt.Wr, rt.Wrq, rt.Wrs, E, sum,
+                           x, xq, xs, logits);
+    else
+        hipLaunchKernelGGL((k_norm_logits<4, RF>), grid, block, 0, st, h, r, w, d, eps, rt.Wr, rt.Wrq, rt.Wrs, E, sum,
+                           x, xq, xs, logits);
+}
+
+} // namespace
+
 hipError_t norm_logits_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
-                              const float *Wr, int64_t E, float *sum, float *x, int8_t *xq, float *xs, double *logits,
-                              hipStream_t st)
+                              const RouterRows &rt, int64_t E, float *sum, float *x, int8_t *xq, float *xs,
+                              double *logits, hipStream_t st)
 {
     const int segs = (int)((d + NORM_SEG - 1) / NORM_SEG);
-    const dim3 grid((unsigned)E, (unsigned)rows), block(NORM_THREADS);
-    if (segs <= 1)
-        hipLaunchKernelGGL((k_norm_logits<1>), grid, block, 0, st, h, r, w, (int)d, eps, Wr, (int)E, sum, x, xq, xs,
-                           logits);
-    else if (segs <= 2)
-        hipLaunchKernelGGL((k_norm_logits<2>), grid, block, 0, st, h, r, w, (int)d, eps, Wr, (int)E, sum, x, xq, xs,
-                           logits);
+    const dim3 grid((unsigned)E, (unsigned)rows);
+    if (!rt.Wrq)
+        norm_logits_go<0>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits);
+    else if (rt.act == 0)
+        norm_logits_go<1>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits);
     else
-        hipLaunchKernelGGL((k_norm_logits<4>), grid, block, 0, st, h, r, w, (int)d, eps, Wr, (int)E, sum, x, xq, xs,
-                           logits);
+        norm_logits_go<2>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits);
     return hipGetLastError();
 }
 

@@ -80,6 +80,70 @@ __global__ void __launch_bounds__(RT_THREADS) k_logits(const float *__restrict__
     }
 }
 
+// The logits over Q8_0 router rows (lane_link.rs fn prim, Moe arm: a router
+// of quantized checkpoint rows): the same grid, a thread taking one 16-byte
+// chunk (half a block) of the row a pass, so a block's halves sit in
+// neighbouring lanes.
+//   ACT 0: l = sum_t (q*s) * x[t]                       in double
+//   ACT 1: l = sum_b (ws*xs) * isum_b, the block's exact int32 dot joined
+//          from the two lanes' halves, added by the even lane
+template <int ACT, int RT>
+__global__ void __launch_bounds__(RT_THREADS)
+    k_logits_q8(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                const int8_t *__restrict__ Wrq, const float *__restrict__ Wrs, int rows, int d, int E,
+                double *__restrict__ logits)
+{
+    __shared__ double part[RT_WAVES][RT];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int e = blockIdx.x;
+    const int r0 = blockIdx.y * RT;
+    const int nch = d >> 4, nb = d >> 5;
+    const int8_t *wq = Wrq + (int64_t)e * d;
+    const float *ws = Wrs + (int64_t)e * nb;
+
+    double acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; r++)
+        acc[r] = 0.0;
+    // nch is even, so both lanes of a block's pair run the same passes
+    for (int c = threadIdx.x; c < nch; c += RT_THREADS) {
+        const i32x4 wv = ld_stream16(wq + c * 16);
+        const float s = __builtin_nontemporal_load(ws + (c >> 1));
+#pragma unroll
+        for (int r = 0; r < RT; r++) {
+            const int64_t xr = min(r0 + r, rows - 1);
+            if (ACT == 0) {
+                const float *xp = x + xr * d + c * 16;
+#pragma unroll
+                for (int v4 = 0; v4 < 4; v4++) {
+                    const f32x4 b = ldf4(xp + v4 * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int q = (int)(int8_t)((wv[v4] >> (8 * i)) & 0xFF);
+                        acc[r] += ((double)q * (double)s) * (double)b[i];
+                    }
+                }
+            } else {
+                int is = chunk_dot_i8(wv, ld16(xq + xr * d + c * 16));
+                is += dpp_i<DPP_XOR1>(is);
+                if ((lane & 1) == 0)
+                    acc[r] += ((double)s * (double)xs[xr * nb + (c >> 1)]) * (double)is;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; r++) {
+        const double v = wave_sum_f64(acc[r]);
+        if (lane == 0)
+            part[wid][r] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < RT && r0 + (int)threadIdx.x < rows) {
+        const int r = threadIdx.x;
+        logits[(int64_t)(r0 + r) * E + e] = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+    }
+}
+
 __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ logits, int E, int k,
                                                      int32_t *__restrict__ idx, float *__restrict__ wts)
 {
@@ -143,6 +207,17 @@ __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ 
         route_finish(t.kl, t.ch, k, idx + row * k, wts + row * k);
 }
 
+namespace {
+
+hipError_t topk_go(const double *logits, int64_t rows, int64_t E, int64_t k, int32_t *idx, float *wts, hipStream_t st)
+{
+    const size_t big = E > TOPK_LDS_E ? (size_t)E * sizeof(double) : 0;
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(RT_THREADS), big, st, logits, (int)E, (int)k, idx, wts);
+    return hipGetLastError();
+}
+
+} // namespace
+
 hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
                         float *wts, void *scratch, hipStream_t st)
 {
@@ -156,9 +231,32 @@ hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
-    const size_t big = E > TOPK_LDS_E ? (size_t)E * sizeof(double) : 0;
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(RT_THREADS), big, st, logits, (int)E, (int)k, idx, wts);
-    return hipGetLastError();
+    return topk_go(logits, rows, E, k, idx, wts, st);
+}
+
+hipError_t route_q8_launch(const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq, const float *Wrs,
+                           int64_t rows, int64_t d, int64_t E, int64_t k, int act, int32_t *idx, float *wts,
+                           void *scratch, hipStream_t st)
+{
+    double *logits = reinterpret_cast<double *>(scratch);
+    const dim3 block(RT_THREADS);
+    const dim3 g1((unsigned)E, (unsigned)rows), g4((unsigned)E, (unsigned)((rows + 3) / 4));
+    if (act == 0 && rows == 1)
+        hipLaunchKernelGGL((k_logits_q8<0, 1>), g1, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
+                           logits);
+    else if (act == 0)
+        hipLaunchKernelGGL((k_logits_q8<0, 4>), g4, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
+                           logits);
+    else if (rows == 1)
+        hipLaunchKernelGGL((k_logits_q8<1, 1>), g1, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
+                           logits);
+    else
+        hipLaunchKernelGGL((k_logits_q8<1, 4>), g4, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
+                           logits);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    return topk_go(logits, rows, E, k, idx, wts, st);
 }
 
 } // namespace q8s

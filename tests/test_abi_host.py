@@ -208,3 +208,78 @@ def test_norm_gemv_refusals():
     assert norm_gemv(out=None) == -1 and "`out` is null" in _err()
     assert norm_gemv(out=D + 64) == -1 and "overlaps input `Wq`" in _err()
     assert norm_gemv(act=2) == -2
+
+
+def route_q8(act=0, rows=1, d=64, E=4, k=2, x=A, xq=A, xs=B, Wrq=C, Wrs=D, idx=F, wts=G, scratch=0x30000000,
+             sb=None):
+    if sb is None:
+        sb = q8.q8s_scratch_bytes(q8.FN_ROUTE, rows, d, 32, E, k)
+    return LIB.moe_route_topk_q8(x, xq, xs, Wrq, Wrs, rows, d, E, k, idx, wts, act, scratch, sb, None)
+
+
+def test_route_q8_refusals():
+    assert route_q8(k=5) == -1 and "1 <= k <= E" in _err()
+    assert route_q8(d=48) == -1 and "multiple of 32" in _err()
+    assert route_q8(act=2) == -2 and "two-word" in _err()
+    assert route_q8(x=None) == -1 and "`x` is null" in _err()
+    assert route_q8(act=1, xq=None) == -1 and "`xq` is null" in _err()
+    assert route_q8(Wrs=None) == -1 and "`Wrs` is null" in _err()
+    assert route_q8(sb=8) == -4 and "scratch" in _err()
+    assert route_q8(scratch=0x30000010) == -3 and "256-byte" in _err()
+    assert route_q8(idx=C + 32) == -1 and "overlaps input `Wrq`" in _err()
+
+
+def norm_router_q8(act=0, rows=1, d=64, E=4, eps=1e-6, Wrq=D, Wrs=0x34000000, x=G, xq=H, xs=J):
+    return LIB.add_rmsnorm_router_q8(A, B, C, ctypes.c_float(eps), Wrq, Wrs, rows, d, E, F, x, xq, xs, 0x30000000,
+                                     act, None)
+
+
+def test_norm_router_q8_refusals():
+    assert norm_router_q8(act=3) == -2 and "unknown activation" in _err()
+    assert norm_router_q8(Wrq=None) == -1 and "`Wrq` is null" in _err()
+    assert norm_router_q8(Wrs=None) == -1 and "`Wrs` is null" in _err()
+    assert norm_router_q8(d=8192 + 32) == -2
+    assert norm_router_q8(x=None, xq=None, xs=None) == -1 and "neither" in _err()
+    assert norm_router_q8(x=D + 16) == -1 and "overlaps input `Wrq`" in _err()
+
+
+def block_ex(act=0, rows=1, d=64, dff=64, sdff=0, E=4, k=2, eps=1e-6, sb=None, scratch=0x3000000, **over):
+    names = ["h", "r", "w", "Wr", "Wrq", "Wrs", "Wgq", "Wgs", "Wuq", "Wus", "Wdq", "Wds",
+             "Sgq", "Sgs", "Suq", "Sus", "Sdq", "Sds", "sum", "idx", "wts", "out"]
+    p = {n: 0x100000 * (i + 1) for i, n in enumerate(names)}
+    p["Wrq"] = p["Wrs"] = None
+    if sdff == 0:
+        for n in ("Sgq", "Sgs", "Suq", "Sus", "Sdq", "Sds"):
+            p[n] = None
+    p.update(over)
+    if sb is None:
+        sb = q8.q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act)
+    return LIB.moe_ffn_block_ex(p["h"], p["r"], p["w"], ctypes.c_float(eps), p["Wr"], p["Wrq"], p["Wrs"], p["Wgq"],
+                                p["Wgs"], p["Wuq"], p["Wus"], p["Wdq"], p["Wds"], p["Sgq"], p["Sgs"], p["Suq"],
+                                p["Sus"], p["Sdq"], p["Sds"], sdff, rows, d, dff, E, k, p["sum"], p["idx"], p["wts"],
+                                p["out"], act, scratch, sb, None)
+
+
+def test_block_ex_scratch_and_refusals():
+    # no shared expert: the same scratch as moe_ffn_block
+    for act in (0, 1):
+        for rows in (1, 64):
+            assert q8.q8s_block_scratch_bytes(rows, 2048, 768, 0, 128, 8, act) == \
+                q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, 2048, 768, 128, 8, act)
+    # a shared expert's hidden row: f32 values, or their Q8_0 form
+    base = q8.q8s_block_scratch_bytes(1, 2048, 768, 0, 128, 8, 0)
+    assert q8.q8s_block_scratch_bytes(1, 2048, 768, 1024, 128, 8, 0) >= base + 1024 * 4
+    base = q8.q8s_block_scratch_bytes(64, 2048, 768, 0, 128, 8, 1)
+    assert q8.q8s_block_scratch_bytes(64, 2048, 768, 1024, 128, 8, 1) >= base + 64 * 1024 * (1 + 4 / 32)
+    assert q8.q8s_block_scratch_bytes(1, 2048, 768, -32, 128, 8, 0) == 0
+    assert block_ex(Wr=None) == -1 and "exactly one" in _err()
+    assert block_ex(Wrq=0x100000 * 5, Wrs=0x100000 * 6) == -1 and "exactly one" in _err()
+    assert block_ex(Wr=None, Wrq=0x100000 * 5) == -1 and "`Wrs` is null" in _err()
+    assert block_ex(sdff=48) == -1 and "sdff" in _err()
+    assert block_ex(sdff=-32) == -1 and "negative" in _err()
+    assert block_ex(Sgq=0x100000 * 13) == -1 and "sdff = 0" in _err()
+    assert block_ex(sdff=64, Sds=None) == -1 and "`Sds` is null" in _err()
+    assert block_ex(sdff=64, out=0x100000 * 17 + 64) == -1 and "overlaps input `Sdq`" in _err()
+    # a shared expert too wide for the down-combine's partials
+    assert block_ex(d=64, dff=65536, k=32, E=32, sdff=32) == -2 and "512" in _err()
+    assert block_ex(sdff=64, sb=64) == -4 and "scratch" in _err()
