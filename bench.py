@@ -51,6 +51,7 @@ def log(*a):
 DOMINANT = {
     "moe": ("k_route_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
     "chunk": ("k_chunk_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe_chunk.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
+    "moe_shared": ("k_route_gate_up", ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")),
     "norm_gemv": ("k_norm_gemv", ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h",
                                   "q8_gemv_sparse_amd/csrc/q8s_norm_row.h")),
 }
@@ -512,6 +513,111 @@ class ChunkBlock(MoeBlock):
         return el / n, "%d chunks of %d rows, %.1f s" % (n, self.rows, el)
 
 
+class MoeSharedBlock(MoeBlock):
+    """The mixture block with its linked variants: the router as Q8_0 rows
+    and an always-on shared expert, one moe_ffn_block_ex call a step (three
+    launches; the shared expert's tiles ride in the gate-up launch, its slices
+    in the down-combine).  The dominant kernel is that gate-up
+    (moe_topk_gate_up_ex on logits from add_rmsnorm_router_q8)."""
+
+    def __init__(self, name, cfg, act, copies, separate=False):
+        if separate:
+            raise SystemExit("workload %s runs as one moe_ffn_block_ex call a step" % name)
+        super().__init__(name, cfg, act, copies)
+        import synthetic
+        np, torch, q8 = self.np, self.torch, self.q8
+        d, E, sdff = cfg["d"], cfg["E"], cfg["sdff"]
+        self.sdff = sdff
+        rng = np.random.default_rng(3)
+        self.Wrq_h = synthetic.quants(rng, E, d)
+        self.Wrs_h = rng.uniform(2e-4, 5e-4, size=(E, d // 32)).astype(np.float32)
+        S = []
+        for rows_, cols in ((sdff, d), (sdff, d), (d, sdff)):
+            S.extend(synthetic.q8_matrix(rng, rows_, cols))
+        self.S_h = S
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        base = [dev(self.Wrq_h), dev(self.Wrs_h)] + [dev(a) for a in S]
+        self.V = [base] + [[t.clone() for t in base] for _ in range(self.copies - 1)]
+        hw = self.k * self.dff + sdff
+        z = lambda *s_, dt=torch.float32: torch.empty(s_, dtype=dt, device="cuda")
+        self.hf, self.hq, self.hs = z(1, hw), z(1, hw, dt=torch.int8), z(1, hw // 32)
+        a = q8.ACT_INT8 if act == "int8" else q8.ACT_F32
+        self.bscratch = torch.zeros(q8.q8s_block_scratch_bytes(1, d, self.dff, sdff, E, self.k, a),
+                                    dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, c):
+        q8 = self.q8
+        W = self.W[c % self.copies]
+        V = self.V[c % self.copies]
+        i = c % self.pool
+        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        q8.moe_ffn_block_ex(self.h[i], self.r[i], self.w, 1e-6, *W[1:], self.k, self.E, act=a, Wrq=V[0], Wrs=V[1],
+                            shared=tuple(V[2:]), sum=self.sum, idx=self.idx[c % self.copies],
+                            wts=self.wts[c % self.copies], out=self.out, scratch=self.bscratch)
+
+    def prepare_dominant(self):
+        q8 = self.q8
+        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        for c in range(self.copies):
+            i = c % self.pool
+            V = self.V[c]
+            q8.add_rmsnorm_router_q8(self.h[i], self.r[i], self.w, 1e-6, V[0], V[1], act=a, sum=self.sum, x=self.y,
+                                     xq=self.xq, xs=self.xs, logits=self.logits[c])
+        self.torch.cuda.synchronize()
+
+    def launch_dominant(self, c):
+        q8 = self.q8
+        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        W = self.W[c % self.copies]
+        V = self.V[c % self.copies]
+        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+        kw = dict(xq=self.xq, xs=self.xs, hq=self.hq, hs=self.hs, want_h=False) if a == q8.ACT_INT8 else \
+            dict(x=self.y, h=self.hf)
+        q8.moe_topk_gate_up_ex(self.logits[c % self.copies], W[1], W[2], W[3], W[4], self.k, shared=tuple(V[2:6]),
+                               idx=idx, wts=wts, act=a, **kw)
+
+    def _q8(self, n_out, n_in):
+        return n_out * n_in + n_out * (n_in // 32) * 4
+
+    def weight_bytes(self, c=None):
+        d, dff, E, k, sdff = self.d, self.dff, self.E, self.k, self.sdff
+        return self._q8(E, d) + k * 3 * self._q8(dff, d) + 3 * self._q8(sdff, d)
+
+    def dominant_bytes(self, c=None):
+        return 2 * self._q8(self.k * self.dff + self.sdff, self.d)
+
+    def _oracle_step(self, i):
+        import oracle
+        np = self.np
+        m = self.host_w
+        s, y64 = oracle.add_rmsnorm(self.pool_h[i], self.pool_r[i], self.norm_w, 1e-6)
+        x = y64.astype(np.float32)
+        a = 1 if self.act == "int8" else 0
+        return oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a, Wrq=self.Wrq_h,
+                                 Wrs=self.Wrs_h, shared=self.S_h)
+
+    def verify(self):
+        np = self.np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        ridx, rw, rh, ry = self._oracle_step(0)
+        got = self.out.cpu().numpy()
+        err = float(np.max(np.abs(got - ry)) / np.max(np.abs(ry)))
+        same_idx = bool(np.array_equal(self.idx[0].cpu().numpy(), ridx))
+        return {"idx_equal": same_idx, "max_rel_err": err, "tol": 2e-3 if self.act == "int8" else 1e-5}
+
+    def cpu_baseline(self, budget):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            self._oracle_step(n % self.pool)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                break
+        return el / n, "%d steps (rows 1, inputs from the same pool), %.1f s" % (n, el)
+
+
 def make_workload(name, act, copies, separate=False):
     import synthetic
     cfg = synthetic.CONFIGS[name]
@@ -521,6 +627,8 @@ def make_workload(name, act, copies, separate=False):
         return NormGemv(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "chunk":
         return ChunkBlock(name, cfg, copies)
+    if cfg["kind"] == "moe_shared":
+        return MoeSharedBlock(name, cfg, act, copies, separate=separate)
     raise SystemExit("workload %s is a parity case, not a bench workload" % name)
 
 

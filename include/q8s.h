@@ -338,6 +338,37 @@ Q8S_API int moe_ffn_block_ex(const float *h, const float *r, const float *w, flo
                      int64_t dff, int64_t E, int64_t k, float *sum, int32_t *idx, float *wts, float *out,
                      int act, void *scratch, size_t scratch_bytes, void *stream);
 
+/*
+ * moe_topk_gate_up_ex -- moe_topk_gate_up with a shared expert (lane_link.rs
+ * fn class_launch, SharedExpertFusion arm): the same launch also forms the
+ * shared expert's hidden row
+ *   h[r][k*dff + o] = SiLU(Sg[o] . x[r]) * (Su[o] . x[r]),   o < sdff
+ * after the K routed ones, so h (and hq/hs) hold k*dff + sdff values a row.
+ * Sgq/Suq: device int8 [sdff, d]; Sgs/Sus: device f32 [sdff, d/32]; sdff a
+ * multiple of 32, or 0 with the four pointers NULL (then exactly
+ * moe_topk_gate_up).  Other arguments and limits as moe_topk_gate_up; rows
+ * run one by one.
+ */
+Q8S_API int moe_topk_gate_up_ex(const double *logits, const float *x, const int8_t *xq, const float *xs,
+                        const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                        const int8_t *Sgq, const float *Sgs, const int8_t *Suq, const float *Sus,
+                        int64_t sdff, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
+                        int32_t *idx, float *wts, float *h, int8_t *hq, float *hs, int act, void *stream);
+
+/*
+ * moe_down_combine_ex -- moe_down_combine with a shared expert's down row
+ * added, unweighted, after the routed sum (as moe_ffn_block_ex):
+ *   y[r][o] = (sum_{j<K} wts[r][j] * (Wd[e*d + o] . h[r][j])) + Sd[o] . h[r][K]
+ * h (or hq/hs) as moe_topk_gate_up_ex writes it: k*dff + sdff values a row.
+ * Sdq: device int8 [d, sdff]; Sds: device f32 [d, sdff/32]; sdff 0 with both
+ * NULL: no shared expert.  Rows run one by one (no scratch); other arguments
+ * and limits as moe_down_combine.
+ */
+Q8S_API int moe_down_combine_ex(const float *h, const int8_t *hq, const float *hs,
+                        const int8_t *Wdq, const float *Wds, const int8_t *Sdq, const float *Sds,
+                        int64_t sdff, const int32_t *idx, const float *wts, int64_t rows, int64_t d,
+                        int64_t dff, int64_t E, int64_t k, float *y, int act, void *stream);
+
 /* Bytes of scratch moe_ffn_block_ex needs for these sizes (0 for invalid). */
 Q8S_API size_t q8s_block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k,
                                int act);

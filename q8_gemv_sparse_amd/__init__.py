@@ -22,6 +22,7 @@ __all__ = [
     "q8_gemv", "q8_quantize_rows", "add_rmsnorm_q8", "moe_route_topk",
     "moe_gate_up", "moe_down_combine", "moe_ffn_block", "add_rmsnorm_router", "moe_topk_gate_up",
     "add_rmsnorm_gemv", "moe_route_topk_q8", "add_rmsnorm_router_q8", "moe_ffn_block_ex",
+    "moe_topk_gate_up_ex", "moe_down_combine_ex",
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "library",
 ]
@@ -61,6 +62,8 @@ _SIGS = {
                               ctypes.c_int, _p],
     "moe_ffn_block_ex": [_p, _p, _p, ctypes.c_float] + [_p] * 15 + [_i64] * 6 + [_p] * 4 + [ctypes.c_int, _p, _sz,
                                                                                            _p],
+    "moe_topk_gate_up_ex": [_p] * 12 + [_i64] * 6 + [_p] * 5 + [ctypes.c_int, _p],
+    "moe_down_combine_ex": [_p] * 7 + [_i64, _p, _p] + [_i64] * 5 + [_p, ctypes.c_int, _p],
     "q8s_scratch_bytes": [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
     "q8s_block_scratch_bytes": [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
 }
@@ -470,3 +473,64 @@ def moe_ffn_block_ex(h, r, w, eps, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, E, act=ACT_F
                                  rows, d, dff, E, k, _ptr(sum), _ptr(idx), _ptr(wts), _ptr(out), act, _ptr(scratch),
                                  scratch.numel(), _stream(stream)))
     return sum, idx, wts, out
+
+
+def _shared4(shared, names):
+    if shared is None:
+        return [None] * len(names), 0
+    for t, n in zip(shared, names):
+        _dev(t, torch.int8 if n.endswith("q") else torch.float32, n)
+    return list(shared), shared[0].shape[0] if names[0] != "Sdq" else shared[0].shape[1]
+
+
+def moe_topk_gate_up_ex(logits, Wgq, Wgs, Wuq, Wus, k, shared=None, x=None, xq=None, xs=None, idx=None, wts=None,
+                        h=None, hq=None, hs=None, act=ACT_F32, want_h=True, stream=None):
+    """moe_topk_gate_up with a shared expert's gate and up, ``shared`` =
+    (Sgq, Sgs, Suq, Sus): the hidden rows hold k*dff + sdff values.  Returns
+    (idx, wts, h or None, hq or None, hs or None)."""
+    _dev(logits, torch.float64, "logits")
+    for t, n in ((Wgs, "Wgs"), (Wus, "Wus"), (x, "x"), (xs, "xs")):
+        _dev(t, torch.float32, n)
+    for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq"), (xq, "xq")):
+        _dev(t, torch.int8, n)
+    sh, sdff = _shared4(shared, ("Sgq", "Sgs", "Suq", "Sus"))
+    rows, E = logits.shape
+    d = Wgq.shape[1]
+    dff = Wgq.shape[0] // E
+    dev = logits.device
+    hw = k * dff + sdff
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    if wts is None:
+        wts = torch.empty((rows, k), dtype=torch.float32, device=dev)
+    if (act == ACT_F32 or want_h) and h is None:
+        h = torch.empty((rows, hw), dtype=torch.float32, device=dev)
+    if act == ACT_INT8 and hq is None:
+        hq = torch.empty((rows, hw), dtype=torch.int8, device=dev)
+        hs = torch.empty((rows, hw // 32), dtype=torch.float32, device=dev)
+    for t, dt, n in ((idx, torch.int32, "idx"), (wts, torch.float32, "wts"), (h, torch.float32, "h"),
+                     (hq, torch.int8, "hq"), (hs, torch.float32, "hs")):
+        _dev(t, dt, n)
+    _check(_lib.moe_topk_gate_up_ex(_ptr(logits), _ptr(x), _ptr(xq), _ptr(xs), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq),
+                                    _ptr(Wus), *[_ptr(t) for t in sh], sdff, rows, d, dff, E, k, _ptr(idx),
+                                    _ptr(wts), _ptr(h), _ptr(hq), _ptr(hs), act, _stream(stream)))
+    return idx, wts, h, hq, hs
+
+
+def moe_down_combine_ex(Wdq, Wds, idx, wts, E, shared=None, h=None, hq=None, hs=None, y=None, act=ACT_F32,
+                        stream=None):
+    """moe_down_combine with a shared expert's down row added, ``shared`` =
+    (Sdq, Sds); h (or hq/hs) hold k*dff + sdff values a row.  Returns y."""
+    _dev(Wdq, torch.int8, "Wdq"); _dev(Wds, torch.float32, "Wds")
+    _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
+    _dev(h, torch.float32, "h"); _dev(hq, torch.int8, "hq"); _dev(hs, torch.float32, "hs")
+    sh, sdff = _shared4(shared, ("Sdq", "Sds"))
+    rows, k = idx.shape
+    dff = Wdq.shape[1]
+    d = Wdq.shape[0] // E
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=Wdq.device)
+    _dev(y, torch.float32, "y")
+    _check(_lib.moe_down_combine_ex(_ptr(h), _ptr(hq), _ptr(hs), _ptr(Wdq), _ptr(Wds), *[_ptr(t) for t in sh], sdff,
+                                    _ptr(idx), _ptr(wts), rows, d, dff, E, k, _ptr(y), act, _stream(stream)))
+    return y

@@ -9,6 +9,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -501,22 +502,54 @@ int add_rmsnorm_router_q8(const float *h, const float *r, const float *w, float 
                               logits, stream);
 }
 
-int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq,
-                     const float *Wgs, const int8_t *Wuq, const float *Wus, int64_t rows, int64_t d, int64_t dff,
-                     int64_t E, int64_t k, int32_t *idx, float *wts, float *h, int8_t *hq, float *hs, int act,
-                     void *stream)
+namespace {
+
+// The shared expert's arguments of a stage call: none (sdff 0, NULL
+// matrices) or sdff a multiple of 32 fitting the down-combine's partials.
+int check_shared(const char *fn, int64_t sdff, int64_t dff, int64_t k, std::initializer_list<const void *> mats)
 {
-    const char *fn = "moe_topk_gate_up";
     int rc;
-    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+    if (sdff < 0)
+        return fail(Q8S_EINVAL, "%s: sdff = %lld is negative", fn, (long long)sdff);
+    if (sdff == 0) {
+        for (const void *p : mats)
+            if (p)
+                return fail(Q8S_EINVAL, "%s: shared-expert matrices given with sdff = 0", fn);
+        return 0;
+    }
+    if ((rc = check_dim32(fn, "sdff", sdff)))
+        return rc;
+    if (!q8s::shared_fits(dff, sdff, k))
+        return fail(Q8S_EUNSUPPORTED, "%s: a shared expert of sdff = %lld next to k = %lld experts of dff = %lld "
+                    "exceeds the down-combine's 512 (slot, slice) partials", fn, (long long)sdff, (long long)k,
+                    (long long)dff);
+    return 0;
+}
+
+int topk_gate_up_common(const char *fn, const double *logits, const float *x, const int8_t *xq, const float *xs,
+                        const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Sgq,
+                        const float *Sgs, const int8_t *Suq, const float *Sus, int64_t sdff, int64_t rows, int64_t d,
+                        int64_t dff, int64_t E, int64_t k, int32_t *idx, float *wts, float *h, int8_t *hq, float *hs,
+                        int act, void *stream)
+{
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)) ||
+        (rc = check_shared(fn, sdff, dff, k, {Sgq, Sgs, Suq, Sus})))
         return rc;
     if (E > q8s::ROUTE_FUSED_MAX_E)
         return fail(Q8S_EUNSUPPORTED, "%s: E = %lld experts exceed the %d a gate-up workgroup ranks itself; use "
                     "moe_route_topk then moe_gate_up", fn, (long long)E, q8s::ROUTE_FUSED_MAX_E);
     const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
-    const size_t nh = (size_t)(rows * k * dff);
+    const size_t nh = (size_t)(rows * (k * dff + sdff));
     std::vector<Span> ins = {{logits, (size_t)(rows * E) * 8, "logits"}, {Wgq, wq, "Wgq"}, {Wgs, wsb, "Wgs"},
                              {Wuq, wq, "Wuq"}, {Wus, wsb, "Wus"}};
+    if (sdff > 0) {
+        const size_t sq = (size_t)sdff * (size_t)d, ss = (size_t)sdff * (size_t)(d / 32) * 4;
+        ins.push_back({Sgq, sq, "Sgq"});
+        ins.push_back({Sgs, ss, "Sgs"});
+        ins.push_back({Suq, sq, "Suq"});
+        ins.push_back({Sus, ss, "Sus"});
+    }
     std::vector<Span> outs = {{idx, (size_t)(rows * k) * 4, "idx"}, {wts, (size_t)(rows * k) * 4, "wts"}};
     if (act == Q8S_ACT_F32) {
         ins.push_back({x, (size_t)(rows * d) * 4, "x"});
@@ -539,6 +572,11 @@ int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, con
     a.Wgs = Wgs;
     a.Wuq = Wuq;
     a.Wus = Wus;
+    a.Sgq = Sgq;
+    a.Sgs = Sgs;
+    a.Suq = Suq;
+    a.Sus = Sus;
+    a.sdff = sdff;
     a.rows = rows;
     a.d = d;
     a.dff = dff;
@@ -555,6 +593,76 @@ int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, con
     return launched(q8s::route_gate_up_launch(a, as_stream(stream)), fn);
 }
 
+} // namespace
+
+int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq,
+                     const float *Wgs, const int8_t *Wuq, const float *Wus, int64_t rows, int64_t d, int64_t dff,
+                     int64_t E, int64_t k, int32_t *idx, float *wts, float *h, int8_t *hq, float *hs, int act,
+                     void *stream)
+{
+    return topk_gate_up_common("moe_topk_gate_up", logits, x, xq, xs, Wgq, Wgs, Wuq, Wus, nullptr, nullptr, nullptr,
+                               nullptr, 0, rows, d, dff, E, k, idx, wts, h, hq, hs, act, stream);
+}
+
+int moe_topk_gate_up_ex(const double *logits, const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq,
+                        const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Sgq, const float *Sgs,
+                        const int8_t *Suq, const float *Sus, int64_t sdff, int64_t rows, int64_t d, int64_t dff,
+                        int64_t E, int64_t k, int32_t *idx, float *wts, float *h, int8_t *hq, float *hs, int act,
+                        void *stream)
+{
+    return topk_gate_up_common("moe_topk_gate_up_ex", logits, x, xq, xs, Wgq, Wgs, Wuq, Wus, Sgq, Sgs, Suq, Sus, sdff,
+                               rows, d, dff, E, k, idx, wts, h, hq, hs, act, stream);
+}
+
+int moe_down_combine_ex(const float *h, const int8_t *hq, const float *hs, const int8_t *Wdq, const float *Wds,
+                        const int8_t *Sdq, const float *Sds, int64_t sdff, const int32_t *idx, const float *wts,
+                        int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, float *y, int act, void *stream)
+{
+    const char *fn = "moe_down_combine_ex";
+    int rc;
+    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)) ||
+        (rc = check_shared(fn, sdff, dff, k, {Sdq, Sds})))
+        return rc;
+    const size_t nh = (size_t)(rows * (k * dff + sdff));
+    std::vector<Span> ins = {{Wdq, (size_t)(E * d) * (size_t)dff, "Wdq"},
+                             {Wds, (size_t)(E * d) * (size_t)(dff / 32) * 4, "Wds"},
+                             {idx, (size_t)(rows * k) * 4, "idx"},
+                             {wts, (size_t)(rows * k) * 4, "wts"}};
+    if (sdff > 0) {
+        ins.push_back({Sdq, (size_t)d * (size_t)sdff, "Sdq"});
+        ins.push_back({Sds, (size_t)d * (size_t)(sdff / 32) * 4, "Sds"});
+    }
+    if (act == Q8S_ACT_F32) {
+        ins.push_back({h, nh * 4, "h"});
+    } else {
+        ins.push_back({hq, nh, "hq"});
+        ins.push_back({hs, nh / 32 * 4, "hs"});
+    }
+    std::vector<Span> outs = {{y, (size_t)(rows * d) * 4, "y"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::MoeArgs a{};
+    a.h = act == 0 ? const_cast<float *>(h) : nullptr;
+    a.hq = act == 1 ? const_cast<int8_t *>(hq) : nullptr;
+    a.hs = act == 1 ? const_cast<float *>(hs) : nullptr;
+    a.Wdq = Wdq;
+    a.Wds = Wds;
+    a.Sdq = Sdq;
+    a.Sds = Sds;
+    a.sdff = sdff;
+    a.idx = idx;
+    a.wts = wts;
+    a.rows = rows;
+    a.d = d;
+    a.dff = dff;
+    a.E = E;
+    a.k = k;
+    a.y = y;
+    a.act = act;
+    clear_stale();
+    return launched(q8s::row_down_launch(a, as_stream(stream)), fn);
+}
+
 namespace {
 
 int block_common(const char *fn, const float *h, const float *r, const float *w, float eps,
@@ -569,18 +677,8 @@ int block_common(const char *fn, const float *h, const float *r, const float *w,
         return rc;
     if (!(eps >= 0.0f) || eps != eps)
         return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
-    if (sdff < 0)
-        return fail(Q8S_EINVAL, "%s: sdff = %lld is negative", fn, (long long)sdff);
-    if (sdff > 0) {
-        if ((rc = check_dim32(fn, "sdff", sdff)))
-            return rc;
-        if (!q8s::shared_fits(dff, sdff, k))
-            return fail(Q8S_EUNSUPPORTED, "%s: a shared expert of sdff = %lld next to k = %lld experts of dff = %lld "
-                        "exceeds the down-combine's 512 (slot, slice) partials", fn, (long long)sdff, (long long)k,
-                        (long long)dff);
-    } else if (Sgq || Sgs || Suq || Sus || Sdq || Sds) {
-        return fail(Q8S_EINVAL, "%s: shared-expert matrices given with sdff = 0", fn);
-    }
+    if ((rc = check_shared(fn, sdff, dff, k, {Sgq, Sgs, Suq, Sus, Sdq, Sds})))
+        return rc;
     const size_t n = (size_t)(rows * d);
     const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
     std::vector<Span> ins = {{h, n * 4, "h"},

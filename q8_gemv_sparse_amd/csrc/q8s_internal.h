@@ -153,6 +153,8 @@ bool shared_fits(int64_t dff, int64_t sdff, int64_t k);
 // the shared expert alone, per row (gate-up, then a down-combine that adds
 // into y): a chunk's grouped kernels carry no shared expert
 hipError_t shared_launch(const MoeArgs &a, hipStream_t st);
+// the down-combine row by row (the decode kernel for any rows: no grouping)
+hipError_t row_down_launch(const MoeArgs &a, hipStream_t st);
 
 // a chunk's mixture (rows > 1, int8 activations): choices grouped by expert,
 // for d <= 2048 and dff <= 4096 (one slice of a wave each)

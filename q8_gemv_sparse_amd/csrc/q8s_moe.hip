@@ -179,16 +179,18 @@ struct GuTile {
     int j, o0;
     bool shared;
 };
+template <bool SH>
 Q8S_DEV GuTile gu_tile(int bx, int k, int tpe, int T)
 {
-    if (bx < k * tpe)
+    if (!SH || bx < k * tpe)
         return {bx / tpe, (bx % tpe) * T, false};
     return {k, (bx - k * tpe) * T, true};
 }
 
 // gate-up with the choices given: one workgroup per tile of one (row, slot),
-// grid (k*dff/T + sdff/T, rows).
-template <int ACT, int LPR, int C>
+// grid (k*dff/T + sdff/T, rows).  SH: with a shared expert (a kernel of its
+// own, so the mixture without one runs the plain code).
+template <int ACT, int LPR, int C, bool SH>
 __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
               const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
@@ -198,8 +200,8 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     constexpr int T = GuShape<ACT, LPR, C>::T;
     __shared__ GuLds<T> sm;
     const int64_t row = blockIdx.y;
-    const GuTile t = gu_tile(blockIdx.x, k, dff / T, T);
-    const int64_t hbase = row * ((int64_t)k * dff + sw.sdff) + (int64_t)t.j * dff + t.o0;
+    const GuTile t = gu_tile<SH>(blockIdx.x, k, dff / T, T);
+    const int64_t hbase = row * ((int64_t)k * dff + (SH ? sw.sdff : 0)) + (int64_t)t.j * dff + t.o0;
     const int e = t.shared ? 0 : idx[row * k + t.j];
     const bool valid = t.shared || (e >= 0 && e < E);
     const int64_t rbase = t.shared ? t.o0 : (int64_t)(valid ? e : 0) * dff + t.o0;
@@ -213,7 +215,7 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
 // reads its expert from the result, so the choices need no launch of their
 // own; the workgroup of tile 0, slot 0 writes the row's idx and wts for the
 // down-combine launch.  The shared expert's workgroups need no ranking.
-template <int ACT, int LPR, int C>
+template <int ACT, int LPR, int C, bool SH>
 __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     k_route_gate_up(const double *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ wts,
                     const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
@@ -226,8 +228,8 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     __shared__ GuLds<T> sm;
     __shared__ TopkLds tk;
     const int64_t row = blockIdx.y;
-    const GuTile t = gu_tile(blockIdx.x, k, dff / T, T);
-    const int64_t hbase = row * ((int64_t)k * dff + sw.sdff) + (int64_t)t.j * dff + t.o0;
+    const GuTile t = gu_tile<SH>(blockIdx.x, k, dff / T, T);
+    const int64_t hbase = row * ((int64_t)k * dff + (SH ? sw.sdff : 0)) + (int64_t)t.j * dff + t.o0;
     if (t.shared) {
         gate_up_tile<ACT, LPR, C>(sm, true, row, t.o0, hbase, x, xq, xs, sw.gq, sw.gs, sw.uq, sw.us, d, ks, h, hq,
                                   hs);
@@ -259,14 +261,16 @@ constexpr int dn_unroll()
 
 // Waves take (slot, slice) pairs: pairs j*ks + s for the K slots, then
 // k*ks + s for the shared expert's kss slices of its sdff-long rows (the same
-// lane shape).  The grid is (d / DN_TILE, rows); acc_out adds the result to y.
-template <int ACT, int LPR, int C>
+// lane shape).  The grid is (d / DN_TILE, rows); with y_add (then y itself)
+// the result is added to what y holds.  SH: with a shared expert (a kernel of
+// its own, so the mixture without one runs the plain code).
+template <int ACT, int LPR, int C, bool SH>
 __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__restrict__ h, const int8_t *__restrict__ hq,
                                                               const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
                                                               const float *__restrict__ Wds, SharedW sw,
                                                               const int32_t *__restrict__ idx,
                                                               const float *__restrict__ wts, int d, int dff, int E, int k,
-                                                              int ks, int kss, int acc_out, float *__restrict__ y)
+                                                              int ks, int kss, const float *y_add, float *y)
 {
     constexpr int G = WAVE / LPR;
     constexpr int U = dn_unroll<ACT, LPR, C>();
@@ -280,11 +284,11 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
     const int nwaves = blockDim.x >> 6;
     const int o0 = blockIdx.x * DN_TILE;
     const int64_t row = blockIdx.y;
-    const int64_t hw = (int64_t)k * dff + sw.sdff;
-    const int rp = k * ks, pairs = rp + kss;
+    const int64_t hw = (int64_t)k * dff + (SH ? sw.sdff : 0);
+    const int rp = k * ks, pairs = rp + (SH ? kss : 0);
 
     for (int p = wid; p < pairs; p += nwaves) {
-        const bool sh = p >= rp;
+        const bool sh = SH && p >= rp;
         const int j = sh ? k : p / ks, s = sh ? p - rp : p % ks;
         const int e = sh ? 0 : idx[row * k + j];
         const bool valid = sh || (e >= 0 && e < E);
@@ -340,14 +344,16 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
                 dj += part[j * ks + s][t];
             acc = __builtin_fmaf(wts[row * k + j], dj, acc);
         }
-        if (kss > 0) {
+        if (SH && kss > 0) {
             float ds = 0.0f;
             for (int s = 0; s < kss; s++)
                 ds += part[rp + s][t];
             acc += ds;
         }
-        float *yo = y + row * d + o0 + t;
-        *yo = acc_out ? *yo + acc : acc;
+        // a branch, not a select: the load of y happens only when asked for
+        if (SH && y_add)
+            acc = y_add[row * d + o0 + t] + acc;
+        y[row * d + o0 + t] = acc;
     }
 }
 
@@ -366,9 +372,14 @@ hipError_t gu_go(const MoeArgs &a, int ks, hipStream_t st)
 {
     using S = GuShape<ACT, LPR, C>;
     dim3 grid((unsigned)((a.k * a.dff + a.sdff) / S::T), (unsigned)a.rows);
-    hipLaunchKernelGGL((k_gate_up<ACT, LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq, a.Wgs,
-                       a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h, a.hq,
-                       a.hs);
+    if (a.sdff)
+        hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, true>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
+                           a.Wgs, a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
+                           a.hq, a.hs);
+    else
+        hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, false>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
+                           a.Wgs, a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
+                           a.hq, a.hs);
     return hipGetLastError();
 }
 
@@ -378,9 +389,14 @@ hipError_t rgu_go(const MoeArgs &a, int ks, hipStream_t st)
     using S = GuShape<ACT, LPR, C>;
     static_assert(S::NW * WAVE >= ROUTE_FUSED_MAX_E, "one thread per logit at least");
     dim3 grid((unsigned)((a.k * a.dff + a.sdff) / S::T), (unsigned)a.rows);
-    hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w, a.wts_w,
-                       a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff, (int)a.E,
-                       (int)a.k, ks, a.h, a.hq, a.hs);
+    if (a.sdff)
+        hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, true>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
+                           a.wts_w, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff,
+                           (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
+    else
+        hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, false>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
+                           a.wts_w, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff,
+                           (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
     return hipGetLastError();
 }
 
@@ -394,8 +410,14 @@ hipError_t dn_go(const MoeArgs &a, int ks, hipStream_t st)
     const int pairs = (int)a.k * ks + kss;
     const int nw = std::min(DN_MAX_WAVES, pairs);
     dim3 grid((unsigned)(a.d / DN_TILE), (unsigned)a.rows);
-    hipLaunchKernelGGL((k_down<ACT, LPR, C>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds, shared_w(a),
-                       a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss, a.acc_out ? 1 : 0, a.y);
+    if (a.sdff)
+        hipLaunchKernelGGL((k_down<ACT, LPR, C, true>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds,
+                           shared_w(a), a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss,
+                           a.acc_out ? a.y : nullptr, a.y);
+    else
+        hipLaunchKernelGGL((k_down<ACT, LPR, C, false>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds,
+                           shared_w(a), a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss, nullptr,
+                           a.y);
     return hipGetLastError();
 }
 
@@ -482,6 +504,11 @@ hipError_t down_launch(const MoeArgs &a, hipStream_t st)
 {
     if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
         return chunk_down_launch(a, st);
+    return a.act == 0 ? by_shape<0, DN>(a, a.dff, st) : by_shape<1, DN>(a, a.dff, st);
+}
+
+hipError_t row_down_launch(const MoeArgs &a, hipStream_t st)
+{
     return a.act == 0 ? by_shape<0, DN>(a, a.dff, st) : by_shape<1, DN>(a, a.dff, st);
 }
 

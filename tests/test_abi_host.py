@@ -283,3 +283,26 @@ def test_block_ex_scratch_and_refusals():
     # a shared expert too wide for the down-combine's partials
     assert block_ex(d=64, dff=65536, k=32, E=32, sdff=32) == -2 and "512" in _err()
     assert block_ex(sdff=64, sb=64) == -4 and "scratch" in _err()
+
+
+def test_shared_stage_refusals():
+    # moe_topk_gate_up_ex: logits x xq xs Wgq Wgs Wuq Wus Sgq Sgs Suq Sus sdff rows d dff E k idx wts h hq hs act
+    def gu(sdff=64, Sgq=0x31000000, act=0, h=J, **kw):
+        a = dict(rows=1, d=64, dff=64, E=4, k=2)
+        a.update(kw)
+        return LIB.moe_topk_gate_up_ex(A, B, B, C, D, F, G, 0x30000000, Sgq, 0x32000000, 0x33000000, 0x34000000,
+                                       sdff, a["rows"], a["d"], a["dff"], a["E"], a["k"], 0x38000000, 0x3C000000,
+                                       h, H, 0xF0000000, act, None)
+    assert gu(sdff=40) == -1 and "sdff" in _err()
+    assert gu(sdff=0) == -1 and "sdff = 0" in _err()
+    assert gu(Sgq=None) == -1 and "`Sgq` is null" in _err()
+    assert gu(E=257) == -2 and "moe_route_topk then moe_gate_up" in _err()
+    assert gu(h=0x33000000 + 64) == -1 and "overlaps input `Suq`" in _err()
+    # moe_down_combine_ex: h hq hs Wdq Wds Sdq Sds sdff idx wts rows d dff E k y act
+    def dn(sdff=64, Sdq=0x31000000, y=G, act=0):
+        return LIB.moe_down_combine_ex(A, None, None, B, C, Sdq, 0x32000000, sdff, D, F, 1, 64, 64, 4, 2, y, act,
+                                       None)
+    assert dn(sdff=-32) == -1 and "negative" in _err()
+    assert dn(Sdq=None) == -1 and "`Sdq` is null" in _err()
+    assert dn(y=0x31000000) == -1 and "overlaps input `Sdq`" in _err()
+    assert dn(act=1) == -1 and "`hq` is null" in _err()

@@ -223,3 +223,31 @@ def test_block_ex_scratch_reuse_and_determinism():
     for a, c in zip(first, again):
         assert np.array_equal(a, c)
     check_ex(one, 1, True, True, again)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_block_ex_equals_its_stage_calls(act):
+    # moe_ffn_block_ex's three launches are add_rmsnorm_router_q8,
+    # moe_topk_gate_up_ex and moe_down_combine_ex: the same values, bit for bit
+    banner("moe_ffn_block_ex vs stage calls act=%d" % act)
+    d, dff, sdff, E, k = 2048, 768, 1024, 128, 8
+    v = synthetic.variant_inputs(40, d, dff, E, k, 1, sdff)
+    b, m = v.block, v.block.moe
+    Wgq, Wgs, Wuq, Wus, Wdq, Wds = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds))
+    Sgq, Sgs, Suq, Sus, Sdq, Sds = (dev(a) for a in (v.Sgq, v.Sgs, v.Suq, v.Sus, v.Sdq, v.Sds))
+    Wrq, Wrs = dev(v.Wrq), dev(v.Wrs)
+    s, x, xq, xs, logits = q8.add_rmsnorm_router_q8(dev(b.h), dev(b.r), dev(b.w), EPS, Wrq, Wrs, act=act)
+    kw = dict(x=x) if act == 0 else dict(xq=xq, xs=xs, want_h=False)
+    idx, wts, h, hq, hs = q8.moe_topk_gate_up_ex(logits, Wgq, Wgs, Wuq, Wus, k, shared=(Sgq, Sgs, Suq, Sus),
+                                                 act=act, **kw)
+    y = q8.moe_down_combine_ex(Wdq, Wds, idx, wts, E, shared=(Sdq, Sds), h=h, hq=hq, hs=hs, act=act)
+    bs, bidx, bw, bout = q8.moe_ffn_block_ex(dev(b.h), dev(b.r), dev(b.w), EPS, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, E,
+                                             act=act, Wrq=Wrq, Wrs=Wrs, shared=(Sgq, Sgs, Suq, Sus, Sdq, Sds))
+    for a, c in ((s, bs), (idx, bidx), (wts, bw), (y, bout)):
+        assert torch.equal(a, c)
+    # the stage calls without a shared expert are the plain ones
+    i2, w2, h2, _, _ = q8.moe_topk_gate_up(logits, Wgq, Wgs, Wuq, Wus, k, x=x, act=0)
+    i3, w3, h3, _, _ = q8.moe_topk_gate_up_ex(logits, Wgq, Wgs, Wuq, Wus, k, x=x, act=0)
+    assert torch.equal(i2, i3) and torch.equal(w2, w3) and torch.equal(h2.reshape(h3.shape), h3)
+    assert torch.equal(q8.moe_down_combine(Wdq, Wds, i2, w2, E, h=h2, act=0),
+                       q8.moe_down_combine_ex(Wdq, Wds, i2, w2, E, h=h2, act=0))
