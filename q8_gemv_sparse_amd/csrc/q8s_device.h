@@ -264,6 +264,23 @@ Q8S_DEV void load_x(XSlice<1, C> &x, const float *, const int8_t *__restrict__ x
     }
 }
 
+// load_x for Q8_0 activations without branches: chunks past the slice read
+// its last chunk and are zeroed by a select.
+template <int LPR, int C>
+Q8S_DEV void load_x_flat(XSlice<1, C> &x, const int8_t *__restrict__ xq, const float *__restrict__ xs, int ch0,
+                         int nch, int lig)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        const int ch = c * LPR + lig;
+        const int cc = min(ch, nch - 1);
+        const i32x4 q = ld16(xq + (int64_t)(ch0 + cc) * 16);
+        const float sc = xs[(ch0 + cc) >> 1];
+        x.q[c] = ch < nch ? q : i32x4{0, 0, 0, 0};
+        x.s[c] = ch < nch ? sc : 0.0f;
+    }
+}
+
 // Quantising an f32 activation slice on the spot, in two halves so the loads
 // can be issued before other traffic (waits on the vector-memory counter are
 // in issue order: a load issued after the weight rows could only be used once

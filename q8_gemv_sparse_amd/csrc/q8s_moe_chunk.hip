@@ -34,47 +34,65 @@ namespace q8s {
 namespace {
 
 constexpr int CK_PASS = 64;  // choices of one expert per pass
+constexpr int CK_GB = 8;     // idx words a lane holds: a scan step covers CK_GB * 64 choices
 
-// Wave 0 gathers the workgroup's pass of the stable list of choices c
-// (increasing c) whose expert is e (for e == E: whose expert is invalid):
-// entries with ordinal in [first, first + CK_PASS) go to list[]; *n gets
-// their count and *total the count of all such choices.  Ends with a
-// workgroup barrier.
-Q8S_DEV void gather_choices(const int32_t *__restrict__ idx, int nchoice, int e, int E, int first, int *list, int *n,
-                            int *total)
+// A wave's copy of idx[c0, c0 + CK_GB*64): straight-line loads (past the end
+// reads the last choice and is marked `E`, which matches no bucket below E).
+struct IdxBatch {
+    int ec[CK_GB];
+};
+
+Q8S_DEV void idx_load(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice, int c0, int E, int lane)
 {
-    constexpr int B = 8;  // idx loads in flight per lane
-    if (threadIdx.x < WAVE) {
-        const int lane = threadIdx.x;
-        int base = 0;
-        for (int c0 = 0; c0 < nchoice; c0 += WAVE * B) {
-            int ec[B];
 #pragma unroll
-            for (int b = 0; b < B; b++) {
-                const int c = c0 + b * WAVE + lane;
-                ec[b] = c < nchoice ? idx[c] : E;  // E: matches no bucket below E, and only the
-            }                                      // invalid bucket, which checks c < nchoice
-#pragma unroll
-            for (int b = 0; b < B; b++) {
-                const int c = c0 + b * WAVE + lane;
-                const bool hit = c < nchoice && ((e < E) ? (ec[b] == e) : (ec[b] < 0 || ec[b] >= E));
-                const uint64_t mask = __ballot(hit);
-                const int ord = base + __popcll(mask & ((1ull << lane) - 1ull));
-                if (hit && ord >= first && ord < first + CK_PASS)
-                    list[ord - first] = c;
-                base += __popcll(mask);
-            }
-        }
-        if (lane == 0) {
-            *n = min(CK_PASS, max(0, base - first));
-            *total = base;
-        }
+    for (int i = 0; i < CK_GB; i++) {
+        const int c = c0 + i * WAVE + lane;
+        const int v = idx[min(c, nchoice - 1)];
+        b.ec[i] = c < nchoice ? v : E;
     }
-    __syncthreads();
+}
+
+// The stable list of choices c (increasing c) whose expert is e (for e == E:
+// whose expert is invalid), scanned a batch at a time by one wave: entries
+// with ordinal in [first, first + CK_PASS) go to list[] (the wave's own LDS
+// row; a wave's LDS operations complete in order, so no barrier is needed);
+// returns the running count of such choices.
+Q8S_DEV int idx_scan(const IdxBatch &b, int c0, int nchoice, int e, int E, int first, int base, int *list, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < CK_GB; i++) {
+        const int c = c0 + i * WAVE + lane;
+        const int v = b.ec[i];
+        const bool hit = c < nchoice && ((e < E) ? (v == e) : (v < 0 || v >= E));
+        const uint64_t mask = __ballot(hit);
+        const int ord = base + __popcll(mask & ((1ull << lane) - 1ull));
+        if (hit && ord >= first && ord < first + CK_PASS)
+            list[ord - first] = c;
+        base += __popcll(mask);
+    }
+    return base;
+}
+
+// The whole scan for the pass starting at ordinal `first`, the first batch
+// already loaded in b.
+Q8S_DEV int idx_gather(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice, int e, int E, int first, int *list,
+                       int lane)
+{
+    int base = idx_scan(b, 0, nchoice, e, E, first, 0, list, lane);
+    for (int c0 = CK_GB * WAVE; c0 < nchoice; c0 += CK_GB * WAVE) {
+        idx_load(b, idx, nchoice, c0, E, lane);
+        base = idx_scan(b, c0, nchoice, e, E, first, base, list, lane);
+    }
+    return base;
 }
 
 } // namespace
 
+// Every wave works on its own: it gathers the expert's choices itself, holds
+// its own weight rows, and writes its own outputs, so no wave of a workgroup
+// waits for another.  The first idx batch is requested before the weight
+// rows, so the scan waits for it alone (waits on the vector-memory counter
+// are in issue order).
 template <int LPR, int C>
 __global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
     k_chunk_gate_up(const int8_t *__restrict__ xq, const float *__restrict__ xs, const int8_t *__restrict__ Wgq,
@@ -82,58 +100,53 @@ __global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
                     const int32_t *__restrict__ idx, int nchoice, int k, int d, int dff, int E, float *__restrict__ h)
 {
     using S = ChunkGuShape<LPR, C>;
-    constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, CG = S::CG;
-    __shared__ int list[CK_PASS];
-    __shared__ int nsh, totsh;
-    __shared__ float hv[CK_PASS][T + 1];
+    constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, CG = S::CG, NW = S::NW;
+    __shared__ int lists[NW][CK_PASS];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
     const int e = blockIdx.y;
     const int o0 = blockIdx.x * T;
-    const int nt = T;  // tiles divide a 32-value block, so they divide dff
     const int nch = d >> 4, nb = d >> 5;
     const int st = wid;  // each wave takes one step of the tile (T = NW * OPS)
+    int *list = lists[wid];
 
+    IdxBatch ib;
+    idx_load(ib, idx, nchoice, 0, E, lane);
+    // the invalid bucket (e == E) writes zeros; its workgroups all read expert
+    // 0's first tile (straight-line loads, served from cache after the first)
+    RowSlice<C> wg[U], wu[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int64_t o = (e < E ? (int64_t)e * dff + o0 : 0) + st * OPS + u * G + grp;
+        load_row_flat<LPR, C>(wg[u], Wgq + o * d, Wgs + o * nb, 0, nch, lig);
+        load_row_flat<LPR, C>(wu[u], Wuq + o * d, Wus + o * nb, 0, nch, lig);
+    }
     for (int first = 0;; first += CK_PASS) {
-        gather_choices(idx, nchoice, e, E, first, list, &nsh, &totsh);
-        const int n = nsh, total = totsh;
+        if (first > 0)
+            idx_load(ib, idx, nchoice, 0, E, lane);
+        const int total = idx_gather(ib, idx, nchoice, e, E, first, list, lane);
+        const int n = min(CK_PASS, max(0, total - first));
         if (n == 0)
             break;
-        if (e < E) {
-            RowSlice<C> wg[U], wu[U];
+        for (int cg = 0; cg < n; cg += CG) {
+            XSlice<1, C> xv[CG];
 #pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int64_t o = (int64_t)e * dff + o0 + min(st * OPS + u * G + grp, nt - 1);
-                load_row<LPR, C>(wg[u], Wgq + o * d, Wgs + o * nb, 0, nch, lig);
-                load_row<LPR, C>(wu[u], Wuq + o * d, Wus + o * nb, 0, nch, lig);
+            for (int q = 0; q < CG; q++) {
+                const int64_t r = list[min(cg + q, n - 1)] / k;
+                load_x_flat<LPR, C>(xv[q], xq + r * d, xs + r * nb, 0, nch, lig);
             }
-            for (int cg = 0; cg < n; cg += CG) {
-                XSlice<1, C> xv[CG];
 #pragma unroll
-                for (int q = 0; q < CG; q++) {
-                    const int64_t r = list[min(cg + q, n - 1)] / k;
-                    load_x<LPR, C>(xv[q], nullptr, xq + r * d, xs + r * nb, 0, nch, lig);
+            for (int q = 0; q < CG; q++)
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const float g = group_sum<LPR>(row_dot(wg[u], xv[q], lig));
+                    const float v = group_sum<LPR>(row_dot(wu[u], xv[q], lig));
+                    if (lig == 0 && cg + q < n)
+                        h[(int64_t)list[cg + q] * dff + o0 + st * OPS + u * G + grp] = e < E ? silu(g) * v : 0.0f;
                 }
-#pragma unroll
-                for (int q = 0; q < CG; q++)
-#pragma unroll
-                    for (int u = 0; u < U; u++) {
-                        const float g = group_sum<LPR>(row_dot(wg[u], xv[q], lig));
-                        const float v = group_sum<LPR>(row_dot(wu[u], xv[q], lig));
-                        if (lig == 0 && cg + q < n)
-                            hv[cg + q][st * OPS + u * G + grp] = silu(g) * v;
-                    }
-            }
-        }
-        __syncthreads();
-        // epilogue: the tile's float32 hidden values of every gathered choice
-        for (int item = threadIdx.x; item < n * nt; item += blockDim.x) {
-            const int rr = item / nt, t = item % nt;
-            h[(int64_t)list[rr] * dff + o0 + t] = e < E ? hv[rr][t] : 0.0f;
         }
         if (total <= first + CK_PASS)
             break;
-        __syncthreads();
     }
 }
 
@@ -141,7 +154,9 @@ __global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
 // front (6-8 16-byte loads a lane), then applies them to the gathered
 // choices CG at a time.  Outputs per workgroup TO = NW * R.  Small
 // workgroups, several to a CU, as for the chunk gate-up (measured 53 vs 64 us
-// for the 64-row chunk's down projection at dff 768).
+// for the 64-row chunk's down projection at dff 768).  Waves work on their
+// own, as in k_chunk_gate_up (measured 52.8 vs 55.1 us with the workgroup
+// barriers).
 template <int LPR, int C>
 struct CkDownShape {
     static constexpr int NW = 4;
@@ -159,32 +174,36 @@ __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
                  float *__restrict__ pa)
 {
     using S = CkDownShape<LPR, C>;
-    constexpr int G = S::G, SW = S::SW, R = S::R, TO = S::TO, CG = S::CG;
-    __shared__ int list[CK_PASS];
-    __shared__ int nsh, totsh;
+    constexpr int G = S::G, SW = S::SW, R = S::R, CG = S::CG, NW = S::NW;
+    __shared__ int lists[NW][CK_PASS];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
     const int e = blockIdx.y;
-    const int o0 = blockIdx.x * TO + wid * R;
+    const int o0 = blockIdx.x * S::TO + wid * R;
     const int nch = dff >> 4, nb = dff >> 5;
+    int *list = lists[wid];
 
+    IdxBatch ib;
+    idx_load(ib, idx, nchoice, 0, E, lane);
+    RowSlice<C> w[SW];
+#pragma unroll
+    for (int u = 0; u < SW; u++) {
+        const int64_t o = (int64_t)e * d + min(o0 + u * G + grp, d - 1);
+        load_row_flat<LPR, C>(w[u], Wdq + o * dff, Wds + o * nb, 0, nch, lig);
+    }
     for (int first = 0;; first += CK_PASS) {
-        gather_choices(idx, nchoice, e, E, first, list, &nsh, &totsh);
-        const int n = nsh, total = totsh;
+        if (first > 0)
+            idx_load(ib, idx, nchoice, 0, E, lane);
+        const int total = idx_gather(ib, idx, nchoice, e, E, first, list, lane);
+        const int n = min(CK_PASS, max(0, total - first));
         if (n == 0)
             break;
-        RowSlice<C> w[SW];
-#pragma unroll
-        for (int u = 0; u < SW; u++) {
-            const int64_t o = (int64_t)e * d + min(o0 + u * G + grp, d - 1);
-            load_row<LPR, C>(w[u], Wdq + o * dff, Wds + o * nb, 0, nch, lig);
-        }
         for (int cg = 0; cg < n; cg += CG) {
             XSlice<1, C> xv[CG];
 #pragma unroll
             for (int q = 0; q < CG; q++) {
                 const int64_t c = list[min(cg + q, n - 1)];
-                load_x<LPR, C>(xv[q], nullptr, hq + c * dff, hs + c * nb, 0, nch, lig);
+                load_x_flat<LPR, C>(xv[q], hq + c * dff, hs + c * nb, 0, nch, lig);
             }
 #pragma unroll
             for (int q = 0; q < CG; q++)
@@ -198,7 +217,6 @@ __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
         }
         if (total <= first + CK_PASS)
             break;
-        __syncthreads();
     }
 }
 
