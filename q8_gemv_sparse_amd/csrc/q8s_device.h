@@ -406,7 +406,16 @@ Q8S_DEV float row_dot(const RowSlice<C> &w, const XSlice<1, C> &x, int lig)
 // ---------------------------------------------------------------------------
 // the MoE block's pieces shared by its decode and chunk kernels
 
-Q8S_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) with the hardware's exp2 and reciprocal (each
+// within a couple of ulps: a few 1e-7 relative, far inside the float32
+// tolerance; the library's correctly rounded division and exp cost ~40
+// instructions, which the chunk gate-up, bound by its vector work, pays per
+// hidden value).  Large |z| behaves: e^-z -> inf gives 0, e^-z -> 0 gives z.
+Q8S_DEV float silu(float z)
+{
+    const float t = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+    return z * __builtin_amdgcn_rcpf(1.0f + t);
+}
 
 // Decode gate-up launch shape per mode and row cut.  At these sizes the kernels are
 // bound by memory latency more than by bandwidth: many waves with one or two
@@ -427,26 +436,6 @@ struct GuShape {
     static constexpr int T = NW * OPS;
     static_assert(QB % T == 0, "a tile divides a 32-value block, so it divides dff");
     static_assert(ACT == 0 || T == QB, "int8 tiles are whole blocks");
-};
-
-// Chunk gate-up shape (int8, rows of up to two chunks a lane): small
-// workgroups of 4 waves, a tile of 8 (lane groups of 64) or 16 (lane groups
-// of 16) hidden outputs; each wave holds its U gate/up pairs and CG choices'
-// activation slices in registers.  Many small workgroups beat fewer large
-// ones here: several fit a CU at once, so one's gather and reductions overlap
-// another's weight stream (measured 106 vs 138 us for the 64-row chunk at
-// d 2048, dff 768, 128 experts).  The tile is less than a Q8_0 block of the
-// hidden row, so the kernel writes the float32 hidden rows and a quantise
-// pass forms their Q8_0 form.
-template <int LPR, int C>
-struct ChunkGuShape {
-    static constexpr int G = WAVE / LPR;
-    static constexpr int NW = 4;
-    static constexpr int U = LPR == 16 ? 1 : 2;
-    static constexpr int CG = 2;
-    static constexpr int OPS = G * U;
-    static constexpr int T = NW * OPS;
-    static_assert(QB % T == 0, "tiles divide a Q8_0 block, so they divide dff");
 };
 
 // ---------------------------------------------------------------------------

@@ -57,6 +57,7 @@ Q8S_DEV void idx_load(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice,
 // with ordinal in [first, first + CK_PASS) go to list[] (the wave's own LDS
 // row; a wave's LDS operations complete in order, so no barrier is needed);
 // returns the running count of such choices.
+template <int PASS = CK_PASS>
 Q8S_DEV int idx_scan(const IdxBatch &b, int c0, int nchoice, int e, int E, int first, int base, int *list, int lane)
 {
 #pragma unroll
@@ -66,87 +67,216 @@ Q8S_DEV int idx_scan(const IdxBatch &b, int c0, int nchoice, int e, int E, int f
         const bool hit = c < nchoice && ((e < E) ? (v == e) : (v < 0 || v >= E));
         const uint64_t mask = __ballot(hit);
         const int ord = base + __popcll(mask & ((1ull << lane) - 1ull));
-        if (hit && ord >= first && ord < first + CK_PASS)
+        if (hit && ord >= first && ord < first + PASS)
             list[ord - first] = c;
         base += __popcll(mask);
     }
     return base;
 }
 
-// The whole scan for the pass starting at ordinal `first`, the first batch
-// already loaded in b.
+// The whole scan for the pass of PASS ordinals starting at `first`, the
+// first batch already loaded in b.
+template <int PASS = CK_PASS>
 Q8S_DEV int idx_gather(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice, int e, int E, int first, int *list,
                        int lane)
 {
-    int base = idx_scan(b, 0, nchoice, e, E, first, 0, list, lane);
+    int base = idx_scan<PASS>(b, 0, nchoice, e, E, first, 0, list, lane);
     for (int c0 = CK_GB * WAVE; c0 < nchoice; c0 += CK_GB * WAVE) {
         idx_load(b, idx, nchoice, c0, E, lane);
-        base = idx_scan(b, c0, nchoice, e, E, first, base, list, lane);
+        base = idx_scan<PASS>(b, c0, nchoice, e, E, first, base, list, lane);
     }
     return base;
 }
 
 } // namespace
 
-// Every wave works on its own: it gathers the expert's choices itself, holds
-// its own weight rows, and writes its own outputs, so no wave of a workgroup
-// waits for another.  The first idx batch is requested before the weight
-// rows, so the scan waits for it alone (waits on the vector-memory counter
-// are in issue order).
-template <int LPR, int C>
-__global__ void __launch_bounds__((ChunkGuShape<LPR, C>::NW * WAVE))
+// The chunk gate-up (rows of up to 2048 values, 64 Q8_0 blocks): one
+// workgroup per (expert e, tile of CKB_T hidden outputs); row E of the grid
+// takes the choices with an invalid expert and writes their zeros.  The
+// kernel is bound by its vector work (a handful of choices per weight row), so
+// the layout spends as few instructions per weight byte as it can:
+//   * every lane holds one whole block of each weight row, so its 8 v_dot4
+//     give an exact block sum with no cross-lane join, and one multiply by
+//     ws*xs scales it: the rows are read as whole 1 KB spans a load (lane l
+//     takes 16-byte chunks l and 64 + l) and lane pairs then trade halves,
+//     leaving block l/2 in even lanes and block 32 + l/2 in odd ones;
+//   * the 8 partial sums of a pair of choices (2 choices x 2 rows x gate/up)
+//     are reduced across the wave together, each exchange step halving the
+//     values a lane keeps (10 exchanges instead of 8 x 6), ending with every
+//     value in one group of 8 lanes;
+//   * each wave requests its rows first (they stay in its registers); wave 0
+//     then gathers up to CK_NA of the expert's choices (choice order) and the
+//     workgroup stages their Q8_0 activation rows in LDS, so the gather and
+//     the staging overlap the weight rows' latency.
+// More than CK_NA choices take further passes over the same registers.
+constexpr int CK_NA = 16;
+constexpr int CKB_NW = 4;               // waves
+#ifndef Q8S_CKB_U
+#define Q8S_CKB_U 4
+#endif
+constexpr int CKB_U = Q8S_CKB_U;        // gate/up row pairs a wave holds (even)
+constexpr int CKB_T = CKB_NW * CKB_U;   // hidden outputs a workgroup
+constexpr int CKB_MAXD = 64 * QB;       // a block a lane
+
+// Sum of v[i] over the wave for eight values at once: lane l ends holding the
+// sum of v[4*b5 + 2*b4 + b3], b5, b4, b3 bits 5, 4, 3 of l (every lane of
+// its group of 8 holds it).
+Q8S_DEV float wave_sum8(const float (&v)[8], int lane)
+{
+    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+    float w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float send = h5 ? v[i] : v[i + 4];
+        const float keep = h5 ? v[i + 4] : v[i];
+        w4[i] = keep + __shfl_xor(send, 32);
+    }
+    float w2[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const float send = h4 ? w4[i] : w4[i + 2];
+        const float keep = h4 ? w4[i + 2] : w4[i];
+        w2[i] = keep + __shfl_xor(send, 16);
+    }
+    // lanes i and 15-i of a row of 16 differ in bit 3
+    const float send = h3 ? w2[0] : w2[1];
+    float w = (h3 ? w2[1] : w2[0]) + dpp_f<DPP_MIRROR>(send);
+    w += dpp_f<DPP_HALF_MIRROR>(w);
+    w += dpp_f<DPP_XOR2>(w);
+    w += dpp_f<DPP_XOR1>(w);
+    return w;
+}
+
+Q8S_DEV int block_dot(const i32x4 (&a)[2], const i32x4 (&b)[2])
+{
+    int s = 0;
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            s = __builtin_amdgcn_sdot4(a[h][i], b[h][i], s, false);
+    return s;
+}
+
+__global__ void __launch_bounds__(CKB_NW * WAVE)
     k_chunk_gate_up(const int8_t *__restrict__ xq, const float *__restrict__ xs, const int8_t *__restrict__ Wgq,
                     const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq, const float *__restrict__ Wus,
                     const int32_t *__restrict__ idx, int nchoice, int k, int d, int dff, int E, float *__restrict__ h)
 {
-    using S = ChunkGuShape<LPR, C>;
-    constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, CG = S::CG, NW = S::NW;
-    __shared__ int lists[NW][CK_PASS];
+    __shared__ int list[CK_NA];
+    __shared__ int totsh;
+    __shared__ __align__(16) int8_t act[CK_NA][CKB_MAXD];
+    __shared__ float asc[CK_NA][CKB_MAXD / QB];
 
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, lig = lane % LPR, grp = lane / LPR;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int e = blockIdx.y;
-    const int o0 = blockIdx.x * T;
-    const int nch = d >> 4, nb = d >> 5;
-    const int st = wid;  // each wave takes one step of the tile (T = NW * OPS)
-    int *list = lists[wid];
+    const int o0 = blockIdx.x * CKB_T;
+    const int nb = d >> 5, nch = d >> 4;
+    const bool odd = lane & 1;
+    const int blk = odd ? 32 + (lane >> 1) : (lane >> 1);  // the lane's block after the trade
+    const int bl = min(blk, nb - 1);   // (blocks past the row: the last one, with zero activations)
+    const bool inb = blk < nb;
+    const int c0 = min(lane, nch - 1), c1 = min(64 + lane, nch - 1);  // the chunks the lane loads
 
-    IdxBatch ib;
-    idx_load(ib, idx, nchoice, 0, E, lane);
-    // the invalid bucket (e == E) writes zeros; its workgroups all read expert
-    // 0's first tile (straight-line loads, served from cache after the first)
-    RowSlice<C> wg[U], wu[U];
+    // the wave's rows o0 + CKB_U*wid + u; the invalid bucket (e == E) writes
+    // zeros and reads expert 0's first rows (served from cache after the first)
+    i32x4 gq[CKB_U][2], uq[CKB_U][2];
+    float gs[CKB_U], us[CKB_U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-        const int64_t o = (e < E ? (int64_t)e * dff + o0 : 0) + st * OPS + u * G + grp;
-        load_row_flat<LPR, C>(wg[u], Wgq + o * d, Wgs + o * nb, 0, nch, lig);
-        load_row_flat<LPR, C>(wu[u], Wuq + o * d, Wus + o * nb, 0, nch, lig);
+    for (int u = 0; u < CKB_U; u++) {
+        const int64_t row = (e < E ? (int64_t)e * dff + o0 : 0) + CKB_U * wid + u;
+        const int8_t *gp = Wgq + row * d;
+        const int8_t *up = Wuq + row * d;
+        gq[u][0] = ld_stream16(gp + 16 * c0);
+        gq[u][1] = ld_stream16(gp + 16 * c1);
+        uq[u][0] = ld_stream16(up + 16 * c0);
+        uq[u][1] = ld_stream16(up + 16 * c1);
+        gs[u] = ld_stream_f32(Wgs + row * nb + bl);
+        us[u] = ld_stream_f32(Wus + row * nb + bl);
     }
-    for (int first = 0;; first += CK_PASS) {
-        if (first > 0)
+    // the trade: even lanes give chunk 64 + l and take their partner's chunk
+    // l + 1; odd lanes give chunk l and take their partner's chunk 63 + l
+    auto trade = [&](i32x4 (&w)[2]) {
+        i32x4 got;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            got[i] = dpp_i<DPP_XOR1>(odd ? w[0][i] : w[1][i]);
+        w[0] = odd ? got : w[0];
+        w[1] = odd ? w[1] : got;
+    };
+#pragma unroll
+    for (int u = 0; u < CKB_U; u++) {
+        trade(gq[u]);
+        trade(uq[u]);
+    }
+    for (int first = 0;; first += CK_NA) {
+        if (wid == 0) {
+            IdxBatch ib;
             idx_load(ib, idx, nchoice, 0, E, lane);
-        const int total = idx_gather(ib, idx, nchoice, e, E, first, list, lane);
-        const int n = min(CK_PASS, max(0, total - first));
+            const int tot = idx_gather<CK_NA>(ib, idx, nchoice, e, E, first, list, lane);
+            if (lane == 0)
+                totsh = tot;
+        }
+        __syncthreads();
+        const int total = totsh, n = min(CK_NA, max(0, total - first));
         if (n == 0)
             break;
-        for (int cg = 0; cg < n; cg += CG) {
-            XSlice<1, C> xv[CG];
+        // stage the n choices' activation rows: 16-byte chunk t of every row by
+        // thread t, four rows' loads in flight at a time (straight-line; a row
+        // past n rereads row n-1)
+        if ((int)threadIdx.x < nch) {
+            const int t = threadIdx.x;
+            for (int q0 = 0; q0 < n; q0 += 4) {
+                i32x4 v[4];
+                float sc[4];
 #pragma unroll
-            for (int q = 0; q < CG; q++) {
-                const int64_t r = list[min(cg + q, n - 1)] / k;
-                load_x_flat<LPR, C>(xv[q], xq + r * d, xs + r * nb, 0, nch, lig);
-            }
-#pragma unroll
-            for (int q = 0; q < CG; q++)
-#pragma unroll
-                for (int u = 0; u < U; u++) {
-                    const float g = group_sum<LPR>(row_dot(wg[u], xv[q], lig));
-                    const float v = group_sum<LPR>(row_dot(wu[u], xv[q], lig));
-                    if (lig == 0 && cg + q < n)
-                        h[(int64_t)list[cg + q] * dff + o0 + st * OPS + u * G + grp] = e < E ? silu(g) * v : 0.0f;
+                for (int q = 0; q < 4; q++) {
+                    const int64_t r = list[min(q0 + q, n - 1)] / k;
+                    v[q] = ld16(xq + r * d + t * 16);
+                    sc[q] = xs[r * nb + (t >> 1)];
                 }
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    *reinterpret_cast<i32x4 *>(&act[q0 + q][t * 16]) = v[q];
+                    if ((t & 1) == 0)
+                        asc[q0 + q][t >> 1] = sc[q];
+                }
+            }
         }
-        if (total <= first + CK_PASS)
+        __syncthreads();
+        for (int cg = 0; cg < n; cg += 2) {
+            i32x4 a[2][2];
+            float sx[2];
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int qq = min(cg + q, n - 1);
+                a[q][0] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * bl]);
+                a[q][1] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * bl + 16]);
+                sx[q] = inb ? asc[qq][bl] : 0.0f;
+            }
+            // rows in pairs: 2 choices x 2 rows x gate/up = 8 values a reduction
+#pragma unroll
+            for (int u0 = 0; u0 < CKB_U; u0 += 2) {
+                float v[8];
+#pragma unroll
+                for (int q = 0; q < 2; q++)
+#pragma unroll
+                    for (int u = 0; u < 2; u++) {
+                        v[4 * q + 2 * u] = (float)block_dot(gq[u0 + u], a[q]) * (gs[u0 + u] * sx[q]);
+                        v[4 * q + 2 * u + 1] = (float)block_dot(uq[u0 + u], a[q]) * (us[u0 + u] * sx[q]);
+                    }
+                const float r = wave_sum8(v, lane);
+                // lanes with bit 3 clear hold a gate sum; the up sum of the
+                // same (choice, row) is in lane 15 - i of the row
+                const float up = dpp_f<DPP_MIRROR>(r);
+                const int q = (lane >> 5) & 1, u = (lane >> 4) & 1;
+                if ((lane & 15) == 0 && cg + q < n)
+                    h[(int64_t)list[cg + q] * dff + o0 + CKB_U * wid + u0 + u] = e < E ? silu(r) * up : 0.0f;
+            }
+        }
+        if (total <= first + CK_NA)
             break;
+        __syncthreads();  // the next pass rewrites the list and the staged rows
     }
 }
 
@@ -246,13 +376,11 @@ bool chunk_supported(int64_t d, int64_t dff) { return d <= 2048 && slice_shape(d
 
 namespace {
 
-template <int LPR, int C>
 hipError_t gu_chunk_go(const MoeArgs &a, hipStream_t st)
 {
-    using S = ChunkGuShape<LPR, C>;
-    dim3 grid((unsigned)(a.dff / S::T), (unsigned)(a.E + 1));  // + one row for invalid choices
-    hipLaunchKernelGGL((k_chunk_gate_up<LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
-                       a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h);
+    dim3 grid((unsigned)(a.dff / CKB_T), (unsigned)(a.E + 1));  // + one row for invalid choices
+    hipLaunchKernelGGL(k_chunk_gate_up, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus,
+                       a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
@@ -297,17 +425,13 @@ hipError_t by_row(const MoeArgs &a, int64_t n_in, hipStream_t st)
 }
 
 template <int LPR, int C>
-struct GUC {
-    static hipError_t go(const MoeArgs &a, hipStream_t st) { return gu_chunk_go<LPR, C>(a, st); }
-};
-template <int LPR, int C>
 struct DNC {
     static hipError_t go(const MoeArgs &a, hipStream_t st) { return dn_chunk_go<LPR, C>(a, st); }
 };
 
 } // namespace
 
-hipError_t chunk_gate_up_launch(const MoeArgs &a, hipStream_t st) { return by_row<GUC, false>(a, a.d, st); }
+hipError_t chunk_gate_up_launch(const MoeArgs &a, hipStream_t st) { return gu_chunk_go(a, st); }
 
 hipError_t chunk_down_launch(const MoeArgs &a, hipStream_t st) { return by_row<DNC, true>(a, a.dff, st); }
 

@@ -186,8 +186,16 @@ def test_topk_gate_up(E, k, ties, act):
     ridx, rw = host_topk(logits, k)
     assert np.array_equal(host(idx), ridx)
     assert rel_err(host(wts), rw) <= 1e-6
-    # the hidden rows are moe_gate_up's for those choices, bit for bit
+    # the hidden rows are moe_gate_up's for those choices: bit for bit in f32
+    # numerics (the same row-by-row kernels); in int8 numerics moe_gate_up
+    # groups the two rows by expert on the matrix cores, whose block sums are
+    # exact but whose float sum over blocks runs in another order, so h agrees
+    # to float rounding and each side's hq/hs is the Q8_0 form of its own h
     h2, hq2, hs2 = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, **kw)
-    assert torch.equal(h, h2)
-    if act == 1:
-        assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
+    if act == 0:
+        assert torch.equal(h, h2)
+    else:
+        assert rel_err(host(h), host(h2)) <= 1e-5
+        for hh, qq, ss in ((h, hq, hs), (h2, hq2, hs2)):
+            rq, rs = q8.q8_quantize_rows(hh.reshape(rows * k, dff))
+            assert torch.equal(qq.reshape(rq.shape), rq) and torch.equal(ss.reshape(rs.shape), rs)
