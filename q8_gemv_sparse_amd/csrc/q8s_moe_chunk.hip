@@ -350,6 +350,151 @@ __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
     }
 }
 
+// The chunk down projection for rows of up to 1024 values (32 blocks), in
+// the gate-up's manner: one workgroup per (expert e, CKD_T outputs); lane
+// groups of 8 lanes per weight row, so one load covers 8 rows x 128
+// contiguous bytes; lane pairs trade halves so every lane holds C/2 whole
+// blocks (blocks (l>>1) + 4*(l&1) + 8m of lane l of the group); the hidden
+// rows of up to CK_NA choices are staged in LDS; four partial sums (2 choices
+// x 2 row slots) are reduced across the 8 lanes together.
+constexpr int CKD_NW = 4;
+constexpr int CKD_U = 2;                       // row slots a wave: 8 rows each
+constexpr int CKD_T = CKD_NW * CKD_U * 8;      // outputs a workgroup
+constexpr int CKD_MAXF = 1024;                 // longest hidden row
+
+template <int C>
+__global__ void __launch_bounds__(CKD_NW * WAVE)
+    k_chunk_down2(const int8_t *__restrict__ hq, const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
+                  const float *__restrict__ Wds, const int32_t *__restrict__ idx, int nchoice, int d, int dff, int E,
+                  float *__restrict__ pa)
+{
+    static_assert(C % 2 == 0 && 8 * C * 16 <= CKD_MAXF * 2, "whole blocks a lane");
+    constexpr int M = C / 2;  // whole blocks a lane
+    __shared__ int list[CK_NA];
+    __shared__ int totsh;
+    __shared__ __align__(16) int8_t act[CK_NA][CKD_MAXF];
+    __shared__ float asc[CK_NA][CKD_MAXF / QB];
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lig = lane & 7, grp = lane >> 3;
+    const int e = blockIdx.y;
+    const int nb = dff >> 5, nch = dff >> 4;
+    const bool odd = lig & 1;
+    int blk[M];
+    bool inb[M];
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+        const int b = (lig >> 1) + 4 * (lig & 1) + 8 * m;
+        inb[m] = b < nb;
+        blk[m] = min(b, nb - 1);
+    }
+
+    // the rows of slot u: o0 + 8*(CKD_U*wid + u) + grp (clamped to d - 1)
+    i32x4 w[CKD_U][C];
+    float ws[CKD_U][M];
+    int orow[CKD_U];
+#pragma unroll
+    for (int u = 0; u < CKD_U; u++) {
+        orow[u] = blockIdx.x * CKD_T + 8 * (CKD_U * wid + u) + grp;
+        const int64_t row = (int64_t)e * d + min(orow[u], d - 1);
+#pragma unroll
+        for (int c = 0; c < C; c++)
+            w[u][c] = ld_stream16(Wdq + row * dff + 16 * min(8 * c + lig, nch - 1));
+#pragma unroll
+        for (int m = 0; m < M; m++)
+            ws[u][m] = ld_stream_f32(Wds + row * nb + blk[m]);
+    }
+    // the trade: for chunk pair (2m, 2m+1) even lanes keep 2m and take the
+    // partner's half of it, odd lanes keep 2m+1 and take the partner's half
+#pragma unroll
+    for (int u = 0; u < CKD_U; u++)
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            i32x4 got;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                got[i] = dpp_i<DPP_XOR1>(odd ? w[u][2 * m][i] : w[u][2 * m + 1][i]);
+            // block: (first half, second half)
+            w[u][2 * m] = odd ? got : w[u][2 * m];
+            w[u][2 * m + 1] = odd ? w[u][2 * m + 1] : got;
+        }
+
+    for (int first = 0;; first += CK_NA) {
+        if (wid == 0) {
+            IdxBatch ib;
+            idx_load(ib, idx, nchoice, 0, E, lane);
+            const int tot = idx_gather<CK_NA>(ib, idx, nchoice, e, E, first, list, lane);
+            if (lane == 0)
+                totsh = tot;
+        }
+        __syncthreads();
+        const int total = totsh, n = min(CK_NA, max(0, total - first));
+        if (n == 0)
+            break;
+        // stage the n choices' hidden rows (chunk t by thread t)
+        if ((int)threadIdx.x < nch) {
+            const int t = threadIdx.x;
+            for (int q0 = 0; q0 < n; q0 += 4) {
+                i32x4 v[4];
+                float sc[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int64_t c = list[min(q0 + q, n - 1)];
+                    v[q] = ld16(hq + c * dff + t * 16);
+                    sc[q] = hs[c * nb + (t >> 1)];
+                }
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    *reinterpret_cast<i32x4 *>(&act[q0 + q][t * 16]) = v[q];
+                    if ((t & 1) == 0)
+                        asc[q0 + q][t >> 1] = sc[q];
+                }
+            }
+        }
+        __syncthreads();
+        for (int cg = 0; cg < n; cg += 2) {
+            float v[2][CKD_U];
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                const int qq = min(cg + q, n - 1);
+#pragma unroll
+                for (int u = 0; u < CKD_U; u++)
+                    v[q][u] = 0.0f;
+#pragma unroll
+                for (int m = 0; m < M; m++) {
+                    i32x4 a[2];
+                    a[0] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * blk[m]]);
+                    a[1] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * blk[m] + 16]);
+                    const float sx = inb[m] ? asc[qq][blk[m]] : 0.0f;
+#pragma unroll
+                    for (int u = 0; u < CKD_U; u++) {
+                        const i32x4 wb[2] = {w[u][2 * m], w[u][2 * m + 1]};
+                        v[q][u] = __builtin_fmaf((float)block_dot(wb, a), ws[u][m] * sx, v[q][u]);
+                    }
+                }
+            }
+            // the four values over the 8 lanes: bit 2 keeps a choice, bit 1
+            // a row slot, bit 0 sums
+            const bool b2 = lig & 4, b1 = lig & 2;
+            float w2[2];
+#pragma unroll
+            for (int u = 0; u < 2; u++) {
+                const float send = b2 ? v[0][u] : v[1][u];
+                w2[u] = (b2 ? v[1][u] : v[0][u]) + dpp_f<DPP_HALF_MIRROR>(send);
+            }
+            const float send = b1 ? w2[0] : w2[1];
+            float r = (b1 ? w2[1] : w2[0]) + dpp_f<DPP_XOR2>(send);
+            r += dpp_f<DPP_XOR1>(r);
+            const int q = b2 ? 1 : 0, u = b1 ? 1 : 0;
+            if (!odd && cg + q < n && orow[u] < d)
+                pa[(int64_t)list[cg + q] * d + orow[u]] = r;
+        }
+        if (total <= first + CK_NA)
+            break;
+        __syncthreads();
+    }
+}
+
 __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__ pa, const int32_t *__restrict__ idx,
                                                      const float *__restrict__ wts, int d, int k, int E,
                                                      float *__restrict__ y)
@@ -388,14 +533,33 @@ hipError_t gu_chunk_go(const MoeArgs &a, hipStream_t st)
     return quantize_launch(a.h, a.rows * a.k, a.dff, a.hq, a.hs, st);
 }
 
+template <int C>
+void dn2_go(const MoeArgs &a, float *pa, hipStream_t st)
+{
+    dim3 grid((unsigned)((a.d + CKD_T - 1) / CKD_T), (unsigned)a.E);
+    hipLaunchKernelGGL((k_chunk_down2<C>), grid, dim3(CKD_NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds, a.idx,
+                       (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa);
+}
+
 template <int LPR, int C>
 hipError_t dn_chunk_go(const MoeArgs &a, hipStream_t st)
 {
     using S = CkDownShape<LPR, C>;
     float *pa = reinterpret_cast<float *>(a.scratch);
-    dim3 grid((unsigned)((a.d + S::TO - 1) / S::TO), (unsigned)a.E);
-    hipLaunchKernelGGL((k_chunk_down<LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds, a.idx,
-                       (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa);
+    const int64_t nch = a.dff / 16;
+    if (nch <= 16)
+        dn2_go<2>(a, pa, st);
+    else if (nch <= 32)
+        dn2_go<4>(a, pa, st);
+    else if (nch <= 48)
+        dn2_go<6>(a, pa, st);
+    else if (nch <= 64)
+        dn2_go<8>(a, pa, st);
+    else {
+        dim3 grid((unsigned)((a.d + S::TO - 1) / S::TO), (unsigned)a.E);
+        hipLaunchKernelGGL((k_chunk_down<LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds, a.idx,
+                           (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
