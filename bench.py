@@ -140,6 +140,7 @@ class Workload:
     name = ""
     dominant = ""          # kernel symbol stem of the dominant kernel
     dominant_src = ()      # sources that define it (for the counter-file check)
+    dominant_timed = "the dominant kernel alone"  # what the graph of its launches runs
 
     def step(self, c):
         raise NotImplementedError
@@ -457,6 +458,7 @@ class ChunkBlock(MoeBlock):
         # kernel
         super().__init__(name, cfg, "int8", copies, rows=cfg["rows"], pool=8, separate=True)
         self.dominant = "k_chunk_gate_up"
+        self.dominant_timed = "moe_gate_up: k_chunk_gate_up, then k_quantize_rows over the hidden rows"
         import synthetic
         np, torch = self.np, self.torch
         rng = np.random.default_rng(2)
@@ -794,6 +796,7 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": int(dom_bytes),
             "us_per_launch": round(kms * 1e3, 3),
+            "timed": wl.dominant_timed,
         },
         "cpu_baseline": cpu,
     }
