@@ -224,11 +224,11 @@ __global__ void __launch_bounds__(NORM_THREADS)
 // ---------------------------------------------------------------------------
 // int8 MFMA GEMM (m >= GEMM_MIN_ROWS)
 //
-// Workgroup tile: 16 outputs x 64 rows (four 16-row MFMA tiles); its four
-// waves take interleaved Q8_0 blocks of k (wave w: blocks w, w + 4, ...).  Per
+// Workgroup tile: 16 outputs x 64 rows (four 16-row MFMA tiles); its eight
+// waves take interleaved Q8_0 blocks of k (wave w: blocks w, w + 8, ...).  Per
 // block and row tile one v_mfma_i32_16x16x32_i8 yields the 16x16 exact int32
 // block sums; each lane then adds isum * (ws[o][b] * xs[r][b]) for the four
-// (r, o) it holds.  The four waves' float partials are summed in wave order
+// (r, o) it holds.  The waves' float partials are summed in wave order
 // through LDS.
 //
 // Latency is the whole cost at these sizes (9.4 MB of weights), so:
@@ -249,16 +249,17 @@ __global__ void __launch_bounds__(NORM_THREADS)
 constexpr int GEMM_TN = 16;
 constexpr int GEMM_TM = 64;
 constexpr int GEMM_PB = 64;            // Q8_0 blocks of k per pass
-constexpr int GEMM_WQ = GEMM_PB / 4;   // of which one wave takes
+constexpr int GEMM_NW = 8;             // waves (measured 15.5 vs 16.3 us with 4 for the 64-row chunk's projection)
+constexpr int GEMM_WQ = GEMM_PB / GEMM_NW;  // blocks of a pass one wave takes
 constexpr int GEMM_AB = 4;             // activation blocks requested ahead
 
-__global__ void __launch_bounds__(256) k_gemm_i8(const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out,
+__global__ void __launch_bounds__(GEMM_NW * 64) k_gemm_i8(const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out,
                                                  int n_in, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                  int m, float *__restrict__ y)
 {
     typedef int v4i __attribute__((ext_vector_type(4)));
     __shared__ __attribute__((aligned(16))) float xsT[GEMM_PB][GEMM_TM];  // activation scales, block-major
-    __shared__ float red[4][GEMM_TM][GEMM_TN + 1];
+    __shared__ float red[GEMM_NW][GEMM_TM][GEMM_TN + 1];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int j = lane & 15, g = lane >> 4;
@@ -282,20 +283,20 @@ __global__ void __launch_bounds__(256) k_gemm_i8(const int8_t *__restrict__ Wq, 
 
     for (int p0 = 0; p0 < nb; p0 += GEMM_PB) {
         // the wave's weight fragments and scales of this pass (blocks
-        // p0 + wid + 4q), all requested at once in straight-line code; a block
+        // p0 + wid + NW q), all requested at once in straight-line code; a block
         // past the row re-reads the row's last block and is not used
         long bfrag[GEMM_WQ];
         float wsc[GEMM_WQ];
 #pragma unroll
         for (int q = 0; q < GEMM_WQ; q++) {
-            const int b = min(p0 + wid + 4 * q, nb - 1);
+            const int b = min(p0 + wid + GEMM_NW * q, nb - 1);
             bfrag[q] = __builtin_nontemporal_load(reinterpret_cast<const long *>(wrow + (int64_t)b * QB));
             wsc[q] = ld_stream_f32(wsrow + b);
         }
         auto load_a = [&](long (&a)[GEMM_AB][4], int q0) {
 #pragma unroll
             for (int u = 0; u < GEMM_AB; u++) {
-                const int b = min(p0 + wid + 4 * (q0 + u), nb - 1);
+                const int b = min(p0 + wid + GEMM_NW * (q0 + u), nb - 1);
 #pragma unroll
                 for (int t = 0; t < 4; t++)
                     a[u][t] = *reinterpret_cast<const long *>(arow[t] + (int64_t)b * QB);
@@ -318,7 +319,7 @@ __global__ void __launch_bounds__(256) k_gemm_i8(const int8_t *__restrict__ Wq, 
 #pragma unroll
             for (int u = 0; u < GEMM_AB; u++) {
                 const int q = q0 + u;
-                const int bb = wid + 4 * q;  // block within the pass
+                const int bb = wid + GEMM_NW * q;  // block within the pass
                 if (p0 + bb < nb) {
 #pragma unroll
                     for (int t = 0; t < 4; t++) {
@@ -341,7 +342,10 @@ __global__ void __launch_bounds__(256) k_gemm_i8(const int8_t *__restrict__ Wq, 
     __syncthreads();
     for (int e = threadIdx.x; e < GEMM_TM * GEMM_TN; e += blockDim.x) {
         const int r = e / GEMM_TN, c = e % GEMM_TN;
-        const float v = ((red[0][r][c] + red[1][r][c]) + red[2][r][c]) + red[3][r][c];
+        float v = red[0][r][c];
+#pragma unroll
+        for (int w = 1; w < GEMM_NW; w++)
+            v += red[w][r][c];
         if (rt0 + r < m && o0 + c < n_out)
             y[(int64_t)(rt0 + r) * n_out + o0 + c] = v;
     }
@@ -420,7 +424,7 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t st)
 {
     if (a.act == 1 && a.m >= GEMM_MIN_ROWS) {
         dim3 grid((unsigned)((a.n_out + GEMM_TN - 1) / GEMM_TN), (unsigned)((a.m + GEMM_TM - 1) / GEMM_TM));
-        hipLaunchKernelGGL(k_gemm_i8, grid, dim3(256), 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
+        hipLaunchKernelGGL(k_gemm_i8, grid, dim3(GEMM_NW * 64), 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
                            (int)a.m, a.y);
         return hipGetLastError();
     }
