@@ -7,17 +7,21 @@
 // choice's weighed result (arena.rs fn scratch: the grouped list, and `pa`,
 // per choice, combined per row).  Here, in one-word int8 numerics:
 //
-//   k_chunk_gate_up  one workgroup per (expert e, tile of 8 or 16 hidden
-//                    outputs).  One wave gathers, in choice order, the choices
-//                    routed to e (a ballot compaction over idx).  Each wave
-//                    loads its gate and up weight rows into registers once,
-//                    then applies them to the gathered choices' activation
-//                    rows two at a time (v_dot4_i32_i8, exact int32 block
-//                    sums).  The epilogue writes SiLU(g)*u per choice row in
-//                    float32; a quantise pass (k_quantize_rows) then writes
-//                    the hidden rows' Q8_0 form.
-//   k_chunk_down     one workgroup per (expert e, tile of outputs): the same
-//                    scheme over Wd[e], writing each choice's result pa[c][o].
+//   k_chunk_gate_up  one workgroup per (expert e, tile of 16 hidden
+//                    outputs).  Wave 0 gathers, in choice order, the choices
+//                    routed to e (a ballot compaction over idx); the
+//                    workgroup stages their activation rows in LDS; each wave
+//                    holds four gate/up row pairs in registers, a whole Q8_0
+//                    block a lane (v_dot4_i32_i8, exact int32 block sums), and
+//                    writes SiLU(g)*u per choice row in float32; a quantise
+//                    pass (k_quantize_rows) then writes the hidden rows' Q8_0
+//                    form.
+//   k_chunk_down2    one workgroup per (expert e, 64 outputs), hidden rows
+//                    of up to 1024 values: 8 lanes a weight row, whole blocks a
+//                    lane, the hidden rows staged in LDS, each choice's result
+//                    written to pa[c][o]; k_chunk_down serves longer rows with
+//                    a lane group per row and the rows' chunks split across
+//                    lanes.
 //   k_chunk_combine  y[r][o] = sum_j wts[r][j] * pa[r*K + j][o], slot order.
 //
 // With a handful of choices per expert the contraction is far from dense, so
