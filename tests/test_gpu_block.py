@@ -199,3 +199,24 @@ def test_topk_gate_up(E, k, ties, act):
         for hh, qq, ss in ((h, hq, hs), (h2, hq2, hs2)):
             rq, rs = q8.q8_quantize_rows(hh.reshape(rows * k, dff))
             assert torch.equal(qq.reshape(rq.shape), rq) and torch.equal(ss.reshape(rs.shape), rs)
+
+
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("d,E", [(4096, 8), (2048, 16), (96, 3)])
+def test_block_few_experts_equals_stage_calls(d, E, act):
+    # the block with few experts is add_rmsnorm_router -> moe_topk_gate_up ->
+    # moe_down_combine: the same sum, choices and output
+    banner("block few experts vs stage calls d=%d E=%d act=%d" % (d, E, act))
+    b = synthetic.block_inputs(29, d, 1024, E, 2, 1)
+    W = weights(b)
+    Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds = W
+    s, x, xq, xs, logits = q8.add_rmsnorm_router(dev(b.h), dev(b.r), dev(b.w), EPS, Wr)
+    kw = dict(x=x) if act == 0 else dict(xq=xq, xs=xs, want_h=False)
+    idx, wts, h, hq, hs = q8.moe_topk_gate_up(logits, Wgq, Wgs, Wuq, Wus, 2, act=act, **kw)
+    y = q8.moe_down_combine(Wdq, Wds, idx, wts, E, h=h, hq=hq, hs=hs, act=act)
+    bs, bidx, bw, bout = run_block(b, act, W)
+    assert np.array_equal(bs, host(s))
+    assert np.array_equal(bidx, host(idx))
+    assert rel_err(bw, host(wts)) <= 1e-6
+    assert rel_err(bout, host(y)) <= 1e-6
+    check(b, act, (bs, bidx, bw, bout))
