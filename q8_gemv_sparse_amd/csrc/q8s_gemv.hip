@@ -224,130 +224,204 @@ __global__ void __launch_bounds__(NORM_THREADS)
 // ---------------------------------------------------------------------------
 // int8 MFMA GEMM (m >= GEMM_MIN_ROWS)
 //
-// Workgroup tile: 16 outputs x 64 rows (four 16-row MFMA tiles); its eight
-// waves take interleaved Q8_0 blocks of k (wave w: blocks w, w + 8, ...).  Per
-// block and row tile one v_mfma_i32_16x16x32_i8 yields the 16x16 exact int32
-// block sums; each lane then adds isum * (ws[o][b] * xs[r][b]) for the four
-// (r, o) it holds.  The waves' float partials are summed in wave order
-// through LDS.
+// Workgroup tile: 16 outputs x 16*MT activation rows (MT = 1 or 2 MFMA row
+// tiles), eight waves.  k is walked in passes of GEMM_KB Q8_0 blocks
+// (1 KiB of every row).  A pass's operands -- the 16 weight rows, the tile's
+// activation rows and both sets of scales -- are read from global memory with
+// coalesced 16-byte loads into registers, stored to LDS, and the MFMA
+// fragments are read back from LDS.  Two passes are in flight: while a pass is
+// contracted, the next one but one is already requested (register double
+// buffer), so at the usual n_in of 2048 every global load of the workgroup is
+// issued before its first MFMA.
 //
-// Latency is the whole cost at these sizes (9.4 MB of weights), so:
-//   * every activation scale of the tile goes to LDS once, up front (one
-//     barrier, not one per pass of k);
-//   * a wave requests all its weight fragments and scales before its first
-//     MFMA, in straight-line code (GEMM_WB blocks a wave at most);
-//   * activation fragments (from cache) are requested a batch of GEMM_AB
-//     blocks ahead of the MFMAs that use them.
+// Wave w takes blocks w, w + 8, w + 16, w + 24 of a pass, for every row tile:
+// per block it reads the weight fragment once, and per row tile one
+// v_mfma_i32_16x16x32_i8 yields the 16x16 exact int32 block sums, to which
+// each lane adds isum * (ws[o][b] * xs[r][b]) for the four (r, o) it holds.
+// The eight waves' partials of an output meet in LDS and are summed in wave
+// order.
 //
 // Operand layout of v_mfma_i32_16x16x32_i8 (lane l, j = l%16, g = l/16):
 //   A (16x32, rows x k):    A[j][8g .. 8g+7]
 //   B (32x16, k x outputs): B[8g .. 8g+7][j]
 //   D (16x16):              D[4g + i][j], i < 4
-// Both operands are read as 8 contiguous bytes of a row: the weight row
-// o0 + j and the activation row (tile row j).
+// Both fragments are 8 contiguous bytes of an LDS row: activation row j of
+// the tile and weight row j (rows swizzled, gemm_swizzle).
 
-constexpr int GEMM_TN = 16;
-constexpr int GEMM_TM = 64;
-constexpr int GEMM_PB = 64;            // Q8_0 blocks of k per pass
-constexpr int GEMM_NW = 8;             // waves (measured 15.5 vs 16.3 us with 4 for the 64-row chunk's projection)
-constexpr int GEMM_WQ = GEMM_PB / GEMM_NW;  // blocks of a pass one wave takes
-constexpr int GEMM_AB = 4;             // activation blocks requested ahead
+constexpr int GEMM_TN = 16;                    // outputs of a tile
+constexpr int GEMM_KB = 32;                    // Q8_0 blocks of k per pass
+constexpr int GEMM_NW = 8;                     // waves
+constexpr int GEMM_ROW = GEMM_KB * QB;        // LDS bytes per staged row
+constexpr int GEMM_CH = GEMM_KB * QB / 16;     // 16-byte chunks of a staged row
 
-__global__ void __launch_bounds__(GEMM_NW * 64) k_gemm_i8(const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out,
-                                                 int n_in, const int8_t *__restrict__ xq, const float *__restrict__ xs,
-                                                 int m, float *__restrict__ y)
+// LDS rows are stored swizzled in 8-byte units: unit u of row r sits at unit
+// u ^ gemm_swizzle(r % 16).  A wave's fragment reads of one block (8 bytes of
+// 16 rows, at the same unit) then fall on distinct banks both when 16 lanes
+// share 32 banks and when 32 lanes share 64 -- without padding, so the
+// staging writes (16-byte units, a permutation of a row) stay whole.
+Q8S_DEV int gemm_swizzle(int r) { return 2 * (r & 15) + ((r >> 3) & 1); }
+
+// Stores the row's 16-byte chunk k (units 2k, 2k + 1) at its swizzled place:
+// chunk k ^ (s >> 1), its two halves exchanged when s is odd.
+Q8S_DEV void put_swizzled(int8_t *row, int r, int k, i32x4 v)
+{
+    const int sw = gemm_swizzle(r);
+    if (sw & 1)
+        v = i32x4{v[2], v[3], v[0], v[1]};
+    *reinterpret_cast<i32x4 *>(row + 16 * (k ^ (sw >> 1))) = v;
+}
+
+template <int MT>
+struct GemmLds {
+    static constexpr int TM = 16 * MT;
+    int8_t w[GEMM_TN][GEMM_ROW];
+    int8_t a[TM][GEMM_ROW];
+    float ws[GEMM_KB][GEMM_TN + 1];
+    float xs[GEMM_KB][TM + 4];
+    float part[GEMM_NW][TM][GEMM_TN + 4];  // row pitch 20: a wave's 64 writes hit 64 banks
+};
+
+// A pass's global loads of one thread.
+template <int MT>
+struct GemmStage {
+    static constexpr int WL = GEMM_TN * GEMM_CH / (GEMM_NW * WAVE);       // weight chunks
+    static constexpr int AL = 16 * MT * GEMM_CH / (GEMM_NW * WAVE);       // activation chunks
+    static constexpr int XL = 16 * MT * GEMM_KB / (GEMM_NW * WAVE);       // activation scales
+    i32x4 w[WL];
+    i32x4 a[AL];
+    float ws;
+    float xs[XL];
+};
+
+template <int MT>
+__global__ void __launch_bounds__(GEMM_NW * WAVE)
+    k_gemm_i8(const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out, int n_in,
+              const int8_t *__restrict__ xq, const float *__restrict__ xs, int m, float *__restrict__ y)
 {
     typedef int v4i __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) float xsT[GEMM_PB][GEMM_TM];  // activation scales, block-major
-    __shared__ float red[GEMM_NW][GEMM_TM][GEMM_TN + 1];
+    using L = GemmLds<MT>;
+    using S = GemmStage<MT>;
+    constexpr int TM = L::TM;
+    __shared__ __attribute__((aligned(16))) L sm;
 
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int j = lane & 15, g = lane >> 4;
-    const int nb = n_in >> 5;
-    const int o0 = blockIdx.x * GEMM_TN;
-    const int rt0 = blockIdx.y * GEMM_TM;
-    const int o = min(o0 + j, n_out - 1);
-    const int8_t *wrow = Wq + (int64_t)o * n_in + 8 * g;
-    const float *wsrow = Ws + (int64_t)o * nb;
-    const int8_t *arow[4];
-#pragma unroll
-    for (int t = 0; t < 4; t++)
-        arow[t] = xq + (int64_t)min(rt0 + 16 * t + j, m - 1) * n_in + 8 * g;
+    const int nb = n_in >> 5, np = (nb + GEMM_KB - 1) / GEMM_KB;
+    const int o0 = blockIdx.x * GEMM_TN, r0 = blockIdx.y * TM;
 
-    float acc[4][4];
+    // Global reads of pass p: chunk c of a staged row is bytes 16c .. 16c+15
+    // of the pass's 1 KiB; rows past the matrix and chunks past the row are
+    // clamped to the last ones (their products are never used).
+    auto issue = [&](S &st, int p) {
+        const int64_t bmax = (int64_t)n_in - 16;
+        const int64_t k0 = (int64_t)p * GEMM_KB * QB;
 #pragma unroll
-    for (int t = 0; t < 4; t++)
+        for (int i = 0; i < S::WL; i++) {
+            const int c = tid + i * GEMM_NW * WAVE;
+            const int64_t o = min(o0 + c / GEMM_CH, n_out - 1);
+            st.w[i] = ld_stream16(Wq + o * n_in + min(k0 + (c % GEMM_CH) * 16, bmax));
+        }
+#pragma unroll
+        for (int i = 0; i < S::AL; i++) {
+            const int c = tid + i * GEMM_NW * WAVE;
+            const int64_t r = min(r0 + c / GEMM_CH, m - 1);
+            st.a[i] = ld16(xq + r * n_in + min(k0 + (c % GEMM_CH) * 16, bmax));
+        }
+        {
+            const int64_t o = min(o0 + tid / GEMM_KB, n_out - 1);
+            st.ws = ld_stream_f32(Ws + o * nb + min(p * GEMM_KB + tid % GEMM_KB, nb - 1));
+        }
+#pragma unroll
+        for (int i = 0; i < S::XL; i++) {
+            const int e = tid + i * GEMM_NW * WAVE;
+            const int64_t r = min(r0 + e / GEMM_KB, m - 1);
+            st.xs[i] = xs[r * nb + min(p * GEMM_KB + e % GEMM_KB, nb - 1)];
+        }
+    };
+    auto stage = [&](const S &st, int p) {
+#pragma unroll
+        for (int i = 0; i < S::WL; i++) {
+            const int c = tid + i * GEMM_NW * WAVE;
+            put_swizzled(&sm.w[c / GEMM_CH][0], c / GEMM_CH, c % GEMM_CH, st.w[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < S::AL; i++) {
+            const int c = tid + i * GEMM_NW * WAVE;
+            put_swizzled(&sm.a[c / GEMM_CH][0], c / GEMM_CH, c % GEMM_CH, st.a[i]);
+        }
+        // a block past the row gets weight scale 0, so it adds exactly 0
+        sm.ws[tid % GEMM_KB][tid / GEMM_KB] = p * GEMM_KB + tid % GEMM_KB < nb ? st.ws : 0.0f;
+#pragma unroll
+        for (int i = 0; i < S::XL; i++) {
+            const int e = tid + i * GEMM_NW * WAVE;
+            sm.xs[e % GEMM_KB][e / GEMM_KB] = st.xs[i];
+        }
+    };
+
+    // Branch-free: blocks past the row carry weight scale 0.
+    float acc[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; t++)
 #pragma unroll
         for (int i = 0; i < 4; i++)
             acc[t][i] = 0.0f;
-
-    for (int p0 = 0; p0 < nb; p0 += GEMM_PB) {
-        // the wave's weight fragments and scales of this pass (blocks
-        // p0 + wid + NW q), all requested at once in straight-line code; a block
-        // past the row re-reads the row's last block and is not used
-        long bfrag[GEMM_WQ];
-        float wsc[GEMM_WQ];
+    auto contract = [&]() {
+        const int sj = gemm_swizzle(j);  // row 16t + j has the same swizzle as row j
 #pragma unroll
-        for (int q = 0; q < GEMM_WQ; q++) {
-            const int b = min(p0 + wid + GEMM_NW * q, nb - 1);
-            bfrag[q] = __builtin_nontemporal_load(reinterpret_cast<const long *>(wrow + (int64_t)b * QB));
-            wsc[q] = ld_stream_f32(wsrow + b);
-        }
-        auto load_a = [&](long (&a)[GEMM_AB][4], int q0) {
+        for (int q = 0; q < GEMM_KB / GEMM_NW; q++) {
+            const int b = wid + GEMM_NW * q;
+            const int off = 8 * ((4 * b + g) ^ sj);  // the fragment's 8 bytes in the row
+            const long bf = *reinterpret_cast<const long *>(&sm.w[j][off]);
+            const float sw = sm.ws[b][j];
 #pragma unroll
-            for (int u = 0; u < GEMM_AB; u++) {
-                const int b = min(p0 + wid + GEMM_NW * (q0 + u), nb - 1);
+            for (int t = 0; t < MT; t++) {
+                const long af = *reinterpret_cast<const long *>(&sm.a[16 * t + j][off]);
+                const v4i isum = __builtin_amdgcn_mfma_i32_16x16x32_i8(af, bf, v4i{0, 0, 0, 0}, 0, 0, 0);
+                const f32x4 sx = *reinterpret_cast<const f32x4 *>(&sm.xs[b][16 * t + 4 * g]);
 #pragma unroll
-                for (int t = 0; t < 4; t++)
-                    a[u][t] = *reinterpret_cast<const long *>(arow[t] + (int64_t)b * QB);
+                for (int i = 0; i < 4; i++)
+                    acc[t][i] = __builtin_fmaf((float)isum[i], sw * sx[i], acc[t][i]);
             }
-        };
-        long afrag[2][GEMM_AB][4];
-        load_a(afrag[0], 0);
-        if (p0 > 0)
-            __syncthreads();  // the previous pass is done with xsT
-        for (int e = threadIdx.x; e < GEMM_PB * GEMM_TM; e += blockDim.x) {
-            const int r = e / GEMM_PB, bb = e % GEMM_PB;
-            xsT[bb][r] = xs[(int64_t)min(rt0 + r, m - 1) * nb + min(p0 + bb, nb - 1)];
+            // one block's fragments live at a time (hoisting every block's
+            // LDS reads above the first MFMA costs registers the staging needs)
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    auto pass = [&](S &st, int p) {
+        if (p > 0)
+            __syncthreads();  // every wave is done with the previous pass's LDS
+        stage(st, p);
         __syncthreads();
-#pragma unroll
-        for (int q0 = 0; q0 < GEMM_WQ; q0 += GEMM_AB) {
-            const int cur = (q0 / GEMM_AB) & 1;
-            if (q0 + GEMM_AB < GEMM_WQ)
-                load_a(afrag[cur ^ 1], q0 + GEMM_AB);
-#pragma unroll
-            for (int u = 0; u < GEMM_AB; u++) {
-                const int q = q0 + u;
-                const int bb = wid + GEMM_NW * q;  // block within the pass
-                if (p0 + bb < nb) {
-#pragma unroll
-                    for (int t = 0; t < 4; t++) {
-                        v4i isum = __builtin_amdgcn_mfma_i32_16x16x32_i8(afrag[cur][u][t], bfrag[q],
-                                                                         v4i{0, 0, 0, 0}, 0, 0, 0);
-                        const f32x4 sx = *reinterpret_cast<const f32x4 *>(&xsT[bb][16 * t + 4 * g]);
-#pragma unroll
-                        for (int i = 0; i < 4; i++)
-                            acc[t][i] = __builtin_fmaf((float)isum[i], wsc[q] * sx[i], acc[t][i]);
-                    }
-                }
-            }
-        }
+        if (p + 2 < np)
+            issue(st, p + 2);
+        contract();
+    };
+
+    S st0, st1;
+    issue(st0, 0);
+    if (np > 1)
+        issue(st1, 1);
+    for (int p = 0; p < np; p += 2) {
+        pass(st0, p);
+        if (p + 1 < np)
+            pass(st1, p + 1);
     }
+
+    // the waves' partials, summed in wave order
 #pragma unroll
-    for (int t = 0; t < 4; t++)
+    for (int t = 0; t < MT; t++)
 #pragma unroll
         for (int i = 0; i < 4; i++)
-            red[wid][16 * t + 4 * g + i][j] = acc[t][i];
+            sm.part[wid][16 * t + 4 * g + i][j] = acc[t][i];
     __syncthreads();
-    for (int e = threadIdx.x; e < GEMM_TM * GEMM_TN; e += blockDim.x) {
+    for (int e = tid; e < TM * GEMM_TN; e += GEMM_NW * WAVE) {
         const int r = e / GEMM_TN, c = e % GEMM_TN;
-        float v = red[0][r][c];
+        float v = sm.part[0][r][c];
 #pragma unroll
         for (int w = 1; w < GEMM_NW; w++)
-            v += red[w][r][c];
-        if (rt0 + r < m && o0 + c < n_out)
-            y[(int64_t)(rt0 + r) * n_out + o0 + c] = v;
+            v += sm.part[w][r][c];
+        if (r0 + r < m && o0 + c < n_out)
+            y[(int64_t)(r0 + r) * n_out + o0 + c] = v;
     }
 }
 
@@ -423,9 +497,19 @@ hipError_t launch_act(const GemvArgs &a, const SliceShape &sh, hipStream_t st)
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t st)
 {
     if (a.act == 1 && a.m >= GEMM_MIN_ROWS) {
-        dim3 grid((unsigned)((a.n_out + GEMM_TN - 1) / GEMM_TN), (unsigned)((a.m + GEMM_TM - 1) / GEMM_TM));
-        hipLaunchKernelGGL(k_gemm_i8, grid, dim3(GEMM_NW * 64), 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
-                           (int)a.m, a.y);
+        // row tiles of 16 rows for m <= 16, else of 32 (64-row tiles would
+        // spill registers; two 32-row tiles of the same weights run on one
+        // XCD, blockIdx.y apart by a multiple of 8 workgroups when n_out is a
+        // multiple of 128, so the second read of the weights can hit its L2)
+        const int mt = a.m <= 16 ? 1 : 2;
+        const dim3 grid((unsigned)((a.n_out + GEMM_TN - 1) / GEMM_TN), (unsigned)((a.m + 16 * mt - 1) / (16 * mt)));
+        const dim3 block(GEMM_NW * WAVE);
+        if (mt == 1)
+            hipLaunchKernelGGL(k_gemm_i8<1>, grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
+                               (int)a.m, a.y);
+        else
+            hipLaunchKernelGGL(k_gemm_i8<2>, grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
+                               (int)a.m, a.y);
         return hipGetLastError();
     }
     const SliceShape sh = slice_shape(a.n_in);

@@ -70,6 +70,9 @@ def test_gemv_f32_fill_closed_form_exact():
 GEMV_I8_CASES = [
     (4096, 2048, 1), (512, 256, 1), (97, 160, 2), (130, 768, 4), (19, 14336, 1),
     (100, 2048, 5), (4096, 2048, 64), (77, 96, 16), (33, 512, 65), (16, 4096, 130),
+    # matrix-core path with an odd number of 32-block passes, the last one
+    # short (65 blocks: three passes; 97 blocks: four)
+    (50, 2080, 24), (40, 3104, 9),
 ]
 
 
