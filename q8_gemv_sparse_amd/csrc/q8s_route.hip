@@ -11,6 +11,8 @@
 //             in quarters, so the whole router streams from HBM across ~E
 //             workgroups.  Products and sums are in double, so near-equal
 //             logits are ranked as the double-precision definition ranks them.
+//             From 16 rows up, k_logits_tile: one workgroup per 4 experts x 8
+//             rows, reading each row from cache once for several products.
 //   k_topk    one workgroup per row: the K best by (logit descending, index
 //             ascending) -- for E <= 256 a coarse count over order-preserving
 //             32-bit keys picks the candidates and an exact double-precision
@@ -77,6 +79,86 @@ __global__ void __launch_bounds__(RT_THREADS) k_logits(const float *__restrict__
     if (threadIdx.x < RT && r0 + (int)threadIdx.x < rows) {
         const int r = threadIdx.x;
         logits[(int64_t)(r0 + r) * E + e] = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+    }
+}
+
+// The 32 sums v[0..31] of a wave, reduced across its 64 lanes together: each
+// exchange halves the values a lane keeps (xor 32, xor 16, then the 16-, 8-
+// and 4-lane mirrors, whose partners differ in lane bits 3, 2 and 1), so lane
+// l ends with the whole wave's sum of v[(l >> 1) & 31], and its neighbour
+// l ^ 1 with the same.  Every index is summed by the same tree of additions.
+Q8S_DEV double wave_sum32_d(const double (&v)[32], int lane)
+{
+    double w16[16], w8[8], w4[4], w2[2];
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+        w16[i] = (b5 ? v[i + 16] : v[i]) + __shfl_xor(b5 ? v[i] : v[i + 16], 32);
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+        w8[i] = (b4 ? w16[i + 8] : w16[i]) + __shfl_xor(b4 ? w16[i] : w16[i + 8], 16);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        w4[i] = (b3 ? w8[i + 4] : w8[i]) + dpp_d<DPP_MIRROR>(b3 ? w8[i] : w8[i + 4]);
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+        w2[i] = (b2 ? w4[i + 2] : w4[i]) + dpp_d<DPP_HALF_MIRROR>(b2 ? w4[i] : w4[i + 2]);
+    const double w = (b1 ? w2[1] : w2[0]) + dpp_d<DPP_XOR2>(b1 ? w2[0] : w2[1]);
+    return w + dpp_d<DPP_XOR1>(w);
+}
+
+// Many rows (a chunk): one workgroup per tile of LG_E experts x LG_R rows, so
+// each router row and activation row it reads from cache serves 8 or 4 dot
+// products.  A thread takes 8 consecutive values of d per 2048 and keeps the
+// 32 products' running sums (double); the sums meet through wave_sum32_d and
+// LDS, waves added in order.
+constexpr int LG_E = 4, LG_R = 8;
+constexpr int64_t LG_MIN_ROWS = 16;
+
+__global__ void __launch_bounds__(RT_THREADS) k_logits_tile(const float *__restrict__ x, const float *__restrict__ Wr,
+                                                            int rows, int d, int E, double *__restrict__ logits)
+{
+    __shared__ double part[RT_WAVES][LG_E * LG_R];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int e0 = blockIdx.x * LG_E, r0 = blockIdx.y * LG_R;
+    double acc[LG_E * LG_R];  // [e][r]
+#pragma unroll
+    for (int i = 0; i < LG_E * LG_R; i++)
+        acc[i] = 0.0;
+    // d is a multiple of 32, so a thread's 8 values lie inside the row
+    for (int k = threadIdx.x * 8; k < d; k += RT_THREADS * 8) {
+        f32x4 w[LG_E][2], xv[LG_R][2];
+#pragma unroll
+        for (int e = 0; e < LG_E; e++) {
+            const float *wp = Wr + (int64_t)min(e0 + e, E - 1) * d + k;
+            w[e][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wp));
+            w[e][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(wp + 4));
+        }
+#pragma unroll
+        for (int r = 0; r < LG_R; r++) {
+            const float *xp = x + (int64_t)min(r0 + r, rows - 1) * d + k;
+            xv[r][0] = ldf4(xp);
+            xv[r][1] = ldf4(xp + 4);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int e = 0; e < LG_E; e++) {
+                const double we = (double)w[e][i >> 2][i & 3];
+#pragma unroll
+                for (int r = 0; r < LG_R; r++)
+                    acc[e * LG_R + r] += we * (double)xv[r][i >> 2][i & 3];
+            }
+    }
+    const double v = wave_sum32_d(acc, lane);
+    if ((lane & 1) == 0)
+        part[wid][(lane >> 1) & 31] = v;
+    __syncthreads();
+    if (threadIdx.x < LG_E * LG_R) {
+        const int e = threadIdx.x / LG_R, r = threadIdx.x % LG_R;
+        if (e0 + e < E && r0 + r < rows)
+            logits[(int64_t)(r0 + r) * E + e0 + e] =
+                ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) + part[3][threadIdx.x];
     }
 }
 
@@ -222,9 +304,13 @@ hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d
                         float *wts, void *scratch, hipStream_t st)
 {
     double *logits = reinterpret_cast<double *>(scratch);
+    static_assert(LG_E * LG_R == 32 && RT_WAVES == 4, "k_logits_tile reduces 32 sums over four waves");
     if (rows == 1)
         hipLaunchKernelGGL((k_logits<1>), dim3((unsigned)E, 1), dim3(RT_THREADS), 0, st, x, Wr, (int)rows, (int)d,
                            (int)E, logits);
+    else if (rows >= LG_MIN_ROWS)
+        hipLaunchKernelGGL(k_logits_tile, dim3((unsigned)((E + LG_E - 1) / LG_E), (unsigned)((rows + LG_R - 1) / LG_R)),
+                           dim3(RT_THREADS), 0, st, x, Wr, (int)rows, (int)d, (int)E, logits);
     else
         hipLaunchKernelGGL((k_logits<4>), dim3((unsigned)E, (unsigned)((rows + 3) / 4)), dim3(RT_THREADS), 0, st, x,
                            Wr, (int)rows, (int)d, (int)E, logits);

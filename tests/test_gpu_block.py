@@ -62,7 +62,9 @@ def check(b, act, got):
 BLOCK_CASES = [
     # (d, dff, E, k, rows): which launches run is noted
     (2048, 768, 128, 8, 1),     # the 128-expert decode block: fused launches
-    (4096, 14336, 8, 2, 1),     # the 8-expert decode block: fused, int8 rows in 2 slices
+    (4096, 14336, 8, 2, 1),     # the 8-expert decode block: fused, int8 rows in 4 slices
+    (2080, 4096, 4, 4, 1),      # int8 rows of 130 chunks: 3 slices, the last of 2 chunks
+    (1056, 8320, 3, 2, 1),      # 520 gate-up tiles, rows of 66 chunks
     (96, 160, 5, 3, 1),         # ragged: lane groups of 16, tiles past dff
     (2080, 96, 7, 2, 1),        # a partial second 2048-value segment in the fused norm
     (256, 64, 5, 5, 1),         # K = E

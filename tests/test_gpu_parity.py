@@ -206,6 +206,10 @@ ROUTE_CASES = [
     (2, 128, 300, 1),    # E not a multiple of the workgroup's 4 experts
     (1, 256, 8192, 32),  # the limits
     (7, 32, 40, 32),
+    # from 16 rows up the logits run as 4-expert x 8-row tiles: ragged rows
+    # and experts, rows shorter than the 2048 values a pass covers, and rows
+    # of two passes, the second one short
+    (16, 64, 6, 2), (37, 4096, 130, 8), (20, 2080, 9, 3),
 ]
 
 
@@ -239,6 +243,22 @@ def test_route_ties_and_zero_router():
     Wr[5] = x[0] / 16
     idx, _ = q8.moe_route_topk(dev(x[:1]), dev(Wr), 3)
     assert list(host(idx)[0]) == [1, 3, 5]
+
+
+def test_route_ties_many_rows():
+    # the tiled logits: experts 1 and 3 share a router row (equal logits in
+    # every row, ranked by index) and expert 5's row is exactly half of it
+    banner("route ties, 24 rows")
+    d = 160
+    rng = np.random.default_rng(8)
+    x = np.abs(synthetic.normal(rng, 24, d)).astype(np.float32)
+    Wr = np.zeros((7, d), np.float32)
+    Wr[1] = Wr[3] = np.abs(synthetic.normal(rng, d)) / 8
+    Wr[5] = Wr[1] / 2
+    idx, wts = q8.moe_route_topk(dev(x), dev(Wr), 3)
+    assert (host(idx) == np.array([1, 3, 5])).all()
+    _, rw, _ = oracle.route(x, Wr, 3)
+    assert rel_err(host(wts), rw) <= TOL_F32
 
 
 def test_route_scratch_reuse():
