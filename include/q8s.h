@@ -386,6 +386,22 @@ Q8S_API const char *q8s_last_error(void);
 /* The library's version string. */
 Q8S_API const char *q8s_version(void);
 
+/*
+ * q8s_stream_read -- the read ceiling the weight streams are measured
+ * against.  Every kernel above is bound by the bytes of its weight rows, so a
+ * caller timing them can state each one's bandwidth as a fraction of what the
+ * plainest reader reaches on the same device.  This call reads `bytes` of
+ * device memory at `buf` once, in 16-byte non-temporal loads spread over
+ * Q8S_STREAM_WGS workgroups (each a contiguous span, its lanes on
+ * consecutive chunks, eight loads in flight a lane), and reduces them (xor of 32-bit words) to one word
+ * per workgroup in `out`, so no load can be dropped.  It computes nothing of
+ * the method.
+ * buf: device, 16-byte aligned, `bytes` a positive multiple of 16; out:
+ * device uint32 [Q8S_STREAM_WGS], owned by the caller, disjoint from buf.
+ */
+#define Q8S_STREAM_WGS 2048
+Q8S_API int q8s_stream_read(const void *buf, int64_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ __all__ = [
     "add_rmsnorm_gemv", "moe_route_topk_q8", "add_rmsnorm_router_q8", "moe_ffn_block_ex",
     "moe_topk_gate_up_ex", "moe_down_combine_ex",
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
-    "q8s_version", "library",
+    "q8s_version", "q8s_stream_read", "STREAM_WGS", "library",
 ]
 
 ACT_F32 = 0
@@ -32,6 +32,7 @@ ACT_INT8 = 1
 FN_ROUTE = 1
 FN_DOWN = 2
 FN_BLOCK = 3
+STREAM_WGS = 2048  # Q8S_STREAM_WGS: words q8s_stream_read writes
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8s.so")
 
@@ -66,6 +67,7 @@ _SIGS = {
     "moe_down_combine_ex": [_p] * 7 + [_i64, _p, _p] + [_i64] * 5 + [_p, ctypes.c_int, _p],
     "q8s_scratch_bytes": [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
     "q8s_block_scratch_bytes": [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
+    "q8s_stream_read": [_p, _i64, _p, _p],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -104,6 +106,25 @@ def q8s_scratch_bytes(fn, rows, d, dff, E, k, act=ACT_F32):
 
 def q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act=ACT_F32):
     return int(_lib.q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act))
+
+
+def q8s_stream_read(buf, out=None, nbytes=None, stream=None):
+    """Reads ``nbytes`` (default: all) of the device tensor ``buf`` once with
+    the library's plain streaming reader, writing one uint32 word per
+    workgroup into ``out`` (int32 [STREAM_WGS]); returns ``out``.  A
+    measuring stick, not part of the method."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous device tensor")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    if n > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if out is None:
+        out = torch.empty(STREAM_WGS, dtype=torch.int32, device=buf.device)
+    out = _dev(out, torch.int32, "out")
+    if out.numel() < STREAM_WGS:
+        raise ValueError("out must hold STREAM_WGS words")
+    _check(_lib.q8s_stream_read(buf.data_ptr(), n, out.data_ptr(), _stream(stream)))
+    return out
 
 
 def _check(rc):

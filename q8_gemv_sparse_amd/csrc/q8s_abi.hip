@@ -140,6 +140,21 @@ const char *q8s_last_error(void) { return g_err.c_str(); }
 
 const char *q8s_version(void) { return "q8s 0.1 gfx950"; }
 
+int q8s_stream_read(const void *buf, int64_t bytes, uint32_t *out, void *stream)
+{
+    const char *fn = "q8s_stream_read";
+    if (bytes <= 0 || bytes % 16 != 0)
+        return fail(Q8S_EINVAL, "%s: `bytes` = %lld is not a positive multiple of 16 (whole 16-byte loads)", fn,
+                    (long long)bytes);
+    std::vector<Span> ins = {{buf, (size_t)bytes, "buf"}};
+    std::vector<Span> outs = {{out, (size_t)Q8S_STREAM_WGS * 4, "out"}};
+    int rc;
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::stream_read_launch(buf, bytes, out, as_stream(stream)), fn);
+}
+
 size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
 {
     if (rows <= 0 || E <= 0 || k <= 0 || d <= 0)

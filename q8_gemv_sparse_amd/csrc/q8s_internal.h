@@ -78,6 +78,7 @@ bool norm_gemv_supported(int64_t rows, int64_t d);
 hipError_t norm_gemv_launch(const NormGemvArgs &a, hipStream_t st);
 
 hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st);
+hipError_t stream_read_launch(const void *buf, int64_t bytes, uint32_t *out, hipStream_t st);
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               float *sum, float *y, int8_t *yq, float *ys, hipStream_t st);
 // The router's rows: float32 Wr [E, d], or Q8_0 Wrq [E, d] + Wrs [E, d/32]

@@ -306,3 +306,11 @@ def test_shared_stage_refusals():
     assert dn(Sdq=None) == -1 and "`Sdq` is null" in _err()
     assert dn(y=0x31000000) == -1 and "overlaps input `Sdq`" in _err()
     assert dn(act=1) == -1 and "`hq` is null" in _err()
+
+
+def test_stream_read_refusals():
+    assert LIB.q8s_stream_read(A, 0, B, None) == -1 and "multiple of 16" in _err()
+    assert LIB.q8s_stream_read(A, 40, B, None) == -1 and "multiple of 16" in _err()
+    assert LIB.q8s_stream_read(None, 64, B, None) == -1 and "`buf` is null" in _err()
+    assert LIB.q8s_stream_read(A + 4, 64, B, None) == -3
+    assert LIB.q8s_stream_read(A, 1 << 20, A + 4096, None) == -1 and "overlaps" in _err()
