@@ -116,6 +116,8 @@ def parse():
     p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     p.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    p.add_argument("--ceiling-only", action="store_true",
+                   help="measure only the streaming-read ceiling (2 GiB and the default workload's gate-up bytes)")
     p.add_argument("--no-graph", action="store_true",
                    help="launch every step eagerly instead of replaying a captured graph (for counter runs, which "
                         "profile each dispatch)")
@@ -721,6 +723,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.ceiling_only:
+        import q8_gemv_sparse_amd as q8
+        stream = torch.cuda.Stream()
+        print(json.dumps({"ceiling": stream_ceiling(torch, q8, stream, 28311552, args.no_graph)}), flush=True)
+        return
     wl = make_workload(args.workload, args.act, args.copies, args.separate)
     ver = wl.verify()
     ver["ok"] = bool(ver.get("idx_equal", True) and ver["max_rel_err"] <= ver["tol"] and
