@@ -12,6 +12,9 @@ counterpart follows (see the header of q8s_oracle.c):
 * ``quantize``   Q, llama.cpp's one-word Q8_0 activation (enum Q8MatKind)
 * ``block_dots`` the exact int32 block sums of the int8 mode
 * ``gemv_i8``    I, one-word int8 activations
+* ``quantize_x2`` Q2, the two-word (~14-bit) activation (CudaKnobs `activations`;
+  arena.rs fn quant_parts: words, low words, one scale a block)
+* ``gemv_i8x2``  I2, two-word int8 activations (two exact block dots a block)
 * ``add_rmsnorm``  N, forward_shim.rs module doc (add_norm)
 * ``route``      R, fn emit_moe_forward (softmax, keep K, renormalise)
 * ``moe``        M, fn emit_moe_forward / struct MoeWeights
@@ -43,6 +46,8 @@ def _load():
     lib.oracle_quantize.argtypes = [_p, _i64, _i64, _p, _p]
     lib.oracle_block_dots.argtypes = [_p, _i64, _i64, _p, _i64, _p]
     lib.oracle_gemv_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p]
+    lib.oracle_quantize_x2.argtypes = [_p, _i64, _i64, _p, _p, _p]
+    lib.oracle_gemv_i8x2.argtypes = [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p]
     lib.oracle_add_rmsnorm.argtypes = [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p]
     lib.oracle_route.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p]
     lib.oracle_route_q8.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p]
@@ -111,6 +116,32 @@ def gemv_i8(Wq, Ws, xq, xs):
     assert xq.shape[1] == n_in and xs.shape == (xq.shape[0], n_in // 32)
     y = np.empty((xq.shape[0], n_out), np.float64)
     _load().oracle_gemv_i8(_ptr(Wq), _ptr(Ws), n_out, n_in, _ptr(xq), _ptr(xs), xq.shape[0], _ptr(y))
+    return y
+
+
+def quantize_x2(v):
+    """Two-word quantise rows of v[rows, n]: returns (q int8 [rows, n], lo int8
+    [rows, n], d f32 [rows, n/32]), v ~= d * (q + lo/128) per block."""
+    v = _c(np.atleast_2d(v), np.float32)
+    rows, n = v.shape
+    assert n % 32 == 0
+    q = np.empty((rows, n), np.int8)
+    lo = np.empty((rows, n), np.int8)
+    d = np.empty((rows, n // 32), np.float32)
+    _load().oracle_quantize_x2(_ptr(v), rows, n, _ptr(q), _ptr(lo), _ptr(d))
+    return q, lo, d
+
+
+def gemv_i8x2(Wq, Ws, xq, xl, xs):
+    """y[m, n_out] (float64) of the two-word int8 mode from quantised rows."""
+    Wq = _c(Wq, np.int8); Ws = _c(Ws, np.float32)
+    xq = _c(np.atleast_2d(xq), np.int8); xl = _c(np.atleast_2d(xl), np.int8)
+    xs = _c(np.atleast_2d(xs), np.float32)
+    n_out, n_in = Wq.shape
+    _check_q8(Wq, Ws, n_in)
+    assert xq.shape[1] == n_in and xl.shape == xq.shape and xs.shape == (xq.shape[0], n_in // 32)
+    y = np.empty((xq.shape[0], n_out), np.float64)
+    _load().oracle_gemv_i8x2(_ptr(Wq), _ptr(Ws), n_out, n_in, _ptr(xq), _ptr(xl), _ptr(xs), xq.shape[0], _ptr(y))
     return y
 
 

@@ -43,6 +43,12 @@
  *                quantised activation is int8 words plus one f32 scale a
  *                32-value block; the decode mixture keeps its hidden row
  *                quantised (hq/hs) in one-word int8 mode.
+ *   [two_word]   codegen_cuda/lane/mod.rs module doc (CudaKnobs
+ *                `activations`: a two-word ~14-bit int8 activation) and
+ *                arena.rs fn scratch / fn quant_parts / fn array_bytes: under
+ *                two words a quantised activation is its words, its low words
+ *                and one f32 scale a block; fn moe_dp4a_kernels' two-pass
+ *                (logit-exact) trio.
  *
  * Readings taken where the pages are silent (each is listed with its reason
  * in the project's design notes):
@@ -55,6 +61,8 @@
  *   - a shared expert is added to the mixture's weighted sum with weight 1 (no
  *     gate of its own; the pages decompose a router/shared-gate merge), after
  *     it; a Q8_0 router under one-word int8 numerics reads the quantised row;
+ *   - the two-word activation's low word is the rest of v*id after the word,
+ *     in 128ths of a step, rounded half away from zero: v ~= d*(q + lo/128);
  *   - SiLU(z) = z / (1 + exp(-z)); the hidden row h = SiLU(g) * u is held as a
  *     float32 tensor between the gate-up and the down projection (and, in int8
  *     mode, quantised per 32-value block of each expert's row).
@@ -158,6 +166,70 @@ void oracle_gemv_i8(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_
                 for (int t = 0; t < QBLOCK; t++)
                     s += (int32_t)Wq[o * n_in + b * QBLOCK + t] * (int32_t)xq[r * n_in + b * QBLOCK + t];
                 acc += ((double)Ws[o * nb + b] * (double)xs[r * nb + b]) * (double)s;
+            }
+            y[r * n_out + o] = acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * Q2 -- the two-word (~14-bit) int8 activation [two_word]: per 32-value block
+ * its words, its low words and one f32 scale.  The words are Q's codes (same
+ * d, same id); the low word holds the rest of v*id in 128ths of one step:
+ *   p  = v * id                       (float32, as in Q)
+ *   q  = Q's code of v
+ *   lo = clamp(round_half_away_from_zero((p - q) * 128), -127, 127)
+ * so v ~= d * (q + lo/128).  |p - q| <= 1/2, so |lo| <= 64 and the clamp never
+ * binds; p - q is exact (Sterbenz) and the factor 128 a power of two, so lo is
+ * the nearest 128th of p - q.  The factor is a reading: the pages print the
+ * two words and the one scale, not the low word's weight.
+ */
+void oracle_quantize_x2(const float *v, int64_t rows, int64_t n, int8_t *q, int8_t *lo, float *d)
+{
+    int64_t nb = n / QBLOCK;
+    oracle_quantize(v, rows, n, q, d);
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < nb; b++) {
+            float dsc = d[r * nb + b];
+            float id = (dsc != 0.0f) ? 1.0f / dsc : 0.0f;
+            for (int t = 0; t < QBLOCK; t++) {
+                int64_t i = r * n + b * QBLOCK + t;
+                float p = v[i] * id;
+                float rest = (p - (float)q[i]) * 128.0f;
+                float rl = roundf(rest);
+                if (rl > 127.0f)
+                    rl = 127.0f;
+                if (rl < -127.0f)
+                    rl = -127.0f;
+                lo[i] = (int8_t)rl;
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------
+ * I2 -- Q8_0 GEMV with two-word int8 activations [two_word]: two exact int32
+ * block dots a block, one against the words and one against the low words,
+ *   y[r][o] = sum_b (Ws[o][b] * xs[r][b]) * (isum_hi[b] + isum_lo[b] / 128)
+ * the block dots exact in int32, the scaling and the sum over blocks in
+ * double (isum_hi + isum_lo/128 is exact in double).
+ */
+void oracle_gemv_i8x2(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in, const int8_t *xq,
+                      const int8_t *xl, const float *xs, int64_t m, double *y)
+{
+    int64_t nb = n_in / QBLOCK;
+    for (int64_t r = 0; r < m; r++) {
+        for (int64_t o = 0; o < n_out; o++) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; b++) {
+                int32_t sh = 0, sl = 0;
+                for (int t = 0; t < QBLOCK; t++) {
+                    int32_t w = (int32_t)Wq[o * n_in + b * QBLOCK + t];
+                    sh += w * (int32_t)xq[r * n_in + b * QBLOCK + t];
+                    sl += w * (int32_t)xl[r * n_in + b * QBLOCK + t];
+                }
+                double blk = (double)sh + (double)sl / 128.0;
+                acc += ((double)Ws[o * nb + b] * (double)xs[r * nb + b]) * blk;
             }
             y[r * n_out + o] = acc;
         }

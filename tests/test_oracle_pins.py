@@ -221,6 +221,134 @@ def test_gemv_i8_within_quantisation_bound_of_f32_mode():
 
 
 # ---------------------------------------------------------------------------
+# Q2 and I2: the two-word (~14-bit) activation and its GEMV.  The pages give
+# the words, the low words and one scale a block (arena.rs fn quant_parts);
+# the low word's weight of 1/128 of a step is the reading pinned here.
+
+
+def _low_word_brute_force(p, q):
+    """Of the 255 low words -127..127, the one whose lo/128 is nearest to the
+    exact rest p - q, ties away from zero."""
+    rest = Fraction(float(p)) - q
+    best = None
+    for c in range(-127, 128):
+        dist = abs(Fraction(c, 128) - rest)
+        if best is None or dist < best[0] or (dist == best[0] and abs(c) > abs(best[1])):
+            best = (dist, c)
+    return best[1]
+
+
+def test_quantize_x2_words_and_scales_are_one_word():
+    rng = np.random.default_rng(41)
+    v = synthetic.normal(rng, 4, 128)
+    q, lo, d = oracle.quantize_x2(v)
+    q1, d1 = oracle.quantize(v)
+    assert np.array_equal(q, q1) and np.array_equal(d, d1)
+
+
+def test_quantize_x2_low_words_brute_force():
+    rng = np.random.default_rng(42)
+    v = np.concatenate([synthetic.normal(rng, 2, 64), 1e-3 * synthetic.normal(rng, 1, 64)], axis=0)
+    q, lo, d = oracle.quantize_x2(v)
+    assert np.max(np.abs(lo.astype(int))) <= 64
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            idv = np.float32(1.0) / d[r, b] if d[r, b] != 0 else np.float32(0.0)
+            for t in range(b * 32, b * 32 + 32):
+                p = np.float32(v[r, t]) * np.float32(idv)
+                assert lo[r, t] == _low_word_brute_force(p, int(q[r, t])), (r, t)
+
+
+def test_quantize_x2_closed_forms():
+    # amax 127 gives d = 1, id = 1: the rest after the word is exact
+    blk = np.zeros(32, np.float32)
+    vals = [127.0, 3.25, -2.75, 2.5, -2.5, 0.75, 1.0 + 1.0 / 256, -1.0 / 512, 5.0 + 63.0 / 128]
+    blk[:len(vals)] = vals
+    q, lo, d = oracle.quantize_x2(blk[None, :])
+    assert d[0, 0] == 1.0
+    assert list(q[0, :len(vals)]) == [127, 3, -3, 3, -3, 1, 1, 0, 5]
+    assert list(lo[0, :len(vals)]) == [0, 32, 32, -64, 64, -32, 1, 0, 63]
+    # a zero block: scale, words and low words all zero
+    q, lo, d = oracle.quantize_x2(np.zeros((1, 32), np.float32))
+    assert d[0, 0] == 0.0 and not q.any() and not lo.any()
+
+
+def test_quantize_x2_reconstruction_bound():
+    rng = np.random.default_rng(43)
+    v = synthetic.normal(rng, 8, 256).astype(np.float64)
+    q, lo, d = oracle.quantize_x2(v.astype(np.float32))
+    dd = np.repeat(d.astype(np.float64), 32, axis=1)
+    back = dd * (q.astype(np.float64) + lo.astype(np.float64) / 128.0)
+    # half a 128th of a step, plus the float32 rounding of v * id
+    assert np.all(np.abs(back - v) <= dd / 256.0 + np.abs(v) * 2.0 ** -22)
+    q1, d1 = oracle.quantize(v.astype(np.float32))
+    err1 = np.abs(q1.astype(np.float64) * dd - v)
+    assert np.mean(np.abs(back - v)) < np.mean(err1) / 32.0
+
+
+def test_gemv_i8x2_matches_exact_rational():
+    rng = np.random.default_rng(44)
+    Wq, Ws = _rand_q8(rng, 4, 96)
+    x = synthetic.normal(rng, 2, 96)
+    xq, xl, xs = oracle.quantize_x2(x)
+    y = oracle.gemv_i8x2(Wq, Ws, xq, xl, xs)
+    for r in range(2):
+        for o in range(4):
+            terms = [Fraction(float(Ws[o, b])) * Fraction(float(xs[r, b])) *
+                     sum(int(Wq[o, t]) * (Fraction(int(xq[r, t])) + Fraction(int(xl[r, t]), 128))
+                         for t in range(32 * b, 32 * b + 32)) for b in range(3)]
+            exact = sum(terms, Fraction(0))
+            mag = float(sum(abs(t) for t in terms))
+            assert abs(Fraction(y[r, o]) - exact) <= Fraction(8 * mag) * Fraction(2) ** -52
+
+
+def test_gemv_i8x2_without_low_words_is_one_word():
+    rng = np.random.default_rng(45)
+    Wq, Ws = _rand_q8(rng, 16, 128)
+    xq, xs = oracle.quantize(synthetic.normal(rng, 3, 128))
+    y1 = oracle.gemv_i8(Wq, Ws, xq, xs)
+    y2 = oracle.gemv_i8x2(Wq, Ws, xq, np.zeros_like(xq), xs)
+    assert np.array_equal(y1, y2)
+
+
+def test_gemv_i8x2_equals_f32_mode_on_exact_rows():
+    # rows that the two words represent exactly: power-of-two block scales,
+    # one word of 127 a block (so the block's amax gives back its scale), low
+    # words of at most 63 (so the word is the rounding of the value)
+    rng = np.random.default_rng(46)
+    m, n = 3, 160
+    q = rng.integers(-126, 127, size=(m, n)).astype(np.int64)
+    lo = rng.integers(-63, 64, size=(m, n)).astype(np.int64)
+    q[:, ::32] = 127
+    lo[:, ::32] = 0
+    d = (2.0 ** rng.integers(-9, -2, size=(m, n // 32))).astype(np.float32)
+    x = (np.repeat(d.astype(np.float64), 32, axis=1) * (q + lo / 128.0)).astype(np.float32)
+    xq, xl, xs = oracle.quantize_x2(x)
+    assert np.array_equal(xs, d) and np.array_equal(xq, q.astype(np.int8)) and np.array_equal(xl, lo.astype(np.int8))
+    Wq, Ws = _rand_q8(rng, 24, n)
+    y2 = oracle.gemv_i8x2(Wq, Ws, xq, xl, xs)
+    yf = oracle.gemv_f32(Wq, Ws, x)
+    assert np.max(np.abs(y2 - yf)) <= 1e-12 * np.max(np.abs(yf))
+
+
+def test_gemv_i8x2_within_quantisation_bound_of_f32_mode():
+    rng = np.random.default_rng(47)
+    Wq, Ws = _rand_q8(rng, 64, 256)
+    x = synthetic.normal(rng, 2, 256)
+    xq, xl, xs = oracle.quantize_x2(x)
+    y2 = oracle.gemv_i8x2(Wq, Ws, xq, xl, xs)
+    yf = oracle.gemv_f32(Wq, Ws, x)
+    Wabs = np.abs(Wq.astype(np.float64)) * np.repeat(Ws.astype(np.float64), 32, axis=1)
+    step = np.repeat(xs.astype(np.float64), 32, axis=1) / 256.0 + np.abs(x.astype(np.float64)) * 2.0 ** -22
+    bound = Wabs @ step.T
+    assert np.all(np.abs(y2 - yf) <= bound.T + 1e-12)
+    # and far inside the one-word bound
+    xq1, xs1 = oracle.quantize(x)
+    y1 = oracle.gemv_i8(Wq, Ws, xq1, xs1)
+    assert np.max(np.abs(y2 - yf)) < np.max(np.abs(y1 - yf)) / 16.0
+
+
+# ---------------------------------------------------------------------------
 # N: residual add + RMSNorm
 
 
