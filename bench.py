@@ -110,7 +110,8 @@ def parse():
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default="moe_d2048_dff768_e128_k8")
-    p.add_argument("--act", choices=["int8", "f32"], default="int8")
+    p.add_argument("--act", choices=["int8", "f32", "x2"], default="int8",
+                   help="activation numerics: one-word int8, float32, or two-word int8 (norm + GEMV workload)")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough to defeat the MALL)")
     p.add_argument("--kernel-launches", type=int, default=400, help="eager launches timed for the dominant kernel")
     p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
@@ -372,8 +373,9 @@ class NormGemv(Workload):
         import synthetic
         self.q8, self.torch, self.np = q8, torch, np
         self.name, self.act = name, act
-        self.separate = separate
-        self.dominant = "k_gemv_rows" if separate else "k_norm_gemv"
+        # two words: add_rmsnorm_q8 (float32 row) -> q8_quantize_rows_x2 -> q8_gemv_x2
+        self.separate = separate or act == "x2"
+        self.dominant = "k_gemv_rows" if self.separate else "k_norm_gemv"
         d, n_out = cfg["d"], cfg["n_out"]
         self.d, self.n_out = d, n_out
         inp = synthetic.norm_gemv_inputs(0, d, n_out, rows=1)
@@ -393,6 +395,7 @@ class NormGemv(Workload):
         z = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device="cuda")
         self.sum, self.y = z(1, d), z(1, d)
         self.xq, self.xs = z(1, d, dt=torch.int8), z(1, d // 32)
+        self.xl = z(1, d, dt=torch.int8)
         self.out = z(1, n_out)
         self.wbytes = wbytes
         torch.cuda.synchronize()
@@ -407,8 +410,12 @@ class NormGemv(Workload):
                                 y=None if a else self.y, yq=self.xq if a else None, ys=self.xs if a else None,
                                 out=self.out)
             return
+        x2 = self.act == "x2"
         q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y,
-                          yq=self.xq if a else None, ys=self.xs if a else None, want_q8=bool(a))
+                          yq=self.xq if a and not x2 else None, ys=self.xs if a and not x2 else None,
+                          want_q8=bool(a) and not x2)
+        if x2:
+            q8.q8_quantize_rows_x2(self.y, xq=self.xq, xl=self.xl, xs=self.xs)
         self.launch_dominant(c)
 
     def launch_dominant(self, c):
@@ -417,7 +424,9 @@ class NormGemv(Workload):
             self.step(c)  # the step is the one fused launch
             return
         W = self.W[c % self.copies]
-        if self.act == "int8":
+        if self.act == "x2":
+            q8.q8_gemv_x2(W[0], W[1], self.xq, self.xl, self.xs, y=self.out)
+        elif self.act == "int8":
             q8.q8_gemv(W[0], W[1], xq=self.xq, xs=self.xs, y=self.out, act=q8.ACT_INT8)
         else:
             q8.q8_gemv(W[0], W[1], x=self.y, y=self.out, act=q8.ACT_F32)
@@ -435,7 +444,10 @@ class NormGemv(Workload):
         self.torch.cuda.synchronize()
         s, y64 = oracle.add_rmsnorm(self.pool_h[0], self.pool_r[0], self.inp.w, 1e-6)
         x = y64.astype(np.float32)
-        if self.act == "int8":
+        if self.act == "x2":
+            q, lo, sc = oracle.quantize_x2(x)
+            ref = oracle.gemv_i8x2(self.inp.Wq, self.inp.Ws, q, lo, sc)
+        elif self.act == "int8":
             q, sc = oracle.quantize(x)
             ref = oracle.gemv_i8(self.inp.Wq, self.inp.Ws, q, sc)
         else:
@@ -452,7 +464,10 @@ class NormGemv(Workload):
             i = n % self.pool
             s, y64 = oracle.add_rmsnorm(self.pool_h[i], self.pool_r[i], self.inp.w, 1e-6)
             x = y64.astype(np.float32)
-            if self.act == "int8":
+            if self.act == "x2":
+                q, lo, sc = oracle.quantize_x2(x)
+                oracle.gemv_i8x2(self.inp.Wq, self.inp.Ws, q, lo, sc)
+            elif self.act == "int8":
                 q, sc = oracle.quantize(x)
                 oracle.gemv_i8(self.inp.Wq, self.inp.Ws, q, sc)
             else:
@@ -647,6 +662,8 @@ class MoeSharedBlock(MoeBlock):
 def make_workload(name, act, copies, separate=False):
     import synthetic
     cfg = synthetic.CONFIGS[name]
+    if act == "x2" and cfg["kind"] != "norm_gemv":
+        raise SystemExit("two-word activations are built for the Q8_0 GEMV only (--workload norm_gemv_2048x4096)")
     if cfg["kind"] == "moe":
         return MoeBlock(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "norm_gemv":
@@ -865,7 +882,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8" if args.act == "int8" else "f32",
+        "dtype": {"int8": "i8", "x2": "i8x2", "f32": "f32"}[args.act],
         "data": "synthetic",
         "config": {
             "workload": wl.name,

@@ -43,7 +43,9 @@
  *     failure returns Q8S_ELAUNCH with the HIP error string.
  *   - `act` picks the activation numerics (enum Q8MatKind): Q8S_ACT_F32 reads
  *     f32 activations; Q8S_ACT_INT8 reads one-word Q8_0 activations and forms
- *     exact int32 dots per 32-value block.
+ *     exact int32 dots per 32-value block.  The two-word activation (act 2)
+ *     has entry points of its own, q8_quantize_rows_x2 and q8_gemv_x2; every
+ *     other call refuses act 2.
  *   - Expert choices (idx) are read on the device.  An index outside [0, E)
  *     is never dereferenced: that choice contributes zero.
  */
@@ -109,6 +111,33 @@ Q8S_API int q8_gemv(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_
  * [rows, n/32].
  */
 Q8S_API int q8_quantize_rows(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, void *stream);
+
+/*
+ * q8_quantize_rows_x2 -- the two-word (~14-bit) int8 activation (the lane's
+ * default numerics, codegen_cuda/lane/mod.rs module doc, CudaKnobs
+ * `activations`; arena.rs fn quant_parts: a quantised array's words, its low
+ * words, one f32 scale a block).  Per 32-value block, in float32:
+ *   d, id and the words q exactly as q8_quantize_rows;
+ *   lo = clamp(round-half-away((v*id - q) * 128), -127, 127)
+ * so v ~= d * (q + lo/128).  The low word's weight of 1/128 of a step is a
+ * reading: the pages print the two words and the one scale, not that weight.
+ * x: device f32 [rows, n]; xq, xl: device int8 [rows, n]; xs: device f32
+ * [rows, n/32].  Limits as q8_quantize_rows.
+ */
+Q8S_API int q8_quantize_rows_x2(const float *x, int64_t rows, int64_t n, int8_t *xq, int8_t *xl, float *xs,
+                                void *stream);
+
+/*
+ * q8_gemv_x2 -- the Q8_0 GEMV with two-word int8 activations (fn
+ * moe_dp4a_kernels' two-pass, logit-exact numerics): two exact int32 block
+ * dots a block, one against the words and one against the low words,
+ *   y[r][o] = sum_b Ws[o][b] * xs[r][b] * (isum_hi[b] + isum_lo[b] / 128)
+ * Wq/Ws as q8_gemv; xq/xl/xs as q8_quantize_rows_x2 writes them, m rows;
+ * y: device f32 [m, n_out].  Every m runs on the vector units.  Limits as
+ * q8_gemv.
+ */
+Q8S_API int q8_gemv_x2(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in, const int8_t *xq,
+                       const int8_t *xl, const float *xs, int64_t m, float *y, void *stream);
 
 /*
  * add_rmsnorm_q8 -- residual add + weighted RMSNorm as one row kernel that

@@ -24,7 +24,7 @@ __all__ = [
     "add_rmsnorm_gemv", "moe_route_topk_q8", "add_rmsnorm_router_q8", "moe_ffn_block_ex",
     "moe_topk_gate_up_ex", "moe_down_combine_ex",
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
-    "q8s_version", "q8s_stream_read", "STREAM_WGS", "library",
+    "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
 ]
 
 ACT_F32 = 0
@@ -68,6 +68,8 @@ _SIGS = {
     "q8s_scratch_bytes": [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
     "q8s_block_scratch_bytes": [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
     "q8s_stream_read": [_p, _i64, _p, _p],
+    "q8_quantize_rows_x2": [_p, _i64, _i64, _p, _p, _p, _p],
+    "q8_gemv_x2": [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -183,6 +185,37 @@ def q8_quantize_rows(x, xq=None, xs=None, stream=None):
     _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
     _check(_lib.q8_quantize_rows(_ptr(x), rows, n, _ptr(xq), _ptr(xs), _stream(stream)))
     return xq, xs
+
+
+def q8_quantize_rows_x2(x, xq=None, xl=None, xs=None, stream=None):
+    """Two-word Q8_0 form of x[rows, n]: returns (xq, xl, xs), the words, the
+    low words and the block scales, x ~= xs * (xq + xl/128) per block."""
+    _dev(x, torch.float32, "x")
+    rows, n = x.shape
+    if xq is None:
+        xq = torch.empty((rows, n), dtype=torch.int8, device=x.device)
+    if xl is None:
+        xl = torch.empty((rows, n), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((rows, n // 32), dtype=torch.float32, device=x.device)
+    _dev(xq, torch.int8, "xq"); _dev(xl, torch.int8, "xl"); _dev(xs, torch.float32, "xs")
+    _check(_lib.q8_quantize_rows_x2(x.data_ptr(), rows, n, xq.data_ptr(), xl.data_ptr(), xs.data_ptr(),
+                                    _stream(stream)))
+    return xq, xl, xs
+
+
+def q8_gemv_x2(Wq, Ws, xq, xl, xs, y=None, stream=None):
+    """y[m, n_out] = Q8_0 W times two-word int8 rows (xq, xl, xs)."""
+    _dev(Wq, torch.int8, "Wq"); _dev(Ws, torch.float32, "Ws")
+    _dev(xq, torch.int8, "xq"); _dev(xl, torch.int8, "xl"); _dev(xs, torch.float32, "xs")
+    n_out, n_in = Wq.shape
+    m = xq.shape[0]
+    if y is None:
+        y = torch.empty((m, n_out), dtype=torch.float32, device=Wq.device)
+    _dev(y, torch.float32, "y")
+    _check(_lib.q8_gemv_x2(Wq.data_ptr(), Ws.data_ptr(), n_out, n_in, xq.data_ptr(), xl.data_ptr(), xs.data_ptr(),
+                           m, y.data_ptr(), _stream(stream)))
+    return y
 
 
 def add_rmsnorm_q8(h, r, w, eps, sum=None, y=None, yq=None, ys=None, want_f32=True, want_q8=True, stream=None):

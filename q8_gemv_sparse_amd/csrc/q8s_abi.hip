@@ -108,7 +108,8 @@ int check_act(const char *fn, int act)
     if (act == Q8S_ACT_F32 || act == Q8S_ACT_INT8)
         return 0;
     if (act == 2)
-        return fail(Q8S_EUNSUPPORTED, "%s: act = 2 (two-word int8 activations) is not implemented", fn);
+        return fail(Q8S_EUNSUPPORTED,
+                    "%s: act = 2 (two-word int8 activations) is served by q8_quantize_rows_x2 and q8_gemv_x2 only", fn);
     return fail(Q8S_EUNSUPPORTED, "%s: unknown activation mode act = %d", fn, act);
 }
 
@@ -215,6 +216,41 @@ int q8_quantize_rows(const float *x, int64_t rows, int64_t n, int8_t *xq, float 
         return rc;
     clear_stale();
     return launched(q8s::quantize_launch(x, rows, n, xq, xs, as_stream(stream)), fn);
+}
+
+int q8_quantize_rows_x2(const float *x, int64_t rows, int64_t n, int8_t *xq, int8_t *xl, float *xs, void *stream)
+{
+    const char *fn = "q8_quantize_rows_x2";
+    int rc;
+    if ((rc = check_count(fn, "rows", rows, 65535)) || (rc = check_dim32(fn, "n", n)))
+        return rc;
+    std::vector<Span> ins = {{x, (size_t)(rows * n) * 4, "x"}};
+    std::vector<Span> outs = {{xq, (size_t)(rows * n), "xq"}, {xl, (size_t)(rows * n), "xl"},
+                              {xs, (size_t)(rows * n / 32) * 4, "xs"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::quantize_x2_launch(x, rows, n, xq, xl, xs, as_stream(stream)), fn);
+}
+
+int q8_gemv_x2(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in, const int8_t *xq, const int8_t *xl,
+               const float *xs, int64_t m, float *y, void *stream)
+{
+    const char *fn = "q8_gemv_x2";
+    int rc;
+    if ((rc = check_dim32(fn, "n_in", n_in)) || (rc = check_count(fn, "n_out", n_out, INT32_MAX / 2)) ||
+        (rc = check_count(fn, "m", m, 65535)))
+        return rc;
+    const size_t nb = (size_t)(n_in / 32);
+    std::vector<Span> ins = {{Wq, (size_t)(n_out * n_in), "Wq"}, {Ws, (size_t)n_out * nb * 4, "Ws"},
+                             {xq, (size_t)(m * n_in), "xq"}, {xl, (size_t)(m * n_in), "xl"},
+                             {xs, (size_t)m * nb * 4, "xs"}};
+    std::vector<Span> outs = {{y, (size_t)(m * n_out) * 4, "y"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::GemvArgs a{Wq, Ws, n_out, n_in, nullptr, xq, xs, m, y, 2, xl};
+    clear_stale();
+    return launched(q8s::gemv_launch(a, as_stream(stream)), fn);
 }
 
 int add_rmsnorm_q8(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps, float *sum,

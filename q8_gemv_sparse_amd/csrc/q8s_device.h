@@ -136,6 +136,18 @@ Q8S_DEV int q8_code(float v, float id)
     return (int)r;
 }
 
+// The two-word activation's low word: the rest of v*id after the word q, in
+// 128ths of a step, rounded half away from zero (v ~= d * (q + lo/128)).
+// p - q is exact and 128 a power of two, so lo is the nearest 128th of the
+// rest; |p - q| <= 1/2 keeps |lo| <= 64 (the clamp never binds).
+Q8S_DEV int q8_low(float v, float id, int q)
+{
+    float p = v * id;
+    float r = roundf((p - (float)q) * 128.0f);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int)r;
+}
+
 // Quantise 8 consecutive values held by one thread of a 4-thread group that
 // owns one 32-value block (the group's lanes are neighbours within a quad):
 // the 8 codes packed in two words, and the block scale.
@@ -169,6 +181,25 @@ Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool lea
         *scale = d;
 }
 
+// quant8 in two words: the same words and scale, plus the 8 low words.
+Q8S_DEV void quant8x2_store(const float (&v)[8], int8_t *q, int8_t *lo, float *scale, bool leader)
+{
+    float d;
+    const uint2 w = quant8(v, d);
+    *reinterpret_cast<uint2 *>(q) = w;
+    const float id = q8_inv(d);
+    uint32_t l0 = 0, l1 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int q0 = (int)(int8_t)((w.x >> (8 * i)) & 0xFF), q1 = (int)(int8_t)((w.y >> (8 * i)) & 0xFF);
+        l0 |= (uint32_t)(q8_low(v[i], id, q0) & 0xFF) << (8 * i);
+        l1 |= (uint32_t)(q8_low(v[4 + i], id, q1) & 0xFF) << (8 * i);
+    }
+    *reinterpret_cast<uint2 *>(lo) = make_uint2(l0, l1);
+    if (leader)
+        *scale = d;
+}
+
 // ---------------------------------------------------------------------------
 // a lane's share of one row: C chunks of 16 bytes plus their block scales
 
@@ -189,6 +220,13 @@ struct XSlice<0, C> {
 template <int C>
 struct XSlice<1, C> {
     i32x4 q[C];
+    float s[C];
+};
+// two-word int8: the words, the low words, one scale a block
+template <int C>
+struct XSlice<2, C> {
+    i32x4 q[C];
+    i32x4 l[C];
     float s[C];
 };
 
@@ -259,6 +297,25 @@ Q8S_DEV void load_x(XSlice<1, C> &x, const float *, const int8_t *__restrict__ x
             x.s[c] = xs[(ch0 + ch) >> 1];
         } else {
             x.q[c] = i32x4{0, 0, 0, 0};
+            x.s[c] = 0.0f;
+        }
+    }
+}
+
+template <int LPR, int C>
+Q8S_DEV void load_x2(XSlice<2, C> &x, const int8_t *__restrict__ xq, const int8_t *__restrict__ xl,
+                     const float *__restrict__ xs, int ch0, int nch, int lig)
+{
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        int ch = c * LPR + lig;
+        if (ch < nch) {
+            x.q[c] = ld16(xq + (int64_t)(ch0 + ch) * 16);
+            x.l[c] = ld16(xl + (int64_t)(ch0 + ch) * 16);
+            x.s[c] = xs[(ch0 + ch) >> 1];
+        } else {
+            x.q[c] = i32x4{0, 0, 0, 0};
+            x.l[c] = i32x4{0, 0, 0, 0};
             x.s[c] = 0.0f;
         }
     }
@@ -398,6 +455,22 @@ Q8S_DEV float row_dot(const RowSlice<C> &w, const XSlice<1, C> &x, int lig)
         int half = chunk_dot_i8(w.q[c], x.q[c]);
         int blk = half + dpp_i<DPP_XOR1>(half);
         float f = (float)blk * (w.s[c] * x.s[c]);
+        acc += (lig & 1) ? 0.0f : f;
+    }
+    return acc;
+}
+
+// two words: the block's two exact dots joined as one int32,
+// 128*isum_hi + isum_lo (|.| < 2^27), scaled by ws*xs/128
+template <int C>
+Q8S_DEV float row_dot(const RowSlice<C> &w, const XSlice<2, C> &x, int lig)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; c++) {
+        const int half = chunk_dot_i8(w.q[c], x.q[c]) * 128 + chunk_dot_i8(w.q[c], x.l[c]);
+        const int blk = half + dpp_i<DPP_XOR1>(half);
+        const float f = (float)blk * ((w.s[c] * x.s[c]) * 0.0078125f);
         acc += (lig & 1) ? 0.0f : f;
     }
     return acc;

@@ -6,9 +6,10 @@
 //                 rows against it (no launch waits for a norm launch).
 //   k_gemv_rows   the streaming GEMV for batch 1 and small m: weights stream
 //                 from HBM once, every activation row a wave serves sits in
-//                 its registers.  f32 activations (dequantise in kernel) or
+//                 its registers.  f32 activations (dequantise in kernel),
 //                 one-word int8 activations (v_dot4_i32_i8, exact int32 block
-//                 sums).  Rows longer than one wave's slice are cut along k
+//                 sums) or two-word ones (two exact block dots a block, the
+//                 low word's weighed 1/128).  Rows longer than one wave's slice are cut along k
 //                 across the waves of a workgroup and joined through LDS in a
 //                 fixed order.
 //   k_gemm_i8     int8 activations with many rows: v_mfma_i32_16x16x32_i8,
@@ -41,7 +42,7 @@ template <int ACT, int LPR, int C, int MR, int U, bool SPLIT>
 __global__ void __launch_bounds__(SPLIT ? 512 : 256) k_gemv_rows(const int8_t *__restrict__ Wq, const float *__restrict__ Ws,
                                                     int n_out, int n_in, const float *__restrict__ x,
                                                     const int8_t *__restrict__ xq, const float *__restrict__ xs, int m,
-                                                    float *__restrict__ y)
+                                                    float *__restrict__ y, const int8_t *__restrict__ xl)
 {
     constexpr int G = WAVE / LPR;
     constexpr int RB = G * U;
@@ -61,9 +62,13 @@ __global__ void __launch_bounds__(SPLIT ? 512 : 256) k_gemv_rows(const int8_t *_
 #pragma unroll
         for (int r = 0; r < MR; r++) {
             const int rr = min(r0 + r, m - 1);
-            load_x<LPR, C>(xv[r], ACT == 0 ? x + (int64_t)rr * n_in : nullptr,
-                           ACT == 1 ? xq + (int64_t)rr * n_in : nullptr, ACT == 1 ? xs + (int64_t)rr * nb : nullptr,
-                           ch0, sl, lig);
+            if constexpr (ACT == 2)
+                load_x2<LPR, C>(xv[r], xq + (int64_t)rr * n_in, xl + (int64_t)rr * n_in, xs + (int64_t)rr * nb, ch0,
+                                sl, lig);
+            else
+                load_x<LPR, C>(xv[r], ACT == 0 ? x + (int64_t)rr * n_in : nullptr,
+                               ACT == 1 ? xq + (int64_t)rr * n_in : nullptr, ACT == 1 ? xs + (int64_t)rr * nb : nullptr,
+                               ch0, sl, lig);
         }
     };
     if (!SPLIT || s < ks)
@@ -451,7 +456,7 @@ hipError_t launch_rows(const GemvArgs &a, int ks, hipStream_t st)
         grid = dim3((unsigned)std::min<int64_t>((nrb + 3) / 4, 16384), (unsigned)((a.m + MR - 1) / MR));
     }
     hipLaunchKernelGGL((k_gemv_rows<ACT, LPR, C, MR, U, SPLIT>), grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out,
-                       (int)a.n_in, a.x, a.xq, a.xs, (int)a.m, a.y);
+                       (int)a.n_in, a.x, a.xq, a.xs, (int)a.m, a.y, a.xl);
     return hipGetLastError();
 }
 
@@ -461,7 +466,7 @@ hipError_t launch_rows(const GemvArgs &a, int ks, hipStream_t st)
 template <int ACT, int C, bool SPLIT>
 constexpr int mr_max()
 {
-    return ACT == 1 ? 4 : (SPLIT ? 1 : (C <= 2 ? 4 : 2));
+    return ACT >= 1 ? 4 : (SPLIT ? 1 : (C <= 2 ? 4 : 2));
 }
 
 template <int ACT, int LPR, int C, bool SPLIT>
@@ -513,6 +518,9 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t st)
         return hipGetLastError();
     }
     const SliceShape sh = slice_shape(a.n_in);
+    // two words: the vector units at every m (two int8 dots a block)
+    if (a.act == 2)
+        return launch_act<2>(a, sh, st);
     return a.act == 0 ? launch_act<0>(a, sh, st) : launch_act<1>(a, sh, st);
 }
 

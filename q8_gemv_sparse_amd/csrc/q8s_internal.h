@@ -58,7 +58,8 @@ struct GemvArgs {
     const float *xs;
     int64_t m;
     float *y;
-    int act;
+    int act;             // 0 f32, 1 one-word int8, 2 two-word int8
+    const int8_t *xl;    // two words: the low words
 };
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t st);
 
@@ -78,6 +79,8 @@ bool norm_gemv_supported(int64_t rows, int64_t d);
 hipError_t norm_gemv_launch(const NormGemvArgs &a, hipStream_t st);
 
 hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st);
+hipError_t quantize_x2_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, int8_t *xl, float *xs,
+                              hipStream_t st);
 hipError_t stream_read_launch(const void *buf, int64_t bytes, uint32_t *out, hipStream_t st);
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               float *sum, float *y, int8_t *yq, float *ys, hipStream_t st);

@@ -213,10 +213,35 @@ __global__ void __launch_bounds__(NORM_THREADS) k_quantize_rows(const float *__r
     quant8_store(v, xq + row * n + base, xs + row * (n / QB) + base / QB, (threadIdx.x & 3) == 0);
 }
 
+// q8_quantize_rows_x2: the two-word form, the same grid (words and scales
+// equal k_quantize_rows', plus the low words).
+__global__ void __launch_bounds__(NORM_THREADS) k_quantize_rows_x2(const float *__restrict__ x, int64_t n,
+                                                                   int8_t *__restrict__ xq, int8_t *__restrict__ xl,
+                                                                   float *__restrict__ xs)
+{
+    const int64_t row = blockIdx.y;
+    const int64_t base = (int64_t)blockIdx.x * NORM_SEG + threadIdx.x * 8;
+    if (base >= n)
+        return;  // whole 4-thread groups leave together: n is a multiple of 32
+    const float *p = x + row * n + base;
+    const f32x4 a0 = ldf4(p), a1 = ldf4(p + 4);
+    const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    quant8x2_store(v, xq + row * n + base, xl + row * n + base, xs + row * (n / QB) + base / QB,
+                   (threadIdx.x & 3) == 0);
+}
+
 hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st)
 {
     dim3 grid((unsigned)((n + NORM_SEG - 1) / NORM_SEG), (unsigned)rows);
     hipLaunchKernelGGL(k_quantize_rows, grid, dim3(NORM_THREADS), 0, st, x, n, xq, xs);
+    return hipGetLastError();
+}
+
+hipError_t quantize_x2_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, int8_t *xl, float *xs,
+                              hipStream_t st)
+{
+    dim3 grid((unsigned)((n + NORM_SEG - 1) / NORM_SEG), (unsigned)rows);
+    hipLaunchKernelGGL(k_quantize_rows_x2, grid, dim3(NORM_THREADS), 0, st, x, n, xq, xl, xs);
     return hipGetLastError();
 }
 

@@ -314,3 +314,20 @@ def test_stream_read_refusals():
     assert LIB.q8s_stream_read(None, 64, B, None) == -1 and "`buf` is null" in _err()
     assert LIB.q8s_stream_read(A + 4, 64, B, None) == -3
     assert LIB.q8s_stream_read(A, 1 << 20, A + 4096, None) == -1 and "overlaps" in _err()
+
+
+def test_two_word_refusals():
+    # the quantiser: whole blocks, disjoint outputs
+    assert LIB.q8_quantize_rows_x2(A, 2, 40, B, C, D, None) == -1 and "multiple of 32" in _err()
+    assert LIB.q8_quantize_rows_x2(A, 2, 64, B, B + 64, D, None) == -1 and "overlap" in _err()
+    assert LIB.q8_quantize_rows_x2(A, 2, 64, B, None, D, None) == -1 and "`xl` is null" in _err()
+    # the GEMV: every array present and aligned, whole blocks
+    gemv2 = lambda n_out=64, n_in=64, m=1, xq=D, xl=F, xs=G, y=H: LIB.q8_gemv_x2(A, B, n_out, n_in, xq, xl, xs, m, y,
+                                                                                 None)
+    assert gemv2(xl=None) == -1 and "`xl` is null" in _err()
+    assert gemv2(n_in=48) == -1 and "multiple of 32" in _err()
+    assert gemv2(m=0) == -1
+    assert gemv2(xq=D + 8) == -3
+    assert gemv2(y=F + 16) == -1 and "overlaps input `xl`" in _err()
+    # the one-word entry points name the two-word ones
+    assert gemv(act=2) == -2 and "q8_gemv_x2" in _err()
