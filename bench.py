@@ -359,8 +359,9 @@ class MoeBlock(Workload):
 
 class NormGemv(Workload):
     """The residual add + RMSNorm feeding the 2048 -> 4096 batch-1 projection:
-    one add_rmsnorm_gemv call a step (one launch); with separate=True the two
-    calls add_rmsnorm_q8 -> q8_gemv."""
+    one add_rmsnorm_gemv call a step (one launch; add_rmsnorm_gemv_x2 in
+    two-word numerics); with separate=True the calls add_rmsnorm_q8 ->
+    q8_gemv (two words: add_rmsnorm_q8 -> q8_quantize_rows_x2 -> q8_gemv_x2)."""
 
     dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h",
                     "q8_gemv_sparse_amd/csrc/q8s_norm_row.h")
@@ -373,8 +374,9 @@ class NormGemv(Workload):
         import synthetic
         self.q8, self.torch, self.np = q8, torch, np
         self.name, self.act = name, act
-        # two words: add_rmsnorm_q8 (float32 row) -> q8_quantize_rows_x2 -> q8_gemv_x2
-        self.separate = separate or act == "x2"
+        # two words: add_rmsnorm_gemv_x2 (one launch), or with separate=True
+        # add_rmsnorm_q8 (float32 row) -> q8_quantize_rows_x2 -> q8_gemv_x2
+        self.separate = separate
         self.dominant = "k_gemv_rows" if self.separate else "k_norm_gemv"
         d, n_out = cfg["d"], cfg["n_out"]
         self.d, self.n_out = d, n_out
@@ -404,6 +406,11 @@ class NormGemv(Workload):
         q8 = self.q8
         i = c % self.pool
         a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        if not self.separate and self.act == "x2":
+            W = self.W[c % self.copies]
+            q8.add_rmsnorm_gemv_x2(self.h[i], self.r[i], self.w, 1e-6, W[0], W[1], sum=self.sum, y=self.y,
+                                   yq=self.xq, yl=self.xl, ys=self.xs, out=self.out)
+            return
         if not self.separate:
             W = self.W[c % self.copies]
             q8.add_rmsnorm_gemv(self.h[i], self.r[i], self.w, 1e-6, W[0], W[1], act=a, sum=self.sum,

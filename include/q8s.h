@@ -236,6 +236,22 @@ Q8S_API int add_rmsnorm_gemv(const float *h, const float *r, const float *w, flo
                      float *sum, float *y, int8_t *yq, float *ys, float *out, int act, void *stream);
 
 /*
+ * add_rmsnorm_gemv_x2 -- add_rmsnorm_gemv in two-word int8 numerics: sum and
+ * y exactly as add_rmsnorm_q8 writes them, (yq, yl, ys) the two-word form of
+ * y as q8_quantize_rows_x2 writes it, and
+ *   out[r] = Q8_0(Wq, Ws) . X2(y[r])         (as q8_gemv_x2)
+ * For one row of d <= 4096 it is one launch: every workgroup forms the normed
+ * row's two-word form in LDS while its weight rows stream in.  Otherwise it
+ * runs add_rmsnorm_q8, q8_quantize_rows_x2 and q8_gemv_x2.  Every output is
+ * required: sum, y: device f32 [rows, d]; yq, yl: device int8 [rows, d]; ys:
+ * device f32 [rows, d/32]; out: device f32 [rows, n_out].  Other arguments
+ * and limits as add_rmsnorm_gemv.
+ */
+Q8S_API int add_rmsnorm_gemv_x2(const float *h, const float *r, const float *w, float eps, const int8_t *Wq,
+                                const float *Ws, int64_t rows, int64_t d, int64_t n_out, float *sum, float *y,
+                                int8_t *yq, int8_t *yl, float *ys, float *out, void *stream);
+
+/*
  * add_rmsnorm_router -- add_rmsnorm_q8 with the mixture's router fused in
  * (forward_shim.rs module doc: the norm as one row kernel writing the sum;
  * fn emit_moe_forward: the router over the normed row):

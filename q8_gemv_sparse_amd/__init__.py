@@ -25,6 +25,7 @@ __all__ = [
     "moe_topk_gate_up_ex", "moe_down_combine_ex",
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
+    "add_rmsnorm_gemv_x2",
 ]
 
 ACT_F32 = 0
@@ -70,6 +71,7 @@ _SIGS = {
     "q8s_stream_read": [_p, _i64, _p, _p],
     "q8_quantize_rows_x2": [_p, _i64, _i64, _p, _p, _p, _p],
     "q8_gemv_x2": [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p],
+    "add_rmsnorm_gemv_x2": [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -216,6 +218,27 @@ def q8_gemv_x2(Wq, Ws, xq, xl, xs, y=None, stream=None):
     _check(_lib.q8_gemv_x2(Wq.data_ptr(), Ws.data_ptr(), n_out, n_in, xq.data_ptr(), xl.data_ptr(), xs.data_ptr(),
                            m, y.data_ptr(), _stream(stream)))
     return y
+
+
+def add_rmsnorm_gemv_x2(h, r, w, eps, Wq, Ws, sum=None, y=None, yq=None, yl=None, ys=None, out=None, stream=None):
+    """add_rmsnorm_q8 feeding q8_gemv_x2 (one launch for one row of d <=
+    4096).  Returns (sum, y, yq, yl, ys, out)."""
+    for t, n in ((h, "h"), (r, "r"), (w, "w"), (Ws, "Ws")):
+        _dev(t, torch.float32, n)
+    _dev(Wq, torch.int8, "Wq")
+    rows, d = h.shape
+    n_out = Wq.shape[0]
+    f = lambda t, shape, dt: t if t is not None else torch.empty(shape, dtype=dt, device=h.device)
+    sum = f(sum, (rows, d), torch.float32); y = f(y, (rows, d), torch.float32)
+    yq = f(yq, (rows, d), torch.int8); yl = f(yl, (rows, d), torch.int8)
+    ys = f(ys, (rows, d // 32), torch.float32); out = f(out, (rows, n_out), torch.float32)
+    for t, n, dt in ((sum, "sum", torch.float32), (y, "y", torch.float32), (yq, "yq", torch.int8),
+                     (yl, "yl", torch.int8), (ys, "ys", torch.float32), (out, "out", torch.float32)):
+        _dev(t, dt, n)
+    _check(_lib.add_rmsnorm_gemv_x2(h.data_ptr(), r.data_ptr(), w.data_ptr(), eps, Wq.data_ptr(), Ws.data_ptr(), rows,
+                                    d, n_out, sum.data_ptr(), y.data_ptr(), yq.data_ptr(), yl.data_ptr(),
+                                    ys.data_ptr(), out.data_ptr(), _stream(stream)))
+    return sum, y, yq, yl, ys, out
 
 
 def add_rmsnorm_q8(h, r, w, eps, sum=None, y=None, yq=None, ys=None, want_f32=True, want_q8=True, stream=None):

@@ -489,6 +489,43 @@ int add_rmsnorm_gemv(const float *h, const float *r, const float *w, float eps, 
     return launched(e, fn);
 }
 
+int add_rmsnorm_gemv_x2(const float *h, const float *r, const float *w, float eps, const int8_t *Wq,
+                        const float *Ws, int64_t rows, int64_t d, int64_t n_out, float *sum, float *y, int8_t *yq,
+                        int8_t *yl, float *ys, float *out, void *stream)
+{
+    const char *fn = "add_rmsnorm_gemv_x2";
+    int rc;
+    if ((rc = check_count(fn, "rows", rows, 65535)) || (rc = check_dim32(fn, "d", d)) ||
+        (rc = check_count(fn, "n_out", n_out, INT32_MAX / 2)))
+        return rc;
+    if (!(eps >= 0.0f) || eps != eps)
+        return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    const size_t n = (size_t)(rows * d);
+    std::vector<Span> ins = {{h, n * 4, "h"},
+                             {r, n * 4, "r"},
+                             {w, (size_t)d * 4, "w"},
+                             {Wq, (size_t)(n_out * d), "Wq"},
+                             {Ws, (size_t)n_out * (size_t)(d / 32) * 4, "Ws"}};
+    std::vector<Span> outs = {{sum, n * 4, "sum"}, {out, (size_t)(rows * n_out) * 4, "out"}, {y, n * 4, "y"},
+                              {yq, n, "yq"}, {yl, n, "yl"}, {ys, n / 32 * 4, "ys"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    const hipStream_t st = as_stream(stream);
+    if (q8s::norm_gemv_supported(rows, d)) {
+        q8s::NormGemvArgs a{h, r, w, eps, Wq, Ws, d, n_out, sum, y, yq, ys, out, 2, yl};
+        return launched(q8s::norm_gemv_launch(a, st), fn);
+    }
+    hipError_t e = q8s::add_rmsnorm_launch(h, r, w, rows, d, eps, sum, y, nullptr, nullptr, st);
+    if (e == hipSuccess)
+        e = q8s::quantize_x2_launch(y, rows, d, yq, yl, ys, st);
+    if (e == hipSuccess) {
+        q8s::GemvArgs g{Wq, Ws, n_out, d, nullptr, yq, ys, rows, out, 2, yl};
+        e = q8s::gemv_launch(g, st);
+    }
+    return launched(e, fn);
+}
+
 namespace {
 
 int norm_router_common(const char *fn, const float *h, const float *r, const float *w, float eps,

@@ -151,15 +151,16 @@ __global__ void __launch_bounds__(NORM_THREADS)
     k_norm_gemv(const float *__restrict__ h, const float *__restrict__ r, const float *__restrict__ w, int d,
                 float eps, const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out,
                 float *__restrict__ sum, float *__restrict__ y, int8_t *__restrict__ yq, float *__restrict__ ys,
-                float *__restrict__ out)
+                float *__restrict__ out, int8_t *__restrict__ yl)
 {
     constexpr int G = WAVE / LPR;
     constexpr int RB = G * U;
     constexpr int NX = NORM_SEG * SEGS;
     __shared__ double wsum[NORM_THREADS / WAVE];
     __shared__ __align__(16) float xf[ACT == 0 ? NX : 4];
-    __shared__ __align__(16) int8_t xqs[ACT == 1 ? NX : 16];
-    __shared__ __align__(16) float xss[ACT == 1 ? NX / QB : 4];
+    __shared__ __align__(16) int8_t xqs[ACT >= 1 ? NX : 16];
+    __shared__ __align__(16) int8_t xls[ACT == 2 ? NX : 16];
+    __shared__ __align__(16) float xss[ACT >= 1 ? NX / QB : 4];
     const int lane = threadIdx.x & 63, lig = lane % LPR, grp = lane / LPR;
     const int wid = threadIdx.x >> 6;
     const int nch = d >> 4, nb = d >> 5;
@@ -198,25 +199,35 @@ __global__ void __launch_bounds__(NORM_THREADS)
         if (base < d) {
             float v[8];
             norm_values(n.sv[g][0], n.sv[g][1], n.wv[g][0], n.wv[g][1], inv, v);
+            const bool lead = (threadIdx.x & 3) == 0;
             if (ACT == 0) {
                 *reinterpret_cast<f32x4 *>(xf + base) = f32x4{v[0], v[1], v[2], v[3]};
                 *reinterpret_cast<f32x4 *>(xf + base + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            } else if (ACT == 1) {
+                quant8_store(v, xqs + base, xss + base / QB, lead);
             } else {
-                quant8_store(v, xqs + base, xss + base / QB, (threadIdx.x & 3) == 0);
+                quant8x2_store(v, xqs + base, xls + base, xss + base / QB, lead);
             }
             if (writer && y) {
                 *reinterpret_cast<f32x4 *>(y + base) = f32x4{v[0], v[1], v[2], v[3]};
                 *reinterpret_cast<f32x4 *>(y + base + 4) = f32x4{v[4], v[5], v[6], v[7]};
             }
-            if (writer && yq)
-                quant8_store(v, yq + base, ys + base / QB, (threadIdx.x & 3) == 0);
+            if (writer && yq) {
+                if (ACT == 2)
+                    quant8x2_store(v, yq + base, yl + base, ys + base / QB, lead);
+                else
+                    quant8_store(v, yq + base, ys + base / QB, lead);
+            }
         }
     }
     __syncthreads();
     if (!rows)
         return;
     XSlice<ACT, C> xv;
-    load_x<LPR, C>(xv, xf, xqs, xss, 0, nch, lig);
+    if constexpr (ACT == 2)
+        load_x2<LPR, C>(xv, xqs, xls, xss, 0, nch, lig);
+    else
+        load_x<LPR, C>(xv, xf, xqs, xss, 0, nch, lig);
 #pragma unroll
     for (int u = 0; u < U; u++) {
         const float a = group_sum<LPR>(row_dot(wr[u], xv, lig));
@@ -540,7 +551,7 @@ hipError_t norm_gemv_go(const NormGemvArgs &a, hipStream_t st)
     const int64_t nrb = (a.n_out + RB - 1) / RB;
     const dim3 grid((unsigned)((nrb + NORM_THREADS / WAVE - 1) / (NORM_THREADS / WAVE)));
     hipLaunchKernelGGL((k_norm_gemv<ACT, LPR, C, SEGS, U>), grid, dim3(NORM_THREADS), 0, st, a.h, a.r, a.w, (int)a.d,
-                       a.eps, a.Wq, a.Ws, (int)a.n_out, a.sum, a.y, a.yq, a.ys, a.out);
+                       a.eps, a.Wq, a.Ws, (int)a.n_out, a.sum, a.y, a.yq, a.ys, a.out, a.yl);
     return hipGetLastError();
 }
 
@@ -568,6 +579,8 @@ hipError_t norm_gemv_shape(const NormGemvArgs &a, hipStream_t st)
 
 hipError_t norm_gemv_launch(const NormGemvArgs &a, hipStream_t st)
 {
+    if (a.act == 2)
+        return norm_gemv_shape<2>(a, st);
     return a.act == 0 ? norm_gemv_shape<0>(a, st) : norm_gemv_shape<1>(a, st);
 }
 

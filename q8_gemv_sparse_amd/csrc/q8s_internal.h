@@ -73,7 +73,8 @@ struct NormGemvArgs {
     float *sum, *y;
     int8_t *yq;
     float *ys, *out;
-    int act;
+    int act;             // 0 f32, 1 one-word int8, 2 two-word int8
+    int8_t *yl;          // two words: the normed row's low words
 };
 bool norm_gemv_supported(int64_t rows, int64_t d);
 hipError_t norm_gemv_launch(const NormGemvArgs &a, hipStream_t st);

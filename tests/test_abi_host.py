@@ -331,3 +331,12 @@ def test_two_word_refusals():
     assert gemv2(y=F + 16) == -1 and "overlaps input `xl`" in _err()
     # the one-word entry points name the two-word ones
     assert gemv(act=2) == -2 and "q8_gemv_x2" in _err()
+
+
+def test_norm_gemv_x2_refusals():
+    f = lambda d=64, yl=J, y=F, eps=1e-6: LIB.add_rmsnorm_gemv_x2(A, B, C, ctypes.c_float(eps), D, 0xF0000000, 1, d,
+                                                                   64, G, y, H, yl, 0xD0000000, 0xB0000000, None)
+    assert f(yl=None) == -1 and "`yl` is null" in _err()
+    assert f(y=None) == -1 and "`y` is null" in _err()
+    assert f(d=40) == -1 and "multiple of 32" in _err()
+    assert f(eps=-1.0) == -1 and "eps" in _err()

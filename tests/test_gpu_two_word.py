@@ -85,3 +85,30 @@ def test_quantize_then_gemv_x2_at_the_norm_gemv_shape():
     yf = oracle.gemv_f32(Wq, Ws, x)
     q1, s1 = oracle.quantize(x)
     assert rel_err(y2, yf) < rel_err(oracle.gemv_i8(Wq, Ws, q1, s1), yf) / 16
+
+
+# (d, n_out, rows): one launch for one row of d <= 4096, else the separate calls
+NORM_CASES = [(2048, 4096, 1), (4096, 1000, 1), (1024, 130, 1), (768, 97, 1), (256, 33, 1), (32, 5, 1),
+              (2080, 64, 1), (2048, 512, 3), (8192, 96, 1)]
+
+
+@pytest.mark.parametrize("d,n_out,rows", NORM_CASES)
+def test_norm_gemv_x2(d, n_out, rows):
+    # against the separate calls bit for bit (the same normed row, its same
+    # two-word form, the same dots), and against the oracle's chain
+    banner("add_rmsnorm_gemv_x2 d=%d n_out=%d rows=%d" % (d, n_out, rows))
+    import torch
+    inp = synthetic.norm_gemv_inputs(40, d, n_out, rows)
+    h, r, w, Wq, Ws = dev(inp.h), dev(inp.r), dev(inp.w), dev(inp.Wq), dev(inp.Ws)
+    s, y, yq, yl, ys, out = q8.add_rmsnorm_gemv_x2(h, r, w, 1e-6, Wq, Ws)
+    s2, y2, _, _ = q8.add_rmsnorm_q8(h, r, w, 1e-6, want_q8=False)
+    q2, l2, d2 = q8.q8_quantize_rows_x2(y2)
+    o2 = q8.q8_gemv_x2(Wq, Ws, q2, l2, d2)
+    for a, b in ((s, s2), (y, y2), (yq, q2), (yl, l2), (ys, d2), (out, o2)):
+        assert torch.equal(a, b)
+    rs, ry = oracle.add_rmsnorm(inp.h, inp.r, inp.w, 1e-6)
+    assert np.array_equal(host(s), rs)
+    ref = oracle.gemv_i8x2(inp.Wq, inp.Ws, *oracle.quantize_x2(ry.astype(np.float32)))
+    got = host(out)
+    for i in range(rows):
+        assert rel_err(got[i], ref[i]) <= TOL, i
