@@ -77,7 +77,7 @@ def summarize_counters(args):
     kernel, srcs = DOMINANT[kind]
     calib = args.calib_copy_mib * 1024  # KiB moved each way by the copy
     run = ("python3 bench.py --workload %s --act %s --no-graph --steps 28 --warmup 14 --kernel-launches 14 "
-           "--no-cpu --calib-copy-mib %d" % (args.workload, args.act, args.calib_copy_mib))
+           "--no-cpu --no-ceiling --calib-copy-mib %d" % (args.workload, args.act, args.calib_copy_mib))
     out = {"kernel": kernel, "workload": args.workload, "act": args.act,
            "source_digest": src_digest(*srcs), "calib_copy_kib": calib,
            "commands": ["rocprofv3 --pmc %s -f csv -d <out> -o run -- %s" % (c, run)
