@@ -361,22 +361,25 @@ int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wr
 
 /* One expert's SwiGLU FFN on one row, for M and MS: gate/up rows gq/gs, uq/us
  * [n, d], down rows dq/ds [d, n]:
- *   g = Wg . x, u = Wu . x                              (G, or I on Q(x))
- *   hj[o] = float32( SiLU(g[o]) * u[o] )                (a float32 tensor)
- *   dn[o'] = Wd[o'] . hj                                (G, or I on Q(hj))
- * act 1 reads the row's Q8_0 form xq/xs. */
-static void expert_ffn(int act, const float *xr, const int8_t *xq, const float *xs, const int8_t *gq,
-                       const float *gs, const int8_t *uq, const float *us, const int8_t *dq, const float *ds,
-                       int64_t d, int64_t n, float *hj, double *dn)
+ *   g = Wg . x, u = Wu . x                    (G, or I on Q(x), or I2 on Q2(x))
+ *   hj[o] = float32( SiLU(g[o]) * u[o] )      (a float32 tensor)
+ *   dn[o'] = Wd[o'] . hj                      (G, or I on Q(hj), or I2 on Q2(hj))
+ * act 1 reads the row's Q8_0 form xq/xs, act 2 its two-word form xq/xl/xs. */
+static void expert_ffn(int act, const float *xr, const int8_t *xq, const int8_t *xl, const float *xs,
+                       const int8_t *gq, const float *gs, const int8_t *uq, const float *us, const int8_t *dq,
+                       const float *ds, int64_t d, int64_t n, float *hj, double *dn)
 {
     double *g = (double *)malloc((size_t)n * sizeof(double));
     double *u = (double *)malloc((size_t)n * sizeof(double));
     if (act == 0) {
         oracle_gemv_f32(gq, gs, n, d, xr, 1, g);
         oracle_gemv_f32(uq, us, n, d, xr, 1, u);
-    } else {
+    } else if (act == 1) {
         oracle_gemv_i8(gq, gs, n, d, xq, xs, 1, g);
         oracle_gemv_i8(uq, us, n, d, xq, xs, 1, u);
+    } else {
+        oracle_gemv_i8x2(gq, gs, n, d, xq, xl, xs, 1, g);
+        oracle_gemv_i8x2(uq, us, n, d, xq, xl, xs, 1, u);
     }
     for (int64_t o = 0; o < n; o++)
         hj[o] = (float)(silu(g[o]) * u[o]);
@@ -384,10 +387,17 @@ static void expert_ffn(int act, const float *xr, const int8_t *xq, const float *
         oracle_gemv_f32(dq, ds, d, n, hj, 1, dn);
     } else {
         int8_t *hq = (int8_t *)malloc((size_t)n);
+        int8_t *hl = (int8_t *)malloc((size_t)n);
         float *hs = (float *)malloc((size_t)(n / QBLOCK) * sizeof(float));
-        oracle_quantize(hj, 1, n, hq, hs);
-        oracle_gemv_i8(dq, ds, d, n, hq, hs, 1, dn);
+        if (act == 1) {
+            oracle_quantize(hj, 1, n, hq, hs);
+            oracle_gemv_i8(dq, ds, d, n, hq, hs, 1, dn);
+        } else {
+            oracle_quantize_x2(hj, 1, n, hq, hl, hs);
+            oracle_gemv_i8x2(dq, ds, d, n, hq, hl, hs, 1, dn);
+        }
         free(hq);
+        free(hl);
         free(hs);
     }
     free(g);
@@ -401,7 +411,8 @@ static void expert_ffn(int act, const float *xr, const int8_t *xq, const float *
  *   y[o'] = sum_{j<K} w[j] * dn[j][o']                  (double, j order)
  * act = 0: f32 activations; act = 1: one-word int8 activations, where x is
  * quantised once per row and each expert's hidden row per 32-value block
- * ([scratch]: hq/hs over K*dff).
+ * ([scratch]: hq/hs over K*dff); act = 2: the same in two words ([two_word]:
+ * Q2 and I2 in place of Q and I).
  * Outputs: idx [rows*k], wts [rows*k] (double), h [rows*k*dff] (float32),
  * y [rows*d] (double).  Returns 0, or -1 for an unknown mode.
  */
@@ -426,7 +437,8 @@ int oracle_moe(int act, const float *x, const float *Wr, const int8_t *Wgq, cons
  *       y[o'] = (sum_{j<K} w[j] * dn[j][o']) + dn_s[o']
  *     its hidden row h_s (float32; Q8_0 per block under act 1) after the K
  *     routed ones.
- * h is [rows, K*dff + sdff].  Returns 0, or -1 for an unknown mode.
+ * h is [rows, K*dff + sdff].  Returns 0, or -1 for an unknown mode (or the
+ * Q8_0 router under two words, which is not built).
  */
 int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wrq, const float *Wrs,
                       const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Wdq,
@@ -434,15 +446,18 @@ int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wr
                       const int8_t *Sdq, const float *Sds, int64_t sdff, int64_t rows, int64_t d, int64_t dff,
                       int64_t E, int64_t k, int32_t *idx, double *wts, float *h, double *y)
 {
-    if (act != 0 && act != 1)
+    if (act < 0 || act > 2 || (act == 2 && Wrq))
         return -1;
     const int64_t nbd = d / QBLOCK, nbf = dff / QBLOCK, hw = k * dff + sdff;
     int8_t *xq = (int8_t *)malloc((size_t)(rows * d));
+    int8_t *xl = (int8_t *)malloc((size_t)(rows * d));
     float *xs = (float *)malloc((size_t)(rows * nbd) * sizeof(float));
     double *dn = (double *)malloc((size_t)d * sizeof(double));
 
     if (act == 1)
         oracle_quantize(x, rows, d, xq, xs);
+    else if (act == 2)
+        oracle_quantize_x2(x, rows, d, xq, xl, xs);
     if (Wrq)
         oracle_route_q8(act, x, xq, xs, Wrq, Wrs, rows, d, E, k, idx, wts, NULL);
     else
@@ -454,20 +469,21 @@ int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wr
             yr[o] = 0.0;
         for (int64_t j = 0; j < k; j++) {
             int64_t e = idx[i * k + j];
-            expert_ffn(act, xr, xq + i * d, xs + i * nbd, Wgq + e * dff * d, Wgs + e * dff * nbd, Wuq + e * dff * d,
+            expert_ffn(act, xr, xq + i * d, xl + i * d, xs + i * nbd, Wgq + e * dff * d, Wgs + e * dff * nbd, Wuq + e * dff * d,
                        Wus + e * dff * nbd, Wdq + e * d * dff, Wds + e * d * nbf, d, dff, h + i * hw + j * dff, dn);
             double wj = wts[i * k + j];
             for (int64_t o = 0; o < d; o++)
                 yr[o] += wj * dn[o];
         }
         if (sdff > 0) {
-            expert_ffn(act, xr, xq + i * d, xs + i * nbd, Sgq, Sgs, Suq, Sus, Sdq, Sds, d, sdff,
+            expert_ffn(act, xr, xq + i * d, xl + i * d, xs + i * nbd, Sgq, Sgs, Suq, Sus, Sdq, Sds, d, sdff,
                        h + i * hw + k * dff, dn);
             for (int64_t o = 0; o < d; o++)
                 yr[o] += dn[o];
         }
     }
     free(xq);
+    free(xl);
     free(xs);
     free(dn);
     return 0;

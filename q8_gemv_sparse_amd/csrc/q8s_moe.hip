@@ -249,13 +249,17 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
 }
 
 // Rows a lane group takes per step of the down-combine (measured: one row a
-// step for lane groups holding 3 or 4 chunks, e.g. 22 vs 23.4 us for the
-// 8-expert block's int8 down projection).
+// step for lane groups of 64 holding 4 chunks, e.g. 22 vs 23.4 us for the
+// 8-expert block's int8 down projection; two for lane groups of 16 holding 3,
+// so a wave's 8 rows of a 768-value hidden row load in one step: 18.25 vs
+// 18.39 us for the 128-expert block).
 template <int ACT, int LPR, int C>
 constexpr int dn_unroll()
 {
     if (ACT == 0)
         return C >= 3 ? 1 : (C == 2 ? 2 : (LPR == 16 ? 2 : 4));
+    if (C == 3 && LPR == 16)
+        return 2;
     return C >= 3 ? 1 : (LPR == 16 ? 2 : 4);
 }
 

@@ -626,7 +626,7 @@ def test_moe_int8_within_bound_of_f32_mode():
 
 def test_moe_chunk_rows_are_independent():
     m = _small_moe(68, E=6, k=2, rows=5)
-    for act in (0, 1):
+    for act in (0, 1, 2):
         idx, wts, h, y = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=act)
         for i in range(5):
             i1, w1, h1, y1 = oracle.moe(m.x[i:i + 1], m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=act)
@@ -636,7 +636,41 @@ def test_moe_chunk_rows_are_independent():
 def test_moe_rejects_unknown_mode():
     m = _small_moe(69, E=2, k=1, rows=1)
     with pytest.raises(AssertionError):
-        oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act=2)
+        oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act=3)
+
+
+def test_moe_x2_gate_up_exact_when_x_is_two_word_exact():
+    # x the two words represent exactly (power-of-two block scales, a word of
+    # 127 in every block, low words within +-63): the two-word mode's hidden
+    # row equals the f32 mode's
+    m = _small_moe(80, d=128, E=4, k=2, rows=1)
+    rng = np.random.default_rng(81)
+    q = rng.integers(-126, 127, size=(1, m.d)).astype(np.int64)
+    lo = rng.integers(-63, 64, size=(1, m.d)).astype(np.int64)
+    q[:, ::32] = 127
+    lo[:, ::32] = 0
+    dd = 2.0 ** rng.integers(-8, -4, size=(1, m.d // 32))
+    x = (np.repeat(dd, 32, axis=1) * (q + lo / 128.0)).astype(np.float32)
+    _, _, hf, _ = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=0)
+    _, _, h2, _ = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=2)
+    assert np.max(np.abs(h2 - hf) / (np.abs(hf) + 1e-30)) <= 2.0 ** -23
+
+
+def test_moe_x2_within_bound_of_f32_mode_and_inside_one_word():
+    m = _small_moe(82, d=128, dff=128, E=4, k=2, rows=2)
+    _, _, _, yf = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=0)
+    _, _, _, y1 = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=1)
+    _, _, _, y2 = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=2)
+    assert np.max(np.abs(y2 - yf)) <= 3e-2 / 64 * np.max(np.abs(yf))
+    assert np.max(np.abs(y2 - yf)) < np.max(np.abs(y1 - yf)) / 16
+
+
+def test_moe_x2_routes_as_f32():
+    # the float router reads the f32 row in every numerics
+    m = _small_moe(83, E=6, k=3, rows=3)
+    i0, w0, _, _ = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 3, act=0)
+    i2, w2, _, _ = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 3, act=2)
+    assert np.array_equal(i0, i2) and np.array_equal(w0, w2)
 
 
 # ---------------------------------------------------------------------------
@@ -656,7 +690,7 @@ def _shared(v):
 
 def test_moe_shared_without_variants_is_moe():
     v, m, x = _variant(71)
-    for act in (0, 1):
+    for act in (0, 1, 2):
         a = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=act)
         b = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act, Wr=m.Wr)
         for u, w in zip(a, b):
