@@ -43,6 +43,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs and effective HBM GB/s per batch-1 MoE FFN block / Q8_0 GEMV (% of peak)"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+ACT_CODE = {"f32": 0, "int8": 1, "x2": 2}  # the library's activation modes
+# the oracle tolerance of each mode's output (two words: one 128th of a
+# one-word code flip, with a margin of 16 flips)
+TOL = {"f32": 1e-5, "int8": 2e-3, "x2": 2.5e-4}
 MALL_BYTES = 256 << 20
 
 
@@ -214,16 +218,18 @@ class MoeBlock(Workload):
         self.sum = z(rows, d)
         self.y = z(rows, d)
         self.xq, self.xs = z(rows, d, dt=torch.int8), z(rows, d // 32)
+        self.xl = z(rows, d, dt=torch.int8)  # two words: the low words of x and of the hidden rows
         self.idx = [z(rows, k, dt=torch.int32) for _ in range(self.copies)]
         self.wts = [z(rows, k) for _ in range(self.copies)]
         self.hf = z(rows, k, dff)
         self.hq, self.hs = z(rows, k, dff, dt=torch.int8), z(rows, k, dff // 32)
+        self.hl = z(rows, k, dff, dt=torch.int8)
         self.out = z(rows, d)
         self.rscratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_ROUTE, rows, d, dff, E, k), dtype=torch.uint8,
                                     device="cuda")
         dn = q8.q8s_scratch_bytes(q8.FN_DOWN, rows, d, dff, E, k)
         self.dscratch = torch.zeros(dn, dtype=torch.uint8, device="cuda") if dn else None
-        a = q8.ACT_INT8 if act == "int8" else q8.ACT_F32
+        a = ACT_CODE[act]
         self.bscratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, a), dtype=torch.uint8,
                                     device="cuda")
         self.logits = [z(rows, E, dt=torch.float64) for _ in range(self.copies)]
@@ -235,7 +241,7 @@ class MoeBlock(Workload):
         q8 = self.q8
         W = self.W[c % self.copies]
         i = c % self.pool
-        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        a = ACT_CODE[self.act]
         idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
         if not self.separate:
             q8.moe_ffn_block(self.h[i], self.r[i], self.w, 1e-6, *W, self.k, act=a, sum=self.sum, idx=idx, wts=wts,
@@ -247,7 +253,7 @@ class MoeBlock(Workload):
     def _norm(self, c):
         q8 = self.q8
         i = c % self.pool
-        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        a = ACT_CODE[self.act]
         q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y,
                           yq=self.xq if a == q8.ACT_INT8 else None, ys=self.xs if a == q8.ACT_INT8 else None,
                           want_q8=(a == q8.ACT_INT8))
@@ -256,7 +262,7 @@ class MoeBlock(Workload):
         """The separate calls after the norm: route, gate-up, down-combine."""
         q8 = self.q8
         W = self.W[c % self.copies]
-        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        a = ACT_CODE[self.act]
         idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
         q8.moe_route_topk(self.y, W[0], self.k, idx=idx, wts=wts, scratch=self.rscratch)
         self._gate_up(c, a)
@@ -284,19 +290,26 @@ class MoeBlock(Workload):
         q8 = self.q8
         for c in range(self.copies):
             i = c % self.pool
+            x2 = self.act == "x2"
             q8.add_rmsnorm_router(self.h[i], self.r[i], self.w, 1e-6, self.W[c][0], sum=self.sum, x=self.y,
-                                  xq=self.xq, xs=self.xs, logits=self.logits[c], want_q8=True)
+                                  xq=None if x2 else self.xq, xs=None if x2 else self.xs, logits=self.logits[c],
+                                  want_q8=not x2)
+            if x2:
+                q8.q8_quantize_rows_x2(self.y, xq=self.xq, xl=self.xl, xs=self.xs)
         self.torch.cuda.synchronize()
 
     def launch_dominant(self, c):
         q8 = self.q8
-        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        a = ACT_CODE[self.act]
         if self.separate:
             self._gate_up(c, a)
             return
         W = self.W[c % self.copies]
         idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
-        if a == q8.ACT_INT8:
+        if a == ACT_CODE["x2"]:
+            q8.moe_topk_gate_up_x2(self.logits[c % self.copies], W[1], W[2], W[3], W[4], self.k, self.xq, self.xl,
+                                   self.xs, idx=idx, wts=wts, hq=self.hq, hl=self.hl, hs=self.hs)
+        elif a == q8.ACT_INT8:
             q8.moe_topk_gate_up(self.logits[c % self.copies], W[1], W[2], W[3], W[4], self.k, xq=self.xq, xs=self.xs,
                                 idx=idx, wts=wts, hq=self.hq, hs=self.hs, act=a, want_h=False)
         else:
@@ -329,24 +342,26 @@ class MoeBlock(Workload):
         m = self.host_w
         s, y64 = oracle.add_rmsnorm(self.pool_h[0], self.pool_r[0], self.norm_w, 1e-6)
         x = y64.astype(np.float32)
-        a = 1 if self.act == "int8" else 0
+        a = ACT_CODE[self.act]
         ridx, rw, rh, ry = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a)
         got = self.out.cpu().numpy()
         err = float(np.max(np.abs(got - ry)) / np.max(np.abs(ry)))
         same_idx = bool(np.array_equal(self.idx[0].cpu().numpy(), ridx))
-        return {"idx_equal": same_idx, "max_rel_err": err, "tol": 2e-3 if a else 1e-5}
+        return {"idx_equal": same_idx, "max_rel_err": err, "tol": TOL[self.act]}
 
     def cpu_baseline(self, budget):
         import oracle
         np = self.np
         m = self.host_w
-        a = 1 if self.act == "int8" else 0
+        a = ACT_CODE[self.act]
         n, t0 = 0, time.perf_counter()
         while True:
             i = n % self.pool
             s, y64 = oracle.add_rmsnorm(self.pool_h[i], self.pool_r[i], self.norm_w, 1e-6)
             x = y64.astype(np.float32)
-            if a:
+            if a == 2:
+                oracle.quantize_x2(x)
+            elif a:
                 oracle.quantize(x)
             oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a)
             n += 1
@@ -669,8 +684,8 @@ class MoeSharedBlock(MoeBlock):
 def make_workload(name, act, copies, separate=False):
     import synthetic
     cfg = synthetic.CONFIGS[name]
-    if act == "x2" and cfg["kind"] != "norm_gemv":
-        raise SystemExit("two-word activations are built for the Q8_0 GEMV only (--workload norm_gemv_2048x4096)")
+    if act == "x2" and (cfg["kind"] not in ("norm_gemv", "moe") or (cfg["kind"] == "moe" and separate)):
+        raise SystemExit("two-word activations are built for the norm + GEMV and the mixture block's one call")
     if cfg["kind"] == "moe":
         return MoeBlock(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "norm_gemv":

@@ -252,6 +252,19 @@ Q8S_API int add_rmsnorm_gemv_x2(const float *h, const float *r, const float *w, 
                                 int8_t *yq, int8_t *yl, float *ys, float *out, void *stream);
 
 /*
+ * moe_topk_gate_up_x2 -- moe_topk_gate_up in two-word numerics (the
+ * mixture's second launch under act 2 of moe_ffn_block): each row's top-K
+ * taken from its logits inside every gate-up workgroup, the gate/up dots over
+ * the row's two-word form (xq, xl, xs, as q8_quantize_rows_x2 writes it), and
+ * each hidden block written in two words (hq, hl, hs; rows of k*dff values).
+ * idx/wts: device [rows, k], written.  E <= 256.  Limits as moe_gate_up.
+ */
+Q8S_API int moe_topk_gate_up_x2(const double *logits, const int8_t *xq, const int8_t *xl, const float *xs,
+                                const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                                int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int32_t *idx,
+                                float *wts, int8_t *hq, int8_t *hl, float *hs, void *stream);
+
+/*
  * add_rmsnorm_router -- add_rmsnorm_q8 with the mixture's router fused in
  * (forward_shim.rs module doc: the norm as one row kernel writing the sum;
  * fn emit_moe_forward: the router over the normed row):
@@ -312,6 +325,12 @@ Q8S_API int moe_topk_gate_up(const double *logits, const float *x, const int8_t 
  * in INT8 mode, E > 256 or d > 8192 run add_rmsnorm_q8, moe_route_topk,
  * moe_gate_up and moe_down_combine.  eps >= 0; limits as moe_route_topk and
  * moe_gate_up.
+ * act = 2 runs the block in two-word numerics (fn moe_dp4a_kernels'
+ * two-pass, logit-exact trio): x and each hidden block in two words (as
+ * q8_quantize_rows_x2), two exact int32 dots a block (as q8_gemv_x2), the
+ * router still reading f32 x; it takes the three-launch form only (E <= 256,
+ * d <= 8192; any rows, each row's weights read for that row), else
+ * Q8S_EUNSUPPORTED.  The other mixture calls refuse act 2.
  */
 Q8S_API int moe_ffn_block(const float *h, const float *r, const float *w, float eps, const float *Wr,
                   const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,

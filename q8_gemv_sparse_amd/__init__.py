@@ -25,11 +25,12 @@ __all__ = [
     "moe_topk_gate_up_ex", "moe_down_combine_ex",
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
-    "add_rmsnorm_gemv_x2",
+    "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2",
 ]
 
 ACT_F32 = 0
 ACT_INT8 = 1
+ACT_X2 = 2  # two-word int8 activations (the *_x2 calls, and moe_ffn_block)
 FN_ROUTE = 1
 FN_DOWN = 2
 FN_BLOCK = 3
@@ -72,6 +73,7 @@ _SIGS = {
     "q8_quantize_rows_x2": [_p, _i64, _i64, _p, _p, _p, _p],
     "q8_gemv_x2": [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p],
     "add_rmsnorm_gemv_x2": [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p],
+    "moe_topk_gate_up_x2": [_p] * 8 + [_i64] * 5 + [_p] * 5 + [_p],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -239,6 +241,30 @@ def add_rmsnorm_gemv_x2(h, r, w, eps, Wq, Ws, sum=None, y=None, yq=None, yl=None
                                     d, n_out, sum.data_ptr(), y.data_ptr(), yq.data_ptr(), yl.data_ptr(),
                                     ys.data_ptr(), out.data_ptr(), _stream(stream)))
     return sum, y, yq, yl, ys, out
+
+
+def moe_topk_gate_up_x2(logits, Wgq, Wgs, Wuq, Wus, k, xq, xl, xs, idx=None, wts=None, hq=None, hl=None, hs=None,
+                        stream=None):
+    """The two-word mixture's gate-up launch: top-K from `logits` inside each
+    workgroup, the two-word row (xq, xl, xs), hidden rows written in two words.
+    Returns (idx, wts, hq, hl, hs)."""
+    _dev(logits, torch.float64, "logits")
+    for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq"), (xq, "xq"), (xl, "xl")):
+        _dev(t, torch.int8, n)
+    for t, n in ((Wgs, "Wgs"), (Wus, "Wus"), (xs, "xs")):
+        _dev(t, torch.float32, n)
+    rows, E = logits.shape
+    d = Wgq.shape[1]
+    dff = Wgq.shape[0] // E
+    dev = Wgq.device
+    f = lambda t, shape, dt: t if t is not None else torch.empty(shape, dtype=dt, device=dev)
+    idx = f(idx, (rows, k), torch.int32); wts = f(wts, (rows, k), torch.float32)
+    hq = f(hq, (rows, k, dff), torch.int8); hl = f(hl, (rows, k, dff), torch.int8)
+    hs = f(hs, (rows, k, dff // 32), torch.float32)
+    _check(_lib.moe_topk_gate_up_x2(_ptr(logits), _ptr(xq), _ptr(xl), _ptr(xs), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq),
+                                    _ptr(Wus), rows, d, dff, E, k, _ptr(idx), _ptr(wts), _ptr(hq), _ptr(hl),
+                                    _ptr(hs), _stream(stream)))
+    return idx, wts, hq, hl, hs
 
 
 def add_rmsnorm_q8(h, r, w, eps, sum=None, y=None, yq=None, ys=None, want_f32=True, want_q8=True, stream=None):

@@ -692,6 +692,51 @@ int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, con
                                nullptr, 0, rows, d, dff, E, k, idx, wts, h, hq, hs, act, stream);
 }
 
+int moe_topk_gate_up_x2(const double *logits, const int8_t *xq, const int8_t *xl, const float *xs,
+                        const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus, int64_t rows,
+                        int64_t d, int64_t dff, int64_t E, int64_t k, int32_t *idx, float *wts, int8_t *hq,
+                        int8_t *hl, float *hs, void *stream)
+{
+    const char *fn = "moe_topk_gate_up_x2";
+    int rc;
+    if ((rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    if (E > q8s::ROUTE_FUSED_MAX_E)
+        return fail(Q8S_EUNSUPPORTED, "%s: E = %lld experts exceed the %d a gate-up workgroup ranks itself", fn,
+                    (long long)E, q8s::ROUTE_FUSED_MAX_E);
+    const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
+    const size_t nh = (size_t)(rows * k * dff), nx = (size_t)(rows * d);
+    std::vector<Span> ins = {{logits, (size_t)(rows * E) * 8, "logits"}, {Wgq, wq, "Wgq"}, {Wgs, wsb, "Wgs"},
+                             {Wuq, wq, "Wuq"}, {Wus, wsb, "Wus"}, {xq, nx, "xq"}, {xl, nx, "xl"},
+                             {xs, nx / 32 * 4, "xs"}};
+    std::vector<Span> outs = {{idx, (size_t)(rows * k) * 4, "idx"}, {wts, (size_t)(rows * k) * 4, "wts"},
+                              {hq, nh, "hq"}, {hl, nh, "hl"}, {hs, nh / 32 * 4, "hs"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::MoeArgs a{};
+    a.xq = xq;
+    a.xl = xl;
+    a.xs = xs;
+    a.Wgq = Wgq;
+    a.Wgs = Wgs;
+    a.Wuq = Wuq;
+    a.Wus = Wus;
+    a.rows = rows;
+    a.d = d;
+    a.dff = dff;
+    a.E = E;
+    a.k = k;
+    a.hq = hq;
+    a.hl = hl;
+    a.hs = hs;
+    a.act = 2;
+    a.logits = logits;
+    a.idx_w = idx;
+    a.wts_w = wts;
+    clear_stale();
+    return launched(q8s::route_gate_up_launch(a, as_stream(stream)), fn);
+}
+
 int moe_topk_gate_up_ex(const double *logits, const float *x, const int8_t *xq, const float *xs, const int8_t *Wgq,
                         const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Sgq, const float *Sgs,
                         const int8_t *Suq, const float *Sus, int64_t sdff, int64_t rows, int64_t d, int64_t dff,
@@ -761,8 +806,17 @@ int block_common(const char *fn, const float *h, const float *r, const float *w,
                  void *scratch, size_t scratch_bytes, void *stream)
 {
     int rc;
-    if ((rc = check_act(fn, act)) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+    if ((act != 2 && (rc = check_act(fn, act))) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
         return rc;
+    if (act == 2) {
+        // two words: the float router, no shared expert, the three-launch form
+        if (rt.Wrq || sdff > 0)
+            return fail(Q8S_EUNSUPPORTED, "%s: two-word numerics (act 2) are built for the float router without a "
+                        "shared expert only", fn);
+        if (!q8s::block_fused(rows, d, dff, E, act))
+            return fail(Q8S_EUNSUPPORTED, "%s: two-word numerics (act 2) need E <= %d and d <= %lld", fn,
+                        (int)q8s::ROUTE_FUSED_MAX_E, (long long)q8s::NORM_LOGITS_MAX_D);
+    }
     if (!(eps >= 0.0f) || eps != eps)
         return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
     if ((rc = check_shared(fn, sdff, dff, k, {Sgq, Sgs, Suq, Sus, Sdq, Sds})))

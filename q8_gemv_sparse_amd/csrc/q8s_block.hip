@@ -43,6 +43,8 @@ struct BlockScratch {
     float *h;
     int8_t *hq;
     float *hs;
+    int8_t *xl;  // two words: the low words of the normed row and of the hidden rows
+    int8_t *hl;
     float *sh;  // a chunk's shared hidden rows (f32, or their Q8_0 form below)
     int8_t *shq;
     float *shs;
@@ -66,11 +68,15 @@ BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t sdf
     const size_t nh = (size_t)rows * (size_t)(k * dff + (chunk ? 0 : sdff));
     s.logits = reinterpret_cast<double *>(take((size_t)(rows * E) * sizeof(double)));
     s.x = reinterpret_cast<float *>(take((size_t)(rows * d) * 4));
-    if (act == 1) {
+    if (act >= 1) {  // one or two int8 words
         s.xq = reinterpret_cast<int8_t *>(take((size_t)(rows * d)));
         s.xs = reinterpret_cast<float *>(take((size_t)(rows * d / QB) * 4));
         s.hq = reinterpret_cast<int8_t *>(take(nh));
         s.hs = reinterpret_cast<float *>(take(nh / QB * 4));
+        if (act == 2) {
+            s.xl = reinterpret_cast<int8_t *>(take((size_t)(rows * d)));
+            s.hl = reinterpret_cast<int8_t *>(take(nh));
+        }
         if (chunk)  // the chunk kernels stage the float32 hidden rows
             s.h = reinterpret_cast<float *>(take(nh * 4));
     } else {
@@ -123,6 +129,8 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
     a.h = s.h;
     a.hq = s.hq;
     a.hs = s.hs;
+    a.xl = s.xl;
+    a.hl = s.hl;
     a.y = b.out;
     a.act = b.act;
     a.scratch = s.down;
@@ -142,7 +150,7 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
     hipError_t err;
     if (block_fused(b.rows, b.d, b.dff, b.E, b.act)) {
         err = norm_logits_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, rt, b.E, b.sum,
-                                 b.act == 0 ? s.x : nullptr, s.xq, s.xs, s.logits, st);
+                                 b.act == 0 ? s.x : nullptr, s.xq, s.xs, s.logits, st, s.xl);
         if (err != hipSuccess)
             return err;
         a.logits = s.logits;

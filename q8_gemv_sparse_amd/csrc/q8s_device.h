@@ -181,12 +181,9 @@ Q8S_DEV void quant8_store(const float (&v)[8], int8_t *q, float *scale, bool lea
         *scale = d;
 }
 
-// quant8 in two words: the same words and scale, plus the 8 low words.
-Q8S_DEV void quant8x2_store(const float (&v)[8], int8_t *q, int8_t *lo, float *scale, bool leader)
+// The 8 low words of v whose words are w (quant8's packing) and scale d.
+Q8S_DEV uint2 low8(const float (&v)[8], uint2 w, float d)
 {
-    float d;
-    const uint2 w = quant8(v, d);
-    *reinterpret_cast<uint2 *>(q) = w;
     const float id = q8_inv(d);
     uint32_t l0 = 0, l1 = 0;
 #pragma unroll
@@ -195,7 +192,16 @@ Q8S_DEV void quant8x2_store(const float (&v)[8], int8_t *q, int8_t *lo, float *s
         l0 |= (uint32_t)(q8_low(v[i], id, q0) & 0xFF) << (8 * i);
         l1 |= (uint32_t)(q8_low(v[4 + i], id, q1) & 0xFF) << (8 * i);
     }
-    *reinterpret_cast<uint2 *>(lo) = make_uint2(l0, l1);
+    return make_uint2(l0, l1);
+}
+
+// quant8 in two words: the same words and scale, plus the 8 low words.
+Q8S_DEV void quant8x2_store(const float (&v)[8], int8_t *q, int8_t *lo, float *scale, bool leader)
+{
+    float d;
+    const uint2 w = quant8(v, d);
+    *reinterpret_cast<uint2 *>(q) = w;
+    *reinterpret_cast<uint2 *>(lo) = low8(v, w, d);
     if (leader)
         *scale = d;
 }
@@ -503,8 +509,8 @@ Q8S_DEV float silu(float z)
 template <int ACT, int LPR, int C>
 struct GuShape {
     static constexpr int G = WAVE / LPR;
-    static constexpr int NW = ACT == 1 ? (LPR == 64 ? 16 : 8) : 8;
-    static constexpr int U = ACT == 1 ? (LPR == 64 ? 2 : 1) : ((C == 1 && LPR == 64) ? 2 : 1);
+    static constexpr int NW = ACT >= 1 ? (LPR == 64 ? 16 : 8) : 8;
+    static constexpr int U = ACT >= 1 ? (LPR == 64 ? 2 : 1) : ((C == 1 && LPR == 64) ? 2 : 1);
     static constexpr int OPS = G * U;
     static constexpr int T = NW * OPS;
     static_assert(QB % T == 0, "a tile divides a 32-value block, so it divides dff");

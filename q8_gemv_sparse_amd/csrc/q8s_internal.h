@@ -101,7 +101,7 @@ struct RouterRows {
 bool norm_logits_supported(int64_t d);
 hipError_t norm_logits_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               const RouterRows &rt, int64_t E, float *sum, float *x, int8_t *xq, float *xs,
-                              double *logits, hipStream_t st);
+                              double *logits, hipStream_t st, int8_t *xl = nullptr);
 
 // router scratch: f64 logits [rows, E]
 size_t route_scratch_bytes(int64_t rows, int64_t E);
@@ -146,6 +146,9 @@ struct MoeArgs {
     int64_t sdff;
     // the down-combine adds its result to y instead of writing it
     bool acc_out;
+    // two-word numerics (act 2): the low words of x and of the hidden rows
+    const int8_t *xl;
+    int8_t *hl;
 };
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st);
 // gate-up that takes each row's top-K from `logits` itself (E <= ROUTE_FUSED_MAX_E)

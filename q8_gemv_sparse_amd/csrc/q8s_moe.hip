@@ -59,7 +59,8 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, bool valid, int64_
                           const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                           const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs,
                           const int8_t *__restrict__ Wuq, const float *__restrict__ Wus, int d, int ks,
-                          float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
+                          float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs,
+                          const int8_t *__restrict__ xl, int8_t *__restrict__ hl)
 {
     using S = GuShape<ACT, LPR, C>;
     constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, NW = S::NW;
@@ -78,11 +79,14 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, bool valid, int64_
     // rows first: the activation slice then lives in registers for less time,
     // which for float32 decides occupancy.
     const int nitems = ks * STEPS;
-    const bool fixed = ACT == 1 && ks > 1 && (NW % ks) == 0;
+    const bool fixed = ACT >= 1 && ks > 1 && (NW % ks) == 0;
     auto load_xs = [&](int s, XSlice<ACT, C> &xv) {
         const int ch0 = s * LPR * C;
-        load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
-                       ACT == 1 ? xs + row * nb : nullptr, ch0, min(LPR * C, nch - ch0), lig);
+        if constexpr (ACT == 2)
+            load_x2<LPR, C>(xv, xq + row * d, xl + row * d, xs + row * nb, ch0, min(LPR * C, nch - ch0), lig);
+        else
+            load_x<LPR, C>(xv, ACT == 0 ? x + row * d : nullptr, ACT == 1 ? xq + row * d : nullptr,
+                           ACT == 1 ? xs + row * nb : nullptr, ch0, min(LPR * C, nch - ch0), lig);
     };
     XSlice<ACT, C> xv;
     if (fixed && wid < nitems)
@@ -115,7 +119,7 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, bool valid, int64_
             if (lig == 0) {
                 if (ks == 1) {
                     const float r = valid ? silu(g) * v : 0.0f;
-                    if (ACT == 1)
+                    if (ACT >= 1)
                         sm.hv[ol] = r;
                     if (h)
                         h[hbase + ol] = r;
@@ -137,15 +141,15 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, bool valid, int64_
                 v += sm.up[s][t];
             }
             const float r = valid ? silu(g) * v : 0.0f;
-            if (ACT == 1)
+            if (ACT >= 1)
                 sm.hv[t] = r;
             if (h)
                 h[hbase + t] = r;
         }
-        if (ACT == 1)
+        if (ACT >= 1)
             __syncthreads();
     }
-    if (ACT == 1 && wid == 0) {
+    if (ACT >= 1 && wid == 0) {
         // the tile is one Q8_0 block of the hidden row: quantise it once
         const int t = lane & 31;
         const float v = sm.hv[t];
@@ -154,8 +158,12 @@ Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, bool valid, int64_
             amax = fmaxf(amax, __shfl_xor(amax, off));
         const float dsc = q8_scale(amax);
         const float id = q8_inv(dsc);
-        if (lane < 32)
-            hq[hbase + t] = (int8_t)q8_code(v, id);
+        if (lane < 32) {
+            const int q = q8_code(v, id);
+            hq[hbase + t] = (int8_t)q;
+            if (ACT == 2)
+                hl[hbase + t] = (int8_t)q8_low(v, id, q);
+        }
         if (lane == 0)
             hs[hbase / QB] = dsc;
     }
@@ -195,7 +203,8 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
               const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
               const float *__restrict__ Wus, SharedW sw, const int32_t *__restrict__ idx, int d, int dff, int E,
-              int k, int ks, float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
+              int k, int ks, float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs,
+              const int8_t *__restrict__ xl, int8_t *__restrict__ hl)
 {
     constexpr int T = GuShape<ACT, LPR, C>::T;
     __shared__ GuLds<T> sm;
@@ -207,7 +216,7 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     const int64_t rbase = t.shared ? t.o0 : (int64_t)(valid ? e : 0) * dff + t.o0;
     gate_up_tile<ACT, LPR, C>(sm, valid, row, rbase, hbase, x, xq, xs, t.shared ? sw.gq : Wgq,
                               t.shared ? sw.gs : Wgs, t.shared ? sw.uq : Wuq, t.shared ? sw.us : Wus, d, ks, h, hq,
-                              hs);
+                              hs, xl, hl);
 }
 
 // gate-up that first takes the row's top-K itself from the router logits:
@@ -221,7 +230,8 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
                     const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                     const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
                     const float *__restrict__ Wus, SharedW sw, int d, int dff, int E, int k, int ks,
-                    float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs)
+                    float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs,
+                    const int8_t *__restrict__ xl, int8_t *__restrict__ hl)
 {
     static_assert(ROUTE_FUSED_MAX_E <= TOPK_LDS_E, "the row's logits fit the top-K LDS");
     constexpr int T = GuShape<ACT, LPR, C>::T;
@@ -232,7 +242,7 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     const int64_t hbase = row * ((int64_t)k * dff + (SH ? sw.sdff : 0)) + (int64_t)t.j * dff + t.o0;
     if (t.shared) {
         gate_up_tile<ACT, LPR, C>(sm, true, row, t.o0, hbase, x, xq, xs, sw.gq, sw.gs, sw.uq, sw.us, d, ks, h, hq,
-                                  hs);
+                                  hs, xl, hl);
         return;
     }
     topk_load(tk, logits + row * E, E);
@@ -241,7 +251,7 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(tk.ch[t.j]);
     gate_up_tile<ACT, LPR, C>(sm, true, row, (int64_t)e * dff + t.o0, hbase, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, ks, h,
-                              hq, hs);
+                              hq, hs, xl, hl);
     // the choices and weights go out after the tile, off its critical path
     // (only the down-combine launch reads them)
     if (blockIdx.x == 0 && threadIdx.x < WAVE)
@@ -274,7 +284,8 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
                                                               const float *__restrict__ Wds, SharedW sw,
                                                               const int32_t *__restrict__ idx,
                                                               const float *__restrict__ wts, int d, int dff, int E, int k,
-                                                              int ks, int kss, const float *y_add, float *y)
+                                                              int ks, int kss, const float *y_add, float *y,
+                                                              const int8_t *__restrict__ hl)
 {
     constexpr int G = WAVE / LPR;
     constexpr int U = dn_unroll<ACT, LPR, C>();
@@ -320,8 +331,11 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
         // The hidden row's chunks are requested first (they come from cache),
         // then the weight rows of step 0.
         XSlice<ACT, C> xv;
-        load_x<LPR, C>(xv, ACT == 0 ? h + hrow : nullptr, ACT == 1 ? hq + hrow : nullptr,
-                       ACT == 1 ? hs + hrow / QB : nullptr, ch0, sl, lig);
+        if constexpr (ACT == 2)
+            load_x2<LPR, C>(xv, hq + hrow, hl + hrow, hs + hrow / QB, ch0, sl, lig);
+        else
+            load_x<LPR, C>(xv, ACT == 0 ? h + hrow : nullptr, ACT == 1 ? hq + hrow : nullptr,
+                           ACT == 1 ? hs + hrow / QB : nullptr, ch0, sl, lig);
         RowSlice<C> wa[UU], wb[UU];
         load_step(wa, 0);
 #pragma unroll
@@ -379,11 +393,11 @@ hipError_t gu_go(const MoeArgs &a, int ks, hipStream_t st)
     if (a.sdff)
         hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, true>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
                            a.Wgs, a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
-                           a.hq, a.hs);
+                           a.hq, a.hs, a.xl, a.hl);
     else
         hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, false>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
                            a.Wgs, a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
-                           a.hq, a.hs);
+                           a.hq, a.hs, a.xl, a.hl);
     return hipGetLastError();
 }
 
@@ -396,11 +410,11 @@ hipError_t rgu_go(const MoeArgs &a, int ks, hipStream_t st)
     if (a.sdff)
         hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, true>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
                            a.wts_w, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff,
-                           (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
+                           (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs, a.xl, a.hl);
     else
         hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, false>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
                            a.wts_w, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff,
-                           (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs);
+                           (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs, a.xl, a.hl);
     return hipGetLastError();
 }
 
@@ -417,11 +431,11 @@ hipError_t dn_go(const MoeArgs &a, int ks, hipStream_t st)
     if (a.sdff)
         hipLaunchKernelGGL((k_down<ACT, LPR, C, true>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds,
                            shared_w(a), a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss,
-                           a.acc_out ? a.y : nullptr, a.y);
+                           a.acc_out ? a.y : nullptr, a.y, a.hl);
     else
         hipLaunchKernelGGL((k_down<ACT, LPR, C, false>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds,
                            shared_w(a), a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss, nullptr,
-                           a.y);
+                           a.y, a.hl);
     return hipGetLastError();
 }
 
@@ -462,30 +476,45 @@ struct DN {
 
 namespace {
 
+// The decode gate-up's int8 shapes (one or two words) for d, then the launch F.
+template <int ACT, template <int, int, int> class F>
+hipError_t gu_int8(const MoeArgs &a, hipStream_t st)
+{
+    // int8 rows past 2048: slices of 1024 values (lane groups of 64, one chunk
+    // each; measured fastest at d 4096), or of 2048 past 32 slices
+    const int64_t nch = a.d / 16;
+    if (nch > 128 && nch <= 64 * GU_MAX_KS)
+        return F<ACT, 64, 1>::go(a, (int)((nch + 63) / 64), st);
+    if (nch > 128)
+        return F<ACT, 64, 2>::go(a, (int)((nch + 127) / 128), st);
+    const SliceShape sh = slice_shape(a.d);
+    switch (sh.lpr * 8 + sh.c) {
+    case 16 * 8 + 1:
+        return F<ACT, 16, 1>::go(a, 1, st);
+    case 16 * 8 + 3:
+        return F<ACT, 16, 3>::go(a, 1, st);
+    case 64 * 8 + 1:
+        return F<ACT, 64, 1>::go(a, 1, st);
+    default:
+        return F<ACT, 64, 2>::go(a, 1, st);
+    }
+}
+
 // The decode gate-up's shape for the mode and d, then the launch F.
 template <template <int, int, int> class F>
 hipError_t gu_dispatch(const MoeArgs &a, hipStream_t st)
 {
     if (a.act == 0)
         return by_shape<0, F>(a, a.d, st);
-    // int8 rows past 2048: slices of 1024 values (lane groups of 64, one chunk
-    // each; measured fastest at d 4096), or of 2048 past 32 slices
-    const int64_t nch = a.d / 16;
-    if (nch > 128 && nch <= 64 * GU_MAX_KS)
-        return F<1, 64, 1>::go(a, (int)((nch + 63) / 64), st);
-    if (nch > 128)
-        return F<1, 64, 2>::go(a, (int)((nch + 127) / 128), st);
-    const SliceShape sh = slice_shape(a.d);
-    switch (sh.lpr * 8 + sh.c) {
-    case 16 * 8 + 1:
-        return F<1, 16, 1>::go(a, 1, st);
-    case 16 * 8 + 3:
-        return F<1, 16, 3>::go(a, 1, st);
-    case 64 * 8 + 1:
-        return F<1, 64, 1>::go(a, 1, st);
-    default:
-        return F<1, 64, 2>::go(a, 1, st);
-    }
+    return a.act == 2 ? gu_int8<2, F>(a, st) : gu_int8<1, F>(a, st);
+}
+
+// The down-combine for the mode, over hidden rows of n_in values.
+hipError_t dn_dispatch(const MoeArgs &a, int64_t n_in, hipStream_t st)
+{
+    if (a.act == 2)
+        return by_shape<2, DN>(a, n_in, st);
+    return a.act == 0 ? by_shape<0, DN>(a, n_in, st) : by_shape<1, DN>(a, n_in, st);
 }
 
 } // namespace
@@ -508,13 +537,10 @@ hipError_t down_launch(const MoeArgs &a, hipStream_t st)
 {
     if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
         return chunk_down_launch(a, st);
-    return a.act == 0 ? by_shape<0, DN>(a, a.dff, st) : by_shape<1, DN>(a, a.dff, st);
+    return dn_dispatch(a, a.dff, st);
 }
 
-hipError_t row_down_launch(const MoeArgs &a, hipStream_t st)
-{
-    return a.act == 0 ? by_shape<0, DN>(a, a.dff, st) : by_shape<1, DN>(a, a.dff, st);
-}
+hipError_t row_down_launch(const MoeArgs &a, hipStream_t st) { return dn_dispatch(a, a.dff, st); }
 
 int64_t down_pairs(int64_t dff, int64_t sdff, int64_t k)
 {
@@ -536,7 +562,7 @@ hipError_t shared_launch(const MoeArgs &a, hipStream_t st)
     hipError_t err = gu_dispatch<GU>(s, st);
     if (err != hipSuccess)
         return err;
-    return s.act == 0 ? by_shape<0, DN>(s, s.sdff, st) : by_shape<1, DN>(s, s.sdff, st);
+    return dn_dispatch(s, s.sdff, st);
 }
 
 } // namespace q8s

@@ -97,7 +97,8 @@ __global__ void __launch_bounds__(NORM_THREADS)
     k_norm_logits(const float *__restrict__ h, const float *__restrict__ r, const float *__restrict__ w, int d,
                   float eps, const float *__restrict__ Wr, const int8_t *__restrict__ Wrq,
                   const float *__restrict__ Wrs, int E, float *__restrict__ sum, float *__restrict__ x,
-                  int8_t *__restrict__ xq, float *__restrict__ xs, double *__restrict__ logits)
+                  int8_t *__restrict__ xq, float *__restrict__ xs, double *__restrict__ logits,
+                  int8_t *__restrict__ xl)
 {
     __shared__ double wsum[NORM_THREADS / WAVE];
     __shared__ double lsum[NORM_THREADS / WAVE];
@@ -174,6 +175,8 @@ __global__ void __launch_bounds__(NORM_THREADS)
                 const bool leader = (threadIdx.x & 3) == 0;
                 if (writer && xq) {
                     *reinterpret_cast<uint2 *>(xq + row * d + base) = c;
+                    if (xl)  // two words: the low words too
+                        *reinterpret_cast<uint2 *>(xl + row * d + base) = low8(v, c, ys);
                     if (leader)
                         xs[row * nb + base / QB] = ys;
                 }
@@ -268,34 +271,34 @@ namespace {
 template <int RF>
 void norm_logits_go(int segs, dim3 grid, hipStream_t st, const float *h, const float *r, const float *w, int d,
                     float eps, const RouterRows &rt, int E, float *sum, float *x, int8_t *xq, float *xs,
-                    double *logits)
+                    double *logits, int8_t *xl)
 {
     const dim3 block(NORM_THREADS);
     if (segs <= 1)
         hipLaunchKernelGGL((k_norm_logits<1, RF>), grid, block, 0, st, h, r, w, d, eps, rt.Wr, rt.Wrq, rt.Wrs, E, sum,
-                           x, xq, xs, logits);
+                           x, xq, xs, logits, xl);
     else if (segs <= 2)
         hipLaunchKernelGGL((k_norm_logits<2, RF>), grid, block, 0, st, h, r, w, d, eps, rt.Wr, rt.Wrq, rt.Wrs, E, sum,
-                           x, xq, xs, logits);
+                           x, xq, xs, logits, xl);
     else
         hipLaunchKernelGGL((k_norm_logits<4, RF>), grid, block, 0, st, h, r, w, d, eps, rt.Wr, rt.Wrq, rt.Wrs, E, sum,
-                           x, xq, xs, logits);
+                           x, xq, xs, logits, xl);
 }
 
 } // namespace
 
 hipError_t norm_logits_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
                               const RouterRows &rt, int64_t E, float *sum, float *x, int8_t *xq, float *xs,
-                              double *logits, hipStream_t st)
+                              double *logits, hipStream_t st, int8_t *xl)
 {
     const int segs = (int)((d + NORM_SEG - 1) / NORM_SEG);
     const dim3 grid((unsigned)E, (unsigned)rows);
     if (!rt.Wrq)
-        norm_logits_go<0>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits);
+        norm_logits_go<0>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits, xl);
     else if (rt.act == 0)
-        norm_logits_go<1>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits);
+        norm_logits_go<1>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits, xl);
     else
-        norm_logits_go<2>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits);
+        norm_logits_go<2>(segs, grid, st, h, r, w, (int)d, eps, rt, (int)E, sum, x, xq, xs, logits, xl);
     return hipGetLastError();
 }
 

@@ -155,7 +155,7 @@ def test_block_scratch_and_refusals():
     assert chunk >= q8.q8s_scratch_bytes(q8.FN_DOWN, 64, 2048, 768, 128, 8, q8.ACT_INT8) + 64 * 128 * 8
     assert block(k=0) == -1 and "1 <= k <= E" in _err()
     assert block(d=40) == -1 and "multiple of 32" in _err()
-    assert block(act=2) == -2 and "two-word" in _err()
+    assert block(act=3) == -2 and "unknown activation" in _err()
     assert block(eps=-1.0) == -1 and "eps" in _err()
     assert block(Wr=None) == -1 and "`Wr` is null" in _err()
     assert block(out=0x100000 * 14 + 8) == -3 and "16-byte" in _err()
@@ -340,3 +340,26 @@ def test_norm_gemv_x2_refusals():
     assert f(y=None) == -1 and "`y` is null" in _err()
     assert f(d=40) == -1 and "multiple of 32" in _err()
     assert f(eps=-1.0) == -1 and "eps" in _err()
+
+
+def test_block_two_word_limits():
+    # two words: the float router without a shared expert, E <= 256, d <= 8192
+    blk = lambda E=4, d=64, act=2: LIB.moe_ffn_block(A, B, C, ctypes.c_float(1e-6), D, F, G, H, J, 0xB0000000,
+                                                      0xC8000000, 1, d, 64, E, 2, 0xD0000000, 0xD8000000,
+                                                      0xE8000000, 0xF0000000, act, 0xF8000000, 1 << 24, None)
+    assert blk(E=300) == -2 and "two-word" in _err()
+    assert blk(d=16384) == -2 and "two-word" in _err()
+    assert blk(act=3) == -2
+    # the stage calls stay one-word
+    assert gate_up(act=2) == -2 and "two-word" in _err()
+
+
+def test_block_scratch_holds_the_two_word_rows():
+    # two words need the one-word arrays (x and the hidden rows in Q8_0 form)
+    # plus their low words; a scratch sized for float32 rows would leave the
+    # int8 arrays unplaced
+    al = lambda n: -(-n // 256) * 256
+    for rows, d, dff, E, k in ((1, 2048, 768, 128, 8), (1, 96, 160, 5, 3)):  # decode rows (no chunk scratch)
+        one = q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, q8.ACT_INT8)
+        two = q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, 2)
+        assert two == one + al(rows * d) + al(rows * k * dff)

@@ -112,3 +112,69 @@ def test_norm_gemv_x2(d, n_out, rows):
     got = host(out)
     for i in range(rows):
         assert rel_err(got[i], ref[i]) <= TOL, i
+
+
+# ---------------------------------------------------------------------------
+# the mixture block in two words: moe_ffn_block(act=2) against the oracle's
+# chain add_rmsnorm -> moe(act=2).  The hidden rows are float32 on both sides
+# but summed in different orders, so a low word can round the other way where
+# the two float32 values straddle a 128th of a step: each such flip moves one
+# value by 1/128 of a one-word flip, so the one-word tolerance of 2e-3 scales
+# to 2e-3 * 16 / 128 = 2.5e-4 (a margin of 16 flips' worth).
+TOL_X2_BLOCK = 2.5e-4
+
+BLOCK_X2_CASES = [
+    # (d, dff, E, k, rows)
+    (2048, 768, 128, 8, 1),     # the 128-expert decode block
+    (4096, 14336, 8, 2, 1),     # the 8-expert decode block: rows in 4 slices
+    (2080, 4096, 4, 4, 1),      # rows of 130 chunks: 3 slices, the last of 2 chunks
+    (96, 160, 5, 3, 1),         # ragged: lane groups of 16, tiles past dff
+    (256, 64, 5, 5, 1),         # K = E
+    (64, 64, 1, 1, 1),          # one expert
+    (512, 96, 256, 32, 1),      # the most experts ranked in the gate-up, the most kept
+    (256, 96, 6, 2, 3),         # several rows (no grouped chunk kernels in two words)
+]
+
+
+@pytest.mark.parametrize("d,dff,E,k,rows", BLOCK_X2_CASES)
+def test_block_x2_matches_oracle(d, dff, E, k, rows):
+    banner("block x2 d=%d dff=%d E=%d k=%d rows=%d" % (d, dff, E, k, rows))
+    b = synthetic.block_inputs(20, d, dff, E, k, rows)
+    m = b.moe
+    W = [dev(a) for a in (m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds)]
+    s, idx, wts, out = q8.moe_ffn_block(dev(b.h), dev(b.r), dev(b.w), 1e-6, *W, k, act=2)
+    rs, y64 = oracle.add_rmsnorm(b.h, b.r, b.w, 1e-6)
+    x = y64.astype(np.float32)
+    ridx, rw, rh, ry = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, k, 2)
+    assert np.array_equal(host(s), rs)
+    assert np.array_equal(host(idx), ridx)
+    assert rel_err(host(wts), rw) <= 1e-5
+    got = host(out)
+    for r in range(rows):
+        assert rel_err(got[r], ry[r]) <= TOL_X2_BLOCK, r
+    # closer to the f32 mode than the one-word block is
+    _, _, _, yf = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, k, 0)
+    _, _, _, y1 = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, k, 1)
+    assert rel_err(got, yf) < rel_err(y1, yf) / 8
+
+
+@pytest.mark.parametrize("d,dff,E,k", [(2048, 768, 128, 8), (4096, 14336, 8, 2), (96, 160, 5, 3)])
+def test_topk_gate_up_x2(d, dff, E, k):
+    # the stage alone: choices as the oracle's, and hidden rows whose two-word
+    # form reads back within half a low-word step of the oracle's float32 rows
+    banner("moe_topk_gate_up_x2 d=%d dff=%d E=%d k=%d" % (d, dff, E, k))
+    b = synthetic.block_inputs(22, d, dff, E, k, 1)
+    m = b.moe
+    rs, y64 = oracle.add_rmsnorm(b.h, b.r, b.w, 1e-6)
+    x = y64.astype(np.float32)
+    ridx, rw, logits = oracle.route(x, m.Wr, k)
+    rq, rl, rsc = oracle.quantize_x2(x)
+    idx, wts, hq, hl, hs = q8.moe_topk_gate_up_x2(dev(logits), dev(m.Wgq), dev(m.Wgs), dev(m.Wuq), dev(m.Wus), k,
+                                                  dev(rq), dev(rl), dev(rsc))
+    _, _, rh, _ = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, k, 2)
+    assert np.array_equal(host(idx), ridx)
+    assert rel_err(host(wts), rw) <= 1e-5
+    step = np.repeat(host(hs).reshape(1, k, dff // 32).astype(np.float64), 32, axis=2)
+    back = step * (host(hq).astype(np.float64) + host(hl).astype(np.float64) / 128.0)
+    ref = rh.astype(np.float64)
+    assert np.all(np.abs(back - ref) <= step / 256.0 * (1 + 1e-6) + 1e-5 * np.max(np.abs(ref)))
