@@ -51,6 +51,7 @@ def _load():
     lib.oracle_add_rmsnorm.argtypes = [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p]
     lib.oracle_route.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p]
     lib.oracle_route_q8.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p]
+    lib.oracle_route_q8x.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _p, _p, _p]
     lib.oracle_moe.argtypes = [ctypes.c_int, _p, _p, _p, _p, _p, _p, _p, _p,
                                _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p]
     lib.oracle_moe.restype = ctypes.c_int
@@ -170,14 +171,14 @@ def route(x, Wr, k):
     return idx, wts, logits
 
 
-def route_q8(Wrq, Wrs, k, x=None, xq=None, xs=None):
+def route_q8(Wrq, Wrs, k, x=None, xq=None, xs=None, xl=None):
     """The router over Q8_0 rows (E rows of d): logits are the Q8_0 GEMV of
-    `x` (float activations) or of `xq`/`xs` (int8 activations, one word each),
-    then the softmax top-K of `route`.  Returns (idx int32 [rows, k], wts
-    float64 [rows, k], logits float64 [rows, E])."""
+    `x` (float activations), of `xq`/`xs` (int8 activations, one word each) or
+    of `xq`/`xl`/`xs` (two words), then the softmax top-K of `route`.  Returns
+    (idx int32 [rows, k], wts float64 [rows, k], logits float64 [rows, E])."""
     Wrq = _c(Wrq, np.int8); Wrs = _c(Wrs, np.float32)
     E, d = Wrq.shape
-    act = 0 if x is not None else 1
+    act = 0 if x is not None else (2 if xl is not None else 1)
     if act == 0:
         x = _c(np.atleast_2d(x), np.float32)
         rows = x.shape[0]
@@ -194,8 +195,13 @@ def route_q8(Wrq, Wrs, k, x=None, xq=None, xs=None):
     idx = np.empty((rows, k), np.int32)
     wts = np.empty((rows, k), np.float64)
     logits = np.empty((rows, E), np.float64)
-    _load().oracle_route_q8(act, x_p, xq_p, xs_p, _ptr(Wrq), _ptr(Wrs), rows, d, E, k,
-                            _ptr(idx), _ptr(wts), _ptr(logits))
+    xl_p = None
+    if act == 2:
+        xl = _c(np.atleast_2d(xl), np.int8)
+        assert xl.shape == xq.shape
+        xl_p = _ptr(xl)
+    _load().oracle_route_q8x(act, x_p, xq_p, xl_p, xs_p, _ptr(Wrq), _ptr(Wrs), rows, d, E, k,
+                             _ptr(idx), _ptr(wts), _ptr(logits))
     return idx, wts, logits
 
 

@@ -329,18 +329,21 @@ void oracle_route(const float *x, const float *Wr, int64_t rows, int64_t d, int6
  * R8 -- the router over quantized checkpoint rows (lane_link.rs fn prim, Moe
  * arm: a mixture's router is either quantized rows or float values).  The
  * router rows Wrq/Wrs are a Q8_0 matrix [Q8Ref] of E rows, so the logits are
- * that matrix's GEMV: G over f32 x (act 0), or I over the one-word int8
- * activation xq/xs (act 1) -- a norm whose readers are all Q8_0 projections
- * is read in its quantised form only under that numerics (lane_link.rs,
- * fn only_projections: a router of float values keeps it f32).  Then the
- * softmax, top-K and renormalisation of R.  logits may be NULL.
+ * that matrix's GEMV: G over f32 x (act 0), I over the one-word int8
+ * activation xq/xs (act 1), or I2 over the two-word one xq/xl/xs (act 2) -- a
+ * norm whose readers are all Q8_0 projections is read in its quantised form
+ * only under those numerics (lane_link.rs, fn only_projections: a router of
+ * float values keeps it f32).  Then the softmax, top-K and renormalisation of
+ * R.  logits may be NULL; xl is read under act 2 only.
  */
-void oracle_route_q8(int act, const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq,
-                     const float *Wrs, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx, double *wts,
-                     double *logits)
+void oracle_route_q8x(int act, const float *x, const int8_t *xq, const int8_t *xl, const float *xs,
+                      const int8_t *Wrq, const float *Wrs, int64_t rows, int64_t d, int64_t E, int64_t k,
+                      int32_t *idx, double *wts, double *logits)
 {
     double *l = (double *)malloc((size_t)(rows * E) * sizeof(double));
-    if (act)
+    if (act == 2)
+        oracle_gemv_i8x2(Wrq, Wrs, E, d, xq, xl, xs, rows, l);
+    else if (act)
         oracle_gemv_i8(Wrq, Wrs, E, d, xq, xs, rows, l);
     else
         oracle_gemv_f32(Wrq, Wrs, E, d, x, rows, l);
@@ -349,6 +352,14 @@ void oracle_route_q8(int act, const float *x, const int8_t *xq, const float *xs,
     if (logits)
         memcpy(logits, l, (size_t)(rows * E) * sizeof(double));
     free(l);
+}
+
+/* R8 in f32 or one-word numerics (act 0 or 1). */
+void oracle_route_q8(int act, const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq,
+                     const float *Wrs, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx, double *wts,
+                     double *logits)
+{
+    oracle_route_q8x(act, x, xq, NULL, xs, Wrq, Wrs, rows, d, E, k, idx, wts, logits);
 }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
@@ -437,8 +448,7 @@ int oracle_moe(int act, const float *x, const float *Wr, const int8_t *Wgq, cons
  *       y[o'] = (sum_{j<K} w[j] * dn[j][o']) + dn_s[o']
  *     its hidden row h_s (float32; Q8_0 per block under act 1) after the K
  *     routed ones.
- * h is [rows, K*dff + sdff].  Returns 0, or -1 for an unknown mode (or the
- * Q8_0 router under two words, which is not built).
+ * h is [rows, K*dff + sdff].  Returns 0, or -1 for an unknown mode.
  */
 int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wrq, const float *Wrs,
                       const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus, const int8_t *Wdq,
@@ -446,7 +456,7 @@ int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wr
                       const int8_t *Sdq, const float *Sds, int64_t sdff, int64_t rows, int64_t d, int64_t dff,
                       int64_t E, int64_t k, int32_t *idx, double *wts, float *h, double *y)
 {
-    if (act < 0 || act > 2 || (act == 2 && Wrq))
+    if (act < 0 || act > 2)
         return -1;
     const int64_t nbd = d / QBLOCK, nbf = dff / QBLOCK, hw = k * dff + sdff;
     int8_t *xq = (int8_t *)malloc((size_t)(rows * d));
@@ -459,7 +469,7 @@ int oracle_moe_shared(int act, const float *x, const float *Wr, const int8_t *Wr
     else if (act == 2)
         oracle_quantize_x2(x, rows, d, xq, xl, xs);
     if (Wrq)
-        oracle_route_q8(act, x, xq, xs, Wrq, Wrs, rows, d, E, k, idx, wts, NULL);
+        oracle_route_q8x(act, x, xq, xl, xs, Wrq, Wrs, rows, d, E, k, idx, wts, NULL);
     else
         oracle_route(x, Wr, rows, d, E, k, idx, wts, NULL);
     for (int64_t i = 0; i < rows; i++) {

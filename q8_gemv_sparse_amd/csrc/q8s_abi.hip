@@ -109,7 +109,8 @@ int check_act(const char *fn, int act)
         return 0;
     if (act == 2)
         return fail(Q8S_EUNSUPPORTED,
-                    "%s: act = 2 (two-word int8 activations) is served by q8_quantize_rows_x2 and q8_gemv_x2 only", fn);
+                    "%s: act = 2 (two-word int8 activations) is served by q8_quantize_rows_x2, q8_gemv_x2, "
+                    "add_rmsnorm_gemv_x2, moe_topk_gate_up_x2 and moe_ffn_block only", fn);
     return fail(Q8S_EUNSUPPORTED, "%s: unknown activation mode act = %d", fn, act);
 }
 

@@ -530,6 +530,52 @@ def test_route_q8_int8_equals_float_when_x_is_q8_exact():
         assert np.array_equal(u, v)
 
 
+def test_route_q8_two_words_brute_force_and_exact_rows():
+    # two-word logits: exact rationals of sum_b ws*xs*(isum_hi + isum_lo/128);
+    # brute force over the K-subsets; and on rows the two words represent
+    # exactly, the same routing and logits as the float router over the rows
+    rng = np.random.default_rng(95)
+    E, d, k = 6, 64, 2
+    Wq, Ws = _rand_q8(rng, E, d)
+    x = synthetic.normal(rng, 2, d)
+    xq, xl, xs = oracle.quantize_x2(x)
+    idx, wts, logits = oracle.route_q8(Wq, Ws, k, xq=xq, xs=xs, xl=xl)
+    for i in range(2):
+        l = [sum(Fraction(float(Ws[e, b])) * Fraction(float(xs[i, b])) *
+                 sum(int(Wq[e, t]) * (Fraction(int(xq[i, t])) + Fraction(int(xl[i, t]), 128))
+                     for t in range(32 * b, 32 * b + 32)) for b in range(2)) for e in range(E)]
+        for e in range(E):
+            assert abs(Fraction(logits[i, e]) - l[e]) <= abs(l[e]) * Fraction(2) ** -50 + Fraction(2) ** -80
+        best = max(itertools.combinations(range(E), k), key=lambda c: (sorted((l[j] for j in c), reverse=True), [-j for j in c]))
+        assert set(idx[i]) == set(best)
+    q = rng.integers(-126, 127, size=(1, d)).astype(np.int64)
+    lo = rng.integers(-63, 64, size=(1, d)).astype(np.int64)
+    q[:, ::32] = 127
+    lo[:, ::32] = 0
+    xe = ((2.0 ** -6) * (q + lo / 128.0)).astype(np.float32)
+    eq, el, es = oracle.quantize_x2(xe)
+    i2, w2, l2 = oracle.route_q8(Wq, Ws, k, xq=eq, xs=es, xl=el)
+    i0, w0, l0 = oracle.route_q8(Wq, Ws, k, x=xe)
+    assert np.array_equal(i2, i0) and np.max(np.abs(l2 - l0)) <= 1e-12 * np.max(np.abs(l0))
+
+
+def test_moe_shared_two_words_with_q8_router():
+    # the Q8_0 router under two words routes as route_q8 over the row's two
+    # words; the shared expert's part equals its own two-word dense FFN
+    v, m, x = _variant(96, sdff=128)
+    idx, wts, h, y = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 2, Wrq=v.Wrq, Wrs=v.Wrs,
+                                       shared=_shared(v))
+    xq, xl, xs = oracle.quantize_x2(x)
+    ridx, rw, _ = oracle.route_q8(v.Wrq, v.Wrs, 2, xq=xq, xs=xs, xl=xl)
+    assert np.array_equal(idx, ridx) and np.array_equal(wts, rw)
+    _, _, h0, y0 = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 2, Wrq=v.Wrq, Wrs=v.Wrs)
+    # the shared part alone: a one-expert mixture of the shared weights
+    _, _, hs1, ys1 = oracle.moe(x, np.zeros((1, x.shape[1]), np.float32), v.Sgq, v.Sgs, v.Suq, v.Sus, v.Sdq, v.Sds,
+                                1, 2)
+    assert np.max(np.abs((y - y0) - ys1)) <= 1e-12 * np.max(np.abs(ys1))
+    assert np.array_equal(h[:, 2 * m.Wgq.shape[0] // m.Wr.shape[0]:], hs1[:, 0])
+
+
 def test_route_q8_scale_index_is_row_then_block():
     # one row of ones per expert, scale 2^-e on block e+1 (mod 4) of row e
     # and 0 elsewhere: expert e's logit is 2^-e times that block's sum of x
