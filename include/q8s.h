@@ -330,7 +330,9 @@ Q8S_API int moe_topk_gate_up(const double *logits, const float *x, const int8_t 
  * q8_quantize_rows_x2), two exact int32 dots a block (as q8_gemv_x2), the
  * router still reading f32 x; it takes the three-launch form only (E <= 256,
  * d <= 8192; any rows, each row's weights read for that row), else
- * Q8S_EUNSUPPORTED.  The other mixture calls refuse act 2.
+ * Q8S_EUNSUPPORTED.  moe_ffn_block_ex takes act 2 the same way, its Q8_0
+ * router reading the row's two words (two exact dots a block) and its shared
+ * expert in two words.  The other mixture calls refuse act 2.
  */
 Q8S_API int moe_ffn_block(const float *h, const float *r, const float *w, float eps, const float *Wr,
                   const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,

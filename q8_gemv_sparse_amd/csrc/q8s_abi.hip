@@ -810,10 +810,7 @@ int block_common(const char *fn, const float *h, const float *r, const float *w,
     if ((act != 2 && (rc = check_act(fn, act))) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
         return rc;
     if (act == 2) {
-        // two words: the float router, no shared expert, the three-launch form
-        if (rt.Wrq || sdff > 0)
-            return fail(Q8S_EUNSUPPORTED, "%s: two-word numerics (act 2) are built for the float router without a "
-                        "shared expert only", fn);
+        // two words: the three-launch form
         if (!q8s::block_fused(rows, d, dff, E, act))
             return fail(Q8S_EUNSUPPORTED, "%s: two-word numerics (act 2) need E <= %d and d <= %lld", fn,
                         (int)q8s::ROUTE_FUSED_MAX_E, (long long)q8s::NORM_LOGITS_MAX_D);

@@ -173,22 +173,29 @@ __global__ void __launch_bounds__(NORM_THREADS)
                 float ys;
                 const uint2 c = quant8(v, ys);
                 const bool leader = (threadIdx.x & 3) == 0;
+                // two words (xl given): the low words, written and dotted
+                const uint2 lw = xl ? low8(v, c, ys) : make_uint2(0u, 0u);
                 if (writer && xq) {
                     *reinterpret_cast<uint2 *>(xq + row * d + base) = c;
-                    if (xl)  // two words: the low words too
-                        *reinterpret_cast<uint2 *>(xl + row * d + base) = low8(v, c, ys);
+                    if (xl)
+                        *reinterpret_cast<uint2 *>(xl + row * d + base) = lw;
                     if (leader)
                         xs[row * nb + base / QB] = ys;
                 }
                 if (RF == 2) {
-                    // the block's exact dot: this thread's 8 products, then
-                    // the four threads of the block (integer adds)
+                    // the block's exact dots: this thread's 8 products, then
+                    // the four threads of the block (integer adds); the low
+                    // words' dot is weighed 1/128 (zero in one word)
                     int is = __builtin_amdgcn_sdot4((int)c.x, (int)rq[g].x, 0, false);
                     is = __builtin_amdgcn_sdot4((int)c.y, (int)rq[g].y, is, false);
                     is += dpp_i<DPP_XOR1>(is);
                     is += dpp_i<DPP_XOR2>(is);
+                    int il = __builtin_amdgcn_sdot4((int)lw.x, (int)rq[g].x, 0, false);
+                    il = __builtin_amdgcn_sdot4((int)lw.y, (int)rq[g].y, il, false);
+                    il += dpp_i<DPP_XOR1>(il);
+                    il += dpp_i<DPP_XOR2>(il);
                     if (leader)
-                        lg += ((double)rs[g] * (double)ys) * (double)is;
+                        lg += ((double)rs[g] * (double)ys) * ((double)is + (double)il / 128.0);
                 }
             }
         }

@@ -178,3 +178,47 @@ def test_topk_gate_up_x2(d, dff, E, k):
     back = step * (host(hq).astype(np.float64) + host(hl).astype(np.float64) / 128.0)
     ref = rh.astype(np.float64)
     assert np.all(np.abs(back - ref) <= step / 256.0 * (1 + 1e-6) + 1e-5 * np.max(np.abs(ref)))
+
+
+# the block's linked variants in two words: moe_ffn_block_ex(act=2) with the
+# Q8_0 router (two exact dots a block over the row's two words) and/or the
+# shared expert, against oracle.moe_shared(act=2)
+X2_EX_CASES = [
+    # (d, dff, sdff, E, k, rows, q8_router)
+    (2048, 768, 0, 128, 8, 1, True),       # the Q8_0 router alone
+    (2048, 768, 1024, 128, 8, 1, True),    # + a shared expert wider than a slice of dff
+    (2048, 1408, 5632, 60, 4, 1, True),    # the shared-expert block's shape
+    (4096, 1408, 5632, 16, 4, 1, True),    # int8 rows in 4 slices
+    (96, 160, 96, 5, 3, 1, False),         # the float router with a shared expert, ragged
+    (256, 64, 800, 6, 2, 3, True),         # several rows
+]
+
+
+@pytest.mark.parametrize("d,dff,sdff,E,k,rows,q8_router", X2_EX_CASES)
+def test_block_ex_x2_matches_oracle(d, dff, sdff, E, k, rows, q8_router):
+    banner("moe_ffn_block_ex x2 d=%d dff=%d sdff=%d E=%d k=%d rows=%d q8_router=%s"
+           % (d, dff, sdff, E, k, rows, q8_router))
+    from gpu_helpers import route_ambiguous
+    v = synthetic.variant_inputs(35, d, dff, E, k, rows, sdff)
+    b, m = v.block, v.block.moe
+    W = [dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds)]
+    rk = dict(Wrq=dev(v.Wrq), Wrs=dev(v.Wrs)) if q8_router else dict(Wr=dev(m.Wr))
+    sh = tuple(dev(a) for a in (v.Sgq, v.Sgs, v.Suq, v.Sus, v.Sdq, v.Sds)) if sdff else None
+    s, idx, wts, out = q8.moe_ffn_block_ex(dev(b.h), dev(b.r), dev(b.w), 1e-6, *W, k, E, act=2, shared=sh, **rk)
+    rs, y64 = oracle.add_rmsnorm(b.h, b.r, b.w, 1e-6)
+    x = y64.astype(np.float32)
+    ork = dict(Wrq=v.Wrq, Wrs=v.Wrs) if q8_router else dict(Wr=m.Wr)
+    osh = (v.Sgq, v.Sgs, v.Suq, v.Sus, v.Sdq, v.Sds) if sdff else None
+    ridx, rw, _, ry = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, k, 2, shared=osh, **ork)
+    if q8_router:
+        xq, xl, xs = oracle.quantize_x2(x)
+        _, _, logits = oracle.route_q8(v.Wrq, v.Wrs, k, xq=xq, xs=xs, xl=xl)
+    else:
+        _, _, logits = oracle.route(x, m.Wr, k)
+    assert np.array_equal(host(s), rs)
+    assert not route_ambiguous(logits, k).any()
+    assert np.array_equal(host(idx), ridx)
+    assert rel_err(host(wts), rw) <= 1e-5
+    got = host(out)
+    for r in range(rows):
+        assert rel_err(got[r], ry[r]) <= TOL_X2_BLOCK, r
