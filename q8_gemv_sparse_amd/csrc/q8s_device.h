@@ -499,8 +499,12 @@ Q8S_DEV float silu(float z)
 // Decode gate-up launch shape per mode and row cut.  At these sizes the kernels are
 // bound by memory latency more than by bandwidth: many waves with one or two
 // rows' loads in flight each beat fewer waves with more (measured).
-//   f32 : 8 waves, one gate/up pair per lane group (two for short rows);
-//         tiles of 8 (or 16, 32) hidden outputs.
+//   f32 : 8 waves, one gate/up pair per lane group (two for rows of one
+//         chunk a lane, and for rows of four: 90.7 vs 93.8 us for the
+//         8-expert block at d 4096, where tiles of 8 outputs made 3584
+//         workgroups each paying the top-K; two pairs at d 2048 measured
+//         20.4 vs 19.6 us, sixteen waves slower everywhere); tiles of 8 (or
+//         16, 32) hidden outputs.
 //   int8: a tile is one 32-value block, so the workgroup also writes the
 //         block's Q8_0 form (the down projection's activation) once, in its
 //         epilogue: 16 waves of 2 pairs (8 of 1 for lane groups of 16); rows
@@ -510,7 +514,7 @@ template <int ACT, int LPR, int C>
 struct GuShape {
     static constexpr int G = WAVE / LPR;
     static constexpr int NW = ACT >= 1 ? (LPR == 64 ? 16 : 8) : 8;
-    static constexpr int U = ACT >= 1 ? (LPR == 64 ? 2 : 1) : ((C == 1 && LPR == 64) ? 2 : 1);
+    static constexpr int U = ACT >= 1 ? (LPR == 64 ? 2 : 1) : ((LPR == 64 && (C == 1 || C == 4)) ? 2 : 1);
     static constexpr int OPS = G * U;
     static constexpr int T = NW * OPS;
     static_assert(QB % T == 0, "a tile divides a 32-value block, so it divides dff");
