@@ -1,7 +1,10 @@
 """The two-word (~14-bit) int8 activation on the GPU against the oracle: the
-quantiser bit-exact (words, low words, scales), the GEMV within 1e-5 of the
-oracle's same-mode result (float32 block partials, as the float32 mode), and
-bit-exact where every float step is exact."""
+quantiser bit-exact (words, low words, scales); the GEMV within 1e-5 of the
+oracle's same-mode result (float32 block partials, as the float32 mode) and
+bit-exact where every float step is exact; the fused norm + GEMV bit-exact
+against the separate calls; the mixture block (moe_ffn_block, its gate-up
+stage, and moe_ffn_block_ex with the Q8_0 router and the shared expert)
+within 2.5e-4 of the oracle's two-word block, routing bit-exact."""
 import numpy as np
 import pytest
 
