@@ -120,6 +120,8 @@ def parse():
     p.add_argument("--kernel-launches", type=int, default=400, help="eager launches timed for the dominant kernel")
     p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="threads for the all-cores oracle run (0: every CPU available; 1: single-core only)")
     p.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     p.add_argument("--warm", action="store_true",
                    help="context only: every step on weight copy 0 and input row 0, so the weights stay cache-resident")
@@ -702,6 +704,18 @@ def make_workload(name, act, copies, separate=False):
 # ---------------------------------------------------------------------------
 
 
+def cpu_all_cores(wl, budget, threads):
+    """The same oracle steps on every host core at once: `threads` Python
+    threads, each running the workload's baseline loop for `budget` seconds
+    (the oracle is C called through ctypes, which releases the interpreter
+    lock, so the threads' steps run in parallel).  Returns the seconds per
+    step of all threads together."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(threads) as ex:
+        per = list(ex.map(lambda _: wl.cpu_baseline(budget)[0], range(threads)))
+    return 1.0 / sum(1.0 / p for p in per)
+
+
 def host_cpu():
     """The host's CPU model and the CPUs this process may run on."""
     model = "unknown CPU"
@@ -915,6 +929,12 @@ def main():
         per_step, sample = wl.cpu_baseline(args.cpu_budget)
         cpu = {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": sample + "; %.1f ms per step" % (per_step * 1e3), "host": host_cpu()}
+        threads = args.cpu_threads or len(os.sched_getaffinity(0))
+        if threads > 1:
+            per_all = cpu_all_cores(wl, args.cpu_budget, threads)
+            cpu["all_cores"] = {"value": round(step_bytes / per_all / 1e9, 4), "unit": "GB/s", "cores": threads,
+                                "sample": "%d threads, each its own steps for %.0f s; %.2f ms per step together"
+                                          % (threads, args.cpu_budget, per_all * 1e3)}
     out = {
         "metric": METRIC,
         "value": round(value, 2),
