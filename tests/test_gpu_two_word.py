@@ -225,3 +225,24 @@ def test_block_ex_x2_matches_oracle(d, dff, sdff, E, k, rows, q8_router):
     got = host(out)
     for r in range(rows):
         assert rel_err(got[r], ry[r]) <= TOL_X2_BLOCK, r
+
+
+def test_block_x2_scratch_needs_no_initial_contents_and_repeats():
+    # the block's scratch holds nothing between calls: a scratch full of
+    # garbage gives the same bits as a fresh one, and calls repeat exactly
+    banner("block x2 scratch reuse and determinism")
+    import torch
+    b = synthetic.block_inputs(23, 2048, 768, 128, 8, 1)
+    m = b.moe
+    W = [dev(a) for a in (m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds)]
+    h, r, w = dev(b.h), dev(b.r), dev(b.w)
+    nbytes = q8.q8s_scratch_bytes(q8.FN_BLOCK, 1, 2048, 768, 128, 8, q8.ACT_X2)
+    scratch = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device="cuda")
+    first = q8.moe_ffn_block(h, r, w, 1e-6, *W, m.k, act=q8.ACT_X2, scratch=scratch)
+    for _ in range(3):
+        again = q8.moe_ffn_block(h, r, w, 1e-6, *W, m.k, act=q8.ACT_X2, scratch=scratch)
+        for a, c in zip(first, again):
+            assert torch.equal(a, c)
+    fresh = q8.moe_ffn_block(h, r, w, 1e-6, *W, m.k, act=q8.ACT_X2)
+    for a, c in zip(first, fresh):
+        assert torch.equal(a, c)
