@@ -75,6 +75,7 @@ extern "C" {
 
 #define Q8S_ACT_F32 0  /* f32 activations (dequantise in kernel) */
 #define Q8S_ACT_INT8 1 /* one-word Q8_0 int8 activations */
+#define Q8S_ACT_X2 2   /* two-word int8 activations (the *_x2 calls and the whole-block calls) */
 
 /* Ids of the calls that take scratch, for q8s_scratch_bytes. */
 #define Q8S_FN_ROUTE 1
