@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the Q8_0 GEMV / sparse-MoE hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--act int8|f32]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--act int8|f32|x2]
 
 A step is one pass of the hot path over one batch of synthetic input.  The
 default workload is the batch-1 MoE FFN block at the Qwen3-30B-A3B-like shape
@@ -27,7 +27,13 @@ replays, and reported against the HBM roofline on its algorithmic bytes (the
 weight bytes one launch must read).  Both are also stated as a fraction of a
 measured ceiling: the library's plain streaming reader (q8s_stream_read) over
 2 GiB, and over cold slices of the dominant kernel's own size.  Each graph
-replay is then timed alone for the p10 / median / p90 of the step time.  The CPU oracle is timed on a bounded sample of the same workload.
+replay is then timed alone for the p10 / median / p90 of the step time.
+
+The CPU oracle is timed on a bounded sample of the same workload, on one core
+and on every available core at once (one thread each).  --act x2 runs the
+two-word numerics (the norm + GEMV and the mixture block); --warm (context
+only) keeps one weight copy and one input row, so the weights stay
+cache-resident.
 
 Prints one JSON line on stdout; details go to stderr.
 """
