@@ -525,7 +525,7 @@ class ChunkBlock(MoeBlock):
         # kernel
         super().__init__(name, cfg, "int8", copies, rows=cfg["rows"], pool=8, separate=True)
         self.dominant = "k_chunk_gate_up"
-        self.dominant_timed = "moe_gate_up: k_chunk_gate_up, then k_quantize_rows over the hidden rows"
+        self.dominant_timed = "moe_gate_up without the hidden rows' Q8_0 pass: k_chunk_gate_up alone"
         import synthetic
         np, torch = self.np, self.torch
         rng = np.random.default_rng(2)
@@ -546,6 +546,14 @@ class ChunkBlock(MoeBlock):
         super().step(c)
         Dq, Ds = self.D[c % self.copies]
         self.q8.q8_gemv(Dq, Ds, xq=self.xq, xs=self.xs, y=self.dense_out, act=self.q8.ACT_INT8)
+
+    def launch_dominant(self, c):
+        # the grouped gate-up kernel alone: the float32 hidden rows, without
+        # the quantise pass the step runs after it
+        q8 = self.q8
+        W = self.W[c % self.copies]
+        q8.moe_gate_up(W[1], W[2], W[3], W[4], self.idx[c % self.copies], self.E, xq=self.xq, xs=self.xs,
+                       h=self.hf, act=q8.ACT_INT8, want_q8=False)
 
     def weight_bytes(self, c=None):
         return super().weight_bytes(c) + self.dense_bytes

@@ -190,7 +190,9 @@ Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_
  * [rows, k, dff] (required for F32, and for INT8 with rows > 1, where the
  * grouped chunk kernels stage the float32 hidden rows in it before a quantise
  * pass forms hq/hs; optional for INT8 with one row).  hq/hs: device int8
- * [rows, k, dff] and f32 [rows, k, dff/32] (INT8 only, required).  A choice
+ * [rows, k, dff] and f32 [rows, k, dff/32] (INT8 only; required, except that
+ * a chunk of rows in the grouped kernels may pass both NULL to write only the
+ * float32 rows and quantise them itself with q8_quantize_rows).  A choice
  * whose expert index is invalid gets zeros.
  */
 Q8S_API int moe_gate_up(const float *x, const int8_t *xq, const float *xs,

@@ -309,11 +309,12 @@ def moe_route_topk(x, Wr, k, idx=None, wts=None, scratch=None, stream=None):
 
 
 def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq=None, hs=None, act=ACT_F32,
-                want_h=True, stream=None):
+                want_h=True, want_q8=True, stream=None):
     """h[rows, k, dff] = SiLU(Wg[e] x) * (Wu[e] x) for each kept expert e.
     Returns (h, hq, hs): INT8 also writes the hidden row's Q8_0 form; h may be
     skipped there for one row (want_h=False); with several rows it is the
-    chunk kernels' staging and is always written."""
+    chunk kernels' staging and is always written, and want_q8=False leaves
+    out the Q8_0 form (hq, hs returned None)."""
     for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq")):
         _dev(t, torch.int8, n)
     for t, n in ((Wgs, "Wgs"), (Wus, "Wus")):
@@ -327,9 +328,9 @@ def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq
         _dev(x, torch.float32, "x")
     else:
         _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
-        if hq is None:
+        if hq is None and want_q8:
             hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
-        if hs is None:
+        if hs is None and want_q8:
             hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
     if h is None and (want_h or act == ACT_F32 or rows > 1):  # several int8 rows stage h
         h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)
@@ -445,9 +446,9 @@ def moe_topk_gate_up(logits, Wgq, Wgs, Wuq, Wus, k, x=None, xq=None, xs=None, id
         _dev(x, torch.float32, "x")
     else:
         _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
-        if hq is None:
+        if hq is None and want_q8:
             hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
-        if hs is None:
+        if hs is None and want_q8:
             hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
     if h is None and (want_h or act == ACT_F32):
         h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)

@@ -361,10 +361,19 @@ int moe_gate_up(const float *x, const int8_t *xq, const float *xs, const int8_t 
                         "stage the float32 hidden rows there before forming their Q8_0 form)", fn);
         ins.push_back({xq, (size_t)(rows * d), "xq"});
         ins.push_back({xs, (size_t)(rows * d / 32) * 4, "xs"});
+        // the grouped chunk kernels write the float32 hidden rows and then
+        // form their Q8_0 form in a pass of their own, which a caller may
+        // leave out (hq and hs both NULL) to quantise the rows itself
+        const bool chunk = rows > 1 && q8s::chunk_supported(d, dff);
+        if (!hq && !hs && !chunk)
+            return fail(Q8S_EINVAL, "%s: int8 numerics: `hq`/`hs` are required (only a chunk of rows in the grouped "
+                        "kernels may leave out the hidden rows' Q8_0 form)", fn);
         if (h)
             outs.push_back({h, nh * 4, "h"});
-        outs.push_back({hq, nh, "hq"});
-        outs.push_back({hs, nh / 32 * 4, "hs"});
+        if (hq || hs) {
+            outs.push_back({hq, nh, "hq"});
+            outs.push_back({hs, nh / 32 * 4, "hs"});
+        }
     }
     if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
         return rc;
@@ -646,10 +655,19 @@ int topk_gate_up_common(const char *fn, const double *logits, const float *x, co
     } else {
         ins.push_back({xq, (size_t)(rows * d), "xq"});
         ins.push_back({xs, (size_t)(rows * d / 32) * 4, "xs"});
+        // the grouped chunk kernels write the float32 hidden rows and then
+        // form their Q8_0 form in a pass of their own, which a caller may
+        // leave out (hq and hs both NULL) to quantise the rows itself
+        const bool chunk = rows > 1 && q8s::chunk_supported(d, dff);
+        if (!hq && !hs && !chunk)
+            return fail(Q8S_EINVAL, "%s: int8 numerics: `hq`/`hs` are required (only a chunk of rows in the grouped "
+                        "kernels may leave out the hidden rows' Q8_0 form)", fn);
         if (h)
             outs.push_back({h, nh * 4, "h"});
-        outs.push_back({hq, nh, "hq"});
-        outs.push_back({hs, nh / 32 * 4, "hs"});
+        if (hq || hs) {
+            outs.push_back({hq, nh, "hq"});
+            outs.push_back({hs, nh / 32 * 4, "hs"});
+        }
     }
     if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
         return rc;

@@ -531,9 +531,10 @@ hipError_t gu_chunk_go(const MoeArgs &a, hipStream_t st)
     hipLaunchKernelGGL(k_chunk_gate_up, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus,
                        a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
+    if (err != hipSuccess || !a.hq)
         return err;
-    // the hidden rows' Q8_0 form, for the down projection
+    // the hidden rows' Q8_0 form, for the down projection (unless the caller
+    // forms it itself)
     return quantize_launch(a.h, a.rows * a.k, a.dff, a.hq, a.hs, st);
 }
 

@@ -363,3 +363,10 @@ def test_block_scratch_holds_the_two_word_rows():
         one = q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, q8.ACT_INT8)
         two = q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, 2)
         assert two == one + al(rows * d) + al(rows * k * dff)
+
+
+def test_gate_up_without_q8_form_only_for_chunks():
+    # one row (the decode kernels quantise in their epilogue): hq/hs required
+    assert gate_up(act=1, rows=1, hq=None, hs=None) == -1 and "only a chunk" in _err()
+    # a chunk may leave both out, not one of them
+    assert gate_up(act=1, rows=4, hq=None) == -1 and "`hq` is null" in _err()

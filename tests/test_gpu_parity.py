@@ -418,3 +418,20 @@ def test_chunk_full_size():
     ref = oracle.gemv_i8(Dq, Ds, rq, rs)
     for r in range(cfg["rows"]):
         assert rel_err(Y[r], ref[r]) <= TOL_I8, r
+
+
+def test_chunk_gate_up_without_q8_pass():
+    # a chunk's gate-up may leave out the hidden rows' Q8_0 pass: the float32
+    # rows are the same bits, and quantising them afterwards gives the pass's
+    # words and scales
+    banner("chunk gate-up without the Q8_0 pass")
+    m = synthetic.moe_inputs(7, 2048, 768, 128, 8, rows=64)
+    xq, xs = q8.q8_quantize_rows(dev(m.x))
+    idx, _ = q8.moe_route_topk(dev(m.x), dev(m.Wr), m.k)
+    W = [dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus)]
+    h1, hq1, hs1 = q8.moe_gate_up(*W, idx, m.E, xq=xq, xs=xs, act=q8.ACT_INT8)
+    h2, hq2, hs2 = q8.moe_gate_up(*W, idx, m.E, xq=xq, xs=xs, act=q8.ACT_INT8, want_q8=False)
+    assert hq2 is None and hs2 is None
+    assert torch.equal(h1, h2)
+    q3, s3 = q8.q8_quantize_rows(h2.reshape(-1, 768))
+    assert torch.equal(q3.reshape(hq1.shape), hq1) and torch.equal(s3.reshape(hs1.shape), hs1)
