@@ -1,0 +1,33 @@
+"""bench.py's host-side contract, without a GPU: it measures one GPU only, so
+any other --gpus exits at once (status 2) with a message saying so, before
+importing torch or touching a device; and two-word numerics are refused for
+the workloads that do not have them."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=120)
+
+
+def test_more_than_one_gpu_is_refused():
+    for n in ("2", "8"):
+        p = run("--gpus", n)
+        assert p.returncode == 2
+        assert "one GPU" in p.stderr and p.stdout == ""
+
+
+def test_two_words_refused_where_not_built():
+    import bench
+    for name, sep in (("chunk64_moe_d2048_dense4096", False), ("moe_shared_d2048_dff1408_e60_k4_s5632", False),
+                      ("moe_d2048_dff768_e128_k8", True)):
+        try:
+            bench.make_workload(name, "x2", 1, separate=sep)
+        except SystemExit as e:
+            assert "two-word" in str(e)
+        else:
+            raise AssertionError("x2 accepted for %s" % name)
