@@ -446,9 +446,9 @@ def moe_topk_gate_up(logits, Wgq, Wgs, Wuq, Wus, k, x=None, xq=None, xs=None, id
         _dev(x, torch.float32, "x")
     else:
         _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
-        if hq is None and want_q8:
+        if hq is None:
             hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
-        if hs is None and want_q8:
+        if hs is None:
             hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
     if h is None and (want_h or act == ACT_F32):
         h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)
