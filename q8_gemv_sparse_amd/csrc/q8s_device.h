@@ -532,24 +532,26 @@ Q8S_DEV bool route_better(double l, int e, double l2, int e2) { return l > l2 ||
 constexpr int TOPK_LDS_E = 256;
 struct alignas(16) TopkLds {
     double L[TOPK_LDS_E];         // the row's logits
-    double cv[TOPK_LDS_E];        // candidates' logits
-    uint32_t ck[TOPK_LDS_E + 4];  // coarse keys, padded with zeros to whole quads
-    int cand[TOPK_LDS_E];         // candidates' expert indices
+    uint32_t ck[TOPK_LDS_E + 4];  // codes' upper halves (coarse keys), padded with zeros to whole quads
+    uint32_t lo[TOPK_LDS_E];      // codes' lower halves
     int ch[32];                   // the choices, in rank order
     double kl[32];                // their logits
-    int n;                        // candidates
 };
 
-// An order-preserving 32-bit coarse key of a logit: the top half of a 64-bit
-// code whose unsigned order is the order of the values (-0 taken as +0, so
-// equal values get equal keys).  A strictly greater key means a strictly
-// greater logit; equal keys decide nothing.  Finite logits never get key 0.
-Q8S_DEV uint32_t coarse_key(double v)
+// An order-preserving 64-bit code of a logit: its unsigned order is the order
+// of the values (-0 taken as +0, so equal values get equal codes).  NaNs get
+// codes too (above +inf or below -inf by their sign), so ranking by code is a
+// strict total order with the index as tie-break and every rank is taken
+// exactly once, whatever the logits hold.
+Q8S_DEV uint64_t route_code(double v)
 {
     const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
-    const uint64_t m = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-    return (uint32_t)(m >> 32);
+    return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
+
+// The code's upper half: a strictly greater key means a strictly greater
+// logit; equal keys decide nothing.  Finite logits never get key 0.
+Q8S_DEV uint32_t coarse_key(double v) { return (uint32_t)(route_code(v) >> 32); }
 
 // Sum over each group of S consecutive lanes, S in {1, 2, 4, 8}, S uniform
 // across the wave; every lane of a group receives its group's sum.
@@ -574,80 +576,78 @@ Q8S_DEV int lanes_per_item(int items)
     return S;
 }
 
-// Loads a row's E logits (E <= TOPK_LDS_E) and their coarse keys; every thread
+// Loads a row's E logits (E <= TOPK_LDS_E) and their codes; every thread
 // calls it, and the caller synchronises before topk_select.
 Q8S_DEV void topk_load(TopkLds &t, const double *__restrict__ lr, int E)
 {
     for (int i = threadIdx.x; i < ((E + 3) & ~3); i += blockDim.x) {
         if (i < E) {
             const double v = lr[i];
+            const uint64_t c = route_code(v);
             t.L[i] = v;
-            t.ck[i] = coarse_key(v);
+            t.ck[i] = (uint32_t)(c >> 32);
+            t.lo[i] = (uint32_t)c;
         } else {
             t.ck[i] = 0u;
         }
     }
-    if (threadIdx.x == 0)
-        t.n = 0;
 }
 
 // The K best of the row's E <= blockDim.x logits by (logit descending, index
 // ascending), in rank order, into t.ch / t.kl.  Every thread calls it; the
-// caller synchronises before reading the choices.
-//   1. Coarse count: logit i's count of strictly greater coarse keys, by S
-//      threads sharing the E keys in interleaved quads.  A logit with K or
-//      more strictly greater keys has K strictly greater logits, so it is not
-//      kept; one with fewer is a candidate.  Every kept logit is a candidate,
-//      and every candidate's key (hence logit) exceeds every non-candidate's,
-//      so a candidate's rank among the candidates is its rank among all E.
-//   2. Exact rank among the candidates (usually exactly K) in double, ties to
-//      the lower index.
-// Both passes are a handful of instructions per thread: the exact compare of
-// all E^2 pairs in double measured several microseconds on a full workgroup.
+// caller synchronises before reading the choices.  Logit i's rank is the
+// number of logits ranked before it, counted by S threads sharing the E keys
+// in interleaved quads:
+//   rank_i = #{w : key_w > key_i}
+//          + #{w != i : key_w == key_i, and (lo_w > lo_i, or lo_w == lo_i and w < i)},
+// which for non-NaN logits is #{w : l_w > l_i, or l_w == l_i and w < i}: the
+// code is order-preserving, so a greater key is a greater logit and, on equal
+// keys, the lower halves decide.  The second term is taken only for a logit
+// whose key some other logit shares (the threads count equal keys alongside
+// greater ones), which near-equal logits make rare.  The ranks are a
+// permutation of 0..E-1, so each of the K slots gets exactly one writer.
+// Ranking all E in one pass with no candidate list keeps it to one LDS pass
+// between two barriers; an exact compare of all E^2 pairs in double measured
+// several microseconds on a full workgroup.
 Q8S_DEV void topk_select(TopkLds &t, int E, int k)
 {
-    {
-        const int S = lanes_per_item(E);
-        const int i = threadIdx.x / S, part = threadIdx.x % S;
-        int c = 0;
-        if (i < E) {
-            const uint32_t ci = t.ck[i];
-            const uint4 *q = reinterpret_cast<const uint4 *>(t.ck);
-            const int nq = (E + 3) >> 2;
-            for (int q0 = part; q0 < nq; q0 += 4 * S) {
-                uint4 v[4];
+    const int S = lanes_per_item(E);
+    const int i = threadIdx.x / S, part = threadIdx.x % S;
+    int gt = 0, ge = 0;
+    uint32_t ci = 0u;
+    if (i < E) {
+        ci = t.ck[i];
+        const uint4 *q = reinterpret_cast<const uint4 *>(t.ck);
+        const int nq = (E + 3) >> 2;
+        for (int q0 = part; q0 < nq; q0 += 4 * S) {
+            uint4 v[4];
 #pragma unroll
-                for (int u = 0; u < 4; u++)
-                    v[u] = q0 + u * S < nq ? q[q0 + u * S] : make_uint4(0u, 0u, 0u, 0u);
+            for (int u = 0; u < 4; u++)
+                v[u] = q0 + u * S < nq ? q[q0 + u * S] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-                for (int u = 0; u < 4; u++)
-                    c += (v[u].x > ci) + (v[u].y > ci) + (v[u].z > ci) + (v[u].w > ci);
+            for (int u = 0; u < 4; u++) {
+                gt += (v[u].x > ci) + (v[u].y > ci) + (v[u].z > ci) + (v[u].w > ci);
+                ge += (v[u].x >= ci) + (v[u].y >= ci) + (v[u].z >= ci) + (v[u].w >= ci);
             }
         }
-        c = sum_lanes8(c, S);
-        if (i < E && part == 0 && c < k) {
-            const int p = atomicAdd(&t.n, 1);
-            t.cand[p] = i;
-            t.cv[p] = t.L[i];
-        }
     }
-    __syncthreads();
-    const int C = t.n;
-    const int S = lanes_per_item(C);
-    const int u = threadIdx.x / S, part = threadIdx.x % S;
-    int r = 0;
-    int i = 0;
-    double li = 0.0;
-    if (u < C) {
-        i = t.cand[u];
-        li = t.cv[u];
-        for (int w = part; w < C; w += S)
-            r += route_better(t.cv[w], t.cand[w], li, i) ? 1 : 0;
+    int r = sum_lanes8(gt, S);
+    // ge counts the logit's own key; more than that is a coarse tie (every
+    // lane of the item's group sees the same sum, so the group branches as one)
+    const int eq = sum_lanes8(ge, S) - r;
+    int extra = 0;
+    if (i < E && eq > 1) {
+        const uint32_t li = t.lo[i];
+        for (int w = part; w < E; w += S)
+            if (w != i && t.ck[w] == ci) {
+                const uint32_t lw = t.lo[w];
+                extra += (lw > li || (lw == li && w < i)) ? 1 : 0;
+            }
     }
-    r = sum_lanes8(r, S);
-    if (u < C && part == 0 && r < k) {
+    r += sum_lanes8(extra, S);
+    if (i < E && part == 0 && r < k) {
         t.ch[r] = i;
-        t.kl[r] = li;
+        t.kl[r] = t.L[i];
     }
 }
 

@@ -14,10 +14,9 @@
 //             From 16 rows up, k_logits_tile: one workgroup per 4 experts x 8
 //             rows, reading each row from cache once for several products.
 //   k_topk    one workgroup per row: the K best by (logit descending, index
-//             ascending) -- for E <= 256 a coarse count over order-preserving
-//             32-bit keys picks the candidates and an exact double-precision
-//             rank orders them (topk_select), beyond that K selection rounds
-//             of a workgroup arg-max -- then the kept weights.
+//             ascending) -- for E <= 256 every logit's exact rank in one pass
+//             over order-preserving 64-bit codes (topk_select), beyond that K
+//             selection rounds of a workgroup arg-max -- then the kept weights.
 // Handing the logits over at the kernel boundary costs one short launch; doing
 // it inside one launch needs a device-scope release by every workgroup, which
 // measured several times slower on this chip.
@@ -280,7 +279,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ 
                 t.ch[jj] = wi;
                 t.kl[jj] = wb;
             }
-            if ((int)threadIdx.x == (wi % RT_THREADS))
+            if (wi < E && (int)threadIdx.x == (wi % RT_THREADS))
                 Lbig[wi] = -INFINITY;
             __syncthreads();
         }

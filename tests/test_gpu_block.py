@@ -171,15 +171,22 @@ def host_topk(logits, k):
 
 
 @pytest.mark.parametrize("act", [0, 1])
-@pytest.mark.parametrize("E,k,ties", [(128, 8, False), (8, 2, False), (256, 32, True), (5, 5, True), (1, 1, False)])
+@pytest.mark.parametrize("E,k,ties", [(128, 8, ""), (8, 2, ""), (256, 32, "exact"), (5, 5, "exact"), (1, 1, ""),
+                                        (128, 8, "near"), (256, 32, "near")])
 def test_topk_gate_up(E, k, ties, act):
     banner("moe_topk_gate_up E=%d k=%d ties=%s act=%d" % (E, k, ties, act))
     rows, d, dff = 2, 256, 96
     m = synthetic.moe_inputs(26, d, dff, E, k, rows)
     rng = np.random.default_rng(27)
     logits = rng.standard_normal((rows, E))
-    if ties:
+    if ties == "exact":
         logits = np.round(logits * 2) / 2  # many exact ties
+    elif ties == "near":
+        # logits equal in their upper 32 bits and apart in the lower ones,
+        # exact ties among them, and signed zeros (equal logits)
+        logits = 1.0 + rng.integers(0, 6, (rows, E)) * 2.0**-40
+        logits[:, 1::7] = np.where(rng.random((rows, logits[:, 1::7].shape[1])) < 0.5, 0.0, -0.0)
+        logits[:, 3] = 1.0 + 9 * 2.0**-40
     Wgq, Wgs, Wuq, Wus = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus))
     x = dev(m.x)
     xq, xs = q8.q8_quantize_rows(x)
