@@ -261,6 +261,29 @@ def test_route_ties_many_rows():
     assert rel_err(host(wts), rw) <= TOL_F32
 
 
+@pytest.mark.parametrize("E", [200, 300])
+def test_route_near_ties(E):
+    # a one-hot row makes each logit exactly its router entry; entries one to
+    # three float32 ulps above 1.0 share the upper 32 bits of their double
+    # code, so the ranking is settled by the lower halves and, on equal
+    # entries, by the index (E 300 takes the arg-max rounds instead)
+    banner("route near ties E=%d" % E)
+    d, k = 64, 8
+    rng = np.random.default_rng(9)
+    x = np.zeros((1, d), np.float32)
+    x[0, 5] = 1.0
+    Wr = (0.01 * synthetic.normal(rng, E, d)).astype(np.float32)
+    col = np.float32(1.0) + rng.integers(0, 4, E).astype(np.float32) * np.float32(2.0 ** -23)
+    col[::9] = np.float32(0.5)
+    Wr[:, 5] = col
+    idx, wts = q8.moe_route_topk(dev(x), dev(Wr), k)
+    logits = col.astype(np.float64)
+    want = np.lexsort((np.arange(E), -logits))[:k]
+    assert list(host(idx)[0]) == list(want)
+    p = np.exp(logits[want] - logits[want[0]])
+    assert rel_err(host(wts)[0], p / p.sum()) <= TOL_F32
+
+
 def test_route_scratch_reuse():
     # one scratch sized for 64 rows serves calls of any smaller size
     banner("route scratch reuse")
