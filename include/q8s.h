@@ -297,7 +297,10 @@ Q8S_API int add_rmsnorm_router(const float *h, const float *r, const float *w, f
  * device int32 [rows, k] and wts: device f32 [rows, k] are outputs here.
  * Rows run one by one (a chunk of rows in INT8 mode reads each expert once
  * per row here; moe_gate_up groups them).  Limits: E <= 256
- * (Q8S_EUNSUPPORTED beyond), k <= min(32, E).
+ * (Q8S_EUNSUPPORTED beyond), k <= min(32, E).  A NaN logit ranks above every
+ * number when its sign bit is clear and below every number when it is set
+ * (its weight is then NaN); the choices are K distinct experts whatever the
+ * logits hold.
  */
 Q8S_API int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, const float *xs,
                      const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,

@@ -545,7 +545,8 @@ struct alignas(16) TopkLds {
 // exactly once, whatever the logits hold.
 Q8S_DEV uint64_t route_code(double v)
 {
-    const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+    // a select, not v + 0.0, so a NaN keeps its sign bit
+    const uint64_t b = (uint64_t)__double_as_longlong(v == 0.0 ? 0.0 : v);
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 

@@ -210,6 +210,32 @@ def test_topk_gate_up(E, k, ties, act):
             assert torch.equal(qq.reshape(rq.shape), rq) and torch.equal(ss.reshape(rs.shape), rs)
 
 
+def test_topk_gate_up_nan_logits():
+    # NaN logits: a NaN with the sign bit clear ranks above every number, one
+    # with it set below; the choices stay K distinct experts in range
+    banner("moe_topk_gate_up NaN logits")
+    rows, d, dff, E, k = 2, 256, 96, 128, 8
+    m = synthetic.moe_inputs(26, d, dff, E, k, rows)
+    rng = np.random.default_rng(28)
+    logits = rng.standard_normal((rows, E))
+    pos, neg = np.float64(np.nan), -np.float64(np.nan)
+    assert not np.signbit(pos) and np.signbit(neg)
+    logits[0, [5, 77]] = pos
+    logits[0, [1, 2, 3]] = neg
+    logits[1, :] = neg
+    logits[1, 9] = 0.5
+    Wgq, Wgs, Wuq, Wus = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus))
+    idx, wts, h, hq, hs = q8.moe_topk_gate_up(dev(logits), Wgq, Wgs, Wuq, Wus, k, x=dev(m.x), act=0)
+    idx = host(idx)
+    for r in range(rows):
+        assert len(set(idx[r].tolist())) == k and idx[r].min() >= 0 and idx[r].max() < E
+    # row 0: the two positive NaNs by index, then the six largest numbers
+    finite = [e for e in np.lexsort((np.arange(E), -np.nan_to_num(logits[0], nan=-np.inf))) if not np.isnan(logits[0, e])]
+    assert list(idx[0]) == [5, 77] + finite[:k - 2]
+    # row 1: the one number, then negative NaNs by index
+    assert list(idx[1]) == [9, 0, 1, 2, 3, 4, 5, 6]
+
+
 @pytest.mark.parametrize("act", [0, 1])
 @pytest.mark.parametrize("d,E", [(4096, 8), (2048, 16), (96, 3)])
 def test_block_few_experts_equals_stage_calls(d, E, act):
