@@ -262,7 +262,9 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
 // step for lane groups of 64 holding 4 chunks, e.g. 22 vs 23.4 us for the
 // 8-expert block's int8 down projection; two for lane groups of 16 holding 3,
 // so a wave's 8 rows of a 768-value hidden row load in one step: 18.25 vs
-// 18.39 us for the 128-expert block).
+// 18.39 us for the 128-expert block; two for lane groups holding 2, in int8
+// as in f32: 24.5 vs 25.2 us a step for the shared-expert block, whose
+// 1408- and 5632-value hidden rows take lane groups of 64 holding 2).
 template <int ACT, int LPR, int C>
 constexpr int dn_unroll()
 {
@@ -270,7 +272,7 @@ constexpr int dn_unroll()
         return C >= 3 ? 1 : (C == 2 ? 2 : (LPR == 16 ? 2 : 4));
     if (C == 3 && LPR == 16)
         return 2;
-    return C >= 3 ? 1 : (LPR == 16 ? 2 : 4);
+    return C >= 3 ? 1 : (C == 2 ? 2 : (LPR == 16 ? 2 : 4));
 }
 
 // Waves take (slot, slice) pairs: pairs j*ks + s for the K slots, then
