@@ -510,11 +510,17 @@ Q8S_DEV float silu(float z)
 //         epilogue: 16 waves of 2 pairs (8 of 1 for lane groups of 16); rows
 //         longer than 2048 are cut into 2048-value slices (gu_slices), which
 //         keeps each wave at 8 loads in flight.
-template <int ACT, int LPR, int C>
+//   V = 1 (int8, lane groups of 64): the same 32-output tile in 8 waves of 4
+//         pairs, for launches of more tiles than the chip has CUs, where
+//         smaller workgroups share the CUs more evenly (the shared-expert
+//         block's 352 tiles: 23.5 vs 24.6 us a step; the 128-expert block's
+//         192 tiles: 18.7 vs 18.1 us, so V = 0 there).
+template <int ACT, int LPR, int C, int V = 0>
 struct GuShape {
+    static_assert(V == 0 || (ACT >= 1 && LPR == 64), "the 8-wave int8 shape is for lane groups of 64");
     static constexpr int G = WAVE / LPR;
-    static constexpr int NW = ACT >= 1 ? (LPR == 64 ? 16 : 8) : 8;
-    static constexpr int U = ACT >= 1 ? (LPR == 64 ? 2 : 1) : ((LPR == 64 && (C == 1 || C == 4)) ? 2 : 1);
+    static constexpr int NW = ACT >= 1 ? (LPR == 64 ? (V ? 8 : 16) : 8) : 8;
+    static constexpr int U = ACT >= 1 ? (LPR == 64 ? (V ? 4 : 2) : 1) : ((LPR == 64 && (C == 1 || C == 4)) ? 2 : 1);
     static constexpr int OPS = G * U;
     static constexpr int T = NW * OPS;
     static_assert(QB % T == 0, "a tile divides a 32-value block, so it divides dff");

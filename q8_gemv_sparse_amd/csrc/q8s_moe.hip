@@ -54,15 +54,15 @@ struct GuLds {
 // partial sums meet in LDS.
 // The tile's weight rows start at row rbase of the gate/up matrices given
 // (an expert's or the shared expert's), its hidden values at hbase.
-template <int ACT, int LPR, int C>
-Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C>::T> &sm, bool valid, int64_t row, int64_t rbase, int64_t hbase,
+template <int ACT, int LPR, int C, int V>
+Q8S_DEV void gate_up_tile(GuLds<GuShape<ACT, LPR, C, V>::T> &sm, bool valid, int64_t row, int64_t rbase, int64_t hbase,
                           const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                           const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs,
                           const int8_t *__restrict__ Wuq, const float *__restrict__ Wus, int d, int ks,
                           float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs,
                           const int8_t *__restrict__ xl, int8_t *__restrict__ hl)
 {
-    using S = GuShape<ACT, LPR, C>;
+    using S = GuShape<ACT, LPR, C, V>;
     constexpr int G = S::G, U = S::U, OPS = S::OPS, T = S::T, NW = S::NW;
     constexpr int STEPS = T / OPS;
 
@@ -198,15 +198,15 @@ Q8S_DEV GuTile gu_tile(int bx, int k, int tpe, int T)
 // gate-up with the choices given: one workgroup per tile of one (row, slot),
 // grid (k*dff/T + sdff/T, rows).  SH: with a shared expert (a kernel of its
 // own, so the mixture without one runs the plain code).
-template <int ACT, int LPR, int C, bool SH>
-__global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
+template <int ACT, int LPR, int C, bool SH, int V>
+__global__ void __launch_bounds__((GuShape<ACT, LPR, C, V>::NW * WAVE))
     k_gate_up(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
               const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
               const float *__restrict__ Wus, SharedW sw, const int32_t *__restrict__ idx, int d, int dff, int E,
               int k, int ks, float *__restrict__ h, int8_t *__restrict__ hq, float *__restrict__ hs,
               const int8_t *__restrict__ xl, int8_t *__restrict__ hl)
 {
-    constexpr int T = GuShape<ACT, LPR, C>::T;
+    constexpr int T = GuShape<ACT, LPR, C, V>::T;
     __shared__ GuLds<T> sm;
     const int64_t row = blockIdx.y;
     const GuTile t = gu_tile<SH>(blockIdx.x, k, dff / T, T);
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     const int e = t.shared ? 0 : idx[row * k + t.j];
     const bool valid = t.shared || (e >= 0 && e < E);
     const int64_t rbase = t.shared ? t.o0 : (int64_t)(valid ? e : 0) * dff + t.o0;
-    gate_up_tile<ACT, LPR, C>(sm, valid, row, rbase, hbase, x, xq, xs, t.shared ? sw.gq : Wgq,
+    gate_up_tile<ACT, LPR, C, V>(sm, valid, row, rbase, hbase, x, xq, xs, t.shared ? sw.gq : Wgq,
                               t.shared ? sw.gs : Wgs, t.shared ? sw.uq : Wuq, t.shared ? sw.us : Wus, d, ks, h, hq,
                               hs, xl, hl);
 }
@@ -224,8 +224,8 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
 // reads its expert from the result, so the choices need no launch of their
 // own; the workgroup of tile 0, slot 0 writes the row's idx and wts for the
 // down-combine launch.  The shared expert's workgroups need no ranking.
-template <int ACT, int LPR, int C, bool SH>
-__global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
+template <int ACT, int LPR, int C, bool SH, int V>
+__global__ void __launch_bounds__((GuShape<ACT, LPR, C, V>::NW * WAVE))
     k_route_gate_up(const double *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ wts,
                     const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                     const int8_t *__restrict__ Wgq, const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq,
@@ -234,14 +234,14 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
                     const int8_t *__restrict__ xl, int8_t *__restrict__ hl)
 {
     static_assert(ROUTE_FUSED_MAX_E <= TOPK_LDS_E, "the row's logits fit the top-K LDS");
-    constexpr int T = GuShape<ACT, LPR, C>::T;
+    constexpr int T = GuShape<ACT, LPR, C, V>::T;
     __shared__ GuLds<T> sm;
     __shared__ TopkLds tk;
     const int64_t row = blockIdx.y;
     const GuTile t = gu_tile<SH>(blockIdx.x, k, dff / T, T);
     const int64_t hbase = row * ((int64_t)k * dff + (SH ? sw.sdff : 0)) + (int64_t)t.j * dff + t.o0;
     if (t.shared) {
-        gate_up_tile<ACT, LPR, C>(sm, true, row, t.o0, hbase, x, xq, xs, sw.gq, sw.gs, sw.uq, sw.us, d, ks, h, hq,
+        gate_up_tile<ACT, LPR, C, V>(sm, true, row, t.o0, hbase, x, xq, xs, sw.gq, sw.gs, sw.uq, sw.us, d, ks, h, hq,
                                   hs, xl, hl);
         return;
     }
@@ -250,7 +250,7 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C>::NW * WAVE))
     topk_select(tk, E, k);
     __syncthreads();
     const int e = __builtin_amdgcn_readfirstlane(tk.ch[t.j]);
-    gate_up_tile<ACT, LPR, C>(sm, true, row, (int64_t)e * dff + t.o0, hbase, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, ks, h,
+    gate_up_tile<ACT, LPR, C, V>(sm, true, row, (int64_t)e * dff + t.o0, hbase, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, ks, h,
                               hq, hs, xl, hl);
     // the choices and weights go out after the tile, off its critical path
     // (only the down-combine launch reads them)
@@ -387,34 +387,34 @@ SharedW shared_w(const MoeArgs &a)
     return SharedW{a.Sgq, a.Sgs, a.Suq, a.Sus, a.Sdq, a.Sds, (int)a.sdff};
 }
 
-template <int ACT, int LPR, int C>
+template <int ACT, int LPR, int C, int V>
 hipError_t gu_go(const MoeArgs &a, int ks, hipStream_t st)
 {
-    using S = GuShape<ACT, LPR, C>;
+    using S = GuShape<ACT, LPR, C, V>;
     dim3 grid((unsigned)((a.k * a.dff + a.sdff) / S::T), (unsigned)a.rows);
     if (a.sdff)
-        hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, true>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
+        hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, true, V>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
                            a.Wgs, a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
                            a.hq, a.hs, a.xl, a.hl);
     else
-        hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, false>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
+        hipLaunchKernelGGL((k_gate_up<ACT, LPR, C, false, V>), grid, dim3(S::NW * WAVE), 0, st, a.x, a.xq, a.xs, a.Wgq,
                            a.Wgs, a.Wuq, a.Wus, shared_w(a), a.idx, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, a.h,
                            a.hq, a.hs, a.xl, a.hl);
     return hipGetLastError();
 }
 
-template <int ACT, int LPR, int C>
+template <int ACT, int LPR, int C, int V>
 hipError_t rgu_go(const MoeArgs &a, int ks, hipStream_t st)
 {
-    using S = GuShape<ACT, LPR, C>;
+    using S = GuShape<ACT, LPR, C, V>;
     static_assert(S::NW * WAVE >= ROUTE_FUSED_MAX_E, "one thread per logit at least");
     dim3 grid((unsigned)((a.k * a.dff + a.sdff) / S::T), (unsigned)a.rows);
     if (a.sdff)
-        hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, true>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
+        hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, true, V>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
                            a.wts_w, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff,
                            (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs, a.xl, a.hl);
     else
-        hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, false>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
+        hipLaunchKernelGGL((k_route_gate_up<ACT, LPR, C, false, V>), grid, dim3(S::NW * WAVE), 0, st, a.logits, a.idx_w,
                            a.wts_w, a.x, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus, shared_w(a), (int)a.d, (int)a.dff,
                            (int)a.E, (int)a.k, ks, a.h, a.hq, a.hs, a.xl, a.hl);
     return hipGetLastError();
@@ -461,13 +461,30 @@ hipError_t by_shape(const MoeArgs &a, int64_t n_in, hipStream_t st)
     }
 }
 
+// Whether an int8 gate-up with lane groups of 64 holding two chunks takes
+// the 8-wave shape (V = 1): when its tiles outnumber the chip's 256 CUs.
+// With one chunk a lane (the 8-expert block, 896 tiles) 8 waves of 4 pairs
+// measured slower (45.5 vs 43.7 us), so V = 0 stays there.
+inline bool gu_wide(const MoeArgs &a) { return a.rows * ((a.k * a.dff + a.sdff) / QB) > 256; }
 template <int ACT, int LPR, int C>
 struct GU {
-    static hipError_t go(const MoeArgs &a, int ks, hipStream_t st) { return gu_go<ACT, LPR, C>(a, ks, st); }
+    static hipError_t go(const MoeArgs &a, int ks, hipStream_t st)
+    {
+        if constexpr (ACT >= 1 && LPR == 64 && C == 2)
+            if (gu_wide(a))
+                return gu_go<ACT, LPR, C, 1>(a, ks, st);
+        return gu_go<ACT, LPR, C, 0>(a, ks, st);
+    }
 };
 template <int ACT, int LPR, int C>
 struct RGU {
-    static hipError_t go(const MoeArgs &a, int ks, hipStream_t st) { return rgu_go<ACT, LPR, C>(a, ks, st); }
+    static hipError_t go(const MoeArgs &a, int ks, hipStream_t st)
+    {
+        if constexpr (ACT >= 1 && LPR == 64 && C == 2)
+            if (gu_wide(a))
+                return rgu_go<ACT, LPR, C, 1>(a, ks, st);
+        return rgu_go<ACT, LPR, C, 0>(a, ks, st);
+    }
 };
 template <int ACT, int LPR, int C>
 struct DN {
