@@ -210,6 +210,25 @@ def test_topk_gate_up(E, k, ties, act):
             assert torch.equal(qq.reshape(rq.shape), rq) and torch.equal(ss.reshape(rs.shape), rs)
 
 
+def test_topk_gate_up_many_tiles():
+    # 8 x 1408 hidden outputs at d 2048 make 352 int8 tiles, more than the
+    # 256 CUs, so the fused gate-up takes its 8-wave shape; the choices are
+    # the host ranking's and the hidden rows agree with moe_gate_up's
+    banner("moe_topk_gate_up 352 tiles")
+    rows, d, dff, E, k = 1, 2048, 1408, 12, 8
+    m = synthetic.moe_inputs(30, d, dff, E, k, rows)
+    logits = np.random.default_rng(31).standard_normal((rows, E))
+    Wgq, Wgs, Wuq, Wus = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus))
+    xq, xs = q8.q8_quantize_rows(dev(m.x))
+    idx, wts, h, hq, hs = q8.moe_topk_gate_up(dev(logits), Wgq, Wgs, Wuq, Wus, k, xq=xq, xs=xs, act=1)
+    ridx, rw = host_topk(logits, k)
+    assert np.array_equal(host(idx), ridx)
+    assert rel_err(host(wts), rw) <= 1e-6
+    # moe_gate_up's 8-wave shape meets the oracle in test_moe_block_small
+    h2, hq2, hs2 = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, xq=xq, xs=xs, act=1)
+    assert torch.equal(h, h2) and torch.equal(hq, hq2) and torch.equal(hs, hs2)
+
+
 def test_topk_gate_up_nan_logits():
     # NaN logits: a NaN with the sign bit clear ranks above every number, one
     # with it set below; the choices stay K distinct experts in range

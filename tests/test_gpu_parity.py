@@ -325,6 +325,9 @@ MOE_SMALL = [
     dict(d=256, dff=96, E=4, k=4, rows=2),
     dict(d=2048, dff=768, E=16, k=8, rows=3),
     dict(d=64, dff=14336 // 4, E=3, k=1, rows=1),
+    # 352 int8 tiles of 32 hidden outputs, more than the 256 CUs: the gate-up
+    # takes its 8-wave shape
+    dict(d=2048, dff=1408, E=12, k=8, rows=1),
 ]
 
 
