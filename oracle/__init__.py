@@ -70,6 +70,15 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
 
+def _finite(*arrays):
+    """The oracle is defined on finite values only: NaN and infinity in an
+    activation, a router row or a scale have no reading on the pages, so it
+    refuses them rather than rank or sum them."""
+    for a in arrays:
+        if a is not None and a.dtype.kind == "f":
+            assert np.all(np.isfinite(a)), "oracle inputs must be finite"
+
+
 def _check_q8(Wq, Ws, n_in):
     assert n_in % 32 == 0, "n_in must be a multiple of 32"
     assert Wq.shape[1] == n_in and Ws.shape == (Wq.shape[0], n_in // 32)
@@ -79,6 +88,7 @@ def gemv_f32(Wq, Ws, x):
     """y[m, n_out] (float64) = dequant(W) @ x[m, n_in]^T."""
     Wq = _c(Wq, np.int8); Ws = _c(Ws, np.float32)
     x = _c(np.atleast_2d(x), np.float32)
+    _finite(Ws, x)
     n_out, n_in = Wq.shape
     _check_q8(Wq, Ws, n_in)
     assert x.shape[1] == n_in
@@ -90,6 +100,7 @@ def gemv_f32(Wq, Ws, x):
 def quantize(v):
     """Q8_0 quantise rows of v[rows, n]: returns (q int8 [rows, n], d f32 [rows, n/32])."""
     v = _c(np.atleast_2d(v), np.float32)
+    _finite(v)
     rows, n = v.shape
     assert n % 32 == 0
     q = np.empty((rows, n), np.int8)
@@ -112,6 +123,7 @@ def gemv_i8(Wq, Ws, xq, xs):
     """y[m, n_out] (float64) of the one-word int8 mode from quantised rows."""
     Wq = _c(Wq, np.int8); Ws = _c(Ws, np.float32)
     xq = _c(np.atleast_2d(xq), np.int8); xs = _c(np.atleast_2d(xs), np.float32)
+    _finite(Ws, xs)
     n_out, n_in = Wq.shape
     _check_q8(Wq, Ws, n_in)
     assert xq.shape[1] == n_in and xs.shape == (xq.shape[0], n_in // 32)
@@ -124,6 +136,7 @@ def quantize_x2(v):
     """Two-word quantise rows of v[rows, n]: returns (q int8 [rows, n], lo int8
     [rows, n], d f32 [rows, n/32]), v ~= d * (q + lo/128) per block."""
     v = _c(np.atleast_2d(v), np.float32)
+    _finite(v)
     rows, n = v.shape
     assert n % 32 == 0
     q = np.empty((rows, n), np.int8)
@@ -138,6 +151,7 @@ def gemv_i8x2(Wq, Ws, xq, xl, xs):
     Wq = _c(Wq, np.int8); Ws = _c(Ws, np.float32)
     xq = _c(np.atleast_2d(xq), np.int8); xl = _c(np.atleast_2d(xl), np.int8)
     xs = _c(np.atleast_2d(xs), np.float32)
+    _finite(Ws, xs)
     n_out, n_in = Wq.shape
     _check_q8(Wq, Ws, n_in)
     assert xq.shape[1] == n_in and xl.shape == xq.shape and xs.shape == (xq.shape[0], n_in // 32)
@@ -150,6 +164,7 @@ def add_rmsnorm(h, r, w, eps):
     """Returns (sum f32 [rows, d], y float64 [rows, d])."""
     h = _c(np.atleast_2d(h), np.float32); r = _c(np.atleast_2d(r), np.float32)
     w = _c(w, np.float32)
+    _finite(h, r, w)
     rows, d = h.shape
     assert r.shape == h.shape and w.shape == (d,)
     s = np.empty((rows, d), np.float32)
@@ -161,6 +176,7 @@ def add_rmsnorm(h, r, w, eps):
 def route(x, Wr, k):
     """Returns (idx int32 [rows, k], wts float64 [rows, k], logits float64 [rows, E])."""
     x = _c(np.atleast_2d(x), np.float32); Wr = _c(Wr, np.float32)
+    _finite(x, Wr)
     rows, d = x.shape
     E = Wr.shape[0]
     assert Wr.shape == (E, d) and 1 <= k <= E
@@ -177,6 +193,7 @@ def route_q8(Wrq, Wrs, k, x=None, xq=None, xs=None, xl=None):
     of `xq`/`xl`/`xs` (two words), then the softmax top-K of `route`.  Returns
     (idx int32 [rows, k], wts float64 [rows, k], logits float64 [rows, E])."""
     Wrq = _c(Wrq, np.int8); Wrs = _c(Wrs, np.float32)
+    _finite(Wrs, None if x is None else np.asarray(x), None if xs is None else np.asarray(xs))
     E, d = Wrq.shape
     act = 0 if x is not None else (2 if xl is not None else 1)
     if act == 0:
@@ -211,6 +228,7 @@ def moe(x, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act):
     Wgq = _c(Wgq, np.int8); Wgs = _c(Wgs, np.float32)
     Wuq = _c(Wuq, np.int8); Wus = _c(Wus, np.float32)
     Wdq = _c(Wdq, np.int8); Wds = _c(Wds, np.float32)
+    _finite(x, Wr, Wgs, Wus, Wds)
     rows, d = x.shape
     E = Wr.shape[0]
     dff = Wgq.shape[0] // E
@@ -236,6 +254,7 @@ def moe_shared(x, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act, Wr=None, Wrq=None, Wrs=N
     Wgq = _c(Wgq, np.int8); Wgs = _c(Wgs, np.float32)
     Wuq = _c(Wuq, np.int8); Wus = _c(Wus, np.float32)
     Wdq = _c(Wdq, np.int8); Wds = _c(Wds, np.float32)
+    _finite(x, Wgs, Wus, Wds, None if Wr is None else np.asarray(Wr), None if Wrs is None else np.asarray(Wrs))
     rows, d = x.shape
     assert (Wr is None) != (Wrq is None)
     if Wr is not None:

@@ -719,6 +719,136 @@ def test_moe_x2_routes_as_f32():
     assert np.array_equal(i0, i2) and np.array_equal(w0, w2)
 
 
+# The down projection of the int8 numerics reads the hidden row's quantised
+# form (arena.rs fn scratch: hq/hs over K*dff; qwen_emit fn moe_dp4a_kernels:
+# quantize, then gate-up-SwiGLU, then down-combine).  With down rows that are
+# unit vectors of power-of-two scale, every output of an expert's down
+# projection is one hidden value exactly as the down kernel sees it, so the
+# block's output exposes the hidden row's codes: they must be the brute-force
+# nearest codes of the float32 hidden row (one word), or its brute-force words
+# and low words (two words).  A down projection fed the float32 row itself, or
+# the wrong word count, moves every output by a fraction of a step.
+
+
+def _identity_down(m, E, scale_exp=0):
+    """m's experts with down rows e_o (output o reads hidden value o) of
+    scale 2**scale_exp: Wd[e*d + o, t] = (t == o), d == dff."""
+    d, dff = m.d, m.dff
+    assert d == dff
+    Wdq = np.tile(np.eye(d, dtype=np.int8), (E, 1))
+    Wds = np.full((E * d, dff // 32), 2.0 ** scale_exp, np.float32)
+    return Wdq, Wds
+
+
+def _block_codes(hrow):
+    """Brute-force one-word codes and float32 scales of a float32 hidden row,
+    from the quantiser's definition: d = amax/127 and id = 1/d in float32,
+    then the nearest code to the float32 product v*id, ties away from zero."""
+    hrow = np.asarray(hrow, np.float32)
+    codes = np.empty(hrow.shape, np.int64)
+    dsc = np.empty(hrow.shape[0] // 32, np.float32)
+    for b in range(hrow.shape[0] // 32):
+        blk = hrow[b * 32:(b + 1) * 32]
+        dd = np.float32(np.max(np.abs(blk))) / np.float32(127.0)
+        idv = np.float32(1.0) / dd if dd != 0 else np.float32(0.0)
+        dsc[b] = dd
+        for t in range(32):
+            codes[b * 32 + t] = _nearest_away(np.float32(blk[t]) * idv)
+    return codes, dsc
+
+
+@pytest.mark.parametrize("seed", [90, 91])
+def test_moe_int8_down_reads_brute_force_codes_of_hidden_row(seed):
+    m = _small_moe(seed, d=64, dff=64, E=3, k=1, rows=2)
+    Wdq, Wds = _identity_down(m, 3)
+    idx, wts, h, y = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, Wdq, Wds, 1, act=1)
+    assert (wts == 1.0).all()
+    moved = 0.0
+    for i in range(2):
+        codes, dsc = _block_codes(h[i, 0])
+        want = np.repeat(dsc.astype(np.float64), 32) * codes
+        assert np.array_equal(y[i], want), (i, np.max(np.abs(y[i] - want)))
+        moved = max(moved, np.max(np.abs(want - h[i, 0].astype(np.float64))))
+    # the codes are not the float row: a down projection of the row itself fails
+    assert moved > 1e-6 * np.max(np.abs(h))
+
+
+def test_moe_int8_down_codes_weighted_over_two_slots():
+    # K = 2: y = w0 * deq(Q(h0)) + w1 * deq(Q(h1)) in double, slot order
+    m = _small_moe(92, d=64, dff=64, E=4, k=2, rows=2)
+    Wdq, Wds = _identity_down(m, 4, scale_exp=-1)
+    idx, wts, h, y = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, Wdq, Wds, 2, act=1)
+    for i in range(2):
+        want = np.zeros(64)
+        for j in range(2):
+            codes, dsc = _block_codes(h[i, j])
+            want += wts[i, j] * (0.5 * np.repeat(dsc.astype(np.float64), 32) * codes)
+        assert np.max(np.abs(y[i] - want)) <= 1e-15 * np.max(np.abs(want))
+        assert abs(wts[i].sum() - 1.0) <= 1e-15
+
+
+@pytest.mark.parametrize("seed", [93, 94])
+def test_moe_x2_down_reads_brute_force_two_words_of_hidden_row(seed):
+    m = _small_moe(seed, d=64, dff=64, E=3, k=1, rows=2)
+    Wdq, Wds = _identity_down(m, 3)
+    idx, wts, h, y = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, Wdq, Wds, 1, act=2)
+    _, _, _, y1 = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, Wdq, Wds, 1, act=1)
+    assert (wts == 1.0).all()
+    for i in range(2):
+        hrow = h[i, 0]
+        codes, dsc = _block_codes(hrow)
+        lows = np.empty(64, np.int64)
+        for t in range(64):
+            dd = dsc[t // 32]
+            idv = np.float32(1.0) / dd if dd != 0 else np.float32(0.0)
+            lows[t] = _low_word_brute_force(np.float32(hrow[t]) * idv, int(codes[t]))
+        want = np.repeat(dsc.astype(np.float64), 32) * (codes * 128 + lows) / 128.0
+        assert np.array_equal(y[i], want), (i, np.max(np.abs(y[i] - want)))
+        # two words are not one word and not the float row
+        assert not np.array_equal(y[i], y1[i])
+        assert not np.array_equal(y[i], hrow.astype(np.float64))
+
+
+def _discriminating_router(x, deq, E=2, seed=95):
+    """Float32 router rows [E, d] whose top-1 expert differs between the row x
+    and its dequantised form deq: rows 1.. add to row 0 a direction whose
+    logit gap is +D/2 on x and -D/2 on deq (D = |x - deq|^2 > 0)."""
+    rng = np.random.default_rng(seed)
+    x = x.astype(np.float64)
+    deq = deq.astype(np.float64)
+    delta = x - deq
+    w = rng.standard_normal(x.shape[0])
+    # gap(s) on x: delta.x + s*w.x; on deq: delta.deq + s*w.deq; their
+    # difference is |delta|^2 + s*w.delta; set gap on x to half of that
+    D2 = float(delta @ delta)
+    s = (D2 / 2 - float(delta @ x)) / (float(w @ x) - float(w @ delta) / 2)
+    v = delta + s * w
+    base = 0.02 * rng.standard_normal(x.shape[0])
+    Wr = np.stack([base] + [base + v * (1.0 + 0.01 * e) for e in range(1, E)]).astype(np.float32)
+    return Wr
+
+
+@pytest.mark.parametrize("act", [1, 2])
+def test_moe_int8_routes_from_float_row_not_its_quantised_form(act):
+    # a float32 router reads the float32 row in the int8 numerics too (lane_link
+    # fn only_projections: a reader that is not a Q8_0 projection keeps the
+    # norm's float output); on this router the row and its quantised form pick
+    # different experts, so a block that routed from the quantised row fails
+    m = _small_moe(96, d=64, dff=64, E=2, k=1, rows=1)
+    if act == 1:
+        xq, xs = oracle.quantize(m.x)
+        deq = xq[0].astype(np.float64) * np.repeat(xs[0].astype(np.float64), 32)
+    else:
+        xq, xl, xs = oracle.quantize_x2(m.x)
+        deq = (xq[0].astype(np.float64) + xl[0] / 128.0) * np.repeat(xs[0].astype(np.float64), 32)
+    Wr = _discriminating_router(m.x[0], deq)
+    lx = Wr.astype(np.float64) @ m.x[0].astype(np.float64)
+    ld = Wr.astype(np.float64) @ deq
+    assert int(np.argmax(lx)) != int(np.argmax(ld)), (lx, ld)
+    idx, wts, _, _ = oracle.moe(m.x, Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 1, act=act)
+    assert idx[0, 0] == int(np.argmax(lx)) and wts[0, 0] == 1.0
+
+
 # ---------------------------------------------------------------------------
 # MS: the mixture with a shared expert and/or Q8_0 router rows
 
@@ -802,3 +932,20 @@ def test_moe_shared_int8_within_bound_of_f32_mode():
     _, _, _, yf = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 0, Wr=m.Wr, shared=_shared(v))
     _, _, _, yi = oracle.moe_shared(x, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, 1, Wr=m.Wr, shared=_shared(v))
     assert np.max(np.abs(yi - yf)) <= 3e-2 * np.max(np.abs(yf))
+
+
+def test_oracle_refuses_non_finite_inputs():
+    # NaN and infinity have no reading on the pages: the oracle refuses them
+    # (the library's own NaN ranking is checked against the test's rule)
+    m = _small_moe(97, E=4, k=2, rows=1)
+    for bad in (np.nan, np.inf, -np.inf):
+        x = m.x.copy()
+        x[0, 3] = bad
+        with pytest.raises(AssertionError, match="finite"):
+            oracle.route(x, m.Wr, 2)
+        with pytest.raises(AssertionError, match="finite"):
+            oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 2, act=1)
+        with pytest.raises(AssertionError, match="finite"):
+            oracle.quantize(x)
+        with pytest.raises(AssertionError, match="finite"):
+            oracle.gemv_f32(m.Wgq[:4], m.Wgs[:4], x)
