@@ -169,6 +169,10 @@ Q8S_API int add_rmsnorm_q8(const float *h, const float *r, const float *w, int64
  * scratch: device, >= q8s_scratch_bytes(Q8S_FN_ROUTE, ...) bytes, 256-byte
  * aligned: the rows' double-precision logits (arena.rs fn scratch, `rl`);
  * no initial contents are needed.  Two kernels run, logits then top-K.
+ * Non-finite logits have a defined rank at every E: a NaN ranks above every
+ * number when its sign bit is clear and below every number when it is set,
+ * ties to the lower index; a kept NaN makes every kept weight NaN.  The
+ * choices are always K distinct experts.
  */
 Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k,
                    int32_t *idx, float *wts, void *scratch, size_t scratch_bytes, void *stream);
@@ -298,9 +302,9 @@ Q8S_API int add_rmsnorm_router(const float *h, const float *r, const float *w, f
  * Rows run one by one (a chunk of rows in INT8 mode reads each expert once
  * per row here; moe_gate_up groups them).  Limits: E <= 256
  * (Q8S_EUNSUPPORTED beyond), k <= min(32, E).  A NaN logit ranks above every
- * number when its sign bit is clear and below every number when it is set
- * (its weight is then NaN); the choices are K distinct experts whatever the
- * logits hold.
+ * number when its sign bit is clear and below every number when it is set;
+ * a kept NaN makes every kept weight NaN (the renormalisation sums them).
+ * The choices are K distinct experts whatever the logits hold.
  */
 Q8S_API int moe_topk_gate_up(const double *logits, const float *x, const int8_t *xq, const float *xs,
                      const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,

@@ -9,6 +9,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <initializer_list>
 #include <string>
 #include <vector>
@@ -913,3 +914,28 @@ int moe_ffn_block_ex(const float *h, const float *r, const float *w, float eps, 
 }
 
 } // extern "C"
+
+namespace q8s {
+
+int device_cus()
+{
+    constexpr int MAX_DEV = 64;
+    static std::atomic<int> cache[MAX_DEV];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEV) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0)
+        return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+} // namespace q8s

@@ -513,7 +513,7 @@ Q8S_DEV float silu(float z)
 //   V = 1 (int8, lane groups of 64): the same 32-output tile in 8 waves of 4
 //         pairs, for launches of more tiles than the chip has CUs, where
 //         smaller workgroups share the CUs more evenly (the shared-expert
-//         block's 352 tiles: 23.5 vs 24.6 us a step; the 128-expert block's
+//         block's 352 tiles: 23.4 vs 24.6 us a step; the 128-expert block's
 //         192 tiles: 18.7 vs 18.1 us, so V = 0 there).
 template <int ACT, int LPR, int C, int V = 0>
 struct GuShape {
@@ -531,8 +531,6 @@ struct GuShape {
 // top-K of one row's router logits, held in LDS (fn emit_moe_forward: the K
 // largest by probability, which is monotone in the logit)
 
-// (l, e) ranks before (l', e') when l > l', or l == l' and e < e'.
-Q8S_DEV bool route_better(double l, int e, double l2, int e2) { return l > l2 || (l == l2 && e < e2); }
 
 // LDS of the in-workgroup top-K, for rows of at most TOPK_LDS_E logits.
 constexpr int TOPK_LDS_E = 256;

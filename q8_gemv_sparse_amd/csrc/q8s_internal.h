@@ -173,6 +173,11 @@ hipError_t chunk_down_launch(const MoeArgs &a, hipStream_t st);
 
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// Compute units of the current device (read once per device, then cached);
+// launch shapes that depend on how many workgroups the chip holds at once
+// compare against it.
+int device_cus();
+
 // the whole mixture block: add + norm, router + top-K, gate-up, down-combine
 struct BlockArgs {
     const float *h, *r, *w;

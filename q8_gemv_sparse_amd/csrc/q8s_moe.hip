@@ -462,10 +462,10 @@ hipError_t by_shape(const MoeArgs &a, int64_t n_in, hipStream_t st)
 }
 
 // Whether an int8 gate-up with lane groups of 64 holding two chunks takes
-// the 8-wave shape (V = 1): when its tiles outnumber the chip's 256 CUs.
-// With one chunk a lane (the 8-expert block, 896 tiles) 8 waves of 4 pairs
-// measured slower (45.5 vs 43.7 us), so V = 0 stays there.
-inline bool gu_wide(const MoeArgs &a) { return a.rows * ((a.k * a.dff + a.sdff) / QB) > 256; }
+// the 8-wave shape (V = 1): when its tiles outnumber the chip's CUs (256 on
+// MI355X).  With one chunk a lane (the 8-expert block, 896 tiles) 8 waves of
+// 4 pairs measured slower (45.5 vs 43.7 us), so V = 0 stays there.
+inline bool gu_wide(const MoeArgs &a) { return a.rows * ((a.k * a.dff + a.sdff) / QB) > device_cus(); }
 template <int ACT, int LPR, int C>
 struct GU {
     static hipError_t go(const MoeArgs &a, int ks, hipStream_t st)

@@ -225,13 +225,29 @@ __global__ void __launch_bounds__(RT_THREADS)
     }
 }
 
+// The logit a route_code came from (route_code maps -0 to +0, which no use
+// of the kept logits tells apart).
+Q8S_DEV double route_decode(uint64_t c)
+{
+    const uint64_t b = (c >> 63) ? (c & 0x7fffffffffffffffull) : ~c;
+    return __longlong_as_double((long long)b);
+}
+
+// (code c, index i) ranks before (c2, i2): the greater code, ties to the
+// lower index; i2 == INT_MAX stands for no candidate yet.
+Q8S_DEV bool code_better(uint64_t c, int i, uint64_t c2, int i2)
+{
+    return i2 == 0x7fffffff || c > c2 || (c == c2 && i < i2);
+}
+
 __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ logits, int E, int k,
                                                      int32_t *__restrict__ idx, float *__restrict__ wts)
 {
-    extern __shared__ double Lbig[];  // [E], for rows of more than TOPK_LDS_E logits
+    extern __shared__ uint64_t Cbig[];  // [E] codes, for rows of more than TOPK_LDS_E logits
     __shared__ TopkLds t;
-    __shared__ double bl[RT_WAVES];
+    __shared__ uint64_t bl[RT_WAVES];
     __shared__ int be[RT_WAVES];
+    __shared__ uint32_t retired[Q8S_MAX_E_DEV / 32];
     const int64_t row = blockIdx.x;
     const double *lr = logits + row * E;
 
@@ -241,24 +257,30 @@ __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ 
         topk_select(t, E, k);
         __syncthreads();
     } else {
+        // K rounds of a workgroup arg-max over the logits' order-preserving
+        // codes (route_code: NaNs rank above +inf or below -inf by their sign
+        // bit, as in the one-pass rank), ties to the lower index; a chosen
+        // expert is retired by a flag of its own, so every round picks a new
+        // one whatever the logits hold (k <= E)
         for (int i = threadIdx.x; i < E; i += RT_THREADS)
-            Lbig[i] = lr[i];
+            Cbig[i] = route_code(lr[i]);
+        for (int i = threadIdx.x; i < (E + 31) / 32; i += RT_THREADS)
+            retired[i] = 0u;
         __syncthreads();
-        // K rounds of a workgroup arg-max; a chosen logit is retired to -inf
-        // by the thread that scans it (real logits are finite and k <= E)
         const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
         for (int jj = 0; jj < k; jj++) {
-            double b = -INFINITY;
+            uint64_t b = 0;
             int bi = 0x7fffffff;
             for (int i = threadIdx.x; i < E; i += RT_THREADS)
-                if (route_better(Lbig[i], i, b, bi)) {
-                    b = Lbig[i];
+                if (!((retired[i >> 5] >> (i & 31)) & 1u) && code_better(Cbig[i], i, b, bi)) {
+                    b = Cbig[i];
                     bi = i;
                 }
             for (int o = 32; o >= 1; o >>= 1) {
-                const double b2 = __shfl_xor(b, o);
+                const uint64_t b2 = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(b >> 32), o) << 32) |
+                                    (uint32_t)__shfl_xor((int)(uint32_t)b, o);
                 const int i2 = __shfl_xor(bi, o);
-                if (route_better(b2, i2, b, bi)) {
+                if (i2 != 0x7fffffff && code_better(b2, i2, b, bi)) {
                     b = b2;
                     bi = i2;
                 }
@@ -268,19 +290,18 @@ __global__ void __launch_bounds__(RT_THREADS) k_topk(const double *__restrict__ 
                 be[wid] = bi;
             }
             __syncthreads();
-            double wb = bl[0];
+            uint64_t wb = bl[0];
             int wi = be[0];
             for (int w = 1; w < RT_WAVES; w++)
-                if (route_better(bl[w], be[w], wb, wi)) {
+                if (be[w] != 0x7fffffff && code_better(bl[w], be[w], wb, wi)) {
                     wb = bl[w];
                     wi = be[w];
                 }
             if (threadIdx.x == 0) {
                 t.ch[jj] = wi;
-                t.kl[jj] = wb;
+                t.kl[jj] = route_decode(wb);
+                retired[wi >> 5] |= 1u << (wi & 31);
             }
-            if (wi < E && (int)threadIdx.x == (wi % RT_THREADS))
-                Lbig[wi] = -INFINITY;
             __syncthreads();
         }
     }
@@ -292,7 +313,7 @@ namespace {
 
 hipError_t topk_go(const double *logits, int64_t rows, int64_t E, int64_t k, int32_t *idx, float *wts, hipStream_t st)
 {
-    const size_t big = E > TOPK_LDS_E ? (size_t)E * sizeof(double) : 0;
+    const size_t big = E > TOPK_LDS_E ? (size_t)E * sizeof(uint64_t) : 0;
     hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(RT_THREADS), big, st, logits, (int)E, (int)k, idx, wts);
     return hipGetLastError();
 }

@@ -284,6 +284,51 @@ def test_route_near_ties(E):
     assert rel_err(host(wts)[0], p / p.sum()) <= TOL_F32
 
 
+def _code_order(l):
+    """The documented rank of logits that may hold NaN or infinity: the
+    order-preserving code of each double (-0 as +0; a NaN above +inf when its
+    sign bit is clear, below -inf when set), ties to the lower index."""
+    b = np.where(l == 0.0, 0.0, l).view(np.uint64)
+    sign = (b >> np.uint64(63)).astype(bool)
+    code = np.where(sign, ~b, b | np.uint64(1 << 63))
+    return sorted(range(len(l)), key=lambda e: (-int(code[e]), e))
+
+
+@pytest.mark.parametrize("E", [200, 300])
+@pytest.mark.parametrize("with_nan", [False, True])
+def test_route_non_finite_logits(E, with_nan):
+    # a one-hot row makes each logit its router entry: -inf everywhere but a
+    # few finite entries (and NaNs of both signs).  The choices are K distinct
+    # experts in the documented rank, at E 200 (the one-pass rank) and E 300
+    # (the arg-max rounds), where a retired expert must not come back.
+    banner("route non-finite logits E=%d nan=%s" % (E, with_nan))
+    d, k = 64, 8
+    x = np.zeros((1, d), np.float32)
+    x[0, 5] = 1.0
+    Wr = np.zeros((E, d), np.float32)
+    col = np.full(E, -np.inf, np.float32)
+    col[[3, 100, E - 1, 150]] = [0.25, 1.5, -3.0, 1.5]
+    if with_nan:
+        col[[7, 180]] = np.float32(np.nan)
+        col[11] = -np.float32(np.nan)
+    Wr[:, 5] = col
+    scratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_ROUTE, 1, d, 32, E, k), dtype=torch.uint8, device="cuda")
+    idx, wts = q8.moe_route_topk(dev(x), dev(Wr), k, scratch=scratch)
+    logits = host(scratch)[:E * 8].view(np.float64)
+    got = host(idx)[0]
+    assert len(set(got.tolist())) == k and got.min() >= 0 and got.max() < E
+    assert list(got) == _code_order(logits)[:k]
+    w = host(wts)[0]
+    if with_nan:
+        # a kept NaN (a NaN whose sign bit is clear ranks first) makes every
+        # kept weight NaN
+        assert np.isnan(logits[got]).any() and np.isnan(w).all()
+    else:
+        assert list(got[:4]) == [100, 150, 3, E - 1] and list(got[4:]) == [0, 1, 2, 4]
+        p = np.exp(logits[got] - logits[got[0]])
+        assert rel_err(w, p / p.sum()) <= TOL_F32 and (w[4:] == 0).all()
+
+
 def test_route_scratch_reuse():
     # one scratch sized for 64 rows serves calls of any smaller size
     banner("route scratch reuse")

@@ -146,6 +146,7 @@ EX_CASES = [
     (2048, 768, 1024, 128, 8, 1),    # + a shared expert wider than a slice of dff
     (2048, 768, 768, 128, 8, 1),     # a shared expert as wide as the routed ones
     (4096, 1408, 5632, 16, 4, 1),    # a shared expert four times dff, int8 rows in 4 slices
+    (2048, 1408, 5632, 60, 4, 1),    # the 60-expert shared block: 352 int8 tiles, the 8-wave gate-up shape
     (96, 160, 96, 5, 3, 1),          # ragged lane groups of 16; sdff < dff
     (256, 64, 800, 6, 2, 3),         # 3 rows: per-row f32; int8 grouped chunk kernels + shared pass
     (128, 64, 128, 300, 4, 1),       # E > 256: separate norm, router, top-K, gate-up
