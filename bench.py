@@ -4,36 +4,36 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--act int8|f32|x2]
 
 A step is one pass of the hot path over one batch of synthetic input.  The
-default workload is the batch-1 MoE FFN block at the Qwen3-30B-A3B-like shape
-(d 2048, dff 768, 128 experts, top 8), fed by its producer, as one
-moe_ffn_block call a step (add + norm fused into the router's logits, the
-top-K taken inside the gate-up launch, then down-combine); --separate runs
-the same block as the separate calls
+headline workload is the batch-1 MoE FFN block at the Qwen3-30B-A3B-like shape
+(d 2048, dff 768, 128 experts, top 8) in one-word int8 numerics, fed by its
+producer, as one moe_ffn_block call a step (add + norm fused into the router's
+logits, the top-K taken inside the gate-up launch, then down-combine);
+--separate runs the same block as the separate calls
 
     add_rmsnorm_q8 -> moe_route_topk -> moe_gate_up -> moe_down_combine
 
 Inputs are resident in HBM before timing starts.  Weight reads are kept
-cache-cold: the step rotates over `copies` copies of every weight array (more
-bytes between two uses of a copy than the 256 MB Infinity Cache holds) and
+cache-cold: the steps rotate over `copies` copies of every weight array (more
+bytes between two uses of a copy than two 256 MB Infinity Caches hold) and
 over a pool of different input rows (so the chosen experts change from step
 to step).
 
-Timing: the steps are captured once in a HIP graph (a graph of `copies`
-consecutive steps) and the graph is replayed; HIP events on the replay stream
-bracket exactly K steps, with a device synchronisation on both sides.  The
-dominant kernel's average duration is measured by replaying a graph of just
-its launches (one per weight copy) back to back, HIP events around the
-replays, and reported against the HBM roofline on its algorithmic bytes (the
-weight bytes one launch must read).  Both are also stated as a fraction of a
-measured ceiling: the library's plain streaming reader (q8s_stream_read) over
-2 GiB, and over cold slices of the dominant kernel's own size.  Each graph
-replay is then timed alone for the p10 / median / p90 of the step time.
+Timing: exactly W untimed steps, then exactly K timed steps, each run as one
+HIP graph of that many consecutive steps (step i on copy i mod C); HIP events
+on the graph's stream bracket the K steps, with a device synchronisation on
+both sides.  The spread (p10 / median / p90) comes from --spread single steps,
+each timed alone between two events.  Each of the step's calls is then timed
+alone (a graph of its launches, one per copy, replayed back to back), beside
+the time the library's plain streaming reader (q8s_stream_read) takes for the
+same weight bytes, cold.  The dominant kernel's average launch time gives the
+roofline object, on its algorithmic bytes (the weight bytes one launch must
+read) against the 8 TB/s HBM peak.
 
-The CPU oracle is timed on a bounded sample of the same workload, on one core
-and on every available core at once (one thread each).  --act x2 runs the
-two-word numerics (the norm + GEMV and the mixture block); --warm (context
-only) keeps one weight copy and one input row, so the weights stay
-cache-resident.
+By default the run goes on to every other workload and numerics (the suite),
+each with the same measurements at 400 steps, into config.workloads; the CPU
+oracle is timed on a bounded sample of the headline workload, on one core and
+on every available core at once (one thread each).  --warm (context only)
+keeps one weight copy and one input row, so the weights stay cache-resident.
 
 Prints one JSON line on stdout; details go to stderr.
 """
@@ -54,6 +54,7 @@ ACT_CODE = {"f32": 0, "int8": 1, "x2": 2}  # the library's activation modes
 # one-word code flip, with a margin of 16 flips)
 TOL = {"f32": 1e-5, "int8": 2e-3, "x2": 2.5e-4}
 MALL_BYTES = 256 << 20
+DEFAULT_WORKLOAD = "moe_d2048_dff768_e128_k8"
 
 
 def log(*a):
@@ -87,7 +88,8 @@ def summarize_counters(args):
     kernel, srcs = DOMINANT[kind]
     calib = args.calib_copy_mib * 1024  # KiB moved each way by the copy
     run = ("python3 bench.py --workload %s --act %s --no-graph --steps 28 --warmup 14 --kernel-launches 14 "
-           "--no-cpu --no-ceiling --calib-copy-mib %d" % (args.workload, args.act, args.calib_copy_mib))
+           "--spread 0 --suite none --no-cpu --no-ceiling --calib-copy-mib %d"
+           % (args.workload, args.act, args.calib_copy_mib))
     out = {"kernel": kernel, "workload": args.workload, "act": args.act,
            "source_digest": src_digest(*srcs), "calib_copy_kib": calib,
            "commands": ["rocprofv3 --pmc %s -f csv -d <out> -o run -- %s" % (c, run)
@@ -119,11 +121,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--workload", default="moe_d2048_dff768_e128_k8")
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--act", choices=["int8", "f32", "x2"], default="int8",
                    help="activation numerics: one-word int8, float32, or two-word int8 (norm + GEMV workload)")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough to defeat the MALL)")
-    p.add_argument("--kernel-launches", type=int, default=400, help="eager launches timed for the dominant kernel")
+    p.add_argument("--kernel-launches", type=int, default=400, help="launches timed for the dominant kernel")
+    p.add_argument("--spread", type=int, default=200, help="single steps timed one by one for the spread (0: none)")
+    p.add_argument("--suite", choices=["auto", "all", "none"], default="auto",
+                   help="after the headline, measure every other workload and numerics into config.workloads "
+                        "(auto: only for the default headline)")
     p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work for the CPU baseline")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     p.add_argument("--cpu-threads", type=int, default=0,
@@ -174,6 +180,20 @@ class Workload:
         elsewhere (called once before they are captured)."""
 
 
+_MOE_MEMO = {}
+
+
+def _moe_inputs(d, dff, E, k):
+    """synthetic.moe_inputs(seed 0) of one shape, kept for the next workload
+    of the same shape (the suite measures each shape in several numerics)."""
+    import synthetic
+    key = (d, dff, E, k)
+    if key not in _MOE_MEMO:
+        _MOE_MEMO.clear()
+        _MOE_MEMO[key] = synthetic.moe_inputs(0, d, dff, E, k, rows=1)
+    return _MOE_MEMO[key]
+
+
 def _copies(step_bytes, want):
     """Weight copies to rotate so that more than two MALLs' worth of weight
     traffic passes between two uses of one copy."""
@@ -204,7 +224,7 @@ class MoeBlock(Workload):
         d, dff, E, k = cfg["d"], cfg["dff"], cfg["E"], cfg["k"]
         self.d, self.dff, self.E, self.k, self.rows = d, dff, E, k, rows
         t0 = time.time()
-        m = synthetic.moe_inputs(0, d, dff, E, k, rows=1)
+        m = _moe_inputs(d, dff, E, k)
         self.host_w = m
         rng = np.random.default_rng(1)
         self.norm_w = rng.uniform(0.5, 1.5, size=d).astype(np.float32)
@@ -325,6 +345,36 @@ class MoeBlock(Workload):
         else:
             q8.moe_topk_gate_up(self.logits[c % self.copies], W[1], W[2], W[3], W[4], self.k, x=self.y, idx=idx,
                                 wts=wts, h=self.hf, act=a)
+
+    def stages(self):
+        """The step's launches, each as a call of its own (one kernel each
+        for one row): (label, launch(c), weight bytes of one launch)."""
+        q8 = self.q8
+        a = ACT_CODE[self.act]
+        d, dff, E, k = self.d, self.dff, self.E, self.k
+        q8b = lambda n_out, n_in: n_out * n_in + n_out * (n_in // 32) * 4
+        if self.separate or self.rows > 1:
+            return []
+
+        def norm_router(c):
+            i = c % self.pool
+            x2 = self.act == "x2"
+            q8.add_rmsnorm_router(self.h[i], self.r[i], self.w, 1e-6, self.W[c % self.copies][0], sum=self.sum,
+                                  x=self.y, xq=None if x2 else self.xq, xs=None if x2 else self.xs,
+                                  logits=self.logits[c % self.copies], want_q8=not x2)
+
+        def down(c):
+            W = self.W[c % self.copies]
+            idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+            if a == q8.ACT_INT8:
+                q8.moe_down_combine(W[5], W[6], idx, wts, E, hq=self.hq, hs=self.hs, y=self.out, act=a)
+            else:
+                q8.moe_down_combine(W[5], W[6], idx, wts, E, h=self.hf, y=self.out, act=a)
+        out = [("add_rmsnorm_router (k_norm_logits)", norm_router, E * d * 4),
+               ("moe_topk_gate_up (k_route_gate_up)", self.launch_dominant, k * 2 * q8b(dff, d))]
+        if self.act != "x2":  # the two-word down projection runs inside moe_ffn_block only
+            out.append(("moe_down_combine (k_down)", down, k * q8b(d, dff)))
+        return out
 
     def distinct_experts(self, c):
         """Experts chosen by copy c's last route (for the bytes a chunk reads)."""
@@ -469,6 +519,11 @@ class NormGemv(Workload):
     def dominant_bytes(self, c=None):
         return self.wbytes
 
+    def stages(self):
+        if self.separate:
+            return [("q8_gemv (k_gemv_rows)", self.launch_dominant, self.wbytes)]
+        return [("add_rmsnorm_gemv%s (k_norm_gemv)" % ("_x2" if self.act == "x2" else ""), self.step, self.wbytes)]
+
     def verify(self):
         import oracle
         np = self.np
@@ -504,6 +559,73 @@ class NormGemv(Workload):
                 oracle.gemv_i8(self.inp.Wq, self.inp.Ws, q, sc)
             else:
                 oracle.gemv_f32(self.inp.Wq, self.inp.Ws, x)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                break
+        return el / n, "%d steps, %.1f s" % (n, el)
+
+
+class Gemv(Workload):
+    """One batch-1 Q8_0 GEMV a step, float32 activations (the 512 x 256
+    matrix: 147 KB, which the caches hold; latency, not bandwidth, bounds
+    it).  The step rotates over 64 weight copies and as many input rows."""
+
+    dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_gemv.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
+    dominant = "k_gemv_rows"
+
+    def __init__(self, name, cfg, act, copies):
+        import numpy as np
+        import torch
+
+        import q8_gemv_sparse_amd as q8
+        import synthetic
+        if act != "f32":
+            raise SystemExit("workload %s is the float32-activation GEMV" % name)
+        self.q8, self.torch, self.np = q8, torch, np
+        self.name, self.act = name, act
+        n_out, n_in = cfg["n_out"], cfg["n_in"]
+        self.inp = synthetic.gemv_inputs(0, n_out, n_in, m=1)
+        self.copies = copies or 64
+        rng = np.random.default_rng(1)
+        self.pool_x = [synthetic.normal(rng, 1, n_in) for _ in range(self.copies)]
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        base = [dev(self.inp.Wq), dev(self.inp.Ws)]
+        self.W = [base] + [[t.clone() for t in base] for _ in range(self.copies - 1)]
+        self.x = [dev(a) for a in self.pool_x]
+        self.out = torch.empty((1, n_out), dtype=torch.float32, device="cuda")
+        self.wbytes = n_out * n_in + n_out * (n_in // 32) * 4
+        self.cache = "warm: the 64 copies (9.4 MB) fit the Infinity Cache; a latency figure"
+        torch.cuda.synchronize()
+
+    def step(self, c):
+        W = self.W[c % self.copies]
+        self.q8.q8_gemv(W[0], W[1], x=self.x[c % self.copies], y=self.out, act=self.q8.ACT_F32)
+
+    launch_dominant = step
+
+    def weight_bytes(self, c=None):
+        return self.wbytes
+
+    dominant_bytes = weight_bytes
+
+    def stages(self):
+        return [("q8_gemv (k_gemv_rows)", self.step, self.wbytes)]
+
+    def verify(self):
+        import oracle
+        np = self.np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        ref = oracle.gemv_f32(self.inp.Wq, self.inp.Ws, self.pool_x[0])
+        got = self.out.cpu().numpy()
+        return {"max_rel_err": float(np.max(np.abs(got - ref)) / np.max(np.abs(ref))), "tol": 1e-5}
+
+    def cpu_baseline(self, budget):
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            oracle.gemv_f32(self.inp.Wq, self.inp.Ws, self.pool_x[n % self.copies])
             n += 1
             el = time.perf_counter() - t0
             if el >= budget:
@@ -557,6 +679,37 @@ class ChunkBlock(MoeBlock):
 
     def weight_bytes(self, c=None):
         return super().weight_bytes(c) + self.dense_bytes
+
+    def stages(self):
+        """The chunk's calls in step order, each timed alone over the copies
+        (the routing each copy's last step left in place)."""
+        q8 = self.q8
+        d, dff, E, k = self.d, self.dff, self.E, self.k
+        q8b = lambda n_out, n_in: n_out * n_in + n_out * (n_in // 32) * 4
+        u = lambda c: self.distinct_experts(c)
+        C = self.copies
+        avg_u = sum(u(c) for c in range(C)) / C
+
+        def route(c):
+            W = self.W[c % C]
+            q8.moe_route_topk(self.y, W[0], k, idx=self.idx[c % C], wts=self.wts[c % C], scratch=self.rscratch)
+
+        def gate_up(c):
+            self._gate_up(c, q8.ACT_INT8)
+
+        def down(c):
+            W = self.W[c % C]
+            q8.moe_down_combine(W[5], W[6], self.idx[c % C], self.wts[c % C], E, hq=self.hq, hs=self.hs, y=self.out,
+                                act=q8.ACT_INT8, scratch=self.dscratch)
+
+        def dense(c):
+            Dq, Ds = self.D[c % C]
+            q8.q8_gemv(Dq, Ds, xq=self.xq, xs=self.xs, y=self.dense_out, act=q8.ACT_INT8)
+        return [("add_rmsnorm_q8 (k_add_rmsnorm_q8, 64 rows)", self._norm, 0),
+                ("moe_route_topk (k_logits_tile + k_topk)", route, E * d * 4),
+                ("moe_gate_up (k_chunk_gate_up + k_quantize_rows)", gate_up, int(avg_u * 2 * q8b(dff, d))),
+                ("moe_down_combine (k_chunk_down2 + k_chunk_combine)", down, int(avg_u * q8b(d, dff))),
+                ("q8_gemv dense 64 x 2048 -> 4096 (k_gemm_i8)", dense, self.dense_bytes)]
 
     def verify(self):
         import oracle
@@ -661,6 +814,28 @@ class MoeSharedBlock(MoeBlock):
     def _q8(self, n_out, n_in):
         return n_out * n_in + n_out * (n_in // 32) * 4
 
+    def stages(self):
+        q8 = self.q8
+        a = q8.ACT_INT8 if self.act == "int8" else q8.ACT_F32
+        d, dff, E, k, sdff = self.d, self.dff, self.E, self.k, self.sdff
+        C = self.copies
+
+        def norm_router(c):
+            i = c % self.pool
+            V = self.V[c % C]
+            q8.add_rmsnorm_router_q8(self.h[i], self.r[i], self.w, 1e-6, V[0], V[1], act=a, sum=self.sum, x=self.y,
+                                     xq=self.xq, xs=self.xs, logits=self.logits[c % C])
+
+        def down(c):
+            W = self.W[c % C]
+            V = self.V[c % C]
+            kw = dict(hq=self.hq, hs=self.hs) if a == q8.ACT_INT8 else dict(h=self.hf)
+            q8.moe_down_combine_ex(W[5], W[6], self.idx[c % C], self.wts[c % C], E, shared=tuple(V[6:8]), y=self.out,
+                                   act=a, **kw)
+        return [("add_rmsnorm_router_q8 (k_norm_logits)", norm_router, self._q8(E, d)),
+                ("moe_topk_gate_up_ex (k_route_gate_up)", self.launch_dominant, self.dominant_bytes()),
+                ("moe_down_combine_ex (k_down)", down, self._q8(d, k * dff + sdff))]
+
     def weight_bytes(self, c=None):
         d, dff, E, k, sdff = self.d, self.dff, self.E, self.k, self.sdff
         return self._q8(E, d) + k * 3 * self._q8(dff, d) + 3 * self._q8(sdff, d)
@@ -712,7 +887,9 @@ def make_workload(name, act, copies, separate=False):
         return ChunkBlock(name, cfg, copies)
     if cfg["kind"] == "moe_shared":
         return MoeSharedBlock(name, cfg, act, copies, separate=separate)
-    raise SystemExit("workload %s is a parity case, not a bench workload" % name)
+    if cfg["kind"] == "gemv":
+        return Gemv(name, cfg, act, copies)
+    raise SystemExit("workload %s is not a bench workload" % name)
 
 
 # ---------------------------------------------------------------------------
@@ -744,17 +921,25 @@ def host_cpu():
     return "%s, %d CPUs available" % (model, len(os.sched_getaffinity(0)))
 
 
-def stream_ceiling(torch, q8, stream, same_bytes, eager):
+class Ceiling:
     """What a plain read reaches on this device: the library's streaming
-    reader over a 2 GiB buffer (eight times the 256 MB Infinity Cache), and
-    over slices of it the size of the dominant kernel's bytes, each slice read
-    once per pass over the buffer so every read is cache-cold."""
-    total = 2 << 30
-    buf = torch.zeros(total, dtype=torch.uint8, device="cuda")
-    out = torch.empty(q8.STREAM_WGS, dtype=torch.int32, device="cuda")
-    torch.cuda.synchronize()
+    reader (q8s_stream_read, which computes nothing of the method) over a
+    2 GiB buffer -- eight times the 256 MB Infinity Cache -- and over cold
+    slices of it of a given size, each slice a launch of its own, every slice
+    read once per pass over the buffer."""
 
-    def timed(fn, reps):
+    def __init__(self, torch, q8, stream, eager):
+        self.torch, self.q8, self.stream, self.eager = torch, q8, stream, eager
+        self.total = 2 << 30
+        self.buf = torch.zeros(self.total, dtype=torch.uint8, device="cuda")
+        self.out = torch.empty(q8.STREAM_WGS, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        whole_ms = self._timed(lambda: q8.q8s_stream_read(self.buf, out=self.out), 20)
+        self.gbs = round(self.total / (whole_ms * 1e-3) / 1e9, 1)
+        self.memo = {}
+
+    def _timed(self, fn, reps):
+        torch, stream = self.torch, self.stream
         with torch.cuda.stream(stream):
             fn()
         torch.cuda.synchronize()
@@ -767,30 +952,224 @@ def stream_ceiling(torch, q8, stream, same_bytes, eager):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / reps
 
-    whole_ms = timed(lambda: q8.q8s_stream_read(buf, out=out), 20)
-    n = max(16, same_bytes // 16 * 16)
-    span = -(-n // 256) * 256
-    slices = max(1, total // span)
-    views = [buf[i * span:i * span + n] for i in range(slices)]
+    def same_bytes(self, nbytes):
+        """(µs, GB/s) of a launch that only reads `nbytes` cold bytes."""
+        n = max(16, int(nbytes) // 16 * 16)
+        if n in self.memo:
+            return self.memo[n]
+        torch, q8 = self.torch, self.q8
+        span = -(-n // 256) * 256
+        slices = max(1, min(4096, self.total // span))
+        views = [self.buf[i * span:i * span + n] for i in range(slices)]
 
-    def read_slices():
-        for v in views:
-            q8.q8s_stream_read(v, out=out)
-    if eager:
-        pass_fn = read_slices
-    else:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            read_slices()
-        pass_fn = g.replay
-    reps = max(1, -(-200 // slices))
-    slice_ms = timed(pass_fn, reps) / slices
-    del buf
-    return {"what": "q8s_stream_read: 16-byte non-temporal loads, each byte once",
-            "stream_read_gbs": round(total / (whole_ms * 1e-3) / 1e9, 1), "stream_read_bytes": total,
-            "same_bytes_us": round(slice_ms * 1e3, 3), "same_bytes_gbs": round(n / (slice_ms * 1e-3) / 1e9, 1),
-            "same_bytes": n, "same_bytes_timing": "%d cold slices a pass, %s" % (
-                slices, "eager" if eager else "graph replayed %d times" % reps)}
+        def read_slices():
+            for v in views:
+                q8.q8s_stream_read(v, out=self.out)
+        if self.eager:
+            pass_fn = read_slices
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=self.stream):
+                read_slices()
+            pass_fn = g.replay
+        reps = max(1, -(-200 // slices))
+        us = self._timed(pass_fn, reps) / slices * 1e3
+        self.memo[n] = (round(us, 3), round(n / (us * 1e-6) / 1e9, 1))
+        return self.memo[n]
+
+    def describe(self, nbytes):
+        us, gbs = self.same_bytes(nbytes)
+        return {"what": "q8s_stream_read: 16-byte non-temporal loads, each byte once",
+                "stream_read_gbs": self.gbs, "stream_read_bytes": self.total,
+                "same_bytes_us": us, "same_bytes_gbs": gbs, "same_bytes": int(nbytes),
+                "same_bytes_timing": "cold slices of a 2 GiB buffer, one launch each, %s"
+                                     % ("eager" if self.eager else "a graph of one pass replayed")}
+
+
+def _capture(torch, stream, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def _pct(vals, q):
+    vals = sorted(vals)
+    return round(vals[min(len(vals) - 1, int(q * len(vals)))], 3)
+
+
+def _timing_events(torch, n, inside):
+    return [torch.cuda.Event(enable_timing=True, external=inside) for _ in range(n)]
+
+
+def measure(wl, steps, warmup, stream, eager=False, spread_n=200):
+    """Times exactly `steps` steps after exactly `warmup` untimed ones, each
+    group run as one graph of that many consecutive steps (step i on weight
+    copy i mod C), a device synchronisation on both sides.  The two events
+    that bracket the timed steps are recorded inside their graph, right
+    before the first step's launches and right after the last one's, so the
+    graph's own launch is not counted.  The spread: a graph of `spread_n`
+    further steps with an event recorded between every two, each step's time
+    the gap between its two events.  Without graphs (or where a graph cannot
+    hold event records) the events go on the stream around the launches."""
+    torch = wl.torch
+    ver = wl.verify()
+    ver["ok"] = bool(ver.get("idx_equal", True) and ver["max_rel_err"] <= ver["tol"] and
+                     ver.get("dense_max_rel_err", 0.0) <= ver["tol"])
+    log("[bench] %s %s: verify against the oracle: %s" % (wl.name, wl.act, ver))
+    if not ver["ok"]:
+        log("[bench] WARNING: the step does not match the oracle; its figures measure a wrong result")
+    C = wl.copies
+    with torch.cuda.stream(stream):
+        for c in range(C):  # eager warm-up of every copy on the timing stream
+            wl.step(c)
+    torch.cuda.synchronize()
+
+    def steps_fn(n, evs=None, first=0):
+        # n steps from step `first`; evs: events recorded before step 0 and
+        # after every step (len n + 1), or only around all (len 2)
+        def fn():
+            if evs is not None:
+                evs[0].record(stream)
+            for i in range(n):
+                wl.step((first + i) % C)
+                if evs is not None and (len(evs) == n + 1 or i == n - 1):
+                    evs[i + 1 if len(evs) == n + 1 else 1].record(stream)
+        return fn
+
+    inside = not eager
+    if inside:
+        try:
+            ek = _timing_events(torch, 2, True)
+            gk = _capture(torch, stream, steps_fn(steps, ek))
+        except Exception as exc:  # a runtime whose graphs do not take event records
+            log("[bench] event records inside a graph refused (%s): events around the replay instead" % exc)
+            inside = False
+    gw = None
+    if not eager and warmup > 0:
+        gw = _capture(torch, stream, steps_fn(warmup))
+    if not inside:
+        ek = _timing_events(torch, 2, False)
+        if not eager:
+            gk = _capture(torch, stream, steps_fn(steps))
+    with torch.cuda.stream(stream):
+        if gw is not None:
+            gw.replay()
+        elif eager:
+            steps_fn(warmup)()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    with torch.cuda.stream(stream):
+        if inside:
+            gk.replay()
+        else:
+            ek[0].record(stream)
+            gk.replay() if not eager else steps_fn(steps)()
+            ek[1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = ek[0].elapsed_time(ek[1]) / steps
+    # the timed run's last step equals the same step run eagerly
+    last = wl.out.clone()
+    with torch.cuda.stream(stream):
+        wl.step((steps - 1) % C)
+    torch.cuda.synchronize()
+    graph_matches = bool(torch.equal(last, wl.out))
+
+    per_step_us = [float("nan")]
+    if spread_n:
+        es = _timing_events(torch, spread_n + 1, inside)
+        if inside:
+            gs = _capture(torch, stream, steps_fn(spread_n, es, steps))
+            with torch.cuda.stream(stream):
+                gs.replay()
+        else:
+            with torch.cuda.stream(stream):
+                steps_fn(spread_n, es, steps)()
+        torch.cuda.synchronize()
+        per_step_us = [es[i].elapsed_time(es[i + 1]) * 1e3 for i in range(spread_n)]
+    step_bytes = sum(wl.weight_bytes(c) for c in range(C)) / C
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    return {
+        "workload": wl.name, "act": wl.act, "rows": getattr(wl, "rows", 1),
+        "steps": steps, "warmup": warmup,
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "us_per_step_p10_p50_p90": [_pct(per_step_us, 0.1), _pct(per_step_us, 0.5), _pct(per_step_us, 0.9)],
+        "spread_samples": spread_n,
+        "spread_timing": ("%d consecutive steps in one graph, an event recorded between every two; each step's "
+                          "time includes one event record" if inside else
+                          "%d consecutive steps, an event on the stream between every two") % spread_n,
+        "weight_bytes_per_step": int(step_bytes),
+        "gbs": round(value, 2),
+        "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "weight_copies": C,
+        "timing": ("eager launches, %d steps, events on the stream around them" % steps if eager else
+                   "one HIP graph of %d steps, its events recorded inside the graph" % steps if inside else
+                   "one HIP graph of %d steps, events on the stream around its replay" % steps),
+        "verified": ver,
+        "graph_equals_eager": graph_matches,
+        "cache": getattr(wl, "cache", "cold: weight copies and input rows rotate past the Infinity Cache"),
+        "wall_s": round(t_wall, 4),
+    }
+
+
+def time_stages(wl, stream, ceil, eager=False, launches=400):
+    """Each of the step's calls alone: a graph of its launches, one per weight
+    copy (on the routing and activations the steps left for that copy),
+    replayed back to back between two events; with the time a plain read of
+    the same weight bytes takes."""
+    torch = wl.torch
+    wl.prepare_dominant()
+    C = wl.copies
+    out = []
+    for label, fn, nbytes in wl.stages():
+        def run_all(f=fn):
+            for c in range(C):
+                f(c)
+        g = run_all if eager else _capture(torch, stream, run_all).replay
+        reps = max(1, -(-launches // C))
+        with torch.cuda.stream(stream):
+            g()
+        torch.cuda.synchronize()
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            k0.record(stream)
+            for _ in range(reps):
+                g()
+            k1.record(stream)
+        torch.cuda.synchronize()
+        us = k0.elapsed_time(k1) / (reps * C) * 1e3
+        ent = {"call": label, "us_per_launch": round(us, 3), "weight_bytes": int(nbytes)}
+        if nbytes:
+            ent["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            ent["hbm_frac_of_peak"] = round(ent["gbs"] / HBM_PEAK_GBS, 4)
+            if ceil is not None:
+                pu, pg = ceil.same_bytes(nbytes)
+                ent["plain_read_us"] = pu
+                ent["frac_of_plain_read"] = round(pu / us, 4)
+        out.append(ent)
+    return out
+
+
+# The suite one default run measures after the headline: every workload the
+# configs name, in each numerics it is built for.
+SUITE = [
+    ("gemv_512x256", "f32"),
+    ("norm_gemv_2048x4096", "int8"),
+    ("norm_gemv_2048x4096", "f32"),
+    ("norm_gemv_2048x4096", "x2"),
+    ("moe_d2048_dff768_e128_k8", "f32"),
+    ("moe_d2048_dff768_e128_k8", "x2"),
+    ("moe_d4096_dff14336_e8_k2", "int8"),
+    ("moe_d4096_dff14336_e8_k2", "f32"),
+    ("moe_d4096_dff14336_e8_k2", "x2"),
+    ("chunk64_moe_d2048_dense4096", "int8"),
+    ("moe_shared_d2048_dff1408_e60_k4_s5632", "int8"),
+    ("moe_shared_d2048_dff1408_e60_k4_s5632", "f32"),
+]
+SUITE_STEPS = 400
+SUITE_WARMUP = 20
 
 
 def main():
@@ -802,94 +1181,40 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    import gc
+
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    import q8_gemv_sparse_amd as q8
+    stream = torch.cuda.Stream()
     if args.ceiling_only:
-        import q8_gemv_sparse_amd as q8
-        stream = torch.cuda.Stream()
-        print(json.dumps({"ceiling": stream_ceiling(torch, q8, stream, 28311552, args.no_graph)}), flush=True)
+        ceil = Ceiling(torch, q8, stream, args.no_graph)
+        print(json.dumps({"ceiling": ceil.describe(28311552)}), flush=True)
         return
+    ceil = None if args.no_ceiling else Ceiling(torch, q8, stream, args.no_graph)
+    t_start = time.perf_counter()
     wl = make_workload(args.workload, args.act, args.copies, args.separate)
-    ver = wl.verify()
-    ver["ok"] = bool(ver.get("idx_equal", True) and ver["max_rel_err"] <= ver["tol"] and
-                     ver.get("dense_max_rel_err", 0.0) <= ver["tol"])
-    log("[bench] verify against the oracle:", ver)
-    if not ver["ok"]:
-        log("[bench] WARNING: the step does not match the oracle; its figures measure a wrong result")
-
     if args.warm:
         # every step (and every dominant launch) on copy 0 with input row 0:
         # the same weights each time, resident in the Infinity Cache
         step0, dom0 = wl.step, wl.launch_dominant
         wl.step = lambda c: step0(0)
         wl.launch_dominant = lambda c: dom0(0)
-    stream = torch.cuda.Stream()
+        wl.cache = "warm: one weight copy and one input row every step (cache-resident, context only)"
+    head = measure(wl, args.steps, args.warmup, stream, args.no_graph, args.spread)
     C = wl.copies
-    with torch.cuda.stream(stream):
-        for c in range(C):  # eager warm-up on the timing stream
-            wl.step(c)
-    torch.cuda.synchronize()
-    if args.no_graph:
-        def run_steps(reps):
-            for _ in range(reps):
-                for c in range(C):
-                    wl.step(c)
-    else:
-        # capture a graph of C consecutive steps, one per weight copy
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for c in range(C):
-                wl.step(c)
-        torch.cuda.synchronize()
-
-        def run_steps(reps):
-            for _ in range(reps):
-                g.replay()
-    replays = max(1, -(-args.steps // C))
-    steps = replays * C
-    wreps = -(-args.warmup // C) if args.warmup > 0 else 0
-    with torch.cuda.stream(stream):
-        run_steps(wreps)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        run_steps(replays)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1)
-    ms_per_step = ms / steps
-    # the replayed result equals an eager step's
-    with torch.cuda.stream(stream):
-        run_steps(1)
-    torch.cuda.synchronize()
-    graph_out = wl.out.clone()
-    with torch.cuda.stream(stream):
-        wl.step(C - 1)
-    torch.cuda.synchronize()
-    graph_matches = bool(torch.equal(graph_out, wl.out))
 
     # the dominant kernel: a graph of its launches on each copy (the routing
     # each copy's last step left in place), replayed back to back; HIP events
     # on the replay stream around the replays
     wl.prepare_dominant()
-    if args.no_graph:
-        def run_dom():
-            for c in range(C):
-                wl.launch_dominant(c)
-    else:
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2, stream=stream):
-            for c in range(C):
-                wl.launch_dominant(c)
 
-        def run_dom():
-            g2.replay()
+    def run_dom_all():
+        for c in range(C):
+            wl.launch_dominant(c)
+    run_dom = run_dom_all if args.no_graph else _capture(torch, stream, run_dom_all).replay
     reps2 = max(1, -(-args.kernel_launches // C))
     with torch.cuda.stream(stream):
         run_dom()
@@ -903,30 +1228,16 @@ def main():
     torch.cuda.synchronize()
     kms = k0.elapsed_time(k1) / (reps2 * C)
     dom_bytes = sum(wl.dominant_bytes(i % C) for i in range(C)) / C
-    step_bytes = sum(wl.weight_bytes(c) for c in range(C)) / C
     achieved = dom_bytes / (kms * 1e-3) / 1e9
-
-    # the spread of the step time: each graph replay alone between events
-    per_step_us = []
-    with torch.cuda.stream(stream):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(min(replays, 200))]
-        for a0, a1 in evs:
-            a0.record(stream)
-            run_steps(1)
-            a1.record(stream)
-    torch.cuda.synchronize()
-    per_step_us = sorted(a0.elapsed_time(a1) * 1e3 / C for a0, a1 in evs)
-    pct = lambda q: round(per_step_us[min(len(per_step_us) - 1, int(q * len(per_step_us)))], 3)
-    spread = [pct(0.1), pct(0.5), pct(0.9)]
-
-    ceiling = None if args.no_ceiling else stream_ceiling(torch, wl.q8, stream, int(dom_bytes), args.no_graph)
+    head["stages"] = [] if args.warm else time_stages(wl, stream, ceil, args.no_graph)
+    ceiling = ceil.describe(dom_bytes) if ceil else None
 
     if args.calib_copy_mib:
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         log("[bench] calibration copy: %d MiB" % args.calib_copy_mib)
 
     traffic = None
@@ -937,9 +1248,9 @@ def main():
         if cnt.get("source_digest") == src_digest(*wl.dominant_src):
             traffic = cnt.get("hbm_bytes_per_launch")
 
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu:
+        step_bytes = head["weight_bytes_per_step"]
         per_step, sample = wl.cpu_baseline(args.cpu_budget)
         cpu = {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": sample + "; %.1f ms per step" % (per_step * 1e3), "host": host_cpu()}
@@ -949,39 +1260,48 @@ def main():
             cpu["all_cores"] = {"value": round(step_bytes / per_all / 1e9, 4), "unit": "GB/s", "cores": threads,
                                 "sample": "%d threads, each its own steps for %.0f s; %.2f ms per step together"
                                           % (threads, args.cpu_budget, per_all * 1e3)}
+    wl_rows, dom_name = getattr(wl, "rows", 1), wl.dominant
+    del wl
+    gc.collect()
+    torch.cuda.empty_cache()
+
+    suite = []
+    run_suite = args.suite == "all" or (args.suite == "auto" and args.workload == DEFAULT_WORKLOAD and
+                                        args.act == "int8" and not (args.warm or args.separate or args.no_graph))
+    if run_suite:
+        for name, act in SUITE:
+            log("[bench] suite: %s %s" % (name, act))
+            w2 = make_workload(name, act, 0)
+            ent = measure(w2, SUITE_STEPS, SUITE_WARMUP, stream, False, args.spread)
+            ent["stages"] = time_stages(w2, stream, ceil)
+            suite.append(ent)
+            del w2
+            gc.collect()
+            torch.cuda.empty_cache()
+
+    value = head["gbs"]
+    cfg = dict(head)
+    for k_ in ("gbs", "steps", "warmup"):
+        cfg.pop(k_)
+    cfg["workloads"] = suite
+    cfg["run_s"] = round(time.perf_counter() - t_start, 1)
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": wreps * C,
-        "ms_per_step": round(ms_per_step, 6),
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": round(head["us_per_step"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"int8": "i8", "x2": "i8x2", "f32": "f32"}[args.act],
         "data": "synthetic",
-        "config": {
-            "workload": wl.name,
-            "act": args.act,
-            "rows": getattr(wl, "rows", 1),
-            "weight_bytes_per_step": int(step_bytes),
-            "us_per_step": round(ms_per_step * 1e3, 3),
-            "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
-            "hbm_frac_of_stream_ceiling": round(value / ceiling["stream_read_gbs"], 4) if ceiling else None,
-            "us_per_step_p10_p50_p90": spread,
-            "weight_copies": C,
-            "timing": ("eager launches, %d rounds of %d steps" if args.no_graph else
-                       "HIP graph of %d steps replayed %d times") % ((replays, C) if args.no_graph else (C, replays)),
-            "verified": ver,
-            "graph_equals_eager": graph_matches,
-            "cache": "warm: one weight copy and one input row every step (cache-resident, context only)"
-                     if args.warm else "cold: weight copies and input rows rotate past the Infinity Cache",
-        },
+        "config": cfg,
         "roofline": {
             "bound": "hbm",
-            "kernel": wl.dominant,
+            "kernel": dom_name,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -989,13 +1309,13 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": int(dom_bytes),
             "us_per_launch": round(kms * 1e3, 3),
-            "timed": wl.dominant_timed,
+            "timed": "a graph of its launches, one per weight copy, replayed %d times back to back" % reps2,
             "ceiling": ceiling,
             "frac_of_stream_ceiling": round(achieved / ceiling["stream_read_gbs"], 4) if ceiling else None,
         },
         "cpu_baseline": cpu,
     }
-    log("[bench] wall %.3fs for %d steps" % (t_wall, steps))
+    log("[bench] timed region %.4fs for %d steps (rows %d)" % (head["wall_s"], head["steps"], wl_rows))
     print(json.dumps(out), flush=True)
 
 

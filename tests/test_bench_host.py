@@ -31,3 +31,24 @@ def test_two_words_refused_where_not_built():
             assert "two-word" in str(e)
         else:
             raise AssertionError("x2 accepted for %s" % name)
+
+
+def test_suite_names_every_config_in_its_numerics():
+    # one default run measures every configured workload (the GEMV, the norm
+    # + GEMV, both mixture shapes, the chunk, the shared-expert variant) in
+    # each numerics it is built for
+    import bench
+    import synthetic
+    names = {n for n, _ in bench.SUITE} | {bench.DEFAULT_WORKLOAD}
+    assert names == set(synthetic.CONFIGS)
+    for name, act in bench.SUITE:
+        assert act in bench.ACT_CODE
+        assert (name, act) != (bench.DEFAULT_WORKLOAD, "int8")  # the headline itself
+    for name in ("norm_gemv_2048x4096", "moe_d4096_dff14336_e8_k2"):
+        assert {a for n, a in bench.SUITE if n == name} == {"int8", "f32", "x2"}
+
+
+def test_percentiles():
+    import bench
+    assert bench._pct([5.0, 1.0, 3.0, 2.0, 4.0], 0.5) == 3.0
+    assert bench._pct(list(range(100)), 0.1) == 10 and bench._pct(list(range(100)), 0.9) == 90
