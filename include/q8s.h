@@ -85,6 +85,9 @@ extern "C" {
 #define Q8S_MAX_K 32
 #define Q8S_MAX_E 8192
 
+/* The static scratch of moe_ffn_block_noalloc, bytes per GPU (32 MiB). */
+#define Q8S_NOALLOC_SCRATCH_BYTES (32ll << 20)
+
 /*
  * q8_gemv -- Q8_0 matrix times activation rows (struct Q8Ref; fn prim,
  * Matmul arm: weight rows are outputs).
@@ -383,6 +386,29 @@ Q8S_API int add_rmsnorm_router_q8(const float *h, const float *r, const float *w
                           const int8_t *Wrq, const float *Wrs, int64_t rows, int64_t d, int64_t E,
                           float *sum, float *x, int8_t *xq, float *xs, double *logits, int act,
                           void *stream);
+
+/*
+ * moe_ffn_block_noalloc -- moe_ffn_block without a scratch argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments (less scratch), outputs, numerics, kernels and
+ * limits as moe_ffn_block; the scratch those kernels use is a fixed array of
+ * Q8S_NOALLOC_SCRATCH_BYTES in device memory that the library holds on each
+ * GPU it runs on until the process ends.  Sizes whose
+ * q8s_scratch_bytes(Q8S_FN_BLOCK, ...) exceed it are refused with
+ * Q8S_EUNSUPPORTED before any HIP call.  The first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress), so make one call
+ * outside any graph capture first.  The array needs no initial contents and
+ * keeps the last call's; every call on one GPU shares it, so calls that
+ * overlap on one GPU (on different streams, or from several threads) race:
+ * order them on one stream.  It calls no device allocation of any kind
+ * (hipMalloc, hipFree or an allocating library routine).
+ */
+Q8S_API int moe_ffn_block_noalloc(const float *h, const float *r, const float *w, float eps, const float *Wr,
+                                  const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                                  const int8_t *Wdq, const float *Wds, int64_t rows, int64_t d, int64_t dff,
+                                  int64_t E, int64_t k, float *sum, int32_t *idx, float *wts, float *out, int act,
+                                  void *stream);
 
 /*
  * moe_ffn_block_ex -- moe_ffn_block with the variants linked into the

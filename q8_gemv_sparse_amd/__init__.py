@@ -25,7 +25,7 @@ __all__ = [
     "moe_topk_gate_up_ex", "moe_down_combine_ex",
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
-    "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2",
+    "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2", "moe_ffn_block_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 ACT_F32 = 0
@@ -35,6 +35,7 @@ FN_ROUTE = 1
 FN_DOWN = 2
 FN_BLOCK = 3
 STREAM_WGS = 2048  # Q8S_STREAM_WGS: words q8s_stream_read writes
+NOALLOC_SCRATCH_BYTES = 32 << 20  # Q8S_NOALLOC_SCRATCH_BYTES: moe_ffn_block_noalloc's static scratch per GPU
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libq8s.so")
 
@@ -56,6 +57,8 @@ _SIGS = {
     "moe_down_combine": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, ctypes.c_int, _p, _sz, _p],
     "moe_ffn_block": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p,
                       _p, _p, ctypes.c_int, _p, _sz, _p],
+    "moe_ffn_block_noalloc": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64,
+                              _p, _p, _p, _p, ctypes.c_int, _p],
     "add_rmsnorm_gemv": [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, ctypes.c_int, _p],
     "add_rmsnorm_router": [_p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p],
     "moe_topk_gate_up": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _p,
@@ -396,6 +399,26 @@ def moe_ffn_block(h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act=ACT_F32
     _check(_lib.moe_ffn_block(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wr), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq),
                               _ptr(Wus), _ptr(Wdq), _ptr(Wds), rows, d, dff, E, k, _ptr(sum), _ptr(idx), _ptr(wts),
                               _ptr(out), act, _ptr(scratch), scratch.numel(), _stream(stream)))
+    return sum, idx, wts, out
+
+
+def moe_ffn_block_noalloc(h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, sum, idx, wts, out, act=ACT_F32,
+                          stream=None):
+    """moe_ffn_block on the library's static scratch: no scratch argument and
+    no allocation by the library.  The outputs are the caller's (sum, idx,
+    wts, out, as moe_ffn_block); returns them."""
+    for t, n in ((h, "h"), (r, "r"), (w, "w"), (Wr, "Wr"), (Wgs, "Wgs"), (Wus, "Wus"), (Wds, "Wds"),
+                 (sum, "sum"), (wts, "wts"), (out, "out")):
+        _dev(t, torch.float32, n)
+    for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq"), (Wdq, "Wdq")):
+        _dev(t, torch.int8, n)
+    _dev(idx, torch.int32, "idx")
+    E, d = Wr.shape
+    rows = h.numel() // d
+    dff = Wgq.shape[0] // E
+    _check(_lib.moe_ffn_block_noalloc(_ptr(h), _ptr(r), _ptr(w), float(eps), _ptr(Wr), _ptr(Wgq), _ptr(Wgs),
+                                      _ptr(Wuq), _ptr(Wus), _ptr(Wdq), _ptr(Wds), rows, d, dff, E, k, _ptr(sum),
+                                      _ptr(idx), _ptr(wts), _ptr(out), act, _stream(stream)))
     return sum, idx, wts, out
 
 

@@ -11,6 +11,7 @@
 
 #include <atomic>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -896,6 +897,74 @@ int moe_ffn_block(const float *h, const float *r, const float *w, float eps, con
     return block_common("moe_ffn_block", h, r, w, eps, q8s::RouterRows{Wr, nullptr, nullptr, 0}, Wgq, Wgs, Wuq, Wus,
                         Wdq, Wds, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, rows, d, dff, E, k, sum, idx,
                         wts, out, act, scratch, scratch_bytes, stream);
+}
+
+} // extern "C"
+
+namespace {
+
+// The allocation-free block's scratch: one fixed array in device memory,
+// which every GPU the library runs on holds from the module's load to the
+// end of the process.  In host code `scratch` names a host-side stand-in, not
+// a device address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel.
+static __device__ __align__(256) char scratch[Q8S_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEV = 64;
+void *g_noalloc_ptr[NOALLOC_MAX_DEV];
+std::mutex g_noalloc_mu;
+
+// This device's copy of the array, looked up on its first use; null (with a
+// message) if the device or the lookup fails.
+void *noalloc_scratch(const char *fn)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEV) {
+        (void)hipGetLastError();
+        fail(Q8S_ELAUNCH, "%s: no current HIP device (or device index %d beyond %d)", fn, dev, NOALLOC_MAX_DEV);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            fail(Q8S_ELAUNCH, "%s: hipGetSymbolAddress of the static scratch failed on device %d: %s", fn, dev,
+                 hipGetErrorString(e));
+            return nullptr;
+        }
+        g_noalloc_ptr[dev] = p;
+    }
+    return g_noalloc_ptr[dev];
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_ffn_block_noalloc(const float *h, const float *r, const float *w, float eps, const float *Wr,
+                          const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
+                          const int8_t *Wdq, const float *Wds, int64_t rows, int64_t d, int64_t dff, int64_t E,
+                          int64_t k, float *sum, int32_t *idx, float *wts, float *out, int act, void *stream)
+{
+    const char *fn = "moe_ffn_block_noalloc";
+    int rc;
+    if ((act != 2 && (rc = check_act(fn, act))) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    const size_t need = q8s::block_scratch_bytes(rows, d, dff, 0, E, k, act);
+    if (need > (size_t)Q8S_NOALLOC_SCRATCH_BYTES)
+        return fail(Q8S_EUNSUPPORTED,
+                    "%s: these sizes need %zu bytes of scratch; the library's static scratch holds %zu "
+                    "(use moe_ffn_block with a scratch of your own)",
+                    fn, need, (size_t)Q8S_NOALLOC_SCRATCH_BYTES);
+    void *p = noalloc_scratch(fn);
+    if (!p)
+        return Q8S_ELAUNCH;
+    return block_common(fn, h, r, w, eps, q8s::RouterRows{Wr, nullptr, nullptr, 0}, Wgq, Wgs, Wuq, Wus, Wdq, Wds,
+                        nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, rows, d, dff, E, k, sum, idx, wts,
+                        out, act, p, (size_t)Q8S_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int moe_ffn_block_ex(const float *h, const float *r, const float *w, float eps, const float *Wr, const int8_t *Wrq,

@@ -370,3 +370,20 @@ def test_gate_up_without_q8_form_only_for_chunks():
     assert gate_up(act=1, rows=1, hq=None, hs=None) == -1 and "only a chunk" in _err()
     # a chunk may leave both out, not one of them
     assert gate_up(act=1, rows=4, hq=None) == -1 and "`hq` is null" in _err()
+
+
+def test_block_noalloc_refusals_before_any_hip_call():
+    # the allocation-free block refuses shapes and sizes beyond its static
+    # scratch before touching a device (fake pointers, never dereferenced)
+    f = LIB.moe_ffn_block_noalloc
+
+    def call(rows=1, d=2048, dff=768, E=128, k=8, act=1):
+        return f(A, A + 0x1000000, A + 0x2000000, ctypes.c_float(1e-6), B, C, D, F, G, H, J, rows, d, dff, E, k,
+                 0x8000000, 0x9000000, 0xA000000, 0xB000000, act, None)
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_float] + [ctypes.c_void_p] * 7 + [ctypes.c_int64] * 5 + \
+        [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p]
+    assert call(rows=512) == -2 and "static scratch holds" in _err()
+    assert q8.q8s_scratch_bytes(q8.FN_BLOCK, 512, 2048, 768, 128, 8, 1) > q8.NOALLOC_SCRATCH_BYTES
+    assert call(act=3) == -2 and "unknown activation" in _err()
+    assert call(k=0) == -1 and "1 <= k <= E" in _err()
+    assert call(d=40) == -1 and "multiple of 32" in _err()
