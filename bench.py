@@ -1085,7 +1085,13 @@ def measure(wl, steps, warmup, stream, eager=False, spread_n=200):
             with torch.cuda.stream(stream):
                 gs.replay()
         else:
+            # eager steps with an event between every two, queued behind about
+            # 30 ms of other GPU work (replays of the timed graph), so the
+            # host's launches run ahead and no step waits for its submission
+            fill = 0 if eager else max(1, int(30.0 / max(ms_per_step * steps, 1e-3)))
             with torch.cuda.stream(stream):
+                for _ in range(fill):
+                    gk.replay()
                 steps_fn(spread_n, es, steps)()
         torch.cuda.synchronize()
         per_step_us = [es[i].elapsed_time(es[i + 1]) * 1e3 for i in range(spread_n)]
@@ -1099,7 +1105,8 @@ def measure(wl, steps, warmup, stream, eager=False, spread_n=200):
         "spread_samples": spread_n,
         "spread_timing": ("%d consecutive steps in one graph, an event recorded between every two; each step's "
                           "time includes one event record" if inside else
-                          "%d consecutive steps, an event on the stream between every two") % spread_n,
+                          "%d consecutive steps launched eagerly behind queued GPU work, an event on the stream "
+                          "between every two; each step's time includes one event record") % spread_n,
         "weight_bytes_per_step": int(step_bytes),
         "gbs": round(value, 2),
         "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
@@ -1114,6 +1121,29 @@ def measure(wl, steps, warmup, stream, eager=False, spread_n=200):
     }
 
 
+def time_launches(torch, stream, fn, C, launches, eager=False):
+    """µs per launch of fn(c): `launches` launches cycling over the C copies,
+    captured as one graph (a graph replay has a fixed cost of its own, several
+    µs, so a graph holds many launches), replayed once untimed and once
+    between two events."""
+    n = max(C, launches // C * C)
+
+    def run_all():
+        for i in range(n):
+            fn(i % C)
+    g = run_all if eager else _capture(torch, stream, run_all).replay
+    with torch.cuda.stream(stream):
+        g()
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        k0.record(stream)
+        g()
+        k1.record(stream)
+    torch.cuda.synchronize()
+    return k0.elapsed_time(k1) / n * 1e3
+
+
 def time_stages(wl, stream, ceil, eager=False, launches=400):
     """Each of the step's calls alone: a graph of its launches, one per weight
     copy (on the routing and activations the steps left for that copy),
@@ -1124,22 +1154,7 @@ def time_stages(wl, stream, ceil, eager=False, launches=400):
     C = wl.copies
     out = []
     for label, fn, nbytes in wl.stages():
-        def run_all(f=fn):
-            for c in range(C):
-                f(c)
-        g = run_all if eager else _capture(torch, stream, run_all).replay
-        reps = max(1, -(-launches // C))
-        with torch.cuda.stream(stream):
-            g()
-        torch.cuda.synchronize()
-        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            k0.record(stream)
-            for _ in range(reps):
-                g()
-            k1.record(stream)
-        torch.cuda.synchronize()
-        us = k0.elapsed_time(k1) / (reps * C) * 1e3
+        us = time_launches(torch, stream, fn, C, launches, eager)
         ent = {"call": label, "us_per_launch": round(us, 3), "weight_bytes": int(nbytes)}
         if nbytes:
             ent["gbs"] = round(nbytes / (us * 1e-6) / 1e9, 1)
@@ -1210,23 +1225,8 @@ def main():
     # each copy's last step left in place), replayed back to back; HIP events
     # on the replay stream around the replays
     wl.prepare_dominant()
-
-    def run_dom_all():
-        for c in range(C):
-            wl.launch_dominant(c)
-    run_dom = run_dom_all if args.no_graph else _capture(torch, stream, run_dom_all).replay
-    reps2 = max(1, -(-args.kernel_launches // C))
-    with torch.cuda.stream(stream):
-        run_dom()
-    torch.cuda.synchronize()
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        k0.record(stream)
-        for _ in range(reps2):
-            run_dom()
-        k1.record(stream)
-    torch.cuda.synchronize()
-    kms = k0.elapsed_time(k1) / (reps2 * C)
+    n_dom = max(C, args.kernel_launches // C * C)
+    kms = time_launches(torch, stream, wl.launch_dominant, C, args.kernel_launches, args.no_graph) / 1e3
     dom_bytes = sum(wl.dominant_bytes(i % C) for i in range(C)) / C
     achieved = dom_bytes / (kms * 1e-3) / 1e9
     head["stages"] = [] if args.warm else time_stages(wl, stream, ceil, args.no_graph)
@@ -1309,7 +1309,7 @@ def main():
             "traffic": traffic,
             "bytes_per_launch": int(dom_bytes),
             "us_per_launch": round(kms * 1e3, 3),
-            "timed": "a graph of its launches, one per weight copy, replayed %d times back to back" % reps2,
+            "timed": "one graph of %d of its launches back to back, cycling over the %d weight copies" % (n_dom, C),
             "ceiling": ceiling,
             "frac_of_stream_ceiling": round(achieved / ceiling["stream_read_gbs"], 4) if ceiling else None,
         },
