@@ -874,10 +874,123 @@ class MoeSharedBlock(MoeBlock):
         return el / n, "%d steps (rows 1, inputs from the same pool), %.1f s" % (n, el)
 
 
+class StackBlocks(Workload):
+    """L layers of the mixture block in a row, each with weights of its own:
+    one moe_ffn_stack call a step (3 launches a layer; each layer's residual
+    add deferred into the next layer's add + norm launch, the last one's into
+    its down-combine).  Stage: one moe_ffn_block call, a layer alone."""
+
+    dominant = "k_route_gate_up"
+    dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_moe.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
+
+    def __init__(self, name, cfg, act, copies, pool=64):
+        import numpy as np
+        import torch
+
+        import q8_gemv_sparse_amd as q8
+        import synthetic
+        self.q8, self.torch, self.np = q8, torch, np
+        self.name, self.act = name, act
+        d, dff, E, k, L = cfg["d"], cfg["dff"], cfg["E"], cfg["k"], cfg["layers"]
+        self.d, self.dff, self.E, self.k, self.L = d, dff, E, k, L
+        t0 = time.time()
+        self.blocks = [synthetic.block_inputs(100 + l, d, dff, E, k, 1) for l in range(L)]
+        rng = np.random.default_rng(1)
+        self.pool_h = [synthetic.normal(rng, 1, d) for _ in range(pool)]
+        self.pool_r = [synthetic.normal(rng, 1, d) for _ in range(pool)]
+        self.pool = pool
+        log("[bench] generated inputs in %.1fs" % (time.time() - t0))
+        per_expert = 3 * dff * d + 3 * dff * (d // 32) * 4
+        self.layer_bytes = E * d * 4 + k * per_expert
+        self.copies = copies or _copies(L * self.layer_bytes, 0)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        base = [tuple(dev(a) for a in (b.w, b.moe.Wr, b.moe.Wgq, b.moe.Wgs, b.moe.Wuq, b.moe.Wus, b.moe.Wdq,
+                                       b.moe.Wds)) for b in self.blocks]
+        self.W = [base] + [[tuple(t.clone() for t in lw) for lw in base] for _ in range(self.copies - 1)]
+        self.h = [dev(a) for a in self.pool_h]
+        self.r = [dev(a) for a in self.pool_r]
+        z = lambda *s_, dt=torch.float32: torch.empty(s_, dtype=dt, device="cuda")
+        self.out = z(1, d)
+        self.idx = [z(L, 1, k, dt=torch.int32) for _ in range(self.copies)]
+        self.wts = [z(L, 1, k) for _ in range(self.copies)]
+        a = ACT_CODE[act]
+        self.scratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_STACK, 1, d, dff, E, k, a), dtype=torch.uint8,
+                                   device="cuda")
+        self.bscratch = torch.zeros(q8.q8s_scratch_bytes(q8.FN_BLOCK, 1, d, dff, E, k, a), dtype=torch.uint8,
+                                    device="cuda")
+        self.bsum, self.bidx, self.bwts, self.bout = z(1, d), z(1, k, dt=torch.int32), z(1, k), z(1, d)
+        torch.cuda.synchronize()
+        log("[bench] %s: %d layers, %d weight copies of %.1f MB on the device"
+            % (name, L, self.copies, L * (E * d * 4 + E * per_expert) / 1e6))
+
+    def step(self, c):
+        i = c % self.pool
+        self.q8.moe_ffn_stack(self.h[i], self.r[i], self.W[c % self.copies], self.k, 1e-6, act=ACT_CODE[self.act],
+                              out=self.out, idx=self.idx[c % self.copies], wts=self.wts[c % self.copies],
+                              scratch=self.scratch)
+
+    def one_block(self, c):
+        """Layer 0 of copy c alone, as one moe_ffn_block call."""
+        i = c % self.pool
+        lw = self.W[c % self.copies][0]
+        self.q8.moe_ffn_block(self.h[i], self.r[i], lw[0], 1e-6, *lw[1:], self.k, act=ACT_CODE[self.act],
+                              sum=self.bsum, idx=self.bidx, wts=self.bwts, out=self.bout, scratch=self.bscratch)
+
+    launch_dominant = one_block
+
+    def weight_bytes(self, c=None):
+        return self.L * self.layer_bytes
+
+    def dominant_bytes(self, c=None):
+        return self.layer_bytes
+
+    def stages(self):
+        return [("moe_ffn_block (one layer alone, for the per-layer comparison)", self.one_block, self.layer_bytes)]
+
+    def verify(self):
+        """One eager step against the oracle's chain add_rmsnorm -> moe a layer."""
+        import oracle
+        np = self.np
+        self.step(0)
+        self.torch.cuda.synchronize()
+        a = ACT_CODE[self.act]
+        hh, rr = self.pool_h[0], self.pool_r[0]
+        same = True
+        for l, b in enumerate(self.blocks):
+            s, y64 = oracle.add_rmsnorm(hh, rr, b.w, 1e-6)
+            m = b.moe
+            ridx, _, _, ry = oracle.moe(y64.astype(np.float32), m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds,
+                                        self.k, a)
+            same = same and bool(np.array_equal(self.idx[0][l].cpu().numpy(), ridx))
+            hh, rr = ry.astype(np.float32), s
+        ref = rr.astype(np.float64) + hh.astype(np.float64)
+        got = self.out.cpu().numpy()
+        err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+        return {"idx_equal": same, "max_rel_err": err, "tol": self.L * TOL[self.act]}
+
+    def cpu_baseline(self, budget):
+        import oracle
+        np = self.np
+        a = ACT_CODE[self.act]
+        n, t0 = 0, time.perf_counter()
+        while True:
+            hh, rr = self.pool_h[n % self.pool], self.pool_r[n % self.pool]
+            for b in self.blocks:
+                s, y64 = oracle.add_rmsnorm(hh, rr, b.w, 1e-6)
+                m = b.moe
+                ry = oracle.moe(y64.astype(np.float32), m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a)[3]
+                hh, rr = ry.astype(np.float32), s
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                break
+        return el / n, "%d steps of %d layers, %.1f s" % (n, self.L, el)
+
+
 def make_workload(name, act, copies, separate=False):
     import synthetic
     cfg = synthetic.CONFIGS[name]
-    if act == "x2" and (cfg["kind"] not in ("norm_gemv", "moe") or (cfg["kind"] == "moe" and separate)):
+    if act == "x2" and (cfg["kind"] not in ("norm_gemv", "moe", "stack") or (cfg["kind"] == "moe" and separate)):
         raise SystemExit("two-word activations are built for the norm + GEMV and the mixture block's one call")
     if cfg["kind"] == "moe":
         return MoeBlock(name, cfg, act, copies, separate=separate)
@@ -889,6 +1002,8 @@ def make_workload(name, act, copies, separate=False):
         return MoeSharedBlock(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "gemv":
         return Gemv(name, cfg, act, copies)
+    if cfg["kind"] == "stack":
+        return StackBlocks(name, cfg, act, copies)
     raise SystemExit("workload %s is not a bench workload" % name)
 
 
@@ -1182,6 +1297,7 @@ SUITE = [
     ("chunk64_moe_d2048_dense4096", "int8"),
     ("moe_shared_d2048_dff1408_e60_k4_s5632", "int8"),
     ("moe_shared_d2048_dff1408_e60_k4_s5632", "f32"),
+    ("stack4_moe_d2048_dff768_e128_k8", "int8"),
 ]
 SUITE_STEPS = 400
 SUITE_WARMUP = 20

@@ -81,6 +81,7 @@ extern "C" {
 #define Q8S_FN_ROUTE 1
 #define Q8S_FN_DOWN 2
 #define Q8S_FN_BLOCK 3
+#define Q8S_FN_STACK 4
 
 #define Q8S_MAX_K 32
 #define Q8S_MAX_E 8192
@@ -386,6 +387,36 @@ Q8S_API int add_rmsnorm_router_q8(const float *h, const float *r, const float *w
                           const int8_t *Wrq, const float *Wrs, int64_t rows, int64_t d, int64_t E,
                           float *sum, float *x, int8_t *xq, float *xs, double *logits, int act,
                           void *stream);
+
+/*
+ * moe_ffn_stack -- `layers` mixture blocks in a row, each layer with weights
+ * of its own, as one call (forward_shim.rs module doc: the sum and the RMS
+ * norm of it as one row kernel; the whole forward captured as one graph):
+ *   s_0 = h + r
+ *   for l = 0 .. layers-1:  x_l = RMSNorm(s_l) * w[l]   (as moe_ffn_block)
+ *                           m_l = mixture_l(x_l)        (router Wr[l], experts
+ *                                                        Wgq[l] .. Wds[l])
+ *                           s_{l+1} = s_l + m_l         (a float32 add)
+ *   out = s_layers (the residual stream after the last layer)
+ * The residual add of layer l is deferred into layer l + 1's add + norm row
+ * kernel (it reads m_l and s_l and forms their sum), and the last layer's is
+ * folded into its down-combine epilogue: each layer is moe_ffn_block's
+ * launches, nothing in between, so out equals the chain of moe_ffn_block
+ * calls (h = m_{l-1}, r = s_{l-1}) followed by one float32 add, bit for bit.
+ * h, r: device f32 [rows, d]; w, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds: HOST
+ * arrays of `layers` device pointers, each as moe_ffn_block's argument of
+ * that name.  Outputs: out (device f32 [rows, d]); idx (device int32
+ * [layers, rows, k]) and wts (device f32 [layers, rows, k]), each layer's
+ * choices.  scratch: device, >= q8s_scratch_bytes(Q8S_FN_STACK, ...) bytes,
+ * 256-byte aligned, no initial contents needed.  1 <= layers <= 1024; other
+ * limits and numerics (act 0, 1 or 2) as moe_ffn_block.
+ */
+Q8S_API int moe_ffn_stack(const float *h, const float *r, int64_t layers, const float *const *w,
+                          const float *const *Wr, const int8_t *const *Wgq, const float *const *Wgs,
+                          const int8_t *const *Wuq, const float *const *Wus, const int8_t *const *Wdq,
+                          const float *const *Wds, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k,
+                          float eps, float *out, int32_t *idx, float *wts, int act, void *scratch,
+                          size_t scratch_bytes, void *stream);
 
 /*
  * moe_ffn_block_noalloc -- moe_ffn_block without a scratch argument and

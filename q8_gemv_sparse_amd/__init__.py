@@ -26,6 +26,7 @@ __all__ = [
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
     "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2", "moe_ffn_block_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "moe_ffn_stack", "FN_STACK",
 ]
 
 ACT_F32 = 0
@@ -34,6 +35,7 @@ ACT_X2 = 2  # two-word int8 activations (the *_x2 calls, and moe_ffn_block)
 FN_ROUTE = 1
 FN_DOWN = 2
 FN_BLOCK = 3
+FN_STACK = 4
 STREAM_WGS = 2048  # Q8S_STREAM_WGS: words q8s_stream_read writes
 NOALLOC_SCRATCH_BYTES = 32 << 20  # Q8S_NOALLOC_SCRATCH_BYTES: moe_ffn_block_noalloc's static scratch per GPU
 
@@ -57,6 +59,7 @@ _SIGS = {
     "moe_down_combine": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, ctypes.c_int, _p, _sz, _p],
     "moe_ffn_block": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p,
                       _p, _p, ctypes.c_int, _p, _sz, _p],
+    "moe_ffn_stack": [_p, _p, _i64] + [_p] * 8 + [_i64] * 5 + [ctypes.c_float, _p, _p, _p, ctypes.c_int, _p, _sz, _p],
     "moe_ffn_block_noalloc": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64,
                               _p, _p, _p, _p, ctypes.c_int, _p],
     "add_rmsnorm_gemv": [_p, _p, _p, ctypes.c_float, _p, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, ctypes.c_int, _p],
@@ -400,6 +403,41 @@ def moe_ffn_block(h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act=ACT_F32
                               _ptr(Wus), _ptr(Wdq), _ptr(Wds), rows, d, dff, E, k, _ptr(sum), _ptr(idx), _ptr(wts),
                               _ptr(out), act, _ptr(scratch), scratch.numel(), _stream(stream)))
     return sum, idx, wts, out
+
+
+def moe_ffn_stack(h, r, layers, k, eps, act=ACT_F32, out=None, idx=None, wts=None, scratch=None, stream=None):
+    """``len(layers)`` mixture blocks in a row: ``layers`` is a list of per-layer
+    tuples (w, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds) of device tensors.  Returns
+    (out, idx [L, rows, k], wts [L, rows, k]); out is the residual stream after
+    the last layer."""
+    _dev(h, torch.float32, "h"); _dev(r, torch.float32, "r")
+    L = len(layers)
+    cols = list(zip(*layers)) if L else [()] * 8
+    dts = (torch.float32, torch.float32, torch.int8, torch.float32, torch.int8, torch.float32, torch.int8,
+           torch.float32)
+    names = ("w", "Wr", "Wgq", "Wgs", "Wuq", "Wus", "Wdq", "Wds")
+    for col, dt, nm in zip(cols, dts, names):
+        for t in col:
+            _dev(t, dt, nm)
+    E, d = layers[0][1].shape
+    dff = layers[0][2].shape[0] // E
+    rows = h.numel() // d
+    dev = h.device
+    if out is None:
+        out = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((L, rows, k), dtype=torch.int32, device=dev)
+    if wts is None:
+        wts = torch.empty((L, rows, k), dtype=torch.float32, device=dev)
+    if scratch is None:
+        scratch = torch.empty(max(q8s_scratch_bytes(FN_STACK, rows, d, dff, E, k, act), 1), dtype=torch.uint8,
+                              device=dev)
+    _dev(out, torch.float32, "out"); _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
+    _dev(scratch, torch.uint8, "scratch")
+    arrs = [(ctypes.c_void_p * L)(*[t.data_ptr() for t in col]) for col in cols]
+    _check(_lib.moe_ffn_stack(_ptr(h), _ptr(r), L, *arrs, rows, d, dff, E, k, float(eps), _ptr(out), _ptr(idx),
+                              _ptr(wts), act, _ptr(scratch), scratch.numel(), _stream(stream)))
+    return out, idx, wts
 
 
 def moe_ffn_block_noalloc(h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, sum, idx, wts, out, act=ACT_F32,

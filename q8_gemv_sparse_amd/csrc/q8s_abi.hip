@@ -170,6 +170,8 @@ size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E
         return q8s::down_scratch_bytes(rows, d, dff, k, act);
     case Q8S_FN_BLOCK:
         return q8s::block_scratch_bytes(rows, d, dff, 0, E, k, act);
+    case Q8S_FN_STACK:
+        return q8s::stack_scratch_bytes(rows, d, dff, E, k, act);
     default:
         return 0;
     }
@@ -897,6 +899,62 @@ int moe_ffn_block(const float *h, const float *r, const float *w, float eps, con
     return block_common("moe_ffn_block", h, r, w, eps, q8s::RouterRows{Wr, nullptr, nullptr, 0}, Wgq, Wgs, Wuq, Wus,
                         Wdq, Wds, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, rows, d, dff, E, k, sum, idx,
                         wts, out, act, scratch, scratch_bytes, stream);
+}
+
+int moe_ffn_stack(const float *h, const float *r, int64_t layers, const float *const *w, const float *const *Wr,
+                  const int8_t *const *Wgq, const float *const *Wgs, const int8_t *const *Wuq,
+                  const float *const *Wus, const int8_t *const *Wdq, const float *const *Wds, int64_t rows,
+                  int64_t d, int64_t dff, int64_t E, int64_t k, float eps, float *out, int32_t *idx, float *wts,
+                  int act, void *scratch, size_t scratch_bytes, void *stream)
+{
+    const char *fn = "moe_ffn_stack";
+    int rc;
+    if ((act != 2 && (rc = check_act(fn, act))) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    if (act == 2 && !q8s::block_fused(rows, d, dff, E, act))
+        return fail(Q8S_EUNSUPPORTED, "%s: two-word numerics (act 2) need E <= %d and d <= %lld", fn,
+                    (int)q8s::ROUTE_FUSED_MAX_E, (long long)q8s::NORM_LOGITS_MAX_D);
+    if (layers < 1 || layers > 1024)
+        return fail(layers < 1 ? Q8S_EINVAL : Q8S_EUNSUPPORTED, "%s: layers = %lld: 1 <= layers <= 1024", fn,
+                    (long long)layers);
+    if (!(eps >= 0.0f) || eps != eps)
+        return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    if (!w || !Wr || !Wgq || !Wgs || !Wuq || !Wus || !Wdq || !Wds)
+        return fail(Q8S_EINVAL, "%s: a per-layer pointer array (w, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds) is null", fn);
+    const size_t n = (size_t)(rows * d);
+    const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
+    const size_t dq = (size_t)(E * d) * (size_t)dff, dsb = (size_t)(E * d) * (size_t)(dff / 32) * 4;
+    std::vector<Span> ins = {{h, n * 4, "h"}, {r, n * 4, "r"}};
+    std::vector<std::string> names;
+    names.reserve((size_t)layers * 8);
+    for (int64_t l = 0; l < layers; l++) {
+        const void *p[8] = {w[l], Wr[l], Wgq[l], Wgs[l], Wuq[l], Wus[l], Wdq[l], Wds[l]};
+        const size_t b[8] = {(size_t)d * 4, (size_t)(E * d) * 4, wq, wsb, wq, wsb, dq, dsb};
+        const char *nm[8] = {"w", "Wr", "Wgq", "Wgs", "Wuq", "Wus", "Wdq", "Wds"};
+        for (int i = 0; i < 8; i++) {
+            names.push_back(std::string(nm[i]) + "[" + std::to_string(l) + "]");
+            ins.push_back({p[i], b[i], names.back().c_str()});
+        }
+    }
+    std::vector<Span> outs = {{out, n * 4, "out"},
+                              {idx, (size_t)(layers * rows * k) * 4, "idx"},
+                              {wts, (size_t)(layers * rows * k) * 4, "wts"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
+        return rc;
+    const size_t need = q8s::stack_scratch_bytes(rows, d, dff, E, k, act);
+    if (!scratch || scratch_bytes < need)
+        return fail(Q8S_ESCRATCH,
+                    "%s: scratch of %zu bytes given, %zu needed (a block's, and the residual stream between layers)",
+                    fn, scratch ? scratch_bytes : (size_t)0, need);
+    if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0)
+        return fail(Q8S_EALIGN, "%s: `scratch` is not 256-byte aligned", fn);
+    outs.push_back({scratch, need, "scratch"});
+    if ((rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::StackArgs a{h, r, layers, w, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, rows, d, dff, E, k, eps, out, idx, wts, act,
+                     scratch};
+    clear_stale();
+    return launched(q8s::stack_launch(a, as_stream(stream)), fn);
 }
 
 } // extern "C"

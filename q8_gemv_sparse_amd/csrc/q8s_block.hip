@@ -134,6 +134,7 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
     a.y = b.out;
     a.act = b.act;
     a.scratch = s.down;
+    a.resid = b.resid;
     if (!chunk) {
         a.Sgq = b.Sgq;
         a.Sgs = b.Sgs;
@@ -187,6 +188,62 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
     sa.hq = s.shq;
     sa.hs = s.shs;
     return shared_launch(sa, st);
+}
+
+// A stack of L layers (forward_shim.rs module doc: the sum and the RMS norm
+// of it as one row kernel; the whole forward one graph of launches):
+//   s_0 = h + r;  for each layer l:  x_l = RMSNorm(s_l) * w_l,
+//   m_l = mixture_l(x_l),  s_{l+1} = s_l + m_l;   out = s_L.
+// Each layer is one block call.  The residual add s_l + m_l of layer l is
+// deferred into layer l + 1's first launch, whose add + norm row kernel reads
+// m_l as h and s_l as r and writes their sum; the last layer's add is folded
+// into its down-combine epilogue, which writes s_L itself.  Nothing runs
+// between the layers' launches.  Scratch: the block's, then the running sums
+// s_l (two, alternating) and the mixture output m_l.
+size_t stack_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
+{
+    return block_scratch_bytes(rows, d, dff, 0, E, k, act) + 3 * align256((size_t)(rows * d) * 4);
+}
+
+hipError_t stack_launch(const StackArgs &a, hipStream_t st)
+{
+    char *base = static_cast<char *>(a.scratch);
+    const size_t bs = block_scratch_bytes(a.rows, a.d, a.dff, 0, a.E, a.k, a.act);
+    const size_t vb = align256((size_t)(a.rows * a.d) * 4);
+    float *S[2] = {reinterpret_cast<float *>(base + bs), reinterpret_cast<float *>(base + bs + vb)};
+    float *M = reinterpret_cast<float *>(base + bs + 2 * vb);
+    const int64_t nk = a.rows * a.k;
+    for (int64_t l = 0; l < a.layers; l++) {
+        const bool last = l == a.layers - 1;
+        BlockArgs b{};
+        b.h = l == 0 ? a.h : M;
+        b.r = l == 0 ? a.r : S[(l - 1) & 1];
+        b.w = a.w[l];
+        b.eps = a.eps;
+        b.rt = RouterRows{a.Wr[l], nullptr, nullptr, 0};
+        b.Wgq = a.Wgq[l];
+        b.Wgs = a.Wgs[l];
+        b.Wuq = a.Wuq[l];
+        b.Wus = a.Wus[l];
+        b.Wdq = a.Wdq[l];
+        b.Wds = a.Wds[l];
+        b.rows = a.rows;
+        b.d = a.d;
+        b.dff = a.dff;
+        b.E = a.E;
+        b.k = a.k;
+        b.sum = S[l & 1];
+        b.idx = a.idx + l * nk;
+        b.wts = a.wts + l * nk;
+        b.out = last ? a.out : M;
+        b.resid = last ? S[l & 1] : nullptr;
+        b.act = a.act;
+        b.scratch = a.scratch;
+        const hipError_t err = block_launch(b, st);
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 } // namespace q8s

@@ -149,6 +149,8 @@ struct MoeArgs {
     // two-word numerics (act 2): the low words of x and of the hidden rows
     const int8_t *xl;
     int8_t *hl;
+    // the residual stream the down-combine adds to its output (null: none)
+    const float *resid;
 };
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st);
 // gate-up that takes each row's top-K from `logits` itself (E <= ROUTE_FUSED_MAX_E)
@@ -204,8 +206,34 @@ struct BlockArgs {
     const int8_t *Sdq;
     const float *Sds;
     int64_t sdff;
+    // the residual stream added to the mixture's output (null: none)
+    const float *resid;
 };
 size_t block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k, int act);
+
+// L mixture blocks in a row (a stack of layers), each layer's weights its
+// own: the per-layer pointers are host arrays of L device pointers
+struct StackArgs {
+    const float *h, *r;
+    int64_t layers;
+    const float *const *w;
+    const float *const *Wr;
+    const int8_t *const *Wgq;
+    const float *const *Wgs;
+    const int8_t *const *Wuq;
+    const float *const *Wus;
+    const int8_t *const *Wdq;
+    const float *const *Wds;
+    int64_t rows, d, dff, E, k;
+    float eps;
+    float *out;
+    int32_t *idx;
+    float *wts;
+    int act;
+    void *scratch;
+};
+size_t stack_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
+hipError_t stack_launch(const StackArgs &s, hipStream_t st);
 bool block_fused(int64_t rows, int64_t d, int64_t dff, int64_t E, int act);
 hipError_t block_launch(const BlockArgs &b, hipStream_t st);
 

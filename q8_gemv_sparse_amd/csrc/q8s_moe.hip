@@ -277,9 +277,12 @@ constexpr int dn_unroll()
 
 // Waves take (slot, slice) pairs: pairs j*ks + s for the K slots, then
 // k*ks + s for the shared expert's kss slices of its sdff-long rows (the same
-// lane shape).  The grid is (d / DN_TILE, rows); with y_add (then y itself)
-// the result is added to what y holds.  SH: with a shared expert (a kernel of
-// its own, so the mixture without one runs the plain code).
+// lane shape).  The grid is (d / DN_TILE, rows).  With y_add the output is
+// y_add + the mixture, one float32 add: the residual stream folded into the
+// epilogue (forward_shim.rs module doc: the mixture's sum and what follows
+// it fused), or, with y_add == y, the result added to what y holds.  SH: with
+// a shared expert (a kernel of its own, so the mixture without one runs the
+// plain code).
 template <int ACT, int LPR, int C, bool SH>
 __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__restrict__ h, const int8_t *__restrict__ hq,
                                                               const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
@@ -370,8 +373,8 @@ __global__ void __launch_bounds__(DN_MAX_WAVES * WAVE) k_down(const float *__res
                 ds += part[rp + s][t];
             acc += ds;
         }
-        // a branch, not a select: the load of y happens only when asked for
-        if (SH && y_add)
+        // a branch, not a select: the load happens only when asked for
+        if (y_add)
             acc = y_add[row * d + o0 + t] + acc;
         y[row * d + o0 + t] = acc;
     }
@@ -433,11 +436,11 @@ hipError_t dn_go(const MoeArgs &a, int ks, hipStream_t st)
     if (a.sdff)
         hipLaunchKernelGGL((k_down<ACT, LPR, C, true>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds,
                            shared_w(a), a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss,
-                           a.acc_out ? a.y : nullptr, a.y, a.hl);
+                           a.acc_out ? a.y : a.resid, a.y, a.hl);
     else
         hipLaunchKernelGGL((k_down<ACT, LPR, C, false>), grid, dim3(64 * nw), 0, st, a.h, a.hq, a.hs, a.Wdq, a.Wds,
-                           shared_w(a), a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss, nullptr,
-                           a.y, a.hl);
+                           shared_w(a), a.idx, a.wts, (int)a.d, (int)a.dff, (int)a.E, (int)a.k, ks, kss,
+                           a.acc_out ? a.y : a.resid, a.y, a.hl);
     return hipGetLastError();
 }
 

@@ -499,9 +499,10 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
     }
 }
 
+// With resid: y = resid + the mixture (the residual stream folded in).
 __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__ pa, const int32_t *__restrict__ idx,
                                                      const float *__restrict__ wts, int d, int k, int E,
-                                                     float *__restrict__ y)
+                                                     const float *__restrict__ resid, float *__restrict__ y)
 {
     const int64_t r = blockIdx.y;
     const int o = blockIdx.x * 256 + threadIdx.x;
@@ -513,6 +514,8 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
         if (e >= 0 && e < E)
             acc = __builtin_fmaf(wts[r * k + jj], pa[(r * k + jj) * d + o], acc);
     }
+    if (resid)
+        acc = resid[r * d + o] + acc;
     y[r * d + o] = acc;
 }
 
@@ -569,7 +572,8 @@ hipError_t dn_chunk_go(const MoeArgs &a, hipStream_t st)
     if (err != hipSuccess)
         return err;
     dim3 g2((unsigned)((a.d + 255) / 256), (unsigned)a.rows);
-    hipLaunchKernelGGL(k_chunk_combine, g2, dim3(256), 0, st, pa, a.idx, a.wts, (int)a.d, (int)a.k, (int)a.E, a.y);
+    hipLaunchKernelGGL(k_chunk_combine, g2, dim3(256), 0, st, pa, a.idx, a.wts, (int)a.d, (int)a.k, (int)a.E,
+                       a.resid, a.y);
     return hipGetLastError();
 }
 

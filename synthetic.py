@@ -196,7 +196,7 @@ def fill_pattern(n, scale=1.0):
     return (((p % 7) - 3) * scale).astype(np.float32)
 
 
-# The five workloads, by name; sizes as in the project's benchmark table.
+# The workloads, by name; sizes as in the project's benchmark table.
 CONFIGS = {
     "gemv_512x256": dict(kind="gemv", n_out=512, n_in=256, m=1),
     "norm_gemv_2048x4096": dict(kind="norm_gemv", d=2048, n_out=4096, eps=1e-6),
@@ -206,4 +206,6 @@ CONFIGS = {
     # a mixture with an always-on shared expert four experts wide and its
     # router as Q8_0 rows (the Qwen1.5-MoE-A2.7B-like FFN shape)
     "moe_shared_d2048_dff1408_e60_k4_s5632": dict(kind="moe_shared", d=2048, dff=1408, E=60, k=4, sdff=5632),
+    # four layers of the 128-expert block in a row, each with weights of its own
+    "stack4_moe_d2048_dff768_e128_k8": dict(kind="stack", d=2048, dff=768, E=128, k=8, layers=4),
 }

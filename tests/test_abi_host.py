@@ -387,3 +387,36 @@ def test_block_noalloc_refusals_before_any_hip_call():
     assert call(act=3) == -2 and "unknown activation" in _err()
     assert call(k=0) == -1 and "1 <= k <= E" in _err()
     assert call(d=40) == -1 and "multiple of 32" in _err()
+
+
+def test_stack_refusals_before_any_hip_call():
+    f = LIB.moe_ffn_stack
+    P = ctypes.c_void_p
+    f.argtypes = [P, P, ctypes.c_int64] + [P] * 8 + [ctypes.c_int64] * 5 + [ctypes.c_float, P, P, P, ctypes.c_int, P,
+                                                                          ctypes.c_size_t, P]
+    d, dff, E, k, rows = 256, 96, 8, 2, 1
+    need = q8.q8s_scratch_bytes(q8.FN_STACK, rows, d, dff, E, k, 1)
+    assert need >= q8.q8s_scratch_bytes(q8.FN_BLOCK, rows, d, dff, E, k, 1) + 3 * rows * d * 4
+
+    def arrays(L, hole=None):
+        out = []
+        for i in range(8):  # w, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds of each layer, far apart
+            vals = [0x1000000 * (1 + 8 * l + i) for l in range(L)]
+            if hole == (i, 1):
+                vals[1] = 0
+            out.append((P * L)(*vals))
+        return out
+
+    def call(L=2, hole=None, arrs=None, sb=None, out=0x7000000000, scratch=0x7100000000):
+        a = arrs if arrs is not None else arrays(L, hole)
+        return f(0x6000000000, 0x6100000000, L, *a, rows, d, dff, E, k, ctypes.c_float(1e-6), out,
+                 0x7200000000, 0x7300000000, 1, scratch, need if sb is None else sb, None)
+    assert call(L=0) == -1 and "layers" in _err()
+    assert call(L=2000) == -2 and "1024" in _err()
+    assert call(hole=(2, 1)) == -1 and "`Wgq[1]` is null" in _err()
+    nulls = arrays(2)
+    nulls[5] = None
+    assert call(arrs=nulls) == -1 and "pointer array" in _err()
+    assert call(sb=64) == -4 and "scratch" in _err()
+    assert call(scratch=0x7100000010) == -3 and "256-byte" in _err()
+    assert call(out=0x1000000 * 2) == -1 and "overlaps input `Wr[0]`" in _err()
