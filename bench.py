@@ -641,11 +641,13 @@ class ChunkBlock(MoeBlock):
     dominant = "k_chunk_gate_up"
     dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_moe_chunk.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
 
-    def __init__(self, name, cfg, copies):
+    def __init__(self, name, cfg, act, copies):
         # the separate calls: the dense projection reads the chunk's Q8_0 rows
-        # that add_rmsnorm_q8 writes, and the grouped gate-up is the dominant
-        # kernel
-        super().__init__(name, cfg, "int8", copies, rows=cfg["rows"], pool=8, separate=True)
+        # that add_rmsnorm_q8 writes (in two words: q8_quantize_rows_x2 of
+        # its float32 rows), and the grouped gate-up is the dominant kernel
+        if act == "f32":
+            raise SystemExit("workload %s runs in int8 numerics (one or two words)" % name)
+        super().__init__(name, cfg, act, copies, rows=cfg["rows"], pool=8, separate=True)
         self.dominant = "k_chunk_gate_up"
         self.dominant_timed = "moe_gate_up without the hidden rows' Q8_0 pass: k_chunk_gate_up alone"
         import synthetic
@@ -666,16 +668,55 @@ class ChunkBlock(MoeBlock):
         # measured 173.2 against 161.7 us a step -- the fork and join cost
         # more than the overlap gains
         super().step(c)
+        self._dense(c)
+
+    def _dense(self, c):
         Dq, Ds = self.D[c % self.copies]
-        self.q8.q8_gemv(Dq, Ds, xq=self.xq, xs=self.xs, y=self.dense_out, act=self.q8.ACT_INT8)
+        if self.act == "x2":
+            self.q8.q8_gemv_x2(Dq, Ds, self.xq, self.xl, self.xs, y=self.dense_out)
+        else:
+            self.q8.q8_gemv(Dq, Ds, xq=self.xq, xs=self.xs, y=self.dense_out, act=self.q8.ACT_INT8)
+
+    def _norm(self, c):
+        if self.act != "x2":
+            return super()._norm(c)
+        q8 = self.q8
+        i = c % self.pool
+        q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y, want_q8=False)
+        q8.q8_quantize_rows_x2(self.y, xq=self.xq, xl=self.xl, xs=self.xs)
+
+    def _gate_up(self, c, a, want_q8=True):
+        if self.act != "x2":
+            W = self.W[c % self.copies]
+            return self.q8.moe_gate_up(W[1], W[2], W[3], W[4], self.idx[c % self.copies], self.E, xq=self.xq,
+                                       xs=self.xs, hq=self.hq if want_q8 else None, hs=self.hs if want_q8 else None,
+                                       h=self.hf, act=self.q8.ACT_INT8, want_q8=want_q8)
+        W = self.W[c % self.copies]
+        self.q8.moe_gate_up_x2(W[1], W[2], W[3], W[4], self.idx[c % self.copies], self.E, self.xq, self.xl, self.xs,
+                               h=self.hf, hq=self.hq if want_q8 else None, hl=self.hl if want_q8 else None,
+                               hs=self.hs if want_q8 else None, want_q8=want_q8)
+
+    def _down(self, c):
+        W = self.W[c % self.copies]
+        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+        if self.act == "x2":
+            self.q8.moe_down_combine_x2(W[5], W[6], idx, wts, self.E, self.hq, self.hl, self.hs, y=self.out,
+                                        scratch=self.dscratch)
+        else:
+            self.q8.moe_down_combine(W[5], W[6], idx, wts, self.E, hq=self.hq, hs=self.hs, y=self.out,
+                                     act=self.q8.ACT_INT8, scratch=self.dscratch)
+
+    def _mixture(self, c):
+        W = self.W[c % self.copies]
+        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+        self.q8.moe_route_topk(self.y, W[0], self.k, idx=idx, wts=wts, scratch=self.rscratch)
+        self._gate_up(c, None)
+        self._down(c)
 
     def launch_dominant(self, c):
         # the grouped gate-up kernel alone: the float32 hidden rows, without
         # the quantise pass the step runs after it
-        q8 = self.q8
-        W = self.W[c % self.copies]
-        q8.moe_gate_up(W[1], W[2], W[3], W[4], self.idx[c % self.copies], self.E, xq=self.xq, xs=self.xs,
-                       h=self.hf, act=q8.ACT_INT8, want_q8=False)
+        self._gate_up(c, None, want_q8=False)
 
     def weight_bytes(self, c=None):
         return super().weight_bytes(c) + self.dense_bytes
@@ -694,22 +735,16 @@ class ChunkBlock(MoeBlock):
             W = self.W[c % C]
             q8.moe_route_topk(self.y, W[0], k, idx=self.idx[c % C], wts=self.wts[c % C], scratch=self.rscratch)
 
-        def gate_up(c):
-            self._gate_up(c, q8.ACT_INT8)
-
-        def down(c):
-            W = self.W[c % C]
-            q8.moe_down_combine(W[5], W[6], self.idx[c % C], self.wts[c % C], E, hq=self.hq, hs=self.hs, y=self.out,
-                                act=q8.ACT_INT8, scratch=self.dscratch)
-
-        def dense(c):
-            Dq, Ds = self.D[c % C]
-            q8.q8_gemv(Dq, Ds, xq=self.xq, xs=self.xs, y=self.dense_out, act=q8.ACT_INT8)
-        return [("add_rmsnorm_q8 (k_add_rmsnorm_q8, 64 rows)", self._norm, 0),
+        x2 = self.act == "x2"
+        sfx = "_x2" if x2 else ""
+        return [("add_rmsnorm_q8%s (k_add_rmsnorm_q8%s, 64 rows)" % (" + q8_quantize_rows_x2" if x2 else "",
+                                                                    " + k_quantize_rows_x2" if x2 else ""),
+                 self._norm, 0),
                 ("moe_route_topk (k_logits_tile + k_topk)", route, E * d * 4),
-                ("moe_gate_up (k_chunk_gate_up + k_quantize_rows)", gate_up, int(avg_u * 2 * q8b(dff, d))),
-                ("moe_down_combine (k_chunk_down2 + k_chunk_combine)", down, int(avg_u * q8b(d, dff))),
-                ("q8_gemv dense 64 x 2048 -> 4096 (k_gemm_i8)", dense, self.dense_bytes)]
+                ("moe_gate_up%s (k_chunk_gate_up + k_quantize_rows%s)" % (sfx, sfx),
+                 lambda c: self._gate_up(c, None), int(avg_u * 2 * q8b(dff, d))),
+                ("moe_down_combine%s (k_chunk_down2 + k_chunk_combine)" % sfx, self._down, int(avg_u * q8b(d, dff))),
+                ("q8_gemv%s dense 64 x 2048 -> 4096 (k_gemm_i8)" % sfx, self._dense, self.dense_bytes)]
 
     def verify(self):
         import oracle
@@ -719,27 +754,33 @@ class ChunkBlock(MoeBlock):
         m = self.host_w
         s, y64 = oracle.add_rmsnorm(self.pool_h[0], self.pool_r[0], self.norm_w, 1e-6)
         x = y64.astype(np.float32)
-        ridx, rw, rh, ry = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, 1)
+        a = ACT_CODE[self.act]
+        ridx, rw, rh, ry = oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a)
         got = self.out.cpu().numpy()
         err = float(np.max(np.abs(got - ry)) / np.max(np.abs(ry)))
-        q, sc = oracle.quantize(x)
-        dref = oracle.gemv_i8(self.Dq_h, self.Ds_h, q, sc)
+        if a == 2:
+            dref = oracle.gemv_i8x2(self.Dq_h, self.Ds_h, *oracle.quantize_x2(x))
+        else:
+            dref = oracle.gemv_i8(self.Dq_h, self.Ds_h, *oracle.quantize(x))
         derr = float(np.max(np.abs(self.dense_out.cpu().numpy() - dref)) / np.max(np.abs(dref)))
         return {"idx_equal": bool(np.array_equal(self.idx[0].cpu().numpy(), ridx)), "max_rel_err": err,
-                "dense_max_rel_err": derr, "tol": 2e-3}
+                "dense_max_rel_err": derr, "tol": TOL[self.act]}
 
     def cpu_baseline(self, budget):
         import oracle
         np = self.np
         m = self.host_w
         n, t0 = 0, time.perf_counter()
+        a = ACT_CODE[self.act]
         while True:
             i = n % self.pool
             s, y64 = oracle.add_rmsnorm(self.pool_h[i], self.pool_r[i], self.norm_w, 1e-6)
             x = y64.astype(np.float32)
-            q, sc = oracle.quantize(x)
-            oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, 1)
-            oracle.gemv_i8(self.Dq_h, self.Ds_h, q, sc)
+            oracle.moe(x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, self.k, a)
+            if a == 2:
+                oracle.gemv_i8x2(self.Dq_h, self.Ds_h, *oracle.quantize_x2(x))
+            else:
+                oracle.gemv_i8(self.Dq_h, self.Ds_h, *oracle.quantize(x))
             n += 1
             el = time.perf_counter() - t0
             if el >= budget:
@@ -990,14 +1031,14 @@ class StackBlocks(Workload):
 def make_workload(name, act, copies, separate=False):
     import synthetic
     cfg = synthetic.CONFIGS[name]
-    if act == "x2" and (cfg["kind"] not in ("norm_gemv", "moe", "stack") or (cfg["kind"] == "moe" and separate)):
+    if act == "x2" and (cfg["kind"] not in ("norm_gemv", "moe", "stack", "chunk") or (cfg["kind"] == "moe" and separate)):
         raise SystemExit("two-word activations are built for the norm + GEMV and the mixture block's one call")
     if cfg["kind"] == "moe":
         return MoeBlock(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "norm_gemv":
         return NormGemv(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "chunk":
-        return ChunkBlock(name, cfg, copies)
+        return ChunkBlock(name, cfg, act, copies)
     if cfg["kind"] == "moe_shared":
         return MoeSharedBlock(name, cfg, act, copies, separate=separate)
     if cfg["kind"] == "gemv":
@@ -1295,6 +1336,7 @@ SUITE = [
     ("moe_d4096_dff14336_e8_k2", "f32"),
     ("moe_d4096_dff14336_e8_k2", "x2"),
     ("chunk64_moe_d2048_dense4096", "int8"),
+    ("chunk64_moe_d2048_dense4096", "x2"),
     ("moe_shared_d2048_dff1408_e60_k4_s5632", "int8"),
     ("moe_shared_d2048_dff1408_e60_k4_s5632", "f32"),
     ("stack4_moe_d2048_dff768_e128_k8", "int8"),

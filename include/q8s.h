@@ -389,6 +389,30 @@ Q8S_API int add_rmsnorm_router_q8(const float *h, const float *r, const float *w
                           void *stream);
 
 /*
+ * moe_gate_up_x2, moe_down_combine_x2 -- moe_gate_up and moe_down_combine in
+ * two-word numerics (fn moe_dp4a_kernels' two-pass, logit-exact trio; arena.rs
+ * fn quant_parts: words, low words, one scale a block): the activation is
+ * xq/xl/xs (as q8_quantize_rows_x2 writes it), each block's value two exact
+ * int32 dots joined as 128 * isum + isum_lo and scaled by ws * xs / 128 (as
+ * q8_gemv_x2), the hidden rows quantised in two words (hq/hl/hs, device int8
+ * [rows, k, dff] twice and f32 [rows, k, dff/32]).  A chunk of rows (rows > 1,
+ * d <= 2048, dff <= 4096) runs the grouped kernels, each chosen expert's
+ * weights read once: moe_gate_up_x2 then requires h (device f32
+ * [rows, k, dff], the float32 hidden rows it stages) and may leave out
+ * hq/hl/hs; moe_down_combine_x2 needs scratch of
+ * q8s_scratch_bytes(Q8S_FN_DOWN, ..., Q8S_ACT_X2).  Other arguments, limits
+ * and refusals as moe_gate_up / moe_down_combine in INT8 mode.
+ */
+Q8S_API int moe_gate_up_x2(const int8_t *xq, const int8_t *xl, const float *xs, const int8_t *Wgq, const float *Wgs,
+                           const int8_t *Wuq, const float *Wus, const int32_t *idx, int64_t rows, int64_t d,
+                           int64_t dff, int64_t E, int64_t k, float *h, int8_t *hq, int8_t *hl, float *hs,
+                           void *stream);
+Q8S_API int moe_down_combine_x2(const int8_t *hq, const int8_t *hl, const float *hs, const int8_t *Wdq,
+                                const float *Wds, const int32_t *idx, const float *wts, int64_t rows, int64_t d,
+                                int64_t dff, int64_t E, int64_t k, float *y, void *scratch, size_t scratch_bytes,
+                                void *stream);
+
+/*
  * moe_ffn_stack -- `layers` mixture blocks in a row, each layer with weights
  * of its own, as one call (forward_shim.rs module doc: the sum and the RMS
  * norm of it as one row kernel; the whole forward captured as one graph):

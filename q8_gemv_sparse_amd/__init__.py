@@ -26,7 +26,7 @@ __all__ = [
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
     "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2", "moe_ffn_block_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "moe_ffn_stack", "FN_STACK",
+    "moe_ffn_stack", "FN_STACK", "moe_gate_up_x2", "moe_down_combine_x2",
 ]
 
 ACT_F32 = 0
@@ -59,6 +59,8 @@ _SIGS = {
     "moe_down_combine": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, ctypes.c_int, _p, _sz, _p],
     "moe_ffn_block": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p,
                       _p, _p, ctypes.c_int, _p, _sz, _p],
+    "moe_gate_up_x2": [_p] * 8 + [_i64] * 5 + [_p] * 5,
+    "moe_down_combine_x2": [_p] * 7 + [_i64] * 5 + [_p, _p, _sz, _p],
     "moe_ffn_stack": [_p, _p, _i64] + [_p] * 8 + [_i64] * 5 + [ctypes.c_float, _p, _p, _p, ctypes.c_int, _p, _sz, _p],
     "moe_ffn_block_noalloc": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64,
                               _p, _p, _p, _p, ctypes.c_int, _p],
@@ -403,6 +405,57 @@ def moe_ffn_block(h, r, w, eps, Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds, k, act=ACT_F32
                               _ptr(Wus), _ptr(Wdq), _ptr(Wds), rows, d, dff, E, k, _ptr(sum), _ptr(idx), _ptr(wts),
                               _ptr(out), act, _ptr(scratch), scratch.numel(), _stream(stream)))
     return sum, idx, wts, out
+
+
+def moe_gate_up_x2(Wgq, Wgs, Wuq, Wus, idx, E, xq, xl, xs, h=None, hq=None, hl=None, hs=None, want_q8=True,
+                   stream=None):
+    """moe_gate_up in two-word numerics.  Returns (h or None, hq, hl, hs); a
+    chunk of rows stages the float32 hidden rows in h (allocated when not
+    given) and, with want_q8=False, leaves out their two-word form."""
+    for t, n in ((Wgq, "Wgq"), (Wuq, "Wuq"), (xq, "xq"), (xl, "xl")):
+        _dev(t, torch.int8, n)
+    for t, n in ((Wgs, "Wgs"), (Wus, "Wus"), (xs, "xs")):
+        _dev(t, torch.float32, n)
+    _dev(idx, torch.int32, "idx")
+    rows, k = idx.shape
+    d = Wgq.shape[1]
+    dff = Wgq.shape[0] // E
+    dev = Wgq.device
+    if h is None and rows > 1:
+        h = torch.empty((rows, k, dff), dtype=torch.float32, device=dev)
+    if want_q8:
+        if hq is None:
+            hq = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
+        if hl is None:
+            hl = torch.empty((rows, k, dff), dtype=torch.int8, device=dev)
+        if hs is None:
+            hs = torch.empty((rows, k, dff // 32), dtype=torch.float32, device=dev)
+    _dev(h, torch.float32, "h"); _dev(hq, torch.int8, "hq"); _dev(hl, torch.int8, "hl"); _dev(hs, torch.float32, "hs")
+    _check(_lib.moe_gate_up_x2(_ptr(xq), _ptr(xl), _ptr(xs), _ptr(Wgq), _ptr(Wgs), _ptr(Wuq), _ptr(Wus), _ptr(idx),
+                               rows, d, dff, E, k, _ptr(h), _ptr(hq), _ptr(hl), _ptr(hs), _stream(stream)))
+    return h, hq, hl, hs
+
+
+def moe_down_combine_x2(Wdq, Wds, idx, wts, E, hq, hl, hs, y=None, scratch=None, stream=None):
+    """moe_down_combine in two-word numerics: y[rows, d]."""
+    _dev(Wdq, torch.int8, "Wdq"); _dev(Wds, torch.float32, "Wds")
+    _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts")
+    _dev(hq, torch.int8, "hq"); _dev(hl, torch.int8, "hl"); _dev(hs, torch.float32, "hs")
+    rows, k = idx.shape
+    dff = Wdq.shape[1]
+    d = Wdq.shape[0] // E
+    dev = Wdq.device
+    if y is None:
+        y = torch.empty((rows, d), dtype=torch.float32, device=dev)
+    _dev(y, torch.float32, "y")
+    need = q8s_scratch_bytes(FN_DOWN, rows, d, dff, E, k, ACT_X2)
+    if need and scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev)
+    _dev(scratch, torch.uint8, "scratch")
+    _check(_lib.moe_down_combine_x2(_ptr(hq), _ptr(hl), _ptr(hs), _ptr(Wdq), _ptr(Wds), _ptr(idx), _ptr(wts), rows,
+                                    d, dff, E, k, _ptr(y), _ptr(scratch), 0 if scratch is None else scratch.numel(),
+                                    _stream(stream)))
+    return y
 
 
 def moe_ffn_stack(h, r, layers, k, eps, act=ACT_F32, out=None, idx=None, wts=None, scratch=None, stream=None):

@@ -112,7 +112,8 @@ int check_act(const char *fn, int act)
     if (act == 2)
         return fail(Q8S_EUNSUPPORTED,
                     "%s: act = 2 (two-word int8 activations) is served by q8_quantize_rows_x2, q8_gemv_x2, "
-                    "add_rmsnorm_gemv_x2, moe_topk_gate_up_x2 and moe_ffn_block only", fn);
+                    "add_rmsnorm_gemv_x2, moe_gate_up_x2, moe_topk_gate_up_x2, moe_down_combine_x2, moe_ffn_block "
+                    "and moe_ffn_stack", fn);
     return fail(Q8S_EUNSUPPORTED, "%s: unknown activation mode act = %d", fn, act);
 }
 
@@ -401,6 +402,110 @@ int moe_gate_up(const float *x, const int8_t *xq, const float *xs, const int8_t 
     a.act = act;
     clear_stale();
     return launched(q8s::gate_up_launch(a, as_stream(stream)), fn);
+}
+
+int moe_gate_up_x2(const int8_t *xq, const int8_t *xl, const float *xs, const int8_t *Wgq, const float *Wgs,
+                   const int8_t *Wuq, const float *Wus, const int32_t *idx, int64_t rows, int64_t d, int64_t dff,
+                   int64_t E, int64_t k, float *h, int8_t *hq, int8_t *hl, float *hs, void *stream)
+{
+    const char *fn = "moe_gate_up_x2";
+    int rc;
+    if ((rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    const size_t wq = (size_t)(E * dff) * (size_t)d, wsb = (size_t)(E * dff) * (size_t)(d / 32) * 4;
+    const size_t nh = (size_t)(rows * k * dff), nx = (size_t)(rows * d);
+    const bool chunk = rows > 1 && q8s::chunk_supported(d, dff);
+    if (chunk && !h)
+        return fail(Q8S_EINVAL, "%s: a chunk of rows: `h` is required (the grouped chunk kernels stage the float32 "
+                    "hidden rows there before forming their two-word form)", fn);
+    const bool q = hq || hl || hs;
+    if (!q && !chunk)
+        return fail(Q8S_EINVAL, "%s: `hq`/`hl`/`hs` are required (only a chunk of rows in the grouped kernels may "
+                    "leave out the hidden rows' two-word form)", fn);
+    std::vector<Span> ins = {{Wgq, wq, "Wgq"}, {Wgs, wsb, "Wgs"}, {Wuq, wq, "Wuq"}, {Wus, wsb, "Wus"},
+                             {idx, (size_t)(rows * k) * 4, "idx"}, {xq, nx, "xq"}, {xl, nx, "xl"},
+                             {xs, nx / 32 * 4, "xs"}};
+    std::vector<Span> outs;
+    if (h)
+        outs.push_back({h, nh * 4, "h"});
+    if (q) {
+        outs.push_back({hq, nh, "hq"});
+        outs.push_back({hl, nh, "hl"});
+        outs.push_back({hs, nh / 32 * 4, "hs"});
+    }
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::MoeArgs a{};
+    a.xq = xq;
+    a.xl = xl;
+    a.xs = xs;
+    a.Wgq = Wgq;
+    a.Wgs = Wgs;
+    a.Wuq = Wuq;
+    a.Wus = Wus;
+    a.idx = idx;
+    a.rows = rows;
+    a.d = d;
+    a.dff = dff;
+    a.E = E;
+    a.k = k;
+    a.h = h;
+    a.hq = hq;
+    a.hl = hl;
+    a.hs = hs;
+    a.act = 2;
+    clear_stale();
+    return launched(q8s::gate_up_launch(a, as_stream(stream)), fn);
+}
+
+int moe_down_combine_x2(const int8_t *hq, const int8_t *hl, const float *hs, const int8_t *Wdq, const float *Wds,
+                        const int32_t *idx, const float *wts, int64_t rows, int64_t d, int64_t dff, int64_t E,
+                        int64_t k, float *y, void *scratch, size_t scratch_bytes, void *stream)
+{
+    const char *fn = "moe_down_combine_x2";
+    int rc;
+    if ((rc = check_moe_shape(fn, rows, d, dff, E, k)))
+        return rc;
+    const size_t nh = (size_t)(rows * k * dff);
+    std::vector<Span> ins = {{Wdq, (size_t)(E * d) * (size_t)dff, "Wdq"},
+                             {Wds, (size_t)(E * d) * (size_t)(dff / 32) * 4, "Wds"},
+                             {idx, (size_t)(rows * k) * 4, "idx"},
+                             {wts, (size_t)(rows * k) * 4, "wts"},
+                             {hq, nh, "hq"},
+                             {hl, nh, "hl"},
+                             {hs, nh / 32 * 4, "hs"}};
+    std::vector<Span> outs = {{y, (size_t)(rows * d) * 4, "y"}};
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
+        return rc;
+    const size_t need = q8s::down_scratch_bytes(rows, d, dff, k, 2);
+    if (need) {
+        if (!scratch || scratch_bytes < need)
+            return fail(Q8S_ESCRATCH, "%s: scratch of %zu bytes given, %zu needed (per-choice results)", fn,
+                        scratch ? scratch_bytes : (size_t)0, need);
+        if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0)
+            return fail(Q8S_EALIGN, "%s: `scratch` is not 256-byte aligned", fn);
+        outs.push_back({scratch, need, "scratch"});
+    }
+    if ((rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    q8s::MoeArgs a{};
+    a.hq = const_cast<int8_t *>(hq);
+    a.hl = const_cast<int8_t *>(hl);
+    a.hs = const_cast<float *>(hs);
+    a.Wdq = Wdq;
+    a.Wds = Wds;
+    a.idx = idx;
+    a.wts = wts;
+    a.rows = rows;
+    a.d = d;
+    a.dff = dff;
+    a.E = E;
+    a.k = k;
+    a.y = y;
+    a.act = 2;
+    a.scratch = need ? scratch : nullptr;
+    clear_stale();
+    return launched(q8s::down_launch(a, as_stream(stream)), fn);
 }
 
 int moe_down_combine(const float *h, const int8_t *hq, const float *hs, const int8_t *Wdq, const float *Wds,
@@ -832,10 +937,11 @@ int block_common(const char *fn, const float *h, const float *r, const float *w,
     if ((act != 2 && (rc = check_act(fn, act))) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
         return rc;
     if (act == 2) {
-        // two words: the three-launch form
-        if (!q8s::block_fused(rows, d, dff, E, act))
-            return fail(Q8S_EUNSUPPORTED, "%s: two-word numerics (act 2) need E <= %d and d <= %lld", fn,
-                        (int)q8s::ROUTE_FUSED_MAX_E, (long long)q8s::NORM_LOGITS_MAX_D);
+        // two words: the three-launch form, or a chunk's grouped kernels
+        if (!q8s::block_chunk(rows, d, dff, act) && !q8s::block_fused(rows, d, dff, E, act))
+            return fail(Q8S_EUNSUPPORTED,
+                        "%s: two-word numerics (act 2) need E <= %d and d <= %lld, or a chunk of rows with d <= 2048 "
+                        "and dff <= 4096", fn, (int)q8s::ROUTE_FUSED_MAX_E, (long long)q8s::NORM_LOGITS_MAX_D);
     }
     if (!(eps >= 0.0f) || eps != eps)
         return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
@@ -911,9 +1017,10 @@ int moe_ffn_stack(const float *h, const float *r, int64_t layers, const float *c
     int rc;
     if ((act != 2 && (rc = check_act(fn, act))) || (rc = check_moe_shape(fn, rows, d, dff, E, k)))
         return rc;
-    if (act == 2 && !q8s::block_fused(rows, d, dff, E, act))
-        return fail(Q8S_EUNSUPPORTED, "%s: two-word numerics (act 2) need E <= %d and d <= %lld", fn,
-                    (int)q8s::ROUTE_FUSED_MAX_E, (long long)q8s::NORM_LOGITS_MAX_D);
+    if (act == 2 && !q8s::block_chunk(rows, d, dff, act) && !q8s::block_fused(rows, d, dff, E, act))
+        return fail(Q8S_EUNSUPPORTED,
+                    "%s: two-word numerics (act 2) need E <= %d and d <= %lld, or a chunk of rows with d <= 2048 "
+                    "and dff <= 4096", fn, (int)q8s::ROUTE_FUSED_MAX_E, (long long)q8s::NORM_LOGITS_MAX_D);
     if (layers < 1 || layers > 1024)
         return fail(layers < 1 ? Q8S_EINVAL : Q8S_EUNSUPPORTED, "%s: layers = %lld: 1 <= layers <= 1024", fn,
                     (long long)layers);

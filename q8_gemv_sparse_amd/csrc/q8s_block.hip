@@ -48,11 +48,12 @@ struct BlockScratch {
     float *sh;  // a chunk's shared hidden rows (f32, or their Q8_0 form below)
     int8_t *shq;
     float *shs;
+    int8_t *shl;  // two words: their low words
     void *down;
     size_t bytes;
 };
 
-bool chunk_mode(int64_t rows, int64_t d, int64_t dff, int act) { return act == 1 && rows > 1 && chunk_supported(d, dff); }
+bool chunk_mode(int64_t rows, int64_t d, int64_t dff, int act) { return act >= 1 && rows > 1 && chunk_supported(d, dff); }
 
 BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t sdff, int64_t E, int64_t k, int act)
 {
@@ -86,6 +87,8 @@ BlockScratch carve(char *base, int64_t rows, int64_t d, int64_t dff, int64_t sdf
         const size_t ns = (size_t)(rows * sdff);
         s.shq = reinterpret_cast<int8_t *>(take(ns));
         s.shs = reinterpret_cast<float *>(take(ns / QB * 4));
+        if (act == 2)
+            s.shl = reinterpret_cast<int8_t *>(take(ns));
     }
     const size_t dn = down_scratch_bytes(rows, d, dff, k, act);
     s.down = dn ? take(dn) : nullptr;
@@ -99,6 +102,8 @@ size_t block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdff, i
 {
     return carve(nullptr, rows, d, dff, sdff, E, k, act).bytes;
 }
+
+bool block_chunk(int64_t rows, int64_t d, int64_t dff, int act) { return chunk_mode(rows, d, dff, act); }
 
 bool block_fused(int64_t rows, int64_t d, int64_t dff, int64_t E, int act)
 {
@@ -159,12 +164,17 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
         a.wts_w = b.wts;
         err = route_gate_up_launch(a, st);
     } else {
-        err = add_rmsnorm_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, b.sum, s.x, s.xq, s.xs, st);
+        // two words: the normed row's words, low words and scales from its
+        // float32 form (the same words and scales as the one-word epilogue's)
+        err = add_rmsnorm_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, b.sum, s.x, b.act == 2 ? nullptr : s.xq,
+                                 b.act == 2 ? nullptr : s.xs, st);
+        if (err == hipSuccess && b.act == 2)
+            err = quantize_x2_launch(s.x, b.rows, b.d, s.xq, s.xl, s.xs, st);
         if (err != hipSuccess)
             return err;
         if (rt.Wrq)
             err = route_q8_launch(s.x, s.xq, s.xs, rt.Wrq, rt.Wrs, b.rows, b.d, b.E, b.k, rt.act, b.idx, b.wts,
-                                  s.logits, st);
+                                  s.logits, st, s.xl);
         else
             err = route_launch(s.x, rt.Wr, b.rows, b.d, b.E, b.k, b.idx, b.wts, s.logits, st);
         if (err != hipSuccess)
@@ -187,6 +197,7 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
     sa.h = nullptr;
     sa.hq = s.shq;
     sa.hs = s.shs;
+    sa.hl = s.shl;
     return shared_launch(sa, st);
 }
 

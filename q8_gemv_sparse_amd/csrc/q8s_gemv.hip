@@ -12,7 +12,7 @@
 //                 low word's weighed 1/128).  Rows longer than one wave's slice are cut along k
 //                 across the waves of a workgroup and joined through LDS in a
 //                 fixed order.
-//   k_gemm_i8     int8 activations with many rows: v_mfma_i32_16x16x32_i8,
+//   k_gemm_i8     int8 activations (one or two words) with many rows: v_mfma_i32_16x16x32_i8,
 //                 whose k of 32 is one Q8_0 block, so every MFMA result is an
 //                 exact int32 block sum that is scaled by its weight and
 //                 activation scales in registers (the register-dequant GEMM of
@@ -287,36 +287,43 @@ Q8S_DEV void put_swizzled(int8_t *row, int r, int k, i32x4 v)
     *reinterpret_cast<i32x4 *>(row + 16 * (k ^ (sw >> 1))) = v;
 }
 
-template <int MT>
+// X2: two-word activations, their low words staged beside the words.
+template <int MT, bool X2>
 struct GemmLds {
     static constexpr int TM = 16 * MT;
     int8_t w[GEMM_TN][GEMM_ROW];
     int8_t a[TM][GEMM_ROW];
+    int8_t l[X2 ? TM : 1][GEMM_ROW];
     float ws[GEMM_KB][GEMM_TN + 1];
     float xs[GEMM_KB][TM + 4];
     float part[GEMM_NW][TM][GEMM_TN + 4];  // row pitch 20: a wave's 64 writes hit 64 banks
 };
 
 // A pass's global loads of one thread.
-template <int MT>
+template <int MT, bool X2>
 struct GemmStage {
     static constexpr int WL = GEMM_TN * GEMM_CH / (GEMM_NW * WAVE);       // weight chunks
     static constexpr int AL = 16 * MT * GEMM_CH / (GEMM_NW * WAVE);       // activation chunks
     static constexpr int XL = 16 * MT * GEMM_KB / (GEMM_NW * WAVE);       // activation scales
     i32x4 w[WL];
     i32x4 a[AL];
+    i32x4 l[X2 ? AL : 1];
     float ws;
     float xs[XL];
 };
 
-template <int MT>
+// X2 (two-word activations, the low words xl): a block's two exact int32
+// sums, one MFMA each against the same weight fragment, joined as
+// 128 * isum + isum_lo (below 2^27 in magnitude) and scaled by ws * xs / 128.
+template <int MT, bool X2>
 __global__ void __launch_bounds__(GEMM_NW * WAVE)
     k_gemm_i8(const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out, int n_in,
-              const int8_t *__restrict__ xq, const float *__restrict__ xs, int m, float *__restrict__ y)
+              const int8_t *__restrict__ xq, const float *__restrict__ xs, int m, float *__restrict__ y,
+              const int8_t *__restrict__ xl)
 {
     typedef int v4i __attribute__((ext_vector_type(4)));
-    using L = GemmLds<MT>;
-    using S = GemmStage<MT>;
+    using L = GemmLds<MT, X2>;
+    using S = GemmStage<MT, X2>;
     constexpr int TM = L::TM;
     __shared__ __attribute__((aligned(16))) L sm;
 
@@ -342,6 +349,8 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
             const int c = tid + i * GEMM_NW * WAVE;
             const int64_t r = min(r0 + c / GEMM_CH, m - 1);
             st.a[i] = ld16(xq + r * n_in + min(k0 + (c % GEMM_CH) * 16, bmax));
+            if constexpr (X2)
+                st.l[i] = ld16(xl + r * n_in + min(k0 + (c % GEMM_CH) * 16, bmax));
         }
         {
             const int64_t o = min(o0 + tid / GEMM_KB, n_out - 1);
@@ -364,6 +373,8 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
         for (int i = 0; i < S::AL; i++) {
             const int c = tid + i * GEMM_NW * WAVE;
             put_swizzled(&sm.a[c / GEMM_CH][0], c / GEMM_CH, c % GEMM_CH, st.a[i]);
+            if constexpr (X2)
+                put_swizzled(&sm.l[c / GEMM_CH][0], c / GEMM_CH, c % GEMM_CH, st.l[i]);
         }
         // a block past the row gets weight scale 0, so it adds exactly 0
         sm.ws[tid % GEMM_KB][tid / GEMM_KB] = p * GEMM_KB + tid % GEMM_KB < nb ? st.ws : 0.0f;
@@ -392,11 +403,20 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
 #pragma unroll
             for (int t = 0; t < MT; t++) {
                 const long af = *reinterpret_cast<const long *>(&sm.a[16 * t + j][off]);
-                const v4i isum = __builtin_amdgcn_mfma_i32_16x16x32_i8(af, bf, v4i{0, 0, 0, 0}, 0, 0, 0);
+                v4i isum = __builtin_amdgcn_mfma_i32_16x16x32_i8(af, bf, v4i{0, 0, 0, 0}, 0, 0, 0);
                 const f32x4 sx = *reinterpret_cast<const f32x4 *>(&sm.xs[b][16 * t + 4 * g]);
+                if constexpr (X2) {
+                    const long lf = *reinterpret_cast<const long *>(&sm.l[16 * t + j][off]);
+                    const v4i ilo = __builtin_amdgcn_mfma_i32_16x16x32_i8(lf, bf, v4i{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; i++)
-                    acc[t][i] = __builtin_fmaf((float)isum[i], sw * sx[i], acc[t][i]);
+                    for (int i = 0; i < 4; i++)
+                        acc[t][i] = __builtin_fmaf((float)(isum[i] * 128 + ilo[i]), (sw * sx[i]) * 0.0078125f,
+                                                   acc[t][i]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        acc[t][i] = __builtin_fmaf((float)isum[i], sw * sx[i], acc[t][i]);
+                }
             }
             // one block's fragments live at a time (hoisting every block's
             // LDS reads above the first MFMA costs registers the staging needs)
@@ -512,7 +532,7 @@ hipError_t launch_act(const GemvArgs &a, const SliceShape &sh, hipStream_t st)
 
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t st)
 {
-    if (a.act == 1 && a.m >= GEMM_MIN_ROWS) {
+    if (a.act >= 1 && a.m >= GEMM_MIN_ROWS) {
         // row tiles of 16 rows for m <= 16, else of 32 (64-row tiles would
         // spill registers; two 32-row tiles of the same weights run on one
         // XCD, blockIdx.y apart by a multiple of 8 workgroups when n_out is a
@@ -520,16 +540,17 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t st)
         const int mt = a.m <= 16 ? 1 : 2;
         const dim3 grid((unsigned)((a.n_out + GEMM_TN - 1) / GEMM_TN), (unsigned)((a.m + 16 * mt - 1) / (16 * mt)));
         const dim3 block(GEMM_NW * WAVE);
-        if (mt == 1)
-            hipLaunchKernelGGL(k_gemm_i8<1>, grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
-                               (int)a.m, a.y);
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
+                               (int)a.m, a.y, a.xl);
+        };
+        if (a.act == 2)
+            mt == 1 ? go(k_gemm_i8<1, true>) : go(k_gemm_i8<2, true>);
         else
-            hipLaunchKernelGGL(k_gemm_i8<2>, grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
-                               (int)a.m, a.y);
+            mt == 1 ? go(k_gemm_i8<1, false>) : go(k_gemm_i8<2, false>);
         return hipGetLastError();
     }
     const SliceShape sh = slice_shape(a.n_in);
-    // two words: the vector units at every m (two int8 dots a block)
     if (a.act == 2)
         return launch_act<2>(a, sh, st);
     return a.act == 0 ? launch_act<0>(a, sh, st) : launch_act<1>(a, sh, st);

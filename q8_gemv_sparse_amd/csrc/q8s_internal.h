@@ -107,10 +107,11 @@ hipError_t norm_logits_launch(const float *h, const float *r, const float *w, in
 size_t route_scratch_bytes(int64_t rows, int64_t E);
 hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
                         float *wts, void *scratch, hipStream_t st);
-// the router over Q8_0 rows: float32 x (act 0) or its Q8_0 form xq/xs (act 1)
+// the router over Q8_0 rows: float32 x (act 0), its Q8_0 form xq/xs (act 1),
+// or its two-word form xq/xl/xs (act 2)
 hipError_t route_q8_launch(const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq, const float *Wrs,
                            int64_t rows, int64_t d, int64_t E, int64_t k, int act, int32_t *idx, float *wts,
-                           void *scratch, hipStream_t st);
+                           void *scratch, hipStream_t st, const int8_t *xl = nullptr);
 
 struct MoeArgs {
     const float *x;
@@ -235,6 +236,8 @@ struct StackArgs {
 size_t stack_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
 hipError_t stack_launch(const StackArgs &s, hipStream_t st);
 bool block_fused(int64_t rows, int64_t d, int64_t dff, int64_t E, int act);
+// a chunk of rows in int8 numerics (one or two words) runs the grouped kernels
+bool block_chunk(int64_t rows, int64_t d, int64_t dff, int act);
 hipError_t block_launch(const BlockArgs &b, hipStream_t st);
 
 } // namespace q8s

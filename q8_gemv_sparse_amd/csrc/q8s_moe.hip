@@ -543,7 +543,7 @@ hipError_t dn_dispatch(const MoeArgs &a, int64_t n_in, hipStream_t st)
 
 hipError_t gate_up_launch(const MoeArgs &a, hipStream_t st)
 {
-    if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
+    if (a.act >= 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
         return chunk_gate_up_launch(a, st);
     return gu_dispatch<GU>(a, st);
 }
@@ -552,12 +552,12 @@ hipError_t route_gate_up_launch(const MoeArgs &a, hipStream_t st) { return gu_di
 
 size_t down_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t k, int act)
 {
-    return (act == 1 && rows > 1 && chunk_supported(d, dff)) ? chunk_down_scratch_bytes(rows, d, k) : 0;
+    return (act >= 1 && rows > 1 && chunk_supported(d, dff)) ? chunk_down_scratch_bytes(rows, d, k) : 0;
 }
 
 hipError_t down_launch(const MoeArgs &a, hipStream_t st)
 {
-    if (a.act == 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
+    if (a.act >= 1 && a.rows > 1 && chunk_supported(a.d, a.dff))
         return chunk_down_launch(a, st);
     return dn_dispatch(a, a.dff, st);
 }

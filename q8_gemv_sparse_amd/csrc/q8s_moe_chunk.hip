@@ -5,7 +5,7 @@
 // projection reading its weights once for the block (codegen_cuda/lane/mod.rs
 // module doc); a chunk's mixture groups its choices by expert and keeps each
 // choice's weighed result (arena.rs fn scratch: the grouped list, and `pa`,
-// per choice, combined per row).  Here, in one-word int8 numerics:
+// per choice, combined per row).  Here, in int8 numerics (one word):
 //
 //   k_chunk_gate_up  one workgroup per (expert e, tile of 16 hidden
 //                    outputs).  Wave 0 gathers, in choice order, the choices
@@ -23,6 +23,11 @@
 //                    a lane group per row and the rows' chunks split across
 //                    lanes.
 //   k_chunk_combine  y[r][o] = sum_j wts[r][j] * pa[r*K + j][o], slot order.
+//
+// In two-word numerics the same kernels stage the activation (or hidden)
+// rows' low words beside the words and join each block's two exact int32
+// sums as 128 * isum + isum_lo before one scale, as the two-word GEMV does;
+// the quantise pass writes the hidden rows in two words.
 //
 // With a handful of choices per expert the contraction is far from dense, so
 // these kernels stay on the vector units; the dense projection of a chunk goes
@@ -162,15 +167,29 @@ Q8S_DEV int block_dot(const i32x4 (&a)[2], const i32x4 (&b)[2])
     return s;
 }
 
+// The two-word form of a block dot: the block's two exact int32 sums (words,
+// low words) joined as 128 * isum + isum_lo (below 2^27 in magnitude).
+Q8S_DEV int block_dot2(const i32x4 (&w)[2], const i32x4 (&a)[2], const i32x4 (&l)[2])
+{
+    return block_dot(w, a) * 128 + block_dot(w, l);
+}
+
+// X2: two-word activations (the low words xl staged beside the words; a
+// block's sum is block_dot2, scaled by ws * xs / 128), CK_NA / 2 choices a
+// pass so the staged rows take the one-word kernel's LDS.
+template <bool X2>
 __global__ void __launch_bounds__(CKB_NW * WAVE)
     k_chunk_gate_up(const int8_t *__restrict__ xq, const float *__restrict__ xs, const int8_t *__restrict__ Wgq,
                     const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq, const float *__restrict__ Wus,
-                    const int32_t *__restrict__ idx, int nchoice, int k, int d, int dff, int E, float *__restrict__ h)
+                    const int32_t *__restrict__ idx, int nchoice, int k, int d, int dff, int E, float *__restrict__ h,
+                    const int8_t *__restrict__ xl)
 {
-    __shared__ int list[CK_NA];
+    constexpr int NA = X2 ? CK_NA / 2 : CK_NA;
+    __shared__ int list[NA];
     __shared__ int totsh;
-    __shared__ __align__(16) int8_t act[CK_NA][CKB_MAXD];
-    __shared__ float asc[CK_NA][CKB_MAXD / QB];
+    __shared__ __align__(16) int8_t act[NA][CKB_MAXD];
+    __shared__ __align__(16) int8_t actl[X2 ? NA : 1][X2 ? CKB_MAXD : 16];
+    __shared__ float asc[NA][CKB_MAXD / QB];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int e = blockIdx.y;
@@ -213,16 +232,16 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
         trade(gq[u]);
         trade(uq[u]);
     }
-    for (int first = 0;; first += CK_NA) {
+    for (int first = 0;; first += NA) {
         if (wid == 0) {
             IdxBatch ib;
             idx_load(ib, idx, nchoice, 0, E, lane);
-            const int tot = idx_gather<CK_NA>(ib, idx, nchoice, e, E, first, list, lane);
+            const int tot = idx_gather<NA>(ib, idx, nchoice, e, E, first, list, lane);
             if (lane == 0)
                 totsh = tot;
         }
         __syncthreads();
-        const int total = totsh, n = min(CK_NA, max(0, total - first));
+        const int total = totsh, n = min(NA, max(0, total - first));
         if (n == 0)
             break;
         // stage the n choices' activation rows: 16-byte chunk t of every row by
@@ -231,17 +250,21 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
         if ((int)threadIdx.x < nch) {
             const int t = threadIdx.x;
             for (int q0 = 0; q0 < n; q0 += 4) {
-                i32x4 v[4];
+                i32x4 v[4], vl[4];
                 float sc[4];
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     const int64_t r = list[min(q0 + q, n - 1)] / k;
                     v[q] = ld16(xq + r * d + t * 16);
+                    if constexpr (X2)
+                        vl[q] = ld16(xl + r * d + t * 16);
                     sc[q] = xs[r * nb + (t >> 1)];
                 }
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     *reinterpret_cast<i32x4 *>(&act[q0 + q][t * 16]) = v[q];
+                    if constexpr (X2)
+                        *reinterpret_cast<i32x4 *>(&actl[q0 + q][t * 16]) = vl[q];
                     if ((t & 1) == 0)
                         asc[q0 + q][t >> 1] = sc[q];
                 }
@@ -249,14 +272,20 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
         }
         __syncthreads();
         for (int cg = 0; cg < n; cg += 2) {
-            i32x4 a[2][2];
+            i32x4 a[2][2], al[2][2];
             float sx[2];
 #pragma unroll
             for (int q = 0; q < 2; q++) {
                 const int qq = min(cg + q, n - 1);
                 a[q][0] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * bl]);
                 a[q][1] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * bl + 16]);
+                if constexpr (X2) {
+                    al[q][0] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * bl]);
+                    al[q][1] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * bl + 16]);
+                }
                 sx[q] = inb ? asc[qq][bl] : 0.0f;
+                if constexpr (X2)
+                    sx[q] *= 0.0078125f;
             }
             // rows in pairs: 2 choices x 2 rows x gate/up = 8 values a reduction
 #pragma unroll
@@ -266,8 +295,13 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
                 for (int q = 0; q < 2; q++)
 #pragma unroll
                     for (int u = 0; u < 2; u++) {
-                        v[4 * q + 2 * u] = (float)block_dot(gq[u0 + u], a[q]) * (gs[u0 + u] * sx[q]);
-                        v[4 * q + 2 * u + 1] = (float)block_dot(uq[u0 + u], a[q]) * (us[u0 + u] * sx[q]);
+                        if constexpr (X2) {
+                            v[4 * q + 2 * u] = (float)block_dot2(gq[u0 + u], a[q], al[q]) * (gs[u0 + u] * sx[q]);
+                            v[4 * q + 2 * u + 1] = (float)block_dot2(uq[u0 + u], a[q], al[q]) * (us[u0 + u] * sx[q]);
+                        } else {
+                            v[4 * q + 2 * u] = (float)block_dot(gq[u0 + u], a[q]) * (gs[u0 + u] * sx[q]);
+                            v[4 * q + 2 * u + 1] = (float)block_dot(uq[u0 + u], a[q]) * (us[u0 + u] * sx[q]);
+                        }
                     }
                 const float r = wave_sum8(v, lane);
                 // lanes with bit 3 clear hold a gate sum; the up sum of the
@@ -278,7 +312,7 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
                     h[(int64_t)list[cg + q] * dff + o0 + CKB_U * wid + u0 + u] = e < E ? silu(r) * up : 0.0f;
             }
         }
-        if (total <= first + CK_NA)
+        if (total <= first + NA)
             break;
         __syncthreads();  // the next pass rewrites the list and the staged rows
     }
@@ -301,11 +335,11 @@ struct CkDownShape {
     static constexpr int CG = C >= 3 ? 1 : 2;
 };
 
-template <int LPR, int C>
+template <int LPR, int C, int ACT>
 __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
     k_chunk_down(const int8_t *__restrict__ hq, const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
                  const float *__restrict__ Wds, const int32_t *__restrict__ idx, int nchoice, int d, int dff, int E,
-                 float *__restrict__ pa)
+                 float *__restrict__ pa, const int8_t *__restrict__ hl)
 {
     using S = CkDownShape<LPR, C>;
     constexpr int G = S::G, SW = S::SW, R = S::R, CG = S::CG, NW = S::NW;
@@ -333,11 +367,14 @@ __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
         if (n == 0)
             break;
         for (int cg = 0; cg < n; cg += CG) {
-            XSlice<1, C> xv[CG];
+            XSlice<ACT, C> xv[CG];
 #pragma unroll
             for (int q = 0; q < CG; q++) {
                 const int64_t c = list[min(cg + q, n - 1)];
-                load_x_flat<LPR, C>(xv[q], hq + c * dff, hs + c * nb, 0, nch, lig);
+                if constexpr (ACT == 2)
+                    load_x2<LPR, C>(xv[q], hq + c * dff, hl + c * dff, hs + c * nb, 0, nch, lig);
+                else
+                    load_x_flat<LPR, C>(xv[q], hq + c * dff, hs + c * nb, 0, nch, lig);
             }
 #pragma unroll
             for (int q = 0; q < CG; q++)
@@ -366,17 +403,19 @@ constexpr int CKD_U = 2;                       // row slots a wave: 8 rows each
 constexpr int CKD_T = CKD_NW * CKD_U * 8;      // outputs a workgroup
 constexpr int CKD_MAXF = 1024;                 // longest hidden row
 
-template <int C>
+// X2: two-word hidden rows (their low words hl staged beside the words).
+template <int C, bool X2>
 __global__ void __launch_bounds__(CKD_NW * WAVE)
     k_chunk_down2(const int8_t *__restrict__ hq, const float *__restrict__ hs, const int8_t *__restrict__ Wdq,
                   const float *__restrict__ Wds, const int32_t *__restrict__ idx, int nchoice, int d, int dff, int E,
-                  float *__restrict__ pa)
+                  float *__restrict__ pa, const int8_t *__restrict__ hl)
 {
     static_assert(C % 2 == 0 && 8 * C * 16 <= CKD_MAXF * 2, "whole blocks a lane");
     constexpr int M = C / 2;  // whole blocks a lane
     __shared__ int list[CK_NA];
     __shared__ int totsh;
     __shared__ __align__(16) int8_t act[CK_NA][CKD_MAXF];
+    __shared__ __align__(16) int8_t actl[X2 ? CK_NA : 1][X2 ? CKD_MAXF : 16];
     __shared__ float asc[CK_NA][CKD_MAXF / QB];
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -439,17 +478,21 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
         if ((int)threadIdx.x < nch) {
             const int t = threadIdx.x;
             for (int q0 = 0; q0 < n; q0 += 4) {
-                i32x4 v[4];
+                i32x4 v[4], vl[4];
                 float sc[4];
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     const int64_t c = list[min(q0 + q, n - 1)];
                     v[q] = ld16(hq + c * dff + t * 16);
+                    if constexpr (X2)
+                        vl[q] = ld16(hl + c * dff + t * 16);
                     sc[q] = hs[c * nb + (t >> 1)];
                 }
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     *reinterpret_cast<i32x4 *>(&act[q0 + q][t * 16]) = v[q];
+                    if constexpr (X2)
+                        *reinterpret_cast<i32x4 *>(&actl[q0 + q][t * 16]) = vl[q];
                     if ((t & 1) == 0)
                         asc[q0 + q][t >> 1] = sc[q];
                 }
@@ -466,14 +509,22 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
                     v[q][u] = 0.0f;
 #pragma unroll
                 for (int m = 0; m < M; m++) {
-                    i32x4 a[2];
+                    i32x4 a[2], al[2];
                     a[0] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * blk[m]]);
                     a[1] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * blk[m] + 16]);
+                    if constexpr (X2) {
+                        al[0] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * blk[m]]);
+                        al[1] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * blk[m] + 16]);
+                    }
                     const float sx = inb[m] ? asc[qq][blk[m]] : 0.0f;
 #pragma unroll
                     for (int u = 0; u < CKD_U; u++) {
                         const i32x4 wb[2] = {w[u][2 * m], w[u][2 * m + 1]};
-                        v[q][u] = __builtin_fmaf((float)block_dot(wb, a), ws[u][m] * sx, v[q][u]);
+                        if constexpr (X2)
+                            v[q][u] = __builtin_fmaf((float)block_dot2(wb, a, al), (ws[u][m] * sx) * 0.0078125f,
+                                                     v[q][u]);
+                        else
+                            v[q][u] = __builtin_fmaf((float)block_dot(wb, a), ws[u][m] * sx, v[q][u]);
                     }
                 }
             }
@@ -531,13 +582,19 @@ namespace {
 hipError_t gu_chunk_go(const MoeArgs &a, hipStream_t st)
 {
     dim3 grid((unsigned)(a.dff / CKB_T), (unsigned)(a.E + 1));  // + one row for invalid choices
-    hipLaunchKernelGGL(k_chunk_gate_up, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq, a.Wus,
-                       a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h);
+    if (a.act == 2)
+        hipLaunchKernelGGL(k_chunk_gate_up<true>, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
+                           a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h, a.xl);
+    else
+        hipLaunchKernelGGL(k_chunk_gate_up<false>, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
+                           a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h, nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !a.hq)
         return err;
-    // the hidden rows' Q8_0 form, for the down projection (unless the caller
-    // forms it itself)
+    // the hidden rows' Q8_0 form (one or two words), for the down projection
+    // (unless the caller forms it itself)
+    if (a.act == 2)
+        return quantize_x2_launch(a.h, a.rows * a.k, a.dff, a.hq, a.hl, a.hs, st);
     return quantize_launch(a.h, a.rows * a.k, a.dff, a.hq, a.hs, st);
 }
 
@@ -545,8 +602,12 @@ template <int C>
 void dn2_go(const MoeArgs &a, float *pa, hipStream_t st)
 {
     dim3 grid((unsigned)((a.d + CKD_T - 1) / CKD_T), (unsigned)a.E);
-    hipLaunchKernelGGL((k_chunk_down2<C>), grid, dim3(CKD_NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds, a.idx,
-                       (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa);
+    if (a.act == 2)
+        hipLaunchKernelGGL((k_chunk_down2<C, true>), grid, dim3(CKD_NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds,
+                           a.idx, (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa, a.hl);
+    else
+        hipLaunchKernelGGL((k_chunk_down2<C, false>), grid, dim3(CKD_NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds,
+                           a.idx, (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa, nullptr);
 }
 
 template <int LPR, int C>
@@ -565,8 +626,12 @@ hipError_t dn_chunk_go(const MoeArgs &a, hipStream_t st)
         dn2_go<8>(a, pa, st);
     else {
         dim3 grid((unsigned)((a.d + S::TO - 1) / S::TO), (unsigned)a.E);
-        hipLaunchKernelGGL((k_chunk_down<LPR, C>), grid, dim3(S::NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds, a.idx,
-                           (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa);
+        if (a.act == 2)
+            hipLaunchKernelGGL((k_chunk_down<LPR, C, 2>), grid, dim3(S::NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds,
+                               a.idx, (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa, a.hl);
+        else
+            hipLaunchKernelGGL((k_chunk_down<LPR, C, 1>), grid, dim3(S::NW * WAVE), 0, st, a.hq, a.hs, a.Wdq, a.Wds,
+                               a.idx, (int)(a.rows * a.k), (int)a.d, (int)a.dff, (int)a.E, pa, nullptr);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)

@@ -168,11 +168,13 @@ __global__ void __launch_bounds__(RT_THREADS) k_logits_tile(const float *__restr
 //   ACT 0: l = sum_t (q*s) * x[t]                       in double
 //   ACT 1: l = sum_b (ws*xs) * isum_b, the block's exact int32 dot joined
 //          from the two lanes' halves, added by the even lane
+//   ACT 2: l = sum_b (ws*xs) * (isum_b + isum_lo_b / 128), the two-word
+//          activation's two exact dots a block (words xq, low words xl)
 template <int ACT, int RT>
 __global__ void __launch_bounds__(RT_THREADS)
     k_logits_q8(const float *__restrict__ x, const int8_t *__restrict__ xq, const float *__restrict__ xs,
                 const int8_t *__restrict__ Wrq, const float *__restrict__ Wrs, int rows, int d, int E,
-                double *__restrict__ logits)
+                double *__restrict__ logits, const int8_t *__restrict__ xl)
 {
     __shared__ double part[RT_WAVES][RT];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -204,11 +206,18 @@ __global__ void __launch_bounds__(RT_THREADS)
                         acc[r] += ((double)q * (double)s) * (double)b[i];
                     }
                 }
-            } else {
+            } else if (ACT == 1) {
                 int is = chunk_dot_i8(wv, ld16(xq + xr * d + c * 16));
                 is += dpp_i<DPP_XOR1>(is);
                 if ((lane & 1) == 0)
                     acc[r] += ((double)s * (double)xs[xr * nb + (c >> 1)]) * (double)is;
+            } else {
+                int is = chunk_dot_i8(wv, ld16(xq + xr * d + c * 16));
+                int il = chunk_dot_i8(wv, ld16(xl + xr * d + c * 16));
+                is += dpp_i<DPP_XOR1>(is);
+                il += dpp_i<DPP_XOR1>(il);
+                if ((lane & 1) == 0)
+                    acc[r] += ((double)s * (double)xs[xr * nb + (c >> 1)]) * ((double)is + (double)il / 128.0);
             }
         }
     }
@@ -342,23 +351,20 @@ hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d
 
 hipError_t route_q8_launch(const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq, const float *Wrs,
                            int64_t rows, int64_t d, int64_t E, int64_t k, int act, int32_t *idx, float *wts,
-                           void *scratch, hipStream_t st)
+                           void *scratch, hipStream_t st, const int8_t *xl)
 {
     double *logits = reinterpret_cast<double *>(scratch);
     const dim3 block(RT_THREADS);
     const dim3 g1((unsigned)E, (unsigned)rows), g4((unsigned)E, (unsigned)((rows + 3) / 4));
-    if (act == 0 && rows == 1)
-        hipLaunchKernelGGL((k_logits_q8<0, 1>), g1, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
-                           logits);
-    else if (act == 0)
-        hipLaunchKernelGGL((k_logits_q8<0, 4>), g4, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
-                           logits);
-    else if (rows == 1)
-        hipLaunchKernelGGL((k_logits_q8<1, 1>), g1, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
-                           logits);
+    auto go = [&](auto kernel, dim3 grid) {
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E, logits, xl);
+    };
+    if (act == 0)
+        rows == 1 ? go(k_logits_q8<0, 1>, g1) : go(k_logits_q8<0, 4>, g4);
+    else if (act == 1)
+        rows == 1 ? go(k_logits_q8<1, 1>, g1) : go(k_logits_q8<1, 4>, g4);
     else
-        hipLaunchKernelGGL((k_logits_q8<1, 4>), g4, block, 0, st, x, xq, xs, Wrq, Wrs, (int)rows, (int)d, (int)E,
-                           logits);
+        rows == 1 ? go(k_logits_q8<2, 1>, g1) : go(k_logits_q8<2, 4>, g4);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

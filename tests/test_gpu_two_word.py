@@ -40,7 +40,9 @@ def test_quantize_rows_x2_bit_exact(rows, n):
 # (n_out, n_in, m): batch 1 at the 512x256 and 4096x2048 shapes, rows cut into
 # slices (n_in > 2048), several rows, ragged n_out, the longest row, the least
 GEMV_CASES = [(512, 256, 1), (4096, 2048, 1), (96, 4096, 3), (50, 9216, 1), (33, 96, 5), (8, 65536, 1),
-              (1, 32, 1), (70, 768, 4), (130, 2048, 9)]
+              (1, 32, 1), (70, 768, 4), (130, 2048, 9),
+              # five rows and more: the matrix-core GEMM, two MFMAs a block
+              (4096, 2048, 16), (4096, 2048, 64), (100, 2080, 20), (16, 65536, 5), (4096, 2048, 33)]
 
 
 @pytest.mark.parametrize("n_out,n_in,m", GEMV_CASES)
@@ -55,11 +57,13 @@ def test_gemv_x2(n_out, n_in, m):
     assert rel_err(host(y), ref) <= TOL
 
 
-def test_gemv_x2_exact_special_case():
+@pytest.mark.parametrize("m", [2, 20])
+def test_gemv_x2_exact_special_case(m):
     # small integers and power-of-two scales: every float step exact, so the
-    # GPU equals the oracle bit for bit (pins the two block dots and the 1/128)
-    banner("q8_gemv_x2 exact special case")
-    n_out, n_in, m = 40, 256, 2
+    # GPU equals the oracle bit for bit (pins the two block dots and the 1/128,
+    # on the vector units at 2 rows and on the matrix cores at 20)
+    banner("q8_gemv_x2 exact special case m=%d" % m)
+    n_out, n_in = 40, 256
     Wq = synthetic.fill_pattern(n_out * n_in).reshape(n_out, n_in).astype(np.int8)
     xq = synthetic.fill_pattern(m * n_in + 3)[3:].reshape(m, n_in).astype(np.int8)
     xl = synthetic.fill_pattern(m * n_in + 5)[5:].reshape(m, n_in).astype(np.int8)
@@ -135,7 +139,10 @@ BLOCK_X2_CASES = [
     (256, 64, 5, 5, 1),         # K = E
     (64, 64, 1, 1, 1),          # one expert
     (512, 96, 256, 32, 1),      # the most experts ranked in the gate-up, the most kept
-    (256, 96, 6, 2, 3),         # several rows (no grouped chunk kernels in two words)
+    (256, 96, 6, 2, 3),         # several rows: the grouped chunk kernels in two words
+    (2048, 768, 128, 8, 64),    # the 64-row chunk of the 128-expert block, each expert read once
+    (1024, 2048, 16, 4, 8),     # hidden rows of 2048: the chunk down projection a lane group a row
+    (96, 160, 5, 3, 4),         # ragged rows in the chunk kernels
 ]
 
 
@@ -246,3 +253,35 @@ def test_block_x2_scratch_needs_no_initial_contents_and_repeats():
     fresh = q8.moe_ffn_block(h, r, w, 1e-6, *W, m.k, act=q8.ACT_X2)
     for a, c in zip(first, fresh):
         assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("rows", [1, 64])
+def test_x2_stage_calls_equal_block(rows):
+    # add_rmsnorm_q8 -> q8_quantize_rows_x2 -> moe_route_topk -> moe_gate_up_x2
+    # -> moe_down_combine_x2 compute what moe_ffn_block(act 2) computes: bit
+    # for bit for a chunk (the block runs these very kernels), and for one row
+    # within float rounding of the routing weights (the block's fused launches
+    # form the logits in another order)
+    banner("x2 stage calls vs block rows=%d" % rows)
+    import torch
+    b = synthetic.block_inputs(31, 2048, 768, 128, 8, rows)
+    m = b.moe
+    W = [dev(a) for a in (m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds)]
+    Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds = W
+    s, x, _, _ = q8.add_rmsnorm_q8(dev(b.h), dev(b.r), dev(b.w), 1e-6, want_q8=False)
+    xq, xl, xs = q8.q8_quantize_rows_x2(x)
+    idx, wts = q8.moe_route_topk(x, Wr, 8)
+    _, hq, hl, hs = q8.moe_gate_up_x2(Wgq, Wgs, Wuq, Wus, idx, 128, xq, xl, xs)
+    y = q8.moe_down_combine_x2(Wdq, Wds, idx, wts, 128, hq, hl, hs)
+    bs, bidx, bw, bout = q8.moe_ffn_block(dev(b.h), dev(b.r), dev(b.w), 1e-6, *W, 8, act=2)
+    assert torch.equal(bs, s) and torch.equal(bidx, idx)
+    if rows > 1:
+        assert torch.equal(bw, wts) and torch.equal(bout, y)
+    else:
+        assert rel_err(host(bw), host(wts)) <= 1e-6 and rel_err(host(bout), host(y)) <= 1e-6
+    rs, y64 = oracle.add_rmsnorm(b.h, b.r, b.w, 1e-6)
+    ridx, _, _, ry = oracle.moe(y64.astype(np.float32), m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, 8, 2)
+    assert np.array_equal(host(idx), ridx)
+    got = host(y)
+    for r in range(rows):
+        assert rel_err(got[r], ry[r]) <= TOL_X2_BLOCK, r
