@@ -44,8 +44,9 @@
  *   - `act` picks the activation numerics (enum Q8MatKind): Q8S_ACT_F32 reads
  *     f32 activations; Q8S_ACT_INT8 reads one-word Q8_0 activations and forms
  *     exact int32 dots per 32-value block.  The two-word activation (act 2)
- *     has entry points of its own, q8_quantize_rows_x2 and q8_gemv_x2; every
- *     other call refuses act 2.
+ *     has entry points of its own (the *_x2 calls) and is taken by the
+ *     whole-block calls (moe_ffn_block, moe_ffn_block_ex, moe_ffn_stack,
+ *     moe_ffn_block_noalloc); every other call refuses act 2.
  *   - Expert choices (idx) are read on the device.  An index outside [0, E)
  *     is never dereferenced: that choice contributes zero.
  */
@@ -138,8 +139,10 @@ Q8S_API int q8_quantize_rows_x2(const float *x, int64_t rows, int64_t n, int8_t 
  * dots a block, one against the words and one against the low words,
  *   y[r][o] = sum_b Ws[o][b] * xs[r][b] * (isum_hi[b] + isum_lo[b] / 128)
  * Wq/Ws as q8_gemv; xq/xl/xs as q8_quantize_rows_x2 writes them, m rows;
- * y: device f32 [m, n_out].  Every m runs on the vector units.  Limits as
- * q8_gemv.
+ * y: device f32 [m, n_out].  Below five rows the vector units form the two
+ * dots; from five rows on, the matrix cores (v_mfma_i32_16x16x32_i8 twice a
+ * block, words and low words against the same weight fragment), each exact
+ * int32.  Limits as q8_gemv.
  */
 Q8S_API int q8_gemv_x2(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in, const int8_t *xq,
                        const int8_t *xl, const float *xs, int64_t m, float *y, void *stream);
@@ -342,11 +345,14 @@ Q8S_API int moe_topk_gate_up(const double *logits, const float *x, const int8_t 
  * act = 2 runs the block in two-word numerics (fn moe_dp4a_kernels'
  * two-pass, logit-exact trio): x and each hidden block in two words (as
  * q8_quantize_rows_x2), two exact int32 dots a block (as q8_gemv_x2), the
- * router still reading f32 x; it takes the three-launch form only (E <= 256,
- * d <= 8192; any rows, each row's weights read for that row), else
- * Q8S_EUNSUPPORTED.  moe_ffn_block_ex takes act 2 the same way, its Q8_0
- * router reading the row's two words (two exact dots a block) and its shared
- * expert in two words.  The other mixture calls refuse act 2.
+ * router still reading f32 x.  A chunk of rows (rows > 1, d <= 2048,
+ * dff <= 4096) runs the grouped kernels in two words, each chosen expert's
+ * weights read once (as moe_gate_up_x2 then moe_down_combine_x2); other
+ * rows take the three-launch form (E <= 256, d <= 8192, each row's weights
+ * read for that row); anything else is Q8S_EUNSUPPORTED.  moe_ffn_block_ex
+ * takes act 2 the same way, its Q8_0 router reading the row's two words (two
+ * exact dots a block) and its shared expert in two words.  The other mixture
+ * calls refuse act 2.
  */
 Q8S_API int moe_ffn_block(const float *h, const float *r, const float *w, float eps, const float *Wr,
                   const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,

@@ -420,3 +420,28 @@ def test_stack_refusals_before_any_hip_call():
     assert call(sb=64) == -4 and "scratch" in _err()
     assert call(scratch=0x7100000010) == -3 and "256-byte" in _err()
     assert call(out=0x1000000 * 2) == -1 and "overlaps input `Wr[0]`" in _err()
+
+
+def test_two_word_stage_refusals_before_any_hip_call():
+    P = ctypes.c_void_p
+    gu = LIB.moe_gate_up_x2
+    gu.argtypes = [P] * 8 + [ctypes.c_int64] * 5 + [P] * 5
+    dn = LIB.moe_down_combine_x2
+    dn.argtypes = [P] * 7 + [ctypes.c_int64] * 5 + [P, P, ctypes.c_size_t, P]
+    base = [0x1000000 * (i + 1) for i in range(8)]  # xq, xl, xs, Wgq, Wgs, Wuq, Wus, idx
+
+    def g(rows=1, d=256, dff=96, E=8, k=2, h=None, hq=0x20000000, hl=0x21000000, hs=0x22000000):
+        return gu(*base, rows, d, dff, E, k, h, hq, hl, hs, None)
+    assert g(rows=4) == -1 and "`h` is required" in _err()
+    assert g(hq=None, hl=None, hs=None) == -1 and "hq`/`hl`/`hs` are required" in _err()
+    assert g(d=40) == -1 and "multiple of 32" in _err()
+    assert g(hl=None) == -1 and "`hl` is null" in _err()
+    need = q8.q8s_scratch_bytes(q8.FN_DOWN, 4, 256, 96, 8, 2, q8.ACT_X2)
+    assert need >= 4 * 2 * 256 * 4  # the per-choice results of a chunk
+
+    def dcall(rows=4, sb=None, scratch=0x30000000):
+        return dn(*[0x1000000 * (i + 1) for i in range(7)], rows, 256, 96, 8, 2, 0x40000000, scratch,
+                  need if sb is None else sb, None)
+    assert dcall(sb=64) == -4 and "per-choice" in _err()
+    assert dcall(scratch=0x30000010) == -3
+    assert dcall(rows=0) == -1
