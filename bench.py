@@ -71,6 +71,18 @@ DOMINANT = {
 }
 
 
+def chunk_kernels(cfg, act):
+    """The grouped gate-up and down kernels a chunk workload runs (the
+    library's own rule: q8s_moe_path)."""
+    import q8_gemv_sparse_amd as q8
+    path = q8.q8s_moe_path(cfg["rows"], cfg["d"], cfg["dff"], cfg["E"], cfg["k"], ACT_CODE[act])
+    if path == q8.PATH_GROUPED_MFMA:
+        return "k_grouped_mfma", "k_grouped_mfma"
+    if path != q8.PATH_GROUPED:
+        raise SystemExit("workload %s does not run the grouped chunk kernels" % cfg)
+    return "k_chunk_gate_up", ("k_chunk_down2" if cfg["dff"] <= 1024 else "k_chunk_down")
+
+
 def counters_path(kernel, workload, act):
     return os.path.join(ROOT, "profiles", "%s_%s_%s_counters.txt" % (kernel, workload, act))
 
@@ -84,8 +96,10 @@ def summarize_counters(args):
     import csv
     import re
     import synthetic
-    kind = synthetic.CONFIGS[args.workload]["kind"]
-    kernel, srcs = DOMINANT[kind]
+    cfg = synthetic.CONFIGS[args.workload]
+    kernel, srcs = DOMINANT[cfg["kind"]]
+    if cfg["kind"] == "chunk":
+        kernel = chunk_kernels(cfg, args.act)[0]
     calib = args.calib_copy_mib * 1024  # KiB moved each way by the copy
     run = ("python3 bench.py --workload %s --act %s --no-graph --steps 28 --warmup 14 --kernel-launches 14 "
            "--spread 0 --suite none --no-cpu --no-ceiling --calib-copy-mib %d"
@@ -634,9 +648,10 @@ class Gemv(Workload):
 
 
 class ChunkBlock(MoeBlock):
-    """A 64-row prefill chunk through the MoE block (choices grouped by expert,
-    int8 activations), then the dense Q8_0 projection of the same rows'
-    Q8_0 form on the matrix cores."""
+    """A prefill chunk (64, 128 or 256 rows) through the MoE block (choices
+    grouped by expert, int8 activations: the vector-unit grouped kernels at 4
+    choices an expert, the matrix-core ones from 8), then the dense Q8_0
+    projection of the same rows' Q8_0 form on the matrix cores."""
 
     dominant = "k_chunk_gate_up"
     dominant_src = ("q8_gemv_sparse_amd/csrc/q8s_moe_chunk.hip", "q8_gemv_sparse_amd/csrc/q8s_device.h")
@@ -648,8 +663,9 @@ class ChunkBlock(MoeBlock):
         if act == "f32":
             raise SystemExit("workload %s runs in int8 numerics (one or two words)" % name)
         super().__init__(name, cfg, act, copies, rows=cfg["rows"], pool=8, separate=True)
-        self.dominant = "k_chunk_gate_up"
-        self.dominant_timed = "moe_gate_up without the hidden rows' Q8_0 pass: k_chunk_gate_up alone"
+        self.gu_kernel, self.dn_kernel = chunk_kernels(cfg, act)
+        self.dominant = self.gu_kernel
+        self.dominant_timed = "moe_gate_up without the hidden rows' Q8_0 pass: %s alone" % self.gu_kernel
         import synthetic
         np, torch = self.np, self.torch
         rng = np.random.default_rng(2)
@@ -737,14 +753,17 @@ class ChunkBlock(MoeBlock):
 
         x2 = self.act == "x2"
         sfx = "_x2" if x2 else ""
-        return [("add_rmsnorm_q8%s (k_add_rmsnorm_q8%s, 64 rows)" % (" + q8_quantize_rows_x2" if x2 else "",
-                                                                    " + k_quantize_rows_x2" if x2 else ""),
+        rows, n_dense = self.rows, self.dense_out.shape[1]
+        return [("add_rmsnorm_q8%s (k_add_rmsnorm_q8%s, %d rows)" % (" + q8_quantize_rows_x2" if x2 else "",
+                                                                    " + k_quantize_rows_x2" if x2 else "", rows),
                  self._norm, 0),
                 ("moe_route_topk (k_logits_tile + k_topk)", route, E * d * 4),
-                ("moe_gate_up%s (k_chunk_gate_up + k_quantize_rows%s)" % (sfx, sfx),
+                ("moe_gate_up%s (%s + k_quantize_rows%s)" % (sfx, self.gu_kernel, sfx),
                  lambda c: self._gate_up(c, None), int(avg_u * 2 * q8b(dff, d))),
-                ("moe_down_combine%s (k_chunk_down2 + k_chunk_combine)" % sfx, self._down, int(avg_u * q8b(d, dff))),
-                ("q8_gemv%s dense 64 x 2048 -> 4096 (k_gemm_i8)" % sfx, self._dense, self.dense_bytes)]
+                ("moe_down_combine%s (%s + k_chunk_combine)" % (sfx, self.dn_kernel), self._down,
+                 int(avg_u * q8b(d, dff))),
+                ("q8_gemv%s dense %d x %d -> %d (k_gemm_i8)" % (sfx, rows, d, n_dense), self._dense,
+                 self.dense_bytes)]
 
     def verify(self):
         import oracle
@@ -1337,6 +1356,9 @@ SUITE = [
     ("moe_d4096_dff14336_e8_k2", "x2"),
     ("chunk64_moe_d2048_dense4096", "int8"),
     ("chunk64_moe_d2048_dense4096", "x2"),
+    ("chunk128_moe_d2048_dense4096", "int8"),
+    ("chunk128_moe_d2048_dense4096", "x2"),
+    ("chunk256_moe_d2048_dense4096", "int8"),
     ("moe_shared_d2048_dff1408_e60_k4_s5632", "int8"),
     ("moe_shared_d2048_dff1408_e60_k4_s5632", "f32"),
     ("stack4_moe_d2048_dff768_e128_k8", "int8"),

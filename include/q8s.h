@@ -543,6 +543,31 @@ Q8S_API size_t q8s_block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int
  */
 Q8S_API size_t q8s_scratch_bytes(int fn, int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
 
+/*
+ * q8s_moe_path -- which kernels the mixture's expert stages run for these
+ * sizes (lane/mod.rs module doc: decode rows one by one, prefill chunks
+ * grouped by expert; lane_link.rs fn class_launch: a chunk's mixture over its
+ * rows sorted by expert).  It covers moe_gate_up, moe_down_combine (and their
+ * _x2 forms), moe_ffn_block and moe_ffn_stack, whose routed stages follow
+ * the same rule:
+ *   Q8S_PATH_ROWS          the decode kernels, row by row (one row, float32
+ *                          activations, or rows past the grouped kernels'
+ *                          limits: d > 2048 or dff > 4096);
+ *   Q8S_PATH_GROUPED       choices grouped by expert, each expert's weights
+ *                          read once a chunk, on the vector units (v_dot4);
+ *   Q8S_PATH_GROUPED_MFMA  the same grouping on the matrix cores, from 8
+ *                          choices an expert on average (rows*k >= 8*E), with
+ *                          d and dff multiples of 256 and 16 staged rows of
+ *                          max(d, dff) values (two words: twice the bytes)
+ *                          within 64 KiB.
+ * Host logic only (no device call).  Returns Q8S_EINVAL for non-positive
+ * sizes, k > E or an unknown act.
+ */
+#define Q8S_PATH_ROWS 0
+#define Q8S_PATH_GROUPED 1
+#define Q8S_PATH_GROUPED_MFMA 2
+Q8S_API int q8s_moe_path(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
+
 /* The message of this thread's last refused or failed call ("" if none). */
 Q8S_API const char *q8s_last_error(void);
 

@@ -26,7 +26,8 @@ __all__ = [
     "q8s_scratch_bytes", "q8s_block_scratch_bytes", "q8s_last_error",
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
     "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2", "moe_ffn_block_noalloc", "NOALLOC_SCRATCH_BYTES",
-    "moe_ffn_stack", "FN_STACK", "moe_gate_up_x2", "moe_down_combine_x2",
+    "moe_ffn_stack", "FN_STACK", "moe_gate_up_x2", "moe_down_combine_x2", "q8s_moe_path", "PATH_ROWS",
+    "PATH_GROUPED", "PATH_GROUPED_MFMA",
 ]
 
 ACT_F32 = 0
@@ -36,6 +37,9 @@ FN_ROUTE = 1
 FN_DOWN = 2
 FN_BLOCK = 3
 FN_STACK = 4
+PATH_ROWS = 0          # q8s_moe_path: the decode kernels, row by row
+PATH_GROUPED = 1       # choices grouped by expert, on the vector units
+PATH_GROUPED_MFMA = 2  # choices grouped by expert, on the matrix cores
 STREAM_WGS = 2048  # Q8S_STREAM_WGS: words q8s_stream_read writes
 NOALLOC_SCRATCH_BYTES = 32 << 20  # Q8S_NOALLOC_SCRATCH_BYTES: moe_ffn_block_noalloc's static scratch per GPU
 
@@ -77,6 +81,7 @@ _SIGS = {
     "moe_down_combine_ex": [_p] * 7 + [_i64, _p, _p] + [_i64] * 5 + [_p, ctypes.c_int, _p],
     "q8s_scratch_bytes": [ctypes.c_int, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
     "q8s_block_scratch_bytes": [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int],
+    "q8s_moe_path": [_i64, _i64, _i64, _i64, _i64, ctypes.c_int],
     "q8s_stream_read": [_p, _i64, _p, _p],
     "q8_quantize_rows_x2": [_p, _i64, _i64, _p, _p, _p, _p],
     "q8_gemv_x2": [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p, _p],
@@ -120,6 +125,15 @@ def q8s_scratch_bytes(fn, rows, d, dff, E, k, act=ACT_F32):
 
 def q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act=ACT_F32):
     return int(_lib.q8s_block_scratch_bytes(rows, d, dff, sdff, E, k, act))
+
+
+def q8s_moe_path(rows, d, dff, E, k, act=ACT_INT8):
+    """Which kernels the mixture's expert stages run for these sizes:
+    PATH_ROWS, PATH_GROUPED or PATH_GROUPED_MFMA (host logic, no device call)."""
+    rc = int(_lib.q8s_moe_path(rows, d, dff, E, k, act))
+    if rc < 0:
+        raise Q8sError(rc, "q8s_moe_path: invalid sizes")
+    return rc
 
 
 def q8s_stream_read(buf, out=None, nbytes=None, stream=None):

@@ -185,6 +185,15 @@ size_t q8s_block_scratch_bytes(int64_t rows, int64_t d, int64_t dff, int64_t sdf
     return q8s::block_scratch_bytes(rows, d, dff, sdff, E, k, act);
 }
 
+int q8s_moe_path(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
+{
+    if (rows <= 0 || d <= 0 || dff <= 0 || E <= 0 || k <= 0 || k > E || act < 0 || act > 2)
+        return Q8S_EINVAL;
+    if (act == 0 || rows == 1 || !q8s::chunk_supported(d, dff))
+        return Q8S_PATH_ROWS;
+    return q8s::chunk_wide_sizes(rows, d, dff, E, k, act) ? Q8S_PATH_GROUPED_MFMA : Q8S_PATH_GROUPED;
+}
+
 int q8_gemv(const int8_t *Wq, const float *Ws, int64_t n_out, int64_t n_in, const float *x, const int8_t *xq,
             const float *xs, int64_t m, float *y, int act, void *stream)
 {

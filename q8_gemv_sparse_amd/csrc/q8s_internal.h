@@ -170,6 +170,9 @@ hipError_t row_down_launch(const MoeArgs &a, hipStream_t st);
 // a chunk's mixture (rows > 1, int8 activations): choices grouped by expert,
 // for d <= 2048 and dff <= 4096 (one slice of a wave each)
 bool chunk_supported(int64_t d, int64_t dff);
+// whether such a chunk's grouped gate-up and down run on the matrix cores
+// (k_grouped_mfma) rather than the vector units
+bool chunk_wide_sizes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act);
 hipError_t chunk_gate_up_launch(const MoeArgs &a, hipStream_t st);
 size_t chunk_down_scratch_bytes(int64_t rows, int64_t d, int64_t k);
 hipError_t chunk_down_launch(const MoeArgs &a, hipStream_t st);

@@ -570,6 +570,286 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
     y[r * d + o] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// Wide chunks on the matrix cores
+//
+// With many choices an expert (a chunk of 128 rows and more: 8 and more
+// choices an expert at 128 experts, top 8), each weight row meets enough
+// activation rows for the contraction to be dense, and the vector-unit
+// kernels above become bound by their per-choice v_dot4 work.
+// k_grouped_mfma is the grouped contraction on the matrix cores
+// (v_mfma_i32_16x16x32_i8, whose k of 32 is one Q8_0 block, so each MFMA
+// gives exact int32 block sums).  It stays bound by the weight stream, so the
+// layout is the stream's:
+//   * one workgroup of GW_NW waves per (expert e, tile of outputs); each wave
+//     owns two 16-row weight streams over the whole reduced dimension, so no
+//     partial sums cross waves;
+//   * B operand: the wave's weight rows read from memory straight into
+//     registers, 16 bytes a lane (lane (j, g) takes bytes 16g .. 16g+15 of
+//     a 64-byte span of row j: half of block 2p or 2p+1), GW_BU blocks ahead
+//     of their use, the rows' scales 16 bytes a load; lanes 32 apart then
+//     trade halves so each holds 8 bytes of one block, the MFMA's fragment.
+//     The first fetch is issued before the choice list is scanned;
+//   * A operand: the rows of up to TM of the expert's choices (gathered in
+//     choice order), staged in LDS once per choice tile with their scales
+//     (only the row tiles in use, several loads a thread in flight); each
+//     row's 16-byte chunks sit XORed with the row index (mod 16), so a
+//     wave's fragment reads (8 bytes of 16 rows at one k) fall on distinct
+//     banks, at the same k-slots the B fragment holds;
+//   * the block sums are scaled by ws * xs and summed block by block in
+//     float32.
+//   PAIR (the gate-up): a wave streams the gate and the up rows of its 16
+//        hidden outputs side by side, so each lane ends holding g and u of
+//        the same (choice, output) and writes SiLU(g) * u (lane_link.rs fn
+//        class_launch: a gated pair fused with what consumes it); a tile is
+//        16 * GW_NW hidden outputs.  A rows are the choices' token rows
+//        (choice c reads row c / a_div, a_div = K); the grid row past the last
+//        expert writes zero hidden rows for the choices whose expert index is
+//        invalid.
+//   otherwise (the down projection): a wave streams output rows o and
+//        o + 16 * GW_NW, a tile is 32 * GW_NW outputs; A rows are the
+//        choices' hidden rows (a_div = 1), and the result goes to pa[c][o]
+//        for the per-row combine.
+//   X2: two-word activations: the low words staged beside the words and a
+//        second MFMA a block against the same weight fragment, the two exact
+//        sums joined as 128 * isum + isum_lo.
+// The grids (hidden or output tiles x experts) are whole multiples of what
+// the chip holds at once at the shapes this path takes (1536 gate-up and 2048
+// down workgroups at d 2048, dff 768, 128 experts, two a CU), so no split of
+// the reduced dimension is needed to fill the chip's last wave of
+// workgroups.  Rows K must be a
+// multiple of 256 bytes (the XOR stays inside aligned groups of 16 chunks),
+// and TM * K * (X2 ? 2 : 1) <= GW_ABYTES.
+constexpr int GW_NW = 4;              // waves a workgroup
+constexpr int GW_ABYTES = 65536;      // most LDS for the staged A rows
+constexpr int GW_BU = 8;              // blocks of B in flight a wave
+constexpr int GW_SB = 8;              // staging loads in flight a thread
+
+template <int TM, bool PAIR, bool X2>
+__global__ void __launch_bounds__(GW_NW * WAVE)
+    k_grouped_mfma(const int8_t *__restrict__ aq, const int8_t *__restrict__ al, const float *__restrict__ as,
+                   int a_div, const int8_t *__restrict__ Wq0, const float *__restrict__ Ws0,
+                   const int8_t *__restrict__ Wq1, const float *__restrict__ Ws1, const int32_t *__restrict__ idx,
+                   int nchoice, int K, int R, int E, float *__restrict__ out, int out_ld)
+{
+    static_assert(TM % 16 == 0, "whole MFMA row tiles");
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    constexpr int TT = TM / 16;          // row tiles
+    constexpr int NB = 2;                // weight rows a lane streams
+    constexpr int OT = PAIR ? 16 * GW_NW : 32 * GW_NW;  // outputs a workgroup
+    constexpr int NF = GW_BU / 2;        // loads a stream a fetch (two blocks a load)
+    constexpr int SB = X2 ? GW_SB / 4 : GW_SB;       // staging loads a thread in flight (a word each)
+    // LDS (gw_lds_bytes): the staged A rows [TM][K] (and their low words),
+    // their scales [K/32][TM], the tile's choice list [TM] and its count
+    extern __shared__ __attribute__((aligned(16))) int8_t gw_lds[];
+    const int nb = K >> 5, nch = K >> 4;
+    int8_t *abuf = gw_lds;
+    int8_t *abl = abuf + TM * K;  // the low words (X2)
+    float *xsb = reinterpret_cast<float *>(gw_lds + TM * K * (X2 ? 2 : 1));
+    int *list = reinterpret_cast<int *>(xsb + TM * nb);
+    int &totsh = list[TM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int j = lane & 15, g = lane >> 4;
+    const int e = blockIdx.y;
+    const int o0 = blockIdx.x * OT;
+
+    // the wave's weight row j (and up row j) of expert e
+    const int64_t wrow = (int64_t)e * R + o0 + 16 * wid + j;
+    const int lofs = 16 * g;
+    const int8_t *bq0 = Wq0 + wrow * K + lofs;
+    const float *bs0 = Ws0 + wrow * nb;
+    // the second stream: the up row (PAIR), else the row 16 * GW_NW further
+    const int8_t *bq1 = PAIR ? Wq1 + wrow * K + lofs : bq0 + (int64_t)(16 * GW_NW) * K;
+    const float *bs1 = PAIR ? Ws1 + wrow * nb : bs0 + (int64_t)(16 * GW_NW) * nb;
+    // the k-slots lane group g supplies within a block (the A fragment reads
+    // the same bytes the B fragment holds)
+    const int chx = g & 1, cho = 8 * (g >> 1);
+    // B fragments of GW_BU blocks, double buffered
+    i32x4 bf[2][NB][NF];
+    float bsc[2][NB][GW_BU];
+    auto fetch = [&](int s, int b0) {
+#pragma unroll
+        for (int u = 0; u < NF; u++) {
+            const int b = b0 + 2 * u;
+            bf[s][0][u] = ld16(bq0 + 32 * b);
+            bf[s][1][u] = ld16(bq1 + 32 * b);
+        }
+        // the rows' scales of the GW_BU blocks, 16 bytes a load (the
+        // lanes of a row load the same ones)
+#pragma unroll
+        for (int u = 0; u < GW_BU; u += 4) {
+            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(bs0 + b0 + u);
+            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(bs1 + b0 + u);
+            for (int i = 0; i < 4; i++) {
+                bsc[s][0][u + i] = v0[i];
+                bsc[s][1][u + i] = v1[i];
+            }
+        }
+    };
+    // the weight fragment of block b0 + u, stream q
+    auto frag = [&](int s, int q, int u) -> long {
+        // lane (j, g) loaded bytes 16g .. 16g+15 of blocks 2p, 2p+1 of row j
+        // (p = u / 2): lane groups 0, 1 hold halves of block 2p, groups 2, 3
+        // of block 2p+1.  Lanes 32 apart trade 8-byte halves, so each lane
+        // ends holding 8 bytes of either block: group g has bytes
+        // 16 (g & 1) + 8 (g >> 1) .. +7 of the block.
+        const i32x4 v = bf[s][q][u >> 1];
+        const bool low = g < 2;
+        const int r0 = __shfl_xor(low ? v[2] : v[0], 32), r1 = __shfl_xor(low ? v[3] : v[1], 32);
+        const bool mine = (u & 1) == (low ? 0 : 1);
+        const int w0 = mine ? ((u & 1) ? v[2] : v[0]) : r0, w1 = mine ? ((u & 1) ? v[3] : v[1]) : r1;
+        return (long)(uint32_t)w0 | ((long)w1 << 32);
+    };
+    // the first blocks' fetch does not wait for the choice list
+    if (e < E)
+        fetch(0, 0);
+
+    for (int first = 0;; first += TM) {
+        if (wid == 0) {
+            IdxBatch ib;
+            idx_load(ib, idx, nchoice, 0, E, lane);
+            const int tot = idx_gather<TM>(ib, idx, nchoice, e, E, first, list, lane);
+            if (lane == 0)
+                totsh = tot;
+        }
+        __syncthreads();
+        const int total = totsh, n = min(TM, max(0, total - first));
+        if (n == 0)
+            break;
+        if (e >= E) {
+            // the choices with an invalid expert: zero outputs
+            for (int t = tid; t < n * OT; t += GW_NW * WAVE)
+                out[(int64_t)list[t / OT] * out_ld + o0 + t % OT] = 0.0f;
+        } else {
+            if (first > 0)
+                fetch(0, 0);
+            // stage the A rows of the tiles in use (rows past n repeat the
+            // last one; their results are never written) and their scales,
+            // block-major; SB loads a thread in flight before their LDS
+            // writes
+            const int nr = (n + 15) & ~15;
+            for (int c0 = tid; c0 < nr * nch; c0 += SB * GW_NW * WAVE) {
+                i32x4 v[SB], vl[X2 ? SB : 1];
+#pragma unroll
+                for (int i = 0; i < SB; i++) {
+                    const int c = c0 + i * GW_NW * WAVE, r = c / nch;
+                    if (c < nr * nch) {
+                        const int64_t src = (int64_t)(list[min(r, n - 1)] / a_div) * K + 16 * (c % nch);
+                        v[i] = ld16(aq + src);
+                        if constexpr (X2)
+                            vl[i] = ld16(al + src);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < SB; i++) {
+                    const int c = c0 + i * GW_NW * WAVE, r = c / nch;
+                    if (c < nr * nch) {
+                        const int dst = r * K + 16 * ((c % nch) ^ (r & 15));
+                        *reinterpret_cast<i32x4 *>(abuf + dst) = v[i];
+                        if constexpr (X2)
+                            *reinterpret_cast<i32x4 *>(abl + dst) = vl[i];
+                    }
+                }
+            }
+            for (int c0 = tid; c0 < nr * nb; c0 += SB * GW_NW * WAVE) {
+                float v[SB];
+#pragma unroll
+                for (int i = 0; i < SB; i++) {
+                    const int c = c0 + i * GW_NW * WAVE, r = c / nb;
+                    if (c < nr * nb)
+                        v[i] = as[(int64_t)(list[min(r, n - 1)] / a_div) * nb + c % nb];
+                }
+#pragma unroll
+                for (int i = 0; i < SB; i++) {
+                    const int c = c0 + i * GW_NW * WAVE;
+                    if (c < nr * nb)
+                        xsb[(c % nb) * TM + c / nb] = v[i];
+                }
+            }
+            __syncthreads();
+
+            float acc[NB][TT][4];
+#pragma unroll
+            for (int q = 0; q < NB; q++)
+#pragma unroll
+                for (int t = 0; t < TT; t++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        acc[q][t][i] = 0.0f;
+            auto contract = [&](int s, int b0) {
+#pragma unroll
+                for (int u = 0; u < GW_BU; u++) {
+                    const int b = b0 + u;
+                    if (b >= nb)
+                        break;
+                    long wf[NB];
+#pragma unroll
+                    for (int q = 0; q < NB; q++)
+                        wf[q] = frag(s, q, u);
+                    const int off = 16 * ((2 * b + chx) ^ j) + cho;
+#pragma unroll
+                    for (int t = 0; t < TT; t++) {
+                        if (16 * t >= n)
+                            break;
+                        const long af = *reinterpret_cast<const long *>(abuf + (16 * t + j) * K + off);
+                        const f32x4 sx = *reinterpret_cast<const f32x4 *>(&xsb[b * TM + 16 * t + 4 * g]);
+                        long lf = 0;
+                        if constexpr (X2)
+                            lf = *reinterpret_cast<const long *>(abl + (16 * t + j) * K + off);
+#pragma unroll
+                        for (int q = 0; q < NB; q++) {
+                            const v4i is = __builtin_amdgcn_mfma_i32_16x16x32_i8(af, wf[q], v4i{0, 0, 0, 0}, 0, 0, 0);
+                            if constexpr (X2) {
+                                const v4i il =
+                                    __builtin_amdgcn_mfma_i32_16x16x32_i8(lf, wf[q], v4i{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                                for (int i = 0; i < 4; i++)
+                                    acc[q][t][i] = __builtin_fmaf((float)(is[i] * 128 + il[i]),
+                                                                  (bsc[s][q][u] * sx[i]) * 0.0078125f, acc[q][t][i]);
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 4; i++)
+                                    acc[q][t][i] = __builtin_fmaf((float)is[i], bsc[s][q][u] * sx[i], acc[q][t][i]);
+                            }
+                        }
+                    }
+                }
+            };
+            for (int b0 = 0; b0 < nb; b0 += 2 * GW_BU) {
+                if (b0 + GW_BU < nb)
+                    fetch(1, b0 + GW_BU);
+                contract(0, b0);
+                if (b0 + GW_BU >= nb)
+                    break;
+                if (b0 + 2 * GW_BU < nb)
+                    fetch(0, b0 + 2 * GW_BU);
+                contract(1, b0 + GW_BU);
+            }
+            // lane (j, g) holds rows 16t + 4g + i of output o0 + 16*wid + j
+            // (and of output o0 + 16 * GW_NW + 16*wid + j)
+#pragma unroll
+            for (int t = 0; t < TT; t++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int r = 16 * t + 4 * g + i;
+                    if (r < n) {
+                        float *o = out + (int64_t)list[r] * out_ld + o0 + 16 * wid + j;
+                        if constexpr (PAIR) {
+                            o[0] = silu(acc[0][t][i]) * acc[1][t][i];
+                        } else {
+                            o[0] = acc[0][t][i];
+                            o[16 * GW_NW] = acc[1][t][i];
+                        }
+                    }
+                }
+        }
+        if (total <= first + TM)
+            break;
+        __syncthreads();  // the next tile rewrites the list and the staged rows
+    }
+}
+
 size_t chunk_down_scratch_bytes(int64_t rows, int64_t d, int64_t k) { return align256((size_t)(rows * k * d) * 4); }
 
 // The grouped kernels take gate-up rows of up to 2048 values (two chunks a
@@ -577,17 +857,55 @@ size_t chunk_down_scratch_bytes(int64_t rows, int64_t d, int64_t k) { return ali
 // by row through the decode kernels.
 bool chunk_supported(int64_t d, int64_t dff) { return d <= 2048 && slice_shape(dff).ks == 1; }
 
+// Choices an expert, on average, from which a chunk's gate-up and down
+// projection run on the matrix cores (k_grouped_mfma) instead of the vector
+// units.
+#ifndef Q8S_WIDE_MIN
+#define Q8S_WIDE_MIN 8
+#endif
+constexpr int64_t WIDE_MIN_PER_EXPERT = Q8S_WIDE_MIN;
+
+bool chunk_wide_sizes(int64_t rows, int64_t d, int64_t dff, int64_t E, int64_t k, int act)
+{
+    // rows of whole 256-byte groups (whole tiles of 16 * GW_NW outputs), 16
+    // of them fit the staging LDS
+    const int64_t words = act == 2 ? 2 : 1;
+    return rows * k >= WIDE_MIN_PER_EXPERT * E && d % 256 == 0 && dff % 256 == 0 &&
+           16 * words * std::max(d, dff) <= GW_ABYTES;
+}
+
 namespace {
+
+bool chunk_wide(const MoeArgs &a) { return chunk_wide_sizes(a.rows, a.d, a.dff, a.E, a.k, a.act); }
+
+// k_grouped_mfma's LDS for tiles of tm rows of K values
+size_t gw_lds_bytes(int tm, int64_t K, bool x2) { return (size_t)(tm * K * (x2 ? 2 : 1) + tm * (K / 32) * 4 + (tm + 1) * 4); }
 
 hipError_t gu_chunk_go(const MoeArgs &a, hipStream_t st)
 {
-    dim3 grid((unsigned)(a.dff / CKB_T), (unsigned)(a.E + 1));  // + one row for invalid choices
-    if (a.act == 2)
-        hipLaunchKernelGGL(k_chunk_gate_up<true>, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
-                           a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h, a.xl);
-    else
-        hipLaunchKernelGGL(k_chunk_gate_up<false>, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs, a.Wuq,
-                           a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E, a.h, nullptr);
+    if (chunk_wide(a)) {
+        // paired gate/up rows, 16 hidden outputs a wave; + one row for invalid choices
+        dim3 grid((unsigned)(a.dff / (16 * GW_NW)), (unsigned)(a.E + 1));
+        auto go = [&](auto kernel, int tm) {
+            hipLaunchKernelGGL(kernel, grid, dim3(GW_NW * WAVE), gw_lds_bytes(tm, a.d, a.act == 2), st, a.xq, a.xl,
+                               a.xs, (int)a.k, a.Wgq, a.Wgs, a.Wuq, a.Wus, a.idx, (int)(a.rows * a.k), (int)a.d,
+                               (int)a.dff, (int)a.E, a.h, (int)a.dff);
+        };
+        if (a.act == 2)
+            a.d <= GW_ABYTES / 2 / 32 ? go(k_grouped_mfma<32, true, true>, 32) : go(k_grouped_mfma<16, true, true>, 16);
+        else
+            a.d <= GW_ABYTES / 32 ? go(k_grouped_mfma<32, true, false>, 32) : go(k_grouped_mfma<16, true, false>, 16);
+    } else {
+        dim3 grid((unsigned)(a.dff / CKB_T), (unsigned)(a.E + 1));  // + one row for invalid choices
+        if (a.act == 2)
+            hipLaunchKernelGGL(k_chunk_gate_up<true>, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs,
+                               a.Wuq, a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E,
+                               a.h, a.xl);
+        else
+            hipLaunchKernelGGL(k_chunk_gate_up<false>, grid, dim3(CKB_NW * WAVE), 0, st, a.xq, a.xs, a.Wgq, a.Wgs,
+                               a.Wuq, a.Wus, a.idx, (int)(a.rows * a.k), (int)a.k, (int)a.d, (int)a.dff, (int)a.E,
+                               a.h, nullptr);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !a.hq)
         return err;
@@ -616,7 +934,20 @@ hipError_t dn_chunk_go(const MoeArgs &a, hipStream_t st)
     using S = CkDownShape<LPR, C>;
     float *pa = reinterpret_cast<float *>(a.scratch);
     const int64_t nch = a.dff / 16;
-    if (nch <= 16)
+    if (chunk_wide(a)) {
+        // two tiles of 16 outputs of d a wave
+        dim3 grid((unsigned)(a.d / (32 * GW_NW)), (unsigned)a.E);
+        auto go = [&](auto kernel, int tm) {
+            hipLaunchKernelGGL(kernel, grid, dim3(GW_NW * WAVE), gw_lds_bytes(tm, a.dff, a.act == 2), st, a.hq, a.hl,
+                               a.hs, 1, a.Wdq, a.Wds, nullptr, nullptr, a.idx, (int)(a.rows * a.k), (int)a.dff,
+                               (int)a.d, (int)a.E, pa, (int)a.d);
+        };
+        if (a.act == 2)
+            a.dff <= GW_ABYTES / 2 / 32 ? go(k_grouped_mfma<32, false, true>, 32)
+                                        : go(k_grouped_mfma<16, false, true>, 16);
+        else
+            a.dff <= GW_ABYTES / 32 ? go(k_grouped_mfma<32, false, false>, 32) : go(k_grouped_mfma<16, false, false>, 16);
+    } else if (nch <= 16)
         dn2_go<2>(a, pa, st);
     else if (nch <= 32)
         dn2_go<4>(a, pa, st);

@@ -203,6 +203,9 @@ CONFIGS = {
     "moe_d2048_dff768_e128_k8": dict(kind="moe", d=2048, dff=768, E=128, k=8),
     "moe_d4096_dff14336_e8_k2": dict(kind="moe", d=4096, dff=14336, E=8, k=2),
     "chunk64_moe_d2048_dense4096": dict(kind="chunk", d=2048, dff=768, E=128, k=8, rows=64, n_dense=4096),
+    # wider prefill chunks through the same block and projection
+    "chunk128_moe_d2048_dense4096": dict(kind="chunk", d=2048, dff=768, E=128, k=8, rows=128, n_dense=4096),
+    "chunk256_moe_d2048_dense4096": dict(kind="chunk", d=2048, dff=768, E=128, k=8, rows=256, n_dense=4096),
     # a mixture with an always-on shared expert four experts wide and its
     # router as Q8_0 rows (the Qwen1.5-MoE-A2.7B-like FFN shape)
     "moe_shared_d2048_dff1408_e60_k4_s5632": dict(kind="moe_shared", d=2048, dff=1408, E=60, k=4, sdff=5632),

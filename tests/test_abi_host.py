@@ -445,3 +445,32 @@ def test_two_word_stage_refusals_before_any_hip_call():
     assert dcall(sb=64) == -4 and "per-choice" in _err()
     assert dcall(scratch=0x30000010) == -3
     assert dcall(rows=0) == -1
+
+
+def test_moe_path_rule():
+    # which kernels the mixture's expert stages run: one row or float32
+    # activations row by row; chunks grouped by expert, on the matrix cores
+    # from 8 choices an expert with d, dff multiples of 256 whose 16 staged
+    # rows fit 64 KiB
+    path = q8.q8s_moe_path
+    R, G, M = q8.PATH_ROWS, q8.PATH_GROUPED, q8.PATH_GROUPED_MFMA
+    assert path(1, 2048, 768, 128, 8, 1) == R
+    assert path(64, 2048, 768, 128, 8, 0) == R
+    assert path(64, 4096, 768, 128, 8, 1) == R          # d past the grouped kernels
+    assert path(64, 2048, 768, 128, 8, 1) == G          # 4 choices an expert
+    assert path(127, 2048, 768, 128, 8, 1) == G         # 7.9
+    assert path(128, 2048, 768, 128, 8, 1) == M         # 8
+    assert path(256, 2048, 768, 128, 8, 2) == M         # two words, 32 KiB rows of 2048
+    assert path(128, 1056, 768, 128, 8, 1) == G         # d not a multiple of 256
+    assert path(150, 128, 96, 2, 1, 1) == G             # rows of 128
+    assert path(40, 512, 4096, 4, 2, 1) == M            # 16 rows of 4096 = 64 KiB
+    assert path(40, 512, 4096, 4, 2, 2) == G            # twice that in two words
+    # the GPU tests' wide cases take the matrix cores
+    for rows, E, k, d, dff in [(150, 2, 1, 256, 256), (200, 3, 3, 512, 256), (70, 5, 2, 256, 512),
+                               (32, 4, 2, 2048, 512), (40, 4, 2, 512, 4096), (12, 2, 2, 256, 256)]:
+        assert path(rows, d, dff, E, k, 1) == M
+    for d, dff, E, k, rows in [(2048, 768, 128, 8, 128), (256, 256, 2, 1, 150), (512, 2048, 4, 2, 40)]:
+        assert path(rows, d, dff, E, k, 2) == M
+    for bad in [(0, 64, 64, 2, 1, 1), (2, 64, 64, 2, 3, 1), (2, 64, 64, 2, 1, 3), (2, 64, 0, 2, 1, 1)]:
+        with pytest.raises(q8.Q8sError):
+            path(*bad)

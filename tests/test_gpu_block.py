@@ -84,9 +84,14 @@ def test_block_matches_oracle(d, dff, E, k, rows, act):
     check(b, act, run_block(b, act))
 
 
-def test_block_chunk_64_rows():
-    banner("block 64-row chunk, int8")
-    b = synthetic.block_inputs(21, 2048, 768, 128, 8, 64)
+@pytest.mark.parametrize("rows", [64, 128, 256])
+def test_block_chunk_rows(rows):
+    # 4 choices an expert at 64 rows (the vector-unit grouped kernels); 8 and
+    # 16 at 128 and 256 (the matrix-core grouped kernels)
+    banner("block %d-row chunk, int8" % rows)
+    want = q8.PATH_GROUPED if rows == 64 else q8.PATH_GROUPED_MFMA
+    assert q8.q8s_moe_path(rows, 2048, 768, 128, 8, q8.ACT_INT8) == want
+    b = synthetic.block_inputs(21, 2048, 768, 128, 8, rows)
     check(b, 1, run_block(b, 1))
 
 

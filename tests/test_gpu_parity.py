@@ -433,6 +433,67 @@ def test_chunk_many_choices_per_expert(rows, E, k):
         assert rel_err(y[r], ry[r]) <= TOL_I8, r
 
 
+# Chunks of 8 and more choices an expert on average, in rows of whole
+# 256-byte groups, run their gate-up and down projection on the matrix cores:
+# 16 weight rows a wave against tiles of 32 staged choice rows (16 where 32
+# would not fit the staging LDS), several tiles for an expert with more.
+WIDE_CASES = [
+    (150, 2, 1, 256, 256),     # 75 choices an expert: three tiles, the last ragged
+    (200, 3, 3, 512, 256),     # 200 an expert: seven tiles
+    (70, 5, 2, 256, 512),      # 28 an expert, unevenly spread: one tile, some experts two
+    (32, 4, 2, 2048, 512),     # token rows of 2 KB, 16 choices an expert
+    (40, 4, 2, 512, 4096),     # hidden rows of 4 KB: down tiles of 16 rows
+]
+
+
+@pytest.mark.parametrize("rows,E,k,d,dff", WIDE_CASES)
+def test_chunk_wide_matches_oracle(rows, E, k, d, dff):
+    banner("chunk wide rows=%d E=%d k=%d d=%d dff=%d" % (rows, E, k, d, dff))
+    assert q8.q8s_moe_path(rows, d, dff, E, k, q8.ACT_INT8) == q8.PATH_GROUPED_MFMA
+    m = synthetic.moe_inputs(14, d, dff, E, k, rows)
+    ridx, rw, rh, ry = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, m.k, 1)
+    idx, wts, h, y = run_moe_gpu(m, 1)
+    assert np.array_equal(idx, ridx)
+    assert rel_err(h, rh) <= TOL_I8
+    for r in range(rows):
+        assert rel_err(y[r], ry[r]) <= TOL_I8, r
+
+
+def test_chunk_wide_invalid_expert_index():
+    # 24 choices over 2 experts (the matrix-core path), a quarter of them
+    # invalid: zero hidden rows, no contribution to the output
+    banner("chunk wide invalid idx")
+    rows, E, k, d, dff = 12, 2, 2, 256, 256
+    assert q8.q8s_moe_path(rows, d, dff, E, k, q8.ACT_INT8) == q8.PATH_GROUPED_MFMA
+    m = synthetic.moe_inputs(15, d, dff, E, k, rows)
+    Wgq, Wgs, Wuq, Wus, Wdq, Wds = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds))
+    xq, xs = q8.q8_quantize_rows(dev(m.x))
+    rng = np.random.default_rng(16)
+    idx = rng.integers(0, E, (rows, k)).astype(np.int32)
+    idx[::4, 0] = -1
+    idx[1::4, 1] = 9
+    wts = rng.random((rows, k)).astype(np.float32)
+    h, hq, hs = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, dev(idx), E, xq=xq, xs=xs, act=q8.ACT_INT8)
+    y = q8.moe_down_combine(Wdq, Wds, dev(idx), dev(wts), E, hq=hq, hs=hs, act=q8.ACT_INT8)
+    h, y = host(h), host(y)
+    xqq, xss = oracle.quantize(m.x)
+    for r in range(rows):
+        yref = np.zeros(d)
+        for c in range(k):
+            e = idx[r, c]
+            if not 0 <= e < E:
+                assert not h[r, c].any(), (r, c)
+                continue
+            sl = slice(e * dff, (e + 1) * dff)
+            g = oracle.gemv_i8(m.Wgq[sl], m.Wgs[sl], xqq[r:r + 1], xss[r:r + 1])
+            u = oracle.gemv_i8(m.Wuq[sl], m.Wus[sl], xqq[r:r + 1], xss[r:r + 1])
+            hid = (g / (1 + np.exp(-g)) * u)
+            assert rel_err(h[r, c], hid[0]) <= TOL_I8, (r, c)
+            hqq, hss = oracle.quantize(h[r, c][None])
+            yref += wts[r, c] * oracle.gemv_i8(m.Wdq[e * d:(e + 1) * d], m.Wds[e * d:(e + 1) * d], hqq, hss)[0]
+        assert rel_err(y[r], yref) <= TOL_I8, r
+
+
 def test_chunk_invalid_expert_index():
     banner("chunk invalid idx")
     m = synthetic.moe_inputs(13, 64, 64, 4, 2, 3)

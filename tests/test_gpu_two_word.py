@@ -143,6 +143,11 @@ BLOCK_X2_CASES = [
     (2048, 768, 128, 8, 64),    # the 64-row chunk of the 128-expert block, each expert read once
     (1024, 2048, 16, 4, 8),     # hidden rows of 2048: the chunk down projection a lane group a row
     (96, 160, 5, 3, 4),         # ragged rows in the chunk kernels
+    # 8 and more choices an expert: the matrix-core grouped kernels, two
+    # MFMAs a block
+    (2048, 768, 128, 8, 128),   # gate-up tiles of 16 rows (two-word token rows of 2 KB)
+    (256, 256, 2, 1, 150),      # 75 choices an expert: three tiles of 32 rows, the last ragged
+    (512, 2048, 4, 2, 40),      # down tiles of 16 rows
 ]
 
 
