@@ -205,6 +205,14 @@ Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_
  * a chunk of rows in the grouped kernels may pass both NULL to write only the
  * float32 rows and quantise them itself with q8_quantize_rows).  A choice
  * whose expert index is invalid gets zeros.
+ * This replaces the plainer form
+ *   moe_gate_up(x, xq, xs, Wgq, Wgs, Wuq, Wus, idx, rows, d, dff, E, k, h,
+ *               act, scratch, scratch_bytes, stream)
+ * in two ways: it also returns the hidden rows' Q8_0 form (hq, hs), which the
+ * int8 down projection reads (arena.rs fn scratch keeps hq/hs beside h); and
+ * it takes no scratch, because each (expert, tile) workgroup of a chunk
+ * gathers its own choices on the device, so no grouping state passes between
+ * calls.
  */
 Q8S_API int moe_gate_up(const float *x, const int8_t *xq, const float *xs,
                 const int8_t *Wgq, const float *Wgs, const int8_t *Wuq, const float *Wus,
@@ -222,6 +230,12 @@ Q8S_API int moe_gate_up(const float *x, const int8_t *xq, const float *xs,
  * y: device f32 [rows, d].  scratch: device, >= q8s_scratch_bytes(Q8S_FN_DOWN,
  * ...) bytes, 256-byte aligned (zero bytes when rows == 1, where NULL is
  * accepted): per-choice results of a chunk, combined per row in slot order.
+ * This replaces the plainer form
+ *   moe_down_combine(h, Wdq, Wds, idx, wts, rows, d, dff, E, k, y, act,
+ *                    scratch, scratch_bytes, stream)
+ * by also taking hq/hs, the hidden rows' Q8_0 form from moe_gate_up: in INT8
+ * the down projection reads those, not h (h may then be NULL).  The scratch
+ * carries only this call's per-choice results, never state from the gate-up.
  */
 Q8S_API int moe_down_combine(const float *h, const int8_t *hq, const float *hs,
                      const int8_t *Wdq, const float *Wds, const int32_t *idx, const float *wts,
