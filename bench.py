@@ -83,6 +83,14 @@ def chunk_kernels(cfg, act):
     return "k_chunk_gate_up", ("k_chunk_down2" if cfg["dff"] <= 1024 else "k_chunk_down")
 
 
+def kernel_pattern(kernel):
+    """The dispatches a counter file covers: the kernel's instantiations, or
+    for the matrix-core grouped kernel only its gate-up (PAIR) ones."""
+    if kernel == "k_grouped_mfma":
+        return r"q8s::k_grouped_mfma<\d+, true, (true|false)>"
+    return r"q8s::%s\b" % kernel
+
+
 def counters_path(kernel, workload, act):
     return os.path.join(ROOT, "profiles", "%s_%s_%s_counters.txt" % (kernel, workload, act))
 
@@ -113,7 +121,7 @@ def summarize_counters(args):
                         % (args.workload, args.act, args.calib_copy_mib)]}
     for counter, path in (("FETCH_SIZE", args.summarize_counters[0]), ("WRITE_SIZE", args.summarize_counters[1])):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        mine = [float(r["Counter_Value"]) for r in rows if re.search(r"q8s::%s\b" % kernel, r["Kernel_Name"])]
+        mine = [float(r["Counter_Value"]) for r in rows if re.search(kernel_pattern(kernel), r["Kernel_Name"])]
         copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
         # the calibration copy is the run's last copy dispatch
         ref = copies[-1]
