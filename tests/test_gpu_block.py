@@ -95,6 +95,27 @@ def test_block_chunk_rows(rows):
     check(b, 1, run_block(b, 1))
 
 
+@pytest.mark.parametrize("rows", [64, 128])
+def test_chunk_block_equals_stage_calls(rows):
+    # a chunk in int8 numerics: add_rmsnorm_q8 -> moe_route_topk ->
+    # moe_gate_up -> moe_down_combine compute bit for bit what moe_ffn_block
+    # computes (the same grouped kernels: the vector-unit ones at 64 rows,
+    # the matrix-core ones at 128)
+    banner("chunk block vs stage calls rows=%d" % rows)
+    b = synthetic.block_inputs(27, 2048, 768, 128, 8, rows)
+    W = weights(b)
+    Wr, Wgq, Wgs, Wuq, Wus, Wdq, Wds = W
+    s, x, xq, xs = q8.add_rmsnorm_q8(dev(b.h), dev(b.r), dev(b.w), EPS)
+    idx, wts = q8.moe_route_topk(x, Wr, 8)
+    _, hq, hs = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, 128, xq=xq, xs=xs, act=1)
+    y = q8.moe_down_combine(Wdq, Wds, idx, wts, 128, hq=hq, hs=hs, act=1)
+    bs, bidx, bw, bout = run_block(b, 1, W)
+    assert np.array_equal(bs, host(s))
+    assert np.array_equal(bidx, host(idx))
+    assert np.array_equal(bw, host(wts))
+    assert np.array_equal(bout, host(y))
+
+
 @pytest.mark.parametrize("act", [0, 1])
 def test_block_equals_separate_calls(act):
     # the fused launches compute what add_rmsnorm_q8 -> moe_route_topk ->

@@ -260,13 +260,14 @@ def test_block_x2_scratch_needs_no_initial_contents_and_repeats():
         assert torch.equal(a, c)
 
 
-@pytest.mark.parametrize("rows", [1, 64])
+@pytest.mark.parametrize("rows", [1, 64, 128])
 def test_x2_stage_calls_equal_block(rows):
     # add_rmsnorm_q8 -> q8_quantize_rows_x2 -> moe_route_topk -> moe_gate_up_x2
     # -> moe_down_combine_x2 compute what moe_ffn_block(act 2) computes: bit
-    # for bit for a chunk (the block runs these very kernels), and for one row
-    # within float rounding of the routing weights (the block's fused launches
-    # form the logits in another order)
+    # for bit for a chunk (the block runs these very kernels: the vector-unit
+    # ones at 64 rows, the matrix-core ones at 128), and for one row within
+    # float rounding of the routing weights (the block's fused launches form
+    # the logits in another order)
     banner("x2 stage calls vs block rows=%d" % rows)
     import torch
     b = synthetic.block_inputs(31, 2048, 768, 128, 8, rows)

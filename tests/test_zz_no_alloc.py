@@ -68,6 +68,19 @@ def test_noalloc_two_calls_second_smaller():
     check_oracle(small, q8.ACT_INT8, got)
 
 
+@pytest.mark.parametrize("act", [1, 2])
+def test_noalloc_wide_chunk_then_smaller(act):
+    # a 128-row chunk (8 choices an expert: the matrix-core grouped kernels)
+    # bit for bit against moe_ffn_block, then a 64-row chunk on the vector
+    # units in the array the first call left
+    banner("moe_ffn_block_noalloc: 128-row chunk act=%d, then 64 rows" % act)
+    assert q8.q8s_moe_path(128, 2048, 768, 128, 8, act) == q8.PATH_GROUPED_MFMA
+    for rows, seed in ((128, 45), (64, 46)):
+        got, ref = both(synthetic.block_inputs(seed, 2048, 768, 128, 8, rows), act)
+        for g, r in zip(got, ref):
+            assert np.array_equal(g, r)
+
+
 @pytest.mark.parametrize("act", [0, 1, 2])
 def test_noalloc_each_numerics(act):
     # a 3-row block, then a smaller 1-row block of another shape, in each
