@@ -459,19 +459,38 @@ def test_chunk_wide_matches_oracle(rows, E, k, d, dff):
         assert rel_err(y[r], ry[r]) <= TOL_I8, r
 
 
-def test_chunk_wide_invalid_expert_index():
-    # 24 choices over 2 experts (the matrix-core path), a quarter of them
-    # invalid: zero hidden rows, no contribution to the output
-    banner("chunk wide invalid idx")
-    rows, E, k, d, dff = 12, 2, 2, 256, 256
+@pytest.mark.parametrize("case", ["quarter", "most", "one_expert", "k1"])
+def test_chunk_wide_invalid_expert_index(case):
+    # choices given directly to the matrix-core path (8 and more an expert):
+    #   quarter     24 choices over 2 experts, a quarter invalid
+    #   most        48 choices, 40 invalid: the invalid row's workgroups
+    #               take two tiles of 32
+    #   one_expert  every valid choice on expert 1 of 4: experts 0, 2, 3
+    #               have none (their workgroups only scan the list)
+    #   k1          one choice a row
+    # An invalid choice gets a zero hidden row and adds nothing to y.
+    banner("chunk wide invalid idx: %s" % case)
+    rows, E, k, d, dff = {"quarter": (12, 2, 2, 256, 256), "most": (24, 2, 2, 256, 256),
+                          "one_expert": (24, 4, 2, 256, 512), "k1": (40, 4, 1, 512, 256)}[case]
     assert q8.q8s_moe_path(rows, d, dff, E, k, q8.ACT_INT8) == q8.PATH_GROUPED_MFMA
     m = synthetic.moe_inputs(15, d, dff, E, k, rows)
     Wgq, Wgs, Wuq, Wus, Wdq, Wds = (dev(a) for a in (m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds))
     xq, xs = q8.q8_quantize_rows(dev(m.x))
     rng = np.random.default_rng(16)
     idx = rng.integers(0, E, (rows, k)).astype(np.int32)
-    idx[::4, 0] = -1
-    idx[1::4, 1] = 9
+    if case == "quarter":
+        idx[::4, 0] = -1
+        idx[1::4, 1] = 9
+    elif case == "most":
+        flat = idx.reshape(-1)
+        bad = rng.permutation(flat.size)[:40]
+        flat[bad] = np.where(rng.random(40) < 0.5, -3, E + 5)
+        assert (~((idx >= 0) & (idx < E))).sum() == 40
+    elif case == "one_expert":
+        idx[:] = 1
+        idx[::3, 1] = -1
+    else:
+        idx[::5, 0] = 77
     wts = rng.random((rows, k)).astype(np.float32)
     h, hq, hs = q8.moe_gate_up(Wgq, Wgs, Wuq, Wus, dev(idx), E, xq=xq, xs=xs, act=q8.ACT_INT8)
     y = q8.moe_down_combine(Wdq, Wds, dev(idx), dev(wts), E, hq=hq, hs=hs, act=q8.ACT_INT8)
