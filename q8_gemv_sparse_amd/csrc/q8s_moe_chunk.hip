@@ -701,9 +701,13 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
         const int w0 = mine ? ((u & 1) ? v[2] : v[0]) : r0, w1 = mine ? ((u & 1) ? v[3] : v[1]) : r1;
         return (long)(uint32_t)w0 | ((long)w1 << 32);
     };
-    // the first blocks' fetch does not wait for the choice list
-    if (e < E)
+    // both buffers' first fetches do not wait for the choice list (nor for
+    // the staging of the choices' rows)
+    if (e < E) {
         fetch(0, 0);
+        if (GW_BU < nb)
+            fetch(1, GW_BU);
+    }
 
     for (int first = 0;; first += TM) {
         if (wid == 0) {
@@ -722,8 +726,11 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
             for (int t = tid; t < n * OT; t += GW_NW * WAVE)
                 out[(int64_t)list[t / OT] * out_ld + o0 + t % OT] = 0.0f;
         } else {
-            if (first > 0)
+            if (first > 0) {
                 fetch(0, 0);
+                if (GW_BU < nb)
+                    fetch(1, GW_BU);
+            }
             // stage the A rows of the tiles in use (rows past n repeat the
             // last one; their results are never written) and their scales,
             // block-major; SB loads a thread in flight before their LDS
@@ -816,15 +823,17 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
                     }
                 }
             };
+            // buffer s holds blocks b0 + s*GW_BU on entry; each is refilled
+            // two steps ahead as soon as its blocks are contracted
             for (int b0 = 0; b0 < nb; b0 += 2 * GW_BU) {
-                if (b0 + GW_BU < nb)
-                    fetch(1, b0 + GW_BU);
                 contract(0, b0);
-                if (b0 + GW_BU >= nb)
-                    break;
                 if (b0 + 2 * GW_BU < nb)
                     fetch(0, b0 + 2 * GW_BU);
+                if (b0 + GW_BU >= nb)
+                    break;
                 contract(1, b0 + GW_BU);
+                if (b0 + 3 * GW_BU < nb)
+                    fetch(1, b0 + 3 * GW_BU);
             }
             // lane (j, g) holds rows 16t + 4g + i of output o0 + 16*wid + j
             // (and of output o0 + 16 * GW_NW + 16*wid + j)
