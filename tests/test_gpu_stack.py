@@ -43,6 +43,8 @@ CASES = [
     (3, 2048, 768, 128, 8, 1, 2),
     (4, 1024, 512, 32, 4, 1, 1),
     (2, 2048, 768, 128, 8, 64, 1),    # a 64-row chunk: the grouped kernels, the add in the combine
+    (2, 2048, 768, 128, 8, 64, 2),    # the same in two words
+    (2, 2048, 768, 128, 8, 128, 1),   # a 128-row chunk: the matrix-core grouped kernels
     (2, 256, 96, 6, 2, 3, 0),         # 3 rows of float32 numerics
     (1, 512, 128, 8, 2, 1, 1),        # one layer: out = s_0 + m_0
 ]
