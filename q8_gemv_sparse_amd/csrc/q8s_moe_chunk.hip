@@ -589,7 +589,8 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
 //     a 64-byte span of row j: half of block 2p or 2p+1), GW_BU blocks ahead
 //     of their use, the rows' scales 16 bytes a load; lanes 32 apart then
 //     trade halves so each holds 8 bytes of one block, the MFMA's fragment.
-//     The first fetch is issued before the choice list is scanned;
+//     Both buffers' first fetches are issued before the choice list is
+//     scanned, and each buffer is refilled as soon as its blocks are used;
 //   * A operand: the rows of up to TM of the expert's choices (gathered in
 //     choice order), staged in LDS once per choice tile with their scales
 //     (only the row tiles in use, several loads a thread in flight); each
@@ -603,9 +604,10 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
 //        the same (choice, output) and writes SiLU(g) * u (lane_link.rs fn
 //        class_launch: a gated pair fused with what consumes it); a tile is
 //        16 * GW_NW hidden outputs.  A rows are the choices' token rows
-//        (choice c reads row c / a_div, a_div = K); the grid row past the last
-//        expert writes zero hidden rows for the choices whose expert index is
-//        invalid.
+//        (choice c reads row c / a_div, a_div = k, the choices a row); the
+//        grid row past the last
+//        expert writes zero hidden rows for the choices whose expert index
+//        is invalid.
 //   otherwise (the down projection): a wave streams output rows o and
 //        o + 16 * GW_NW, a tile is 32 * GW_NW outputs; A rows are the
 //        choices' hidden rows (a_div = 1), and the result goes to pa[c][o]
@@ -617,9 +619,8 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
 // the chip holds at once at the shapes this path takes (1536 gate-up and 2048
 // down workgroups at d 2048, dff 768, 128 experts, two a CU), so no split of
 // the reduced dimension is needed to fill the chip's last wave of
-// workgroups.  Rows K must be a
-// multiple of 256 bytes (the XOR stays inside aligned groups of 16 chunks),
-// and TM * K * (X2 ? 2 : 1) <= GW_ABYTES.
+// workgroups.  Rows K must be a multiple of 256 bytes (the XOR stays inside
+// aligned groups of 16 chunks), and TM * K * (X2 ? 2 : 1) <= GW_ABYTES.
 constexpr int GW_NW = 4;              // waves a workgroup
 constexpr int GW_ABYTES = 65536;      // most LDS for the staged A rows
 constexpr int GW_BU = 8;              // blocks of B in flight a wave
