@@ -605,9 +605,8 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
 //        class_launch: a gated pair fused with what consumes it); a tile is
 //        16 * GW_NW hidden outputs.  A rows are the choices' token rows
 //        (choice c reads row c / a_div, a_div = k, the choices a row); the
-//        grid row past the last
-//        expert writes zero hidden rows for the choices whose expert index
-//        is invalid.
+//        grid row past the last expert writes zero hidden rows for the
+//        choices whose expert index is invalid.
 //   otherwise (the down projection): a wave streams output rows o and
 //        o + 16 * GW_NW, a tile is 32 * GW_NW outputs; A rows are the
 //        choices' hidden rows (a_div = 1), and the result goes to pa[c][o]
