@@ -220,10 +220,12 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C, V>::NW * WAVE))
 }
 
 // gate-up that first takes the row's top-K itself from the router logits:
-// every routed workgroup ranks the row's E logits in LDS (topk_select) and
-// reads its expert from the result, so the choices need no launch of their
-// own; the workgroup of tile 0, slot 0 writes the row's idx and wts for the
+// every routed workgroup ranks the row's E logits in LDS (topk_select), or
+// for at most TOPK_WAVE_E experts in each wave's registers, and reads its
+// expert from the result, so the choices need no launch of their own; the
+// workgroup of tile 0, slot 0 writes the row's idx and wts for the
 // down-combine launch.  The shared expert's workgroups need no ranking.
+constexpr int TOPK_WAVE_E = 16;
 template <int ACT, int LPR, int C, bool SH, int V>
 __global__ void __launch_bounds__((GuShape<ACT, LPR, C, V>::NW * WAVE))
     k_route_gate_up(const double *__restrict__ logits, int32_t *__restrict__ idx, float *__restrict__ wts,
@@ -245,11 +247,34 @@ __global__ void __launch_bounds__((GuShape<ACT, LPR, C, V>::NW * WAVE))
                                   hs, xl, hl);
         return;
     }
-    topk_load(tk, logits + row * E, E);
-    __syncthreads();
-    topk_select(tk, E, k);
-    __syncthreads();
-    const int e = __builtin_amdgcn_readfirstlane(tk.ch[t.j]);
+    const double *lr = logits + row * E;
+    int e;
+    if (E <= TOPK_WAVE_E) {
+        // few experts: every wave ranks them itself, lane i logit i against
+        // all E (the order of topk_select: code descending, index
+        // ascending), and takes slot t.j's expert by ballot -- no LDS pass,
+        // no barrier before the tile's first weight request
+        const int lane = threadIdx.x & (WAVE - 1);
+        const double li = lr[min(lane, E - 1)];
+        const uint64_t ci = route_code(li);
+        int rank = 0;
+        for (int w = 0; w < E; w++) {
+            const uint64_t cw = route_code(lr[w]);
+            rank += (cw > ci || (cw == ci && w < lane)) ? 1 : 0;
+        }
+        const bool mine = lane < E;
+        e = (int)__builtin_ctzll(__ballot(mine && rank == t.j));
+        if (blockIdx.x == 0 && threadIdx.x < WAVE && mine && rank < k) {
+            tk.ch[rank] = lane;  // for route_finish, read by this same wave
+            tk.kl[rank] = li;
+        }
+    } else {
+        topk_load(tk, lr, E);
+        __syncthreads();
+        topk_select(tk, E, k);
+        __syncthreads();
+        e = __builtin_amdgcn_readfirstlane(tk.ch[t.j]);
+    }
     gate_up_tile<ACT, LPR, C, V>(sm, true, row, (int64_t)e * dff + t.o0, hbase, x, xq, xs, Wgq, Wgs, Wuq, Wus, d, ks, h,
                               hq, hs, xl, hl);
     // the choices and weights go out after the tile, off its critical path

@@ -197,8 +197,11 @@ def host_topk(logits, k):
 
 
 @pytest.mark.parametrize("act", [0, 1])
+# E <= 16 ranks in each wave's registers, more experts in LDS: both orders
+# are checked on exact ties, near-ties (equal upper 32 bits) and signed zeros
 @pytest.mark.parametrize("E,k,ties", [(128, 8, ""), (8, 2, ""), (256, 32, "exact"), (5, 5, "exact"), (1, 1, ""),
-                                        (128, 8, "near"), (256, 32, "near")])
+                                        (128, 8, "near"), (256, 32, "near"), (16, 4, "near"), (16, 16, "exact"),
+                                        (12, 8, "near")])
 def test_topk_gate_up(E, k, ties, act):
     banner("moe_topk_gate_up E=%d k=%d ties=%s act=%d" % (E, k, ties, act))
     rows, d, dff = 2, 256, 96
@@ -255,17 +258,20 @@ def test_topk_gate_up_many_tiles():
     assert torch.equal(h, h2) and torch.equal(hq, hq2) and torch.equal(hs, hs2)
 
 
-def test_topk_gate_up_nan_logits():
+@pytest.mark.parametrize("E", [128, 12])
+def test_topk_gate_up_nan_logits(E):
     # NaN logits: a NaN with the sign bit clear ranks above every number, one
-    # with it set below; the choices stay K distinct experts in range
-    banner("moe_topk_gate_up NaN logits")
-    rows, d, dff, E, k = 2, 256, 96, 128, 8
+    # with it set below; the choices stay K distinct experts in range (128
+    # experts ranked in LDS, 12 in registers)
+    banner("moe_topk_gate_up NaN logits E=%d" % E)
+    rows, d, dff, k = 2, 256, 96, 8
     m = synthetic.moe_inputs(26, d, dff, E, k, rows)
     rng = np.random.default_rng(28)
     logits = rng.standard_normal((rows, E))
     pos, neg = np.float64(np.nan), -np.float64(np.nan)
     assert not np.signbit(pos) and np.signbit(neg)
-    logits[0, [5, 77]] = pos
+    hi = E - 3
+    logits[0, [5, hi]] = pos
     logits[0, [1, 2, 3]] = neg
     logits[1, :] = neg
     logits[1, 9] = 0.5
@@ -276,7 +282,7 @@ def test_topk_gate_up_nan_logits():
         assert len(set(idx[r].tolist())) == k and idx[r].min() >= 0 and idx[r].max() < E
     # row 0: the two positive NaNs by index, then the six largest numbers
     finite = [e for e in np.lexsort((np.arange(E), -np.nan_to_num(logits[0], nan=-np.inf))) if not np.isnan(logits[0, e])]
-    assert list(idx[0]) == [5, 77] + finite[:k - 2]
+    assert list(idx[0]) == [5, hi] + finite[:k - 2]
     # row 1: the one number, then negative NaNs by index
     assert list(idx[1]) == [9, 0, 1, 2, 3, 4, 5, 6]
 
