@@ -38,6 +38,16 @@ Q8S_DEV float ld_stream_f32(const float *p) { return __builtin_nontemporal_load(
 Q8S_DEV i32x4 ld16(const void *p) { return *reinterpret_cast<const i32x4 *>(p); }
 Q8S_DEV f32x4 ldf4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 
+// A raw buffer resource over n bytes from a wave-uniform base (held in
+// scalar registers): its loads take a 32-bit byte offset a lane, so they keep
+// no 64-bit address in vector registers; a load at or past n bytes returns
+// zero.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+Q8S_DEV BufRes buf_res(const void *p, uint32_t n)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // cross-lane reductions
 
@@ -47,15 +57,17 @@ constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <- lane 7-i within each 8
 constexpr int DPP_MIRROR = 0x140;      // lane i <- lane 15-i within each 16
 
+// (every control here is a whole permutation; a lane whose source is
+// inactive reads 0, and no register needs clearing before the move)
 template <int CTRL>
 Q8S_DEV float dpp_f(float v)
 {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 Q8S_DEV int dpp_i(int v)
 {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 // Sum over each 16-lane row; every lane of the row receives the row's sum.

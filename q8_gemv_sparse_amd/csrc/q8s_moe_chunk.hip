@@ -45,19 +45,21 @@ namespace {
 constexpr int CK_PASS = 64;  // choices of one expert per pass
 constexpr int CK_GB = 8;     // idx words a lane holds: a scan step covers CK_GB * 64 choices
 
-// A wave's copy of idx[c0, c0 + CK_GB*64): straight-line loads (past the end
-// reads the last choice and is marked `E`, which matches no bucket below E).
+// A wave's copy of idx[c0, c0 + CK_GB*64): straight-line buffer loads from
+// a scalar base (past the end reads the last choice, which the scan leaves
+// out).  Nothing here uses the values, so a caller can put other loads
+// behind these without waiting for them.
 struct IdxBatch {
     int ec[CK_GB];
 };
 
-Q8S_DEV void idx_load(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice, int c0, int E, int lane)
+Q8S_DEV void idx_load(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice, int c0, int lane)
 {
+    const BufRes r = buf_res(idx, 4u * (uint32_t)nchoice);
 #pragma unroll
     for (int i = 0; i < CK_GB; i++) {
         const int c = c0 + i * WAVE + lane;
-        const int v = idx[min(c, nchoice - 1)];
-        b.ec[i] = c < nchoice ? v : E;
+        b.ec[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(r, 4u * (uint32_t)min(c, nchoice - 1), 0, 0);
     }
 }
 
@@ -91,7 +93,7 @@ Q8S_DEV int idx_gather(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice
 {
     int base = idx_scan<PASS>(b, 0, nchoice, e, E, first, 0, list, lane);
     for (int c0 = CK_GB * WAVE; c0 < nchoice; c0 += CK_GB * WAVE) {
-        idx_load(b, idx, nchoice, c0, E, lane);
+        idx_load(b, idx, nchoice, c0, lane);
         base = idx_scan<PASS>(b, c0, nchoice, e, E, first, base, list, lane);
     }
     return base;
@@ -106,13 +108,13 @@ Q8S_DEV int idx_gather(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice
 // the layout spends as few instructions per weight byte as it can:
 //   * every lane holds one whole block of each weight row, so its 8 v_dot4
 //     give an exact block sum with no cross-lane join, and one multiply by
-//     ws*xs scales it: the rows are read as whole 1 KB spans a load (lane l
-//     takes 16-byte chunks l and 64 + l) and lane pairs then trade halves,
-//     leaving block l/2 in even lanes and block 32 + l/2 in odd ones;
+//     ws*xs scales it: the rows are read as whole 1 KB spans a load, lanes l
+//     and l + 32 taking the two halves of blocks l and 32 + l, and one
+//     lane-half swap a word (v_permlane32_swap) then leaves block l in lane l;
 //   * the 8 partial sums of a pair of choices (2 choices x 2 rows x gate/up)
 //     are reduced across the wave together, each exchange step halving the
-//     values a lane keeps (10 exchanges instead of 8 x 6), ending with every
-//     value in one group of 8 lanes;
+//     values a lane keeps (10 exchanges instead of 8 x 6; the first two are
+//     lane-half swaps), ending with every value in one group of 8 lanes;
 //   * each wave requests its rows first (they stay in its registers); wave 0
 //     then gathers up to CK_NA of the expert's choices (choice order) and the
 //     workgroup stages their Q8_0 activation rows in LDS, so the gather and
@@ -130,22 +132,24 @@ constexpr int CKB_MAXD = 64 * QB;       // a block a lane
 // Sum of v[i] over the wave for eight values at once: lane l ends holding the
 // sum of v[4*b5 + 2*b4 + b3], b5, b4, b3 bits 5, 4, 3 of l (every lane of
 // its group of 8 holds it).
+// The first two steps are gfx950's lane-half swaps: swapping the upper 32
+// lanes of v[i] with the lower 32 of v[i + 4] leaves the lower lanes both
+// halves' v[i] and the upper lanes both halves' v[i + 4]; the 16-lane swap
+// does the same between rows of 16.
 Q8S_DEV float wave_sum8(const float (&v)[8], int lane)
 {
-    const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+    const bool h3 = lane & 8;
     float w4[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const float send = h5 ? v[i] : v[i + 4];
-        const float keep = h5 ? v[i + 4] : v[i];
-        w4[i] = keep + __shfl_xor(send, 32);
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+        w4[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
     float w2[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
-        const float send = h4 ? w4[i] : w4[i + 2];
-        const float keep = h4 ? w4[i + 2] : w4[i];
-        w2[i] = keep + __shfl_xor(send, 16);
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(w4[i]), __float_as_uint(w4[i + 2]), false, false);
+        w2[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
     // lanes i and 15-i of a row of 16 differ in bit 3
     const float send = h3 ? w2[0] : w2[1];
@@ -176,9 +180,11 @@ Q8S_DEV int block_dot2(const i32x4 (&w)[2], const i32x4 (&a)[2], const i32x4 (&l
 
 // X2: two-word activations (the low words xl staged beside the words; a
 // block's sum is block_dot2, scaled by ws * xs / 128), CK_NA / 2 choices a
-// pass so the staged rows take the one-word kernel's LDS.
+// pass so the staged rows take the one-word kernel's LDS.  One word fits 128
+// registers, four workgroups a CU (measured 75.2 against 78.7 us at three,
+// for the 64-row chunk of the 128-expert block); two words take three.
 template <bool X2>
-__global__ void __launch_bounds__(CKB_NW * WAVE)
+__global__ void __launch_bounds__(CKB_NW * WAVE, X2 ? 3 : 4)
     k_chunk_gate_up(const int8_t *__restrict__ xq, const float *__restrict__ xs, const int8_t *__restrict__ Wgq,
                     const float *__restrict__ Wgs, const int8_t *__restrict__ Wuq, const float *__restrict__ Wus,
                     const int32_t *__restrict__ idx, int nchoice, int k, int d, int dff, int E, float *__restrict__ h,
@@ -195,11 +201,13 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
     const int e = blockIdx.y;
     const int o0 = blockIdx.x * CKB_T;
     const int nb = d >> 5, nch = d >> 4;
-    const bool odd = lane & 1;
-    const int blk = odd ? 32 + (lane >> 1) : (lane >> 1);  // the lane's block after the trade
-    const int bl = min(blk, nb - 1);   // (blocks past the row: the last one, with zero activations)
-    const bool inb = blk < nb;
-    const int c0 = min(lane, nch - 1), c1 = min(64 + lane, nch - 1);  // the chunks the lane loads
+    // lane l ends holding block l: it loads the halves 2l, 64 + 2l (l < 32)
+    // or the halves 2l - 63, 2l + 1 (l >= 32), so each load still covers 1 KB
+    // of a row, and the lanes 32 apart then swap halves
+    const int bl = min(lane, nb - 1);   // (blocks past the row: the last one, with zero activations)
+    const bool inb = lane < nb;
+    const int f0 = lane < 32 ? 2 * lane : 2 * lane - 63;
+    const int c0 = min(f0, nch - 1), c1 = min(64 + f0, nch - 1);  // the chunks the lane loads
 
     // the wave's rows o0 + CKB_U*wid + u; the invalid bucket (e == E) writes
     // zeros and reads expert 0's first rows (served from cache after the first)
@@ -217,15 +225,15 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
         gs[u] = ld_stream_f32(Wgs + row * nb + bl);
         us[u] = ld_stream_f32(Wus + row * nb + bl);
     }
-    // the trade: even lanes give chunk 64 + l and take their partner's chunk
-    // l + 1; odd lanes give chunk l and take their partner's chunk 63 + l
+    // the trade: lane l < 32 gives its second load (half of block 32 + l) to
+    // lane l + 32 and takes that lane's first (the other half of block l)
     auto trade = [&](i32x4 (&w)[2]) {
-        i32x4 got;
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            got[i] = dpp_i<DPP_XOR1>(odd ? w[0][i] : w[1][i]);
-        w[0] = odd ? got : w[0];
-        w[1] = odd ? w[1] : got;
+        for (int i = 0; i < 4; i++) {
+            const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)w[0][i], (uint32_t)w[1][i], false, false);
+            w[0][i] = (int)r[0];
+            w[1][i] = (int)r[1];
+        }
     };
 #pragma unroll
     for (int u = 0; u < CKB_U; u++) {
@@ -235,7 +243,7 @@ __global__ void __launch_bounds__(CKB_NW * WAVE)
     for (int first = 0;; first += NA) {
         if (wid == 0) {
             IdxBatch ib;
-            idx_load(ib, idx, nchoice, 0, E, lane);
+            idx_load(ib, idx, nchoice, 0, lane);
             const int tot = idx_gather<NA>(ib, idx, nchoice, e, E, first, list, lane);
             if (lane == 0)
                 totsh = tot;
@@ -352,7 +360,7 @@ __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
     int *list = lists[wid];
 
     IdxBatch ib;
-    idx_load(ib, idx, nchoice, 0, E, lane);
+    idx_load(ib, idx, nchoice, 0, lane);
     RowSlice<C> w[SW];
 #pragma unroll
     for (int u = 0; u < SW; u++) {
@@ -361,7 +369,7 @@ __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
     }
     for (int first = 0;; first += CK_PASS) {
         if (first > 0)
-            idx_load(ib, idx, nchoice, 0, E, lane);
+            idx_load(ib, idx, nchoice, 0, lane);
         const int total = idx_gather(ib, idx, nchoice, e, E, first, list, lane);
         const int n = min(CK_PASS, max(0, total - first));
         if (n == 0)
@@ -465,7 +473,7 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
     for (int first = 0;; first += CK_NA) {
         if (wid == 0) {
             IdxBatch ib;
-            idx_load(ib, idx, nchoice, 0, E, lane);
+            idx_load(ib, idx, nchoice, 0, lane);
             const int tot = idx_gather<CK_NA>(ib, idx, nchoice, e, E, first, list, lane);
             if (lane == 0)
                 totsh = tot;
@@ -712,7 +720,7 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
     for (int first = 0;; first += TM) {
         if (wid == 0) {
             IdxBatch ib;
-            idx_load(ib, idx, nchoice, 0, E, lane);
+            idx_load(ib, idx, nchoice, 0, lane);
             const int tot = idx_gather<TM>(ib, idx, nchoice, e, E, first, list, lane);
             if (lane == 0)
                 totsh = tot;
