@@ -404,8 +404,8 @@ __global__ void __launch_bounds__((CkDownShape<LPR, C>::NW * WAVE))
 // groups of 8 lanes per weight row, so one load covers 8 rows x 128
 // contiguous bytes; lane pairs trade halves so every lane holds C/2 whole
 // blocks (blocks (l>>1) + 4*(l&1) + 8m of lane l of the group); the hidden
-// rows of up to CK_NA choices are staged in LDS; four partial sums (2 choices
-// x 2 row slots) are reduced across the 8 lanes together.
+// rows of up to CK_NA choices are staged in LDS; a choice's two partial sums
+// (2 row slots) are reduced across the 8 lanes together.
 constexpr int CKD_NW = 4;
 constexpr int CKD_U = 2;                       // row slots a wave: 8 rows each
 constexpr int CKD_T = CKD_NW * CKD_U * 8;      // outputs a workgroup
@@ -507,50 +507,42 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
             }
         }
         __syncthreads();
-        for (int cg = 0; cg < n; cg += 2) {
-            float v[2][CKD_U];
+        // one choice a step (two at once held twice the activation registers
+        // and kept the kernel at three workgroups a CU)
+        for (int q = 0; q < n; q++) {
+            float v[CKD_U];
 #pragma unroll
-            for (int q = 0; q < 2; q++) {
-                const int qq = min(cg + q, n - 1);
+            for (int u = 0; u < CKD_U; u++)
+                v[u] = 0.0f;
 #pragma unroll
-                for (int u = 0; u < CKD_U; u++)
-                    v[q][u] = 0.0f;
+            for (int m = 0; m < M; m++) {
+                i32x4 a[2], al[2];
+                a[0] = *reinterpret_cast<const i32x4 *>(&act[q][QB * blk[m]]);
+                a[1] = *reinterpret_cast<const i32x4 *>(&act[q][QB * blk[m] + 16]);
+                if constexpr (X2) {
+                    al[0] = *reinterpret_cast<const i32x4 *>(&actl[q][QB * blk[m]]);
+                    al[1] = *reinterpret_cast<const i32x4 *>(&actl[q][QB * blk[m] + 16]);
+                }
+                float sx = asc[q][blk[m]];
+                sx = inb[m] ? sx : 0.0f;
 #pragma unroll
-                for (int m = 0; m < M; m++) {
-                    i32x4 a[2], al[2];
-                    a[0] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * blk[m]]);
-                    a[1] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * blk[m] + 16]);
-                    if constexpr (X2) {
-                        al[0] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * blk[m]]);
-                        al[1] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * blk[m] + 16]);
-                    }
-                    const float sx = inb[m] ? asc[qq][blk[m]] : 0.0f;
-#pragma unroll
-                    for (int u = 0; u < CKD_U; u++) {
-                        const i32x4 wb[2] = {w[u][2 * m], w[u][2 * m + 1]};
-                        if constexpr (X2)
-                            v[q][u] = __builtin_fmaf((float)block_dot2(wb, a, al), (ws[u][m] * sx) * 0.0078125f,
-                                                     v[q][u]);
-                        else
-                            v[q][u] = __builtin_fmaf((float)block_dot(wb, a), ws[u][m] * sx, v[q][u]);
-                    }
+                for (int u = 0; u < CKD_U; u++) {
+                    const i32x4 wb[2] = {w[u][2 * m], w[u][2 * m + 1]};
+                    if constexpr (X2)
+                        v[u] = __builtin_fmaf((float)block_dot2(wb, a, al), (ws[u][m] * sx) * 0.0078125f, v[u]);
+                    else
+                        v[u] = __builtin_fmaf((float)block_dot(wb, a), ws[u][m] * sx, v[u]);
                 }
             }
-            // the four values over the 8 lanes: bit 2 keeps a choice, bit 1
-            // a row slot, bit 0 sums
-            const bool b2 = lig & 4, b1 = lig & 2;
-            float w2[2];
-#pragma unroll
-            for (int u = 0; u < 2; u++) {
-                const float send = b2 ? v[0][u] : v[1][u];
-                w2[u] = (b2 ? v[1][u] : v[0][u]) + dpp_f<DPP_HALF_MIRROR>(send);
-            }
-            const float send = b1 ? w2[0] : w2[1];
-            float r = (b1 ? w2[1] : w2[0]) + dpp_f<DPP_XOR2>(send);
+            // the two values over the 8 lanes: bit 2 keeps a row slot, bits 1
+            // and 0 sum
+            const bool b2 = lig & 4;
+            float r = (b2 ? v[1] : v[0]) + dpp_f<DPP_HALF_MIRROR>(b2 ? v[0] : v[1]);
+            r += dpp_f<DPP_XOR2>(r);
             r += dpp_f<DPP_XOR1>(r);
-            const int q = b2 ? 1 : 0, u = b1 ? 1 : 0;
-            if (!odd && cg + q < n && orow[u] < d)
-                pa[(int64_t)list[cg + q] * d + orow[u]] = r;
+            const int u = b2 ? 1 : 0;
+            if ((lig & 3) == 0 && orow[u] < d)
+                pa[(int64_t)list[q] * d + orow[u]] = r;
         }
         if (total <= first + CK_NA)
             break;
