@@ -111,8 +111,8 @@ Q8S_DEV int idx_gather(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice
 //     ws*xs scales it: the rows are read as whole 1 KB spans a load, lanes l
 //     and l + 32 taking the two halves of blocks l and 32 + l, and one
 //     lane-half swap a word (v_permlane32_swap) then leaves block l in lane l;
-//   * the 8 partial sums of a pair of choices (2 choices x 2 rows x gate/up)
-//     are reduced across the wave together, each exchange step halving the
+//   * the 8 partial sums of a choice (4 rows x gate/up) are reduced across
+//     the wave together, each exchange step halving the
 //     values a lane keeps (10 exchanges instead of 8 x 6; the first two are
 //     lane-half swaps), ending with every value in one group of 8 lanes;
 //   * each wave requests its rows first (they stay in its registers); wave 0
@@ -279,46 +279,38 @@ __global__ void __launch_bounds__(CKB_NW * WAVE, X2 ? 3 : 4)
             }
         }
         __syncthreads();
-        for (int cg = 0; cg < n; cg += 2) {
-            i32x4 a[2][2], al[2][2];
-            float sx[2];
+        static_assert(CKB_U == 4, "a choice's four row pairs x gate/up = 8 values a reduction");
+        for (int q = 0; q < n; q++) {
+            i32x4 a[2], al[2];
+            a[0] = *reinterpret_cast<const i32x4 *>(&act[q][QB * bl]);
+            a[1] = *reinterpret_cast<const i32x4 *>(&act[q][QB * bl + 16]);
+            if constexpr (X2) {
+                al[0] = *reinterpret_cast<const i32x4 *>(&actl[q][QB * bl]);
+                al[1] = *reinterpret_cast<const i32x4 *>(&actl[q][QB * bl + 16]);
+            }
+            float sx = asc[q][bl];
+            sx = inb ? sx : 0.0f;
+            if constexpr (X2)
+                sx *= 0.0078125f;
+            // one choice a step, its 4 row pairs x gate/up = 8 values a
+            // reduction (a choice's activations in registers, not two's)
+            float v[8];
 #pragma unroll
-            for (int q = 0; q < 2; q++) {
-                const int qq = min(cg + q, n - 1);
-                a[q][0] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * bl]);
-                a[q][1] = *reinterpret_cast<const i32x4 *>(&act[qq][QB * bl + 16]);
+            for (int u = 0; u < CKB_U; u++) {
                 if constexpr (X2) {
-                    al[q][0] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * bl]);
-                    al[q][1] = *reinterpret_cast<const i32x4 *>(&actl[qq][QB * bl + 16]);
+                    v[2 * u] = (float)block_dot2(gq[u], a, al) * (gs[u] * sx);
+                    v[2 * u + 1] = (float)block_dot2(uq[u], a, al) * (us[u] * sx);
+                } else {
+                    v[2 * u] = (float)block_dot(gq[u], a) * (gs[u] * sx);
+                    v[2 * u + 1] = (float)block_dot(uq[u], a) * (us[u] * sx);
                 }
-                sx[q] = inb ? asc[qq][bl] : 0.0f;
-                if constexpr (X2)
-                    sx[q] *= 0.0078125f;
             }
-            // rows in pairs: 2 choices x 2 rows x gate/up = 8 values a reduction
-#pragma unroll
-            for (int u0 = 0; u0 < CKB_U; u0 += 2) {
-                float v[8];
-#pragma unroll
-                for (int q = 0; q < 2; q++)
-#pragma unroll
-                    for (int u = 0; u < 2; u++) {
-                        if constexpr (X2) {
-                            v[4 * q + 2 * u] = (float)block_dot2(gq[u0 + u], a[q], al[q]) * (gs[u0 + u] * sx[q]);
-                            v[4 * q + 2 * u + 1] = (float)block_dot2(uq[u0 + u], a[q], al[q]) * (us[u0 + u] * sx[q]);
-                        } else {
-                            v[4 * q + 2 * u] = (float)block_dot(gq[u0 + u], a[q]) * (gs[u0 + u] * sx[q]);
-                            v[4 * q + 2 * u + 1] = (float)block_dot(uq[u0 + u], a[q]) * (us[u0 + u] * sx[q]);
-                        }
-                    }
-                const float r = wave_sum8(v, lane);
-                // lanes with bit 3 clear hold a gate sum; the up sum of the
-                // same (choice, row) is in lane 15 - i of the row
-                const float up = dpp_f<DPP_MIRROR>(r);
-                const int q = (lane >> 5) & 1, u = (lane >> 4) & 1;
-                if ((lane & 15) == 0 && cg + q < n)
-                    h[(int64_t)list[cg + q] * dff + o0 + CKB_U * wid + u0 + u] = e < E ? silu(r) * up : 0.0f;
-            }
+            const float r = wave_sum8(v, lane);
+            // lanes with bit 3 clear hold a gate sum (row pair (lane >> 4) & 3);
+            // the up sum of the same row is in lane 15 - i of the row
+            const float up = dpp_f<DPP_MIRROR>(r);
+            if ((lane & 15) == 0)
+                h[(int64_t)list[q] * dff + o0 + CKB_U * wid + ((lane >> 4) & 3)] = e < E ? silu(r) * up : 0.0f;
         }
         if (total <= first + NA)
             break;
