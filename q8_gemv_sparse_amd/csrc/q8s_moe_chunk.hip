@@ -580,7 +580,8 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
 //     registers, 16 bytes a lane (lane (j, g) takes bytes 16g .. 16g+15 of
 //     a 64-byte span of row j: half of block 2p or 2p+1), GW_BU blocks ahead
 //     of their use, the rows' scales 16 bytes a load; lanes 32 apart then
-//     trade halves so each holds 8 bytes of one block, the MFMA's fragment.
+//     swap halves (v_permlane32_swap) so each holds 8 bytes of block 2p and
+//     8 of block 2p+1, the MFMA's fragments.
 //     Both buffers' first fetches are issued before the choice list is
 //     scanned, and each buffer is refilled as soon as its blocks are used;
 //   * A operand: the rows of up to TM of the expert's choices (gathered in
@@ -679,19 +680,17 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
             }
         }
     };
-    // the weight fragment of block b0 + u, stream q
-    auto frag = [&](int s, int q, int u) -> long {
-        // lane (j, g) loaded bytes 16g .. 16g+15 of blocks 2p, 2p+1 of row j
-        // (p = u / 2): lane groups 0, 1 hold halves of block 2p, groups 2, 3
-        // of block 2p+1.  Lanes 32 apart trade 8-byte halves, so each lane
-        // ends holding 8 bytes of either block: group g has bytes
-        // 16 (g & 1) + 8 (g >> 1) .. +7 of the block.
-        const i32x4 v = bf[s][q][u >> 1];
-        const bool low = g < 2;
-        const int r0 = __shfl_xor(low ? v[2] : v[0], 32), r1 = __shfl_xor(low ? v[3] : v[1], 32);
-        const bool mine = (u & 1) == (low ? 0 : 1);
-        const int w0 = mine ? ((u & 1) ? v[2] : v[0]) : r0, w1 = mine ? ((u & 1) ? v[3] : v[1]) : r1;
-        return (long)(uint32_t)w0 | ((long)w1 << 32);
+    // the weight fragments of blocks b0 + 2p and b0 + 2p + 1, stream q: lane
+    // (j, g) loaded bytes 16g .. 16g+15 of both (groups 0, 1 hold halves of
+    // block 2p, groups 2, 3 of block 2p+1); one lane-half swap of each word
+    // pair (v_permlane32_swap: lanes 32 apart) leaves every lane 8 bytes of
+    // either block, group g bytes 16 (g & 1) + 8 (g >> 1) .. +7 of it
+    auto frag2 = [&](int s, int q, int p, long &f0, long &f1) {
+        const i32x4 v = bf[s][q][p];
+        const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)v[0], (uint32_t)v[2], false, false);
+        const auto c = __builtin_amdgcn_permlane32_swap((uint32_t)v[1], (uint32_t)v[3], false, false);
+        f0 = (long)(uint32_t)a[0] | ((long)(uint32_t)c[0] << 32);
+        f1 = (long)(uint32_t)a[1] | ((long)(uint32_t)c[1] << 32);
     };
     // both buffers' first fetches do not wait for the choice list (nor for
     // the staging of the choices' rows)
@@ -777,15 +776,21 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
                     for (int i = 0; i < 4; i++)
                         acc[q][t][i] = 0.0f;
             auto contract = [&](int s, int b0) {
+                long wf2[NB][2];
 #pragma unroll
                 for (int u = 0; u < GW_BU; u++) {
                     const int b = b0 + u;
                     if (b >= nb)
                         break;
                     long wf[NB];
+                    if ((u & 1) == 0) {
+#pragma unroll
+                        for (int q = 0; q < NB; q++)
+                            frag2(s, q, u >> 1, wf2[q][0], wf2[q][1]);
+                    }
 #pragma unroll
                     for (int q = 0; q < NB; q++)
-                        wf[q] = frag(s, q, u);
+                        wf[q] = wf2[q][u & 1];
                     const int off = 16 * ((2 * b + chx) ^ j) + cho;
 #pragma unroll
                     for (int t = 0; t < TT; t++) {
