@@ -687,19 +687,22 @@ class ChunkBlock(MoeBlock):
         torch.cuda.synchronize()
 
     def step(self, c):
-        # sequential: the dense projection on a parallel graph branch (a
-        # second stream forked after the norm, joined at the step's end)
-        # measured 173.2 against 161.7 us a step -- the fork and join cost
-        # more than the overlap gains
-        super().step(c)
-        self._dense(c)
+        # the dense projection reads the same normed rows as the router, so
+        # one call runs both, the top-K inside the projection's launch (a
+        # parallel graph branch for the projection instead, forked after the
+        # norm and joined at the step's end, measured 173.2 against 161.7 us
+        # a step: the fork and join cost more than the overlap gained)
+        self._norm(c)
+        self._route_dense(c)
+        self._gate_up(c, None)
+        self._down(c)
 
-    def _dense(self, c):
-        Dq, Ds = self.D[c % self.copies]
-        if self.act == "x2":
-            self.q8.q8_gemv_x2(Dq, Ds, self.xq, self.xl, self.xs, y=self.dense_out)
-        else:
-            self.q8.q8_gemv(Dq, Ds, xq=self.xq, xs=self.xs, y=self.dense_out, act=self.q8.ACT_INT8)
+    def _route_dense(self, c):
+        W, (Dq, Ds) = self.W[c % self.copies], self.D[c % self.copies]
+        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
+        self.q8.moe_route_topk_gemv(self.y, W[0], self.k, Dq, Ds, self.xq, self.xs,
+                                    xl=self.xl if self.act == "x2" else None, idx=idx, wts=wts, y=self.dense_out,
+                                    scratch=self.rscratch)
 
     def _norm(self, c):
         if self.act != "x2":
@@ -730,13 +733,6 @@ class ChunkBlock(MoeBlock):
             self.q8.moe_down_combine(W[5], W[6], idx, wts, self.E, hq=self.hq, hs=self.hs, y=self.out,
                                      act=self.q8.ACT_INT8, scratch=self.dscratch)
 
-    def _mixture(self, c):
-        W = self.W[c % self.copies]
-        idx, wts = self.idx[c % self.copies], self.wts[c % self.copies]
-        self.q8.moe_route_topk(self.y, W[0], self.k, idx=idx, wts=wts, scratch=self.rscratch)
-        self._gate_up(c, None)
-        self._down(c)
-
     def launch_dominant(self, c):
         # the grouped gate-up kernel alone: the float32 hidden rows, without
         # the quantise pass the step runs after it
@@ -748,16 +744,11 @@ class ChunkBlock(MoeBlock):
     def stages(self):
         """The chunk's calls in step order, each timed alone over the copies
         (the routing each copy's last step left in place)."""
-        q8 = self.q8
-        d, dff, E, k = self.d, self.dff, self.E, self.k
+        d, dff, E = self.d, self.dff, self.E
         q8b = lambda n_out, n_in: n_out * n_in + n_out * (n_in // 32) * 4
         u = lambda c: self.distinct_experts(c)
         C = self.copies
         avg_u = sum(u(c) for c in range(C)) / C
-
-        def route(c):
-            W = self.W[c % C]
-            q8.moe_route_topk(self.y, W[0], k, idx=self.idx[c % C], wts=self.wts[c % C], scratch=self.rscratch)
 
         x2 = self.act == "x2"
         sfx = "_x2" if x2 else ""
@@ -765,13 +756,13 @@ class ChunkBlock(MoeBlock):
         return [("add_rmsnorm_q8%s (k_add_rmsnorm_q8%s, %d rows)" % (" + q8_quantize_rows_x2" if x2 else "",
                                                                     " + k_quantize_rows_x2" if x2 else "", rows),
                  self._norm, 0),
-                ("moe_route_topk (k_logits_tile + k_topk)", route, E * d * 4),
+                ("moe_route_topk_gemv%s: router + dense %d x %d -> %d (k_logits_tile + k_gemm_i8 carrying the "
+                 "top-K)" % (" (two words)" if x2 else "", rows, d, n_dense), self._route_dense,
+                 E * d * 4 + self.dense_bytes),
                 ("moe_gate_up%s (%s + k_quantize_rows%s)" % (sfx, self.gu_kernel, sfx),
                  lambda c: self._gate_up(c, None), int(avg_u * 2 * q8b(dff, d))),
                 ("moe_down_combine%s (%s + k_chunk_combine)" % (sfx, self.dn_kernel), self._down,
-                 int(avg_u * q8b(d, dff))),
-                ("q8_gemv%s dense %d x %d -> %d (k_gemm_i8)" % (sfx, rows, d, n_dense), self._dense,
-                 self.dense_bytes)]
+                 int(avg_u * q8b(d, dff)))]
 
     def verify(self):
         import oracle

@@ -185,6 +185,37 @@ Q8S_API int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_
                    int32_t *idx, float *wts, void *scratch, size_t scratch_bytes, void *stream);
 
 /*
+ * moe_route_topk_gemv -- moe_route_topk of a chunk's rows and a dense Q8_0
+ * projection of the same rows in one call (a prefill chunk runs each
+ * projection of the step over the block of rows, codegen_cuda/lane/mod.rs
+ * module doc; the router and a projection that reads the same normed rows,
+ * such as a shared expert's gate and up or a dense layer beside the mixture,
+ * are independent of each other):
+ *   idx, wts      exactly as moe_route_topk(x, Wr, ...) writes them
+ *   y = D . x     exactly as q8_gemv(Dq, Ds, n_out, d, xq, xs, act = INT8)
+ *                 (act 1) or q8_gemv_x2(Dq, Ds, n_out, d, xq, xl, xs) (act 2)
+ *                 writes it, each element bit for bit
+ * The top-K runs inside the projection's launch: its workgroups rank the
+ * rows' logits while their first weight tiles are in flight, so the call is
+ * two launches (logits, then projection + top-K) where the two calls are
+ * three.  This holds from 5 rows up with E <= 256; otherwise the call runs
+ * the two calls' launches in turn, with the same results.
+ * x: device f32 [rows, d] (the router's input); Wr: device f32 [E, d];
+ * idx/wts: device int32/f32 [rows, k]; Dq: device int8 [n_out, d]; Ds:
+ * device f32 [n_out, d/32]; xq/xs: device int8 [rows, d] and f32
+ * [rows, d/32], x's Q8_0 form (add_rmsnorm_q8's epilogue, q8_quantize_rows
+ * or q8_quantize_rows_x2); xl: device int8 [rows, d], the low words, for
+ * act 2 and NULL for act 1; y: device f32 [rows, n_out].  act: 1 or 2 (the
+ * f32 mode is refused with Q8S_EUNSUPPORTED).  scratch as moe_route_topk.
+ * Limits: those of moe_route_topk and q8_gemv; every output is disjoint
+ * from every input.
+ */
+Q8S_API int moe_route_topk_gemv(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k,
+                                int32_t *idx, float *wts, const int8_t *Dq, const float *Ds, int64_t n_out,
+                                const int8_t *xq, const int8_t *xl, const float *xs, float *y, int act,
+                                void *scratch, size_t scratch_bytes, void *stream);
+
+/*
  * moe_gate_up -- each kept expert's gate and up projections with SiLU gating
  * (fn emit_moe_forward; struct MoeWeights stacked rows, expert base taken from
  * idx on the device):

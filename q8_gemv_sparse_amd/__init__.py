@@ -27,7 +27,7 @@ __all__ = [
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
     "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2", "moe_ffn_block_noalloc", "NOALLOC_SCRATCH_BYTES",
     "moe_ffn_stack", "FN_STACK", "moe_gate_up_x2", "moe_down_combine_x2", "q8s_moe_path", "PATH_ROWS",
-    "PATH_GROUPED", "PATH_GROUPED_MFMA",
+    "PATH_GROUPED", "PATH_GROUPED_MFMA", "moe_route_topk_gemv",
 ]
 
 ACT_F32 = 0
@@ -59,6 +59,8 @@ _SIGS = {
     "q8_quantize_rows": [_p, _i64, _i64, _p, _p, _p],
     "add_rmsnorm_q8": [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p],
     "moe_route_topk": [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p],
+    "moe_route_topk_gemv": [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _i64, _p, _p, _p, _p, ctypes.c_int, _p,
+                            _sz, _p],
     "moe_gate_up": [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p, ctypes.c_int, _p],
     "moe_down_combine": [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, ctypes.c_int, _p, _sz, _p],
     "moe_ffn_block": [_p, _p, _p, ctypes.c_float, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p, _p,
@@ -328,6 +330,33 @@ def moe_route_topk(x, Wr, k, idx=None, wts=None, scratch=None, stream=None):
     _check(_lib.moe_route_topk(_ptr(x), _ptr(Wr), rows, d, E, k, _ptr(idx), _ptr(wts), _ptr(scratch),
                                scratch.numel(), _stream(stream)))
     return idx, wts
+
+
+def moe_route_topk_gemv(x, Wr, k, Dq, Ds, xq, xs, xl=None, idx=None, wts=None, y=None, scratch=None, stream=None):
+    """moe_route_topk(x, Wr, k) and the dense projection of the same rows' Q8_0
+    form (q8_gemv in one word, or q8_gemv_x2 when the low words ``xl`` are
+    given) in one call: (idx, wts, y)."""
+    _dev(x, torch.float32, "x"); _dev(Wr, torch.float32, "Wr")
+    _dev(Dq, torch.int8, "Dq"); _dev(Ds, torch.float32, "Ds")
+    _dev(xq, torch.int8, "xq"); _dev(xs, torch.float32, "xs")
+    if xl is not None:
+        _dev(xl, torch.int8, "xl")
+    E, d = Wr.shape
+    rows = x.numel() // d
+    n_out = Dq.shape[0]
+    dev = x.device
+    f = lambda t, shape, dt: t if t is not None else torch.empty(shape, dtype=dt, device=dev)
+    idx = f(idx, (rows, k), torch.int32); wts = f(wts, (rows, k), torch.float32)
+    y = f(y, (rows, n_out), torch.float32)
+    if scratch is None:
+        scratch = torch.empty(q8s_scratch_bytes(FN_ROUTE, rows, d, 32, E, k), dtype=torch.uint8, device=dev)
+    _dev(idx, torch.int32, "idx"); _dev(wts, torch.float32, "wts"); _dev(y, torch.float32, "y")
+    _dev(scratch, torch.uint8, "scratch")
+    act = ACT_X2 if xl is not None else ACT_INT8
+    _check(_lib.moe_route_topk_gemv(_ptr(x), _ptr(Wr), rows, d, E, k, _ptr(idx), _ptr(wts), _ptr(Dq), _ptr(Ds),
+                                    n_out, _ptr(xq), _ptr(xl), _ptr(xs), _ptr(y), act, _ptr(scratch),
+                                    scratch.numel(), _stream(stream)))
+    return idx, wts, y
 
 
 def moe_gate_up(Wgq, Wgs, Wuq, Wus, idx, E, x=None, xq=None, xs=None, h=None, hq=None, hs=None, act=ACT_F32,

@@ -112,8 +112,8 @@ int check_act(const char *fn, int act)
     if (act == 2)
         return fail(Q8S_EUNSUPPORTED,
                     "%s: act = 2 (two-word int8 activations) is served by q8_quantize_rows_x2, q8_gemv_x2, "
-                    "add_rmsnorm_gemv_x2, moe_gate_up_x2, moe_topk_gate_up_x2, moe_down_combine_x2, moe_ffn_block "
-                    "and moe_ffn_stack", fn);
+                    "add_rmsnorm_gemv_x2, moe_gate_up_x2, moe_topk_gate_up_x2, moe_down_combine_x2, moe_route_topk_gemv, "
+                    "moe_ffn_block and moe_ffn_stack", fn);
     return fail(Q8S_EUNSUPPORTED, "%s: unknown activation mode act = %d", fn, act);
 }
 
@@ -318,6 +318,56 @@ int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_t d, int
         return rc;
     clear_stale();
     return launched(q8s::route_launch(x, Wr, rows, d, E, k, idx, wts, scratch, as_stream(stream)), fn);
+}
+
+int moe_route_topk_gemv(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
+                        float *wts, const int8_t *Dq, const float *Ds, int64_t n_out, const int8_t *xq,
+                        const int8_t *xl, const float *xs, float *y, int act, void *scratch, size_t scratch_bytes,
+                        void *stream)
+{
+    const char *fn = "moe_route_topk_gemv";
+    int rc;
+    if (act != Q8S_ACT_INT8 && act != 2)
+        return fail(act == Q8S_ACT_F32 ? Q8S_EUNSUPPORTED : Q8S_EINVAL,
+                    "%s: act = %d: the projection reads the rows' Q8_0 form, in one word (act 1) or two (act 2)",
+                    fn, act);
+    if ((act == 2) != (xl != nullptr))
+        return fail(Q8S_EINVAL, "%s: `xl` (the low words) is given for act 2 and only then", fn);
+    if ((rc = check_moe_shape(fn, rows, d, 32, E, k)) || (rc = check_count(fn, "n_out", n_out, INT32_MAX / 2)))
+        return rc;
+    const size_t n = (size_t)(rows * d), nb = (size_t)(d / 32);
+    std::vector<Span> ins = {{x, n * 4, "x"},
+                             {Wr, (size_t)(E * d) * 4, "Wr"},
+                             {Dq, (size_t)n_out * (size_t)d, "Dq"},
+                             {Ds, (size_t)n_out * nb * 4, "Ds"},
+                             {xq, n, "xq"},
+                             {xs, (size_t)rows * nb * 4, "xs"}};
+    if (act == 2)
+        ins.push_back({xl, n, "xl"});
+    std::vector<Span> outs = {{idx, (size_t)(rows * k) * 4, "idx"},
+                              {wts, (size_t)(rows * k) * 4, "wts"},
+                              {y, (size_t)rows * (size_t)n_out * 4, "y"}};
+    const size_t need = q8s::route_scratch_bytes(rows, E);
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)))
+        return rc;
+    if (!scratch || scratch_bytes < need)
+        return fail(Q8S_ESCRATCH, "%s: scratch of %zu bytes given, %zu needed (the logits)", fn,
+                    scratch ? scratch_bytes : (size_t)0, need);
+    if (reinterpret_cast<uintptr_t>(scratch) % 256 != 0)
+        return fail(Q8S_EALIGN, "%s: `scratch` is not 256-byte aligned", fn);
+    outs.push_back({scratch, need, "scratch"});
+    if ((rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    const hipStream_t st = as_stream(stream);
+    const q8s::GemvArgs a{Dq, Ds, n_out, d, nullptr, xq, xs, rows, y, act, xl};
+    double *logits = reinterpret_cast<double *>(scratch);
+    if (!q8s::gemv_topk_fused(rows, E, act)) {
+        const hipError_t err = q8s::route_launch(x, Wr, rows, d, E, k, idx, wts, scratch, st);
+        return launched(err != hipSuccess ? err : q8s::gemv_launch(a, st), fn);
+    }
+    const hipError_t err = q8s::logits_launch(x, Wr, rows, d, E, logits, st);
+    return launched(err != hipSuccess ? err : q8s::gemv_topk_launch(a, logits, rows, E, k, idx, wts, st), fn);
 }
 
 int moe_route_topk_q8(const float *x, const int8_t *xq, const float *xs, const int8_t *Wrq, const float *Wrs,

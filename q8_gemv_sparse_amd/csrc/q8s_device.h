@@ -626,6 +626,36 @@ Q8S_DEV void topk_load(TopkLds &t, const double *__restrict__ lr, int E)
 // Ranking all E in one pass with no candidate list keeps it to one LDS pass
 // between two barriers; an exact compare of all E^2 pairs in double measured
 // several microseconds on a full workgroup.
+// topk_load's LDS writes for one logit a thread, already in a register:
+// thread t holds logit t (the workgroup has at least E threads).
+Q8S_DEV void topk_put(TopkLds &t, double v, int E)
+{
+    const int i = threadIdx.x;
+    if (i < E) {
+        const uint64_t c = route_code(v);
+        t.L[i] = v;
+        t.ck[i] = (uint32_t)(c >> 32);
+        t.lo[i] = (uint32_t)c;
+    } else if (i < ((E + 3) & ~3)) {
+        t.ck[i] = 0u;
+    }
+}
+
+// The top-K of `rows` rows of E logits (E <= TOPK_LDS_E), ridden on another
+// launch's workgroups; idx/wts as k_topk writes them.
+struct TopkRider {
+    const double *logits;
+    int rows, E, k;
+    int32_t *idx;
+    float *wts;
+};
+
+// A row's kept choices and logits in rank order, for route_finish.
+struct TopkKept {
+    double kl[32];
+    int ch[32];
+};
+
 Q8S_DEV void topk_select(TopkLds &t, int E, int k)
 {
     const int S = lanes_per_item(E);

@@ -296,7 +296,10 @@ struct GemmLds {
     int8_t l[X2 ? TM : 1][GEMM_ROW];
     float ws[GEMM_KB][GEMM_TN + 1];
     float xs[GEMM_KB][TM + 4];
-    float part[GEMM_NW][TM][GEMM_TN + 4];  // row pitch 20: a wave's 64 writes hit 64 banks
+    union {
+        float part[GEMM_NW][TM][GEMM_TN + 4];  // row pitch 20: a wave's 64 writes hit 64 banks
+        TopkLds tk;                            // the top-K rider's rows, done before the first pass
+    };
 };
 
 // A pass's global loads of one thread.
@@ -315,17 +318,29 @@ struct GemmStage {
 // X2 (two-word activations, the low words xl): a block's two exact int32
 // sums, one MFMA each against the same weight fragment, joined as
 // 128 * isum + isum_lo (below 2^27 in magnitude) and scaled by ws * xs / 128.
-template <int MT, bool X2>
+//
+// TK: the launch also carries the top-K of `tk.rows` rows of router logits
+// (E <= TOPK_LDS_E), as k_topk computes it, so the top-K needs no launch of
+// its own.  Workgroup w ranks row w after its first two passes' loads are
+// issued, so the ranking runs while they are in flight (its logit requested
+// before them, so its wait does not wait for them), and keeps the kept
+// choices in LDS; their weights (a double exp each) are formed after the
+// contraction, when its registers are free.  Rows past the workgroups (a
+// grid smaller than the rows) are ranked at the end.
+template <int MT, bool X2, bool TK>
 __global__ void __launch_bounds__(GEMM_NW * WAVE)
     k_gemm_i8(const int8_t *__restrict__ Wq, const float *__restrict__ Ws, int n_out, int n_in,
               const int8_t *__restrict__ xq, const float *__restrict__ xs, int m, float *__restrict__ y,
-              const int8_t *__restrict__ xl)
+              const int8_t *__restrict__ xl, TopkRider tk)
 {
     typedef int v4i __attribute__((ext_vector_type(4)));
     using L = GemmLds<MT, X2>;
     using S = GemmStage<MT, X2>;
     constexpr int TM = L::TM;
+    static_assert(sizeof(TopkLds) <= sizeof(float) * GEMM_NW * TM * (GEMM_TN + 4), "the rider fits the partials");
+    static_assert(GEMM_NW * WAVE >= TOPK_LDS_E, "one thread a logit");
     __shared__ __attribute__((aligned(16))) L sm;
+    __shared__ TopkKept kept;  // (TK) row w's choices, from the ranking to the weights
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int j = lane & 15, g = lane >> 4;
@@ -433,10 +448,30 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
         contract();
     };
 
+    const int wg = blockIdx.x + gridDim.x * blockIdx.y, nwg = gridDim.x * gridDim.y;
+    double lv = 0.0;
+    if constexpr (TK)  // a relaxed atomic load: kept in place, ahead of the passes' loads
+        lv = __hip_atomic_load(tk.logits + (int64_t)min(wg, tk.rows - 1) * tk.E + min(tid, tk.E - 1),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     S st0, st1;
     issue(st0, 0);
-    if (np > 1)
+    if constexpr (TK)
+        issue(st1, min(1, np - 1));  // unconditional, so the logit's wait is exact (np = 1 reloads pass 0)
+    else if (np > 1)
         issue(st1, 1);
+    if constexpr (TK) {
+        if (wg < tk.rows) {
+            topk_put(sm.tk, lv, tk.E);
+            __syncthreads();
+            topk_select(sm.tk, tk.E, tk.k);
+            __syncthreads();
+            if (tid < tk.k) {
+                kept.kl[tid] = sm.tk.kl[tid];
+                kept.ch[tid] = sm.tk.ch[tid];
+            }
+            // the first pass's barriers order these before the partials' writes
+        }
+    }
     for (int p = 0; p < np; p += 2) {
         pass(st0, p);
         if (p + 1 < np)
@@ -458,6 +493,20 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
             v += sm.part[w][r][c];
         if (r0 + r < m && o0 + c < n_out)
             y[(int64_t)(r0 + r) * n_out + o0 + c] = v;
+    }
+    if constexpr (TK) {
+        // the kept choices were written by wave 0's own lanes
+        if (wg < tk.rows && tid < WAVE)
+            route_finish(kept.kl, kept.ch, tk.k, tk.idx + (int64_t)wg * tk.k, tk.wts + (int64_t)wg * tk.k);
+        for (int row = wg + nwg; row < tk.rows; row += nwg) {
+            __syncthreads();  // the partials (or the previous row) are read
+            topk_load(sm.tk, tk.logits + (int64_t)row * tk.E, tk.E);
+            __syncthreads();
+            topk_select(sm.tk, tk.E, tk.k);
+            __syncthreads();
+            if (tid < WAVE)
+                route_finish(sm.tk.kl, sm.tk.ch, tk.k, tk.idx + (int64_t)row * tk.k, tk.wts + (int64_t)row * tk.k);
+        }
     }
 }
 
@@ -530,30 +579,47 @@ hipError_t launch_act(const GemvArgs &a, const SliceShape &sh, hipStream_t st)
 
 } // namespace
 
+namespace {
+
+// The matrix-core path: row tiles of 16 rows for m <= 16, else of 32 (64-row
+// tiles would spill registers; two 32-row tiles of the same weights run on
+// one XCD, blockIdx.y apart by a multiple of 8 workgroups when n_out is a
+// multiple of 128, so the second read of the weights can hit its L2).
+template <bool TK>
+hipError_t gemm_go(const GemvArgs &a, const TopkRider &tk, hipStream_t st)
+{
+    const int mt = a.m <= 16 ? 1 : 2;
+    const dim3 grid((unsigned)((a.n_out + GEMM_TN - 1) / GEMM_TN), (unsigned)((a.m + 16 * mt - 1) / (16 * mt)));
+    const dim3 block(GEMM_NW * WAVE);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs, (int)a.m,
+                           a.y, a.xl, tk);
+    };
+    if (a.act == 2)
+        mt == 1 ? go(k_gemm_i8<1, true, TK>) : go(k_gemm_i8<2, true, TK>);
+    else
+        mt == 1 ? go(k_gemm_i8<1, false, TK>) : go(k_gemm_i8<2, false, TK>);
+    return hipGetLastError();
+}
+
+} // namespace
+
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t st)
 {
-    if (a.act >= 1 && a.m >= GEMM_MIN_ROWS) {
-        // row tiles of 16 rows for m <= 16, else of 32 (64-row tiles would
-        // spill registers; two 32-row tiles of the same weights run on one
-        // XCD, blockIdx.y apart by a multiple of 8 workgroups when n_out is a
-        // multiple of 128, so the second read of the weights can hit its L2)
-        const int mt = a.m <= 16 ? 1 : 2;
-        const dim3 grid((unsigned)((a.n_out + GEMM_TN - 1) / GEMM_TN), (unsigned)((a.m + 16 * mt - 1) / (16 * mt)));
-        const dim3 block(GEMM_NW * WAVE);
-        auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, grid, block, 0, st, a.Wq, a.Ws, (int)a.n_out, (int)a.n_in, a.xq, a.xs,
-                               (int)a.m, a.y, a.xl);
-        };
-        if (a.act == 2)
-            mt == 1 ? go(k_gemm_i8<1, true>) : go(k_gemm_i8<2, true>);
-        else
-            mt == 1 ? go(k_gemm_i8<1, false>) : go(k_gemm_i8<2, false>);
-        return hipGetLastError();
-    }
+    if (a.act >= 1 && a.m >= GEMM_MIN_ROWS)
+        return gemm_go<false>(a, TopkRider{}, st);
     const SliceShape sh = slice_shape(a.n_in);
     if (a.act == 2)
         return launch_act<2>(a, sh, st);
     return a.act == 0 ? launch_act<0>(a, sh, st) : launch_act<1>(a, sh, st);
+}
+
+bool gemv_topk_fused(int64_t m, int64_t E, int act) { return act >= 1 && m >= GEMM_MIN_ROWS && E <= TOPK_LDS_E; }
+
+hipError_t gemv_topk_launch(const GemvArgs &a, const double *logits, int64_t rows, int64_t E, int64_t k, int32_t *idx,
+                            float *wts, hipStream_t st)
+{
+    return gemm_go<true>(a, TopkRider{logits, (int)rows, (int)E, (int)k, idx, wts}, st);
 }
 
 bool norm_gemv_supported(int64_t rows, int64_t d)

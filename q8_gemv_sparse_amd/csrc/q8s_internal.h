@@ -62,6 +62,12 @@ struct GemvArgs {
     const int8_t *xl;    // two words: the low words
 };
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t st);
+// The matrix-core GEMM of `a` (act 1 or 2, m >= GEMM_MIN_ROWS) carrying the
+// top-K of `rows` rows of E logits (E <= 256): idx/wts as route_launch
+// writes them, in the same launch.  gemv_topk_fused says when it applies.
+bool gemv_topk_fused(int64_t m, int64_t E, int act);
+hipError_t gemv_topk_launch(const GemvArgs &a, const double *logits, int64_t rows, int64_t E, int64_t k, int32_t *idx,
+                            float *wts, hipStream_t st);
 
 // add + norm fused into the batch-1 GEMV (one row, d <= 4096)
 struct NormGemvArgs {
@@ -105,6 +111,9 @@ hipError_t norm_logits_launch(const float *h, const float *r, const float *w, in
 
 // router scratch: f64 logits [rows, E]
 size_t route_scratch_bytes(int64_t rows, int64_t E);
+// the first of route_launch's two launches: the f64 logits [rows, E]
+hipError_t logits_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, double *logits,
+                         hipStream_t st);
 hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
                         float *wts, void *scratch, hipStream_t st);
 // the router over Q8_0 rows: float32 x (act 0), its Q8_0 form xq/xs (act 1),

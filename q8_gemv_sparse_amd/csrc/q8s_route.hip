@@ -329,10 +329,9 @@ hipError_t topk_go(const double *logits, int64_t rows, int64_t E, int64_t k, int
 
 } // namespace
 
-hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
-                        float *wts, void *scratch, hipStream_t st)
+hipError_t logits_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, double *logits,
+                         hipStream_t st)
 {
-    double *logits = reinterpret_cast<double *>(scratch);
     static_assert(LG_E * LG_R == 32 && RT_WAVES == 4, "k_logits_tile reduces 32 sums over four waves");
     if (rows == 1)
         hipLaunchKernelGGL((k_logits<1>), dim3((unsigned)E, 1), dim3(RT_THREADS), 0, st, x, Wr, (int)rows, (int)d,
@@ -343,7 +342,14 @@ hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d
     else
         hipLaunchKernelGGL((k_logits<4>), dim3((unsigned)E, (unsigned)((rows + 3) / 4)), dim3(RT_THREADS), 0, st, x,
                            Wr, (int)rows, (int)d, (int)E, logits);
-    hipError_t err = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t route_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
+                        float *wts, void *scratch, hipStream_t st)
+{
+    double *logits = reinterpret_cast<double *>(scratch);
+    hipError_t err = logits_launch(x, Wr, rows, d, E, logits, st);
     if (err != hipSuccess)
         return err;
     return topk_go(logits, rows, E, k, idx, wts, st);
