@@ -115,10 +115,11 @@ Q8S_DEV int idx_gather(IdxBatch &b, const int32_t *__restrict__ idx, int nchoice
 //     the wave together, each exchange step halving the
 //     values a lane keeps (10 exchanges instead of 8 x 6; the first two are
 //     lane-half swaps), ending with every value in one group of 8 lanes;
-//   * each wave requests its rows first (they stay in its registers); wave 0
-//     then gathers up to CK_NA of the expert's choices (choice order) and the
-//     workgroup stages their Q8_0 activation rows in LDS, so the gather and
-//     the staging overlap the weight rows' latency.
+//   * wave 0 requests the choice list, then each wave its rows (they stay in
+//     its registers); wave 0 gathers up to CK_NA of the expert's choices
+//     (choice order) and the workgroup stages their Q8_0 activation rows in
+//     LDS, so the gather and the staging overlap the weight rows' latency;
+//     the lanes trade halves only after that (the trade waits for the rows).
 // More than CK_NA choices take further passes over the same registers.
 constexpr int CK_NA = 16;
 constexpr int CKB_NW = 4;               // waves
@@ -209,6 +210,11 @@ __global__ void __launch_bounds__(CKB_NW * WAVE, X2 ? 3 : 4)
     const int f0 = lane < 32 ? 2 * lane : 2 * lane - 63;
     const int c0 = min(f0, nch - 1), c1 = min(64 + f0, nch - 1);  // the chunks the lane loads
 
+    // wave 0 requests the choice list first, so waiting for it does not wait
+    // for the weight rows requested after it
+    IdxBatch ib;
+    if (wid == 0)
+        idx_load(ib, idx, nchoice, 0, lane);
     // the wave's rows o0 + CKB_U*wid + u; the invalid bucket (e == E) writes
     // zeros and reads expert 0's first rows (served from cache after the first)
     i32x4 gq[CKB_U][2], uq[CKB_U][2];
@@ -225,36 +231,25 @@ __global__ void __launch_bounds__(CKB_NW * WAVE, X2 ? 3 : 4)
         gs[u] = ld_stream_f32(Wgs + row * nb + bl);
         us[u] = ld_stream_f32(Wus + row * nb + bl);
     }
-    // the trade: lane l < 32 gives its second load (half of block 32 + l) to
-    // lane l + 32 and takes that lane's first (the other half of block l)
-    auto trade = [&](i32x4 (&w)[2]) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)w[0][i], (uint32_t)w[1][i], false, false);
-            w[0][i] = (int)r[0];
-            w[1][i] = (int)r[1];
-        }
-    };
-#pragma unroll
-    for (int u = 0; u < CKB_U; u++) {
-        trade(gq[u]);
-        trade(uq[u]);
-    }
-    for (int first = 0;; first += NA) {
+
+    // gathers the pass of choices from `first` (wave 0) and stages their
+    // activation rows; returns how many (n), and the expert's total in `total`
+    auto prepare = [&](int first, int &total) {
         if (wid == 0) {
-            IdxBatch ib;
-            idx_load(ib, idx, nchoice, 0, lane);
+            if (first > 0)
+                idx_load(ib, idx, nchoice, 0, lane);
             const int tot = idx_gather<NA>(ib, idx, nchoice, e, E, first, list, lane);
             if (lane == 0)
                 totsh = tot;
         }
         __syncthreads();
-        const int total = totsh, n = min(NA, max(0, total - first));
+        total = totsh;
+        const int n = min(NA, max(0, total - first));
         if (n == 0)
-            break;
-        // stage the n choices' activation rows: 16-byte chunk t of every row by
-        // thread t, four rows' loads in flight at a time (straight-line; a row
-        // past n rereads row n-1)
+            return 0;
+        // stage the n choices' activation rows: 16-byte chunk t of every row
+        // by thread t, four rows' loads in flight at a time (straight-line; a
+        // row past n rereads row n-1)
         if ((int)threadIdx.x < nch) {
             const int t = threadIdx.x;
             for (int q0 = 0; q0 < n; q0 += 4) {
@@ -279,7 +274,29 @@ __global__ void __launch_bounds__(CKB_NW * WAVE, X2 ? 3 : 4)
             }
         }
         __syncthreads();
-        static_assert(CKB_U == 4, "a choice's four row pairs x gate/up = 8 values a reduction");
+        return n;
+    };
+
+    int first = 0, total;
+    int n = prepare(0, total);
+    // the trade, once the rows are staged: lane l < 32 gives its second load
+    // (half of block 32 + l) to lane l + 32 and takes that lane's first (the
+    // other half of block l)
+    auto trade = [&](i32x4 (&w)[2]) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)w[0][i], (uint32_t)w[1][i], false, false);
+            w[0][i] = (int)r[0];
+            w[1][i] = (int)r[1];
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < CKB_U; u++) {
+        trade(gq[u]);
+        trade(uq[u]);
+    }
+    static_assert(CKB_U == 4, "a choice's four row pairs x gate/up = 8 values a reduction");
+    while (n > 0) {
         for (int q = 0; q < n; q++) {
             i32x4 a[2], al[2];
             a[0] = *reinterpret_cast<const i32x4 *>(&act[q][QB * bl]);
@@ -315,6 +332,8 @@ __global__ void __launch_bounds__(CKB_NW * WAVE, X2 ? 3 : 4)
         if (total <= first + NA)
             break;
         __syncthreads();  // the next pass rewrites the list and the staged rows
+        first += NA;
+        n = prepare(first, total);
     }
 }
 
@@ -432,6 +451,12 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
         blk[m] = min(b, nb - 1);
     }
 
+    // wave 0 requests the choice list first, so waiting for it does not wait
+    // for the weight rows requested after it; the list's scan, the staging of
+    // the hidden rows and the weight rows' latency then overlap
+    IdxBatch ib;
+    if (wid == 0)
+        idx_load(ib, idx, nchoice, 0, lane);
     // the rows of slot u: o0 + 8*(CKD_U*wid + u) + grp (clamped to d - 1)
     i32x4 w[CKD_U][C];
     float ws[CKD_U][M];
@@ -447,33 +472,22 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
         for (int m = 0; m < M; m++)
             ws[u][m] = ld_stream_f32(Wds + row * nb + blk[m]);
     }
-    // the trade: for chunk pair (2m, 2m+1) even lanes keep 2m and take the
-    // partner's half of it, odd lanes keep 2m+1 and take the partner's half
-#pragma unroll
-    for (int u = 0; u < CKD_U; u++)
-#pragma unroll
-        for (int m = 0; m < M; m++) {
-            i32x4 got;
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                got[i] = dpp_i<DPP_XOR1>(odd ? w[u][2 * m][i] : w[u][2 * m + 1][i]);
-            // block: (first half, second half)
-            w[u][2 * m] = odd ? got : w[u][2 * m];
-            w[u][2 * m + 1] = odd ? w[u][2 * m + 1] : got;
-        }
 
-    for (int first = 0;; first += CK_NA) {
+    // gathers the pass of choices from `first` (wave 0) and stages their
+    // hidden rows; returns how many (n), and the expert's total in `total`
+    auto prepare = [&](int first, int &total) {
         if (wid == 0) {
-            IdxBatch ib;
-            idx_load(ib, idx, nchoice, 0, lane);
+            if (first > 0)
+                idx_load(ib, idx, nchoice, 0, lane);
             const int tot = idx_gather<CK_NA>(ib, idx, nchoice, e, E, first, list, lane);
             if (lane == 0)
                 totsh = tot;
         }
         __syncthreads();
-        const int total = totsh, n = min(CK_NA, max(0, total - first));
+        total = totsh;
+        const int n = min(CK_NA, max(0, total - first));
         if (n == 0)
-            break;
+            return 0;
         // stage the n choices' hidden rows (chunk t by thread t)
         if ((int)threadIdx.x < nch) {
             const int t = threadIdx.x;
@@ -499,6 +513,28 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
             }
         }
         __syncthreads();
+        return n;
+    };
+
+    int first = 0, total;
+    int n = prepare(0, total);
+    // the trade, once the rows are staged: for chunk pair (2m, 2m+1) even
+    // lanes keep 2m and take the partner's half of it, odd lanes keep 2m+1
+    // and take the partner's half
+#pragma unroll
+    for (int u = 0; u < CKD_U; u++)
+#pragma unroll
+        for (int m = 0; m < M; m++) {
+            i32x4 got;
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                got[i] = dpp_i<DPP_XOR1>(odd ? w[u][2 * m][i] : w[u][2 * m + 1][i]);
+            // block: (first half, second half)
+            w[u][2 * m] = odd ? got : w[u][2 * m];
+            w[u][2 * m + 1] = odd ? w[u][2 * m + 1] : got;
+        }
+
+    while (n > 0) {
         // one choice a step (two at once held twice the activation registers
         // and kept the kernel at three workgroups a CU)
         for (int q = 0; q < n; q++) {
@@ -538,7 +574,9 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
         }
         if (total <= first + CK_NA)
             break;
-        __syncthreads();
+        __syncthreads();  // the next pass rewrites the list and the staged rows
+        first += CK_NA;
+        n = prepare(first, total);
     }
 }
 
