@@ -620,8 +620,9 @@ __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__
 //     of their use, the rows' scales 16 bytes a load; lanes 32 apart then
 //     swap halves (v_permlane32_swap) so each holds 8 bytes of block 2p and
 //     8 of block 2p+1, the MFMA's fragments.
-//     Both buffers' first fetches are issued before the choice list is
-//     scanned, and each buffer is refilled as soon as its blocks are used;
+//     Wave 0 requests the choice list, then both buffers' first fetches
+//     are issued, so the list scan and the staging overlap them, and each
+//     buffer is refilled as soon as its blocks are used;
 //   * A operand: the rows of up to TM of the expert's choices (gathered in
 //     choice order), staged in LDS once per choice tile with their scales
 //     (only the row tiles in use, several loads a thread in flight); each
@@ -657,7 +658,7 @@ constexpr int GW_BU = 4;              // blocks of B a buffer (two buffers a wav
 constexpr int GW_SB = 8;              // staging loads in flight a thread
 
 template <int TM, bool PAIR, bool X2>
-__global__ void __launch_bounds__(GW_NW * WAVE)
+__global__ void __launch_bounds__(GW_NW * WAVE) __attribute__((amdgpu_waves_per_eu(TM == 16 ? 3 : 2)))
     k_grouped_mfma(const int8_t *__restrict__ aq, const int8_t *__restrict__ al, const float *__restrict__ as,
                    int a_div, const int8_t *__restrict__ Wq0, const float *__restrict__ Ws0,
                    const int8_t *__restrict__ Wq1, const float *__restrict__ Ws1, const int32_t *__restrict__ idx,
@@ -685,8 +686,9 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
     const int e = blockIdx.y;
     const int o0 = blockIdx.x * OT;
 
-    // the wave's weight row j (and up row j) of expert e
-    const int64_t wrow = (int64_t)e * R + o0 + 16 * wid + j;
+    // the wave's weight row j (and up row j) of expert e (the invalid
+    // bucket, e == E, reads expert 0's rows and never uses them)
+    const int64_t wrow = (int64_t)(e < E ? e : 0) * R + o0 + 16 * wid + j;
     const int lofs = 16 * g;
     const int8_t *bq0 = Wq0 + wrow * K + lofs;
     const float *bs0 = Ws0 + wrow * nb;
@@ -730,24 +732,32 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
         f0 = (long)(uint32_t)a[0] | ((long)(uint32_t)c[0] << 32);
         f1 = (long)(uint32_t)a[1] | ((long)(uint32_t)c[1] << 32);
     };
-    // both buffers' first fetches do not wait for the choice list (nor for
-    // the staging of the choices' rows)
-    if (e < E) {
-        fetch(0, 0);
-        if (GW_BU < nb)
-            fetch(1, GW_BU);
-    }
+    // wave 0 requests the choice list first, then both buffers' first
+    // fetches go out, unconditionally (rows are whole multiples of 256 bytes,
+    // so nb >= 2 * GW_BU): waiting for the list then waits for nothing else,
+    // and the list scan and the staging overlap the fetches' latency
+    IdxBatch ib;
+    if (wid == 0)
+        idx_load(ib, idx, nchoice, 0, lane);
+    fetch(0, 0);
+    fetch(1, GW_BU);
 
-    for (int first = 0;; first += TM) {
+    // wave 0 gathers the tile of choices from `first`; returns the expert's
+    // total (the first call is apart from the loop, so its wait is exact)
+    auto gather = [&](int first) {
         if (wid == 0) {
-            IdxBatch ib;
-            idx_load(ib, idx, nchoice, 0, lane);
+            if (first > 0)
+                idx_load(ib, idx, nchoice, 0, lane);
             const int tot = idx_gather<TM>(ib, idx, nchoice, e, E, first, list, lane);
             if (lane == 0)
                 totsh = tot;
         }
         __syncthreads();
-        const int total = totsh, n = min(TM, max(0, total - first));
+        return totsh;
+    };
+    int first = 0, total = gather(0);
+    for (;;) {
+        const int n = min(TM, max(0, total - first));
         if (n == 0)
             break;
         if (e >= E) {
@@ -757,8 +767,7 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
         } else {
             if (first > 0) {
                 fetch(0, 0);
-                if (GW_BU < nb)
-                    fetch(1, GW_BU);
+                fetch(1, GW_BU);
             }
             // stage the A rows of the tiles in use (rows past n repeat the
             // last one; their results are never written) and their scales,
@@ -891,6 +900,8 @@ __global__ void __launch_bounds__(GW_NW * WAVE)
         if (total <= first + TM)
             break;
         __syncthreads();  // the next tile rewrites the list and the staged rows
+        first += TM;
+        total = gather(first);
     }
 }
 
