@@ -581,23 +581,41 @@ __global__ void __launch_bounds__(CKD_NW * WAVE)
 }
 
 // With resid: y = resid + the mixture (the residual stream folded in).
+// Lane j of each wave reads slot j's choice and weight (k <= 32), and every
+// slot's result row is read whatever its choice (a choice outside [0, E)
+// drops it by a select), 8 slots' loads in flight at a time, so the slots
+// cost a round trip a batch instead of one each; the sum runs in slot order.
+constexpr int CMB_B = 8;  // slots a batch
 __global__ void __launch_bounds__(256) k_chunk_combine(const float *__restrict__ pa, const int32_t *__restrict__ idx,
                                                      const float *__restrict__ wts, int d, int k, int E,
                                                      const float *__restrict__ resid, float *__restrict__ y)
 {
-    const int64_t r = blockIdx.y;
-    const int o = blockIdx.x * 256 + threadIdx.x;
-    if (o >= d)
-        return;
+    const int64_t r = blockIdx.y, rk = r * k;
+    const int o = blockIdx.x * 256 + threadIdx.x, oc = min(o, d - 1);  // every lane reads; lanes past d store nothing
+    const int lane = threadIdx.x & (WAVE - 1);
+    const float rv = resid ? resid[r * d + oc] : 0.0f;  // requested first: the waits below do not wait for it
+    const int ej = idx[rk + min(lane, k - 1)];
+    const float wj = wts[rk + min(lane, k - 1)];
     float acc = 0.0f;
-    for (int jj = 0; jj < k; jj++) {
-        const int e = idx[r * k + jj];
-        if (e >= 0 && e < E)
-            acc = __builtin_fmaf(wts[r * k + jj], pa[(r * k + jj) * d + o], acc);
+    for (int j0 = 0; j0 < k; j0 += CMB_B) {
+        float pv[CMB_B];
+#pragma unroll
+        for (int u = 0; u < CMB_B; u++)
+            pv[u] = pa[(rk + min(j0 + u, k - 1)) * d + oc];
+        __builtin_amdgcn_sched_barrier(0);  // the batch's loads go out before any slot's choice is read
+#pragma unroll
+        for (int u = 0; u < CMB_B; u++) {
+            const int j = min(j0 + u, k - 1);
+            const int e = __builtin_amdgcn_readlane(ej, j);
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
+            const bool use = j0 + u < k && e >= 0 && e < E;
+            acc = use ? __builtin_fmaf(w, pv[u], acc) : acc;
+        }
     }
     if (resid)
-        acc = resid[r * d + o] + acc;
-    y[r * d + o] = acc;
+        acc = rv + acc;
+    if (o < d)
+        y[r * d + o] = acc;
 }
 
 // ---------------------------------------------------------------------------
