@@ -209,49 +209,49 @@ __global__ void __launch_bounds__(NORM_THREADS)
 }
 
 // q8_quantize_rows: the same epilogue on a given f32 row set.  Threads own 8
-// values; the grid covers rows x 2048-value segments.
-__global__ void __launch_bounds__(NORM_THREADS) k_quantize_rows(const float *__restrict__ x, int64_t n,
+// values of the rows taken as one array (n is a multiple of 32, so a block
+// never straddles two rows and block b of the array is block b of xs), so
+// every thread of every workgroup has work whatever n is: 512 hidden rows of
+// 768 values are 192 full workgroups, not 512 of which 62 % sat idle.
+__global__ void __launch_bounds__(NORM_THREADS) k_quantize_rows(const float *__restrict__ x, int64_t total,
                                                                 int8_t *__restrict__ xq, float *__restrict__ xs)
 {
-    const int64_t row = blockIdx.y;
-    const int64_t base = (int64_t)blockIdx.x * NORM_SEG + threadIdx.x * 8;
-    if (base >= n)
-        return;  // whole 4-thread groups leave together: n is a multiple of 32
-    const float *p = x + row * n + base;
-    const f32x4 a0 = ldf4(p), a1 = ldf4(p + 4);
+    const int64_t base = ((int64_t)blockIdx.x * NORM_THREADS + threadIdx.x) * 8;
+    if (base >= total)
+        return;  // whole 4-thread groups leave together: total is a multiple of 32
+    const f32x4 a0 = ldf4(x + base), a1 = ldf4(x + base + 4);
     const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    quant8_store(v, xq + row * n + base, xs + row * (n / QB) + base / QB, (threadIdx.x & 3) == 0);
+    quant8_store(v, xq + base, xs + base / QB, (threadIdx.x & 3) == 0);
 }
 
 // q8_quantize_rows_x2: the two-word form, the same grid (words and scales
 // equal k_quantize_rows', plus the low words).
-__global__ void __launch_bounds__(NORM_THREADS) k_quantize_rows_x2(const float *__restrict__ x, int64_t n,
+__global__ void __launch_bounds__(NORM_THREADS) k_quantize_rows_x2(const float *__restrict__ x, int64_t total,
                                                                    int8_t *__restrict__ xq, int8_t *__restrict__ xl,
                                                                    float *__restrict__ xs)
 {
-    const int64_t row = blockIdx.y;
-    const int64_t base = (int64_t)blockIdx.x * NORM_SEG + threadIdx.x * 8;
-    if (base >= n)
-        return;  // whole 4-thread groups leave together: n is a multiple of 32
-    const float *p = x + row * n + base;
-    const f32x4 a0 = ldf4(p), a1 = ldf4(p + 4);
+    const int64_t base = ((int64_t)blockIdx.x * NORM_THREADS + threadIdx.x) * 8;
+    if (base >= total)
+        return;  // whole 4-thread groups leave together: total is a multiple of 32
+    const f32x4 a0 = ldf4(x + base), a1 = ldf4(x + base + 4);
     const float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    quant8x2_store(v, xq + row * n + base, xl + row * n + base, xs + row * (n / QB) + base / QB,
-                   (threadIdx.x & 3) == 0);
+    quant8x2_store(v, xq + base, xl + base, xs + base / QB, (threadIdx.x & 3) == 0);
 }
 
 hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, float *xs, hipStream_t st)
 {
-    dim3 grid((unsigned)((n + NORM_SEG - 1) / NORM_SEG), (unsigned)rows);
-    hipLaunchKernelGGL(k_quantize_rows, grid, dim3(NORM_THREADS), 0, st, x, n, xq, xs);
+    const int64_t total = rows * n;
+    const dim3 grid((unsigned)((total + 8 * NORM_THREADS - 1) / (8 * NORM_THREADS)));
+    hipLaunchKernelGGL(k_quantize_rows, grid, dim3(NORM_THREADS), 0, st, x, total, xq, xs);
     return hipGetLastError();
 }
 
 hipError_t quantize_x2_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, int8_t *xl, float *xs,
                               hipStream_t st)
 {
-    dim3 grid((unsigned)((n + NORM_SEG - 1) / NORM_SEG), (unsigned)rows);
-    hipLaunchKernelGGL(k_quantize_rows_x2, grid, dim3(NORM_THREADS), 0, st, x, n, xq, xl, xs);
+    const int64_t total = rows * n;
+    const dim3 grid((unsigned)((total + 8 * NORM_THREADS - 1) / (8 * NORM_THREADS)));
+    hipLaunchKernelGGL(k_quantize_rows_x2, grid, dim3(NORM_THREADS), 0, st, x, total, xq, xl, xs);
     return hipGetLastError();
 }
 

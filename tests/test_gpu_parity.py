@@ -433,6 +433,21 @@ def test_chunk_many_choices_per_expert(rows, E, k):
         assert rel_err(y[r], ry[r]) <= TOL_I8, r
 
 
+@pytest.mark.parametrize("k", [12, 32])
+def test_chunk_combine_many_slots(k):
+    # the per-row combine takes the slots in batches of 8 (k = 12: a full
+    # batch and a ragged one; k = 32: the most kept, four batches); the sum
+    # still runs in slot order
+    banner("chunk combine k=%d" % k)
+    m = synthetic.moe_inputs(13, 128, 96, 40, k, 24)
+    ridx, rw, rh, ry = oracle.moe(m.x, m.Wr, m.Wgq, m.Wgs, m.Wuq, m.Wus, m.Wdq, m.Wds, m.k, 1)
+    idx, wts, h, y = run_moe_gpu(m, 1)
+    assert np.array_equal(idx, ridx)
+    assert rel_err(h, rh) <= TOL_I8
+    for r in range(m.x.shape[0]):
+        assert rel_err(y[r], ry[r]) <= TOL_I8, r
+
+
 # Chunks of 8 and more choices an expert on average, in rows of whole
 # 256-byte groups, run their gate-up and down projection on the matrix cores:
 # 16 weight rows a wave against tiles of 32 staged choice rows (16 where 32
