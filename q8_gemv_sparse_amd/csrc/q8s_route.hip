@@ -11,7 +11,7 @@
 //             in quarters, so the whole router streams from HBM across ~E
 //             workgroups.  Products and sums are in double, so near-equal
 //             logits are ranked as the double-precision definition ranks them.
-//             From 16 rows up, k_logits_tile: one workgroup per 4 experts x 8
+//             From 16 rows up, k_logits_tile: one workgroup per 4 experts x 4
 //             rows, reading each row from cache once for several products.
 //   k_topk    one workgroup per row: the K best by (logit descending, index
 //             ascending) -- for E <= 256 every logit's exact rank in one pass
@@ -81,37 +81,39 @@ __global__ void __launch_bounds__(RT_THREADS) k_logits(const float *__restrict__
     }
 }
 
-// The 32 sums v[0..31] of a wave, reduced across its 64 lanes together: each
-// exchange halves the values a lane keeps (xor 32, xor 16, then the 16-, 8-
-// and 4-lane mirrors, whose partners differ in lane bits 3, 2 and 1), so lane
-// l ends with the whole wave's sum of v[(l >> 1) & 31], and its neighbour
-// l ^ 1 with the same.  Every index is summed by the same tree of additions.
-Q8S_DEV double wave_sum32_d(const double (&v)[32], int lane)
+// The 16 sums v[0..15] of a wave, reduced across its 64 lanes together: each
+// exchange halves the values a lane keeps (xor 32, xor 16, then the 16- and
+// 8-lane mirrors, whose partners differ in lane bits 3 and 2), and two more
+// exchanges (xor 2, xor 1) add the rest, so lane l ends with the whole wave's
+// sum of v[(l >> 2) & 15], as do lanes l ^ 1, l ^ 2 and l ^ 3.  Every index is
+// summed by the same tree of additions.
+Q8S_DEV double wave_sum16_d(const double (&v)[16], int lane)
 {
-    double w16[16], w8[8], w4[4], w2[2];
-    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
-#pragma unroll
-    for (int i = 0; i < 16; i++)
-        w16[i] = (b5 ? v[i + 16] : v[i]) + __shfl_xor(b5 ? v[i] : v[i + 16], 32);
+    double w8[8], w4[4], w2[2];
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8, b2 = lane & 4;
 #pragma unroll
     for (int i = 0; i < 8; i++)
-        w8[i] = (b4 ? w16[i + 8] : w16[i]) + __shfl_xor(b4 ? w16[i] : w16[i + 8], 16);
+        w8[i] = (b5 ? v[i + 8] : v[i]) + __shfl_xor(b5 ? v[i] : v[i + 8], 32);
 #pragma unroll
     for (int i = 0; i < 4; i++)
-        w4[i] = (b3 ? w8[i + 4] : w8[i]) + dpp_d<DPP_MIRROR>(b3 ? w8[i] : w8[i + 4]);
+        w4[i] = (b4 ? w8[i + 4] : w8[i]) + __shfl_xor(b4 ? w8[i] : w8[i + 4], 16);
 #pragma unroll
     for (int i = 0; i < 2; i++)
-        w2[i] = (b2 ? w4[i + 2] : w4[i]) + dpp_d<DPP_HALF_MIRROR>(b2 ? w4[i] : w4[i + 2]);
-    const double w = (b1 ? w2[1] : w2[0]) + dpp_d<DPP_XOR2>(b1 ? w2[0] : w2[1]);
+        w2[i] = (b3 ? w4[i + 2] : w4[i]) + dpp_d<DPP_MIRROR>(b3 ? w4[i] : w4[i + 2]);
+    double w = (b2 ? w2[1] : w2[0]) + dpp_d<DPP_HALF_MIRROR>(b2 ? w2[0] : w2[1]);
+    w += dpp_d<DPP_XOR2>(w);
     return w + dpp_d<DPP_XOR1>(w);
 }
 
 // Many rows (a chunk): one workgroup per tile of LG_E experts x LG_R rows, so
-// each router row and activation row it reads from cache serves 8 or 4 dot
+// each router row and activation row it reads from cache serves 4 dot
 // products.  A thread takes 8 consecutive values of d per 2048 and keeps the
-// 32 products' running sums (double); the sums meet through wave_sum32_d and
-// LDS, waves added in order.
-constexpr int LG_E = 4, LG_R = 8;
+// 16 products' running sums (double); the sums meet through wave_sum16_d and
+// LDS, waves added in order.  (Tiles of 4 experts x 8 rows, 32 sums a thread,
+// gave half the workgroups, one a CU with one wave a SIMD, and took the chunk's
+// router + dense projection call 0.6 us longer: 12.9 against 12.3 us at 64
+// rows, the logits the same to the bit.)
+constexpr int LG_E = 4, LG_R = 4;
 constexpr int64_t LG_MIN_ROWS = 16;
 
 __global__ void __launch_bounds__(RT_THREADS) k_logits_tile(const float *__restrict__ x, const float *__restrict__ Wr,
@@ -149,9 +151,9 @@ __global__ void __launch_bounds__(RT_THREADS) k_logits_tile(const float *__restr
                     acc[e * LG_R + r] += we * (double)xv[r][i >> 2][i & 3];
             }
     }
-    const double v = wave_sum32_d(acc, lane);
-    if ((lane & 1) == 0)
-        part[wid][(lane >> 1) & 31] = v;
+    const double v = wave_sum16_d(acc, lane);
+    if ((lane & 3) == 0)
+        part[wid][(lane >> 2) & 15] = v;
     __syncthreads();
     if (threadIdx.x < LG_E * LG_R) {
         const int e = threadIdx.x / LG_R, r = threadIdx.x % LG_R;
@@ -332,7 +334,7 @@ hipError_t topk_go(const double *logits, int64_t rows, int64_t E, int64_t k, int
 hipError_t logits_launch(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, double *logits,
                          hipStream_t st)
 {
-    static_assert(LG_E * LG_R == 32 && RT_WAVES == 4, "k_logits_tile reduces 32 sums over four waves");
+    static_assert(LG_E * LG_R == 16 && RT_WAVES == 4, "k_logits_tile reduces 16 sums over four waves");
     if (rows == 1)
         hipLaunchKernelGGL((k_logits<1>), dim3((unsigned)E, 1), dim3(RT_THREADS), 0, st, x, Wr, (int)rows, (int)d,
                            (int)E, logits);
