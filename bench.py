@@ -666,8 +666,8 @@ class ChunkBlock(MoeBlock):
 
     def __init__(self, name, cfg, act, copies):
         # the separate calls: the dense projection reads the chunk's Q8_0 rows
-        # that add_rmsnorm_q8 writes (in two words: q8_quantize_rows_x2 of
-        # its float32 rows), and the grouped gate-up is the dominant kernel
+        # that add_rmsnorm_q8 writes (in two words: add_rmsnorm_q8_x2's
+        # two-word form), and the grouped gate-up is the dominant kernel
         if act == "f32":
             raise SystemExit("workload %s runs in int8 numerics (one or two words)" % name)
         super().__init__(name, cfg, act, copies, rows=cfg["rows"], pool=8, separate=True)
@@ -707,10 +707,9 @@ class ChunkBlock(MoeBlock):
     def _norm(self, c):
         if self.act != "x2":
             return super()._norm(c)
-        q8 = self.q8
         i = c % self.pool
-        q8.add_rmsnorm_q8(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y, want_q8=False)
-        q8.q8_quantize_rows_x2(self.y, xq=self.xq, xl=self.xl, xs=self.xs)
+        self.q8.add_rmsnorm_q8_x2(self.h[i], self.r[i], self.w, 1e-6, sum=self.sum, y=self.y, yq=self.xq, yl=self.xl,
+                                  ys=self.xs)
 
     def _gate_up(self, c, a, want_q8=True):
         if self.act != "x2":
@@ -753,9 +752,7 @@ class ChunkBlock(MoeBlock):
         x2 = self.act == "x2"
         sfx = "_x2" if x2 else ""
         rows, n_dense = self.rows, self.dense_out.shape[1]
-        return [("add_rmsnorm_q8%s (k_add_rmsnorm_q8%s, %d rows)" % (" + q8_quantize_rows_x2" if x2 else "",
-                                                                    " + k_quantize_rows_x2" if x2 else "", rows),
-                 self._norm, 0),
+        return [("add_rmsnorm_q8%s (k_add_rmsnorm_q8, %d rows)" % ("_x2" if x2 else "", rows), self._norm, 0),
                 ("moe_route_topk_gemv%s: router + dense %d x %d -> %d (k_logits_tile + k_gemm_i8 carrying the "
                  "top-K)" % (" (two words)" if x2 else "", rows, d, n_dense), self._route_dense,
                  E * d * 4 + self.dense_bytes),

@@ -164,6 +164,21 @@ Q8S_API int add_rmsnorm_q8(const float *h, const float *r, const float *w, int64
                    float eps, float *sum, float *y, int8_t *yq, float *ys, void *stream);
 
 /*
+ * add_rmsnorm_q8_x2 -- add_rmsnorm_q8 with the normed rows' two-word form
+ * (the lane's default activations, codegen_cuda/lane/mod.rs module doc;
+ * arena.rs fn quant_parts) written in the same epilogue:
+ *   sum, y          exactly as add_rmsnorm_q8
+ *   yq, yl, ys      exactly as q8_quantize_rows_x2(y) writes them (yq and ys
+ *                   equal add_rmsnorm_q8's one-word form)
+ * One launch where add_rmsnorm_q8 followed by q8_quantize_rows_x2 is two.
+ * h, r, w, sum as add_rmsnorm_q8; y: device f32 [rows, d] or NULL; yq, yl:
+ * device int8 [rows, d]; ys: device f32 [rows, d/32] (all three required).
+ * eps >= 0.  Limits as add_rmsnorm_q8.
+ */
+Q8S_API int add_rmsnorm_q8_x2(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
+                              float *sum, float *y, int8_t *yq, int8_t *yl, float *ys, void *stream);
+
+/*
  * moe_route_topk -- the mixture's router and top-K (fn emit_moe_forward:
  * softmax, keep K, renormalise; fn kernel_refusal: no bias, a softmax over
  * every expert):

@@ -27,7 +27,7 @@ __all__ = [
     "q8s_version", "q8s_stream_read", "STREAM_WGS", "library", "q8_quantize_rows_x2", "q8_gemv_x2",
     "add_rmsnorm_gemv_x2", "moe_topk_gate_up_x2", "ACT_X2", "moe_ffn_block_noalloc", "NOALLOC_SCRATCH_BYTES",
     "moe_ffn_stack", "FN_STACK", "moe_gate_up_x2", "moe_down_combine_x2", "q8s_moe_path", "PATH_ROWS",
-    "PATH_GROUPED", "PATH_GROUPED_MFMA", "moe_route_topk_gemv",
+    "PATH_GROUPED", "PATH_GROUPED_MFMA", "moe_route_topk_gemv", "add_rmsnorm_q8_x2",
 ]
 
 ACT_F32 = 0
@@ -58,6 +58,7 @@ _SIGS = {
     "q8_gemv": [_p, _p, _i64, _i64, _p, _p, _p, _i64, _p, ctypes.c_int, _p],
     "q8_quantize_rows": [_p, _i64, _i64, _p, _p, _p],
     "add_rmsnorm_q8": [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p],
+    "add_rmsnorm_q8_x2": [_p, _p, _p, _i64, _i64, ctypes.c_float, _p, _p, _p, _p, _p, _p],
     "moe_route_topk": [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _sz, _p],
     "moe_route_topk_gemv": [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _i64, _p, _p, _p, _p, ctypes.c_int, _p,
                             _sz, _p],
@@ -310,6 +311,25 @@ def add_rmsnorm_q8(h, r, w, eps, sum=None, y=None, yq=None, ys=None, want_f32=Tr
     _check(_lib.add_rmsnorm_q8(_ptr(h), _ptr(r), _ptr(w), rows, d, float(eps), _ptr(sum), _ptr(y), _ptr(yq),
                                _ptr(ys), _stream(stream)))
     return sum, y, yq, ys
+
+
+def add_rmsnorm_q8_x2(h, r, w, eps, sum=None, y=None, yq=None, yl=None, ys=None, want_f32=True, stream=None):
+    """sum = h + r; y = RMSNorm(sum) * w; its two-word form in the same launch.
+    Returns (sum, y or None, yq, yl, ys)."""
+    _dev(h, torch.float32, "h"); _dev(r, torch.float32, "r"); _dev(w, torch.float32, "w")
+    d = h.shape[-1]
+    rows = h.numel() // d
+    f = lambda t, shape, dt: t if t is not None else torch.empty(shape, dtype=dt, device=h.device)
+    sum = f(sum, (rows, d), torch.float32)
+    if want_f32:
+        y = f(y, (rows, d), torch.float32)
+    yq = f(yq, (rows, d), torch.int8); yl = f(yl, (rows, d), torch.int8); ys = f(ys, (rows, d // 32), torch.float32)
+    for t, dt, n in ((sum, torch.float32, "sum"), (y, torch.float32, "y"), (yq, torch.int8, "yq"),
+                     (yl, torch.int8, "yl"), (ys, torch.float32, "ys")):
+        _dev(t, dt, n)
+    _check(_lib.add_rmsnorm_q8_x2(_ptr(h), _ptr(r), _ptr(w), rows, d, float(eps), _ptr(sum), _ptr(y), _ptr(yq),
+                                  _ptr(yl), _ptr(ys), _stream(stream)))
+    return sum, y, yq, yl, ys
 
 
 def moe_route_topk(x, Wr, k, idx=None, wts=None, scratch=None, stream=None):

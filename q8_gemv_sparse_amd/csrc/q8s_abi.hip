@@ -296,6 +296,26 @@ int add_rmsnorm_q8(const float *h, const float *r, const float *w, int64_t rows,
     return launched(q8s::add_rmsnorm_launch(h, r, w, rows, d, eps, sum, y, yq, ys, as_stream(stream)), fn);
 }
 
+int add_rmsnorm_q8_x2(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps, float *sum,
+                      float *y, int8_t *yq, int8_t *yl, float *ys, void *stream)
+{
+    const char *fn = "add_rmsnorm_q8_x2";
+    int rc;
+    if ((rc = check_count(fn, "rows", rows, INT32_MAX)) || (rc = check_dim32(fn, "d", d)))
+        return rc;
+    if (!(eps >= 0.0f) || eps != eps)
+        return fail(Q8S_EINVAL, "%s: eps must be a finite value >= 0", fn);
+    const size_t n = (size_t)(rows * d);
+    std::vector<Span> ins = {{h, n * 4, "h"}, {r, n * 4, "r"}, {w, (size_t)d * 4, "w"}};
+    std::vector<Span> outs = {{sum, n * 4, "sum"}, {yq, n, "yq"}, {yl, n, "yl"}, {ys, n / 32 * 4, "ys"}};
+    if (y)
+        outs.push_back({y, n * 4, "y"});
+    if ((rc = check_ptrs(fn, ins)) || (rc = check_ptrs(fn, outs)) || (rc = check_disjoint(fn, ins, outs)))
+        return rc;
+    clear_stale();
+    return launched(q8s::add_rmsnorm_launch(h, r, w, rows, d, eps, sum, y, yq, ys, as_stream(stream), yl), fn);
+}
+
 int moe_route_topk(const float *x, const float *Wr, int64_t rows, int64_t d, int64_t E, int64_t k, int32_t *idx,
                    float *wts, void *scratch, size_t scratch_bytes, void *stream)
 {
@@ -694,9 +714,7 @@ int add_rmsnorm_gemv_x2(const float *h, const float *r, const float *w, float ep
         q8s::NormGemvArgs a{h, r, w, eps, Wq, Ws, d, n_out, sum, y, yq, ys, out, 2, yl};
         return launched(q8s::norm_gemv_launch(a, st), fn);
     }
-    hipError_t e = q8s::add_rmsnorm_launch(h, r, w, rows, d, eps, sum, y, nullptr, nullptr, st);
-    if (e == hipSuccess)
-        e = q8s::quantize_x2_launch(y, rows, d, yq, yl, ys, st);
+    hipError_t e = q8s::add_rmsnorm_launch(h, r, w, rows, d, eps, sum, y, yq, ys, st, yl);
     if (e == hipSuccess) {
         q8s::GemvArgs g{Wq, Ws, n_out, d, nullptr, yq, ys, rows, out, 2, yl};
         e = q8s::gemv_launch(g, st);

@@ -164,12 +164,10 @@ hipError_t block_launch(const BlockArgs &b, hipStream_t st)
         a.wts_w = b.wts;
         err = route_gate_up_launch(a, st);
     } else {
-        // two words: the normed row's words, low words and scales from its
-        // float32 form (the same words and scales as the one-word epilogue's)
-        err = add_rmsnorm_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, b.sum, s.x, b.act == 2 ? nullptr : s.xq,
-                                 b.act == 2 ? nullptr : s.xs, st);
-        if (err == hipSuccess && b.act == 2)
-            err = quantize_x2_launch(s.x, b.rows, b.d, s.xq, s.xl, s.xs, st);
+        // two words: the normed row's words, low words and scales in the same
+        // epilogue (the same words and scales as the one-word epilogue's)
+        err = add_rmsnorm_launch(b.h, b.r, b.w, b.rows, b.d, b.eps, b.sum, s.x, s.xq, s.xs, st,
+                                 b.act == 2 ? s.xl : nullptr);
         if (err != hipSuccess)
             return err;
         if (rt.Wrq)

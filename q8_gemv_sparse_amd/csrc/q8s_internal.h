@@ -89,8 +89,9 @@ hipError_t quantize_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, 
 hipError_t quantize_x2_launch(const float *x, int64_t rows, int64_t n, int8_t *xq, int8_t *xl, float *xs,
                               hipStream_t st);
 hipError_t stream_read_launch(const void *buf, int64_t bytes, uint32_t *out, hipStream_t st);
+// with yl (and yq, ys): the normed rows' two-word form in the epilogue
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
-                              float *sum, float *y, int8_t *yq, float *ys, hipStream_t st);
+                              float *sum, float *y, int8_t *yq, float *ys, hipStream_t st, int8_t *yl = nullptr);
 // The router's rows: float32 Wr [E, d], or Q8_0 Wrq [E, d] + Wrs [E, d/32]
 // (Wrq non-null); a Q8_0 router reads float32 activations (act 0) or their
 // one-word int8 form (act 1).

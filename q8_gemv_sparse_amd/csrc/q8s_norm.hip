@@ -24,7 +24,8 @@ template <int SEGS>
 __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__restrict__ h, const float *__restrict__ r,
                                                                  const float *__restrict__ w, int d, float eps,
                                                                  float *__restrict__ sum, float *__restrict__ y,
-                                                                 int8_t *__restrict__ yq, float *__restrict__ ys)
+                                                                 int8_t *__restrict__ yq, float *__restrict__ ys,
+                                                                 int8_t *__restrict__ yl)
 {
     constexpr int NS = SEGS > 0 ? SEGS : 1;
     __shared__ double wsum[NORM_THREADS / WAVE];
@@ -73,8 +74,14 @@ __global__ void __launch_bounds__(NORM_THREADS) k_add_rmsnorm_q8(const float *__
             *reinterpret_cast<f32x4 *>(y + row * d + base) = f32x4{v[0], v[1], v[2], v[3]};
             *reinterpret_cast<f32x4 *>(y + row * d + base + 4) = f32x4{v[4], v[5], v[6], v[7]};
         }
-        if (yq)
-            quant8_store(v, yq + row * d + base, ys + row * (d / QB) + base / QB, (threadIdx.x & 3) == 0);
+        if (yq) {
+            // with yl: the two-word form (words and scales those of the one-word form)
+            if (yl)
+                quant8x2_store(v, yq + row * d + base, yl + row * d + base, ys + row * (d / QB) + base / QB,
+                               (threadIdx.x & 3) == 0);
+            else
+                quant8_store(v, yq + row * d + base, ys + row * (d / QB) + base / QB, (threadIdx.x & 3) == 0);
+        }
     }
 }
 
@@ -256,18 +263,18 @@ hipError_t quantize_x2_launch(const float *x, int64_t rows, int64_t n, int8_t *x
 }
 
 hipError_t add_rmsnorm_launch(const float *h, const float *r, const float *w, int64_t rows, int64_t d, float eps,
-                              float *sum, float *y, int8_t *yq, float *ys, hipStream_t st)
+                              float *sum, float *y, int8_t *yq, float *ys, hipStream_t st, int8_t *yl)
 {
     const int segs = (int)((d + NORM_SEG - 1) / NORM_SEG);
     const dim3 grid((unsigned)rows), block(NORM_THREADS);
     if (segs <= 1)
-        hipLaunchKernelGGL((k_add_rmsnorm_q8<1>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<1>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys, yl);
     else if (segs <= 2)
-        hipLaunchKernelGGL((k_add_rmsnorm_q8<2>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<2>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys, yl);
     else if (segs <= 4)
-        hipLaunchKernelGGL((k_add_rmsnorm_q8<4>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<4>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys, yl);
     else
-        hipLaunchKernelGGL((k_add_rmsnorm_q8<0>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys);
+        hipLaunchKernelGGL((k_add_rmsnorm_q8<0>), grid, block, 0, st, h, r, w, (int)d, eps, sum, y, yq, ys, yl);
     return hipGetLastError();
 }
 

@@ -81,6 +81,20 @@ def test_norm_refusals():
     assert norm(y=D) == -1 and "outputs `sum` and `y` overlap" in _err()
 
 
+def norm_x2(rows=1, d=64, eps=1e-6, h=A, r=B, w=C, s=D, y=F, yq=G, yl=H, ys=J):
+    return LIB.add_rmsnorm_q8_x2(h, r, w, rows, d, ctypes.c_float(eps), s, y, yq, yl, ys, None)
+
+
+def test_norm_x2_refusals():
+    assert norm_x2(d=20) == -1 and "multiple of 32" in _err()
+    assert norm_x2(yl=None) == -1 and "`yl` is null" in _err()
+    assert norm_x2(yq=None) == -1 and "`yq` is null" in _err()
+    assert norm_x2(s=None) == -1 and "`sum` is null" in _err()
+    assert norm_x2(eps=-1.0) == -1 and "eps" in _err()
+    assert norm_x2(yl=G + 32) == -1 and "overlap" in _err()
+    assert norm_x2(y=A) == -1 and "overlaps input `h`" in _err()
+
+
 def route(rows=1, d=64, E=8, k=2, sb=None, scratch=J, x=A, Wr=B, idx=C, wts=D):
     if sb is None:
         sb = q8.q8s_scratch_bytes(q8.FN_ROUTE, rows, d, 32, E, k)
@@ -103,6 +117,26 @@ def test_route_refusals_and_scratch():
 
 def gate_up(act=0, rows=1, d=64, dff=64, E=4, k=2, x=A, xq=A, xs=B, h=J, hq=H, hs=0xF0000000):
     return LIB.moe_gate_up(x, xq, xs, C, D, F, G, 0xD0000000, rows, d, dff, E, k, h, hq, hs, act, None)
+
+
+def route_gemv(rows=8, d=64, E=8, k=2, n_out=32, act=1, xl=None, sb=None, scratch=0x100000000, x=A, Wr=B, idx=C,
+               wts=D, Dq=F, Ds=G, xq=H, xs=J, y=0x110000000):
+    if sb is None:
+        sb = q8.q8s_scratch_bytes(q8.FN_ROUTE, rows, d, 32, E, k)
+    return LIB.moe_route_topk_gemv(x, Wr, rows, d, E, k, idx, wts, Dq, Ds, n_out, xq, xl, xs, y, act, scratch, sb,
+                                   None)
+
+
+def test_route_gemv_refusals():
+    assert route_gemv(act=0) == -2 and "Q8_0 form" in _err()
+    assert route_gemv(act=3) == -1
+    assert route_gemv(act=1, xl=0x120000000) == -1 and "`xl`" in _err()
+    assert route_gemv(act=2) == -1 and "`xl`" in _err()
+    assert route_gemv(k=9) == -1 and "1 <= k <= E" in _err()
+    assert route_gemv(n_out=0) == -1
+    assert route_gemv(d=40) == -1 and "multiple of 32" in _err()
+    assert route_gemv(sb=8) == -4 and "scratch" in _err()
+    assert route_gemv(y=H) == -1 and "overlaps input `xq`" in _err()
 
 
 def test_gate_up_refusals():

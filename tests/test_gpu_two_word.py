@@ -291,3 +291,26 @@ def test_x2_stage_calls_equal_block(rows):
     got = host(y)
     for r in range(rows):
         assert rel_err(got[r], ry[r]) <= TOL_X2_BLOCK, r
+
+
+@pytest.mark.parametrize("rows,d", [(1, 2048), (64, 2048), (3, 96), (2, 2080), (1, 4096), (2, 16384)])
+def test_add_rmsnorm_q8_x2_equals_norm_then_quantiser(rows, d):
+    # the two-word epilogue writes exactly what add_rmsnorm_q8 followed by
+    # q8_quantize_rows_x2 writes, every byte, and its words and scales are
+    # add_rmsnorm_q8's one-word form
+    banner("add_rmsnorm_q8_x2 rows=%d d=%d" % (rows, d))
+    rng = np.random.default_rng(31)
+    h, r = synthetic.normal(rng, rows, d), synthetic.normal(rng, rows, d)
+    w = rng.uniform(0.5, 1.5, d).astype(np.float32)
+    hd, rd, wd = dev(h), dev(r), dev(w)
+    s1, y1, q1, l1, s1c = q8.add_rmsnorm_q8_x2(hd, rd, wd, 1e-6)
+    s0, y0, _, _ = q8.add_rmsnorm_q8(hd, rd, wd, 1e-6, want_q8=False)
+    q0, l0, c0 = q8.q8_quantize_rows_x2(y0)
+    _, _, q1w, c1w = q8.add_rmsnorm_q8(hd, rd, wd, 1e-6)
+    for a, b in ((s1, s0), (y1, y0), (q1, q0), (l1, l0), (s1c, c0), (q1, q1w), (s1c, c1w)):
+        assert np.array_equal(host(a).view(np.uint8), host(b).view(np.uint8))
+    # without the float32 rows
+    _, none_y, q2, l2, c2 = q8.add_rmsnorm_q8_x2(hd, rd, wd, 1e-6, want_f32=False)
+    assert none_y is None
+    for a, b in ((q2, q0), (l2, l0), (c2, c0)):
+        assert np.array_equal(host(a).view(np.uint8), host(b).view(np.uint8))
