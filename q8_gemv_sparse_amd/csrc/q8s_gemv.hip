@@ -241,16 +241,17 @@ __global__ void __launch_bounds__(NORM_THREADS)
 // int8 MFMA GEMM (m >= GEMM_MIN_ROWS)
 //
 // Workgroup tile: 16 outputs x 16*MT activation rows (MT = 1 or 2 MFMA row
-// tiles), eight waves.  k is walked in passes of GEMM_KB Q8_0 blocks
-// (1 KiB of every row).  A pass's operands -- the 16 weight rows, the tile's
+// tiles), eight waves.  k is walked in passes of GemmPass::KB Q8_0 blocks
+// (1 KiB of every row; 512 bytes for 32-row tiles in two words).  A pass's operands -- the 16 weight rows, the tile's
 // activation rows and both sets of scales -- are read from global memory with
 // coalesced 16-byte loads into registers, stored to LDS, and the MFMA
 // fragments are read back from LDS.  Two passes are in flight: while a pass is
 // contracted, the next one but one is already requested (register double
-// buffer), so at the usual n_in of 2048 every global load of the workgroup is
-// issued before its first MFMA.
+// buffer), so at the usual n_in of 2048 in one word every global load of the
+// workgroup is issued before its first MFMA.
 //
-// Wave w takes blocks w, w + 8, w + 16, w + 24 of a pass, for every row tile:
+// Wave w takes blocks w, w + 8, w + 16, w + 24 of a pass (w, w + 8 at 16
+// blocks a pass: the same blocks in the same order over k), for every row tile:
 // per block it reads the weight fragment once, and per row tile one
 // v_mfma_i32_16x16x32_i8 yields the 16x16 exact int32 block sums, to which
 // each lane adds isum * (ws[o][b] * xs[r][b]) for the four (r, o) it holds.
@@ -265,10 +266,17 @@ __global__ void __launch_bounds__(NORM_THREADS)
 // the tile and weight row j (rows swizzled, gemm_swizzle).
 
 constexpr int GEMM_TN = 16;                    // outputs of a tile
-constexpr int GEMM_KB = 32;                    // Q8_0 blocks of k per pass
+// Q8_0 blocks of k per pass: 32 (1 KiB of a row), 16 for 32-row tiles in two
+// words, so the staged words and low words of the 32 rows (32 KiB) leave
+// room for two workgroups a CU (at 32 a pass they took 107 KiB of LDS: one a
+// CU, and a 64-row chunk's 512 workgroups ran in two rounds)
+template <int MT, bool X2>
+struct GemmPass {
+    static constexpr int KB = (X2 && MT == 2) ? 16 : 32;
+    static constexpr int ROW = KB * QB;          // LDS bytes per staged row
+    static constexpr int CH = KB * QB / 16;      // 16-byte chunks of a staged row
+};
 constexpr int GEMM_NW = 8;                     // waves
-constexpr int GEMM_ROW = GEMM_KB * QB;        // LDS bytes per staged row
-constexpr int GEMM_CH = GEMM_KB * QB / 16;     // 16-byte chunks of a staged row
 
 // LDS rows are stored swizzled in 8-byte units: unit u of row r sits at unit
 // u ^ gemm_swizzle(r % 16).  A wave's fragment reads of one block (8 bytes of
@@ -291,11 +299,12 @@ Q8S_DEV void put_swizzled(int8_t *row, int r, int k, i32x4 v)
 template <int MT, bool X2>
 struct GemmLds {
     static constexpr int TM = 16 * MT;
-    int8_t w[GEMM_TN][GEMM_ROW];
-    int8_t a[TM][GEMM_ROW];
-    int8_t l[X2 ? TM : 1][GEMM_ROW];
-    float ws[GEMM_KB][GEMM_TN + 1];
-    float xs[GEMM_KB][TM + 4];
+    using P = GemmPass<MT, X2>;
+    int8_t w[GEMM_TN][P::ROW];
+    int8_t a[TM][P::ROW];
+    int8_t l[X2 ? TM : 1][P::ROW];
+    float ws[P::KB][GEMM_TN + 1];
+    float xs[P::KB][TM + 4];
     union {
         float part[GEMM_NW][TM][GEMM_TN + 4];  // row pitch 20: a wave's 64 writes hit 64 banks
         TopkLds tk;                            // the top-K rider's rows, done before the first pass
@@ -305,9 +314,11 @@ struct GemmLds {
 // A pass's global loads of one thread.
 template <int MT, bool X2>
 struct GemmStage {
-    static constexpr int WL = GEMM_TN * GEMM_CH / (GEMM_NW * WAVE);       // weight chunks
-    static constexpr int AL = 16 * MT * GEMM_CH / (GEMM_NW * WAVE);       // activation chunks
-    static constexpr int XL = 16 * MT * GEMM_KB / (GEMM_NW * WAVE);       // activation scales
+    using P = GemmPass<MT, X2>;
+    static constexpr int WL = GEMM_TN * P::CH / (GEMM_NW * WAVE);       // weight chunks
+    static constexpr int AL = 16 * MT * P::CH / (GEMM_NW * WAVE);       // activation chunks
+    static constexpr int XL = 16 * MT * P::KB / (GEMM_NW * WAVE);       // activation scales
+    static_assert(WL >= 1 && AL >= 1 && XL >= 1, "every thread stages whole chunks");
     i32x4 w[WL];
     i32x4 a[AL];
     i32x4 l[X2 ? AL : 1];
@@ -337,6 +348,7 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
     using L = GemmLds<MT, X2>;
     using S = GemmStage<MT, X2>;
     constexpr int TM = L::TM;
+    constexpr int GEMM_KB = GemmPass<MT, X2>::KB, GEMM_CH = GemmPass<MT, X2>::CH;
     static_assert(sizeof(TopkLds) <= sizeof(float) * GEMM_NW * TM * (GEMM_TN + 4), "the rider fits the partials");
     static_assert(GEMM_NW * WAVE >= TOPK_LDS_E, "one thread a logit");
     __shared__ __attribute__((aligned(16))) L sm;
@@ -368,7 +380,9 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
                 st.l[i] = ld16(xl + r * n_in + min(k0 + (c % GEMM_CH) * 16, bmax));
         }
         {
-            const int64_t o = min(o0 + tid / GEMM_KB, n_out - 1);
+            // the tile's GEMM_TN x GEMM_KB scales, one a thread (threads past
+            // them, at 16 blocks a pass, reload the last row's)
+            const int64_t o = min(o0 + min(tid / GEMM_KB, GEMM_TN - 1), n_out - 1);
             st.ws = ld_stream_f32(Ws + o * nb + min(p * GEMM_KB + tid % GEMM_KB, nb - 1));
         }
 #pragma unroll
@@ -392,7 +406,8 @@ __global__ void __launch_bounds__(GEMM_NW * WAVE)
                 put_swizzled(&sm.l[c / GEMM_CH][0], c / GEMM_CH, c % GEMM_CH, st.l[i]);
         }
         // a block past the row gets weight scale 0, so it adds exactly 0
-        sm.ws[tid % GEMM_KB][tid / GEMM_KB] = p * GEMM_KB + tid % GEMM_KB < nb ? st.ws : 0.0f;
+        if (tid < GEMM_KB * GEMM_TN)
+            sm.ws[tid % GEMM_KB][tid / GEMM_KB] = p * GEMM_KB + tid % GEMM_KB < nb ? st.ws : 0.0f;
 #pragma unroll
         for (int i = 0; i < S::XL; i++) {
             const int e = tid + i * GEMM_NW * WAVE;
